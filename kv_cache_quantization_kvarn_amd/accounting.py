@@ -1,0 +1,46 @@
+"""Byte and token accounting for the benchmark (host-side arithmetic only).
+
+KV bytes of an uncompressed cache follow the size formula on the "KV Cache"
+glossary page, section "Boyutu ve Yönetimi": 2 x layers x KV heads x head_dim x
+tokens x bytes per element.  Packed page sizes come from the library
+(``kvarn_page_bytes``) so that this module never restates the format.
+"""
+from __future__ import annotations
+
+BLOCK_TOKENS = 128
+HEAD_DIM = 128
+FP16_BYTES = 2
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth, GB/s
+
+
+def fp16_kv_bytes(layers: int, kv_heads: int, tokens: int, head_dim: int = HEAD_DIM) -> int:
+    """Uncompressed K+V bytes: 2 x layers x heads x head_dim x tokens x 2 bytes."""
+    return 2 * layers * kv_heads * head_dim * tokens * FP16_BYTES
+
+
+def packed_bytes_per_block_head(k_page: int, v_page: int) -> int:
+    """Packed K+V bytes of one 128-token block of one KV head."""
+    return k_page + v_page
+
+
+def capacity_ratio(k_page: int, v_page: int) -> float:
+    """FP16 bytes / packed bytes for one 128-token block of one KV head."""
+    return fp16_kv_bytes(1, 1, BLOCK_TOKENS) / packed_bytes_per_block_head(k_page, v_page)
+
+
+def quantize_bytes(n_blocks: int, kv_heads: int, k_page: int, v_page: int) -> int:
+    """Algorithmic HBM bytes of one quantize call: fp16 K and V in, packed pages out."""
+    return n_blocks * kv_heads * (fp16_kv_bytes(1, 1, BLOCK_TOKENS) + k_page + v_page)
+
+
+def decode_bytes(total_blocks_attended: int, kv_heads: int, batch: int, q_heads: int, k_page: int, v_page: int,
+                 max_blocks_per_seq: int = 0) -> int:
+    """Algorithmic HBM bytes of one decode step.
+
+    Packed pages of every attended (block, KV head), the fp16 query (256 B per
+    query head), the fp32 output (512 B per query head), the block-table
+    entries read (4 B per attended block) and the sequence lengths.
+    """
+    return (total_blocks_attended * kv_heads * (k_page + v_page)
+            + batch * q_heads * (HEAD_DIM * 2 + HEAD_DIM * 4)
+            + total_blocks_attended * 4 + batch * 4)

@@ -1,0 +1,291 @@
+"""CPU oracle for KVarN block quantisation and decode attention over the packed cache.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: it exists so that the tests, the package smoke check and the
+CPU-baseline leg of the benchmark can compare the HIP path against a plain, slow
+and obviously correct definition.  It shares no code, constants table or helper
+with the HIP library; it only reads the page byte format, which it implements
+on its own from the description below.
+
+Sources.  The method is described in the KVarN blog post ("KVarN: Huawei'den
+KV-Cache Kuantizasyonu için Yerel vLLM Backend'i"), section "KVarN Nasıl
+Çalışır?": the cache is quantised in fixed-size token blocks, and every block
+goes through four stages -- the raw fp16 block, an orthonormal Hadamard rotation
+along the channel dimension, a Sinkhorn-like row/column variance normalisation
+in log space, and low-bit asymmetric round-to-nearest with 4-bit keys and 2-bit
+values.  Section "Pratik Çıkarımlar" of the same post names the format
+``kvarn_k4v2_g128`` (group size 128).  Paged storage with a block table and
+GQA head sharing come from the "KV Cache" glossary page, sections "Boyutu ve
+Yönetimi" and "Türleri".
+
+Parameters the pages leave open, fixed here (each is one reading):
+  * block = 128 tokens, head_dim = 128, normalisation iterations T = 4,
+    eps = 1e-6 added to the variance, log base 2;
+  * rotation: the natural-order Sylvester Hadamard matrix H[j,k] =
+    (-1)^popcount(j&k) / sqrt(128), no random signs, applied to K and V;
+  * "variance" = centred population variance; each iteration does the row pass
+    (over channels, per token) first, then the column pass (over tokens, per
+    channel); both normalisers start at 0;
+  * key groups: one channel over the 128 tokens of the block (L = 15);
+    value groups: one token over the 128 channels (L = 3);
+  * scale and zero stored as fp16; the zero is the group minimum (a float
+    offset); normalisers stored as fp32 log2 values, and the normalised values
+    that get quantised use the stored fp32 normalisers;
+  * the rounding decision is taken in fp32 (the precision the kernel computes
+    in): u = fp32(fp32(N - z) / s), code = clamp(round-half-even(u), 0, L);
+    a group whose fp16 scale is 0 stores all-zero codes;
+  * decode: query head h reads KV head h // (Hq / Hkv); logits scaled by
+    1/sqrt(128) unless a positive scale is given; plain softmax; output in the
+    original (unrotated) basis.
+
+Floating point is fp64 everywhere except where the format stores a narrower
+type or where the rounding decision is taken (fp32, see above).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 128
+HEAD_DIM = 128
+ITERS = 4
+EPS = 1e-6
+K_LEVELS = 15  # 4-bit keys
+V_LEVELS = 3   # 2-bit values
+
+# Page byte format (one page = one 128-token block of one KV head).
+K_CODES_BYTES = BLOCK * HEAD_DIM // 2      # 8192: token-major, two channels per byte
+V_CODES_BYTES = BLOCK * HEAD_DIM // 4      # 4096: channel-major, four tokens per byte
+K_PAGE_BYTES = K_CODES_BYTES + 2 * 256 + 2 * 512   # 9728
+V_PAGE_BYTES = V_CODES_BYTES + 2 * 256 + 2 * 512   # 5632
+
+
+# --------------------------------------------------------------------------
+# Stage 2: rotation (blog post, "KVarN Nasıl Çalışır?", rotated-cache stage)
+# --------------------------------------------------------------------------
+def hadamard(n: int = HEAD_DIM) -> np.ndarray:
+    """Orthonormal Sylvester Hadamard matrix, entry (j, k) = (-1)^popcount(j & k) / sqrt(n)."""
+    h = np.empty((n, n), dtype=np.float64)
+    for j in range(n):
+        for k in range(n):
+            h[j, k] = -1.0 if bin(j & k).count("1") % 2 else 1.0
+    return h / np.sqrt(n)
+
+
+_H = hadamard()
+
+
+def rotate(x: np.ndarray) -> np.ndarray:
+    """Rotate every token row of a [tokens, 128] block along channels: R[t] = H @ x[t]."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ _H.T
+
+
+# --------------------------------------------------------------------------
+# Stage 3: log-space row/column variance normalisation
+# (blog post, "KVarN Nasıl Çalışır?", normalised-cache stage)
+# --------------------------------------------------------------------------
+def normalize(r: np.ndarray, iters: int = ITERS, eps: float = EPS):
+    """Return log2 normalisers (rho per token row, gamma per channel column), fp64.
+
+    The normalised block is N[t, j] = R[t, j] * 2^-(rho[t] + gamma[j]).  Each
+    iteration: for every row, add half the log2 of (row variance + eps) to rho;
+    then for every column, add half the log2 of (column variance + eps) to
+    gamma, each variance taken of the current normalised block.
+    """
+    r = np.asarray(r, dtype=np.float64)
+    rho = np.zeros(r.shape[0])
+    gam = np.zeros(r.shape[1])
+    for _ in range(iters):
+        y = r * np.exp2(-(rho[:, None] + gam[None, :]))
+        rho = rho + 0.5 * np.log2(y.var(axis=1) + eps)
+        y = r * np.exp2(-(rho[:, None] + gam[None, :]))
+        gam = gam + 0.5 * np.log2(y.var(axis=0) + eps)
+    return rho, gam
+
+
+def normalized(r: np.ndarray, rho32: np.ndarray, gam32: np.ndarray) -> np.ndarray:
+    """N = R * 2^-(rho + gamma) from the stored fp32 normalisers, in fp64."""
+    rho = np.asarray(rho32, dtype=np.float32).astype(np.float64)
+    gam = np.asarray(gam32, dtype=np.float32).astype(np.float64)
+    return np.asarray(r, dtype=np.float64) * np.exp2(-(rho[:, None] + gam[None, :]))
+
+
+# --------------------------------------------------------------------------
+# Stage 4: asymmetric round-to-nearest
+# (blog post, "KVarN Nasıl Çalışır?", quantised-cache stage: 4-bit keys, 2-bit
+# values; "Pratik Çıkarımlar": group size 128)
+# --------------------------------------------------------------------------
+def rtn_group(values: np.ndarray, levels: int):
+    """Quantise one group of normalised values.  Returns (codes uint8, scale fp16, zero fp16).
+
+    The decision is taken in fp32: the group minimum and maximum of the fp32
+    values give scale = fp16(fp32(fp32(max - min) / levels)) and zero =
+    fp16(min); each code is round-half-even of fp32(fp32(v - zero) / scale),
+    clamped to [0, levels].  A zero scale gives all-zero codes.
+    """
+    v = np.asarray(values, dtype=np.float32)
+    mn = v.min()
+    mx = v.max()
+    s32 = np.float32(np.float32(mx - mn) / np.float32(levels))
+    s16 = np.float16(s32)
+    z16 = np.float16(mn)
+    if float(s16) == 0.0:
+        return np.zeros(v.shape, dtype=np.uint8), s16, z16
+    u = (v - np.float32(z16)).astype(np.float32) / np.float32(s16)
+    u = u.astype(np.float32)
+    q = np.clip(np.rint(u), 0, levels)
+    return q.astype(np.uint8), s16, z16
+
+
+def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS) -> dict:
+    """Quantise one fp16 block [128 tokens, 128 channels] of K (is_v False) or V.
+
+    Returns the stored fields: codes [128, 128] (token, channel), scale and zero
+    (fp16, per channel for K, per token for V), rho (fp32 per token) and gamma
+    (fp32 per channel).
+    """
+    x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    r = rotate(x)
+    rho, gam = normalize(r, iters, eps)
+    rho32 = rho.astype(np.float32)
+    gam32 = gam.astype(np.float32)
+    n32 = normalized(r, rho32, gam32).astype(np.float32)
+    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
+    ngroups = BLOCK if is_v else HEAD_DIM
+    scale = np.zeros(ngroups, dtype=np.float16)
+    zero = np.zeros(ngroups, dtype=np.float16)
+    for g in range(ngroups):
+        if is_v:
+            codes[g, :], scale[g], zero[g] = rtn_group(n32[g, :], V_LEVELS)
+        else:
+            codes[:, g], scale[g], zero[g] = rtn_group(n32[:, g], K_LEVELS)
+    return {"codes": codes, "scale": scale, "zero": zero, "rho": rho32, "gamma": gam32}
+
+
+def dequantize_tile(fields: dict, is_v: bool) -> np.ndarray:
+    """Rebuild a block in the original basis: N^ = s*q + z, R^ = N^ * 2^(rho+gamma), X^[t] = H @ R^[t]."""
+    q = fields["codes"].astype(np.float64)
+    s = fields["scale"].astype(np.float64)
+    z = fields["zero"].astype(np.float64)
+    if is_v:
+        n_hat = q * s[:, None] + z[:, None]
+    else:
+        n_hat = q * s[None, :] + z[None, :]
+    rho = fields["rho"].astype(np.float64)
+    gam = fields["gamma"].astype(np.float64)
+    r_hat = n_hat * np.exp2(rho[:, None] + gam[None, :])
+    # H is symmetric and its own inverse, so the inverse rotation is H again.
+    return r_hat @ _H.T
+
+
+# --------------------------------------------------------------------------
+# Page byte format (stage 4 output; the layout itself is a reading)
+# --------------------------------------------------------------------------
+def pack_k_codes(codes: np.ndarray) -> bytes:
+    """K codes [token, channel] -> 8192 bytes: byte 64*t + k = ch 2k (bits 0-3) | ch 2k+1 (bits 4-7)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8).tobytes()
+
+
+def unpack_k_codes(buf: bytes) -> np.ndarray:
+    b = np.frombuffer(bytes(buf[:K_CODES_BYTES]), dtype=np.uint8).reshape(BLOCK, HEAD_DIM // 2)
+    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
+    codes[:, 0::2] = b & 0xF
+    codes[:, 1::2] = b >> 4
+    return codes
+
+
+def pack_v_codes(codes: np.ndarray) -> bytes:
+    """V codes [token, channel] -> 4096 bytes: byte 32*c + k holds token 4k+i at bits 2i..2i+1."""
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.zeros((HEAD_DIM, BLOCK // 4), dtype=np.uint8)
+    for i in range(4):
+        out |= (c[i::4, :].T << (2 * i)).astype(np.uint8)
+    return out.tobytes()
+
+
+def unpack_v_codes(buf: bytes) -> np.ndarray:
+    b = np.frombuffer(bytes(buf[:V_CODES_BYTES]), dtype=np.uint8).reshape(HEAD_DIM, BLOCK // 4)
+    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
+    for i in range(4):
+        codes[i::4, :] = ((b >> (2 * i)) & 3).T
+    return codes
+
+
+def encode_page(fields: dict, is_v: bool) -> bytes:
+    """Page = codes | scale fp16[128] | zero fp16[128] | rho fp32[128 tokens] | gamma fp32[128 channels], little endian."""
+    codes = pack_v_codes(fields["codes"]) if is_v else pack_k_codes(fields["codes"])
+    meta = (np.asarray(fields["scale"], dtype="<f2").tobytes() + np.asarray(fields["zero"], dtype="<f2").tobytes()
+            + np.asarray(fields["rho"], dtype="<f4").tobytes() + np.asarray(fields["gamma"], dtype="<f4").tobytes())
+    return codes + meta
+
+
+def decode_page(buf: bytes, is_v: bool) -> dict:
+    buf = bytes(buf)
+    ncode = V_CODES_BYTES if is_v else K_CODES_BYTES
+    if len(buf) != ncode + 1536:
+        raise ValueError("page has %d bytes, expected %d" % (len(buf), ncode + 1536))
+    codes = unpack_v_codes(buf[:ncode]) if is_v else unpack_k_codes(buf[:ncode])
+    o = ncode
+    scale = np.frombuffer(buf[o:o + 256], dtype="<f2").copy()
+    zero = np.frombuffer(buf[o + 256:o + 512], dtype="<f2").copy()
+    rho = np.frombuffer(buf[o + 512:o + 1024], dtype="<f4").copy()
+    gam = np.frombuffer(buf[o + 1024:o + 1536], dtype="<f4").copy()
+    return {"codes": codes, "scale": scale, "zero": zero, "rho": rho, "gamma": gam}
+
+
+# --------------------------------------------------------------------------
+# Whole-call drivers (the two entry points of the path)
+# --------------------------------------------------------------------------
+def quantize_blocks(k16: np.ndarray, v16: np.ndarray, dst_pages, k_pool: np.ndarray, v_pool: np.ndarray) -> None:
+    """k16, v16: fp16 [n_blocks*128, Hkv, 128]; block b of head h goes to page dst_pages[b] of each pool.
+
+    Pools are uint8 arrays [num_pages, Hkv, page_bytes], written in place.
+    """
+    n_tok, hkv, _ = k16.shape
+    for b in range(n_tok // BLOCK):
+        p = int(dst_pages[b])
+        for h in range(hkv):
+            sl = slice(BLOCK * b, BLOCK * (b + 1))
+            k_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(k16[sl, h, :], False), False), np.uint8)
+            v_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(v16[sl, h, :], True), True), np.uint8)
+
+
+def dequantize_pages(pool: np.ndarray, pages, head: int, is_v: bool) -> np.ndarray:
+    """Concatenate dequantised blocks of one KV head over a page list -> [len(pages)*128, 128] fp64."""
+    if len(pages) == 0:
+        return np.zeros((0, HEAD_DIM))
+    return np.concatenate([dequantize_tile(decode_page(pool[int(p), head].tobytes(), is_v), is_v) for p in pages])
+
+
+def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float) -> np.ndarray:
+    """out = softmax(scale * K^ q) V^ for one query vector (fp64, max-subtracted)."""
+    if k_hat.shape[0] == 0:
+        return np.zeros(HEAD_DIM)
+    logits = scale * (k_hat @ np.asarray(q, dtype=np.float64))
+    w = np.exp(logits - logits.max())
+    return (w / w.sum()) @ v_hat
+
+
+def decode(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray,
+           seq_lens: np.ndarray, num_kv_heads: int, softmax_scale: float = 0.0, seqs=None, heads=None) -> np.ndarray:
+    """Decode attention of q [B, Hq, 128] over the packed cache -> fp64 [B, Hq, 128].
+
+    Sequence b attends to pages block_table[b, :seq_lens[b] // 128]; query head
+    h reads KV head h // (Hq // Hkv).  ``seqs`` / ``heads`` restrict the work to
+    a sample (other rows stay NaN).
+    """
+    bsz, hq, _ = q16.shape
+    group = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
+    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    for b in (range(bsz) if seqs is None else seqs):
+        pages = block_table[b, : int(seq_lens[b]) // BLOCK]
+        hs = range(hq) if heads is None else heads
+        cache = {}
+        for h in hs:
+            g = h // group
+            if g not in cache:
+                cache[g] = (dequantize_pages(k_pool, pages, g, False), dequantize_pages(v_pool, pages, g, True))
+            out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
+    return out

@@ -1,0 +1,407 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+Every test here checks the oracle against something other than itself: a
+closed form, an independent construction, a library routine, brute force on a
+tiny input, or a figure printed on the pages (tests/golden/page_figures.txt).
+They run on the CPU only.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import kvarn_oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.txt")
+
+
+def golden():
+    vals = {}
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(None, 1)
+            vals[k] = v
+    return vals
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def fp16_block(seed=0, outliers=4, mult=20.0):
+    r = rng(seed)
+    x = r.standard_normal((128, 128))
+    if outliers:
+        x[:, r.choice(128, outliers, replace=False)] *= mult
+    return x.astype(np.float16)
+
+
+# ----------------------------------------------------------------- rotation
+def test_hadamard_equals_sylvester_recursion():
+    h = np.array([[1.0]])
+    while h.shape[0] < 128:
+        h = np.block([[h, h], [h, -h]])
+    assert np.array_equal(o.hadamard() * np.sqrt(128), h)
+
+
+def test_hadamard_equals_scipy():
+    assert np.allclose(o.hadamard(), scipy.linalg.hadamard(128) / np.sqrt(128), rtol=0, atol=1e-15)
+
+
+def test_hadamard_orthonormal_symmetric_involution():
+    h = o.hadamard()
+    assert np.array_equal(h, h.T)
+    assert np.abs(h @ h.T - np.eye(128)).max() < 1e-14
+    assert np.all(np.abs(np.abs(h) - 2.0 ** -3.5) < 1e-16)
+
+
+def test_rotate_acts_along_channels_of_each_token():
+    x = np.zeros((128, 128))
+    x[5, 3] = 1.0
+    r = o.rotate(x)
+    assert np.count_nonzero(np.abs(r).sum(axis=1)) == 1  # only token 5 is touched
+    # a unit impulse at channel 3 maps to column 3 of H: sign (-1)^popcount(j & 3)
+    expect = np.array([(-1.0) ** bin(j & 3).count("1") for j in range(128)]) / np.sqrt(128)
+    assert np.allclose(r[5], expect, atol=1e-15)
+
+
+def test_rotate_constant_row_and_parseval():
+    x = np.full((1, 128), 0.75)
+    r = o.rotate(x)
+    e0 = np.zeros(128)
+    e0[0] = np.sqrt(128) * 0.75
+    assert np.allclose(r[0], e0, atol=1e-13)
+    y = rng(1).standard_normal((128, 128))
+    assert np.allclose(np.linalg.norm(o.rotate(y), axis=1), np.linalg.norm(y, axis=1), rtol=1e-13)
+
+
+def test_joint_rotation_preserves_scores_fp32():
+    # The rotation is orthonormal, so attention scores are unchanged (rotated-cache stage).
+    r = rng(2)
+    q = r.standard_normal((64, 128))
+    k = r.standard_normal((64, 128)) * np.where(r.random(128) < 0.05, 30.0, 1.0)
+    qr = o.rotate(q).astype(np.float32)
+    kr = o.rotate(k).astype(np.float32)
+    s_rot = np.einsum("ij,ij->i", qr, kr, dtype=np.float32)
+    s_ref = np.einsum("ij,ij->i", q, k)
+    assert np.all(np.abs(s_rot - s_ref) <= 1e-5 * np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1))
+
+
+# ------------------------------------------------------------ normalisation
+def brute_normalize(r, iters, eps):
+    """Loop-by-loop textbook version on a small matrix (independent of numpy.var)."""
+    nr, nc = len(r), len(r[0])
+    rho = [0.0] * nr
+    gam = [0.0] * nc
+    for _ in range(iters):
+        for t in range(nr):
+            ys = [r[t][j] * 2.0 ** (-(rho[t] + gam[j])) for j in range(nc)]
+            m = sum(ys) / nc
+            v = sum((y - m) ** 2 for y in ys) / nc
+            rho[t] += 0.5 * np.log2(v + eps)
+        for j in range(nc):
+            ys = [r[t][j] * 2.0 ** (-(rho[t] + gam[j])) for t in range(nr)]
+            m = sum(ys) / nr
+            v = sum((y - m) ** 2 for y in ys) / nr
+            gam[j] += 0.5 * np.log2(v + eps)
+    return np.array(rho), np.array(gam)
+
+
+@pytest.mark.parametrize("shape,iters", [((6, 5), 1), ((8, 8), 4), ((3, 7), 3)])
+def test_normalize_matches_brute_force(shape, iters):
+    r = rng(3).standard_normal(shape) * rng(4).lognormal(0, 1, shape)
+    rho, gam = o.normalize(r, iters, 1e-6)
+    rb, gb = brute_normalize(r.tolist(), iters, 1e-6)
+    assert np.allclose(rho, rb, atol=1e-12) and np.allclose(gam, gb, atol=1e-12)
+
+
+def test_final_column_pass_gives_unit_column_variance():
+    r = o.rotate(fp16_block(5).astype(np.float64))
+    rho, gam = o.normalize(r)
+    n = r * np.exp2(-(rho[:, None] + gam[None, :]))
+    v = n.var(axis=0)
+    assert np.all(np.abs(v - 1.0) < 1e-5)
+    # columns are equalised last, so rows are only approximately unit variance
+    assert np.abs(np.log2(n.var(axis=1))).max() < 0.5
+
+
+def test_rows_are_normalised_before_columns():
+    # With one iteration the column pass runs last, so columns are exact and rows are not.
+    r = rng(6).standard_normal((128, 128)) * rng(7).lognormal(0, 1.0, (128, 1)) * rng(8).lognormal(0, 1.0, (1, 128))
+    rho, gam = o.normalize(r, 1)
+    n = r * np.exp2(-(rho[:, None] + gam[None, :]))
+    # closed form of the last (column) pass: variance v becomes v / (v + eps)
+    v_before = (r * np.exp2(-rho[:, None])).var(axis=0)
+    assert np.allclose(n.var(axis=0), v_before / (v_before + 1e-6), rtol=1e-12)
+    # and the row pass ran first on the raw rows: rho = log2(row variance + eps) / 2
+    assert np.allclose(rho, 0.5 * np.log2(r.var(axis=1) + 1e-6), rtol=0, atol=1e-12)
+    assert np.abs(n.var(axis=1) - 1).max() > 1e-2
+
+
+def test_sinkhorn_fixed_point_with_many_iterations():
+    r = o.rotate(fp16_block(9).astype(np.float64)) * rng(10).lognormal(0, 1.0, (128, 1))
+    rho, gam = o.normalize(r, 60)
+    n = r * np.exp2(-(rho[:, None] + gam[None, :]))
+    rho1, gam1 = o.normalize(r, 61)
+    n1 = r * np.exp2(-(rho1[:, None] + gam1[None, :]))
+    # the alternating passes reach a fixed point of the normalised block: columns at unit
+    # variance, every row at one common variance (centred variances of rows and columns
+    # need not both be 1, since removing row means and column means differ)
+    assert np.abs(n1 - n).max() < 1e-9
+    assert np.abs(n.var(axis=0) - 1).max() < 1e-5
+    rv = np.log2(n.var(axis=1))
+    assert rv.max() - rv.min() < 1e-6 and abs(rv.mean()) < 0.05
+
+
+def test_row_log_variance_spread_shrinks_with_iterations():
+    r = o.rotate(fp16_block(11).astype(np.float64)) * rng(12).lognormal(0, 1.5, (128, 1))
+    spreads = []
+    for t in (0, 1, 2, 4):
+        rho, gam = o.normalize(r, t)
+        n = r * np.exp2(-(rho[:, None] + gam[None, :]))
+        spreads.append(np.log2(n.var(axis=1)).std())
+    assert spreads[0] > spreads[1] > spreads[2] > spreads[3]
+
+
+def test_zero_token_row_closed_form():
+    x = fp16_block(13).astype(np.float64)
+    x[17, :] = 0
+    r = o.rotate(x)
+    rho, _ = o.normalize(r)
+    # the zero row's variance is 0 every iteration, so rho gains log2(eps)/2 four times (log base 2)
+    assert abs(rho[17] - 2.0 * np.log2(1e-6)) < 1e-9
+    fv = o.quantize_tile(x.astype(np.float16), True)
+    assert np.all(fv["codes"][17] == 0) and fv["scale"][17] == 0
+    assert np.all(o.dequantize_tile(fv, True)[17] == 0.0)
+    fk = o.quantize_tile(x.astype(np.float16), False)
+    assert np.abs(o.dequantize_tile(fk, False)[17]).max() < 1e-9
+
+
+def test_power_of_two_token_scaling_shifts_rho():
+    x = fp16_block(14).astype(np.float64)
+    y = x.copy()
+    y[3] *= 8.0  # exact in fp16 for these magnitudes
+    assert np.array_equal(y.astype(np.float16).astype(np.float64), y)
+    fx = o.quantize_tile(x.astype(np.float16), False)
+    fy = o.quantize_tile(y.astype(np.float16), False)
+    assert abs((fy["rho"][3] - fx["rho"][3]) - 3.0) < 1e-4
+    assert np.abs(np.delete(fy["rho"] - fx["rho"], 3)).max() < 1e-4
+    assert np.mean(fy["codes"] != fx["codes"]) < 1e-3
+
+
+# ---------------------------------------------------------------- rounding
+@pytest.mark.parametrize("levels", [15, 3])
+def test_rtn_picks_nearest_grid_point(levels):
+    r = rng(15)
+    for trial in range(50):
+        v = (r.standard_normal(128) * r.lognormal(0, 1)).astype(np.float32)
+        q, s, z = o.rtn_group(v, levels)
+        s, z = float(s), float(z)
+        grid = z + s * np.arange(levels + 1)
+        for i in range(128):
+            d = np.abs(grid - float(v[i]))
+            best = d.min()
+            # the chosen level is a nearest grid point (ties within fp32 noise may go either way)
+            assert d[q[i]] <= best + 1e-6 * s
+        assert q.min() == 0 and q.max() == levels
+        assert q[np.argmin(v)] == 0 and q[np.argmax(v)] == levels
+
+
+@pytest.mark.parametrize("levels", [15, 3])
+def test_rtn_scale_zero_and_error_bound(levels):
+    r = rng(16)
+    for trial in range(50):
+        v = (r.standard_normal(128) * 3.0).astype(np.float32)
+        q, s, z = o.rtn_group(v, levels)
+        mn, mx = float(v.min()), float(v.max())
+        assert abs(float(z) - mn) <= 2.0 ** -11 * abs(mn)           # fp16 rounding of the minimum
+        assert abs(float(s) - (mx - mn) / levels) <= 2.0 ** -11 * (mx - mn) / levels * 1.01
+        err = np.abs(float(s) * q + float(z) - v.astype(np.float64))
+        slack = abs(float(z) - mn) + levels * abs(float(s) - (mx - mn) / levels)
+        assert err.max() <= float(s) / 2 * (1 + 1e-5) + slack
+        assert q.dtype == np.uint8 and q.max() <= levels
+
+
+def test_rtn_constant_group_is_degenerate():
+    v = np.full(128, 1.2345, dtype=np.float32)
+    q, s, z = o.rtn_group(v, 15)
+    assert float(s) == 0.0 and np.all(q == 0) and float(z) == float(np.float16(1.2345))
+
+
+def test_group_axes_key_per_channel_value_per_token():
+    x = fp16_block(17)
+    fk = o.quantize_tile(x, False)
+    fv = o.quantize_tile(x, True)
+    # every K group is a channel column: its min maps to 0 and its max to 15
+    assert np.all(fk["codes"].min(axis=0) == 0) and np.all(fk["codes"].max(axis=0) == 15)
+    # every V group is a token row: its min maps to 0 and its max to 3
+    assert np.all(fv["codes"].min(axis=1) == 0) and np.all(fv["codes"].max(axis=1) == 3)
+    assert fk["codes"].max() <= 15 and fv["codes"].max() <= 3
+
+
+def test_constant_in_time_block_gives_zero_key_scales():
+    row = rng(18).standard_normal(128).astype(np.float16)
+    x = np.tile(row, (128, 1))
+    fk = o.quantize_tile(x, False)
+    assert np.all(fk["scale"] == 0) and np.all(fk["codes"] == 0)
+    xh = o.dequantize_tile(fk, False)
+    # only the fp16 rounding of the stored zero remains
+    assert np.abs(xh - x.astype(np.float64)).max() <= 2.0 ** -10 * np.abs(x).max() * 4
+
+
+# ----------------------------------------------------------------- packing
+def test_k_pack_roundtrip_every_byte_value():
+    b = np.arange(8192, dtype=np.int64) * 7 % 256
+    buf = b.astype(np.uint8).tobytes()
+    assert o.pack_k_codes(o.unpack_k_codes(buf)) == buf
+    codes = rng(19).integers(0, 16, (128, 128)).astype(np.uint8)
+    assert np.array_equal(o.unpack_k_codes(o.pack_k_codes(codes)), codes)
+
+
+def test_v_pack_roundtrip_every_byte_value():
+    b = np.arange(4096, dtype=np.int64) * 11 % 256
+    buf = b.astype(np.uint8).tobytes()
+    assert o.pack_v_codes(o.unpack_v_codes(buf)) == buf
+    codes = rng(20).integers(0, 4, (128, 128)).astype(np.uint8)
+    assert np.array_equal(o.unpack_v_codes(o.pack_v_codes(codes)), codes)
+
+
+@pytest.mark.parametrize("t,c", [(0, 0), (0, 1), (5, 64), (127, 127), (33, 2)])
+def test_single_code_bit_positions(t, c):
+    ck = np.zeros((128, 128), np.uint8)
+    ck[t, c] = 9
+    bk = np.frombuffer(o.pack_k_codes(ck), np.uint8)
+    assert np.flatnonzero(bk).tolist() == [64 * t + c // 2]
+    assert bk[64 * t + c // 2] == 9 << (4 * (c % 2))
+    cv = np.zeros((128, 128), np.uint8)
+    cv[t, c] = 2
+    bv = np.frombuffer(o.pack_v_codes(cv), np.uint8)
+    assert np.flatnonzero(bv).tolist() == [32 * c + t // 4]
+    assert bv[32 * c + t // 4] == 2 << (2 * (t % 4))
+
+
+def test_page_roundtrip_and_sizes():
+    x = fp16_block(21)
+    for is_v, size in ((False, 9728), (True, 5632)):
+        f = o.quantize_tile(x, is_v)
+        pg = o.encode_page(f, is_v)
+        assert len(pg) == size
+        g = o.decode_page(pg, is_v)
+        for k in f:
+            assert np.array_equal(np.asarray(f[k]), np.asarray(g[k]))
+
+
+# ------------------------------------------------------------- dequantise
+def test_dequantize_closed_form():
+    f = {"codes": np.zeros((128, 128), np.uint8), "scale": np.zeros(128, np.float16),
+         "zero": np.ones(128, np.float16), "rho": np.zeros(128, np.float32), "gamma": np.zeros(128, np.float32)}
+    f["rho"][7] = 1.0
+    xh = o.dequantize_tile(f, False)
+    expect = np.zeros((128, 128))
+    expect[:, 0] = np.sqrt(128)
+    expect[7, 0] = 2 * np.sqrt(128)
+    assert np.allclose(xh, expect, atol=1e-12)
+
+
+def test_kvarn_beats_plain_rtn_on_outlier_keys():
+    # The rotation and normalisation exist to cut the quantisation error (normalised-cache stage).
+    x = fp16_block(22, outliers=4, mult=20.0)
+    xd = x.astype(np.float64)
+    err_kvarn = np.linalg.norm(o.dequantize_tile(o.quantize_tile(x, False), False) - xd)
+    plain = np.zeros_like(xd)
+    for j in range(128):
+        q, s, z = o.rtn_group(xd[:, j].astype(np.float32), 15)
+        plain[:, j] = q * float(s) + float(z)
+    err_plain = np.linalg.norm(plain - xd)
+    assert err_kvarn < err_plain
+    assert err_kvarn / np.linalg.norm(xd) < 0.12
+
+
+# --------------------------------------------------------------- attention
+def small_cache(seed, nblocks, hkv, perm=None):
+    r = rng(seed)
+    k = (r.standard_normal((nblocks * 128, hkv, 128))).astype(np.float16)
+    v = (r.standard_normal((nblocks * 128, hkv, 128))).astype(np.float16)
+    pages = np.arange(nblocks) if perm is None else np.asarray(perm)
+    kp = np.zeros((nblocks, hkv, 9728), np.uint8)
+    vp = np.zeros((nblocks, hkv, 5632), np.uint8)
+    o.quantize_blocks(k, v, pages, kp, vp)
+    return k, v, kp, vp, pages
+
+
+def test_zero_query_gives_mean_of_values():
+    _, _, kp, vp, pages = small_cache(23, 2, 1)
+    q = np.zeros((1, 1, 128), np.float16)
+    out = o.decode(q, kp, vp, pages[None, :], np.array([256]), 1)
+    vh = o.dequantize_pages(vp, pages, 0, True)
+    assert np.allclose(out[0, 0], vh.mean(axis=0), atol=1e-12)
+
+
+def test_aligned_query_selects_one_value_row():
+    _, _, kp, vp, pages = small_cache(24, 1, 1)
+    kh = o.dequantize_pages(kp, pages, 0, False)
+    vh = o.dequantize_pages(vp, pages, 0, True)
+    q = (kh[40] / np.linalg.norm(kh[40]) * 200.0).astype(np.float16)[None, None, :]
+    out = o.decode(q, kp, vp, pages[None, :], np.array([128]), 1, softmax_scale=1.0)
+    assert np.allclose(out[0, 0], vh[40], atol=1e-6)
+
+
+def test_gqa_head_mapping_and_sdpa():
+    _, _, kp, vp, pages = small_cache(25, 3, 2)
+    q = rng(26).standard_normal((1, 6, 128)).astype(np.float16)
+    out = o.decode(q, kp, vp, pages[None, :], np.array([384]), 2)
+    for h in range(6):
+        g = h // 3
+        kh = torch.from_numpy(o.dequantize_pages(kp, pages, g, False))
+        vh = torch.from_numpy(o.dequantize_pages(vp, pages, g, True))
+        qq = torch.from_numpy(q[0, h].astype(np.float64))
+        ref = torch.nn.functional.scaled_dot_product_attention(qq[None, None, None], kh[None, None], vh[None, None])
+        assert np.allclose(out[0, h], ref[0, 0, 0].numpy(), atol=1e-10)
+
+
+def test_page_permutation_invariance():
+    perm = [2, 0, 3, 1]
+    k, v, kp, vp, pages = small_cache(27, 4, 1)
+    kp2 = np.zeros_like(kp)
+    vp2 = np.zeros_like(vp)
+    o.quantize_blocks(k, v, perm, kp2, vp2)
+    q = rng(28).standard_normal((1, 2, 128)).astype(np.float16)
+    a = o.decode(q, kp, vp, np.arange(4)[None, :], np.array([512]), 1)
+    b = o.decode(q, kp2, vp2, np.array(perm)[None, :], np.array([512]), 1)
+    assert np.array_equal(a, b)
+
+
+def test_empty_sequence_gives_zero_output():
+    _, _, kp, vp, pages = small_cache(29, 1, 1)
+    q = rng(30).standard_normal((2, 1, 128)).astype(np.float16)
+    out = o.decode(q, kp, vp, np.array([[0], [0]]), np.array([0, 128]), 1)
+    assert np.all(out[0, 0] == 0) and np.all(np.isfinite(out[1, 0]))
+
+
+# ------------------------------------------------------- page figures (golden)
+def test_format_capacity_inside_published_range():
+    g = golden()
+    ratio = (2 * 128 * 128 * 2) / (o.K_PAGE_BYTES + o.V_PAGE_BYTES)
+    assert float(g["capacity_ratio_vs_fp16_min"]) <= ratio <= float(g["capacity_ratio_vs_fp16_max"])
+    assert g["format_name"] == "kvarn_k4v2_g128"
+    assert int(g["key_bits"]) == 4 and int(g["value_bits"]) == 2 and int(g["group_size"]) == 128
+    # the page sizes follow from the bit widths: codes plus 2 fp16 and 2 fp32 vectors of 128
+    assert o.K_PAGE_BYTES == 128 * 128 * int(g["key_bits"]) // 8 + 1536
+    assert o.V_PAGE_BYTES == 128 * 128 * int(g["value_bits"]) // 8 + 1536
+
+
+def test_page_metadata_offsets():
+    f = {"codes": np.zeros((128, 128), np.uint8), "scale": np.full(128, 1.0, np.float16),
+         "zero": np.full(128, 2.0, np.float16), "rho": np.full(128, 0.5, np.float32),
+         "gamma": np.full(128, -1.0, np.float32)}
+    for is_v, base in ((False, 8192), (True, 4096)):
+        pg = np.frombuffer(o.encode_page(f, is_v), np.uint8)
+        assert pg[base:base + 2].tolist() == [0x00, 0x3C]            # fp16 1.0, little endian
+        assert pg[base + 256:base + 258].tolist() == [0x00, 0x40]    # fp16 2.0
+        assert pg[base + 512:base + 516].tolist() == [0, 0, 0, 0x3F]  # fp32 0.5
+        assert pg[base + 1024:base + 1028].tolist() == [0, 0, 0x80, 0xBF]  # fp32 -1.0
