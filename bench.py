@@ -1,0 +1,253 @@
+"""Benchmark of the KVarN hot path on one MI355X: quantize + packed decode attention.
+
+One step = one pass of the whole path over one batch of synthetic input:
+quantise every 128-token block of K and V of the workload into packed pages,
+then one decode-attention step of every sequence over the packed cache.  The
+default workload is one Llama-3-8B-shaped layer (16 sequences x 8192 tokens,
+32 query / 8 KV heads, head_dim 128).  Inputs are resident in HBM before the
+timed region starts.
+
+Prints one JSON line (rank 0).  Throughput is algorithmic bytes / time:
+  quantize: 65536 B of fp16 in + 15360 B of pages out per (block, KV head)
+  decode:   15360 B of pages per attended (block, KV head) + q, out, table
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3_8b_layer_16x8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
+    return ap.parse_args()
+
+
+class Case:
+    """Device buffers and the two launches of one workload."""
+
+    def __init__(self, K, w, cfg):
+        import torch
+        from kv_cache_quantization_kvarn_amd import synth
+        self.K, self.w, self.cfg = K, w, cfg
+        pm = synth.make_page_map(w)
+        self.pm = pm
+        n_prefix = synth.total_prefix_blocks(w)
+        self.layers = []
+        for layer in range(w.layers):
+            if w.append_blocks:
+                # paged mixed: the prefix is filled once outside the timed region; a step
+                # quantises the appended block of every sequence and decodes over prefix + append
+                k, v = synth.layer_kv(w, layer, n_prefix * 128, "cuda")
+                ka, va = synth.layer_kv(w, layer, w.batch * 128, "cuda", append=True)
+                kp, vp = K.alloc_pools(cfg, pm.num_pages, w.hkv)
+                K.kvarn_quantize_blocks(cfg, k, v, pm.prefix_pages.cuda(), kp, vp)
+                del k, v
+                qk, qv, dst = ka, va, pm.append_pages.cuda()
+            else:
+                qk, qv = synth.layer_kv(w, layer, n_prefix * 128, "cuda")
+                kp, vp = K.alloc_pools(cfg, pm.num_pages, w.hkv)
+                dst = pm.prefix_pages.cuda()
+            q = synth.make_q(w, layer, "cuda")
+            self.layers.append(dict(k=qk, v=qv, dst=dst, kp=kp, vp=vp, q=q))
+        self.bt = pm.block_table.cuda()
+        self.sl = pm.seq_lens.cuda()
+        self.ws = K.alloc_workspace(cfg, w.batch, w.hq, w.hkv, pm.block_table.shape[1])
+        self.out = torch.empty(w.batch, w.hq, 128, dtype=torch.float32, device="cuda")
+        self.flags = torch.zeros(1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        from kv_cache_quantization_kvarn_amd import accounting as acc
+        kb, vb = K.kvarn_page_bytes(cfg, False), K.kvarn_page_bytes(cfg, True)
+        qblocks = self.layers[0]["dst"].numel()
+        attended = int(pm.seq_lens.sum().item()) // 128
+        self.q_bytes = acc.quantize_bytes(qblocks, w.hkv, kb, vb) * w.layers
+        self.d_bytes = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb) * w.layers
+        self.q_bytes_launch = acc.quantize_bytes(qblocks, w.hkv, kb, vb)
+        self.d_bytes_launch = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb)
+        self.q_tokens = qblocks * 128 * w.layers
+        self.ctx_tokens = attended * 128
+
+    def quantize(self, L):
+        self.K.kvarn_quantize_blocks(self.cfg, L["k"], L["v"], L["dst"], L["kp"], L["vp"], self.flags)
+
+    def decode(self, L):
+        self.K.kvarn_decode_attention(self.cfg, L["q"], L["kp"], L["vp"], self.bt, self.sl, self.w.hkv, self.out,
+                                      self.ws, dev_flags=self.flags)
+
+
+def cpu_baseline(w, seconds):
+    """The oracle on a bounded sample of the same workload, single thread, in the same GB/s units."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_quantization_kvarn_amd import synth
+    from oracle import kvarn_oracle as o
+
+    torch.set_num_threads(1)
+    k, v = synth.layer_kv(w, 0, 4 * 128, "cpu")
+    kh, vh = k.numpy(), v.numpy()
+    pm = synth.make_page_map(w)
+    nb_seq = int(pm.seq_lens[0]) // 128
+    with threadpool_limits(limits=1):
+        # quantize: (block, KV head) pairs, K and V tiles each
+        t0 = time.perf_counter()
+        nq = 0
+        while time.perf_counter() - t0 < seconds / 2 or nq < 4:
+            b, h = nq % 4, (nq // 4) % w.hkv
+            sl = slice(128 * b, 128 * b + 128)
+            o.encode_page(o.quantize_tile(kh[sl, h], False), False)
+            o.encode_page(o.quantize_tile(vh[sl, h], True), True)
+            nq += 1
+        tq = time.perf_counter() - t0
+        # decode: every query head of one KV head of one sequence over its blocks
+        kp = np.zeros((4, 1, o.K_PAGE_BYTES), np.uint8)
+        vp = np.zeros((4, 1, o.V_PAGE_BYTES), np.uint8)
+        o.quantize_blocks(kh[:, :1], vh[:, :1], np.arange(4), kp, vp)
+        blocks = np.arange(nb_seq) % 4  # the sequence's length, pages recycled from the sample
+        q = np.random.default_rng(0).standard_normal((1, w.gqa, 128)).astype(np.float16)
+        t0 = time.perf_counter()
+        nd = 0
+        while time.perf_counter() - t0 < seconds / 2 or nd < 1:
+            o.decode(q, kp, vp, blocks[None, :], np.array([nb_seq * 128]), 1)
+            nd += 1
+        td = time.perf_counter() - t0
+    q_bytes = nq * (65536 + 15360)
+    d_bytes = nd * (nb_seq * 15360 + w.gqa * 768 + nb_seq * 4)
+    return {
+        "value": round((q_bytes + d_bytes) / (tq + td) / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("%d (block, KV head) pairs quantized (K and V tiles) + %d decode(s) of %d query heads over one "
+                   "%d-block sequence of one KV head; fp64 numpy oracle, 1 thread" % (nq, nd, w.gqa, nb_seq)),
+        "quantize_gbps": round(q_bytes / tq / 1e9, 6),
+        "decode_gbps": round(d_bytes / td / 1e9, 6),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("this build measures one GPU only; --gpus %d is not supported (run with --gpus 1)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from kv_cache_quantization_kvarn_amd import accounting as acc
+    from kv_cache_quantization_kvarn_amd import kvarn as K
+    from kv_cache_quantization_kvarn_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
+    case = Case(K, w, cfg)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li, L in enumerate(case.layers):
+            if events is not None:
+                events[li][0].record(stream)
+            case.quantize(L)
+            if events is not None:
+                events[li][1].record(stream)
+        for li, L in enumerate(case.layers):
+            if events is not None:
+                events[li][2].record(stream)
+            case.decode(L)
+            if events is not None:
+                events[li][3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in case.layers] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert K.kvarn_read_flags(case.flags) == 0, "device flags set during the benchmark"
+    q_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    d_ms = [e[2].elapsed_time(e[3]) for st in evs for e in st]
+    q_avg_s = sum(q_ms) / len(q_ms) / 1e3
+    d_avg_s = sum(d_ms) / len(d_ms) / 1e3
+
+    # decode alone after writing 512 MB (flushes the 256 MB last-level cache), timed per launch
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    df_ms = []
+    L0 = case.layers[0]
+    for _ in range(args.flush_reps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        case.decode(L0)
+        b.record(stream)
+        b.synchronize()
+        df_ms.append(a.elapsed_time(b))
+    df_ms.sort()
+    d_flush_s = df_ms[len(df_ms) // 2] / 1e3
+
+    step_bytes = case.q_bytes + case.d_bytes
+    ms_per_step = elapsed / args.steps * 1e3
+    value = step_bytes / (elapsed / args.steps) / 1e9
+    q_gbps = case.q_bytes_launch / q_avg_s / 1e9
+    d_gbps = case.d_bytes_launch / d_avg_s / 1e9
+    d_flush_gbps = case.d_bytes_launch / d_flush_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: K N(0,1) with outlier channels, V N(0,1) x per-token lognormal scale, q N(0,1); fp16)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len or list(w.seq_len_range),
+                   "q_heads": w.hq, "kv_heads": w.hkv, "head_dim": 128, "layers": w.layers,
+                   "format": "kvarn_k4v2_g128", "parallelism": "single GPU"},
+        "pct_hbm_peak": round(100.0 * value / acc.HBM_PEAK_GBPS, 2),
+        "quantize": {"gbps": round(q_gbps, 1), "pct_peak": round(100 * q_gbps / acc.HBM_PEAK_GBPS, 2),
+                     "us_per_launch": round(q_avg_s * 1e6, 2), "tokens_per_s": round(case.q_tokens / (q_avg_s * w.layers), 1),
+                     "bytes_per_launch": case.q_bytes_launch},
+        "decode": {"gbps": round(d_gbps, 1), "pct_peak": round(100 * d_gbps / acc.HBM_PEAK_GBPS, 2),
+                   "us_per_launch": round(d_avg_s * 1e6, 2),
+                   "tokens_per_s": round(w.batch / (d_avg_s * w.layers), 1),
+                   "context_tokens_per_s": round(case.ctx_tokens / d_avg_s, 1),
+                   "bytes_per_launch": case.d_bytes_launch,
+                   "after_cache_flush": {"gbps": round(d_flush_gbps, 1),
+                                         "pct_peak": round(100 * d_flush_gbps / acc.HBM_PEAK_GBPS, 2),
+                                         "us_median": round(d_flush_s * 1e6, 2)}},
+    }
+    # dominant kernel by time: the one whose launches take longer in the step
+    if q_avg_s >= d_avg_s:
+        dom, ach, traffic = "kvarn quantize_kernel", q_gbps, None
+    else:
+        dom, ach, traffic = "kvarn decode_kernel", d_gbps, None
+    line["roofline"] = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": acc.HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(ach / acc.HBM_PEAK_GBPS, 4), "traffic": traffic}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * libkvarn: KVarN KV-cache block quantisation and decode attention over the
+ * packed, paged cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Method: the KVarN blog post ("KVarN: Huawei'den KV-Cache Kuantizasyonu için
+ * Yerel vLLM Backend'i"), section "KVarN Nasıl Çalışır?": the KV cache is
+ * quantised in fixed-size token blocks, each block passing through a Hadamard
+ * rotation along channels, a log-space row/column variance normalisation and
+ * low-bit asymmetric round-to-nearest (4-bit keys, 2-bit values); section
+ * "Pratik Çıkarımlar" names the format "kvarn_k4v2_g128".  Paged storage
+ * with a block table and GQA heads: the "KV Cache" glossary page, sections
+ * "Boyutu ve Yönetimi" and "Türleri".
+ *
+ * Conventions for every call:
+ *   - All tensor arguments are device pointers owned by the caller; the library
+ *     never allocates, frees or synchronises (except kvarn_read_flags).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously.  Calls are re-entrant; two calls that write the
+ *     same pages or the same workspace must not overlap.
+ *   - The return value reports host-side validation and launch errors only.
+ *     Problems that only the device can see (a page id outside [0, num_pages),
+ *     a bad sequence length) set bits in the optional `dev_flags` word (device
+ *     memory, OR-ed atomically) and the offending unit of work is skipped.
+ *   - Shapes: tokens of a 128-token block are consecutive rows; head_dim is 128.
+ *   - No exceptions cross this boundary; kvarn_last_error() describes the last
+ *     failure of the calling thread.
+ */
+#ifndef KVARN_H
+#define KVARN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVARN_OK = 0,
+  KVARN_ERR_NULL = -1,        /* a required pointer is NULL */
+  KVARN_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
+  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k4v2_g128 / head_dim 128 / block 128 */
+  KVARN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  KVARN_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
+} kvarn_status;
+
+/* Device-side flag bits written to *dev_flags. */
+#define KVARN_FLAG_BAD_PAGE 1u    /* a page id outside [0, num_pages): that block is skipped */
+#define KVARN_FLAG_BAD_SEQLEN 2u  /* seq_len < 0, not a multiple of 128, or above max_blocks*128: sequence output is 0 */
+
+/* Format parameters.  Only the values of "kvarn_k4v2_g128" are supported:
+ * head_dim 128, block_tokens 128, k_bits 4, v_bits 2, group_size 128,
+ * norm_iters 4, eps 1e-6. */
+typedef struct {
+  int32_t head_dim;
+  int32_t block_tokens;
+  int32_t k_bits;
+  int32_t v_bits;
+  int32_t group_size;
+  int32_t norm_iters;
+  float eps;
+} kvarn_config;
+
+/* Fill *out from a cache dtype name of the form "kvarn_k<K>v<V>_g<G>"
+ * (blog post, section "Pratik Çıkarımlar").  Parses any such name; names other
+ * than "kvarn_k4v2_g128" parse but return KVARN_ERR_UNSUPPORTED. */
+kvarn_status kvarn_config_parse(const char* name, kvarn_config* out);
+
+/* Bytes of one page (one 128-token block of one KV head): 9728 for K
+ * (is_v = 0), 5632 for V (is_v = 1); 0 for an unsupported config.
+ *
+ * K page: [0, 8192) codes, token-major: byte 64*t + k holds channel 2k in bits
+ *         0-3 and channel 2k+1 in bits 4-7 of token t;
+ *         [8192, 8448) scale fp16[128 channels]; [8448, 8704) zero fp16[128 channels];
+ *         [8704, 9216) rho fp32[128 tokens];     [9216, 9728) gamma fp32[128 channels].
+ * V page: [0, 4096) codes, channel-major: byte 32*c + k holds token 4k+i in bits
+ *         2i..2i+1 of channel c;
+ *         [4096, 4352) scale fp16[128 tokens]; [4352, 4608) zero fp16[128 tokens];
+ *         [4608, 5120) rho fp32[128 tokens];   [5120, 5632) gamma fp32[128 channels].
+ * All little endian.  Dequantisation: x^[t] = H (N^ * 2^(rho[t] + gamma)), with
+ * N^ = scale * code + zero and H the orthonormal Sylvester Hadamard matrix. */
+size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v);
+
+/* Quantise n_blocks 128-token blocks of K and V (blog post, "KVarN Nasıl
+ * Çalışır?": rotate, normalise, round to nearest, pack) into pages.
+ *   k, v       fp16 [n_blocks*128, num_kv_heads, 128], contiguous; block b is
+ *              rows 128b .. 128b+127.
+ *   dst_pages  int32 [n_blocks] (device): page receiving block b (all heads).
+ *              Entries must be distinct.  An entry outside [0, num_pages)
+ *              sets KVARN_FLAG_BAD_PAGE and that block is not written.
+ *   k_pool     bytes [num_pages, num_kv_heads, 9728]; v_pool bytes
+ *              [num_pages, num_kv_heads, 5632]; written in place.  The pools
+ *              must not overlap k or v.
+ *   n_blocks == 0 is a no-op returning KVARN_OK. */
+kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
+                                   int32_t num_kv_heads, const int32_t* dst_pages, void* k_pool, void* v_pool,
+                                   int32_t num_pages, uint32_t* dev_flags, void* stream);
+
+/* Rebuild fp32 K^ and V^ (original basis) from pages: block b of head h is read
+ * from page pages[b].  k_out, v_out: fp32 [n_blocks*128, num_kv_heads, 128].
+ * Either output may be NULL to skip it.  A test and inspection export; the
+ * decode path never materialises K^ or V^. */
+kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool, const void* v_pool,
+                                     int32_t num_pages, const int32_t* pages, int32_t n_blocks,
+                                     int32_t num_kv_heads, float* k_out, float* v_out, uint32_t* dev_flags,
+                                     void* stream);
+
+/* Workspace bytes kvarn_decode_attention needs for these sizes (split
+ * partials and per-(sequence, KV head) arrival counters).  The workspace
+ * must be zero-filled before its first use; every call leaves the counter
+ * region zero again, so later calls with the same or smaller sizes need no
+ * clearing. */
+size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_blocks_per_seq);
+
+/* One decode step: for every sequence b and query head h, attention of q[b, h]
+ * over the packed K/V pages of KV head h / (num_q_heads / num_kv_heads), pages
+ * block_table[b, 0 .. seq_lens[b]/128).  The query is rotated by the same
+ * Hadamard matrix, so scores equal those of the dequantised cache ("KVarN Nasıl
+ * Çalışır?": the rotation is orthonormal and keeps attention scores).
+ *   q            fp16 [batch, num_q_heads, 128]
+ *   block_table  int32 [batch, max_blocks_per_seq] (device)
+ *   seq_lens     int32 [batch] (device), multiples of 128; 0 gives a zero row
+ *   softmax_scale  <= 0 selects 1/sqrt(128)
+ *   out          fp32 [batch, num_q_heads, 128]
+ *   workspace    device bytes, at least kvarn_decode_workspace_bytes(...) */
+kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                    const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
+                                    void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
+
+/* Copy *dev_flags to *host_out after the work queued on `stream` finishes
+ * (synchronises the stream). */
+kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream);
+
+const char* kvarn_status_string(kvarn_status s);
+const char* kvarn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVARN_H */

@@ -1,0 +1,208 @@
+// C ABI of libkvarn: argument validation, launch planning and error reporting.
+// The declarations and their contracts are in include/kvarn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kvarn.h"
+
+namespace kvarn {
+hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
+                           void* k_pool, void* v_pool, int num_pages, uint32_t* flags, hipStream_t stream);
+hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
+                             int n_blocks, int hkv, float* k_out, float* v_out, uint32_t* flags, hipStream_t stream);
+hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
+                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
+                         int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
+                         uint32_t* counters, uint32_t* flags, hipStream_t stream);
+}  // namespace kvarn
+
+namespace {
+
+constexpr int kKPage = 9728;
+constexpr int kVPage = 5632;
+constexpr int kMaxGroup = 8;
+constexpr int kPartFloats = 128 + 2;
+constexpr int kMaxSplitsPerPair = 32;
+constexpr long kTargetWaves = 4096;
+
+thread_local std::string g_last_error;
+
+kvarn_status fail(kvarn_status s, const char* msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool config_ok(const kvarn_config* c) {
+  return c && c->head_dim == 128 && c->block_tokens == 128 && c->k_bits == 4 && c->v_bits == 2 &&
+         c->group_size == 128 && c->norm_iters == 4 && std::fabs(c->eps - 1e-6f) <= 1e-12f;
+}
+
+kvarn_status check_config(const kvarn_config* c) {
+  if (!c) return fail(KVARN_ERR_NULL, "config is NULL");
+  if (!config_ok(c)) return fail(KVARN_ERR_UNSUPPORTED, "only kvarn_k4v2_g128 (head_dim 128, block 128) is supported");
+  return KVARN_OK;
+}
+
+struct DecodePlan {
+  int blocks_per_split;
+  int max_splits;
+};
+
+// Pages per wave: enough waves to fill the chip, at most kMaxSplitsPerPair partials per (sequence, KV head).
+DecodePlan plan_decode(int batch, int hkv, int max_blocks) {
+  const long units = static_cast<long>(batch) * hkv * max_blocks;
+  long bps = (units + kTargetWaves - 1) / kTargetWaves;
+  const long min_bps = (max_blocks + kMaxSplitsPerPair - 1) / kMaxSplitsPerPair;
+  if (bps < min_bps) bps = min_bps;
+  if (bps < 1) bps = 1;
+  if (bps > max_blocks) bps = max_blocks > 0 ? max_blocks : 1;
+  DecodePlan p;
+  p.blocks_per_split = static_cast<int>(bps);
+  p.max_splits = static_cast<int>((max_blocks + bps - 1) / bps);
+  if (p.max_splits < 1) p.max_splits = 1;
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+size_t counter_bytes(int batch, int hkv) { return align256(static_cast<size_t>(batch) * hkv * sizeof(uint32_t)); }
+
+size_t workspace_bytes(int batch, int hkv, int max_blocks) {
+  const DecodePlan p = plan_decode(batch, hkv, max_blocks);
+  return counter_bytes(batch, hkv) +
+         static_cast<size_t>(batch) * hkv * p.max_splits * kMaxGroup * kPartFloats * sizeof(float);
+}
+
+kvarn_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return KVARN_OK;
+  g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(e);
+  return KVARN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvarn_status kvarn_config_parse(const char* name, kvarn_config* out) {
+  if (!name || !out) return fail(KVARN_ERR_NULL, "name or out is NULL");
+  int kb = 0, vb = 0, gs = 0, used = 0;
+  if (std::sscanf(name, "kvarn_k%dv%d_g%d%n", &kb, &vb, &gs, &used) != 3 || name[used] != '\0')
+    return fail(KVARN_ERR_UNSUPPORTED, "cache dtype name is not of the form kvarn_k<K>v<V>_g<G>");
+  out->head_dim = 128;
+  out->block_tokens = 128;
+  out->k_bits = kb;
+  out->v_bits = vb;
+  out->group_size = gs;
+  out->norm_iters = 4;
+  out->eps = 1e-6f;
+  if (!config_ok(out)) return fail(KVARN_ERR_UNSUPPORTED, "only kvarn_k4v2_g128 is implemented");
+  return KVARN_OK;
+}
+
+size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v) {
+  if (!config_ok(cfg)) return 0;
+  return is_v ? kVPage : kKPage;
+}
+
+kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
+                                   int32_t num_kv_heads, const int32_t* dst_pages, void* k_pool, void* v_pool,
+                                   int32_t num_pages, uint32_t* dev_flags, void* stream) {
+  kvarn_status s = check_config(cfg);
+  if (s != KVARN_OK) return s;
+  if (n_blocks < 0 || num_kv_heads <= 0 || num_pages < 0) return fail(KVARN_ERR_SHAPE, "negative or zero size");
+  if (n_blocks == 0) return KVARN_OK;
+  if (!k || !v || !dst_pages || !k_pool || !v_pool) return fail(KVARN_ERR_NULL, "a tensor pointer is NULL");
+  if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  if (static_cast<long>(n_blocks) * num_kv_heads * 2 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "too many tiles");
+  if ((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15)
+    return fail(KVARN_ERR_SHAPE, "k and v must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  return launch_status(kvarn::launch_quantize(k, v, n_blocks, num_kv_heads, dst_pages, k_pool, v_pool, num_pages,
+                                              dev_flags, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool, const void* v_pool,
+                                     int32_t num_pages, const int32_t* pages, int32_t n_blocks,
+                                     int32_t num_kv_heads, float* k_out, float* v_out, uint32_t* dev_flags,
+                                     void* stream) {
+  kvarn_status s = check_config(cfg);
+  if (s != KVARN_OK) return s;
+  if (n_blocks < 0 || num_kv_heads <= 0 || num_pages < 0) return fail(KVARN_ERR_SHAPE, "negative or zero size");
+  if (n_blocks == 0 || (!k_out && !v_out)) return KVARN_OK;
+  if (!pages || (k_out && !k_pool) || (v_out && !v_pool)) return fail(KVARN_ERR_NULL, "a tensor pointer is NULL");
+  if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, k_out, v_out,
+                                                dev_flags, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t max_blocks_per_seq) {
+  if (!config_ok(cfg) || batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq < 0) return 0;
+  if (batch == 0) return 0;
+  return workspace_bytes(batch, num_kv_heads, max_blocks_per_seq > 0 ? max_blocks_per_seq : 1);
+}
+
+kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                    const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                    int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
+                                    void* workspace, size_t ws_bytes, uint32_t* dev_flags, void* stream) {
+  kvarn_status s = check_config(cfg);
+  if (s != KVARN_OK) return s;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
+    return fail(KVARN_ERR_SHAPE, "negative or zero size");
+  if (num_q_heads % num_kv_heads != 0) return fail(KVARN_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / num_kv_heads > kMaxGroup)
+    return fail(KVARN_ERR_UNSUPPORTED, "more than 8 query heads per KV head is not supported");
+  if (batch == 0) return KVARN_OK;
+  if (!q || !seq_lens || !out) return fail(KVARN_ERR_NULL, "q, seq_lens or out is NULL");
+  if (max_blocks_per_seq > 0 && (!block_table || !k_pool || !v_pool))
+    return fail(KVARN_ERR_NULL, "block_table or a pool is NULL");
+  if (static_cast<long>(max_blocks_per_seq) * 128 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
+  if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
+  const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
+  const size_t need = workspace_bytes(batch, num_kv_heads, mb);
+  if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  const DecodePlan p = plan_decode(batch, num_kv_heads, mb);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(batch, num_kv_heads));
+  // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
+  const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
+  return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens, batch,
+                                            num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2,
+                                            out, part, counters, dev_flags, static_cast<hipStream_t>(stream)));
+}
+
+kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {
+  if (!dev_flags || !host_out) return fail(KVARN_ERR_NULL, "dev_flags or host_out is NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(host_out, dev_flags, sizeof(uint32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return launch_status(e);
+}
+
+const char* kvarn_status_string(kvarn_status s) {
+  switch (s) {
+    case KVARN_OK: return "ok";
+    case KVARN_ERR_NULL: return "null pointer";
+    case KVARN_ERR_SHAPE: return "bad shape";
+    case KVARN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVARN_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVARN_ERR_LAUNCH: return "launch failed";
+  }
+  return "unknown status";
+}
+
+const char* kvarn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

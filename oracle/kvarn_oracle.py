@@ -129,12 +129,17 @@ def rtn_group(values: np.ndarray, levels: int):
     s32 = np.float32(np.float32(mx - mn) / np.float32(levels))
     s16 = np.float16(s32)
     z16 = np.float16(mn)
+    return rtn_codes(v, s16, z16, levels), s16, z16
+
+
+def rtn_codes(values: np.ndarray, s16, z16, levels: int) -> np.ndarray:
+    """Codes of fp32 values on the stored grid z + s*c: clamp(rint(fp32(fp32(v - z) / s)), 0, levels); s == 0 gives 0."""
+    v = np.asarray(values, dtype=np.float32)
     if float(s16) == 0.0:
-        return np.zeros(v.shape, dtype=np.uint8), s16, z16
+        return np.zeros(v.shape, dtype=np.uint8)
     u = (v - np.float32(z16)).astype(np.float32) / np.float32(s16)
     u = u.astype(np.float32)
-    q = np.clip(np.rint(u), 0, levels)
-    return q.astype(np.uint8), s16, z16
+    return np.clip(np.rint(u), 0, levels).astype(np.uint8)
 
 
 def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS) -> dict:

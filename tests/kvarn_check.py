@@ -1,0 +1,90 @@
+"""Comparison of the HIP path against the CPU oracle (test infrastructure).
+
+Tolerances (from the spec parity bar and the fp32 arithmetic of the kernels):
+  * codes: mismatch fraction <= 1e-4 and every mismatch within one level;
+    near-ties decide differently because the kernel computes the normalised
+    value in fp32 in a different order than the fp64 oracle;
+  * scale / zero: fp16 values equal or one fp16 ulp apart (a group minimum or
+    range that lands within fp32 noise of an fp16 rounding boundary);
+  * rho / gamma: |diff| <= NORM_TOL * max(1, |x|) (log2 units); the kernel's
+    variances carry fp32 sums of 128 terms and hardware log2/exp2;
+  * dequantised cache and attention output: max-abs <= 2e-3 with the same
+    packed bytes on both sides (fp32 accumulation on the GPU).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import kvarn_oracle as o
+
+CODE_MISMATCH_FRACTION = 1e-4
+NORM_TOL = 2e-5
+DEQUANT_TOL = 2e-3
+ATTN_TOL = 2e-3
+
+
+def f16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in fp16 ulps between two fp16 arrays (sign-magnitude ordering)."""
+    ia = np.asarray(a, dtype=np.float16).view(np.int16).astype(np.int32)
+    ib = np.asarray(b, dtype=np.float16).view(np.int16).astype(np.int32)
+    ia = np.where(ia < 0, -(ia & 0x7FFF), ia)
+    ib = np.where(ib < 0, -(ib & 0x7FFF), ib)
+    return np.abs(ia - ib)
+
+
+class TileStats:
+    def __init__(self):
+        self.codes = 0
+        self.code_mismatch = 0
+        self.code_maxdiff = 0
+        self.cond_mismatch = 0
+        self.groups = 0
+        self.sz_exact = 0
+        self.sz_maxulp = 0
+        self.norm_maxerr = 0.0
+        self.tiles = 0
+
+    def summary(self) -> str:
+        return ("tiles %d codes %d mismatch %d (%.2e) maxdiff %d | given-stored-grid mismatch %d | "
+                "scale/zero exact %d/%d max ulp %d | rho/gamma max rel err %.2e"
+                % (self.tiles, self.codes, self.code_mismatch, self.code_mismatch / max(1, self.codes),
+                   self.code_maxdiff, self.cond_mismatch, self.sz_exact, 2 * self.groups, self.sz_maxulp,
+                   self.norm_maxerr))
+
+    def check(self):
+        assert self.code_maxdiff <= 1, self.summary()
+        assert self.code_mismatch <= CODE_MISMATCH_FRACTION * self.codes, self.summary()
+        assert self.cond_mismatch <= CODE_MISMATCH_FRACTION * self.codes, self.summary()
+        assert self.sz_maxulp <= 1, self.summary()
+        assert self.norm_maxerr <= NORM_TOL, self.summary()
+
+
+def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: bool) -> None:
+    """Compare one GPU-written page against the oracle's quantisation of the same fp16 tile."""
+    ref = o.quantize_tile(x16, is_v)
+    got = o.decode_page(page_bytes, is_v)
+    stats.tiles += 1
+    for key in ("rho", "gamma"):
+        a = got[key].astype(np.float64)
+        b = ref[key].astype(np.float64)
+        err = np.abs(a - b) / np.maximum(1.0, np.abs(b))
+        stats.norm_maxerr = max(stats.norm_maxerr, float(err.max()))
+    for key in ("scale", "zero"):
+        d = f16_ulp_distance(got[key], ref[key])
+        stats.sz_exact += int((d == 0).sum())
+        stats.sz_maxulp = max(stats.sz_maxulp, int(d.max()))
+    stats.groups += len(ref["scale"])
+    diff = np.abs(got["codes"].astype(np.int32) - ref["codes"].astype(np.int32))
+    stats.codes += diff.size
+    stats.code_mismatch += int((diff != 0).sum())
+    stats.code_maxdiff = max(stats.code_maxdiff, int(diff.max()))
+    # the rounding decision alone: oracle codes on the GPU's stored normalisers and grid
+    n32 = o.normalized(o.rotate(x16.astype(np.float64)), got["rho"], got["gamma"]).astype(np.float32)
+    cond = np.zeros_like(got["codes"])
+    levels = o.V_LEVELS if is_v else o.K_LEVELS
+    for gi in range(128):
+        if is_v:
+            cond[gi, :] = o.rtn_codes(n32[gi, :], got["scale"][gi], got["zero"][gi], levels)
+        else:
+            cond[:, gi] = o.rtn_codes(n32[:, gi], got["scale"][gi], got["zero"][gi], levels)
+    stats.cond_mismatch += int((cond != got["codes"]).sum())

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: exports, config parsing, page
+sizes, argument validation (every rejected call returns before any HIP call)
+and the benchmark's byte accounting against the pages' printed figures."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_quantization_kvarn_amd import accounting
+from kv_cache_quantization_kvarn_amd import kvarn as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "kvarn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_config_parse():
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
+    assert (cfg.head_dim, cfg.block_tokens, cfg.k_bits, cfg.v_bits, cfg.group_size, cfg.norm_iters) == \
+        (128, 128, 4, 2, 128, 4)
+    assert abs(cfg.eps - 1e-6) < 1e-12
+    for bad in ("kvarn_k8v4_g64", "kvarn_k4v2_g128x", "fp8", "kvarn_k4v2"):
+        with pytest.raises(K.KvarnError) as e:
+            K.kvarn_config_parse(bad)
+        assert e.value.status == K.KVARN_ERR_UNSUPPORTED
+    lib = K.library()
+    assert lib.kvarn_config_parse(None, None) == K.KVARN_ERR_NULL
+
+
+def test_page_bytes_match_the_oracle_format():
+    from oracle import kvarn_oracle as o
+    cfg = K.kvarn_config_parse()
+    assert K.kvarn_page_bytes(cfg, False) == o.K_PAGE_BYTES == 9728
+    assert K.kvarn_page_bytes(cfg, True) == o.V_PAGE_BYTES == 5632
+    bad = K.kvarn_config()
+    assert K.kvarn_page_bytes(bad, False) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def quant(cfg, k=FAKE, v=FAKE, n=1, h=8, pages=FAKE, kp=FAKE, vp=FAKE, npages=4):
+    return K.library().kvarn_quantize_blocks(ctypes.byref(cfg) if cfg is not None else None, k, v, n, h, pages, kp,
+                                             vp, npages, None, None)
+
+
+def test_quantize_validation():
+    cfg = K.kvarn_config_parse()
+    assert quant(None) == K.KVARN_ERR_NULL
+    assert quant(K.kvarn_config()) == K.KVARN_ERR_UNSUPPORTED
+    assert quant(cfg, n=-1) == K.KVARN_ERR_SHAPE
+    assert quant(cfg, h=0) == K.KVARN_ERR_SHAPE
+    assert quant(cfg, n=0) == K.KVARN_OK  # empty call is a no-op
+    assert quant(cfg, k=None) == K.KVARN_ERR_NULL
+    assert quant(cfg, pages=None) == K.KVARN_ERR_NULL
+    assert quant(cfg, npages=0) == K.KVARN_ERR_SHAPE
+    assert quant(cfg, k=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE  # misaligned
+    assert "aligned" in K.library().kvarn_last_error().decode()
+
+
+def decode(cfg, q=FAKE, kp=FAKE, vp=FAKE, npages=4, bt=FAKE, mb=2, sl=FAKE, b=1, hq=32, hkv=8, out=FAKE,
+           ws=ctypes.c_void_p(0x10000), wsb=1 << 30):
+    return K.library().kvarn_decode_attention(ctypes.byref(cfg), q, kp, vp, npages, bt, mb, sl, b, hq, hkv, 0.0, out,
+                                              ws, wsb, None, None)
+
+
+def test_decode_validation():
+    cfg = K.kvarn_config_parse()
+    assert decode(cfg, hq=30) == K.KVARN_ERR_SHAPE          # not a multiple of Hkv
+    assert decode(cfg, hq=128, hkv=8) == K.KVARN_ERR_UNSUPPORTED  # 16 query heads per KV head
+    assert decode(cfg, b=-1) == K.KVARN_ERR_SHAPE
+    assert decode(cfg, b=0) == K.KVARN_OK
+    assert decode(cfg, q=None) == K.KVARN_ERR_NULL
+    assert decode(cfg, bt=None) == K.KVARN_ERR_NULL
+    assert decode(cfg, wsb=16) == K.KVARN_ERR_WORKSPACE
+    assert decode(cfg, ws=None) == K.KVARN_ERR_WORKSPACE
+    assert decode(cfg, ws=ctypes.c_void_p(0x10010)) == K.KVARN_ERR_WORKSPACE  # not 256-byte aligned
+    assert decode(cfg, kp=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
+
+
+def test_workspace_sizes():
+    cfg = K.kvarn_config_parse()
+    a = K.kvarn_decode_workspace_bytes(cfg, 16, 32, 8, 64)
+    b = K.kvarn_decode_workspace_bytes(cfg, 16, 32, 8, 1024)
+    assert a > 0 and b >= a
+    assert K.kvarn_decode_workspace_bytes(cfg, 0, 32, 8, 64) == 0
+    assert K.kvarn_decode_workspace_bytes(cfg, 4, 32, 8, 0) > 0  # empty tables still need the counters
+    assert K.kvarn_decode_workspace_bytes(K.kvarn_config(), 16, 32, 8, 64) == 0
+
+
+def test_status_strings():
+    lib = K.library()
+    for s in range(-5, 1):
+        assert lib.kvarn_status_string(s)
+
+
+def golden():
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "page_figures.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            k, v = line.split(None, 1)
+            vals[k] = v
+    return vals
+
+
+def test_byte_accounting_reproduces_page_figures():
+    g = golden()
+    cfg = K.kvarn_config_parse(g["format_name"])
+    kb, vb = K.kvarn_page_bytes(cfg, False), K.kvarn_page_bytes(cfg, True)
+    ratio = accounting.capacity_ratio(kb, vb)
+    assert float(g["capacity_ratio_vs_fp16_min"]) <= ratio <= float(g["capacity_ratio_vs_fp16_max"])
+    # 7B-class model at 4096 tokens: about 500 MB
+    b7 = accounting.fp16_kv_bytes(int(g["kv7b_layers"]), int(g["kv7b_kv_heads"]), int(g["kv7b_tokens"]))
+    assert abs(b7 / 1e6 - float(g["kv7b_approx_mb"])) / float(g["kv7b_approx_mb"]) < 0.1
+    # Qwen2.5-1.5B: about 29 KB per token
+    per_tok = accounting.fp16_kv_bytes(int(g["qwen_layers"]), int(g["qwen_kv_heads"]), 1)
+    assert abs(per_tok / 1000 - float(g["qwen_kb_per_token"])) / float(g["qwen_kb_per_token"]) < 0.05
+    # quantize moves 64 KiB of fp16 in and one K+V page pair out per (block, KV head)
+    assert accounting.quantize_bytes(1, 1, kb, vb) == 65536 + 15360
