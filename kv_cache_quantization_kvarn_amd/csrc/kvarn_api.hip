@@ -26,8 +26,9 @@ constexpr int kKPage = 9728;
 constexpr int kVPage = 5632;
 constexpr int kMaxGroup = 8;
 constexpr int kPartFloats = 128 + 2;
-constexpr int kMaxSplitsPerPair = 32;
-constexpr long kTargetWaves = 4096;
+constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
+constexpr long kTargetGroups = 512;    // workgroups (4 waves each) for one pass over the chip at 2 waves/SIMD
+constexpr long kMaxPagesPerSplit = 32;
 
 thread_local std::string g_last_error;
 
@@ -52,14 +53,16 @@ struct DecodePlan {
   int max_splits;
 };
 
-// Pages per wave: enough waves to fill the chip, at most kMaxSplitsPerPair partials per (sequence, KV head).
+// Pages per split (a multiple of the 4 waves of a workgroup): about one pass of workgroups over the
+// chip, at most 32 pages per split so mixed lengths balance, and at most 64 splits per
+// (sequence, KV head) so the final merge stays short.
 DecodePlan plan_decode(int batch, int hkv, int max_blocks) {
   const long units = static_cast<long>(batch) * hkv * max_blocks;
-  long bps = (units + kTargetWaves - 1) / kTargetWaves;
+  long bps = (units + kTargetGroups - 1) / kTargetGroups;
+  if (bps > kMaxPagesPerSplit) bps = kMaxPagesPerSplit;
   const long min_bps = (max_blocks + kMaxSplitsPerPair - 1) / kMaxSplitsPerPair;
   if (bps < min_bps) bps = min_bps;
-  if (bps < 1) bps = 1;
-  if (bps > max_blocks) bps = max_blocks > 0 ? max_blocks : 1;
+  bps = (bps + 3) / 4 * 4;
   DecodePlan p;
   p.blocks_per_split = static_cast<int>(bps);
   p.max_splits = static_cast<int>((max_blocks + bps - 1) / bps);

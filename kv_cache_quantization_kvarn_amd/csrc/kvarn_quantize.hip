@@ -14,10 +14,16 @@
 // 8 tokens x 8 channels,
 //     token   T(i) = 32w + 16*(i/4) + 4g + i%4          i = 0..7
 //     channel C(c) = 32*(c/2) + 16*(c%2) + n            c = 0..7
-// Row statistics (over channels) reduce over the 16 lanes of a DPP row;
-// column statistics (over tokens) reduce over the four rows of the wave and
-// then over the four waves through LDS.  Every reduction uses a fixed
-// pairing so all lanes that share a row or column see identical bits.
+//
+// Normalisation.  A pass needs, per row (or column), the mean and the mean
+// square of Y = R 2^-rho 2^-gamma.  Each lane forms partial sums over its 8
+// channels (or tokens) with one FMA per element for each moment (R and R^2
+// are kept in registers), writes them to LDS, and a pair of threads per row
+// (column) adds the 16 partials, takes the variance, and updates that row's
+// (column's) normaliser, which it keeps in a register across iterations.
+// Where the variance is small against the mean square (mean^2 > var, so the
+// one-sweep formula could lose digits) the pass is redone with centred sums.
+// Every sum has a fixed order, so all threads see identical values.
 #include "kvarn_common.h"
 
 namespace kvarn {
@@ -26,6 +32,32 @@ namespace {
 
 __device__ __forceinline__ int tok_of(int w, int g, int i) { return 32 * w + 16 * (i >> 2) + 4 * g + (i & 3); }
 __device__ __forceinline__ int chan_of(int n, int c) { return 32 * (c >> 1) + 16 * (c & 1) + n; }
+// position of channel ch in the per-lane-contiguous order used for per-channel LDS arrays
+__device__ __forceinline__ int chan_slot(int ch) { return 8 * (ch & 15) + 2 * (ch >> 5) + ((ch >> 4) & 1); }
+
+constexpr int kPartStride = 36;  // floats per row of the partial-sum array (16 slots x 2 + pad)
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float dpp_xor1(float x) { return dpp<kDppXor1>(x); }
+
+// Sum of the 8 (s1, s2) slot pairs of one row half, then with the partner thread (lane ^ 1).
+__device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
+  const float4* p = reinterpret_cast<const float4*>(row + 16 * hf);
+  float a = 0.f, b = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float4 v = p[k];
+    a += v.x;
+    b += v.y;
+    a += v.z;
+    b += v.w;
+  }
+  // both threads of the pair add (first half + second half) in the same order
+  const float a2 = dpp_xor1(a), b2 = dpp_xor1(b);
+  return hf ? make_float2(a2 + a, b2 + b) : make_float2(a + a2, b + b2);
+}
 
 }  // namespace
 
@@ -34,8 +66,12 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
                                                          const int32_t* __restrict__ dst_pages,
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
-  __shared__ float red[2][4][kHeadDim];                // cross-wave column partials (double buffered)
-  __shared__ __align__(16) uint8_t codes[kBlockTokens * kHeadDim];  // staged codes, one byte each
+  __shared__ __align__(16) float part[kBlockTokens][kPartStride];  // per row / column: 16 partial pairs
+  __shared__ __align__(16) float rfl[kBlockTokens];                // 2^-rho, token order
+  __shared__ __align__(16) float cfl[kHeadDim];                    // 2^-gamma, chan_slot order
+  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim]; // 1/s and -z/s of each group
+  __shared__ __align__(16) float mul_c[kHeadDim];                  // means for centred fallback
+  __shared__ __align__(16) uint8_t codes[kBlockTokens * kHeadDim]; // staged codes, one byte each
 
   const int tile = blockIdx.x;
   const bool is_v = tile & 1;
@@ -88,86 +124,123 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       }
     }
   }
+  float P[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) P[i][c] = R[i][c] * R[i][c];
 
   // ---- 2. log2-variance normalisation, rows then columns, kNormIters times --
-  float rho[8], gam[8], rf[8], cf[8];
+  // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes).
+  const int t_red = tid >> 1, hf = tid & 1;
+  float rho_t = 0.f, rf_t = 1.f;   // normaliser of row t_red
+  float gam_c = 0.f, cf_c = 1.f;   // normaliser of column c_red (= t_red)
+  float rf[8], cf[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    rho[k] = 0.f;
-    gam[k] = 0.f;
     rf[k] = 1.f;
     cf[k] = 1.f;
   }
-  int buf = 0;
-  // Column reduction of v[c] over all 128 tokens (rows of the wave, then waves).
-  auto col_sum = [&](float (&v)[8]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) v[c] = rows4_sum(v[c]);
-    if (g == 0) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) red[buf][w][chan_of(n, c)] = v[c];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int ch = chan_of(n, c);
-      v[c] = ((red[buf][0][ch] + red[buf][1][ch]) + red[buf][2][ch]) + red[buf][3][ch];
-    }
-    buf ^= 1;
-  };
-
   constexpr float inv128 = 1.0f / 128.0f;
+
   for (int it = 0; it < kNormIters; ++it) {
-    // row pass: variance over channels of Y = R * rf[i] * cf[c]
-    float mu[8];
+    // ---------------- row pass: moments over channels of R * cf -------------
+    {
+      float c2[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) s = fmaf(R[i][c], cf[c], s);
-      mu[i] = row16_sum(s) * inv128;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float q = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float d = fmaf(R[i][c], cf[c], -mu[i]);
-        q = fmaf(d, d, q);
-      }
-      const float var = row16_sum(q) * inv128 * (rf[i] * rf[i]);
-      rho[i] += 0.5f * log2f(var + kNormEps);
-      rf[i] = exp2f(-rho[i]);
-    }
-    // column pass: variance over tokens of Y = R * rf[i] * cf[c]
-    float cm[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(R[i][c], rf[i], s);
-      cm[c] = s;
-    }
-    col_sum(cm);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) cm[c] *= inv128;
-    float cq[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float q = 0.f;
+      for (int c = 0; c < 8; ++c) c2[c] = cf[c] * cf[c];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float d = fmaf(R[i][c], rf[i], -cm[c]);
-        q = fmaf(d, d, q);
-      }
-      cq[c] = q;
-    }
-    col_sum(cq);
+        float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float var = cq[c] * inv128 * (cf[c] * cf[c]);
-      gam[c] += 0.5f * log2f(var + kNormEps);
-      cf[c] = exp2f(-gam[c]);
+        for (int c = 0; c < 8; ++c) {
+          s1 = fmaf(R[i][c], cf[c], s1);
+          s2 = fmaf(P[i][c], c2[c], s2);
+        }
+        *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
+      }
+    }
+    __syncthreads();
+    float2 m = reduce_pairs(part[t_red], hf);
+    float mu = m.x * inv128, ey2 = m.y * inv128;
+    float var = fmaf(-mu, mu, ey2);
+    if (__syncthreads_or(!(var >= 0.5f * ey2))) {
+      // centred second moment for the whole pass
+      if (hf == 0) mul_c[t_red] = mu;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float mi = mul_c[tok_of(w, g, i)];
+        float q = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float d = fmaf(R[i][c], cf[c], -mi);
+          q = fmaf(d, d, q);
+        }
+        *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
+      }
+      __syncthreads();
+      var = reduce_pairs(part[t_red], hf).x * inv128;
+    }
+    rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
+    rf_t = ex2(-rho_t);
+    if (hf == 0) rfl[t_red] = rf_t;
+    __syncthreads();
+    {
+      const float4 a = *reinterpret_cast<const float4*>(&rfl[32 * w + 4 * g]);
+      const float4 b = *reinterpret_cast<const float4*>(&rfl[32 * w + 16 + 4 * g]);
+      rf[0] = a.x; rf[1] = a.y; rf[2] = a.z; rf[3] = a.w;
+      rf[4] = b.x; rf[5] = b.y; rf[6] = b.z; rf[7] = b.w;
+    }
+    // ---------------- column pass: moments over tokens of R * rf ------------
+    {
+      float r2[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r2[i] = rf[i] * rf[i];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          s1 = fmaf(R[i][c], rf[i], s1);
+          s2 = fmaf(P[i][c], r2[i], s2);
+        }
+        *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(s1, s2);
+      }
+    }
+    __syncthreads();
+    m = reduce_pairs(part[t_red], hf);
+    mu = m.x * inv128;
+    ey2 = m.y * inv128;
+    var = fmaf(-mu, mu, ey2);
+    if (__syncthreads_or(!(var >= 0.5f * ey2))) {
+      if (hf == 0) mul_c[chan_slot(t_red)] = mu;
+      __syncthreads();
+      const float4 ma = *reinterpret_cast<const float4*>(&mul_c[8 * n]);
+      const float4 mb = *reinterpret_cast<const float4*>(&mul_c[8 * n + 4]);
+      const float mc[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float q = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float d = fmaf(R[i][c], rf[i], -mc[c]);
+          q = fmaf(d, d, q);
+        }
+        *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
+      }
+      __syncthreads();
+      var = reduce_pairs(part[t_red], hf).x * inv128;
+    }
+    gam_c += 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
+    cf_c = ex2(-gam_c);
+    if (hf == 0) cfl[chan_slot(t_red)] = cf_c;
+    __syncthreads();
+    {
+      const float4 a = *reinterpret_cast<const float4*>(&cfl[8 * n]);
+      const float4 b = *reinterpret_cast<const float4*>(&cfl[8 * n + 4]);
+      cf[0] = a.x; cf[1] = a.y; cf[2] = a.z; cf[3] = a.w;
+      cf[4] = b.x; cf[5] = b.y; cf[6] = b.z; cf[7] = b.w;
     }
   }
 
@@ -180,11 +253,17 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
   uint8_t* page_base = is_v ? v_pool + (static_cast<size_t>(page) * hkv + head) * kVPageBytes
                             : k_pool + (static_cast<size_t>(page) * hkv + head) * kKPageBytes;
   uint8_t* meta = page_base + (is_v ? kVCodeBytes : kKCodeBytes);
+  if (hf == 0) {
+    reinterpret_cast<float*>(meta + kMetaRho)[t_red] = rho_t;
+    reinterpret_cast<float*>(meta + kMetaGamma)[t_red] = gam_c;
+  }
 
   // ---- 3. per-group min/max, fp16 scale and zero, round to nearest ----------
+  // Codes come out of u + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
+  constexpr float kRoundMagic = 12582912.0f;
+  constexpr uint32_t kMagicBits = 0x4B400000u;
   if (!is_v) {
     // key groups: one channel over the 128 tokens, 16 levels
-    float mn[8], mx[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float a = R[0][c], b = R[0][c];
@@ -193,40 +272,46 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
         a = fminf(a, R[i][c]);
         b = fmaxf(b, R[i][c]);
       }
-      mn[c] = rows4_min(a);
-      mx[c] = rows4_max(b);
+      *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(a, b);
     }
-    __syncthreads();  // the last column reduction may still be reading red
-    if (g == 0) {
+    __syncthreads();
+    {
+      const float4* p = reinterpret_cast<const float4*>(part[t_red] + 16 * hf);
+      float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        red[0][w][chan_of(n, c)] = mn[c];
-        red[1][w][chan_of(n, c)] = mx[c];
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = p[k];
+        mn = fminf(mn, fminf(v.x, v.z));
+        mx = fmaxf(mx, fmaxf(v.y, v.w));
+      }
+      mn = fminf(mn, dpp_xor1(mn));
+      mx = fmaxf(mx, dpp_xor1(mx));
+      const uint32_t sb = float_to_half_bits((mx - mn) / 15.0f);
+      const uint32_t zb = float_to_half_bits(mn);
+      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+      if (hf == 0) {
+        reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
+        reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
+        mul_a[chan_slot(t_red)] = inv;
+        mul_b[chan_slot(t_red)] = -zf * inv;
       }
     }
     __syncthreads();
+    const float4 a0 = *reinterpret_cast<const float4*>(&mul_a[8 * n]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&mul_a[8 * n + 4]);
+    const float4 b0 = *reinterpret_cast<const float4*>(&mul_b[8 * n]);
+    const float4 b1 = *reinterpret_cast<const float4*>(&mul_b[8 * n + 4]);
+    const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int ch = chan_of(n, c);
-      mn[c] = fminf(fminf(red[0][0][ch], red[0][1][ch]), fminf(red[0][2][ch], red[0][3][ch]));
-      mx[c] = fmaxf(fmaxf(red[1][0][ch], red[1][1][ch]), fmaxf(red[1][2][ch], red[1][3][ch]));
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sb = float_to_half_bits((mx[c] - mn[c]) / 15.0f);
-      const uint32_t zb = float_to_half_bits(mn[c]);
-      const float s = half_bits_to_float(sb), z = half_bits_to_float(zb);
-      const float inv = s > 0.f ? 1.0f / s : 0.f;
       const int ch = chan_of(n, c);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float u = rintf((R[i][c] - z) * inv);
-        const float qc = fminf(fmaxf(u, 0.f), 15.f);
-        codes[tok_of(w, g, i) * kHeadDim + ch] = static_cast<uint8_t>(qc);
-      }
-      if (w == 0 && g == 0) {
-        reinterpret_cast<uint16_t*>(meta + kMetaScale)[ch] = static_cast<uint16_t>(sb);
-        reinterpret_cast<uint16_t*>(meta + kMetaZero)[ch] = static_cast<uint16_t>(zb);
+        const float u = fmaf(R[i][c], qa[c], qb[c]) + kRoundMagic;
+        const uint32_t bits = min(max(__float_as_uint(u), kMagicBits), kMagicBits + 15u);
+        codes[tok_of(w, g, i) * kHeadDim + ch] = static_cast<uint8_t>(bits);
       }
     }
   } else {
@@ -239,40 +324,58 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
         a = fminf(a, R[i][c]);
         b = fmaxf(b, R[i][c]);
       }
-      const float mn = row16_min(a), mx = row16_max(b);
+      *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+    }
+    __syncthreads();
+    {
+      const float4* p = reinterpret_cast<const float4*>(part[t_red] + 16 * hf);
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 v = p[k];
+        mn = fminf(mn, fminf(v.x, v.z));
+        mx = fmaxf(mx, fmaxf(v.y, v.w));
+      }
+      mn = fminf(mn, dpp_xor1(mn));
+      mx = fmaxf(mx, dpp_xor1(mx));
       const uint32_t sb = float_to_half_bits((mx - mn) / 3.0f);
       const uint32_t zb = float_to_half_bits(mn);
-      const float s = half_bits_to_float(sb), z = half_bits_to_float(zb);
-      const float inv = s > 0.f ? 1.0f / s : 0.f;
+      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+      if (hf == 0) {
+        reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
+        reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
+        mul_a[t_red] = inv;
+        mul_b[t_red] = -zf * inv;
+      }
+    }
+    __syncthreads();
+    float qa[8], qb[8];
+    {
+      const float4 a0 = *reinterpret_cast<const float4*>(&mul_a[32 * w + 4 * g]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&mul_a[32 * w + 16 + 4 * g]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&mul_b[32 * w + 4 * g]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&mul_b[32 * w + 16 + 4 * g]);
+      qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
+      qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
       const int t = tok_of(w, g, i);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float u = rintf((R[i][c] - z) * inv);
-        const float qc = fminf(fmaxf(u, 0.f), 3.f);
-        codes[chan_of(n, c) * kBlockTokens + t] = static_cast<uint8_t>(qc);
-      }
-      if (n == 0) {
-        reinterpret_cast<uint16_t*>(meta + kMetaScale)[t] = static_cast<uint16_t>(sb);
-        reinterpret_cast<uint16_t*>(meta + kMetaZero)[t] = static_cast<uint16_t>(zb);
+        const float u = fmaf(R[i][c], qa[i], qb[i]) + kRoundMagic;
+        const uint32_t bits = min(max(__float_as_uint(u), kMagicBits), kMagicBits + 3u);
+        codes[chan_of(n, c) * kBlockTokens + t] = static_cast<uint8_t>(bits);
       }
     }
-  }
-
-  // normalisers: rho per token (lanes n == 0), gamma per channel (wave 0, row 0)
-  if (n == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) reinterpret_cast<float*>(meta + kMetaRho)[tok_of(w, g, i)] = rho[i];
-  }
-  if (w == 0 && g == 0) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) reinterpret_cast<float*>(meta + kMetaGamma)[chan_of(n, c)] = gam[c];
   }
   __syncthreads();
 
   // ---- 4. pack codes and store ---------------------------------------------
   if (!is_v) {
     // K: token t = tid/2, channels 64*(tid%2) .. +63 -> 32 bytes, two nibbles per byte
-    const int t = tid >> 1, hf = tid & 1;
+    const int t = tid >> 1;
     const u32x4* srcv = reinterpret_cast<const u32x4*>(codes + t * kHeadDim + 64 * hf);
     u32x4 o[2];
 #pragma unroll
@@ -284,7 +387,6 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
         const uint32_t v = x[e];  // four codes, one per byte
         pk[e] = (v & 0xFu) | ((v >> 4) & 0xF0u) | (((v >> 16) & 0xFu) << 8) | (((v >> 20) & 0xF0u) << 8);
       }
-      // 8 input dwords (32 codes) -> 4 output dwords: out dword = pk[2e] | pk[2e+1] << 16
       o[q4 >> 1][(q4 & 1) * 2 + 0] = pk[0] | (pk[1] << 16);
       o[q4 >> 1][(q4 & 1) * 2 + 1] = pk[2] | (pk[3] << 16);
     }
@@ -293,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
     dst[1] = o[1];
   } else {
     // V: channel c = tid/2, tokens 64*(tid%2) .. +63 -> 16 bytes, four codes per byte
-    const int c = tid >> 1, hf = tid & 1;
+    const int c = tid >> 1;
     const u32x4* srcv = reinterpret_cast<const u32x4*>(codes + c * kBlockTokens + 64 * hf);
     u32x4 o;
 #pragma unroll
