@@ -2,10 +2,10 @@
 //
 // A workgroup of four waves handles one (sequence, KV head, split): the G <= 8
 // query heads that share the KV head attend to a run of 128-token pages, wave
-// w taking every fourth page.  Nothing is dequantised to memory.  Because the
-// rotation is orthonormal (KVarN blog post, section "KVarN Nasıl Çalışır?": it
-// keeps attention scores), the query is rotated once, q~ = H q, and both
-// contractions run in the rotated basis:
+// w taking every fourth page of the run.  Nothing is dequantised to memory.
+// Because the rotation is orthonormal (KVarN blog post, section "KVarN Nasıl
+// Çalışır?": it keeps attention scores), the query is rotated once, q~ = H q,
+// and both contractions run in the rotated basis:
 //
 //   key page:   score_t = 2^rho_t * ( sum_j a_j c_tj + b ),
 //               a_j = q~_j 2^gamma_j s_j,   b = sum_j q~_j 2^gamma_j z_j
@@ -14,15 +14,21 @@
 //
 // with online softmax over the pages (scores in log2 units).  Both sums over
 // codes are dense (G x 128) x (128 x 128) products per page and run on
-// v_mfma_f32_16x16x32_f16.  Codes enter as exact fp16 integers 16 + c (4-bit
-// keys) or 4 + c (2-bit values): one shift and one mask-and-or per pair of codes
-// places c in the top mantissa bits under a fixed exponent.  The offset is
-// removed afterwards with the page's sum of coefficients (16 sum a, 4 sum w).
-// (fp16 subnormal operands would avoid the offset, but the matrix cores lose
-// precision on them, biased toward zero.)  The fp32 coefficients a_j and w_t
-// enter as an fp16 hi + lo pair (hi in matrix columns 0-7, lo in columns 8-15,
-// after a power-of-two page scale keeps them in fp16 range); lane n and lane
-// n^8 of a DPP row then hold the two halves of the same query head.
+// v_mfma_f32_16x16x32_f16.  Codes enter as exact fp16 integers off + c: one
+// mask-and-or (and for most pairs one shift) places a pair of codes in the
+// mantissa under a fixed exponent, which fixes the offset (16 or 64 for keys,
+// 4 or 16 for values).  The offsets are removed with sums of the very fp16
+// coefficients the matrix cores multiplied.  (fp16 subnormal operands would
+// need no offset, but the matrix cores lose precision on them, biased toward
+// zero.)  The fp32 coefficients a_j and w_t enter as an fp16 hi + lo pair (hi in
+// matrix columns 0-7, lo in columns 8-15) after a power-of-two page scale keeps
+// them in fp16 range; lanes n and n^8 of a 16-lane row then hold the two halves
+// of one query head.  The per-head constants (b and u, offsets removed) enter
+// as the accumulator input of the first product of each chain.
+//
+// Latency: a wave issues the loads of its next page before it computes the
+// current one (two register sets, alternating), so a page's HBM latency
+// overlaps the previous page's arithmetic.
 //
 // Each wave keeps (m, l, o[128]) per head; the four waves merge through LDS,
 // the workgroup writes one partial per split, and the last workgroup of a
@@ -37,47 +43,50 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kPartStride = kHeadDim + 2;  // o[128], m, l per (split, query head)
 constexpr int kCoefStride = 68;            // dwords per coefficient column (64 slots + pad)
+constexpr int kPageList = 64;              // page ids of a split staged in LDS (longer splits read the table)
 constexpr int kMaxSplits = 64;             // the host plan never exceeds this many splits per (sequence, KV head)
 
-// Mask-and-or with the mask in a scalar register and the fp16 exponent pattern in a
-// vector register (one v_and_or_b32; the two literal constants would not fit one VOP3).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Mask-and-or with the fp16 exponent pattern kept in a vector register (one v_and_or_b32;
+// two literal constants would not fit one VOP3 encoding).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
   return (x & mask) | bits;
 }
 
-// Four fp16 pairs (16 + c) from one dword of 8 key nibbles (channel c at bits 4c):
-// elements (0..7) = channels 0,4,1,5,2,6,3,7.  `mag` holds 0x4C004C00 (fp16 16.0 twice).
-__device__ __forceinline__ f16x8 key_codes(uint32_t x, uint32_t mag) {
+// Four fp16 pairs from one dword of 8 key nibbles (channel 8m+i at bits 4i):
+// elements (0..7) = nibbles 0,4,1,5,2,6,3,7.  Nibbles 1 and 5 sit at mantissa bits
+// 4-7 under `mag64` (fp16 64.0 twice) and read 64 + c; the others are shifted to
+// bits 6-9 under `mag16` (16.0) and read 16 + c.
+__device__ __forceinline__ f16x8 key_codes(uint32_t x, uint32_t mag16, uint32_t mag64) {
   u32x4 p;
-  p[0] = and_or(x << 6, 0x03C003C0u, mag);
-  p[1] = and_or(x << 2, 0x03C003C0u, mag);
-  p[2] = and_or(x >> 2, 0x03C003C0u, mag);
-  p[3] = and_or(x >> 6, 0x03C003C0u, mag);
+  p[0] = and_or(x << 6, 0x03C003C0u, mag16);
+  p[1] = and_or(x, 0x00F000F0u, mag64);
+  p[2] = and_or(x >> 2, 0x03C003C0u, mag16);
+  p[3] = and_or(x >> 6, 0x03C003C0u, mag16);
   return __builtin_bit_cast(f16x8, p);
 }
 
-// Four fp16 pairs (4 + c) from a word of 16 value codes (code k at bits 2k), K-step half hf:
-// pair j holds codes k = 4hf + j and k + 8, moved to mantissa bits 8-9 of each half.
-// `mag` holds 0x44004400 (fp16 4.0 twice).
-__device__ __forceinline__ f16x8 value_codes(uint32_t w, int hf, uint32_t mag) {
-  u32x4 p;
-  if (hf == 0) {
-    p[0] = and_or(w << 8, 0x03000300u, mag);
-    p[1] = and_or(w << 6, 0x03000300u, mag);
-    p[2] = and_or(w << 4, 0x03000300u, mag);
-    p[3] = and_or(w << 2, 0x03000300u, mag);
-  } else {
-    p[0] = and_or(w, 0x03000300u, mag);
-    p[1] = and_or(w >> 2, 0x03000300u, mag);
-    p[2] = and_or(w >> 4, 0x03000300u, mag);
-    p[3] = and_or(w >> 6, 0x03000300u, mag);
-  }
-  return __builtin_bit_cast(f16x8, p);
+// Two f16x8 operands from a word of 16 value codes (code k at bits 2k).  Operand hf
+// holds pairs j = 0..3 of codes (4hf + j, 4hf + j + 8).  Even codes sit at mantissa
+// bits 8-9 under `mag4` (fp16 4.0) and read 4 + c; odd codes at bits 6-7 under
+// `mag16` (16.0) and read 16 + c.  Four shifts and eight mask-and-ors for 16 codes.
+__device__ __forceinline__ void value_codes(uint32_t w, uint32_t mag4, uint32_t mag16, f16x8& lo, f16x8& hi) {
+  const uint32_t r4 = w >> 4, l4 = w << 4, l8 = w << 8, r8 = w >> 8;
+  u32x4 a, b;
+  a[0] = and_or(l8, 0x03000300u, mag4);    // codes 0, 8
+  a[1] = and_or(l4, 0x00C000C0u, mag16);   // codes 1, 9
+  a[2] = and_or(l4, 0x03000300u, mag4);    // codes 2, 10
+  a[3] = and_or(w, 0x00C000C0u, mag16);    // codes 3, 11
+  b[0] = and_or(w, 0x03000300u, mag4);     // codes 4, 12
+  b[1] = and_or(r4, 0x00C000C0u, mag16);   // codes 5, 13
+  b[2] = and_or(r4, 0x03000300u, mag4);    // codes 6, 14
+  b[3] = and_or(r8, 0x00C000C0u, mag16);   // codes 7, 15
+  lo = __builtin_bit_cast(f16x8, a);
+  hi = __builtin_bit_cast(f16x8, b);
 }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Split two fp32 values into packed fp16 hi and lo parts, both rounded to nearest even
 // (v_cvt_pk_f16_f32, which keeps fp16 subnormals; the round-toward-zero packing
@@ -110,17 +119,74 @@ __device__ __forceinline__ uint32_t dpp_u32_xor8(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), kDppXor8, 0xF, 0xF, true));
 }
 
+// x from lane l^16 and l^32 (v_permlane16_swap / v_permlane32_swap on two copies of x).  The
+// pair (self, partner) is returned in lane order, so both lanes of a pair combine the same two
+// values in the same order and get identical bits.
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Max / sum over the 8 lanes that hold one query head (lanes n, n^8 in each of the 4 rows).
 __device__ __forceinline__ float head_max(float x) {
   x = fmaxf(x, dpp<kDppXor8>(x));
-  return rows4_max(x);
+  return max_xor32(max_xor16(x));
 }
 __device__ __forceinline__ float head_sum(float x) {
   x += dpp<kDppXor8>(x);
-  return rows4_sum(x);
+  return sum_xor32(sum_xor16(x));
+}
+// Max over the whole wave, identical in every lane.
+__device__ __forceinline__ float wave_max_all(float x) { return max_xor32(max_xor16(row16_max(x))); }
+
+// Sum over all 64 lanes of v[l & 7] (for each lane l): a transpose-reduce that halves the
+// number of values per lane at each of the first three stages (partners l^1, l^2 and l+4 mod
+// 16, the last one a row rotation), then adds across lanes l^8, l^16, l^32.
+__device__ __forceinline__ float head_reduce8(const float (&v)[kMaxGroup], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+  float s4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b0 ? v[2 * k + 1] : v[2 * k];
+    const float send = b0 ? v[2 * k] : v[2 * k + 1];
+    s4[k] = keep + dpp<kDppXor1>(send);
+  }
+  float s2[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    // s4[k] holds head 2k + b0; keep the two whose bit 1 (= k & 1) matches this lane
+    const float keep = b1 ? s4[2 * m + 1] : s4[2 * m];
+    const float send = b1 ? s4[2 * m] : s4[2 * m + 1];
+    s2[m] = keep + dpp<kDppXor2>(send);
+  }
+  // s2[k] holds head 4k + 2 b1 + b0; lane (l + 4) mod 16 always has the other value of b2
+  const float keep = b2 ? s2[1] : s2[0];
+  const float send = b2 ? s2[0] : s2[1];
+  float s = keep + dpp<kDppRor4>(send);
+  s += dpp<kDppXor8>(s);
+  return sum_xor32(sum_xor16(s));
 }
 
-__device__ __forceinline__ float wave_sum(float x) { return rows4_sum(row16_sum(x)); }
+// Agent-scope relaxed accesses to the split partials: on gfx950 they bypass the XCD-private L2
+// state that other XCDs cannot see.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // In-LDS 128-point Walsh-Hadamard transform of `rows` vectors (whole workgroup).
 __device__ void lds_fwht(float (*v)[kHeadDim], int rows) {
@@ -138,13 +204,241 @@ __device__ void lds_fwht(float (*v)[kHeadDim], int rows) {
 
 struct WaveLds {
   uint32_t coef[16][kCoefStride];  // key-side B operand: [column][slot] packed fp16 pairs
-  float pk[kHeadDim];              // 2^rho (K) per token
-  float fv[kHeadDim];              // 2^rho s (V) * value scale, per token
-  float zv[kHeadDim];              // 2^rho z (V) per token
-  float gv[kHeadDim];              // 2^gamma (V) per channel
-  float gs[kHeadDim];              // 2^gamma (V) / value scale, per channel
-  float bq[kMaxGroup];             // b = sum_j q~_j 2^gamma_j z_j per query head
+  float pk[kHeadDim];              // 2^rho (K) / key page scale, per token
+  float fv[kHeadDim];              // 2^rho s (V) * value page scale, per token
+  float zv[kHeadDim];              // 2^rho z (V), per token
+  float gs[kHeadDim];              // 2^gamma (V) / value page scale, per channel
 };
+
+// One page of one KV head as this lane loads it.
+struct PageRegs {
+  u32x4 kc[8];         // key codes: M-tile mt, row n -> token 32*(n/4) + 4*mt + n%4, channels 32g .. 32g+31
+  u32x2 vc[8];         // value codes: M-tile mt, row n -> channel 16mt + n, tokens 32g .. 32g+31
+  uint32_t ks0, ks1;   // key scale (fp16 bits) of channels ch0, ch1
+  uint32_t kz0, kz1;   // key zero
+  float kg0, kg1;      // key gamma
+  float2 kr;           // key rho of tokens 2*lane, 2*lane+1
+  uint32_t vs2, vz2;   // value scale / zero (fp16 pairs) of tokens 2*lane, 2*lane+1
+  float2 vr, vg;       // value rho of those tokens, value gamma of channels 2*lane, 2*lane+1
+  bool ok;
+};
+
+// Issues every load of one page without a branch: a bad page id reads page 0 instead (the
+// caller guarantees num_pages > 0) and only clears `ok`.
+__device__ __forceinline__ void load_page(PageRegs& P, int page, int num_pages, int hkv, int kvh,
+                                          const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+                                          int lane, int n, int g, int ch0) {
+  P.ok = page >= 0 && page < num_pages;
+  const int safe = P.ok ? page : 0;
+  const uint8_t* kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * kKPageBytes;
+  const uint8_t* vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * kVPageBytes;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+    P.kc[mt] = *reinterpret_cast<const u32x4*>(kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * 64 + 16 * g);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) P.vc[mt] = *reinterpret_cast<const u32x2*>(vp + (16 * mt + n) * 32 + 8 * g);
+  const uint8_t* km = kp + kKCodeBytes;
+  const uint8_t* vm = vp + kVCodeBytes;
+  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + kMetaScale);
+  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + kMetaZero);
+  const float* kgm = reinterpret_cast<const float*>(km + kMetaGamma);
+  P.ks0 = ksc[ch0];
+  P.ks1 = ksc[ch0 + 4];
+  P.kz0 = kzr[ch0];
+  P.kz1 = kzr[ch0 + 4];
+  P.kg0 = kgm[ch0];
+  P.kg1 = kgm[ch0 + 4];
+  P.kr = reinterpret_cast<const float2*>(km + kMetaRho)[lane];
+  P.vs2 = reinterpret_cast<const uint32_t*>(vm + kMetaScale)[lane];
+  P.vz2 = reinterpret_cast<const uint32_t*>(vm + kMetaZero)[lane];
+  P.vr = reinterpret_cast<const float2*>(vm + kMetaRho)[lane];
+  P.vg = reinterpret_cast<const float2*>(vm + kMetaGamma)[lane];
+}
+
+// Per-wave state carried across pages.
+struct WaveState {
+  float q0[kMaxGroup], q1[kMaxGroup];  // rotated, scaled query at this lane's two coefficient slots
+  float qmax;                          // max |q0|, |q1| over the wave and the heads
+  float m_run, l_run;                  // online softmax of this lane's head (log2 units)
+  float acc[8][4];                     // o (rotated basis, hi or lo column) of channels 16mt + 4g + r
+};
+
+__device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, WaveLds& L, int G, int lane, int g,
+                                             int lo_col, uint32_t mag16, uint32_t mag64, uint32_t mag4) {
+  // ---- key-side coefficients (this lane: slots ch0 and ch0 + 4, all heads) ---
+  const float s0 = half_bits_to_float(P.ks0), s1 = half_bits_to_float(P.ks1);
+  const float z0 = half_bits_to_float(P.kz0), z1 = half_bits_to_float(P.kz1);
+  const float eg0 = ex2(P.kg0), eg1 = ex2(P.kg1);
+  const float e0 = eg0 * s0, e1 = eg1 * s1;
+  const float f0 = eg0 * z0, f1 = eg1 * z1;
+  // ---- value-side per-token factors (this lane: tokens 2*lane, 2*lane+1) -----
+  const float vr0 = ex2(P.vr.x), vr1 = ex2(P.vr.y);
+  const float F0 = vr0 * half_bits_to_float(P.vs2 & 0xFFFFu), F1 = vr1 * half_bits_to_float(P.vs2 >> 16);
+  const float emax = wave_max_all(fmaxf(e0, e1));
+  const float fmaxv = wave_max_all(fmaxf(F0, F1));
+
+  int ex;
+  const float prod = S.qmax * emax;
+  frexpf(prod, &ex);
+  ex = min(max(ex, -100), 100);
+  const bool live = prod > 0.f;
+  const float sa = live ? pow2i(14 - ex) : 1.f;  // |a * sa| < 2^14
+  const float inv_sa = live ? pow2i(ex - 14) : 0.f;
+  const float e0s = e0 * sa, e1s = e1 * sa;
+  // the key offsets of this lane's two slots: 64 for nibbles 1 and 5 of a dword, else 16
+  const _Float16 off = (lane & 3) == 1 ? static_cast<_Float16>(64.0f) : static_cast<_Float16>(16.0f);
+  const f16x2 offp = {off, off};
+  float bp[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      uint32_t hi, lo;
+      split_pair(S.q0[h] * e0s, S.q1[h] * e1s, hi, lo);
+      L.coef[h][lane] = hi;
+      L.coef[8 + h][lane] = lo;
+      // offset contribution of exactly the fp16 coefficients the matrix cores use
+      const float aoff = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo), offp,
+                                                __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi), offp, 0.f, false),
+                                                false);
+      bp[h] = fmaf(-inv_sa, aoff, fmaf(S.q0[h], f0, S.q1[h] * f1));
+    } else {
+      bp[h] = 0.f;
+    }
+  }
+
+  int exf;
+  frexpf(fmaxv, &exf);
+  exf = min(max(exf, -100), 100);
+  const bool livef = fmaxv > 0.f;
+  const float sw = livef ? pow2i(14 - exf) : 1.f;  // p <= 1, so |w * sw| < 2^14
+  const float inv_sw = livef ? pow2i(exf - 14) : 0.f;
+  const int t0 = 2 * lane;
+  L.pk[t0] = ex2(P.kr.x) * inv_sa;
+  L.pk[t0 + 1] = ex2(P.kr.y) * inv_sa;
+  L.fv[t0] = F0 * sw;
+  L.fv[t0 + 1] = F1 * sw;
+  L.zv[t0] = vr0 * half_bits_to_float(P.vz2 & 0xFFFFu);
+  L.zv[t0 + 1] = vr1 * half_bits_to_float(P.vz2 >> 16);
+  L.gs[t0] = ex2(P.vg.x) * inv_sw;
+  L.gs[t0 + 1] = ex2(P.vg.y) * inv_sw;
+  // b (offsets removed) of this lane's head, in key-page-scaled units, enters the hi columns
+  const float bsum = head_reduce8(bp, lane);
+  const float kinit = sel_lo(bsum * sa, 0.f);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- key side: scores ---------------------------------------------------
+  const int n = lane & 15;
+  f16x8 cb[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    cb[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&L.coef[n][16 * g + 4 * ks]));
+  float s[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    f32x4 d = {kinit, kinit, kinit, kinit};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) d = mfma16x16x32(key_codes(P.kc[mt][ks], mag16, mag64), cb[ks], d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[mt][r] = d[r] + dpp<kDppXor8>(d[r]);
+  }
+  // this lane keeps tokens 32g + 16*lo_col + 4mt' + r (mt' = 0..3)
+  float sm[4][4];
+  float mloc = -INFINITY;
+  const float* pkp = &L.pk[32 * g + 16 * lo_col];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
+    const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sm[mt][r] = pkv[r] * sel_lo(s[mt][r], s[mt + 4][r]);
+      mloc = fmaxf(mloc, sm[mt][r]);
+    }
+  }
+  mloc = head_max(mloc);
+  const float m_new = fmaxf(S.m_run, mloc);
+  const float alpha = ex2(S.m_run - m_new);
+  S.m_run = m_new;
+
+  // ---- softmax weights, value-side B operand -------------------------------
+  const float* fvp = &L.fv[32 * g + 16 * lo_col];
+  const float* zvp = &L.zv[32 * g + 16 * lo_col];
+  float lsum = 0.f, usum = 0.f, wev = 0.f, wod = 0.f;
+  float wv[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const float4 f4 = *reinterpret_cast<const float4*>(fvp + 4 * mt);
+    const float4 z4 = *reinterpret_cast<const float4*>(zvp + 4 * mt);
+    const float fvv[4] = {f4.x, f4.y, f4.z, f4.w};
+    const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = ex2(sm[mt][r] - m_new);
+      lsum += p;
+      usum = fmaf(p, zvv[r], usum);
+      wv[mt][r] = p * fvv[r];
+    }
+  }
+  // pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
+  uint32_t own_hi[2][4], own_lo[2][4];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split_pair(wv[hf][j], wv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
+  // value offsets (4 for even tokens, 16 for odd) of exactly the fp16 weights used
+  {
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float& acc = (j & 1) ? wod : wev;
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_hi[hf][j]), ones, acc, false);
+        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_lo[hf][j]), ones, acc, false);
+      }
+  }
+  lsum = head_sum(lsum);
+  S.l_run = fmaf(S.l_run, alpha, lsum);
+  // u minus the value offsets, in value-page-scaled units, enters the hi columns
+  const float ucorr = head_sum(fmaf(usum, sw, -fmaf(16.f, wod, 4.f * wev)));
+  const float vinit = sel_lo(ucorr, 0.f);
+  f16x8 wb[2][2];  // [u][hf]
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    u32x4 mine, other;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mine[j] = sel_lo_u32(own_hi[hf][j], own_lo[hf][j]);
+      other[j] = dpp_u32_xor8(sel_lo_u32(own_lo[hf][j], own_hi[hf][j]));
+    }
+    u32x4 u0, u1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u0[j] = sel_lo_u32(mine[j], other[j]);
+      u1[j] = sel_lo_u32(other[j], mine[j]);
+    }
+    wb[0][hf] = __builtin_bit_cast(f16x8, u0);
+    wb[1][hf] = __builtin_bit_cast(f16x8, u1);
+  }
+
+  // ---- value side: o (rotated basis), hi and lo columns kept apart ----------
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    f32x4 d = {vinit, vinit, vinit, vinit};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f16x8 c0, c1;
+      value_codes(P.vc[mt][u], mag4, mag16, c0, c1);
+      d = mfma16x16x32(c0, wb[u][0], d);
+      d = mfma16x16x32(c1, wb[u][1], d);
+    }
+    const float4 gs4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
+    const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(S.acc[mt][r], alpha, d[r] * gsv[r]);
+  }
+}
 
 }  // namespace
 
@@ -158,6 +452,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   __shared__ float wm[kWaves][kMaxGroup], wls[kWaves][kMaxGroup];
   __shared__ float wacc[kWaves][kMaxGroup][kHeadDim];
   __shared__ float mw[kMaxGroup][kMaxSplits];
+  __shared__ int pg[kPageList];
   __shared__ int last_flag;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -180,7 +475,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   const int nsplit = (nblk + blocks_per_split - 1) / blocks_per_split;
   if (split >= nsplit) return;
   const int blk0 = split * blocks_per_split;
-  const int blk1 = min(nblk, blk0 + blocks_per_split);
+  const int cnt = min(nblk, blk0 + blocks_per_split) - blk0;
+  const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + blk0;
+  const bool listed = cnt <= kPageList;
+  if (listed && tid < cnt) pg[tid] = bt[tid];
 
   // ---- rotated, scaled query ------------------------------------------------
   const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
@@ -191,239 +489,51 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   __syncthreads();
   lds_fwht(qs, kMaxGroup);
   WaveLds& L = wl[w];
-  // coefficient slot of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
+  // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
   const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
-  const int ch1 = ch0 + 4;
-  uint32_t kmag = 0x4C004C00u, vmag = 0x44004400u;  // fp16 16.0 / 4.0 pairs, kept in vector registers
-  asm volatile("" : "+v"(kmag), "+v"(vmag));
-  float q0[kMaxGroup], q1[kMaxGroup];
+  uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
+  asm volatile("" : "+v"(mag16), "+v"(mag64), "+v"(mag4));
+  WaveState S;
   float qmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
-    q0[h] = qs[h][ch0] * (kInvSqrt128 * scale_log2);
-    q1[h] = qs[h][ch1] * (kInvSqrt128 * scale_log2);
-    qmax = fmaxf(qmax, fmaxf(fabsf(q0[h]), fabsf(q1[h])));
+    S.q0[h] = qs[h][ch0] * (kInvSqrt128 * scale_log2);
+    S.q1[h] = qs[h][ch0 + 4] * (kInvSqrt128 * scale_log2);
+    qmax = fmaxf(qmax, fmaxf(fabsf(S.q0[h]), fabsf(S.q1[h])));
   }
-  qmax = wave_max(qmax);
-  // unused coefficient columns stay zero
-  for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
-
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[8][4];
+  S.qmax = wave_max_all(qmax);
+  S.m_run = -INFINITY;
+  S.l_run = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[mt][r] = 0.f;
+    for (int r = 0; r < 4; ++r) S.acc[mt][r] = 0.f;
+  // unused coefficient columns stay zero
+  for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
 
-  const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
-  for (int blk = blk0 + w; blk < blk1; blk += kWaves) {
-    const int page = bt[blk];
-    if (page < 0 || page >= num_pages) {
-      if (lane == 0 && flags) atomicOr(flags, kFlagBadPage);
-      continue;
-    }
-    const uint8_t* kp = k_pool + (static_cast<size_t>(page) * hkv + kvh) * kKPageBytes;
-    const uint8_t* vp = v_pool + (static_cast<size_t>(page) * hkv + kvh) * kVPageBytes;
-    const uint8_t* km = kp + kKCodeBytes;
-    const uint8_t* vm = vp + kVCodeBytes;
-
-    // key codes: M-tile mt, row n -> token 32*(n/4) + 4*mt + n%4, channels 32g .. 32g+31
-    u32x4 kc[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-      kc[mt] = *reinterpret_cast<const u32x4*>(kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * 64 + 16 * g);
-    // value codes: M-tile mt, row n -> channel 16mt + n, tokens 32g .. 32g+31
-    u32x2 vc[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) vc[mt] = *reinterpret_cast<const u32x2*>(vp + (16 * mt + n) * 32 + 8 * g);
-    // metadata
-    const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + kMetaScale);
-    const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + kMetaZero);
-    const float* kgm = reinterpret_cast<const float*>(km + kMetaGamma);
-    const float s0 = half_bits_to_float(ksc[ch0]), s1 = half_bits_to_float(ksc[ch1]);
-    const float z0 = half_bits_to_float(kzr[ch0]), z1 = half_bits_to_float(kzr[ch1]);
-    const float eg0 = ex2(kgm[ch0]), eg1 = ex2(kgm[ch1]);
-    const float2 kr2 = reinterpret_cast<const float2*>(km + kMetaRho)[lane];
-    const uint32_t vs2 = reinterpret_cast<const uint32_t*>(vm + kMetaScale)[lane];
-    const uint32_t vz2 = reinterpret_cast<const uint32_t*>(vm + kMetaZero)[lane];
-    const float2 vr2 = reinterpret_cast<const float2*>(vm + kMetaRho)[lane];
-    const float2 vg2 = reinterpret_cast<const float2*>(vm + kMetaGamma)[lane];
-
-    // ---- key-side coefficients (this lane: one slot, all heads) -------------
-    const float e0 = eg0 * s0, e1 = eg1 * s1;
-    const float emax = wave_max(fmaxf(e0, e1));
-    int ex;
-    frexpf(qmax * emax, &ex);
-    ex = min(max(ex, -100), 100);
-    const bool live = qmax * emax > 0.f;
-    const float sa = live ? pow2i(14 - ex) : 1.f;        // |a * sa| < 2^14
-    const float inv_sa = live ? pow2i(ex - 14) : 0.f;
-    const float f0 = eg0 * z0, f1 = eg1 * z1;
-    const float e0s = e0 * sa, e1s = e1 * sa;
-    float bh[kMaxGroup];
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
-        uint32_t hi, lo;
-        split_pair(q0[h] * e0s, q1[h] * e1s, hi, lo);
-        L.coef[h][lane] = hi;
-        L.coef[8 + h][lane] = lo;
-        const f16x2 hv = __builtin_bit_cast(f16x2, hi), lv = __builtin_bit_cast(f16x2, lo);
-        const float asum = (static_cast<float>(hv[0]) + static_cast<float>(lv[0])) +
-                           (static_cast<float>(hv[1]) + static_cast<float>(lv[1]));
-        // b minus the 16-offset of the key codes, both per query head
-        bh[h] = fmaf(-16.f * inv_sa, asum, fmaf(q0[h], f0, q1[h] * f1));
-      } else {
-        bh[h] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) bh[h] = wave_sum(bh[h]);
-      if (lane == h) L.bq[h] = bh[h];
-    }
-
-    // ---- per-token / per-channel factors (this lane: entries 2*lane, 2*lane+1)
-    const float pr0 = ex2(kr2.x), pr1 = ex2(kr2.y);
-    const float vr0 = ex2(vr2.x), vr1 = ex2(vr2.y);
-    const float F0 = vr0 * half_bits_to_float(vs2 & 0xFFFFu), F1 = vr1 * half_bits_to_float(vs2 >> 16);
-    const float fmaxv = wave_max(fmaxf(F0, F1));
-    int exf;
-    frexpf(fmaxv, &exf);
-    exf = min(max(exf, -100), 100);
-    const bool livef = fmaxv > 0.f;
-    const float sw = livef ? pow2i(14 - exf) : 1.f;       // p <= 1, so |w * sw| < 2^14
-    const float inv_sw = livef ? pow2i(exf - 14) : 0.f;
-    const int t0 = 2 * lane;
-    L.pk[t0] = pr0;
-    L.pk[t0 + 1] = pr1;
-    L.fv[t0] = F0 * sw;
-    L.fv[t0 + 1] = F1 * sw;
-    L.zv[t0] = vr0 * half_bits_to_float(vz2 & 0xFFFFu);
-    L.zv[t0 + 1] = vr1 * half_bits_to_float(vz2 >> 16);
-    const float gv0 = ex2(vg2.x), gv1 = ex2(vg2.y);
-    L.gv[t0] = gv0;
-    L.gv[t0 + 1] = gv1;
-    L.gs[t0] = gv0 * inv_sw;
-    L.gs[t0 + 1] = gv1 * inv_sw;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    const float bmine = L.bq[hd];
-
-    // ---- key side: scores ---------------------------------------------------
-    f16x8 cb[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      cb[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&L.coef[n][16 * g + 4 * ks]));
-    float s[8][4];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) d = mfma16x16x32(key_codes(kc[mt][ks], kmag), cb[ks], d);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[mt][r] = d[r] + dpp<kDppXor8>(d[r]);
-    }
-    // this lane keeps tokens 32g + 16*lo_col + 4mt' + r (mt' = 0..3)
-    float sm[4][4];
-    float mloc = -INFINITY;
-    const float* pkp = &L.pk[32 * g + 16 * lo_col];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
-      const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sv = sel_lo(s[mt][r], s[mt + 4][r]);
-        sm[mt][r] = pkv[r] * fmaf(sv, inv_sa, bmine);
-        mloc = fmaxf(mloc, sm[mt][r]);
-      }
-    }
-    mloc = head_max(mloc);
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = ex2(m_run - m_new);
-    m_run = m_new;
-
-    // ---- softmax weights, value-side B operand -------------------------------
-    const float* fvp = &L.fv[32 * g + 16 * lo_col];
-    const float* zvp = &L.zv[32 * g + 16 * lo_col];
-    float lsum = 0.f, usum = 0.f, wsum = 0.f;
-    float wv[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float4 f4 = *reinterpret_cast<const float4*>(fvp + 4 * mt);
-      const float4 z4 = *reinterpret_cast<const float4*>(zvp + 4 * mt);
-      const float fvv[4] = {f4.x, f4.y, f4.z, f4.w};
-      const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = ex2(sm[mt][r] - m_new);
-        lsum += p;
-        usum = fmaf(p, zvv[r], usum);
-        wv[mt][r] = p * fvv[r];
-        wsum += wv[mt][r];
-      }
-    }
-    lsum = head_sum(lsum);
-    // u minus the 4-offset of the value codes (w is carried with the page scale sw)
-    usum = fmaf(-4.f * inv_sw, head_sum(wsum), head_sum(usum));
-    l_run = fmaf(l_run, alpha, lsum);
-    // pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
-    uint32_t own_hi[2][4], own_lo[2][4];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) split_pair(wv[hf][j], wv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
-    f16x8 wb[2][2];  // [u][hf]
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      u32x4 mine, other;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mine[j] = sel_lo_u32(own_hi[hf][j], own_lo[hf][j]);
-        other[j] = dpp_u32_xor8(sel_lo_u32(own_lo[hf][j], own_hi[hf][j]));
-      }
-      u32x4 u0, u1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u0[j] = sel_lo_u32(mine[j], other[j]);
-        u1[j] = sel_lo_u32(other[j], mine[j]);
-      }
-      wb[0][hf] = __builtin_bit_cast(f16x8, u0);
-      wb[1][hf] = __builtin_bit_cast(f16x8, u1);
-    }
-    const float ulane = sel_lo(usum, 0.f);
-
-    // ---- value side: o (rotated basis), hi and lo columns kept apart ----------
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) d = mfma16x16x32(value_codes(vc[mt][u], hf, vmag), wb[u][hf], d);
-      const float4 gs4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
-      const float4 gv4 = *reinterpret_cast<const float4*>(&L.gv[16 * mt + 4 * g]);
-      const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
-      const float gvv[4] = {gv4.x, gv4.y, gv4.z, gv4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(acc[mt][r], alpha, fmaf(d[r], gsv[r], ulane * gvv[r]));
-    }
+  // ---- pages of this wave: w, w + 4, ... ---------------------------------------
+  bool bad_page = num_pages <= 0 && w < cnt;  // with no pages every id is out of range
+  for (int i = w; i < cnt && num_pages > 0; i += kWaves) {
+    PageRegs A;
+    load_page(A, listed ? pg[i] : bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+    bad_page |= !A.ok;
+    if (A.ok) process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
   }
+  if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
 
   // ---- merge the four waves through LDS --------------------------------------
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[mt][r] += dpp<kDppXor8>(acc[mt][r]);
+    for (int r = 0; r < 4; ++r) S.acc[mt][r] += dpp<kDppXor8>(S.acc[mt][r]);
   if (!lo_col && hd < G) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wacc[w][hd][16 * mt + 4 * g + r] = acc[mt][r];
+      for (int r = 0; r < 4; ++r) wacc[w][hd][16 * mt + 4 * g + r] = S.acc[mt][r];
     if (g == 0) {
-      wm[w][hd] = m_run;
-      wls[w][hd] = l_run;
+      wm[w][hd] = S.m_run;
+      wls[w][hd] = S.l_run;
     }
   }
   __syncthreads();
@@ -442,27 +552,32 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
       lsum = fmaf(wgt, wls[x][h], lsum);
     }
     float* pp = pbase + (static_cast<size_t>(split) * kMaxGroup + h) * kPartStride;
-    pp[j] = o;
+    store_coherent(pp + j, o);
     if (j == 0) {
-      pp[kHeadDim] = mx;
-      pp[kHeadDim + 1] = lsum;
+      store_coherent(pp + kHeadDim, mx);
+      store_coherent(pp + kHeadDim + 1, lsum);
     }
   }
-  __threadfence();
+  // Hand-off between workgroups without fences.  Every XCD has its own L2, so an agent-scope
+  // fence would write back (release) or invalidate (acquire) this XCD's whole L2.  Instead the
+  // partials are written and read with agent-scope atomic accesses, which go through to the
+  // device-coherent level, and each wave waits until its stores are acknowledged before the
+  // workgroup counts itself in.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counters + pair, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t prev = __hip_atomic_fetch_add(counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last_flag = (prev == static_cast<uint32_t>(nsplit - 1));
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
-  if (tid == 0) counters[pair] = 0u;  // leave the counter ready for the next call
+  if (tid == 0) __hip_atomic_store(counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 
   // ---- merge the splits (log-sum-exp) and undo the rotation ---------------
   for (int e = tid; e < G * kMaxSplits; e += blockDim.x) {
     const int h = e / kMaxSplits, sp = e % kMaxSplits;
-    mw[h][sp] = sp < nsplit ? pbase[(static_cast<size_t>(sp) * kMaxGroup + h) * kPartStride + kHeadDim] : -INFINITY;
+    mw[h][sp] = sp < nsplit ? load_coherent(pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * kPartStride + kHeadDim)
+                            : -INFINITY;
   }
   __syncthreads();
   for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
@@ -474,8 +589,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
       const float ms = mw[h][sp];
       const float wgt = ms == -INFINITY ? 0.f : ex2(ms - mx);
       const float* pp = pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * kPartStride;
-      num = fmaf(wgt, pp[j], num);
-      den = fmaf(wgt, pp[kHeadDim + 1], den);
+      num = fmaf(wgt, load_coherent(pp + j), num);
+      den = fmaf(wgt, load_coherent(pp + kHeadDim + 1), den);
     }
     qs[h][j] = den > 0.f ? num / den : 0.f;
   }
