@@ -5,15 +5,19 @@
 // Çalışır?"): Hadamard rotation along channels, four row/column passes of
 // log2-variance normalisation, per-group min/max, round to nearest, packing.
 //
-// Data distribution.  Wave w owns tokens [32w, 32w+32).  The rotation runs on
-// the matrix cores: the 128-point Hadamard factors as H4 (x) H32 (channel bits
-// 5-6 and 0-4), so each wave multiplies its fp16 tokens by the exact +-1 H32
-// block (v_mfma_f32_16x16x32_f16, fp32 accumulation; the products are exact)
-// and finishes H4 with two in-register butterfly stages.  The MFMA result
-// layout then fixes what each lane holds: lane (n = lane%16, g = lane/16) keeps
-// 8 tokens x 8 channels,
+// Data distribution.  Wave w owns tokens [32w, 32w+32).  The rotation runs
+// entirely on the matrix cores: the 128-point Hadamard factors as H4 (x) H32
+// over channel-index bits (5-6) and (0-4), so each output tile is a chain of
+// four v_mfma_f32_16x16x32_f16 products of the wave's fp16 tokens with the
+// exact +-1 H32 block, each input chunk entering with the sign of the H4 entry
+// (fp32 accumulation; the products are exact).  The rotation is left
+// unnormalised (R' = sqrt(128) R); the factor 2^-3.5 rides in the row
+// normaliser 2^-rho instead, which leaves every normalised value unchanged.
+// The MFMA result layout fixes what each lane holds: lane (n = lane%16,
+// g = lane/16) keeps 8 tokens x 8 channels,
 //     token   T(i) = 32w + 16*(i/4) + 4g + i%4          i = 0..7
-//     channel C(c) = 32*(c/2) + 16*(c%2) + n            c = 0..7
+//     channel C(c) = 32*(c/2) + 2n + c%2                c = 0..7
+// so a lane holds channel pairs (2k, 2k+1), the two nibbles of one key byte.
 //
 // Normalisation.  A pass needs, per row (or column), the mean and the mean
 // square of Y = R 2^-rho 2^-gamma.  Each lane forms partial sums over its 8
@@ -24,6 +28,12 @@
 // Where the variance is small against the mean square (mean^2 > var, so the
 // one-sweep formula could lose digits) the pass is redone with centred sums.
 // Every sum has a fixed order, so all threads see identical values.
+//
+// Codes.  The normaliser of the group axis is folded into the rounding FMA
+// (u = M * (2^-x / s) - z / s with M the value scaled by the other normaliser),
+// codes are packed in registers (two nibbles or four 2-bit codes per byte),
+// transposed across lanes into whole dwords of the page (DPP within a quad for
+// keys, v_permlane16/32_swap across rows for values) and stored directly.
 #include "kvarn_common.h"
 
 namespace kvarn {
@@ -31,9 +41,10 @@ namespace kvarn {
 namespace {
 
 __device__ __forceinline__ int tok_of(int w, int g, int i) { return 32 * w + 16 * (i >> 2) + 4 * g + (i & 3); }
-__device__ __forceinline__ int chan_of(int n, int c) { return 32 * (c >> 1) + 16 * (c & 1) + n; }
+__device__ __forceinline__ int chan_of(int n, int c) { return 32 * (c >> 1) + 2 * n + (c & 1); }
 // position of channel ch in the per-lane-contiguous order used for per-channel LDS arrays
-__device__ __forceinline__ int chan_slot(int ch) { return 8 * (ch & 15) + 2 * (ch >> 5) + ((ch >> 4) & 1); }
+// (lane n reads slots 8n .. 8n+7, slot 8n + c holding channel chan_of(n, c))
+__device__ __forceinline__ int chan_slot(int ch) { return 8 * ((ch >> 1) & 15) + 2 * (ch >> 5) + (ch & 1); }
 
 constexpr int kPartStride = 36;  // floats per row of the partial-sum array (16 slots x 2 + pad)
 
@@ -41,6 +52,11 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
 __device__ __forceinline__ float dpp_xor1(float x) { return dpp<kDppXor1>(x); }
+
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, int ctrl_xor2) {
+  return ctrl_xor2 ? static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), kDppXor2, 0xF, 0xF, true))
+                   : static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), kDppXor1, 0xF, 0xF, true));
+}
 
 // Sum of the 8 (s1, s2) slot pairs of one row half, then with the partner thread (lane ^ 1).
 __device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
@@ -59,6 +75,41 @@ __device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
   return hf ? make_float2(a2 + a, b2 + b) : make_float2(a + a2, b + b2);
 }
 
+// Rounded product that the compiler may not fuse into a later add: the group range is a
+// difference of two such products, and contracting one of them into an FMA would turn an
+// exactly constant group (max == min) into a range of one rounding error, of either sign.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+  float p = a * b;
+  asm("" : "+v"(p));
+  return p;
+}
+
+// Low bytes of four registers, packed little endian into one dword.
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);  // [b0.0, b1.0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);  // [0, 0, b2.0, b3.0]
+  return lo | hi;
+}
+
+// 4x4 byte transpose inside each quad of lanes (DPP): lane j holds bytes B[j][0..3] and
+// receives B[0..3][j].
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t v, int j) {
+  const uint32_t p = dpp_u32(v, 1);                                              // lane j ^ 2
+  const uint32_t t = __builtin_amdgcn_perm(p, v, (j & 2) ? 0x03020706u : 0x05040100u);
+  const uint32_t q = dpp_u32(t, 0);                                              // lane j ^ 1
+  return __builtin_amdgcn_perm(q, t, (j & 1) ? 0x03070105u : 0x06020400u);
+}
+
+// The same transpose across the four 16-lane rows (row r holds B[r][0..3], receives B[0..3][r]).
+// v_permlane32_swap on two copies of v returns (value of row r & 1, value of row r | 2) in that
+// order; v_permlane16_swap returns (value of row r & ~1, value of row r | 1).
+__device__ __forceinline__ uint32_t row_transpose(uint32_t v, int r) {
+  const auto a = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t t = __builtin_amdgcn_perm(a[1], a[0], (r & 2) ? 0x07060302u : 0x05040100u);
+  const auto b = __builtin_amdgcn_permlane16_swap(t, t, false, false);
+  return __builtin_amdgcn_perm(b[1], b[0], (r & 1) ? 0x07030501u : 0x06020400u);
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
@@ -67,11 +118,10 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
   __shared__ __align__(16) float part[kBlockTokens][kPartStride];  // per row / column: 16 partial pairs
-  __shared__ __align__(16) float rfl[kBlockTokens];                // 2^-rho, token order
+  __shared__ __align__(16) float rfl[kBlockTokens];                // 2^-rho / sqrt(128), token order
   __shared__ __align__(16) float cfl[kHeadDim];                    // 2^-gamma, chan_slot order
-  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim]; // 1/s and -z/s of each group
+  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim]; // rounding FMA of each group
   __shared__ __align__(16) float mul_c[kHeadDim];                  // means for centred fallback
-  __shared__ __align__(16) uint8_t codes[kBlockTokens * kHeadDim]; // staged codes, one byte each
 
   const int tile = blockIdx.x;
   const bool is_v = tile & 1;
@@ -87,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
   const size_t tstride = static_cast<size_t>(hkv) * kHeadDim;
   const uint16_t* src = (is_v ? vin : kin) + (static_cast<size_t>(blk) * kBlockTokens * hkv + head) * kHeadDim;
 
-  // ---- 1. rotation: R = X H / sqrt(128) --------------------------------------
+  // ---- 1. rotation: R' = X H (unnormalised) ------------------------------------
   float R[8][8];
   {
     f16x8 xa[2][4];
@@ -97,29 +147,29 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       for (int gi = 0; gi < 4; ++gi)
         xa[mt][gi] = *reinterpret_cast<const f16x8*>(src + static_cast<size_t>(32 * w + 16 * mt + n) * tstride +
                                                       32 * gi + 8 * g);
-    f16x8 hb[2];
+    // H32 block: B[k][col] = (-1)^popcount(k & o), input index k = 8g + i, output o = 2n + hh;
+    // hbn = -hb for the H4 entries that are -1
+    f16x8 hb[2], hbn[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        hb[hh][i] = (__popc((8 * g + i) & (16 * hh + n)) & 1) ? static_cast<_Float16>(-1.0f)
-                                                              : static_cast<_Float16>(1.0f);
+      for (int i = 0; i < 8; ++i) {
+        const bool neg = __popc((8 * g + i) & (2 * n + hh)) & 1;
+        hb[hh][i] = neg ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
+        hbn[hh][i] = neg ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+      }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 d0 = mfma16x16x32(xa[mt][0], hb[hh], z);
-        f32x4 d1 = mfma16x16x32(xa[mt][1], hb[hh], z);
-        f32x4 d2 = mfma16x16x32(xa[mt][2], hb[hh], z);
-        f32x4 d3 = mfma16x16x32(xa[mt][3], hb[hh], z);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = d0[r] + d1[r], b = d0[r] - d1[r], c = d2[r] + d3[r], e = d2[r] - d3[r];
-          R[4 * mt + r][0 + hh] = (a + c) * kInvSqrt128;
-          R[4 * mt + r][2 + hh] = (b + e) * kInvSqrt128;
-          R[4 * mt + r][4 + hh] = (a - c) * kInvSqrt128;
-          R[4 * mt + r][6 + hh] = (b - e) * kInvSqrt128;
+        for (int h4 = 0; h4 < 4; ++h4) {
+          // output chunk h4 = sum over input chunks gi of H4[gi][h4] * (X_gi H32)
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) d = mfma16x16x32(xa[mt][gi], (__popc(gi & h4) & 1) ? hbn[hh] : hb[hh], d);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) R[4 * mt + r][2 * h4 + hh] = d[r];
         }
       }
     }
@@ -132,19 +182,20 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
 
   // ---- 2. log2-variance normalisation, rows then columns, kNormIters times --
   // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes).
+  // rf = 2^-rho / sqrt(128) multiplies the unnormalised R' (so R' rf = R 2^-rho).
   const int t_red = tid >> 1, hf = tid & 1;
-  float rho_t = 0.f, rf_t = 1.f;   // normaliser of row t_red
-  float gam_c = 0.f, cf_c = 1.f;   // normaliser of column c_red (= t_red)
+  float rho_t = 0.f, rf_t = kInvSqrt128;  // normaliser of row t_red
+  float gam_c = 0.f, cf_c = 1.f;          // normaliser of column c_red (= t_red)
   float rf[8], cf[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    rf[k] = 1.f;
+    rf[k] = kInvSqrt128;
     cf[k] = 1.f;
   }
   constexpr float inv128 = 1.0f / 128.0f;
 
   for (int it = 0; it < kNormIters; ++it) {
-    // ---------------- row pass: moments over channels of R * cf -------------
+    // ---------------- row pass: moments over channels of R' * cf ------------
     {
       float c2[8];
 #pragma unroll
@@ -161,38 +212,45 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       }
     }
     __syncthreads();
-    float2 m = reduce_pairs(part[t_red], hf);
-    float mu = m.x * inv128, ey2 = m.y * inv128;
-    float var = fmaf(-mu, mu, ey2);
-    if (__syncthreads_or(!(var >= 0.5f * ey2))) {
-      // centred second moment for the whole pass
-      if (hf == 0) mul_c[t_red] = mu;
-      __syncthreads();
+    {
+      const float2 m = reduce_pairs(part[t_red], hf);
+      const float mu = m.x * inv128, ey2 = m.y * inv128;
+      float var = fmaf(-mu, mu, ey2);
+      float rho_new = rho_t + 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
+      float rf_new = ex2(-rho_new) * kInvSqrt128;
+      if (hf == 0) rfl[t_red] = rf_new;
+      if (__syncthreads_or(!(var >= 0.5f * ey2))) {
+        // centred second moment for the whole pass
+        if (hf == 0) mul_c[t_red] = mu;
+        __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float mi = mul_c[tok_of(w, g, i)];
-        float q = 0.f;
+        for (int i = 0; i < 8; ++i) {
+          const float mi = mul_c[tok_of(w, g, i)];
+          float q = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float d = fmaf(R[i][c], cf[c], -mi);
-          q = fmaf(d, d, q);
+          for (int c = 0; c < 8; ++c) {
+            const float d = fmaf(R[i][c], cf[c], -mi);
+            q = fmaf(d, d, q);
+          }
+          *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
         }
-        *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
+        __syncthreads();
+        var = reduce_pairs(part[t_red], hf).x * inv128;
+        rho_new = rho_t + 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
+        rf_new = ex2(-rho_new) * kInvSqrt128;
+        if (hf == 0) rfl[t_red] = rf_new;
+        __syncthreads();
       }
-      __syncthreads();
-      var = reduce_pairs(part[t_red], hf).x * inv128;
+      rho_t = rho_new;
+      rf_t = rf_new;
     }
-    rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
-    rf_t = ex2(-rho_t);
-    if (hf == 0) rfl[t_red] = rf_t;
-    __syncthreads();
     {
       const float4 a = *reinterpret_cast<const float4*>(&rfl[32 * w + 4 * g]);
       const float4 b = *reinterpret_cast<const float4*>(&rfl[32 * w + 16 + 4 * g]);
       rf[0] = a.x; rf[1] = a.y; rf[2] = a.z; rf[3] = a.w;
       rf[4] = b.x; rf[5] = b.y; rf[6] = b.z; rf[7] = b.w;
     }
-    // ---------------- column pass: moments over tokens of R * rf ------------
+    // ---------------- column pass: moments over tokens of R' * rf -----------
     {
       float r2[8];
 #pragma unroll
@@ -209,33 +267,39 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       }
     }
     __syncthreads();
-    m = reduce_pairs(part[t_red], hf);
-    mu = m.x * inv128;
-    ey2 = m.y * inv128;
-    var = fmaf(-mu, mu, ey2);
-    if (__syncthreads_or(!(var >= 0.5f * ey2))) {
-      if (hf == 0) mul_c[chan_slot(t_red)] = mu;
-      __syncthreads();
-      const float4 ma = *reinterpret_cast<const float4*>(&mul_c[8 * n]);
-      const float4 mb = *reinterpret_cast<const float4*>(&mul_c[8 * n + 4]);
-      const float mc[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+    {
+      const float2 m = reduce_pairs(part[t_red], hf);
+      const float mu = m.x * inv128, ey2 = m.y * inv128;
+      float var = fmaf(-mu, mu, ey2);
+      float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
+      float cf_new = ex2(-gam_new);
+      if (hf == 0) cfl[chan_slot(t_red)] = cf_new;
+      if (__syncthreads_or(!(var >= 0.5f * ey2))) {
+        if (hf == 0) mul_c[chan_slot(t_red)] = mu;
+        __syncthreads();
+        const float4 ma = *reinterpret_cast<const float4*>(&mul_c[8 * n]);
+        const float4 mb = *reinterpret_cast<const float4*>(&mul_c[8 * n + 4]);
+        const float mc[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float q = 0.f;
+        for (int c = 0; c < 8; ++c) {
+          float q = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float d = fmaf(R[i][c], rf[i], -mc[c]);
-          q = fmaf(d, d, q);
+          for (int i = 0; i < 8; ++i) {
+            const float d = fmaf(R[i][c], rf[i], -mc[c]);
+            q = fmaf(d, d, q);
+          }
+          *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
         }
-        *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
+        __syncthreads();
+        var = reduce_pairs(part[t_red], hf).x * inv128;
+        gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
+        cf_new = ex2(-gam_new);
+        if (hf == 0) cfl[chan_slot(t_red)] = cf_new;
+        __syncthreads();
       }
-      __syncthreads();
-      var = reduce_pairs(part[t_red], hf).x * inv128;
+      gam_c = gam_new;
+      cf_c = cf_new;
     }
-    gam_c += 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
-    cf_c = ex2(-gam_c);
-    if (hf == 0) cfl[chan_slot(t_red)] = cf_c;
-    __syncthreads();
     {
       const float4 a = *reinterpret_cast<const float4*>(&cfl[8 * n]);
       const float4 b = *reinterpret_cast<const float4*>(&cfl[8 * n + 4]);
@@ -243,12 +307,6 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       cf[4] = b.x; cf[5] = b.y; cf[6] = b.z; cf[7] = b.w;
     }
   }
-
-  // Normalised values N = R * 2^-rho * 2^-gamma (in place).
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) R[i][c] = R[i][c] * rf[i] * cf[c];
 
   uint8_t* page_base = is_v ? v_pool + (static_cast<size_t>(page) * hkv + head) * kVPageBytes
                             : k_pool + (static_cast<size_t>(page) * hkv + head) * kKPageBytes;
@@ -258,12 +316,18 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
     reinterpret_cast<float*>(meta + kMetaGamma)[t_red] = gam_c;
   }
 
-  // ---- 3. per-group min/max, fp16 scale and zero, round to nearest ----------
-  // Codes come out of u + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
+  // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
+  // M = R' times the normaliser across the group axis; N = M times the group's own
+  // normaliser (positive), so the group's min and max of N are those of M scaled, and
+  // that factor is folded into the rounding FMA.  Codes come out of
+  // clamp(u, 0, L) + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
   constexpr float kRoundMagic = 12582912.0f;
-  constexpr uint32_t kMagicBits = 0x4B400000u;
   if (!is_v) {
     // key groups: one channel over the 128 tokens, 16 levels
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) R[i][c] *= rf[i];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float a = R[0][c], b = R[0][c];
@@ -284,8 +348,8 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
         mn = fminf(mn, fminf(v.x, v.z));
         mx = fmaxf(mx, fmaxf(v.y, v.w));
       }
-      mn = fminf(mn, dpp_xor1(mn));
-      mx = fmaxf(mx, dpp_xor1(mx));
+      mn = mul_rn(fminf(mn, dpp_xor1(mn)), cf_c);
+      mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), cf_c);
       const uint32_t sb = float_to_half_bits((mx - mn) / 15.0f);
       const uint32_t zb = float_to_half_bits(mn);
       const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
@@ -293,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       if (hf == 0) {
         reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
         reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
-        mul_a[chan_slot(t_red)] = inv;
+        mul_a[chan_slot(t_red)] = cf_c * inv;
         mul_b[chan_slot(t_red)] = -zf * inv;
       }
     }
@@ -304,18 +368,31 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
     const float4 b1 = *reinterpret_cast<const float4*>(&mul_b[8 * n + 4]);
     const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
     const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
+    // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
+    const int j = n & 3, q = n >> 2;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int ch = chan_of(n, c);
+    for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float u = fmaf(R[i][c], qa[c], qb[c]) + kRoundMagic;
-        const uint32_t bits = min(max(__float_as_uint(u), kMagicBits), kMagicBits + 15u);
-        codes[tok_of(w, g, i) * kHeadDim + ch] = static_cast<uint8_t>(bits);
+      for (int h4 = 0; h4 < 4; ++h4) {
+        uint32_t by[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int i = 4 * ih + y;
+          const float ulo = fminf(fmaxf(fmaf(R[i][2 * h4], qa[2 * h4], qb[2 * h4]), 0.f), 15.f) + kRoundMagic;
+          const float uhi = fminf(fmaxf(fmaf(R[i][2 * h4 + 1], qa[2 * h4 + 1], qb[2 * h4 + 1]), 0.f), 15.f) + kRoundMagic;
+          by[y] = __float_as_uint(ulo) | (__float_as_uint(uhi) << 4);
+        }
+        const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
+        *reinterpret_cast<uint32_t*>(page_base + tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q) = word;
       }
     }
   } else {
     // value groups: one token over the 128 channels, 4 levels
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) R[i][c] *= cf[c];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float a = R[i][0], b = R[i][0];
@@ -336,8 +413,8 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
         mn = fminf(mn, fminf(v.x, v.z));
         mx = fmaxf(mx, fmaxf(v.y, v.w));
       }
-      mn = fminf(mn, dpp_xor1(mn));
-      mx = fmaxf(mx, dpp_xor1(mx));
+      mn = mul_rn(fminf(mn, dpp_xor1(mn)), rf_t);
+      mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), rf_t);
       const uint32_t sb = float_to_half_bits((mx - mn) / 3.0f);
       const uint32_t zb = float_to_half_bits(mn);
       const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
@@ -345,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       if (hf == 0) {
         reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
         reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
-        mul_a[t_red] = inv;
+        mul_a[t_red] = rf_t * inv;
         mul_b[t_red] = -zf * inv;
       }
     }
@@ -359,58 +436,28 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
       qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
       qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
     }
+    // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
+    // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
+    // of unit u: bytes 8w + 4ih .. +3 of that channel.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = tok_of(w, g, i);
+    for (int u = 0; u < 4; ++u) {
+      uint32_t by[4];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float u = fmaf(R[i][c], qa[i], qb[i]) + kRoundMagic;
-        const uint32_t bits = min(max(__float_as_uint(u), kMagicBits), kMagicBits + 3u);
-        codes[chan_of(n, c) * kBlockTokens + t] = static_cast<uint8_t>(bits);
+      for (int y = 0; y < 4; ++y) {
+        const int c = 2 * u + (y >> 1), ih = y & 1;
+        uint32_t b = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int i = 4 * ih + k;
+          const float v = fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), 3.f) + kRoundMagic;
+          b = k == 0 ? __float_as_uint(v) : (b | (__float_as_uint(v) << (2 * k)));
+        }
+        by[y] = b;
       }
+      const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
+      const int c = 2 * u + (g >> 1), ih = g & 1;
+      *reinterpret_cast<uint32_t*>(page_base + chan_of(n, c) * 32 + 8 * w + 4 * ih) = word;
     }
-  }
-  __syncthreads();
-
-  // ---- 4. pack codes and store ---------------------------------------------
-  if (!is_v) {
-    // K: token t = tid/2, channels 64*(tid%2) .. +63 -> 32 bytes, two nibbles per byte
-    const int t = tid >> 1;
-    const u32x4* srcv = reinterpret_cast<const u32x4*>(codes + t * kHeadDim + 64 * hf);
-    u32x4 o[2];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const u32x4 x = srcv[q4];
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t v = x[e];  // four codes, one per byte
-        pk[e] = (v & 0xFu) | ((v >> 4) & 0xF0u) | (((v >> 16) & 0xFu) << 8) | (((v >> 20) & 0xF0u) << 8);
-      }
-      o[q4 >> 1][(q4 & 1) * 2 + 0] = pk[0] | (pk[1] << 16);
-      o[q4 >> 1][(q4 & 1) * 2 + 1] = pk[2] | (pk[3] << 16);
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(page_base + t * 64 + 32 * hf);
-    dst[0] = o[0];
-    dst[1] = o[1];
-  } else {
-    // V: channel c = tid/2, tokens 64*(tid%2) .. +63 -> 16 bytes, four codes per byte
-    const int c = tid >> 1;
-    const u32x4* srcv = reinterpret_cast<const u32x4*>(codes + c * kBlockTokens + 64 * hf);
-    u32x4 o;
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const u32x4 x = srcv[q4];
-      uint32_t word = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t v = x[e];
-        const uint32_t byte = (v & 3u) | ((v >> 6) & 0xCu) | ((v >> 12) & 0x30u) | ((v >> 18) & 0xC0u);
-        word |= byte << (8 * e);
-      }
-      o[q4] = word;
-    }
-    *reinterpret_cast<u32x4*>(page_base + c * 32 + 16 * hf) = o;
   }
 }
 

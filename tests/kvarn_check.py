@@ -51,6 +51,13 @@ class TileStats:
                    self.code_maxdiff, self.cond_mismatch, self.sz_exact, 2 * self.groups, self.sz_maxulp,
                    self.norm_maxerr))
 
+    def merge(self, other: "TileStats") -> None:
+        for key in ("codes", "code_mismatch", "cond_mismatch", "groups", "sz_exact", "tiles"):
+            setattr(self, key, getattr(self, key) + getattr(other, key))
+        self.code_maxdiff = max(self.code_maxdiff, other.code_maxdiff)
+        self.sz_maxulp = max(self.sz_maxulp, other.sz_maxulp)
+        self.norm_maxerr = max(self.norm_maxerr, other.norm_maxerr)
+
     def check(self):
         assert self.code_maxdiff <= 1, self.summary()
         assert self.code_mismatch <= CODE_MISMATCH_FRACTION * self.codes, self.summary()

@@ -65,8 +65,12 @@ def compare_quantize(k_host, v_host, kp_host, vp_host, pages, tiles):
     for blk, h in tiles:
         p = int(pages[blk])
         sl = slice(128 * blk, 128 * blk + 128)
-        chk.compare_tile(stats, k_host[sl, h, :], kp_host[p, h].tobytes(), False)
-        chk.compare_tile(stats, v_host[sl, h, :], vp_host[p, h].tobytes(), True)
+        for is_v, host, pool in ((False, k_host, kp_host), (True, v_host, vp_host)):
+            one = chk.TileStats()
+            chk.compare_tile(one, host[sl, h, :], pool[p, h].tobytes(), is_v)
+            if one.code_maxdiff > 1 or one.sz_maxulp > 1 or one.norm_maxerr > chk.NORM_TOL:
+                say("  bad tile: block %d head %d %s: %s" % (blk, h, "V" if is_v else "K", one.summary()))
+            stats.merge(one)
     say("  " + stats.summary())
     stats.check()
     return stats
