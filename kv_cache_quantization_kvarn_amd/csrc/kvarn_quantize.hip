@@ -75,6 +75,12 @@ __device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
   return hf ? make_float2(a2 + a, b2 + b) : make_float2(a + a2, b + b2);
 }
 
+// Orders LDS accesses between lanes of one wave (LDS operations of a wave complete in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Rounded product that the compiler may not fuse into a later add: the group range is a
 // difference of two such products, and contracting one of them into an FMA would turn an
 // exactly constant group (max == min) into a range of one rounding error, of either sign.
@@ -117,11 +123,17 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
                                                          const int32_t* __restrict__ dst_pages,
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
-  __shared__ __align__(16) float part[kBlockTokens][kPartStride];  // per row / column: 16 partial pairs
-  __shared__ __align__(16) float rfl[kBlockTokens];                // 2^-rho / sqrt(128), token order
-  __shared__ __align__(16) float cfl[kHeadDim];                    // 2^-gamma, chan_slot order
-  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim]; // rounding FMA of each group
-  __shared__ __align__(16) float mul_c[kHeadDim];                  // means for centred fallback
+  // Row partials (indexed by token) are written and read only by the wave that owns the token;
+  // column partials (indexed by channel) are written by every wave.  Separate arrays let a wave
+  // run its next row pass while others still reduce a column pass.
+  __shared__ __align__(16) float part_row[kBlockTokens][kPartStride];  // per token: 16 partial pairs
+  __shared__ __align__(16) float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
+  __shared__ __align__(16) float rfl[kBlockTokens];                    // 2^-rho / sqrt(128), token order
+  __shared__ __align__(16) float cfl[kHeadDim];                        // 2^-gamma, chan_slot order
+  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim];     // rounding FMA of each group
+  __shared__ __align__(16) float mul_c[kHeadDim];                      // column means for the centred fallback
+  __shared__ __align__(16) float mul_r[kBlockTokens];                  // row means for the centred fallback
+  __shared__ int recenter[2];                                          // column-pass fallback flag, by parity
 
   const int tile = blockIdx.x;
   const bool is_v = tile & 1;
@@ -194,8 +206,14 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
   }
   constexpr float inv128 = 1.0f / 128.0f;
 
+  if (tid == 0) {
+    recenter[0] = 0;
+    recenter[1] = 0;
+  }
   for (int it = 0; it < kNormIters; ++it) {
     // ---------------- row pass: moments over channels of R' * cf ------------
+    // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
+    // the wave (no workgroup barrier) is enough.
     {
       float c2[8];
 #pragma unroll
@@ -208,42 +226,37 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
           s1 = fmaf(R[i][c], cf[c], s1);
           s2 = fmaf(P[i][c], c2[c], s2);
         }
-        *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
+        *reinterpret_cast<float2*>(&part_row[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
       }
     }
-    __syncthreads();
+    wave_lds_sync();
     {
-      const float2 m = reduce_pairs(part[t_red], hf);
+      const float2 m = reduce_pairs(part_row[t_red], hf);
       const float mu = m.x * inv128, ey2 = m.y * inv128;
       float var = fmaf(-mu, mu, ey2);
-      float rho_new = rho_t + 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
-      float rf_new = ex2(-rho_new) * kInvSqrt128;
-      if (hf == 0) rfl[t_red] = rf_new;
-      if (__syncthreads_or(!(var >= 0.5f * ey2))) {
-        // centred second moment for the whole pass
-        if (hf == 0) mul_c[t_red] = mu;
-        __syncthreads();
+      if (__builtin_amdgcn_ballot_w64(!(var >= 0.5f * ey2)) != 0) {
+        // centred second moment for every token of this wave
+        if (hf == 0) mul_r[t_red] = mu;
+        wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float mi = mul_c[tok_of(w, g, i)];
+          const float mi = mul_r[tok_of(w, g, i)];
           float q = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const float d = fmaf(R[i][c], cf[c], -mi);
             q = fmaf(d, d, q);
           }
-          *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
+          *reinterpret_cast<float2*>(&part_row[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
         }
-        __syncthreads();
-        var = reduce_pairs(part[t_red], hf).x * inv128;
-        rho_new = rho_t + 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
-        rf_new = ex2(-rho_new) * kInvSqrt128;
-        if (hf == 0) rfl[t_red] = rf_new;
-        __syncthreads();
+        wave_lds_sync();
+        var = reduce_pairs(part_row[t_red], hf).x * inv128;
       }
-      rho_t = rho_new;
-      rf_t = rf_new;
+      rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
+      rf_t = ex2(-rho_t) * kInvSqrt128;
+      if (hf == 0) rfl[t_red] = rf_t;
     }
+    wave_lds_sync();
     {
       const float4 a = *reinterpret_cast<const float4*>(&rfl[32 * w + 4 * g]);
       const float4 b = *reinterpret_cast<const float4*>(&rfl[32 * w + 16 + 4 * g]);
@@ -270,11 +283,16 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
     {
       const float2 m = reduce_pairs(part[t_red], hf);
       const float mu = m.x * inv128, ey2 = m.y * inv128;
-      float var = fmaf(-mu, mu, ey2);
-      float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
-      float cf_new = ex2(-gam_new);
-      if (hf == 0) cfl[chan_slot(t_red)] = cf_new;
-      if (__syncthreads_or(!(var >= 0.5f * ey2))) {
+      const float var = fmaf(-mu, mu, ey2);
+      const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
+      if (hf == 0) cfl[chan_slot(t_red)] = ex2(-gam_new);
+      // any column whose one-sweep variance could have lost digits redoes the pass centred;
+      // the flag of the next pass is cleared here (every read of it happened before this
+      // pass's first barrier)
+      if (!(var >= 0.5f * ey2)) recenter[it & 1] = 1;
+      if (tid == 0) recenter[(it + 1) & 1] = 0;
+      __syncthreads();
+      if (recenter[it & 1]) {
         if (hf == 0) mul_c[chan_slot(t_red)] = mu;
         __syncthreads();
         const float4 ma = *reinterpret_cast<const float4*>(&mul_c[8 * n]);
@@ -291,14 +309,15 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
           *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
         }
         __syncthreads();
-        var = reduce_pairs(part[t_red], hf).x * inv128;
-        gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
-        cf_new = ex2(-gam_new);
-        if (hf == 0) cfl[chan_slot(t_red)] = cf_new;
+        const float cvar = reduce_pairs(part[t_red], hf).x * inv128;
+        gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
+        cf_c = ex2(-gam_c);
+        if (hf == 0) cfl[chan_slot(t_red)] = cf_c;
         __syncthreads();
+      } else {
+        gam_c = gam_new;
+        cf_c = ex2(-gam_new);
       }
-      gam_c = gam_new;
-      cf_c = cf_new;
     }
     {
       const float4 a = *reinterpret_cast<const float4*>(&cfl[8 * n]);
