@@ -27,7 +27,7 @@ constexpr int kVPage = 5632;
 constexpr int kMaxGroup = 8;
 constexpr int kPartFloats = 128 + 2;
 constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
-constexpr long kTargetGroups = 512;    // workgroups (4 waves each) for one pass over the chip at 2 waves/SIMD
+constexpr long kTargetGroups = 768;    // workgroups (4 waves each): one pass over 256 CUs at 3 workgroups per CU
 constexpr long kMaxPagesPerSplit = 32;
 
 thread_local std::string g_last_error;

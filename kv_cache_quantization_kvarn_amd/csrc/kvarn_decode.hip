@@ -43,8 +43,8 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kPartStride = kHeadDim + 2;  // o[128], m, l per (split, query head)
 constexpr int kCoefStride = 68;            // dwords per coefficient column (64 slots + pad)
-constexpr int kPageList = 64;              // page ids of a split staged in LDS (longer splits read the table)
 constexpr int kMaxSplits = 64;             // the host plan never exceeds this many splits per (sequence, KV head)
+constexpr int kQLaneStride = 20;           // floats per lane row of q~ (16 used; 20 keeps float4 reads conflict-free)
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -88,19 +88,17 @@ __device__ __forceinline__ void value_codes(uint32_t w, uint32_t mag4, uint32_t 
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Split two fp32 values into packed fp16 hi and lo parts, both rounded to nearest even
-// (v_cvt_pk_f16_f32, which keeps fp16 subnormals; the round-toward-zero packing
-// instruction flushes them, and a flushed lo part biases every sum it enters).  The
-// residual x - hi is exact in fp32, so hi + lo carries about 22 significant bits.
-// The empty asm pins a and b as rounded fp32 values: otherwise the compiler may fuse the
-// caller's product into a mixed-precision FMA for one of the two uses of hi (rounding the
-// exact product to fp16 once) and not for the other, and at an fp32 rounding tie the two
-// hi values differ by one fp16 ulp, which hi + lo then carries as an error.
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  asm("" : "+v"(a), "+v"(b));
-  const f16x2 h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
-  const f16x2 l = {static_cast<_Float16>(a - static_cast<float>(h[0])),
-                   static_cast<_Float16>(b - static_cast<float>(h[1]))};
+// Split the products x0*y0 and x1*y1 into packed fp16 hi and lo parts.  hi is the nearest fp16
+// of the fp32 product (v_cvt_pk_f16_f32 rounds to nearest even and keeps fp16 subnormals; the
+// round-toward-zero packing instruction flushes them, and a flushed lo part biases every sum it
+// enters); lo is the nearest fp16 of the exact residual x*y - hi (one v_fma_mix each), so
+// hi + lo carries about 22 significant bits.  hi is pinned by the empty asm so that the value
+// stored and the value subtracted are the same one.
+__device__ __forceinline__ void split_prod(float x0, float y0, float x1, float y1, uint32_t& hi, uint32_t& lo) {
+  f16x2 h = {static_cast<_Float16>(x0 * y0), static_cast<_Float16>(x1 * y1)};
+  asm("" : "+v"(h));
+  const f16x2 l = {static_cast<_Float16>(__builtin_fmaf(x0, y0, -static_cast<float>(h[0]))),
+                   static_cast<_Float16>(__builtin_fmaf(x1, y1, -static_cast<float>(h[1])))};
   hi = __builtin_bit_cast(uint32_t, h);
   lo = __builtin_bit_cast(uint32_t, l);
 }
@@ -202,7 +200,7 @@ __device__ void lds_fwht(float (*v)[kHeadDim], int rows) {
   }
 }
 
-struct WaveLds {
+struct __align__(16) WaveLds {
   uint32_t coef[16][kCoefStride];  // key-side B operand: [column][slot] packed fp16 pairs
   float pk[kHeadDim];              // 2^rho (K) / key page scale, per token
   float fv[kHeadDim];              // 2^rho s (V) * value page scale, per token
@@ -257,8 +255,8 @@ __device__ __forceinline__ void load_page(PageRegs& P, int page, int num_pages, 
 
 // Per-wave state carried across pages.
 struct WaveState {
-  float q0[kMaxGroup], q1[kMaxGroup];  // rotated, scaled query at this lane's two coefficient slots
-  float qmax;                          // max |q0|, |q1| over the wave and the heads
+  const float* ql;                     // rotated, scaled query at this lane's two slots: [h] and [8 + h]
+  float qmax;                          // max over the heads of |q~| at every slot
   float m_run, l_run;                  // online softmax of this lane's head (log2 units)
   float acc[8][4];                     // o (rotated basis, hi or lo column) of channels 16mt + 4g + r
 };
@@ -288,19 +286,26 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   // the key offsets of this lane's two slots: 64 for nibbles 1 and 5 of a dword, else 16
   const _Float16 off = (lane & 3) == 1 ? static_cast<_Float16>(64.0f) : static_cast<_Float16>(16.0f);
   const f16x2 offp = {off, off};
+  float q0[kMaxGroup], q1[kMaxGroup];
+  {
+    const float4* qv = reinterpret_cast<const float4*>(__builtin_assume_aligned(S.ql, 16));
+    const float4 a = qv[0], b = qv[1], c = qv[2], d = qv[3];
+    q0[0] = a.x; q0[1] = a.y; q0[2] = a.z; q0[3] = a.w; q0[4] = b.x; q0[5] = b.y; q0[6] = b.z; q0[7] = b.w;
+    q1[0] = c.x; q1[1] = c.y; q1[2] = c.z; q1[3] = c.w; q1[4] = d.x; q1[5] = d.y; q1[6] = d.z; q1[7] = d.w;
+  }
   float bp[kMaxGroup];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h < G) {
       uint32_t hi, lo;
-      split_pair(S.q0[h] * e0s, S.q1[h] * e1s, hi, lo);
+      split_prod(q0[h], e0s, q1[h], e1s, hi, lo);
       L.coef[h][lane] = hi;
       L.coef[8 + h][lane] = lo;
       // offset contribution of exactly the fp16 coefficients the matrix cores use
       const float aoff = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo), offp,
                                                 __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi), offp, 0.f, false),
                                                 false);
-      bp[h] = fmaf(-inv_sa, aoff, fmaf(S.q0[h], f0, S.q1[h] * f1));
+      bp[h] = fmaf(-inv_sa, aoff, fmaf(q0[h], f0, q1[h] * f1));
     } else {
       bp[h] = 0.f;
     }
@@ -333,59 +338,67 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     cb[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&L.coef[n][16 * g + 4 * ks]));
-  float s[8][4];
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    f32x4 d = {kinit, kinit, kinit, kinit};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) d = mfma16x16x32(key_codes(P.kc[mt][ks], mag16, mag64), cb[ks], d);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s[mt][r] = d[r] + dpp<kDppXor8>(d[r]);
-  }
-  // this lane keeps tokens 32g + 16*lo_col + 4mt' + r (mt' = 0..3)
+  // M-tiles mt and mt + 4 give this lane's tokens of the hi and lo halves; lanes 0-7 of a row
+  // keep tile mt, lanes 8-15 tile mt + 4 (tokens 32g + 16*lo_col + 4mt + r)
   float sm[4][4];
   float mloc = -INFINITY;
   const float* pkp = &L.pk[32 * g + 16 * lo_col];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
+    f32x4 da = {kinit, kinit, kinit, kinit}, db = da;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      da = mfma16x16x32(key_codes(P.kc[mt][ks], mag16, mag64), cb[ks], da);
+      db = mfma16x16x32(key_codes(P.kc[mt + 4][ks], mag16, mag64), cb[ks], db);
+    }
     const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
     const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sm[mt][r] = pkv[r] * sel_lo(s[mt][r], s[mt + 4][r]);
+      const float sa = da[r] + dpp<kDppXor8>(da[r]);
+      const float sb = db[r] + dpp<kDppXor8>(db[r]);
+      sm[mt][r] = pkv[r] * sel_lo(sa, sb);
       mloc = fmaxf(mloc, sm[mt][r]);
     }
   }
   mloc = head_max(mloc);
   const float m_new = fmaxf(S.m_run, mloc);
   const float alpha = ex2(S.m_run - m_new);
+  // o needs rescaling only if some head of the wave has a new maximum (alpha is exactly 1 otherwise)
+  if (__builtin_amdgcn_ballot_w64(m_new != S.m_run) != 0) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.acc[mt][r] *= alpha;
+  }
   S.m_run = m_new;
 
   // ---- softmax weights, value-side B operand -------------------------------
   const float* fvp = &L.fv[32 * g + 16 * lo_col];
   const float* zvp = &L.zv[32 * g + 16 * lo_col];
   float lsum = 0.f, usum = 0.f, wev = 0.f, wod = 0.f;
-  float wv[4][4];
+  float pv[4][4], fvv[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const float4 f4 = *reinterpret_cast<const float4*>(fvp + 4 * mt);
     const float4 z4 = *reinterpret_cast<const float4*>(zvp + 4 * mt);
-    const float fvv[4] = {f4.x, f4.y, f4.z, f4.w};
+    fvv[mt][0] = f4.x; fvv[mt][1] = f4.y; fvv[mt][2] = f4.z; fvv[mt][3] = f4.w;
     const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = ex2(sm[mt][r] - m_new);
       lsum += p;
       usum = fmaf(p, zvv[r], usum);
-      wv[mt][r] = p * fvv[r];
+      pv[mt][r] = p;
     }
   }
-  // pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
+  // w_t = p_t * fv_t; pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
   uint32_t own_hi[2][4], own_lo[2][4];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split_pair(wv[hf][j], wv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
+    for (int j = 0; j < 4; ++j)
+      split_prod(pv[hf][j], fvv[hf][j], pv[hf + 2][j], fvv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
   // value offsets (4 for even tokens, 16 for odd) of exactly the fp16 weights used
   {
     const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
@@ -436,24 +449,33 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
     const float4 gs4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
     const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(S.acc[mt][r], alpha, d[r] * gsv[r]);
+    for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(d[r], gsv[r], S.acc[mt][r]);
   }
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 2) void decode_kernel(
+__global__ __launch_bounds__(256, 3) void decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
     int hq, int hkv, int blocks_per_split, int max_splits, float scale_log2, float* __restrict__ out,
     float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
-  __shared__ float qs[kMaxGroup][kHeadDim];
-  __shared__ WaveLds wl[kWaves];
+  // The per-wave page buffers are live only inside the page loop; the query transform before it
+  // and the merge after it share their memory.
+  __shared__ union __align__(16) {
+    WaveLds wl[kWaves];
+    struct {
+      float qs[kMaxGroup][kHeadDim];             // query / output rows for the transforms
+      float wacc[kWaves][kMaxGroup][kHeadDim];   // per-wave o
+      float mw[kMaxGroup][kMaxSplits];           // split maxima
+    } t;
+  } U;
+  __shared__ __align__(16) float qlane[64][kQLaneStride];  // q~ of each lane's slots, shared by the waves
   __shared__ float wm[kWaves][kMaxGroup], wls[kWaves][kMaxGroup];
-  __shared__ float wacc[kWaves][kMaxGroup][kHeadDim];
-  __shared__ float mw[kMaxGroup][kMaxSplits];
-  __shared__ int pg[kPageList];
   __shared__ int last_flag;
+  float (*qs)[kHeadDim] = U.t.qs;
+  float (*wacc)[kMaxGroup][kHeadDim] = U.t.wacc;
+  float (*mw)[kMaxSplits] = U.t.mw;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = hq / hkv;
@@ -477,8 +499,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   const int blk0 = split * blocks_per_split;
   const int cnt = min(nblk, blk0 + blocks_per_split) - blk0;
   const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + blk0;
-  const bool listed = cnt <= kPageList;
-  if (listed && tid < cnt) pg[tid] = bt[tid];
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, known uniform: page ids load as scalars
 
   // ---- rotated, scaled query ------------------------------------------------
   const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   }
   __syncthreads();
   lds_fwht(qs, kMaxGroup);
-  WaveLds& L = wl[w];
+  WaveLds& L = U.wl[w];
   // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
   const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
   uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
@@ -497,11 +518,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   float qmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
-    S.q0[h] = qs[h][ch0] * (kInvSqrt128 * scale_log2);
-    S.q1[h] = qs[h][ch0 + 4] * (kInvSqrt128 * scale_log2);
-    qmax = fmaxf(qmax, fmaxf(fabsf(S.q0[h]), fabsf(S.q1[h])));
+    const float a = qs[h][ch0] * (kInvSqrt128 * scale_log2);
+    const float b = qs[h][ch0 + 4] * (kInvSqrt128 * scale_log2);
+    if (w == 0) {
+      qlane[lane][h] = a;
+      qlane[lane][kMaxGroup + h] = b;
+    }
+    qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
   }
   S.qmax = wave_max_all(qmax);
+  S.ql = &qlane[lane][0];
+  __syncthreads();  // qlane complete; qs (aliased by the page buffers) no longer read
   S.m_run = -INFINITY;
   S.l_run = 0.f;
 #pragma unroll
@@ -512,12 +539,16 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
 
   // ---- pages of this wave: w, w + 4, ... ---------------------------------------
-  bool bad_page = num_pages <= 0 && w < cnt;  // with no pages every id is out of range
-  for (int i = w; i < cnt && num_pages > 0; i += kWaves) {
+  bool bad_page = false;
+  for (int i = wu; i < cnt; i += kWaves) {
+    const int page = bt[i];
+    if (page < 0 || page >= num_pages) {
+      bad_page = true;
+      continue;
+    }
     PageRegs A;
-    load_page(A, listed ? pg[i] : bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
-    bad_page |= !A.ok;
-    if (A.ok) process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+    load_page(A, page, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+    process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
   }
   if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
 
@@ -526,6 +557,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S.acc[mt][r] += dpp<kDppXor8>(S.acc[mt][r]);
+  __syncthreads();  // every wave is out of the page loop: its page buffers may be reused
   if (!lo_col && hd < G) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
