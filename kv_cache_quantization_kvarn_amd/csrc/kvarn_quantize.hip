@@ -1,6 +1,6 @@
 // KVarN block quantisation kernel for gfx950.
 //
-// One workgroup (4 waves) quantises one tile: a 128-token x 128-channel fp16
+// A workgroup (4 waves) quantises one tile at a time: a 128-token x 128-channel fp16
 // block of one KV head of K or V (KVarN blog post, section "KVarN Nasıl
 // Çalışır?"): Hadamard rotation along channels, four row/column passes of
 // log2-variance normalisation, per-group min/max, round to nearest, packing.
@@ -34,6 +34,12 @@
 // codes are packed in registers (two nibbles or four 2-bit codes per byte),
 // transposed across lanes into whole dwords of the page (DPP within a quad for
 // keys, v_permlane16/32_swap across rows for values) and stored directly.
+//
+// Scheduling.  Workgroups are persistent, one per compute unit for keys and one for values, and
+// walk their tiles with a fixed stride.  The input of the next tile is fetched while the current
+// one is normalised; the page stores go through a buffer resource (size zero for an invalid page)
+// so that every tile issues the same memory operations and the wait for the prefetched input
+// never has to drain the stores.
 #include "kvarn_common.h"
 
 namespace kvarn {
@@ -116,367 +122,420 @@ __device__ __forceinline__ uint32_t row_transpose(uint32_t v, int r) {
   return __builtin_amdgcn_perm(b[1], b[0], (r & 1) ? 0x07030501u : 0x06020400u);
 }
 
-}  // namespace
 
-__global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
-                                                         const uint16_t* __restrict__ vin, int hkv,
-                                                         const int32_t* __restrict__ dst_pages,
-                                                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
-                                                         int num_pages, uint32_t* __restrict__ flags) {
-  // Row partials (indexed by token) are written and read only by the wave that owns the token;
-  // column partials (indexed by channel) are written by every wave.  Separate arrays let a wave
-  // run its next row pass while others still reduce a column pass.
-  __shared__ __align__(16) float part_row[kBlockTokens][kPartStride];  // per token: 16 partial pairs
-  __shared__ __align__(16) float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
-  __shared__ __align__(16) float rfl[kBlockTokens];                    // 2^-rho / sqrt(128), token order
-  __shared__ __align__(16) float cfl[kHeadDim];                        // 2^-gamma, chan_slot order
-  __shared__ __align__(16) float mul_a[kHeadDim], mul_b[kHeadDim];     // rounding FMA of each group
-  __shared__ __align__(16) float mul_c[kHeadDim];                      // column means for the centred fallback
-  __shared__ __align__(16) float mul_r[kBlockTokens];                  // row means for the centred fallback
-  __shared__ int recenter[2];                                          // column-pass fallback flag, by parity
+// Shared memory of one quantising workgroup.  Row partials (indexed by token) are written and
+// read only by the wave that owns the token; column partials (indexed by channel) are written by
+// every wave.  Separate arrays let a wave run its next row pass while others still reduce a
+// column pass.
+struct QuantLds {
+  float part_row[kBlockTokens][kPartStride];  // per token: 16 partial pairs
+  float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
+  float rfl[kBlockTokens];                    // 2^-rho / sqrt(128), token order
+  float cfl[kHeadDim];                        // 2^-gamma, chan_slot order
+  float mul_a[kHeadDim], mul_b[kHeadDim];     // rounding FMA of each group
+  float mul_c[kHeadDim];                      // column means for the centred fallback
+  float mul_r[kBlockTokens];                  // row means for the centred fallback
+  int recenter[2];                            // column-pass fallback flag, by parity
+};
 
-  const int tile = blockIdx.x;
-  const bool is_v = tile & 1;
-  const int bh = tile >> 1;
-  const int blk = bh / hkv;
-  const int head = bh - blk * hkv;
-  const int page = dst_pages[blk];
-  if (page < 0 || page >= num_pages) {
-    if (threadIdx.x == 0 && flags) atomicOr(flags, kFlagBadPage);
-    return;
-  }
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+// Stores into a page go through a buffer resource.  An invalid destination page gets a resource
+// of size zero, so the hardware drops its stores and every tile issues the same memory
+// operations (the prefetch of the next tile then needs no conservative wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_resource(uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
+// fp16 input of tile `tile` (block tile / hkv, head tile % hkv) in the MFMA A-operand layout:
+// xa[mt][gi] = X[32w + 16mt + n][32gi + 8g .. +7].
+__device__ __forceinline__ void load_tile(f16x8 (&xa)[2][4], const uint16_t* __restrict__ in, int tile, int hkv,
+                                          int w, int n, int g) {
+  const int blk = tile / hkv;
+  const int head = tile - blk * hkv;
   const size_t tstride = static_cast<size_t>(hkv) * kHeadDim;
-  const uint16_t* src = (is_v ? vin : kin) + (static_cast<size_t>(blk) * kBlockTokens * hkv + head) * kHeadDim;
+  const uint16_t* src = in + (static_cast<size_t>(blk) * kBlockTokens * hkv + head) * kHeadDim;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+      xa[mt][gi] = *reinterpret_cast<const f16x8*>(src + static_cast<size_t>(32 * w + 16 * mt + n) * tstride +
+                                                    32 * gi + 8 * g);
+}
 
-  // ---- 1. rotation: R' = X H (unnormalised) ------------------------------------
-  float R[8][8];
-  {
-    f16x8 xa[2][4];
+// R' = X H for the wave's 32 tokens (unnormalised): output chunk h4 of each 16-token tile is the
+// sum over input chunks gi of H4[gi][h4] * (X_gi H32), with H4's -1 entries taken by hbn = -hb.
+__device__ __forceinline__ void rotate(const f16x8 (&xa)[2][4], const f16x8 (&hb)[2], const f16x8 (&hbn)[2],
+                                       float (&R)[8][8], float (&P)[8][8]) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi)
-        xa[mt][gi] = *reinterpret_cast<const f16x8*>(src + static_cast<size_t>(32 * w + 16 * mt + n) * tstride +
-                                                      32 * gi + 8 * g);
-    // H32 block: B[k][col] = (-1)^popcount(k & o), input index k = 8g + i, output o = 2n + hh;
-    // hbn = -hb for the H4 entries that are -1
-    f16x8 hb[2], hbn[2];
+    for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int h4 = 0; h4 < 4; ++h4) {
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool neg = __popc((8 * g + i) & (2 * n + hh)) & 1;
-        hb[hh][i] = neg ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
-        hbn[hh][i] = neg ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-      }
+        for (int gi = 0; gi < 4; ++gi) d = mfma16x16x32(xa[mt][gi], (__popc(gi & h4) & 1) ? hbn[hh] : hb[hh], d);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-          // output chunk h4 = sum over input chunks gi of H4[gi][h4] * (X_gi H32)
-          f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int gi = 0; gi < 4; ++gi) d = mfma16x16x32(xa[mt][gi], (__popc(gi & h4) & 1) ? hbn[hh] : hb[hh], d);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) R[4 * mt + r][2 * h4 + hh] = d[r];
-        }
+        for (int r = 0; r < 4; ++r) R[4 * mt + r][2 * h4 + hh] = d[r];
       }
     }
   }
-  float P[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int c = 0; c < 8; ++c) P[i][c] = R[i][c] * R[i][c];
+}
 
-  // ---- 2. log2-variance normalisation, rows then columns, kNormIters times --
-  // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes).
-  // rf = 2^-rho / sqrt(128) multiplies the unnormalised R' (so R' rf = R 2^-rho).
+// All tiles of one kind (keys or values) owned by this workgroup: tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...  The next tile's input is loaded while the current one is
+// normalised and packed.
+template <bool kIsV>
+__device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, int hkv, int tiles,
+                                               const int32_t* __restrict__ dst_pages, uint8_t* __restrict__ pool,
+                                               int num_pages, uint32_t* __restrict__ flags, QuantLds& s) {
+  constexpr int kPageBytes = kIsV ? kVPageBytes : kKPageBytes;
+  constexpr int kCodeBytes = kIsV ? kVCodeBytes : kKCodeBytes;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes) = t_red;
+  // the two threads of a pair (hf = 0, 1) compute identical values.
   const int t_red = tid >> 1, hf = tid & 1;
-  float rho_t = 0.f, rf_t = kInvSqrt128;  // normaliser of row t_red
-  float gam_c = 0.f, cf_c = 1.f;          // normaliser of column c_red (= t_red)
-  float rf[8], cf[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    rf[k] = kInvSqrt128;
-    cf[k] = 1.f;
-  }
   constexpr float inv128 = 1.0f / 128.0f;
 
-  if (tid == 0) {
-    recenter[0] = 0;
-    recenter[1] = 0;
-  }
-  for (int it = 0; it < kNormIters; ++it) {
-    // ---------------- row pass: moments over channels of R' * cf ------------
-    // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
-    // the wave (no workgroup barrier) is enough.
-    {
-      float c2[8];
+  // H32 block: B[k][col] = (-1)^popcount(k & o), input index k = 8g + i, output o = 2n + hh;
+  // hbn = -hb for the H4 entries that are -1
+  f16x8 hb[2], hbn[2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) c2[c] = cf[c] * cf[c];
+  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          s1 = fmaf(R[i][c], cf[c], s1);
-          s2 = fmaf(P[i][c], c2[c], s2);
-        }
-        *reinterpret_cast<float2*>(&part_row[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const bool neg = __popc((8 * g + i) & (2 * n + hh)) & 1;
+      hb[hh][i] = neg ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
+      hbn[hh][i] = neg ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
     }
-    wave_lds_sync();
-    {
-      const float2 m = reduce_pairs(part_row[t_red], hf);
-      const float mu = m.x * inv128, ey2 = m.y * inv128;
-      float var = fmaf(-mu, mu, ey2);
-      if (__builtin_amdgcn_ballot_w64(!(var >= 0.5f * ey2)) != 0) {
-        // centred second moment for every token of this wave
-        if (hf == 0) mul_r[t_red] = mu;
-        wave_lds_sync();
+
+  if (tid == 0) {
+    s.recenter[0] = 0;
+    s.recenter[1] = 0;
+  }
+  bool bad = false;
+  const int stride = static_cast<int>(gridDim.x);
+  int tile = blockIdx.x;
+  // software pipeline: the loop body packs tile `tile`, then rotates the next tile (whose input
+  // arrived meanwhile) and fetches the one after it; past the end, the last tile stands in
+  f16x8 xa[2][4];
+  float R[8][8], P[8][8];
+  load_tile(xa, in, tile, hkv, w, n, g);
+  rotate(xa, hb, hbn, R, P);
+  load_tile(xa, in, tile + stride < tiles ? tile + stride : tile, hkv, w, n, g);
+  for (; tile < tiles; tile += stride) {
+    const int blk = tile / hkv;
+    const int head = tile - blk * hkv;
+    const int page = dst_pages[blk];
+    const bool ok = page >= 0 && page < num_pages;
+    bad |= !ok;
+    const __amdgpu_buffer_rsrc_t dst =
+        page_resource(pool + (static_cast<size_t>(ok ? page : 0) * hkv + head) * kPageBytes, ok ? kPageBytes : 0);
+
+    // ---- 2. log2-variance normalisation, rows then columns, kNormIters times --
+    // rf = 2^-rho / sqrt(128) multiplies the unnormalised R' (so R' rf = R 2^-rho).
+    float rho_t = 0.f, rf_t = kInvSqrt128;  // normaliser of row t_red
+    float gam_c = 0.f, cf_c = 1.f;          // normaliser of column c_red (= t_red)
+    float rf[8], cf[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      rf[k] = kInvSqrt128;
+      cf[k] = 1.f;
+    }
+    for (int it = 0; it < kNormIters; ++it) {
+      // ---------------- row pass: moments over channels of R' * cf ------------
+      // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
+      // the wave (no workgroup barrier) is enough.
+      {
+        float c2[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) c2[c] = cf[c] * cf[c];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float mi = mul_r[tok_of(w, g, i)];
-          float q = 0.f;
+          float s1 = 0.f, s2 = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const float d = fmaf(R[i][c], cf[c], -mi);
-            q = fmaf(d, d, q);
+            s1 = fmaf(R[i][c], cf[c], s1);
+            s2 = fmaf(P[i][c], c2[c], s2);
           }
-          *reinterpret_cast<float2*>(&part_row[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
+          *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
         }
-        wave_lds_sync();
-        var = reduce_pairs(part_row[t_red], hf).x * inv128;
       }
-      rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
-      rf_t = ex2(-rho_t) * kInvSqrt128;
-      if (hf == 0) rfl[t_red] = rf_t;
-    }
-    wave_lds_sync();
-    {
-      const float4 a = *reinterpret_cast<const float4*>(&rfl[32 * w + 4 * g]);
-      const float4 b = *reinterpret_cast<const float4*>(&rfl[32 * w + 16 + 4 * g]);
-      rf[0] = a.x; rf[1] = a.y; rf[2] = a.z; rf[3] = a.w;
-      rf[4] = b.x; rf[5] = b.y; rf[6] = b.z; rf[7] = b.w;
-    }
-    // ---------------- column pass: moments over tokens of R' * rf -----------
-    {
-      float r2[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) r2[i] = rf[i] * rf[i];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          s1 = fmaf(R[i][c], rf[i], s1);
-          s2 = fmaf(P[i][c], r2[i], s2);
-        }
-        *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(s1, s2);
-      }
-    }
-    __syncthreads();
-    {
-      const float2 m = reduce_pairs(part[t_red], hf);
-      const float mu = m.x * inv128, ey2 = m.y * inv128;
-      const float var = fmaf(-mu, mu, ey2);
-      const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
-      if (hf == 0) cfl[chan_slot(t_red)] = ex2(-gam_new);
-      // any column whose one-sweep variance could have lost digits redoes the pass centred;
-      // the flag of the next pass is cleared here (every read of it happened before this
-      // pass's first barrier)
-      if (!(var >= 0.5f * ey2)) recenter[it & 1] = 1;
-      if (tid == 0) recenter[(it + 1) & 1] = 0;
-      __syncthreads();
-      if (recenter[it & 1]) {
-        if (hf == 0) mul_c[chan_slot(t_red)] = mu;
-        __syncthreads();
-        const float4 ma = *reinterpret_cast<const float4*>(&mul_c[8 * n]);
-        const float4 mb = *reinterpret_cast<const float4*>(&mul_c[8 * n + 4]);
-        const float mc[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          float q = 0.f;
+      wave_lds_sync();
+      {
+        const float2 m = reduce_pairs(s.part_row[t_red], hf);
+        const float mu = m.x * inv128, ey2 = m.y * inv128;
+        float var = fmaf(-mu, mu, ey2);
+        if (__builtin_amdgcn_ballot_w64(!(var >= 0.5f * ey2)) != 0) {
+          // centred second moment for every token of this wave
+          if (hf == 0) s.mul_r[t_red] = mu;
+          wave_lds_sync();
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float d = fmaf(R[i][c], rf[i], -mc[c]);
-            q = fmaf(d, d, q);
+            const float mi = s.mul_r[tok_of(w, g, i)];
+            float q = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float d = fmaf(R[i][c], cf[c], -mi);
+              q = fmaf(d, d, q);
+            }
+            *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
           }
-          *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
+          wave_lds_sync();
+          var = reduce_pairs(s.part_row[t_red], hf).x * inv128;
         }
+        rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
+        rf_t = ex2(-rho_t) * kInvSqrt128;
+        if (hf == 0) s.rfl[t_red] = rf_t;
+      }
+      wave_lds_sync();
+      {
+        const float4 a = *reinterpret_cast<const float4*>(&s.rfl[32 * w + 4 * g]);
+        const float4 b = *reinterpret_cast<const float4*>(&s.rfl[32 * w + 16 + 4 * g]);
+        rf[0] = a.x; rf[1] = a.y; rf[2] = a.z; rf[3] = a.w;
+        rf[4] = b.x; rf[5] = b.y; rf[6] = b.z; rf[7] = b.w;
+      }
+      // ---------------- column pass: moments over tokens of R' * rf -----------
+      {
+        float r2[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r2[i] = rf[i] * rf[i];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            s1 = fmaf(R[i][c], rf[i], s1);
+            s2 = fmaf(P[i][c], r2[i], s2);
+          }
+          *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(s1, s2);
+        }
+      }
+      __syncthreads();
+      {
+        const float2 m = reduce_pairs(s.part[t_red], hf);
+        const float mu = m.x * inv128, ey2 = m.y * inv128;
+        const float var = fmaf(-mu, mu, ey2);
+        const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
+        if (hf == 0) s.cfl[chan_slot(t_red)] = ex2(-gam_new);
+        // any column whose one-sweep variance could have lost digits redoes the pass centred;
+        // the flag of the next pass is cleared here (every read of it happened before this
+        // pass's first barrier)
+        if (!(var >= 0.5f * ey2)) s.recenter[it & 1] = 1;
+        if (tid == 0) s.recenter[(it + 1) & 1] = 0;
         __syncthreads();
-        const float cvar = reduce_pairs(part[t_red], hf).x * inv128;
-        gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
-        cf_c = ex2(-gam_c);
-        if (hf == 0) cfl[chan_slot(t_red)] = cf_c;
-        __syncthreads();
-      } else {
-        gam_c = gam_new;
-        cf_c = ex2(-gam_new);
+        if (s.recenter[it & 1]) {
+          if (hf == 0) s.mul_c[chan_slot(t_red)] = mu;
+          __syncthreads();
+          const float4 ma = *reinterpret_cast<const float4*>(&s.mul_c[8 * n]);
+          const float4 mb = *reinterpret_cast<const float4*>(&s.mul_c[8 * n + 4]);
+          const float mc[8] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float q = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float d = fmaf(R[i][c], rf[i], -mc[c]);
+              q = fmaf(d, d, q);
+            }
+            *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
+          }
+          __syncthreads();
+          const float cvar = reduce_pairs(s.part[t_red], hf).x * inv128;
+          gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
+          cf_c = ex2(-gam_c);
+          if (hf == 0) s.cfl[chan_slot(t_red)] = cf_c;
+          __syncthreads();
+        } else {
+          gam_c = gam_new;
+          cf_c = ex2(-gam_new);
+        }
+      }
+      {
+        const float4 a = *reinterpret_cast<const float4*>(&s.cfl[8 * n]);
+        const float4 b = *reinterpret_cast<const float4*>(&s.cfl[8 * n + 4]);
+        cf[0] = a.x; cf[1] = a.y; cf[2] = a.z; cf[3] = a.w;
+        cf[4] = b.x; cf[5] = b.y; cf[6] = b.z; cf[7] = b.w;
       }
     }
-    {
-      const float4 a = *reinterpret_cast<const float4*>(&cfl[8 * n]);
-      const float4 b = *reinterpret_cast<const float4*>(&cfl[8 * n + 4]);
-      cf[0] = a.x; cf[1] = a.y; cf[2] = a.z; cf[3] = a.w;
-      cf[4] = b.x; cf[5] = b.y; cf[6] = b.z; cf[7] = b.w;
-    }
-  }
 
-  uint8_t* page_base = is_v ? v_pool + (static_cast<size_t>(page) * hkv + head) * kVPageBytes
-                            : k_pool + (static_cast<size_t>(page) * hkv + head) * kKPageBytes;
-  uint8_t* meta = page_base + (is_v ? kVCodeBytes : kKCodeBytes);
-  if (hf == 0) {
-    reinterpret_cast<float*>(meta + kMetaRho)[t_red] = rho_t;
-    reinterpret_cast<float*>(meta + kMetaGamma)[t_red] = gam_c;
-  }
+    // normalisers: rho of row t_red from one thread of the pair, gamma of column t_red from the other
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hf ? gam_c : rho_t), dst,
+                                          kCodeBytes + (hf ? kMetaGamma : kMetaRho) + 4 * t_red, 0, 0);
 
-  // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
-  // M = R' times the normaliser across the group axis; N = M times the group's own
-  // normaliser (positive), so the group's min and max of N are those of M scaled, and
-  // that factor is folded into the rounding FMA.  Codes come out of
-  // clamp(u, 0, L) + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
-  constexpr float kRoundMagic = 12582912.0f;
-  if (!is_v) {
-    // key groups: one channel over the 128 tokens, 16 levels
+    // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
+    // M = R' times the normaliser across the group axis; N = M times the group's own
+    // normaliser (positive), so the group's min and max of N are those of M scaled, and
+    // that factor is folded into the rounding FMA.  Codes come out of
+    // clamp(u, 0, L) + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
+    constexpr float kRoundMagic = 12582912.0f;
+    if constexpr (!kIsV) {
+      // key groups: one channel over the 128 tokens, 16 levels
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int c = 0; c < 8; ++c) R[i][c] *= rf[i];
+        for (int c = 0; c < 8; ++c) R[i][c] *= rf[i];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float a = R[0][c], b = R[0][c];
+      for (int c = 0; c < 8; ++c) {
+        float a = R[0][c], b = R[0][c];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        a = fminf(a, R[i][c]);
-        b = fmaxf(b, R[i][c]);
+        for (int i = 1; i < 8; ++i) {
+          a = fminf(a, R[i][c]);
+          b = fmaxf(b, R[i][c]);
+        }
+        *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(a, b);
       }
-      *reinterpret_cast<float2*>(&part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(a, b);
-    }
-    __syncthreads();
-    {
-      const float4* p = reinterpret_cast<const float4*>(part[t_red] + 16 * hf);
-      float mn = INFINITY, mx = -INFINITY;
+      __syncthreads();
+      {
+        const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
+        float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = p[k];
-        mn = fminf(mn, fminf(v.x, v.z));
-        mx = fmaxf(mx, fmaxf(v.y, v.w));
+        for (int k = 0; k < 4; ++k) {
+          const float4 v = p[k];
+          mn = fminf(mn, fminf(v.x, v.z));
+          mx = fmaxf(mx, fmaxf(v.y, v.w));
+        }
+        mn = mul_rn(fminf(mn, dpp_xor1(mn)), cf_c);
+        mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), cf_c);
+        const uint32_t sb = float_to_half_bits((mx - mn) / 15.0f);
+        const uint32_t zb = float_to_half_bits(mn);
+        const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+        const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+        // scale from one thread of the pair, zero from the other
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
+                                              kCodeBytes + (hf ? kMetaZero : kMetaScale) + 2 * t_red, 0, 0);
+        if (hf == 0) {
+          s.mul_a[chan_slot(t_red)] = cf_c * inv;
+        } else {
+          s.mul_b[chan_slot(t_red)] = -zf * inv;
+        }
       }
-      mn = mul_rn(fminf(mn, dpp_xor1(mn)), cf_c);
-      mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), cf_c);
-      const uint32_t sb = float_to_half_bits((mx - mn) / 15.0f);
-      const uint32_t zb = float_to_half_bits(mn);
-      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
-      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-      if (hf == 0) {
-        reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
-        reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
-        mul_a[chan_slot(t_red)] = cf_c * inv;
-        mul_b[chan_slot(t_red)] = -zf * inv;
+      __syncthreads();
+      const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[8 * n]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[8 * n + 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[8 * n]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[8 * n + 4]);
+      const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
+      // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
+      const int j = n & 3, q = n >> 2;
+#pragma unroll
+      for (int ih = 0; ih < 2; ++ih) {
+#pragma unroll
+        for (int h4 = 0; h4 < 4; ++h4) {
+          uint32_t by[4];
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            const int i = 4 * ih + y;
+            const float ulo = fminf(fmaxf(fmaf(R[i][2 * h4], qa[2 * h4], qb[2 * h4]), 0.f), 15.f) + kRoundMagic;
+            const float uhi =
+                fminf(fmaxf(fmaf(R[i][2 * h4 + 1], qa[2 * h4 + 1], qb[2 * h4 + 1]), 0.f), 15.f) + kRoundMagic;
+            by[y] = __float_as_uint(ulo) | (__float_as_uint(uhi) << 4);
+          }
+          const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
+          __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q, 0, 0);
+        }
       }
-    }
-    __syncthreads();
-    const float4 a0 = *reinterpret_cast<const float4*>(&mul_a[8 * n]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&mul_a[8 * n + 4]);
-    const float4 b0 = *reinterpret_cast<const float4*>(&mul_b[8 * n]);
-    const float4 b1 = *reinterpret_cast<const float4*>(&mul_b[8 * n + 4]);
-    const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
-    // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
-    const int j = n & 3, q = n >> 2;
+    } else {
+      // value groups: one token over the 128 channels, 4 levels
 #pragma unroll
-    for (int ih = 0; ih < 2; ++ih) {
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int h4 = 0; h4 < 4; ++h4) {
+        for (int c = 0; c < 8; ++c) R[i][c] *= cf[c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float a = R[i][0], b = R[i][0];
+#pragma unroll
+        for (int c = 1; c < 8; ++c) {
+          a = fminf(a, R[i][c]);
+          b = fmaxf(b, R[i][c]);
+        }
+        *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+      }
+      __syncthreads();
+      {
+        const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
+        float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 v = p[k];
+          mn = fminf(mn, fminf(v.x, v.z));
+          mx = fmaxf(mx, fmaxf(v.y, v.w));
+        }
+        mn = mul_rn(fminf(mn, dpp_xor1(mn)), rf_t);
+        mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), rf_t);
+        const uint32_t sb = float_to_half_bits((mx - mn) / 3.0f);
+        const uint32_t zb = float_to_half_bits(mn);
+        const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+        const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
+                                              kCodeBytes + (hf ? kMetaZero : kMetaScale) + 2 * t_red, 0, 0);
+        if (hf == 0) {
+          s.mul_a[t_red] = rf_t * inv;
+        } else {
+          s.mul_b[t_red] = -zf * inv;
+        }
+      }
+      __syncthreads();
+      float qa[8], qb[8];
+      {
+        const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[32 * w + 4 * g]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[32 * w + 16 + 4 * g]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[32 * w + 4 * g]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[32 * w + 16 + 4 * g]);
+        qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
+        qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
+      }
+      // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
+      // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
+      // of unit u: bytes 8w + 4ih .. +3 of that channel.
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         uint32_t by[4];
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-          const int i = 4 * ih + y;
-          const float ulo = fminf(fmaxf(fmaf(R[i][2 * h4], qa[2 * h4], qb[2 * h4]), 0.f), 15.f) + kRoundMagic;
-          const float uhi = fminf(fmaxf(fmaf(R[i][2 * h4 + 1], qa[2 * h4 + 1], qb[2 * h4 + 1]), 0.f), 15.f) + kRoundMagic;
-          by[y] = __float_as_uint(ulo) | (__float_as_uint(uhi) << 4);
+          const int c = 2 * u + (y >> 1), ih = y & 1;
+          uint32_t b = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int i = 4 * ih + k;
+            const float v = fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), 3.f) + kRoundMagic;
+            b = k == 0 ? __float_as_uint(v) : (b | (__float_as_uint(v) << (2 * k)));
+          }
+          by[y] = b;
         }
-        const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
-        *reinterpret_cast<uint32_t*>(page_base + tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q) = word;
+        const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
+        const int c = 2 * u + (g >> 1), ih = g & 1;
+        __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 32 + 8 * w + 4 * ih, 0, 0);
       }
     }
+    {
+      const int next = tile + stride < tiles ? tile + stride : tile;
+      rotate(xa, hb, hbn, R, P);
+      load_tile(xa, in, next + stride < tiles ? next + stride : next, hkv, w, n, g);
+    }
+  }
+  if (bad && tid == 0 && flags) atomicOr(flags, kFlagBadPage);
+}
+
+}  // namespace
+
+// Persistent quantiser: blockIdx.y selects keys (0) or values (1); every workgroup walks the
+// tiles of that kind with stride gridDim.x.
+__global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
+                                                         const uint16_t* __restrict__ vin, int hkv, int tiles,
+                                                         const int32_t* __restrict__ dst_pages,
+                                                         uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                         int num_pages, uint32_t* __restrict__ flags) {
+  __shared__ __align__(16) QuantLds lds;
+  if (blockIdx.y == 0) {
+    quantize_tiles<false>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
   } else {
-    // value groups: one token over the 128 channels, 4 levels
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) R[i][c] *= cf[c];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float a = R[i][0], b = R[i][0];
-#pragma unroll
-      for (int c = 1; c < 8; ++c) {
-        a = fminf(a, R[i][c]);
-        b = fmaxf(b, R[i][c]);
-      }
-      *reinterpret_cast<float2*>(&part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
-    }
-    __syncthreads();
-    {
-      const float4* p = reinterpret_cast<const float4*>(part[t_red] + 16 * hf);
-      float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 v = p[k];
-        mn = fminf(mn, fminf(v.x, v.z));
-        mx = fmaxf(mx, fmaxf(v.y, v.w));
-      }
-      mn = mul_rn(fminf(mn, dpp_xor1(mn)), rf_t);
-      mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), rf_t);
-      const uint32_t sb = float_to_half_bits((mx - mn) / 3.0f);
-      const uint32_t zb = float_to_half_bits(mn);
-      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
-      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-      if (hf == 0) {
-        reinterpret_cast<uint16_t*>(meta + kMetaScale)[t_red] = static_cast<uint16_t>(sb);
-        reinterpret_cast<uint16_t*>(meta + kMetaZero)[t_red] = static_cast<uint16_t>(zb);
-        mul_a[t_red] = rf_t * inv;
-        mul_b[t_red] = -zf * inv;
-      }
-    }
-    __syncthreads();
-    float qa[8], qb[8];
-    {
-      const float4 a0 = *reinterpret_cast<const float4*>(&mul_a[32 * w + 4 * g]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&mul_a[32 * w + 16 + 4 * g]);
-      const float4 b0 = *reinterpret_cast<const float4*>(&mul_b[32 * w + 4 * g]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&mul_b[32 * w + 16 + 4 * g]);
-      qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
-      qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
-    }
-    // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
-    // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
-    // of unit u: bytes 8w + 4ih .. +3 of that channel.
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint32_t by[4];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int c = 2 * u + (y >> 1), ih = y & 1;
-        uint32_t b = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int i = 4 * ih + k;
-          const float v = fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), 3.f) + kRoundMagic;
-          b = k == 0 ? __float_as_uint(v) : (b | (__float_as_uint(v) << (2 * k)));
-        }
-        by[y] = b;
-      }
-      const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
-      const int c = 2 * u + (g >> 1), ih = g & 1;
-      *reinterpret_cast<uint32_t*>(page_base + chan_of(n, c) * 32 + 8 * w + 4 * ih) = word;
-    }
+    quantize_tiles<true>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
   }
 }
 
@@ -546,9 +605,17 @@ namespace kvarn {
 
 hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
                            void* k_pool, void* v_pool, int num_pages, uint32_t* flags, hipStream_t stream) {
-  const unsigned tiles = 2u * static_cast<unsigned>(n_blocks) * static_cast<unsigned>(hkv);
-  hipLaunchKernelGGL(quantize_kernel, dim3(tiles), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), hkv, dst_pages, static_cast<uint8_t*>(k_pool),
+  const int tiles = n_blocks * hkv;  // per kind
+  if (tiles == 0) return hipSuccess;
+  // one persistent workgroup per compute unit for each of keys and values: two resident per unit
+  int device = 0, cus = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  const int groups = tiles < cus ? tiles : cus;
+  hipLaunchKernelGGL(quantize_kernel, dim3(groups, 2), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), hkv, tiles, dst_pages, static_cast<uint8_t*>(k_pool),
                      static_cast<uint8_t*>(v_pool), num_pages, flags);
   return hipGetLastError();
 }
