@@ -35,8 +35,8 @@
 // transposed across lanes into whole dwords of the page (DPP within a quad for
 // keys, v_permlane16/32_swap across rows for values) and stored directly.
 //
-// Scheduling.  Workgroups are persistent, one per compute unit for keys and one for values, and
-// walk their tiles with a fixed stride.  The input of the next tile is fetched while the current
+// Scheduling.  Workgroups are persistent, two per compute unit; each walks its share of the key
+// tiles and then of the value tiles with a fixed stride.  The input of the next tile is fetched while the current
 // one is normalised; the page stores go through a buffer resource (size zero for an invalid page)
 // so that every tile issues the same memory operations and the wait for the prefetched input
 // never has to drain the stores.
@@ -130,8 +130,8 @@ __device__ __forceinline__ uint32_t row_transpose(uint32_t v, int r) {
 struct QuantLds {
   float part_row[kBlockTokens][kPartStride];  // per token: 16 partial pairs
   float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
-  float rfl[kBlockTokens];                    // 2^-rho / sqrt(128), token order
-  float cfl[kHeadDim];                        // 2^-gamma, chan_slot order
+  float rfl[kBlockTokens], rfl2[kBlockTokens];  // 2^-rho / sqrt(128) and its square, token order
+  float cfl[kHeadDim], cfl2[kHeadDim];          // 2^-gamma and its square, chan_slot order
   float mul_a[kHeadDim], mul_b[kHeadDim];     // rounding FMA of each group
   float mul_c[kHeadDim];                      // column means for the centred fallback
   float mul_r[kBlockTokens];                  // row means for the centred fallback
@@ -239,20 +239,19 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // rf = 2^-rho / sqrt(128) multiplies the unnormalised R' (so R' rf = R 2^-rho).
     float rho_t = 0.f, rf_t = kInvSqrt128;  // normaliser of row t_red
     float gam_c = 0.f, cf_c = 1.f;          // normaliser of column c_red (= t_red)
-    float rf[8], cf[8];
+    float rf[8], cf[8], r2[8], c2[8];  // normalisers of the lane's tokens / channels, and squares
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       rf[k] = kInvSqrt128;
       cf[k] = 1.f;
+      r2[k] = kInvSqrt128 * kInvSqrt128;
+      c2[k] = 1.f;
     }
     for (int it = 0; it < kNormIters; ++it) {
       // ---------------- row pass: moments over channels of R' * cf ------------
       // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
       // the wave (no workgroup barrier) is enough.
       {
-        float c2[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) c2[c] = cf[c] * cf[c];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float s1 = 0.f, s2 = 0.f;
@@ -289,7 +288,11 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         }
         rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
         rf_t = ex2(-rho_t) * kInvSqrt128;
-        if (hf == 0) s.rfl[t_red] = rf_t;
+        if (hf == 0) {
+          s.rfl[t_red] = rf_t;
+        } else {
+          s.rfl2[t_red] = rf_t * rf_t;
+        }
       }
       wave_lds_sync();
       {
@@ -297,12 +300,13 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         const float4 b = *reinterpret_cast<const float4*>(&s.rfl[32 * w + 16 + 4 * g]);
         rf[0] = a.x; rf[1] = a.y; rf[2] = a.z; rf[3] = a.w;
         rf[4] = b.x; rf[5] = b.y; rf[6] = b.z; rf[7] = b.w;
+        const float4 a2 = *reinterpret_cast<const float4*>(&s.rfl2[32 * w + 4 * g]);
+        const float4 b2 = *reinterpret_cast<const float4*>(&s.rfl2[32 * w + 16 + 4 * g]);
+        r2[0] = a2.x; r2[1] = a2.y; r2[2] = a2.z; r2[3] = a2.w;
+        r2[4] = b2.x; r2[5] = b2.y; r2[6] = b2.z; r2[7] = b2.w;
       }
       // ---------------- column pass: moments over tokens of R' * rf -----------
       {
-        float r2[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r2[i] = rf[i] * rf[i];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float s1 = 0.f, s2 = 0.f;
@@ -320,7 +324,12 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         const float mu = m.x * inv128, ey2 = m.y * inv128;
         const float var = fmaf(-mu, mu, ey2);
         const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
-        if (hf == 0) s.cfl[chan_slot(t_red)] = ex2(-gam_new);
+        const float cf_new = ex2(-gam_new);
+        if (hf == 0) {
+          s.cfl[chan_slot(t_red)] = cf_new;
+        } else {
+          s.cfl2[chan_slot(t_red)] = cf_new * cf_new;
+        }
         // any column whose one-sweep variance could have lost digits redoes the pass centred;
         // the flag of the next pass is cleared here (every read of it happened before this
         // pass's first barrier)
@@ -347,11 +356,15 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           const float cvar = reduce_pairs(s.part[t_red], hf).x * inv128;
           gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
           cf_c = ex2(-gam_c);
-          if (hf == 0) s.cfl[chan_slot(t_red)] = cf_c;
+          if (hf == 0) {
+            s.cfl[chan_slot(t_red)] = cf_c;
+          } else {
+            s.cfl2[chan_slot(t_red)] = cf_c * cf_c;
+          }
           __syncthreads();
         } else {
           gam_c = gam_new;
-          cf_c = ex2(-gam_new);
+          cf_c = cf_new;
         }
       }
       {
@@ -359,6 +372,10 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         const float4 b = *reinterpret_cast<const float4*>(&s.cfl[8 * n + 4]);
         cf[0] = a.x; cf[1] = a.y; cf[2] = a.z; cf[3] = a.w;
         cf[4] = b.x; cf[5] = b.y; cf[6] = b.z; cf[7] = b.w;
+        const float4 a2 = *reinterpret_cast<const float4*>(&s.cfl2[8 * n]);
+        const float4 b2 = *reinterpret_cast<const float4*>(&s.cfl2[8 * n + 4]);
+        c2[0] = a2.x; c2[1] = a2.y; c2[2] = a2.z; c2[3] = a2.w;
+        c2[4] = b2.x; c2[5] = b2.y; c2[6] = b2.z; c2[7] = b2.w;
       }
     }
 
@@ -524,19 +541,17 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 
 }  // namespace
 
-// Persistent quantiser: blockIdx.y selects keys (0) or values (1); every workgroup walks the
-// tiles of that kind with stride gridDim.x.
+// Persistent quantiser: every workgroup walks the key tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+// and then the value tiles with the same stride, so all workgroups carry the same mix of the two
+// kinds (a value tile costs more than a key tile).
 __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin, int hkv, int tiles,
                                                          const int32_t* __restrict__ dst_pages,
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
   __shared__ __align__(16) QuantLds lds;
-  if (blockIdx.y == 0) {
-    quantize_tiles<false>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
-  } else {
-    quantize_tiles<true>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
-  }
+  quantize_tiles<false>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
+  quantize_tiles<true>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
 }
 
 // Test / inspection export: rebuild fp32 K^ or V^ of one tile in the original basis.
@@ -607,14 +622,14 @@ hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, 
                            void* k_pool, void* v_pool, int num_pages, uint32_t* flags, hipStream_t stream) {
   const int tiles = n_blocks * hkv;  // per kind
   if (tiles == 0) return hipSuccess;
-  // one persistent workgroup per compute unit for each of keys and values: two resident per unit
+  // two persistent workgroups per compute unit
   int device = 0, cus = 0;
   hipError_t e = hipGetDevice(&device);
   if (e != hipSuccess) return e;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
-  const int groups = tiles < cus ? tiles : cus;
-  hipLaunchKernelGGL(quantize_kernel, dim3(groups, 2), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
+  const int groups = tiles < 2 * cus ? tiles : 2 * cus;
+  hipLaunchKernelGGL(quantize_kernel, dim3(groups), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), hkv, tiles, dst_pages, static_cast<uint8_t*>(k_pool),
                      static_cast<uint8_t*>(v_pool), num_pages, flags);
   return hipGetLastError();
