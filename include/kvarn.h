@@ -118,11 +118,11 @@ size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int3
  * block_table[b, 0 .. seq_lens[b]/128).  The query is rotated by the same
  * Hadamard matrix, so scores equal those of the dequantised cache ("KVarN Nasıl
  * Çalışır?": the rotation is orthonormal and keeps attention scores).
- *   q            fp16 [batch, num_q_heads, 128]
+ *   q            fp16 [batch, num_q_heads, 128], 16-byte aligned
  *   block_table  int32 [batch, max_blocks_per_seq] (device)
  *   seq_lens     int32 [batch] (device), multiples of 128; 0 gives a zero row
  *   softmax_scale  <= 0 selects 1/sqrt(128)
- *   out          fp32 [batch, num_q_heads, 128]
+ *   out          fp32 [batch, num_q_heads, 128], 16-byte aligned
  *   workspace    device bytes, at least kvarn_decode_workspace_bytes(...) */
 kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, const void* k_pool,
                                     const void* v_pool, int32_t num_pages, const int32_t* block_table,

@@ -174,6 +174,9 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
+  if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
   const DecodePlan p = plan_decode(batch, num_kv_heads, mb);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   const float scale_log2 = scale * 1.4426950408889634f;

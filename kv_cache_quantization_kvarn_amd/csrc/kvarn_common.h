@@ -35,6 +35,7 @@ constexpr uint32_t kFlagBadSeqLen = 2u;
 // lanes of a pair.
 constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppXor3 = 0x1B;   // quad_perm [3,2,1,0]
 constexpr int kDppXor7 = 0x141;  // row_half_mirror: lane ^ 7 inside 8 lanes
 constexpr int kDppXor8 = 0x128;  // row_ror:8: lane ^ 8 inside 16 lanes
 constexpr int kDppRor4 = 0x124;  // row_ror:4: lane +- 4 (mod 16) inside 16 lanes (not an involution)

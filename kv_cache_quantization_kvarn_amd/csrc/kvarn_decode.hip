@@ -26,9 +26,12 @@
 // of one query head.  The per-head constants (b and u, offsets removed) enter
 // as the accumulator input of the first product of each chain.
 //
-// Latency: a wave issues the loads of its next page before it computes the
-// current one (two register sets, alternating), so a page's HBM latency
-// overlaps the previous page's arithmetic.
+// Latency: three workgroups (twelve waves) share a compute unit, so one wave's
+// page loads overlap the others' arithmetic; a wave's first page is requested
+// together with the query, before the query transform, which then runs under
+// that page's HBM latency.  Both 128-point transforms (q~ = H q at the start,
+// H o at the end) run in registers, two entries per lane, with DPP and
+// permlane exchanges: no workgroup barrier.
 //
 // Each wave keeps (m, l, o[128]) per head; the four waves merge through LDS,
 // the workgroup writes one partial per split, and the last workgroup of a
@@ -44,6 +47,7 @@ constexpr int kWaves = 4;
 constexpr int kPartStride = kHeadDim + 2;  // o[128], m, l per (split, query head)
 constexpr int kCoefStride = 68;            // dwords per coefficient column (64 slots + pad)
 constexpr int kMaxSplits = 64;             // the host plan never exceeds this many splits per (sequence, KV head)
+static_assert(kMaxSplits <= 64, "the split merge gives every split its own lane");
 constexpr int kQLaneStride = 20;           // floats per lane row of q~ (16 used; 20 keeps float4 reads conflict-free)
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -186,19 +190,44 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// In-LDS 128-point Walsh-Hadamard transform of `rows` vectors (whole workgroup).
-__device__ void lds_fwht(float (*v)[kHeadDim], int rows) {
-  for (int half = 1; half < kHeadDim; half <<= 1) {
-    for (int u = threadIdx.x; u < rows * 64; u += blockDim.x) {
-      const int r = u >> 6, p = u & 63;
-      const int i = (p / half) * 2 * half + (p % half);
-      const float a = v[r][i], b = v[r][i + half];
-      v[r][i] = a + b;
-      v[r][i + half] = a - b;
-    }
-    __syncthreads();
+// In-register 128-point Walsh-Hadamard transform (natural order, unnormalised) of one vector
+// held two entries per lane, x0 = v[2l] and x1 = v[2l + 1].  Index bit 0 is inside the lane;
+// index bit s >= 1 is lane bit s - 1, so stage s pairs lane l with l ^ 2^(s-1): the lane whose
+// bit is clear keeps the sum, the other the difference (partner minus own).
+__device__ __forceinline__ void wave_fwht(float& x0, float& x1, int lane) {
+  {
+    const float a = x0 + x1, b = x0 - x1;
+    x0 = a;
+    x1 = b;
+  }
+  auto dpp_stage = [&](float p0, float p1, int bit) {
+    const float sg = (lane & bit) ? -1.f : 1.f;
+    x0 = fmaf(sg, x0, p0);
+    x1 = fmaf(sg, x1, p1);
+  };
+  dpp_stage(dpp<kDppXor1>(x0), dpp<kDppXor1>(x1), 1);
+  dpp_stage(dpp<kDppXor2>(x0), dpp<kDppXor2>(x1), 2);
+  // lane ^ 4 = (lane ^ 7) ^ 3 inside 8 lanes
+  dpp_stage(dpp<kDppXor3>(dpp<kDppXor7>(x0)), dpp<kDppXor3>(dpp<kDppXor7>(x1)), 4);
+  dpp_stage(dpp<kDppXor8>(x0), dpp<kDppXor8>(x1), 8);
+  // the swaps return (value of the lower partner, value of the upper partner): lower + sign * upper
+  {
+    const float sg = (lane & 16) ? -1.f : 1.f;
+    const auto r0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x0), false, false);
+    const auto r1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x1), __float_as_uint(x1), false, false);
+    x0 = fmaf(sg, __uint_as_float(r0[1]), __uint_as_float(r0[0]));
+    x1 = fmaf(sg, __uint_as_float(r1[1]), __uint_as_float(r1[0]));
+  }
+  {
+    const float sg = (lane & 32) ? -1.f : 1.f;
+    const auto r0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x0), false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x1), __float_as_uint(x1), false, false);
+    x0 = fmaf(sg, __uint_as_float(r0[1]), __uint_as_float(r0[0]));
+    x1 = fmaf(sg, __uint_as_float(r1[1]), __uint_as_float(r1[0]));
   }
 }
+
+__device__ __forceinline__ float wave_sum_all(float x) { return sum_xor32(sum_xor16(row16_sum(x))); }
 
 struct __align__(16) WaveLds {
   uint32_t coef[16][kCoefStride];  // key-side B operand: [column][slot] packed fp16 pairs
@@ -228,6 +257,9 @@ __device__ __forceinline__ void load_page(PageRegs& P, int page, int num_pages, 
                                           int lane, int n, int g, int ch0) {
   P.ok = page >= 0 && page < num_pages;
   const int safe = P.ok ? page : 0;
+  // lane offsets are recomputed for every page (a few integer operations) rather than kept live
+  // across the page loop, where registers are short
+  asm volatile("" : "+v"(lane), "+v"(n), "+v"(g), "+v"(ch0));
   const uint8_t* kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * kKPageBytes;
   const uint8_t* vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * kVPageBytes;
 #pragma unroll
@@ -460,22 +492,18 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
     int hq, int hkv, int blocks_per_split, int max_splits, float scale_log2, float* __restrict__ out,
     float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
-  // The per-wave page buffers are live only inside the page loop; the query transform before it
-  // and the merge after it share their memory.
+  // The per-wave page buffers are live only inside the page loop; before it each wave uses its own
+  // buffer as scratch for the query transform, and the four-wave merge after it reuses the memory.
   __shared__ union __align__(16) {
     WaveLds wl[kWaves];
     struct {
-      float qs[kMaxGroup][kHeadDim];             // query / output rows for the transforms
       float wacc[kWaves][kMaxGroup][kHeadDim];   // per-wave o
-      float mw[kMaxGroup][kMaxSplits];           // split maxima
     } t;
   } U;
   __shared__ __align__(16) float qlane[64][kQLaneStride];  // q~ of each lane's slots, shared by the waves
   __shared__ float wm[kWaves][kMaxGroup], wls[kWaves][kMaxGroup];
   __shared__ int last_flag;
-  float (*qs)[kHeadDim] = U.t.qs;
   float (*wacc)[kMaxGroup][kHeadDim] = U.t.wacc;
-  float (*mw)[kMaxSplits] = U.t.mw;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = hq / hkv;
@@ -501,34 +529,53 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
   const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + blk0;
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, known uniform: page ids load as scalars
 
-  // ---- rotated, scaled query ------------------------------------------------
+  // ---- query loads, then the loads of this wave's first page ----------------
+  // Both are issued before the query transform so that the page's HBM latency overlaps it.  Lane
+  // l takes channels 2l and 2l + 1 of every head (heads past G re-read head 0 and are zeroed).
   const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
-  for (int e = tid; e < kMaxGroup * kHeadDim; e += blockDim.x) {
-    const int h = e >> 7, j = e & 127;
-    qs[h][j] = h < G ? half_bits_to_float(qb[h * kHeadDim + j]) : 0.f;
-  }
-  __syncthreads();
-  lds_fwht(qs, kMaxGroup);
-  WaveLds& L = U.wl[w];
+  uint32_t qraw[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h)
+    qraw[h] = reinterpret_cast<const uint32_t*>(qb + (h < G ? h : 0) * kHeadDim)[lane];
+  __builtin_amdgcn_sched_barrier(0);
   // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
   const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
+  PageRegs A;
+  load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- rotated, scaled query ------------------------------------------------
+  // Every wave transforms all heads itself (in registers) and writes the same values into the
+  // shared per-lane array, so no workgroup barrier is needed; the wave's own page buffer serves as
+  // scratch for the change of layout.
+  WaveLds& L = U.wl[w];
+  float (*qt)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&L.coef[0][0]);  // [kMaxGroup][128]
+  const float qscale = kInvSqrt128 * scale_log2;
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    float x0 = h < G ? half_bits_to_float(qraw[h] & 0xFFFFu) : 0.f;
+    float x1 = h < G ? half_bits_to_float(qraw[h] >> 16) : 0.f;
+    wave_fwht(x0, x1, lane);
+    reinterpret_cast<float2*>(qt[h])[lane] = make_float2(x0 * qscale, x1 * qscale);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
   asm volatile("" : "+v"(mag16), "+v"(mag64), "+v"(mag4));
   WaveState S;
   float qmax = 0.f;
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
-    const float a = qs[h][ch0] * (kInvSqrt128 * scale_log2);
-    const float b = qs[h][ch0 + 4] * (kInvSqrt128 * scale_log2);
-    if (w == 0) {
-      qlane[lane][h] = a;
-      qlane[lane][kMaxGroup + h] = b;
-    }
-    qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(b)));
+    const float a = qt[h][ch0];
+    const float c = qt[h][ch0 + 4];
+    qlane[lane][h] = a;
+    qlane[lane][kMaxGroup + h] = c;
+    qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(c)));
   }
   S.qmax = wave_max_all(qmax);
   S.ql = &qlane[lane][0];
-  __syncthreads();  // qlane complete; qs (aliased by the page buffers) no longer read
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   S.m_run = -INFINITY;
   S.l_run = 0.f;
 #pragma unroll
@@ -540,15 +587,20 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
 
   // ---- pages of this wave: w, w + 4, ... ---------------------------------------
   bool bad_page = false;
-  for (int i = wu; i < cnt; i += kWaves) {
-    const int page = bt[i];
-    if (page < 0 || page >= num_pages) {
+  if (wu < cnt) {
+    if (A.ok) {
+      process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+    } else {
       bad_page = true;
-      continue;
     }
-    PageRegs A;
-    load_page(A, page, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
-    process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+  }
+  for (int i = wu + kWaves; i < cnt; i += kWaves) {
+    load_page(A, bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+    if (A.ok) {
+      process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+    } else {
+      bad_page = true;
+    }
   }
   if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
 
@@ -606,29 +658,43 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
   if (tid == 0) __hip_atomic_store(counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 
   // ---- merge the splits (log-sum-exp) and undo the rotation ---------------
-  for (int e = tid; e < G * kMaxSplits; e += blockDim.x) {
-    const int h = e / kMaxSplits, sp = e % kMaxSplits;
-    mw[h][sp] = sp < nsplit ? load_coherent(pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * kPartStride + kHeadDim)
-                            : -INFINITY;
-  }
-  __syncthreads();
-  for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
-    const int h = e >> 7, j = e & 127;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, mw[h][sp]);
-    float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ms = mw[h][sp];
-      const float wgt = ms == -INFINITY ? 0.f : ex2(ms - mx);
-      const float* pp = pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * kPartStride;
-      num = fmaf(wgt, load_coherent(pp + j), num);
-      den = fmaf(wgt, load_coherent(pp + kHeadDim + 1), den);
+  // Wave w takes heads w and w + 4; lane l holds output channels 2l and 2l + 1, and lane s the
+  // maximum and sum of split s (nsplit <= 64).
+  for (int h = w; h < G; h += kWaves) {
+    const float* ph = pbase + static_cast<size_t>(h) * kPartStride;
+    constexpr size_t kSplitStride = static_cast<size_t>(kMaxGroup) * kPartStride;
+    const int sp = lane < nsplit ? lane : 0;
+    const float ms = load_coherent(ph + sp * kSplitStride + kHeadDim);
+    const float ls = load_coherent(ph + sp * kSplitStride + kHeadDim + 1);
+    const float msv = lane < nsplit ? ms : -INFINITY;
+    const float mx = wave_max_all(msv);
+    const float wgt = msv == -INFINITY ? 0.f : ex2(msv - mx);
+    const float den = wave_sum_all(wgt * (lane < nsplit ? ls : 0.f));
+    float n0 = 0.f, n1 = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      // eight splits at a time, so that their loads are in flight together
+      float2 o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sk = s0 + k < nsplit ? s0 + k : 0;
+        const float* pp = ph + sk * kSplitStride + 2 * lane;
+        o[k] = make_float2(load_coherent(pp), load_coherent(pp + 1));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int src = s0 + k < nsplit ? s0 + k : 0;
+        const float wsrc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src));
+        const float wk = s0 + k < nsplit ? wsrc : 0.f;
+        n0 = fmaf(wk, o[k].x, n0);
+        n1 = fmaf(wk, o[k].y, n1);
+      }
     }
-    qs[h][j] = den > 0.f ? num / den : 0.f;
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    float x0 = n0 * inv, x1 = n1 * inv;
+    wave_fwht(x0, x1, lane);
+    reinterpret_cast<float2*>(out_b + static_cast<size_t>(h) * kHeadDim)[lane] =
+        make_float2(x0 * kInvSqrt128, x1 * kInvSqrt128);
   }
-  __syncthreads();
-  lds_fwht(qs, G);
-  for (int e = tid; e < G * kHeadDim; e += blockDim.x) out_b[e] = qs[e >> 7][e & 127] * kInvSqrt128;
 }
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,

@@ -90,6 +90,9 @@ def test_decode_validation():
     assert decode(cfg, ws=None) == K.KVARN_ERR_WORKSPACE
     assert decode(cfg, ws=ctypes.c_void_p(0x10010)) == K.KVARN_ERR_WORKSPACE  # not 256-byte aligned
     assert decode(cfg, kp=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
+    assert decode(cfg, q=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE   # q not 16-byte aligned
+    assert decode(cfg, out=ctypes.c_void_p(0x1008)) == K.KVARN_ERR_SHAPE  # out not 16-byte aligned
+    assert decode(cfg, npages=0) == K.KVARN_ERR_SHAPE                     # pages referenced, none exist
 
 
 def test_workspace_sizes():
