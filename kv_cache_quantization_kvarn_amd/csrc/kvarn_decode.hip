@@ -505,10 +505,11 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
   __shared__ int last_flag;
   float (*wacc)[kMaxGroup][kHeadDim] = U.t.wacc;
 
-  // The sequence index varies fastest in dispatch order: workgroups go to the XCDs round-robin, so
-  // the XCDs share out sequences (of mixed lengths) rather than split positions (of which the high
-  // ones are empty for all but the longest sequences).  Empty splits also come last.
-  const int b = blockIdx.x, kvh = blockIdx.y, split = blockIdx.z;
+  // Dispatch order is KV head fastest, then sequence, then split.  Workgroups go to the XCDs
+  // round-robin, so consecutive KV heads of one sequence (equal work) land on different XCDs and
+  // every XCD gets the same share of each sequence, whatever the mix of lengths; split positions
+  // (the high ones empty for all but the longest sequences) vary slowest, so empty splits come last.
+  const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = hq / hkv;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int hd = n & 7;
@@ -704,7 +705,7 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, 
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                          int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
                          uint32_t* counters, uint32_t* flags, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3(batch, hkv, max_splits), dim3(256), 0, stream,
+  hipLaunchKernelGGL(decode_kernel, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens, hq, hkv,
                      blocks_per_split, max_splits, scale_log2, out, part, counters, flags);
