@@ -130,6 +130,23 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
                                     int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                     void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
 
+/* The uncompressed baseline on the same harness: decode attention over fp16
+ * K/V pages, for comparison with the packed cache ("KVarN (Varyans Normalize
+ * Edilmiş KV-Cache) Nedir?": the packed cache against FP16 serving).  Same
+ * arguments, plan, workspace (kvarn_decode_workspace_bytes), error model and
+ * output as kvarn_decode_attention, except the pools:
+ *   k_cache, v_cache  fp16 [num_pages, num_kv_heads, 128 tokens, 128 channels],
+ *                     16-byte aligned; page p of KV head g holds the 128 token
+ *                     rows of one block, unrotated and unquantised
+ * No rotation is involved: out[b, h] = softmax(scale * K q) V over the pages.
+ * A page id outside [0, num_pages) sets flag 1 and the page is skipped. */
+size_t kvarn_fp16_page_bytes(const kvarn_config* cfg); /* 32768 per (page, KV head), K or V; 0 for an unsupported config */
+kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q, const void* k_cache,
+                                         const void* v_cache, int32_t num_pages, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
+                                         void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
+
 /* Copy *dev_flags to *host_out after the work queued on `stream` finishes
  * (synchronises the stream). */
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream);

@@ -18,6 +18,10 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, 
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                          int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
                          uint32_t* counters, uint32_t* flags, hipStream_t stream);
+hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_cache, int num_pages,
+                              const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
+                              int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
+                              uint32_t* counters, uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
@@ -84,6 +88,52 @@ kvarn_status launch_status(hipError_t e) {
   if (e == hipSuccess) return KVARN_OK;
   g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(e);
   return KVARN_ERR_LAUNCH;
+}
+
+// Validation and launch shared by the packed decode and the fp16 baseline (same plan, workspace,
+// partials and error model; only the page pools and the kernel differ).
+kvarn_status decode_common(bool fp16_pages, const kvarn_config* cfg, const void* q, const void* k_pool,
+                           const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                           int32_t num_kv_heads, float softmax_scale, float* out, void* workspace, size_t ws_bytes,
+                           uint32_t* dev_flags, void* stream) {
+  kvarn_status s = check_config(cfg);
+  if (s != KVARN_OK) return s;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
+    return fail(KVARN_ERR_SHAPE, "negative or zero size");
+  if (num_q_heads % num_kv_heads != 0) return fail(KVARN_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / num_kv_heads > kMaxGroup)
+    return fail(KVARN_ERR_UNSUPPORTED, "more than 8 query heads per KV head is not supported");
+  if (batch == 0) return KVARN_OK;
+  if (!q || !seq_lens || !out) return fail(KVARN_ERR_NULL, "q, seq_lens or out is NULL");
+  if (max_blocks_per_seq > 0 && (!block_table || !k_pool || !v_pool))
+    return fail(KVARN_ERR_NULL, "block_table or a pool is NULL");
+  if (static_cast<long>(max_blocks_per_seq) * 128 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
+  if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
+  const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
+  const size_t need = workspace_bytes(batch, num_kv_heads, mb);
+  if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
+  if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  const DecodePlan p = plan_decode(batch, num_kv_heads, mb);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  uint32_t* counters = static_cast<uint32_t*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(batch, num_kv_heads));
+  // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
+  const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fp16_pages)
+    return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
+                                                   batch, num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits,
+                                                   scale_log2, out, part, counters, dev_flags, st));
+  return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens, batch,
+                                            num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2,
+                                            out, part, counters, dev_flags, st));
 }
 
 }  // namespace
@@ -155,38 +205,21 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
                                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
                                     int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                     void* workspace, size_t ws_bytes, uint32_t* dev_flags, void* stream) {
-  kvarn_status s = check_config(cfg);
-  if (s != KVARN_OK) return s;
-  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
-    return fail(KVARN_ERR_SHAPE, "negative or zero size");
-  if (num_q_heads % num_kv_heads != 0) return fail(KVARN_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
-  if (num_q_heads / num_kv_heads > kMaxGroup)
-    return fail(KVARN_ERR_UNSUPPORTED, "more than 8 query heads per KV head is not supported");
-  if (batch == 0) return KVARN_OK;
-  if (!q || !seq_lens || !out) return fail(KVARN_ERR_NULL, "q, seq_lens or out is NULL");
-  if (max_blocks_per_seq > 0 && (!block_table || !k_pool || !v_pool))
-    return fail(KVARN_ERR_NULL, "block_table or a pool is NULL");
-  if (static_cast<long>(max_blocks_per_seq) * 128 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
-  if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
-  const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
-  const size_t need = workspace_bytes(batch, num_kv_heads, mb);
-  if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
-    return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
-    return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
-  if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
-  const DecodePlan p = plan_decode(batch, num_kv_heads, mb);
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
-  const float scale_log2 = scale * 1.4426950408889634f;
-  uint32_t* counters = static_cast<uint32_t*>(workspace);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(batch, num_kv_heads));
-  // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
-  const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
-  return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens, batch,
-                                            num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2,
-                                            out, part, counters, dev_flags, static_cast<hipStream_t>(stream)));
+  return decode_common(false, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq, seq_lens, batch,
+                       num_q_heads, num_kv_heads, softmax_scale, out, workspace, ws_bytes, dev_flags, stream);
+}
+
+size_t kvarn_fp16_page_bytes(const kvarn_config* cfg) {
+  return config_ok(cfg) ? static_cast<size_t>(128) * 128 * sizeof(uint16_t) : 0;
+}
+
+kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q, const void* k_cache,
+                                         const void* v_cache, int32_t num_pages, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
+                                         void* workspace, size_t ws_bytes, uint32_t* dev_flags, void* stream) {
+  return decode_common(true, cfg, q, k_cache, v_cache, num_pages, block_table, max_blocks_per_seq, seq_lens, batch,
+                       num_q_heads, num_kv_heads, softmax_scale, out, workspace, ws_bytes, dev_flags, stream);
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

@@ -31,8 +31,8 @@ class kvarn_config(ctypes.Structure):
 
 
 EXPORTS = ("kvarn_config_parse", "kvarn_page_bytes", "kvarn_quantize_blocks", "kvarn_dequantize_blocks",
-           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_read_flags", "kvarn_status_string",
-           "kvarn_last_error")
+           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_fp16_page_bytes",
+           "kvarn_fp16_decode_attention", "kvarn_read_flags", "kvarn_status_string", "kvarn_last_error")
 
 KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_SHAPE, KVARN_ERR_UNSUPPORTED, KVARN_ERR_WORKSPACE, KVARN_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 FLAG_BAD_PAGE, FLAG_BAD_SEQLEN = 1, 2
@@ -51,6 +51,8 @@ def _load() -> ctypes.CDLL:
         "kvarn_dequantize_blocks": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, P]),
         "kvarn_decode_workspace_bytes": (SZ, [CFG, I32, I32, I32, I32]),
         "kvarn_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
+        "kvarn_fp16_page_bytes": (SZ, [CFG]),
+        "kvarn_fp16_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
         "kvarn_read_flags": (I32, [P, P, P]),
         "kvarn_status_string": (ctypes.c_char_p, [I32]),
         "kvarn_last_error": (ctypes.c_char_p, []),
@@ -130,6 +132,23 @@ def kvarn_decode_attention(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                                        num_kv_heads, float(softmax_scale), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _ptr(dev_flags),
                                        _stream(stream)))
+
+
+def kvarn_fp16_page_bytes(cfg) -> int:
+    return int(_lib.kvarn_fp16_page_bytes(ctypes.byref(cfg)))
+
+
+def kvarn_fp16_decode_attention(cfg, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_table: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int,
+                                out: torch.Tensor, workspace: torch.Tensor, softmax_scale: float = 0.0,
+                                dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The fp16 baseline: k_cache, v_cache fp16 [num_pages, Hkv, 128, 128]; other arguments as kvarn_decode_attention."""
+    batch, hq = q.shape[0], q.shape[1]
+    _check(_lib.kvarn_fp16_decode_attention(ctypes.byref(cfg), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                            k_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                            _ptr(seq_lens), batch, hq, num_kv_heads, float(softmax_scale), _ptr(out),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _ptr(dev_flags), _stream(stream)))
 
 
 def kvarn_read_flags(dev_flags: torch.Tensor, stream=None) -> int:

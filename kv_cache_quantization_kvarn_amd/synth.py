@@ -169,3 +169,19 @@ def make_page_map(w: Workload) -> PageMap:
 
 def total_prefix_blocks(w: Workload) -> int:
     return sum(p // BLOCK_TOKENS for p in seq_lens_for(w))
+
+
+def fp16_pages(x: torch.Tensor, dst_pages: torch.Tensor, num_pages: int,
+               pool: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Lay token-major fp16 K or V ``[n_blocks*128, Hkv, 128]`` out as uncompressed pages.
+
+    Block b goes to page ``dst_pages[b]`` of a pool ``[num_pages, Hkv, 128 tokens, 128 channels]``
+    (the layout of the fp16 baseline decode); pages not written stay zero.  A pure copy.
+    """
+    n_blocks = x.shape[0] // BLOCK_TOKENS
+    hkv = x.shape[1]
+    if pool is None:
+        pool = torch.zeros((num_pages, hkv, BLOCK_TOKENS, HEAD_DIM), dtype=torch.float16, device=x.device)
+    blocks = x[: n_blocks * BLOCK_TOKENS].view(n_blocks, BLOCK_TOKENS, hkv, HEAD_DIM).permute(0, 2, 1, 3)
+    pool[dst_pages.to(device=x.device, dtype=torch.long)] = blocks.to(torch.float16)
+    return pool

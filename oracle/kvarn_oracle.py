@@ -294,3 +294,38 @@ def decode(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table:
                 cache[g] = (dequantize_pages(k_pool, pages, g, False), dequantize_pages(v_pool, pages, g, True))
             out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# The uncompressed baseline: decode over fp16 pages (blog post, "KVarN (Varyans
+# Normalize Edilmiş KV-Cache) Nedir?": the packed cache is compared against FP16
+# serving; paged storage and grouped heads as in the "KV Cache" glossary page).
+# --------------------------------------------------------------------------
+def fp16_pages(cache16: np.ndarray, pages, head: int) -> np.ndarray:
+    """Concatenate the fp16 token rows of one KV head over a page list -> [len(pages)*128, 128] fp64.
+
+    cache16: fp16 [num_pages, Hkv, 128 tokens, 128 channels].
+    """
+    if len(pages) == 0:
+        return np.zeros((0, HEAD_DIM))
+    return np.concatenate([np.asarray(cache16[int(p), head], dtype=np.float64) for p in pages])
+
+
+def fp16_decode(q16: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block_table: np.ndarray,
+                seq_lens: np.ndarray, num_kv_heads: int, softmax_scale: float = 0.0, seqs=None,
+                heads=None) -> np.ndarray:
+    """Decode attention of q [B, Hq, 128] over fp16 pages -> fp64 [B, Hq, 128] (no rotation, no quantisation).
+
+    Same addressing and scale as ``decode``; ``seqs`` / ``heads`` restrict the work to a sample.
+    """
+    bsz, hq, _ = q16.shape
+    group = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
+    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    for b in (range(bsz) if seqs is None else seqs):
+        pages = block_table[b, : int(seq_lens[b]) // BLOCK]
+        for h in (range(hq) if heads is None else heads):
+            g = h // group
+            out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), fp16_pages(k_cache, pages, g),
+                                  fp16_pages(v_cache, pages, g), scale)
+    return out

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def header_functions():
     src = open(os.path.join(ROOT, "include", "kvarn.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvarn_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kvarn_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -135,3 +135,23 @@ def test_byte_accounting_reproduces_page_figures():
     assert abs(per_tok / 1000 - float(g["qwen_kb_per_token"])) / float(g["qwen_kb_per_token"]) < 0.05
     # quantize moves 64 KiB of fp16 in and one K+V page pair out per (block, KV head)
     assert accounting.quantize_bytes(1, 1, kb, vb) == 65536 + 15360
+
+
+def test_fp16_decode_validation():
+    cfg = K.kvarn_config_parse()
+    assert K.kvarn_fp16_page_bytes(cfg) == 32768
+    assert K.kvarn_fp16_page_bytes(K.kvarn_config()) == 0
+
+    def f16(q=FAKE, kc=FAKE, vc=FAKE, npages=4, bt=FAKE, mb=2, sl=FAKE, b=1, hq=32, hkv=8, out=FAKE,
+            ws=ctypes.c_void_p(0x10000), wsb=1 << 30):
+        return K.library().kvarn_fp16_decode_attention(ctypes.byref(cfg), q, kc, vc, npages, bt, mb, sl, b, hq, hkv,
+                                                       0.0, out, ws, wsb, None, None)
+
+    assert f16(hq=30) == K.KVARN_ERR_SHAPE
+    assert f16(hq=128, hkv=8) == K.KVARN_ERR_UNSUPPORTED
+    assert f16(b=0) == K.KVARN_OK
+    assert f16(kc=None) == K.KVARN_ERR_NULL
+    assert f16(wsb=16) == K.KVARN_ERR_WORKSPACE
+    assert f16(vc=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
+    assert f16(q=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE
+    assert f16(npages=0) == K.KVARN_ERR_SHAPE

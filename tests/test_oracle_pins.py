@@ -405,3 +405,54 @@ def test_page_metadata_offsets():
         assert pg[base + 256:base + 258].tolist() == [0x00, 0x40]    # fp16 2.0
         assert pg[base + 512:base + 516].tolist() == [0, 0, 0, 0x3F]  # fp32 0.5
         assert pg[base + 1024:base + 1028].tolist() == [0, 0, 0x80, 0xBF]  # fp32 -1.0
+
+
+# ---- the fp16 baseline decode ------------------------------------------------
+def fp16_cache(seed, seqs, hkv, num_pages):
+    """Token-major fp16 K/V per sequence, scattered into fp16 pages through a random permutation."""
+    r = rng(seed)
+    perm = r.permutation(num_pages)
+    kc = np.zeros((num_pages, hkv, 128, 128), np.float16)
+    vc = np.zeros_like(kc)
+    rows, table, nxt = [], np.zeros((len(seqs), max(seqs) // 128), np.int32), 0
+    for b, n in enumerate(seqs):
+        k = r.standard_normal((n, hkv, 128)).astype(np.float16)
+        v = r.standard_normal((n, hkv, 128)).astype(np.float16)
+        for blk in range(n // 128):
+            p = perm[nxt]
+            nxt += 1
+            table[b, blk] = p
+            kc[p] = k[128 * blk:128 * (blk + 1)].transpose(1, 0, 2)
+            vc[p] = v[128 * blk:128 * (blk + 1)].transpose(1, 0, 2)
+        rows.append((k, v))
+    return rows, kc, vc, table
+
+
+def test_fp16_decode_matches_sdpa_on_token_rows():
+    seqs = [256, 384]
+    rows, kc, vc, table = fp16_cache(40, seqs, 2, 6)
+    q = rng(41).standard_normal((2, 6, 128)).astype(np.float16)
+    out = o.fp16_decode(q, kc, vc, table, np.array(seqs), 2)
+    for b in range(2):
+        k, v = rows[b]
+        for h in range(6):
+            g = h // 3
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, h].astype(np.float64))[None, None, None],
+                torch.from_numpy(k[:, g].astype(np.float64))[None, None],
+                torch.from_numpy(v[:, g].astype(np.float64))[None, None])
+            assert np.allclose(out[b, h], ref[0, 0, 0].numpy(), atol=1e-12)
+
+
+def test_fp16_decode_equal_keys_give_mean_of_values():
+    rows, kc, vc, table = fp16_cache(42, [256], 1, 2)
+    kc[:] = kc[0, 0, 0]  # every key row the same: uniform weights
+    q = rng(43).standard_normal((1, 1, 128)).astype(np.float16)
+    out = o.fp16_decode(q, kc, vc, table, np.array([256]), 1)
+    assert np.allclose(out[0, 0], rows[0][1][:, 0].astype(np.float64).mean(axis=0), atol=1e-12)
+
+
+def test_fp16_decode_empty_sequence_is_zero():
+    _, kc, vc, table = fp16_cache(44, [128], 1, 1)
+    q = rng(45).standard_normal((1, 1, 128)).astype(np.float16)
+    assert np.all(o.fp16_decode(q, kc, vc, table, np.array([0]), 1) == 0.0)
