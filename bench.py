@@ -10,6 +10,9 @@ timed region starts.
 Prints one JSON line (rank 0).  Throughput is algorithmic bytes / time:
   quantize: 65536 B of fp16 in + 15360 B of pages out per (block, KV head)
   decode:   15360 B of pages per attended (block, KV head) + q, out, table
+Outside the timed steps it also times, after a last-level-cache flush, the
+packed decode and the same decode over uncompressed fp16 pages (65536 B per
+attended (block, KV head)), and reports their ratio.
 """
 from __future__ import annotations
 
@@ -62,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
+    ap.add_argument("--no-fp16-baseline", action="store_true",
+                    help="skip the fp16 paged decode baseline (measured outside the timed steps)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -183,6 +188,59 @@ def cpu_baseline(w, seconds):
     }
 
 
+def timed_after_flush(fn, reps, stream, flush, sink):
+    """Median time (s) of fn() launches, each after reading 512 MB (evicts the 256 MB last-level cache)."""
+    import torch
+    ms = []
+    for _ in range(reps):
+        torch.sum(flush, dim=0, out=sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return ms[len(ms) // 2] / 1e3
+
+
+def fp16_baseline(case, K, synth, acc, stream, reps, flush, sink, kvarn_flush_s):
+    """The same decode over uncompressed fp16 pages (layer 0), cache-flushed like the packed decode."""
+    import torch
+    w, pm = case.w, case.pm
+    n_prefix = synth.total_prefix_blocks(w)
+    k, v = synth.layer_kv(w, 0, n_prefix * 128, "cuda")
+    kc = synth.fp16_pages(k, pm.prefix_pages, pm.num_pages)
+    vc = synth.fp16_pages(v, pm.prefix_pages, pm.num_pages)
+    del k, v
+    if w.append_blocks:
+        ka, va = synth.layer_kv(w, 0, w.batch * 128, "cuda", append=True)
+        synth.fp16_pages(ka, pm.append_pages, pm.num_pages, pool=kc)
+        synth.fp16_pages(va, pm.append_pages, pm.num_pages, pool=vc)
+        del ka, va
+    q = case.layers[0]["q"]
+
+    def run():
+        K.kvarn_fp16_decode_attention(case.cfg, q, kc, vc, case.bt, case.sl, w.hkv, case.out, case.ws,
+                                      dev_flags=case.flags)
+
+    run()
+    torch.cuda.synchronize()
+    t = timed_after_flush(run, reps, stream, flush, sink)
+    assert K.kvarn_read_flags(case.flags) == 0, "device flags set by the fp16 baseline"
+    page = K.kvarn_fp16_page_bytes(case.cfg)
+    attended = int(pm.seq_lens.sum().item()) // 128
+    nbytes = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, page, page)
+    gbps = nbytes / t / 1e9
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"us_median": round(t * 1e6, 2), "gbps": round(gbps, 1),
+            "pct_peak": round(100 * gbps / acc.HBM_PEAK_GBPS, 2), "bytes_per_launch": nbytes,
+            "tokens_per_s": round(w.batch / t, 1),
+            "packed_decode_speedup": round(t / kvarn_flush_s, 3),
+            "protocol": "both decodes timed after a 512 MB read that evicts the last-level cache; median of %d" % reps}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -237,18 +295,11 @@ def main():
     # the decode pays no write-back of the flush), timed per launch
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     flush_sink = torch.empty(1, dtype=torch.float32, device="cuda")
-    df_ms = []
     L0 = case.layers[0]
-    for _ in range(args.flush_reps):
-        torch.sum(flush, dim=0, out=flush_sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        case.decode(L0)
-        b.record(stream)
-        b.synchronize()
-        df_ms.append(a.elapsed_time(b))
-    df_ms.sort()
-    d_flush_s = df_ms[len(df_ms) // 2] / 1e3
+    d_flush_s = timed_after_flush(lambda: case.decode(L0), args.flush_reps, stream, flush, flush_sink)
+    fp16 = None
+    if not args.no_fp16_baseline:
+        fp16 = fp16_baseline(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
 
     step_bytes = case.q_bytes + case.d_bytes
     ms_per_step = elapsed / args.steps * 1e3
@@ -285,6 +336,8 @@ def main():
                                          "pct_peak": round(100 * d_flush_gbps / acc.HBM_PEAK_GBPS, 2),
                                          "us_median": round(d_flush_s * 1e6, 2)}},
     }
+    if fp16 is not None:
+        line["fp16_baseline"] = fp16
     # dominant kernel by time: the one whose launches take longer in the step
     if q_avg_s >= d_avg_s:
         dom, ach = "quantize_kernel", q_gbps
