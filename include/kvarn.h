@@ -130,6 +130,27 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
                                     int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                     void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
 
+/* Decode over the packed pages plus an fp16 tail: the tokens past the last
+ * full block stay uncompressed until their block fills (blocks are quantised
+ * whole, "KVarN Nasıl Çalışır?").  Same arguments, plan, workspace
+ * (kvarn_decode_workspace_bytes), error model and output as
+ * kvarn_decode_attention, except:
+ *   seq_lens   any length in [0, 128*max_blocks_per_seq + 127]: the first
+ *              seq_lens[b]/128 blocks are pages block_table[b, ...], the
+ *              remaining seq_lens[b] % 128 tokens are rows 0 .. of the tail
+ *   k_tail, v_tail  fp16 [batch, 128 tokens, num_kv_heads, 128], 16-byte
+ *              aligned; rows at or past seq_lens[b] % 128 are never read
+ * The tail of sequence b has the layout of kvarn_quantize_blocks' input for
+ * one block, so a full tail is packed by kvarn_quantize_blocks(k_tail + b's
+ * offset, v_tail + b's offset, 1, ...) into the page that then joins the
+ * block table.  One launch: the tail is one more split of the same merge. */
+kvarn_status kvarn_decode_attention_tail(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                         const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, const void* k_tail,
+                                         const void* v_tail, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                         uint32_t* dev_flags, void* stream);
+
 /* The uncompressed baseline on the same harness: decode attention over fp16
  * K/V pages, for comparison with the packed cache ("KVarN (Varyans Normalize
  * Edilmiş KV-Cache) Nedir?": the packed cache against FP16 serving).  Same

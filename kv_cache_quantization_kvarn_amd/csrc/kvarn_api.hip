@@ -15,9 +15,10 @@ hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, 
 hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
                              int n_blocks, int hkv, float* k_out, float* v_out, uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
-                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
-                         int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
-                         uint32_t* counters, uint32_t* flags, hipStream_t stream);
+                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
+                         const void* v_tail, int batch, int hq, int hkv, int blocks_per_split, int max_splits,
+                         float scale_log2, float* out, float* part, uint32_t* counters, uint32_t* flags,
+                         hipStream_t stream);
 hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_cache, int num_pages,
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
@@ -59,18 +60,20 @@ struct DecodePlan {
 
 // Pages per split (a multiple of the 4 waves of a workgroup): about one pass of workgroups over the
 // chip, at most 32 pages per split so mixed lengths balance, and at most 64 splits per
-// (sequence, KV head) so the final merge stays short.
-DecodePlan plan_decode(int batch, int hkv, int max_blocks) {
+// (sequence, KV head) so the final merge stays short (63 page splits when an fp16 tail adds one).
+DecodePlan plan_decode(int batch, int hkv, int max_blocks, bool tail = false) {
   const long units = static_cast<long>(batch) * hkv * max_blocks;
   long bps = (units + kTargetGroups - 1) / kTargetGroups;
   if (bps > kMaxPagesPerSplit) bps = kMaxPagesPerSplit;
-  const long min_bps = (max_blocks + kMaxSplitsPerPair - 1) / kMaxSplitsPerPair;
+  const long page_splits = tail ? kMaxSplitsPerPair - 1 : kMaxSplitsPerPair;
+  const long min_bps = (max_blocks + page_splits - 1) / page_splits;
   if (bps < min_bps) bps = min_bps;
   bps = (bps + 3) / 4 * 4;
   DecodePlan p;
   p.blocks_per_split = static_cast<int>(bps);
   p.max_splits = static_cast<int>((max_blocks + bps - 1) / bps);
   if (p.max_splits < 1) p.max_splits = 1;
+  if (tail) p.max_splits += 1;  // the tail split
   return p;
 }
 
@@ -78,10 +81,12 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 size_t counter_bytes(int batch, int hkv) { return align256(static_cast<size_t>(batch) * hkv * sizeof(uint32_t)); }
 
+// Room for the partials of either plan (with or without an fp16 tail split).
 size_t workspace_bytes(int batch, int hkv, int max_blocks) {
-  const DecodePlan p = plan_decode(batch, hkv, max_blocks);
+  const int a = plan_decode(batch, hkv, max_blocks).max_splits;
+  const int b = plan_decode(batch, hkv, max_blocks, true).max_splits;
   return counter_bytes(batch, hkv) +
-         static_cast<size_t>(batch) * hkv * p.max_splits * kMaxGroup * kPartFloats * sizeof(float);
+         static_cast<size_t>(batch) * hkv * (a > b ? a : b) * kMaxGroup * kPartFloats * sizeof(float);
 }
 
 kvarn_status launch_status(hipError_t e) {
@@ -90,13 +95,16 @@ kvarn_status launch_status(hipError_t e) {
   return KVARN_ERR_LAUNCH;
 }
 
-// Validation and launch shared by the packed decode and the fp16 baseline (same plan, workspace,
-// partials and error model; only the page pools and the kernel differ).
-kvarn_status decode_common(bool fp16_pages, const kvarn_config* cfg, const void* q, const void* k_pool,
+enum class DecodeKind { packed, packed_tail, fp16 };
+
+// Validation and launch shared by the packed decode (with or without an fp16 tail) and the fp16
+// baseline (same plan, workspace, partials and error model; the pools and the kernel differ).
+kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void* q, const void* k_pool,
                            const void* v_pool, int32_t num_pages, const int32_t* block_table,
-                           int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
-                           int32_t num_kv_heads, float softmax_scale, float* out, void* workspace, size_t ws_bytes,
-                           uint32_t* dev_flags, void* stream) {
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens, const void* k_tail,
+                           const void* v_tail, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           float softmax_scale, float* out, void* workspace, size_t ws_bytes, uint32_t* dev_flags,
+                           void* stream) {
   kvarn_status s = check_config(cfg);
   if (s != KVARN_OK) return s;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
@@ -108,7 +116,7 @@ kvarn_status decode_common(bool fp16_pages, const kvarn_config* cfg, const void*
   if (!q || !seq_lens || !out) return fail(KVARN_ERR_NULL, "q, seq_lens or out is NULL");
   if (max_blocks_per_seq > 0 && (!block_table || !k_pool || !v_pool))
     return fail(KVARN_ERR_NULL, "block_table or a pool is NULL");
-  if (static_cast<long>(max_blocks_per_seq) * 128 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
+  if (static_cast<long>(max_blocks_per_seq) * 128 + 127 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
   if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
   const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
   const size_t need = workspace_bytes(batch, num_kv_heads, mb);
@@ -119,7 +127,13 @@ kvarn_status decode_common(bool fp16_pages, const kvarn_config* cfg, const void*
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
   if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
-  const DecodePlan p = plan_decode(batch, num_kv_heads, mb);
+  const bool tail = kind == DecodeKind::packed_tail;
+  if (tail) {
+    if (!k_tail || !v_tail) return fail(KVARN_ERR_NULL, "k_tail or v_tail is NULL");
+    if ((reinterpret_cast<uintptr_t>(k_tail) | reinterpret_cast<uintptr_t>(v_tail)) & 15)
+      return fail(KVARN_ERR_SHAPE, "tails must be 16-byte aligned");
+  }
+  const DecodePlan p = plan_decode(batch, num_kv_heads, mb, tail);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   const float scale_log2 = scale * 1.4426950408889634f;
   uint32_t* counters = static_cast<uint32_t*>(workspace);
@@ -127,13 +141,14 @@ kvarn_status decode_common(bool fp16_pages, const kvarn_config* cfg, const void*
   // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
   const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (fp16_pages)
+  if (kind == DecodeKind::fp16)
     return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                                    batch, num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits,
                                                    scale_log2, out, part, counters, dev_flags, st));
-  return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens, batch,
-                                            num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2,
-                                            out, part, counters, dev_flags, st));
+  return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
+                                            tail ? k_tail : nullptr, tail ? v_tail : nullptr, batch, num_q_heads,
+                                            num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2, out, part,
+                                            counters, dev_flags, st));
 }
 
 }  // namespace
@@ -205,8 +220,20 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
                                     int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
                                     int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                     void* workspace, size_t ws_bytes, uint32_t* dev_flags, void* stream) {
-  return decode_common(false, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq, seq_lens, batch,
-                       num_q_heads, num_kv_heads, softmax_scale, out, workspace, ws_bytes, dev_flags, stream);
+  return decode_common(DecodeKind::packed, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq,
+                       seq_lens, nullptr, nullptr, batch, num_q_heads, num_kv_heads, softmax_scale, out, workspace,
+                       ws_bytes, dev_flags, stream);
+}
+
+kvarn_status kvarn_decode_attention_tail(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                         const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, const void* k_tail,
+                                         const void* v_tail, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                         float softmax_scale, float* out, void* workspace, size_t ws_bytes,
+                                         uint32_t* dev_flags, void* stream) {
+  return decode_common(DecodeKind::packed_tail, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq,
+                       seq_lens, k_tail, v_tail, batch, num_q_heads, num_kv_heads, softmax_scale, out, workspace,
+                       ws_bytes, dev_flags, stream);
 }
 
 size_t kvarn_fp16_page_bytes(const kvarn_config* cfg) {
@@ -218,8 +245,9 @@ kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q,
                                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
                                          int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                          void* workspace, size_t ws_bytes, uint32_t* dev_flags, void* stream) {
-  return decode_common(true, cfg, q, k_cache, v_cache, num_pages, block_table, max_blocks_per_seq, seq_lens, batch,
-                       num_q_heads, num_kv_heads, softmax_scale, out, workspace, ws_bytes, dev_flags, stream);
+  return decode_common(DecodeKind::fp16, cfg, q, k_cache, v_cache, num_pages, block_table, max_blocks_per_seq,
+                       seq_lens, nullptr, nullptr, batch, num_q_heads, num_kv_heads, softmax_scale, out, workspace,
+                       ws_bytes, dev_flags, stream);
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

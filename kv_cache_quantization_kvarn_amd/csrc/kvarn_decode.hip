@@ -485,13 +485,145 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   }
 }
 
+// The fp16 tail of one (sequence, KV head): the ntail < 128 tokens after the last full block, token
+// t of KV head kvh at kt + t * tstride (the layout of the quantiser's input, one block per
+// sequence).  Wave 0 computes (m, l, o) of the G heads over the tail exactly as over an fp16 page
+// (MFMA scores, masked past ntail; V transposed by a selection-matrix product; p as fp16 hi + lo),
+// rotates o by H~ so that it merges with the packed splits (whose o is in the rotated basis), and
+// stores the partial at pp.  scratch: 8 x 128 floats of LDS.
+__device__ __forceinline__ void tail_partial(const uint16_t* __restrict__ qrow0, const uint16_t* __restrict__ kt,
+                                             const uint16_t* __restrict__ vt, size_t tstride, int ntail, int G,
+                                             float scale_log2, float* __restrict__ pp, float (*scratch)[kHeadDim],
+                                             float* __restrict__ ml, int lane) {
+  const int n = lane & 15, g = lane >> 4;
+  f16x8 qb[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    const f16x8 v = *reinterpret_cast<const f16x8*>(qrow0 + (n < G ? n : 0) * kHeadDim + 32 * cg + 8 * g);
+    const f16x8 zero = {};
+    qb[cg] = n < G ? v : zero;
+  }
+  f16x8 sel[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      sel[h2][x] = (8 * g + x == 16 * h2 + n) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(0.0f);
+  const f16x8 zero8 = {};
+  // rows past the tail are never read as data: their operands are zero and their scores -inf
+  auto row = [&](const uint16_t* base, int t, int cg) {
+    const f16x8 v = *reinterpret_cast<const f16x8*>(base + static_cast<size_t>(t < ntail ? t : 0) * tstride +
+                                                    32 * cg + 8 * g);
+    return t < ntail ? v : zero8;
+  };
+  float s[8][4];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) d = mfma16x16x32(row(kt, 16 * mt + n, cg), qb[cg], d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[mt][r] = 16 * mt + 4 * g + r < ntail ? d[r] * scale_log2 : -INFINITY;
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, s[mt][r]);
+  m = max_xor32(max_xor16(m));  // lanes n, n^16, n^32, n^48 hold the 128 tokens of head n
+  float l = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[mt][r] = ex2(s[mt][r] - m);  // 0 past the tail
+      l += s[mt][r];
+    }
+  l = sum_xor32(sum_xor16(l));
+  f32x4 acc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f16x8 hi, lo;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float pv = s[2 * c + (k >> 2)][k & 3];
+      hi[k] = static_cast<_Float16>(pv);
+      lo[k] = static_cast<_Float16>(pv - static_cast<float>(hi[k]));
+    }
+    // rows 0-7 take p in fp16, rows 8-15 the remainder of head n - 8 (from lane n ^ 8).  The lane
+    // move runs in every lane before the select: under a branch on n, lanes n < 8 would be
+    // inactive and the move would read zeros from them.
+    f16x8 ap;
+    {
+      const u32x4 lo_u = __builtin_bit_cast(u32x4, lo), hi_u = __builtin_bit_cast(u32x4, hi);
+      u32x4 r;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const uint32_t from8 = dpp_u32_xor8(lo_u[x]);
+        r[x] = n < 8 ? hi_u[x] : from8;
+      }
+      ap = __builtin_bit_cast(f16x8, r);
+    }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      const f16x8 v0 = row(vt, 32 * c + n, cg);
+      const f16x8 v1 = row(vt, 32 * c + 16 + n, cg);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 t0 = mfma16x16x32(v0, sel[h2], z);
+        const f32x4 t1 = mfma16x16x32(v1, sel[h2], z);
+        f16x8 bv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bv[r] = static_cast<_Float16>(t0[r]);
+          bv[4 + r] = static_cast<_Float16>(t1[r]);
+        }
+        acc[2 * cg + h2] = mfma16x16x32(ap, bv, acc[2 * cg + h2]);
+      }
+    }
+  }
+  // hi + lo rows; lanes g < 2 then hold o of heads 4g + r for channel 16ct + n
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[ct][r] = sum_xor32(acc[ct][r]);
+  if (g < 2) {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) scratch[4 * g + r][16 * ct + n] = acc[ct][r];
+  }
+  if (g == 0 && n < kMaxGroup) {
+    ml[2 * n] = m;
+    ml[2 * n + 1] = l;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int h = 0; h < G; ++h) {
+    const float2 ov = reinterpret_cast<const float2*>(scratch[h])[lane];
+    float x0 = ov.x, x1 = ov.y;
+    wave_fwht(x0, x1, lane);
+    float* ph = pp + static_cast<size_t>(h) * kPartStride;
+    store_coherent(ph + 2 * lane, x0 * kInvSqrt128);
+    store_coherent(ph + 2 * lane + 1, x1 * kInvSqrt128);
+    if (lane == 0) {
+      store_coherent(ph + kHeadDim, ml[2 * h]);
+      store_coherent(ph + kHeadDim + 1, ml[2 * h + 1]);
+    }
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256, 3) void decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
-    int hq, int hkv, int blocks_per_split, int max_splits, float scale_log2, float* __restrict__ out,
-    float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
+    const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, int hq, int hkv,
+    int blocks_per_split, int max_splits, float scale_log2, float* __restrict__ out, float* __restrict__ part,
+    uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
   // The per-wave page buffers are live only inside the page loop; before it each wave uses its own
   // buffer as scratch for the query transform, and the four-wave merge after it reuses the memory.
   __shared__ union __align__(16) {
@@ -517,133 +649,151 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
   const int sl = seq_lens[b];
   float* out_b = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
 
-  const bool bad = sl < 0 || (sl & (kBlockTokens - 1)) != 0 || sl > max_blocks * kBlockTokens;
+  // Without a tail the length must be whole blocks; with one, the tokens past the last full block
+  // are in the fp16 tail and form one more split.
+  const bool has_tail = k_tail != nullptr;
+  const bool bad = sl < 0 || sl > max_blocks * kBlockTokens + (has_tail ? kBlockTokens - 1 : 0) ||
+                   (!has_tail && (sl & (kBlockTokens - 1)) != 0);
   const int nblk = bad ? 0 : sl / kBlockTokens;
-  if (nblk == 0) {
+  const int ntail = bad || !has_tail ? 0 : (sl & (kBlockTokens - 1));
+  if (nblk == 0 && ntail == 0) {
     if (split == 0) {
       if (bad && tid == 0 && flags) atomicOr(flags, kFlagBadSeqLen);
       for (int e = tid; e < G * kHeadDim; e += blockDim.x) out_b[e] = 0.f;
     }
     return;
   }
-  const int nsplit = (nblk + blocks_per_split - 1) / blocks_per_split;
+  const int npsplit = (nblk + blocks_per_split - 1) / blocks_per_split;  // splits over packed pages
+  const int nsplit = npsplit + (ntail > 0 ? 1 : 0);
   if (split >= nsplit) return;
-  const int blk0 = split * blocks_per_split;
-  const int cnt = min(nblk, blk0 + blocks_per_split) - blk0;
-  const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + blk0;
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, known uniform: page ids load as scalars
-
-  // ---- query loads, then the loads of this wave's first page ----------------
-  // Both are issued before the query transform so that the page's HBM latency overlaps it.  Lane
-  // l takes channels 2l and 2l + 1 of every head (heads past G re-read head 0 and are zeroed).
-  const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
-  uint32_t qraw[kMaxGroup];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-    qraw[h] = reinterpret_cast<const uint32_t*>(qb + (h < G ? h : 0) * kHeadDim)[lane];
-  __builtin_amdgcn_sched_barrier(0);
-  // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
-  const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
-  PageRegs A;
-  load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- rotated, scaled query ------------------------------------------------
-  // Every wave transforms all heads itself (in registers) and writes the same values into the
-  // shared per-lane array, so no workgroup barrier is needed; the wave's own page buffer serves as
-  // scratch for the change of layout.
-  WaveLds& L = U.wl[w];
-  float (*qt)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&L.coef[0][0]);  // [kMaxGroup][128]
-  const float qscale = kInvSqrt128 * scale_log2;
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    float x0 = h < G ? half_bits_to_float(qraw[h] & 0xFFFFu) : 0.f;
-    float x1 = h < G ? half_bits_to_float(qraw[h] >> 16) : 0.f;
-    wave_fwht(x0, x1, lane);
-    reinterpret_cast<float2*>(qt[h])[lane] = make_float2(x0 * qscale, x1 * qscale);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
-  asm volatile("" : "+v"(mag16), "+v"(mag64), "+v"(mag4));
-  WaveState S;
-  float qmax = 0.f;
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    const float a = qt[h][ch0];
-    const float c = qt[h][ch0 + 4];
-    qlane[lane][h] = a;
-    qlane[lane][kMaxGroup + h] = c;
-    qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(c)));
-  }
-  S.qmax = wave_max_all(qmax);
-  S.ql = &qlane[lane][0];
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  S.m_run = -INFINITY;
-  S.l_run = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S.acc[mt][r] = 0.f;
-  // unused coefficient columns stay zero
-  for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
-
-  // ---- pages of this wave: w, w + 4, ... ---------------------------------------
-  bool bad_page = false;
-  if (wu < cnt) {
-    if (A.ok) {
-      process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
-    } else {
-      bad_page = true;
-    }
-  }
-  for (int i = wu + kWaves; i < cnt; i += kWaves) {
-    load_page(A, bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
-    if (A.ok) {
-      process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
-    } else {
-      bad_page = true;
-    }
-  }
-  if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
-
-  // ---- merge the four waves through LDS --------------------------------------
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) S.acc[mt][r] += dpp<kDppXor8>(S.acc[mt][r]);
-  __syncthreads();  // every wave is out of the page loop: its page buffers may be reused
-  if (!lo_col && hd < G) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wacc[w][hd][16 * mt + 4 * g + r] = S.acc[mt][r];
-    if (g == 0) {
-      wm[w][hd] = S.m_run;
-      wls[w][hd] = S.l_run;
-    }
-  }
-  __syncthreads();
   const size_t pair = static_cast<size_t>(b) * hkv + kvh;
   float* pbase = part + pair * max_splits * kMaxGroup * kPartStride;
-  for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
-    const int h = e >> 7, j = e & 127;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < kWaves; ++x) mx = fmaxf(mx, wm[x][h]);
-    float o = 0.f, lsum = 0.f;
-#pragma unroll
-    for (int x = 0; x < kWaves; ++x) {
-      const float wgt = wm[x][h] == -INFINITY ? 0.f : ex2(wm[x][h] - mx);
-      o = fmaf(wgt, wacc[x][h][j], o);
-      lsum = fmaf(wgt, wls[x][h], lsum);
+  if (split == npsplit) {
+    // ---- the fp16 tail --------------------------------------------------------
+    if (w == 0) {
+      const uint16_t* qrow0 = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
+      const size_t tstride = static_cast<size_t>(hkv) * kHeadDim;
+      const size_t t0 = (static_cast<size_t>(b) * kBlockTokens * hkv + kvh) * kHeadDim;
+      tail_partial(qrow0, k_tail + t0, v_tail + t0, tstride, ntail, G, scale_log2,
+                   pbase + static_cast<size_t>(split) * kMaxGroup * kPartStride, wacc[0], &wm[0][0], lane);
     }
-    float* pp = pbase + (static_cast<size_t>(split) * kMaxGroup + h) * kPartStride;
-    store_coherent(pp + j, o);
-    if (j == 0) {
-      store_coherent(pp + kHeadDim, mx);
-      store_coherent(pp + kHeadDim + 1, lsum);
+  } else {
+    // ---- packed page splits -------------------------------------------------
+    const int blk0 = split * blocks_per_split;
+    const int cnt = min(nblk, blk0 + blocks_per_split) - blk0;
+    const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + blk0;
+    const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index, known uniform: page ids load as scalars
+
+    // ---- query loads, then the loads of this wave's first page ----------------
+    // Both are issued before the query transform so that the page's HBM latency overlaps it.  Lane
+    // l takes channels 2l and 2l + 1 of every head (heads past G re-read head 0 and are zeroed).
+    const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * kHeadDim;
+    uint32_t qraw[kMaxGroup];
+  #pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      qraw[h] = reinterpret_cast<const uint32_t*>(qb + (h < G ? h : 0) * kHeadDim)[lane];
+    __builtin_amdgcn_sched_barrier(0);
+    // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
+    const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
+    PageRegs A;
+    load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- rotated, scaled query ------------------------------------------------
+    // Every wave transforms all heads itself (in registers) and writes the same values into the
+    // shared per-lane array, so no workgroup barrier is needed; the wave's own page buffer serves as
+    // scratch for the change of layout.
+    WaveLds& L = U.wl[w];
+    float (*qt)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&L.coef[0][0]);  // [kMaxGroup][128]
+    const float qscale = kInvSqrt128 * scale_log2;
+  #pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      float x0 = h < G ? half_bits_to_float(qraw[h] & 0xFFFFu) : 0.f;
+      float x1 = h < G ? half_bits_to_float(qraw[h] >> 16) : 0.f;
+      wave_fwht(x0, x1, lane);
+      reinterpret_cast<float2*>(qt[h])[lane] = make_float2(x0 * qscale, x1 * qscale);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
+    asm volatile("" : "+v"(mag16), "+v"(mag64), "+v"(mag4));
+    WaveState S;
+    float qmax = 0.f;
+  #pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      const float a = qt[h][ch0];
+      const float c = qt[h][ch0 + 4];
+      qlane[lane][h] = a;
+      qlane[lane][kMaxGroup + h] = c;
+      qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(c)));
+    }
+    S.qmax = wave_max_all(qmax);
+    S.ql = &qlane[lane][0];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    S.m_run = -INFINITY;
+    S.l_run = 0.f;
+  #pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) S.acc[mt][r] = 0.f;
+    // unused coefficient columns stay zero
+    for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
+
+    // ---- pages of this wave: w, w + 4, ... ---------------------------------------
+    bool bad_page = false;
+    if (wu < cnt) {
+      if (A.ok) {
+        process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+      } else {
+        bad_page = true;
+      }
+    }
+    for (int i = wu + kWaves; i < cnt; i += kWaves) {
+      load_page(A, bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+      if (A.ok) {
+        process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+      } else {
+        bad_page = true;
+      }
+    }
+    if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
+
+    // ---- merge the four waves through LDS --------------------------------------
+  #pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) S.acc[mt][r] += dpp<kDppXor8>(S.acc[mt][r]);
+    __syncthreads();  // every wave is out of the page loop: its page buffers may be reused
+    if (!lo_col && hd < G) {
+  #pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) wacc[w][hd][16 * mt + 4 * g + r] = S.acc[mt][r];
+      if (g == 0) {
+        wm[w][hd] = S.m_run;
+        wls[w][hd] = S.l_run;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kHeadDim; e += blockDim.x) {
+      const int h = e >> 7, j = e & 127;
+      float mx = -INFINITY;
+  #pragma unroll
+      for (int x = 0; x < kWaves; ++x) mx = fmaxf(mx, wm[x][h]);
+      float o = 0.f, lsum = 0.f;
+  #pragma unroll
+      for (int x = 0; x < kWaves; ++x) {
+        const float wgt = wm[x][h] == -INFINITY ? 0.f : ex2(wm[x][h] - mx);
+        o = fmaf(wgt, wacc[x][h][j], o);
+        lsum = fmaf(wgt, wls[x][h], lsum);
+      }
+      float* pp = pbase + (static_cast<size_t>(split) * kMaxGroup + h) * kPartStride;
+      store_coherent(pp + j, o);
+      if (j == 0) {
+        store_coherent(pp + kHeadDim, mx);
+        store_coherent(pp + kHeadDim + 1, lsum);
+      }
     }
   }
   // Hand-off between workgroups without fences.  Every XCD has its own L2, so an agent-scope
@@ -702,12 +852,14 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
 }
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
-                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
-                         int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
-                         uint32_t* counters, uint32_t* flags, hipStream_t stream) {
+                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
+                         const void* v_tail, int batch, int hq, int hkv, int blocks_per_split, int max_splits,
+                         float scale_log2, float* out, float* part, uint32_t* counters, uint32_t* flags,
+                         hipStream_t stream) {
   hipLaunchKernelGGL(decode_kernel, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
-                     static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens, hq, hkv,
+                     static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens,
+                     static_cast<const uint16_t*>(k_tail), static_cast<const uint16_t*>(v_tail), hq, hkv,
                      blocks_per_split, max_splits, scale_log2, out, part, counters, flags);
   return hipGetLastError();
 }

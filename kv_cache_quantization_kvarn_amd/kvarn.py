@@ -31,7 +31,8 @@ class kvarn_config(ctypes.Structure):
 
 
 EXPORTS = ("kvarn_config_parse", "kvarn_page_bytes", "kvarn_quantize_blocks", "kvarn_dequantize_blocks",
-           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_fp16_page_bytes",
+           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_decode_attention_tail",
+           "kvarn_fp16_page_bytes",
            "kvarn_fp16_decode_attention", "kvarn_read_flags", "kvarn_status_string", "kvarn_last_error")
 
 KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_SHAPE, KVARN_ERR_UNSUPPORTED, KVARN_ERR_WORKSPACE, KVARN_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
@@ -51,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "kvarn_dequantize_blocks": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, P]),
         "kvarn_decode_workspace_bytes": (SZ, [CFG, I32, I32, I32, I32]),
         "kvarn_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
+        "kvarn_decode_attention_tail": (I32, [CFG, P, P, P, I32, P, I32, P, P, P, I32, I32, I32, F32, P, P, SZ, P, P]),
         "kvarn_fp16_page_bytes": (SZ, [CFG]),
         "kvarn_fp16_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
         "kvarn_read_flags": (I32, [P, P, P]),
@@ -132,6 +134,20 @@ def kvarn_decode_attention(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                                        num_kv_heads, float(softmax_scale), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _ptr(dev_flags),
                                        _stream(stream)))
+
+
+def kvarn_decode_attention_tail(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                block_table: torch.Tensor, seq_lens: torch.Tensor, k_tail: torch.Tensor,
+                                v_tail: torch.Tensor, num_kv_heads: int, out: torch.Tensor, workspace: torch.Tensor,
+                                softmax_scale: float = 0.0, dev_flags: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """As kvarn_decode_attention, plus fp16 tails k_tail, v_tail [B, 128, Hkv, 128] holding seq_lens % 128 tokens."""
+    batch, hq = q.shape[0], q.shape[1]
+    _check(_lib.kvarn_decode_attention_tail(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), _ptr(k_tail),
+                                            _ptr(v_tail), batch, hq, num_kv_heads, float(softmax_scale), _ptr(out),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                            _ptr(dev_flags), _stream(stream)))
 
 
 def kvarn_fp16_page_bytes(cfg) -> int:

@@ -329,3 +329,33 @@ def fp16_decode(q16: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block
             out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), fp16_pages(k_cache, pages, g),
                                   fp16_pages(v_cache, pages, g), scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# Packed pages plus an fp16 tail: blocks are quantised whole (blog post, "KVarN
+# Nasıl Çalışır?": the cache is quantised in fixed-size token blocks), so the
+# tokens past the last full block are attended in fp16 until their block fills.
+# --------------------------------------------------------------------------
+def decode_tail(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray,
+                seq_lens: np.ndarray, k_tail: np.ndarray, v_tail: np.ndarray, num_kv_heads: int,
+                softmax_scale: float = 0.0, seqs=None, heads=None) -> np.ndarray:
+    """Decode of q [B, Hq, 128] over the first seq_lens[b] // 128 packed blocks followed by the
+    seq_lens[b] % 128 tail tokens k_tail[b, :t, g], v_tail[b, :t, g] (fp16 [B, 128, Hkv, 128]) -> fp64.
+    """
+    bsz, hq, _ = q16.shape
+    group = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
+    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    for b in (range(bsz) if seqs is None else seqs):
+        nblk, ntail = int(seq_lens[b]) // BLOCK, int(seq_lens[b]) % BLOCK
+        pages = block_table[b, :nblk]
+        cache = {}
+        for h in (range(hq) if heads is None else heads):
+            g = h // group
+            if g not in cache:
+                cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False),
+                                            np.asarray(k_tail[b, :ntail, g], dtype=np.float64)]),
+                            np.concatenate([dequantize_pages(v_pool, pages, g, True),
+                                            np.asarray(v_tail[b, :ntail, g], dtype=np.float64)]))
+            out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
+    return out

@@ -10,6 +10,7 @@ import os
 import numpy as np
 import pytest
 import scipy.linalg
+import scipy.special
 import torch
 
 from oracle import kvarn_oracle as o
@@ -456,3 +457,37 @@ def test_fp16_decode_empty_sequence_is_zero():
     _, kc, vc, table = fp16_cache(44, [128], 1, 1)
     q = rng(45).standard_normal((1, 1, 128)).astype(np.float16)
     assert np.all(o.fp16_decode(q, kc, vc, table, np.array([0]), 1) == 0.0)
+
+
+# ---- packed pages plus an fp16 tail ------------------------------------------
+def test_decode_tail_reduces_to_packed_decode_and_to_plain_attention():
+    k, v, kp, vp, pages = small_cache(46, 2, 2)
+    q = rng(47).standard_normal((1, 4, 128)).astype(np.float16)
+    tails = rng(48).standard_normal((2, 1, 128, 2, 128)).astype(np.float16)  # (K, V) x [B=1, 128, Hkv, 128]
+    # no tail tokens: the packed decode
+    a = o.decode_tail(q, kp, vp, pages[None, :], np.array([256]), tails[0], tails[1], 2)
+    b = o.decode(q, kp, vp, pages[None, :], np.array([256]), 2)
+    assert np.array_equal(a, b)
+    # tail only: attention over the fp16 rows, checked with torch
+    t = 77
+    a = o.decode_tail(q, kp, vp, pages[None, :], np.array([t]), tails[0], tails[1], 2)
+    for h in range(4):
+        g = h // 2
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[0, h].astype(np.float64))[None, None, None],
+            torch.from_numpy(tails[0][0, :t, g].astype(np.float64))[None, None],
+            torch.from_numpy(tails[1][0, :t, g].astype(np.float64))[None, None])
+        assert np.allclose(a[0, h], ref[0, 0, 0].numpy(), atol=1e-12)
+
+
+def test_decode_tail_equals_softmax_over_pages_and_tail_rows():
+    k, v, kp, vp, pages = small_cache(49, 2, 1)
+    q = rng(50).standard_normal((1, 1, 128)).astype(np.float16)
+    kt = rng(51).standard_normal((1, 128, 1, 128)).astype(np.float16)
+    vt = rng(52).standard_normal((1, 128, 1, 128)).astype(np.float16)
+    got = o.decode_tail(q, kp, vp, pages[None, :], np.array([256 + 5]), kt, vt, 1)
+    kh = np.concatenate([o.dequantize_pages(kp, pages, 0, False), kt[0, :5, 0].astype(np.float64)])
+    vh = np.concatenate([o.dequantize_pages(vp, pages, 0, True), vt[0, :5, 0].astype(np.float64)])
+    logits = kh @ q[0, 0].astype(np.float64) / np.sqrt(128.0)
+    w = scipy.special.softmax(logits)
+    assert np.allclose(got[0, 0], w @ vh, atol=1e-12)
