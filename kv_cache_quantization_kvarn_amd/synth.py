@@ -185,3 +185,77 @@ def fp16_pages(x: torch.Tensor, dst_pages: torch.Tensor, num_pages: int,
     blocks = x[: n_blocks * BLOCK_TOKENS].view(n_blocks, BLOCK_TOKENS, hkv, HEAD_DIM).permute(0, 2, 1, 3)
     pool[dst_pages.to(device=x.device, dtype=torch.long)] = blocks.to(torch.float16)
     return pool
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill: every sequence holds ``prefix`` packed tokens, then a chunk of
+# ``chunk`` new fp16 rows, all of which are queries (causal within the chunk).
+# The chunk's rows use the same outlier channels as the prefix (same layer).
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    prefix: int          # packed tokens per sequence (multiple of 128)
+    chunk: int           # new fp16 rows per sequence; every one is a query
+    n_outlier: int = 4
+    outlier_mult: float = 20.0
+    index: int = 0
+
+    @property
+    def gqa(self) -> int:
+        return self.hq // self.hkv
+
+
+PREFILL_WORKLOADS: Dict[str, PrefillWorkload] = {
+    w.name: w
+    for w in [
+        PrefillWorkload("prefill_tiny_2x256p200", batch=2, hq=8, hkv=2, prefix=256, chunk=200, index=10),
+        PrefillWorkload("prefill_llama3_8b_16x7680p512", batch=16, hq=32, hkv=8, prefix=7680, chunk=512, index=11),
+    ]
+}
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    """Inputs of one chunked-prefill step (device tensors unless noted).
+
+    ``k_prefix``/``v_prefix``: fp16 [batch*prefix, Hkv, 128], sequence-major (quantise input);
+    ``pages``: int32 [batch*prefix/128] page of every prefix block; ``block_table``: int32
+    [batch, prefix/128 + chunk/128 + 1] (-1 past the prefix); ``prefix_lens``, ``new_lens``,
+    ``q_lens``: int32 [batch]; ``k_new``/``v_new``: fp16 [batch, chunk, Hkv, 128];
+    ``q``: fp16 [batch, chunk, Hq, 128].
+    """
+    k_prefix: torch.Tensor
+    v_prefix: torch.Tensor
+    pages: torch.Tensor
+    block_table: torch.Tensor
+    prefix_lens: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    new_lens: torch.Tensor
+    q_lens: torch.Tensor
+    q: torch.Tensor
+    num_pages: int
+
+
+def prefill_inputs(w: PrefillWorkload, device) -> PrefillInputs:
+    nblk = w.prefix // BLOCK_TOKENS
+    outl = outlier_channels(w, 0)
+    kp, vp = make_kv(w.batch * w.prefix, w.hkv, n_outlier=w.n_outlier, outlier_mult=w.outlier_mult,
+                     outliers=outl, seed_k=stream_seed(w, 1), seed_v=stream_seed(w, 2), device=device)
+    kn, vn = make_kv(w.batch * w.chunk, w.hkv, n_outlier=w.n_outlier, outlier_mult=w.outlier_mult,
+                     outliers=outl, seed_k=stream_seed(w, 7), seed_v=stream_seed(w, 8), device=device)
+    g = _gen(device, stream_seed(w, 3))
+    q = torch.randn(w.batch, w.chunk, w.hq, HEAD_DIM, generator=g, device=device, dtype=torch.float32)
+    total = max(w.batch * nblk, 1)
+    pages = torch.arange(w.batch * nblk, dtype=torch.int32)
+    table = torch.full((w.batch, nblk + (w.chunk + BLOCK_TOKENS - 1) // BLOCK_TOKENS + 1), -1, dtype=torch.int32)
+    for b in range(w.batch):
+        table[b, :nblk] = pages[b * nblk:(b + 1) * nblk]
+    lens = lambda v: torch.full((w.batch,), v, dtype=torch.int32, device=device)
+    return PrefillInputs(kp, vp, pages.to(device), table.to(device), lens(w.prefix),
+                         kn.view(w.batch, w.chunk, w.hkv, HEAD_DIM), vn.view(w.batch, w.chunk, w.hkv, HEAD_DIM),
+                         lens(w.chunk), lens(w.chunk), q.to(torch.float16), total)

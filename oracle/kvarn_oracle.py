@@ -359,3 +359,49 @@ def decode_tail(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_t
                                             np.asarray(v_tail[b, :ntail, g], dtype=np.float64)]))
             out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
     return out
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill over the packed cache.  A chunk of new tokens attends to the
+# packed blocks before it and, causally, to its own rows, which are still fp16:
+# blocks are quantised whole once they fill (blog post, "KVarN Nasıl Çalışır?"),
+# and the post's long-context serving reads the packed cache for every earlier
+# token ("KVarN (Varyans Normalize Edilmiş KV-Cache) Nedir?").
+# --------------------------------------------------------------------------
+def prefill(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table: np.ndarray,
+            prefix_lens: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, new_lens: np.ndarray,
+            q_lens: np.ndarray, num_kv_heads: int, softmax_scale: float = 0.0, seqs=None, rows=None,
+            heads=None) -> np.ndarray:
+    """Chunked-prefill attention -> fp64 [B, max_q, Hq, 128].
+
+    q16 fp16 [B, max_q, Hq, 128]; k_new, v_new fp16 [B, max_new, Hkv, 128].  Sequence b holds
+    prefix_lens[b] // 128 packed blocks (pages block_table[b, ...]) followed by new_lens[b] fp16
+    rows.  Its queries are the last q_lens[b] of those rows: query i sits at fp16 row
+    new_lens[b] - q_lens[b] + i and attends to every packed token and to fp16 rows 0 .. that row.
+    Query rows at or past q_lens[b] are zero.  ``seqs`` / ``rows`` / ``heads`` restrict the work
+    to a sample (the rest stays NaN).
+    """
+    bsz, max_q, hq, _ = q16.shape
+    group = hq // num_kv_heads
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
+    out = np.full((bsz, max_q, hq, HEAD_DIM), np.nan)
+    for b in (range(bsz) if seqs is None else seqs):
+        pages = block_table[b, : int(prefix_lens[b]) // BLOCK]
+        n_new, n_q = int(new_lens[b]), int(q_lens[b])
+        n_pre = len(pages) * BLOCK
+        cache = {}
+        for i in (range(max_q) if rows is None else rows):
+            for h in (range(hq) if heads is None else heads):
+                if i >= n_q:
+                    out[b, i, h] = 0.0
+                    continue
+                g = h // group
+                if g not in cache:
+                    cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False),
+                                                np.asarray(k_new[b, :n_new, g], dtype=np.float64)]),
+                                np.concatenate([dequantize_pages(v_pool, pages, g, True),
+                                                np.asarray(v_new[b, :n_new, g], dtype=np.float64)]))
+                last = n_pre + (n_new - n_q) + i  # the query's own row
+                out[b, i, h] = attention(np.asarray(q16[b, i, h], dtype=np.float64), cache[g][0][: last + 1],
+                                         cache[g][1][: last + 1], scale)
+    return out

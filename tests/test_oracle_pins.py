@@ -491,3 +491,66 @@ def test_decode_tail_equals_softmax_over_pages_and_tail_rows():
     logits = kh @ q[0, 0].astype(np.float64) / np.sqrt(128.0)
     w = scipy.special.softmax(logits)
     assert np.allclose(got[0, 0], w @ vh, atol=1e-12)
+
+
+# ----------------------------------------------------------- chunked prefill
+def _sdpa(q, k, v, mask=None, causal=False):
+    """torch SDPA in fp64 for one head: q [n, 128], k/v [m, 128], boolean mask [n, m] (True = attend)."""
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, is_causal=causal)[0, 0].numpy()
+
+
+def test_prefill_equals_masked_sdpa_over_prefix_and_rows():
+    # 2 packed blocks, 40 fp16 rows of which the last 25 are queries; G = 2
+    _, _, kp, vp, pages = small_cache(61, 2, 2)
+    r = rng(62)
+    n_new, n_q = 40, 25
+    kn = r.standard_normal((1, 48, 2, 128)).astype(np.float16)
+    vn = r.standard_normal((1, 48, 2, 128)).astype(np.float16)
+    q = r.standard_normal((1, 32, 4, 128)).astype(np.float16)
+    got = o.prefill(q, kp, vp, pages[None, :], np.array([256]), kn, vn, np.array([n_new]), np.array([n_q]), 2)
+    assert np.all(got[0, n_q:] == 0)
+    for h in range(4):
+        g = h // 2
+        k = np.concatenate([o.dequantize_pages(kp, pages, g, False), kn[0, :n_new, g].astype(np.float64)])
+        v = np.concatenate([o.dequantize_pages(vp, pages, g, True), vn[0, :n_new, g].astype(np.float64)])
+        # query i (position 256 + 15 + i) sees keys 0 .. 256 + 15 + i
+        mask = np.arange(256 + n_new)[None, :] <= (256 + n_new - n_q + np.arange(n_q))[:, None]
+        ref = _sdpa(q[0, :n_q, h], k, v, mask)
+        assert np.abs(got[0, :n_q, h] - ref).max() < 1e-12
+
+
+def test_prefill_single_query_is_decode_with_tail():
+    _, _, kp, vp, pages = small_cache(63, 3, 1)
+    r = rng(64)
+    kt = r.standard_normal((1, 128, 1, 128)).astype(np.float16)
+    vt = r.standard_normal((1, 128, 1, 128)).astype(np.float16)
+    q = r.standard_normal((1, 1, 3, 128)).astype(np.float16)
+    for n_new in (1, 77, 127):
+        a = o.prefill(q, kp, vp, pages[None, :], np.array([384]), kt, vt, np.array([n_new]), np.array([1]), 1)
+        b = o.decode_tail(q[:, 0], kp, vp, pages[None, :], np.array([384 + n_new]), kt, vt, 1)
+        assert np.abs(a[:, 0] - b).max() < 1e-12
+
+
+def test_prefill_is_causal_and_empty_prefix_is_causal_sdpa():
+    r = rng(65)
+    n = 60
+    kn = r.standard_normal((1, n, 1, 128)).astype(np.float16)
+    vn = r.standard_normal((1, n, 1, 128)).astype(np.float16)
+    q = r.standard_normal((1, n, 2, 128)).astype(np.float16)
+    kp = np.zeros((1, 1, 9728), np.uint8)
+    vp = np.zeros((1, 1, 5632), np.uint8)
+    bt = np.full((1, 2), -1, np.int32)
+    args = (kp, vp, bt, np.array([0]))
+    a = o.prefill(q, *args, kn, vn, np.array([n]), np.array([n]), 1)
+    for h in range(2):
+        ref = _sdpa(q[0, :, h], kn[0, :, 0], vn[0, :, 0], causal=True)
+        assert np.abs(a[0, :, h] - ref).max() < 1e-12
+    # rows after a query's own position do not reach it
+    kn2, vn2 = kn.copy(), vn.copy()
+    kn2[0, 30:] = r.standard_normal((n - 30, 1, 128)).astype(np.float16)
+    vn2[0, 30:] = 7.0
+    b = o.prefill(q, *args, kn2, vn2, np.array([n]), np.array([n]), 1)
+    assert np.array_equal(a[0, :30], b[0, :30])
+    assert not np.allclose(a[0, 30:], b[0, 30:])
