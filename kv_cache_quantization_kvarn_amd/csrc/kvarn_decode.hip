@@ -313,7 +313,8 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   ex = min(max(ex, -100), 100);
   const bool live = prod > 0.f;
   const float sa = live ? pow2i(14 - ex) : 1.f;  // |a * sa| < 2^14
-  const float inv_sa = live ? pow2i(ex - 14) : 0.f;
+  // with no positive key scale the coefficients are all zero but b is not: keep the page at unit scale
+  const float inv_sa = live ? pow2i(ex - 14) : 1.f;
   const float e0s = e0 * sa, e1s = e1 * sa;
   // the key offsets of this lane's two slots: 64 for nibbles 1 and 5 of a dword, else 16
   const _Float16 off = (lane & 3) == 1 ? static_cast<_Float16>(64.0f) : static_cast<_Float16>(16.0f);
@@ -348,7 +349,8 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   exf = min(max(exf, -100), 100);
   const bool livef = fmaxv > 0.f;
   const float sw = livef ? pow2i(14 - exf) : 1.f;  // p <= 1, so |w * sw| < 2^14
-  const float inv_sw = livef ? pow2i(exf - 14) : 0.f;
+  // with no positive value scale the weights are all zero but u is not: unit scale again
+  const float inv_sw = livef ? pow2i(exf - 14) : 1.f;
   const int t0 = 2 * lane;
   L.pk[t0] = ex2(P.kr.x) * inv_sa;
   L.pk[t0 + 1] = ex2(P.kr.y) * inv_sa;

@@ -248,6 +248,37 @@ def test_degenerate_tiles(K, cfg):
                      [(b, h) for b in range(4) for h in range(2)])
 
 
+def test_decode_over_zero_scale_pages(K, cfg):
+    """Pages whose every key scale or every value scale is zero still carry the zero point:
+    keys constant in time (each key group is one channel over the block, so min = max), and
+    values with only channel 0 non-zero (the rotation spreads each such row evenly over all
+    channels, so each value group, one token over the channels, is constant)."""
+    say("case: decode over pages with all key scales zero / all value scales zero")
+    g = torch.Generator().manual_seed(808)
+    hkv = 2
+    const_k = torch.randn(1, hkv, 128, generator=g).expand(128, hkv, 128).clone()
+    e0_v = torch.zeros(128, hkv, 128)
+    e0_v[:, :, 0] = torch.randn(128, hkv, generator=g) * 3
+    rk = torch.randn(128, hkv, 128, generator=g)
+    rv = torch.randn(128, hkv, 128, generator=g)
+    # page 0: both degenerate; page 1: degenerate keys, random values; page 2: random keys, degenerate values
+    k = torch.cat([const_k, const_k, rk]).half()
+    v = torch.cat([e0_v, rv, e0_v]).half()
+    pages = torch.arange(3, dtype=torch.int32)
+    kp, vp, fl = gpu_quantize(K, cfg, k.cuda(), v.cuda(), pages, 3)
+    assert fl == 0
+    kh = kp.cpu().numpy()
+    assert np.all(kh[0, :, 8192:8448] == 0)  # every key scale of page 0 is zero (fp16 bits)
+    assert np.all(vp.cpu().numpy()[0, :, 4096:4352] == 0)  # every value scale of page 0 is zero
+    q = torch.randn(4, 8, 128, generator=g).half().cuda()
+    bt = torch.tensor([[0, -1, -1], [1, -1, -1], [2, -1, -1], [0, 1, 2]], dtype=torch.int32)
+    sl = torch.tensor([128, 128, 128, 384], dtype=torch.int32)
+    out, fl = gpu_decode(K, cfg, q, kp, vp, bt, sl, hkv)
+    assert fl == 0
+    compare_decode(out.cpu().numpy(), q.cpu().numpy(), kh, vp.cpu().numpy(), bt.numpy(), sl.numpy(), hkv,
+                   [(b, h) for b in range(4) for h in range(8)])
+
+
 def test_device_flags(K, cfg):
     say("case: out-of-range page ids and bad sequence lengths set device flags")
     g = torch.Generator().manual_seed(5)
