@@ -168,6 +168,34 @@ kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q,
                                          int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                          void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
 
+/* Chunked prefill over the packed cache.  Sequence b holds prefix_lens[b]/128
+ * packed blocks (pages block_table[b, ...]) followed by new_lens[b] fp16 rows:
+ * the chunk being prefilled, which is quantised block by block only once whole
+ * ("KVarN Nasıl Çalışır?": fixed-size blocks).  Its queries are the last
+ * q_lens[b] of those rows; query i sits at fp16 row new_lens[b] - q_lens[b] + i
+ * and attends to every packed token and, causally, to fp16 rows 0 .. that row.
+ * Scores are scaled as in kvarn_decode_attention; query head h reads KV head
+ * h / (num_q_heads / num_kv_heads).
+ *   q            fp16 [batch, max_q, num_q_heads, 128], 16-byte aligned
+ *   block_table  int32 [batch, max_blocks_per_seq] (device)
+ *   prefix_lens  int32 [batch] (device): multiples of 128, at most 128*max_blocks_per_seq
+ *   k_new, v_new fp16 [batch, max_new, num_kv_heads, 128], 16-byte aligned;
+ *                rows at or past new_lens[b] are never read
+ *   new_lens     int32 [batch] (device), 0 .. max_new
+ *   q_lens       int32 [batch] (device), 0 .. min(new_lens[b], max_q)
+ *   out          fp32 [batch, max_q, num_q_heads, 128], 16-byte aligned; every
+ *                row is written, rows at or past q_lens[b] with zeros
+ * The rows of sequence b in k_new have the layout of kvarn_quantize_blocks'
+ * input, so its full blocks are packed by that call after the step.  No
+ * workspace.  Device flags: a page id out of range (that page is skipped), a
+ * length out of range (every row of the sequence is zero). */
+kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int32_t max_q, const void* k_pool,
+                                     const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, const int32_t* prefix_lens, const void* k_new,
+                                     const void* v_new, int32_t max_new, const int32_t* new_lens,
+                                     const int32_t* q_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     float softmax_scale, float* out, uint32_t* dev_flags, void* stream);
+
 /* Copy *dev_flags to *host_out after the work queued on `stream` finishes
  * (synchronises the stream). */
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream);

@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvarn.so")
-SOURCES = ["kvarn_api.hip", "kvarn_quantize.hip", "kvarn_decode.hip", "kvarn_fp16_decode.hip"]
+SOURCES = ["kvarn_api.hip", "kvarn_quantize.hip", "kvarn_decode.hip", "kvarn_fp16_decode.hip",
+           "kvarn_prefill.hip"]
 
 # Packed fp32 VALU instructions are disabled for device code; the host pass
 # ignores the feature (and says so).

@@ -23,6 +23,10 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
                               uint32_t* counters, uint32_t* flags, hipStream_t stream);
+hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
+                          const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
+                          const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
+                          int hq, int hkv, float scale_log2, float* out, uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
@@ -248,6 +252,44 @@ kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q,
   return decode_common(DecodeKind::fp16, cfg, q, k_cache, v_cache, num_pages, block_table, max_blocks_per_seq,
                        seq_lens, nullptr, nullptr, batch, num_q_heads, num_kv_heads, softmax_scale, out, workspace,
                        ws_bytes, dev_flags, stream);
+}
+
+kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int32_t max_q, const void* k_pool,
+                                     const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                     int32_t max_blocks_per_seq, const int32_t* prefix_lens, const void* k_new,
+                                     const void* v_new, int32_t max_new, const int32_t* new_lens,
+                                     const int32_t* q_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                     float softmax_scale, float* out, uint32_t* dev_flags, void* stream) {
+  kvarn_status s = check_config(cfg);
+  if (s != KVARN_OK) return s;
+  if (batch < 0 || max_q < 0 || max_new < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+      num_pages < 0)
+    return fail(KVARN_ERR_SHAPE, "negative or zero size");
+  if (num_q_heads % num_kv_heads != 0) return fail(KVARN_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
+  if (num_q_heads / num_kv_heads > kMaxGroup)
+    return fail(KVARN_ERR_UNSUPPORTED, "more than 8 query heads per KV head is not supported");
+  if (batch == 0 || max_q == 0) return KVARN_OK;
+  if (!q || !prefix_lens || !new_lens || !q_lens || !out) return fail(KVARN_ERR_NULL, "q, a length array or out is NULL");
+  if (max_new > 0 && (!k_new || !v_new)) return fail(KVARN_ERR_NULL, "k_new or v_new is NULL");
+  if (max_blocks_per_seq > 0 && (!block_table || !k_pool || !v_pool))
+    return fail(KVARN_ERR_NULL, "block_table or a pool is NULL");
+  if (static_cast<long>(max_blocks_per_seq) * 128 + 127 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
+  if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
+  if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
+    return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(k_new) |
+       reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return fail(KVARN_ERR_SHAPE, "q, out, k_new and v_new must be 16-byte aligned");
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  const float scale_log2 = scale * 1.4426950408889634f;
+  // an empty block table / fp16 region is passed as a harmless non-null pointer; nothing is read from it
+  const int32_t* bt = max_blocks_per_seq > 0 ? block_table : prefix_lens;
+  const void* kn = max_new > 0 ? k_new : q;
+  const void* vn = max_new > 0 ? v_new : q;
+  return launch_status(kvarn::launch_prefill(q, max_q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, prefix_lens,
+                                             kn, vn, max_new, new_lens, q_lens, batch, num_q_heads, num_kv_heads,
+                                             scale_log2, out, dev_flags, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

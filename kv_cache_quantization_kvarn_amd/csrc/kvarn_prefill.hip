@@ -1,0 +1,667 @@
+// Chunked-prefill attention over the packed KVarN cache for gfx950.
+//
+// A sequence holds prefix_len / 128 packed blocks (pages of its block-table row) and then new_len
+// fp16 rows: the chunk being prefilled, whose blocks are quantised only once whole (KVarN blog
+// post, section "KVarN Nasıl Çalışır?").  Its queries are the last q_len of those rows: query i sits
+// at fp16 row new_len - q_len + i and attends to every packed token and, causally, to the fp16 rows
+// up to its own.
+//
+// A workgroup of four waves takes 64 (query token, head) rows of one (sequence, KV head): 64 / G
+// query tokens times the G heads that share the KV head.  Wave w owns rows 16w .. 16w + 15, one
+// 16-column tile of v_mfma_f32_16x16x32_f16.  The KV blocks stream through LDS once per workgroup:
+//
+//   * a packed page is loaded by all 256 lanes and its codes are written to LDS as exact fp16
+//     integers (0..15 for keys, 0..3 for values: normal numbers or zero, which the matrix cores
+//     multiply exactly, so no offset has to be removed), keys as [token][channel] rows and values
+//     as [channel][token] rows, the 16-byte chunks of a row XOR-swizzled so that the 16 lanes of a
+//     fragment read hit distinct banks;
+//   * the page metadata becomes per-channel and per-token factors, and both products run with the
+//     codes as the A operand and the fp32 coefficients as an fp16 hi + lo pair of B operands (two
+//     products into one fp32 accumulator):
+//
+//       score_rt = 2^rho_t ( sum_j a_rj c_tj + b_r ), a_rj = q~_rj 2^gamma_j s_j, b_r = sum_j q~_rj 2^gamma_j z_j
+//       o_rj    += 2^gamma_j ( sum_t w_rt c_tj + u_r ), w_rt = p_rt 2^rho_t s_t, u_r = sum_t p_rt 2^rho_t z_t
+//
+//     in the rotated basis (q~ = H q; the rotation is orthonormal and keeps scores, same section);
+//     b_r and u_r enter as the accumulator input of each product chain;
+//   * after the packed pages o is rotated back to the original basis in registers, and the fp16
+//     rows follow in blocks of 128 through the same LDS layout (keys copied, values transposed),
+//     with unit factors, the raw query and the causal mask.
+//
+// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.
+#include "kvarn_common.h"
+
+namespace kvarn {
+
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kCt = 1;                          // 16-column MFMA tiles (16 rows each) per wave
+constexpr int kPfRows = 16 * kCt * kPfWaves;    // (query token, head) rows per workgroup
+constexpr int kMetaWords = kMetaBytes / 4;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct __align__(16) PfLds {
+  u32x4 kf[kBlockTokens * 16];  // keys: token row t, chunk c (8 channel slots) at 16t + (c ^ kkey(t))
+  u32x4 vf[kHeadDim * 16];      // values: channel row j, chunk c (8 token slots) at 16j + (c ^ (j & 15))
+  uint32_t kmeta[kMetaWords];   // the page's raw key / value metadata
+  uint32_t vmeta[kMetaWords];
+  float ep[kHeadDim];           // per channel: key 2^gamma s * sa
+  float fz[kHeadDim];           // per channel: key 2^gamma z
+  float gs[kHeadDim];           // per channel: value 2^gamma / sw
+  float pk[kBlockTokens];       // per token: key 2^rho / sa
+  float fv[kBlockTokens];       // per token: value 2^rho s * sw
+  float zv[kBlockTokens];       // per token: value 2^rho z
+  float sa, sw;                 // the block's power-of-two coefficient scales
+  float qmax[kPfWaves];         // per wave: max |query coefficient| of the current phase
+};
+
+// Swizzle key of a key row: the 16 lanes of a score fragment read tokens 32(n/4) + 4mt + n%4, whose
+// keys are exactly n = 0..15.
+__device__ __forceinline__ int kkey(int t) { return (t & 3) | ((t >> 3) & 12); }
+
+// Slot order inside a key chunk (channels 8c .. 8c+7): slot s holds channel 8c + kslot(s).
+//   kslot = 0, 4, 1, 5, 2, 6, 3, 7
+// Slot order inside a value chunk c (tokens of 16-token word c/2, half c%2):
+//   slot s holds token 16(c/2) + 4(c%2) + {0, 8, 1, 9, 2, 10, 3, 11}[s].
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two codes placed at bits 0.. and 16.. of a dword under the fp16 pattern of 1024 (where the ulp is
+// 1) read 1024 + c exactly; subtracting 1024 in packed fp16 leaves the exact integers.
+__device__ __forceinline__ uint32_t code_pair(uint32_t x, uint32_t mask) {
+  const uint32_t biased = (x & mask) | 0x64006400u;
+  const f16x2 c = __builtin_bit_cast(f16x2, biased) - f16x2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+// hi = nearest fp16 of x0*y0 and x1*y1 (round to nearest even, subnormals kept), lo = nearest fp16
+// of the exact residual; hi is pinned so that the stored and the subtracted value are one value.
+__device__ __forceinline__ void split2(float x0, float y0, float x1, float y1, uint32_t& hi, uint32_t& lo) {
+  f16x2 h = {static_cast<_Float16>(x0 * y0), static_cast<_Float16>(x1 * y1)};
+  asm("" : "+v"(h));
+  const f16x2 l = {static_cast<_Float16>(__builtin_fmaf(x0, y0, -static_cast<float>(h[0]))),
+                   static_cast<_Float16>(__builtin_fmaf(x1, y1, -static_cast<float>(h[1])))};
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Lanes l and l ^ 16 (l ^ 32): v_permlane16_swap / v_permlane32_swap on two copies return the pair
+// (lower lane's value, upper lane's value) in both lanes.
+__device__ __forceinline__ float sum16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 128-point Sylvester transform (unnormalised) of rows held 32 values per lane, a row in lanes
+// n, n + 16, n + 32, n + 48: five bits of the channel index are bits of the array index, the other
+// two are lane bits 4 and 5.  Every stage maps a pair differing in one bit to (sum, difference).
+__device__ __forceinline__ void fwht_rows(float (&v)[32], int lane) {
+#pragma unroll
+  for (int bit = 1; bit < 32; bit <<= 1)
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (!(i & bit)) {
+        const float a = v[i], c = v[i | bit];
+        v[i] = a + c;
+        v[i | bit] = a - c;
+      }
+  const float s16 = (lane & 16) ? -1.f : 1.f, s32 = (lane & 32) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i]), false, false);
+    v[i] = fmaf(s16, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i]), false, false);
+    v[i] = fmaf(s32, __uint_as_float(r[1]), __uint_as_float(r[0]));
+  }
+}
+
+// Scale 2^(14 - e) that brings values of magnitude < x (x = f 2^e, f in [0.5, 1)) below 2^14, and
+// its inverse; unit scale when x is 0 (all coefficients are then zero, the constants are not).
+__device__ __forceinline__ void page_scale(float x, float& s, float& inv) {
+  int e;
+  frexpf(x, &e);
+  e = min(max(e, -100), 100);
+  const bool live = x > 0.f;
+  s = live ? pow2i(14 - e) : 1.f;
+  inv = live ? pow2i(e - 14) : 1.f;
+}
+
+// Per-wave state: the lane's rows (column n of each of the wave's tiles).
+struct PfState {
+  float qv[kCt][32];  // query coefficient of channel 32(i/8) + 8g + i%8 (scaled; rotated in the packed phase)
+  float o[kCt][32];   // output accumulator of channel 16(i/4) + 4g + i%4
+  float m[kCt];       // running maximum (log2 units), identical in the row's four lanes
+  float l[kCt];       // this lane's share of the running sum
+};
+
+// ---------------------------------------------------------------------------------------------
+// Staging of one block into LDS
+// ---------------------------------------------------------------------------------------------
+
+// The 960 16-byte chunks of a packed page (key page 608, value page 352): thread tid takes chunks
+// tid, tid + 256, tid + 512 and tid + 768.
+struct PageRaw {
+  u32x4 c[4];
+};
+
+__device__ __forceinline__ void load_page_raw(PageRaw& R, const uint8_t* __restrict__ kp,
+                                              const uint8_t* __restrict__ vp, int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int id = tid + kPfThreads * k;
+    if (id < 608) {
+      R.c[k] = *reinterpret_cast<const u32x4*>(kp + 16 * id);
+    } else if (id < 960) {
+      R.c[k] = *reinterpret_cast<const u32x4*>(vp + 16 * (id - 608));
+    }
+  }
+}
+
+__device__ __forceinline__ void store_page(PfLds& L, const PageRaw& R, int tid) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int id = tid + kPfThreads * k;
+    const u32x4 x = R.c[k];
+    if (id < 512) {
+      // key codes of token t, channels 32q .. 32q + 31 (dword m: channels 8(4q + m) + i at bits 4i)
+      const int t = id >> 2, q = id & 3;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x4 p;
+        p[0] = code_pair(x[m], 0x000F000Fu);        // channels 0, 4
+        p[1] = code_pair(x[m] >> 4, 0x000F000Fu);   // 1, 5
+        p[2] = code_pair(x[m] >> 8, 0x000F000Fu);   // 2, 6
+        p[3] = code_pair(x[m] >> 12, 0x000F000Fu);  // 3, 7
+        L.kf[16 * t + ((4 * q + m) ^ kkey(t))] = p;
+      }
+    } else if (id < 608) {
+      *reinterpret_cast<u32x4*>(&L.kmeta[4 * (id - 512)]) = x;
+    } else if (id < 864) {
+      // value codes of channel j, tokens 64h .. 64h + 63 (dword k: token 64h + 16k + m at bits 2m)
+      const int v = id - 608, j = v >> 1, h = v & 1;
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const uint32_t w = x[k2];
+        u32x4 a, b;
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+          a[pr] = code_pair(w >> (2 * pr), 0x00030003u);        // tokens pr, pr + 8
+          b[pr] = code_pair(w >> (2 * pr + 8), 0x00030003u);    // tokens 4 + pr, 12 + pr
+        }
+        const int c0 = 2 * (4 * h + k2);
+        L.vf[16 * j + (c0 ^ (j & 15))] = a;
+        L.vf[16 * j + ((c0 + 1) ^ (j & 15))] = b;
+      }
+    } else if (id < 960) {
+      *reinterpret_cast<u32x4*>(&L.vmeta[4 * (id - 864)]) = x;
+    }
+  }
+}
+
+// Factors of a packed page (every wave finds the maxima itself; threads 0-127 write the per-channel
+// arrays, 128-255 the per-token ones).
+__device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
+  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaScale / 2;
+  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaZero / 2;
+  const float* krho = reinterpret_cast<const float*>(L.kmeta) + kMetaRho / 4;
+  const float* kgam = reinterpret_cast<const float*>(L.kmeta) + kMetaGamma / 4;
+  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(L.vmeta) + kMetaScale / 2;
+  const uint16_t* vzr = reinterpret_cast<const uint16_t*>(L.vmeta) + kMetaZero / 2;
+  const float* vrho = reinterpret_cast<const float*>(L.vmeta) + kMetaRho / 4;
+  const float* vgam = reinterpret_cast<const float*>(L.vmeta) + kMetaGamma / 4;
+  const int i0 = 2 * lane, i1 = 2 * lane + 1;
+  const float e = fmaxf(ex2(kgam[i0]) * half_bits_to_float(ksc[i0]), ex2(kgam[i1]) * half_bits_to_float(ksc[i1]));
+  const float f = fmaxf(ex2(vrho[i0]) * half_bits_to_float(vsc[i0]), ex2(vrho[i1]) * half_bits_to_float(vsc[i1]));
+  const float emax = wave_max(e), fmax = wave_max(f);
+  const float qmax = fmaxf(fmaxf(L.qmax[0], L.qmax[1]), fmaxf(L.qmax[2], L.qmax[3]));
+  float sa, inv_sa, sw, inv_sw;
+  page_scale(qmax * emax, sa, inv_sa);
+  page_scale(fmax, sw, inv_sw);
+  if (tid < kHeadDim) {
+    const int j = tid;
+    const float eg = ex2(kgam[j]);
+    L.ep[j] = eg * half_bits_to_float(ksc[j]) * sa;
+    L.fz[j] = eg * half_bits_to_float(kzr[j]);
+    L.gs[j] = ex2(vgam[j]) * inv_sw;
+  } else {
+    const int t = tid - kHeadDim;
+    const float ev = ex2(vrho[t]);
+    L.pk[t] = ex2(krho[t]) * inv_sa;
+    L.fv[t] = ev * half_bits_to_float(vsc[t]) * sw;
+    L.zv[t] = ev * half_bits_to_float(vzr[t]);
+  }
+  if (tid == 0) {
+    L.sa = sa;
+    L.sw = sw;
+  }
+}
+
+// fp16 rows r0 .. r0 + 127 of one (sequence, KV head) (row r at base + r * rstride halves); rows at
+// or past nrows are stored as zeros.  Keys are copied into the key layout (channel slots reordered),
+// values transposed into the value layout.
+__device__ __forceinline__ void store_fp16_block(PfLds& L, const uint16_t* __restrict__ kbase,
+                                                 const uint16_t* __restrict__ vbase, size_t rstride, int r0,
+                                                 int nrows, int tid) {
+  _Float16* vh = reinterpret_cast<_Float16*>(L.vf);
+#pragma unroll 2
+  for (int k = 0; k < 8; ++k) {
+    const int id = tid + kPfThreads * k;
+    const int t = id >> 4, c = id & 15;  // token t, channels 8c .. 8c + 7
+    const bool live = r0 + t < nrows;
+    const size_t off = static_cast<size_t>(live ? r0 + t : 0) * rstride + 8 * c;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 kx = live ? *reinterpret_cast<const u32x4*>(kbase + off) : zero;
+    const u32x4 vx = live ? *reinterpret_cast<const u32x4*>(vbase + off) : zero;
+    u32x4 p;
+    p[0] = (kx[0] & 0xFFFFu) | (kx[2] << 16);          // channels 0, 4
+    p[1] = (kx[0] >> 16) | (kx[2] & 0xFFFF0000u);      // 1, 5
+    p[2] = (kx[1] & 0xFFFFu) | (kx[3] << 16);          // 2, 6
+    p[3] = (kx[1] >> 16) | (kx[3] & 0xFFFF0000u);      // 3, 7
+    L.kf[16 * t + (c ^ kkey(t))] = p;
+    // token t's slot in every value row: word t/16, pair j = t%8 (second of the pair if t%16 >= 8)
+    const int m = t & 15, jp = m & 7;
+    const int chunk = 2 * (t >> 4) + (jp >> 2);
+    const int slot = 2 * (jp & 3) + (m >> 3);
+    const f16x8 vv = __builtin_bit_cast(f16x8, vx);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 8 * c + i;
+      vh[8 * (16 * j + (chunk ^ (j & 15))) + slot] = vv[i];
+    }
+  }
+}
+
+// Unit factors of an fp16 block under the scale of the raw query.
+__device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
+  const float qmax = fmaxf(fmaxf(L.qmax[0], L.qmax[1]), fmaxf(L.qmax[2], L.qmax[3]));
+  float sa, inv_sa, sw, inv_sw;
+  page_scale(qmax, sa, inv_sa);
+  page_scale(1.0f, sw, inv_sw);
+  if (tid < kHeadDim) {
+    L.ep[tid] = sa;
+    L.fz[tid] = 0.f;
+    L.gs[tid] = inv_sw;
+  } else {
+    const int t = tid - kHeadDim;
+    L.pk[t] = inv_sa;
+    L.fv[t] = sw;
+    L.zv[t] = 0.f;
+  }
+  if (tid == 0) {
+    L.sa = sa;
+    L.sw = sw;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// One block against the wave's 32 rows
+// ---------------------------------------------------------------------------------------------
+// masked: apply the causal limit lim[ct] (block-relative index of the last key row the lane's row
+// may see) to this block.
+__device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, bool masked, const int (&lim)[kCt]) {
+  const int n = lane & 15, g = lane >> 4;
+  const float sa = L.sa, sw = L.sw;
+
+  // ---- b_r over this lane's 32 channels, then over the row's four lanes ---------------------------
+  float kinit[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) kinit[ct] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float4 f0 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g]);
+    const float4 f1 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g + 4]);
+    const float fz8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) kinit[ct] = fmaf(S.qv[ct][8 * ks + s], fz8[s], kinit[ct]);
+  }
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) kinit[ct] = sa * sum32(sum16(kinit[ct]));
+
+  // ---- scores: D[token][row] = codes x coefficients ----------------------------------------------
+  // lane (n, g) ends with tokens 32g + 4mt + r of its row
+  f32x4 sc[kCt][8];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) sc[ct][mt] = f32x4{kinit[ct], kinit[ct], kinit[ct], kinit[ct]};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const float4 e0 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g]);
+    const float4 e1 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g + 4]);
+    const float ep8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+    f16x8 bhi[kCt], blo[kCt];
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)  // slots 2s2, 2s2 + 1 hold channels s2, s2 + 4 of the chunk
+        split2(S.qv[ct][8 * ks + s2], ep8[s2], S.qv[ct][8 * ks + s2 + 4], ep8[s2 + 4], h[s2], l[s2]);
+      bhi[ct] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
+      blo[ct] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int t = 32 * (n >> 2) + 4 * mt + (n & 3);
+      const f16x8 a = __builtin_bit_cast(f16x8, L.kf[16 * t + ((4 * ks + g) ^ n)]);
+#pragma unroll
+      for (int ct = 0; ct < kCt; ++ct) {
+        sc[ct][mt] = mfma16x16x32(a, bhi[ct], sc[ct][mt]);
+        sc[ct][mt] = mfma16x16x32(a, blo[ct], sc[ct][mt]);
+      }
+    }
+  }
+
+  // ---- online softmax, value-side B operands -----------------------------------------------------
+  f16x8 whi[kCt][2][2], wlo[kCt][2][2];  // [ct][vv][hf]
+  float vinit[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float4 p4 = *reinterpret_cast<const float4*>(&L.pk[32 * g + 4 * mt]);
+      const float pkv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float s = sc[ct][mt][r] * pkv[r];
+        if (masked && 32 * g + 4 * mt + r > lim[ct]) s = -INFINITY;
+        sc[ct][mt][r] = s;
+        mloc = fmaxf(mloc, s);
+      }
+    }
+    mloc = max32(max16(mloc));
+    const float m_new = fmaxf(S.m[ct], mloc);
+    const float alpha = ex2(S.m[ct] - m_new);
+    if (__builtin_amdgcn_ballot_w64(m_new != S.m[ct]) != 0) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) S.o[ct][i] *= alpha;
+    }
+    S.m[ct] = m_new;
+    float lsum = 0.f, usum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const float4 z4 = *reinterpret_cast<const float4*>(&L.zv[32 * g + 4 * mt]);
+      const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = ex2(sc[ct][mt][r] - m_new);
+        lsum += p;
+        usum = fmaf(p, zvv[r], usum);
+        sc[ct][mt][r] = p;
+      }
+    }
+    S.l[ct] = fmaf(S.l[ct], alpha, lsum);
+    vinit[ct] = sw * sum32(sum16(usum));
+    // slot pair j of operand (vv, hf): tokens 32g + 16vv + 4hf + j (tile 4vv + hf) and + 8 (tile + 2)
+#pragma unroll
+    for (int vv = 0; vv < 2; ++vv)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int m1 = 4 * vv + hf, m2 = m1 + 2;
+        const float4 fa = *reinterpret_cast<const float4*>(&L.fv[32 * g + 4 * m1]);
+        const float4 fb = *reinterpret_cast<const float4*>(&L.fv[32 * g + 4 * m2]);
+        const float fva[4] = {fa.x, fa.y, fa.z, fa.w}, fvb[4] = {fb.x, fb.y, fb.z, fb.w};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) split2(sc[ct][m1][j], fva[j], sc[ct][m2][j], fvb[j], h[j], l[j]);
+        whi[ct][vv][hf] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
+        wlo[ct][vv][hf] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
+      }
+  }
+
+  // ---- values: D[channel][row] = codes x weights, then o += 2^gamma D -----------------------------
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int j = 16 * mt + n;
+    f32x4 d[kCt];
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) d[ct] = f32x4{vinit[ct], vinit[ct], vinit[ct], vinit[ct]};
+#pragma unroll
+    for (int vv = 0; vv < 2; ++vv)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const f16x8 a = __builtin_bit_cast(f16x8, L.vf[16 * j + ((4 * g + 2 * vv + hf) ^ n)]);
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) {
+          d[ct] = mfma16x16x32(a, whi[ct][vv][hf], d[ct]);
+          d[ct] = mfma16x16x32(a, wlo[ct][vv][hf], d[ct]);
+        }
+      }
+    const float4 g4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
+    const float gsv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.o[ct][4 * mt + r] = fmaf(d[ct][r], gsv[r], S.o[ct][4 * mt + r]);
+  }
+}
+
+// The lane's query coefficients of one row in channel order 32(i/8) + 8g + i%8, times `scale`; with
+// `rotate` the row is first transformed by H (the unnormalised transform; scale carries 2^-3.5).
+__device__ __forceinline__ float load_query(float (&qv)[32], const uint16_t* __restrict__ row, bool live, int g,
+                                            int lane, bool rotate, float scale) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 x = live ? *reinterpret_cast<const u32x4*>(row + 32 * ks + 8 * g) : zero;
+    const f16x8 h = __builtin_bit_cast(f16x8, x);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[8 * ks + s] = static_cast<float>(h[s]);
+  }
+  if (rotate) fwht_rows(qv, lane);
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    qv[i] *= scale;
+    mx = fmaxf(mx, fabsf(qv[i]));
+  }
+  return mx;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
+    const uint16_t* __restrict__ q, int max_q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+    int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ prefix_lens,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int max_new,
+    const int32_t* __restrict__ new_lens, const int32_t* __restrict__ q_lens, int batch, int hq, int hkv, int qt,
+    int ntile, float scale_log2, float* __restrict__ out, uint32_t* __restrict__ flags) {
+  __shared__ PfLds L;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
+
+  // Workgroups reach the eight XCDs round-robin by linear id: all query tiles of one (sequence, KV
+  // head) go to one XCD, consecutively, so its pages are fetched into that XCD's L2 once.
+  const int lin = blockIdx.x;
+  const int jlin = lin >> 3;
+  const int pair = (jlin / ntile) * 8 + (lin & 7);
+  const int tile = jlin % ntile;
+  if (pair >= batch * hkv) return;
+  const int b = pair / hkv, kvh = pair - b * hkv;
+  const int G = hq / hkv;
+  const int i0 = tile * qt;
+
+  const int prefix = prefix_lens[b], nnew = new_lens[b], nq = q_lens[b];
+  const bool bad = prefix < 0 || (prefix & 127) || prefix > kBlockTokens * max_blocks || nnew < 0 || nnew > max_new ||
+                   nq < 0 || nq > nnew || nq > max_q;
+
+  // the lane's two rows
+  int ri[kCt], rh[kCt];
+  bool inrange[kCt], valid[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    const int r = 16 * (kCt * w + ct) + n;
+    ri[ct] = r / G;
+    rh[ct] = r - ri[ct] * G;
+    inrange[ct] = r < qt * G && i0 + ri[ct] < max_q;
+    valid[ct] = !bad && inrange[ct] && i0 + ri[ct] < nq;
+  }
+  auto out_row = [&](int ct) {
+    return out + ((static_cast<size_t>(b) * max_q + i0 + ri[ct]) * hq + static_cast<size_t>(kvh) * G + rh[ct]) *
+                     kHeadDim;
+  };
+  auto q_row = [&](int ct) {
+    const int i = valid[ct] ? i0 + ri[ct] : 0;
+    return q + ((static_cast<size_t>(b) * max_q + i) * hq + static_cast<size_t>(kvh) * G + (valid[ct] ? rh[ct] : 0)) *
+                   kHeadDim;
+  };
+
+  if (bad || i0 >= nq) {
+    // no query of this tile: zero rows (and flag a bad length)
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+      if (inrange[ct]) {
+        float* o = out_row(ct);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<float4*>(o + 16 * mt + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    if (bad && tid == 0 && flags) atomicOr(flags, kFlagBadSeqLen);
+    return;
+  }
+
+  PfState S;
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    S.m[ct] = -INFINITY;
+    S.l[ct] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) S.o[ct][i] = 0.f;
+  }
+  const int nblk = prefix >> 7;
+
+  // ---- packed prefix (rotated basis) ----------------------------------------------------------------
+  if (nblk > 0) {
+    float mx = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+      mx = fmaxf(mx, load_query(S.qv[ct], q_row(ct), valid[ct], g, lane, true, scale_log2 * kInvSqrt128));
+    mx = wave_max(mx);
+    if (lane == 0) L.qmax[w] = mx;
+    const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
+    const size_t kstride = static_cast<size_t>(kKPageBytes), vstride = static_cast<size_t>(kVPageBytes);
+    bool bad_page = false;
+    // page p + 1 is requested before page p is attended; a page id out of range reads page 0 and
+    // is skipped (the caller guarantees num_pages > 0)
+    auto request = [&](PageRaw& R, int page) {
+      const size_t unit = static_cast<size_t>(page >= 0 && page < num_pages ? page : 0) * hkv + kvh;
+      load_page_raw(R, k_pool + unit * kstride, v_pool + unit * vstride, tid);
+    };
+    PageRaw R;
+    int cur = bt[0];
+    request(R, cur);
+    for (int p = 0; p < nblk; ++p) {
+      const bool ok = cur >= 0 && cur < num_pages;
+      __syncthreads();  // every wave is done with the previous block
+      if (ok) store_page(L, R, tid);
+      const int nxt = p + 1 < nblk ? bt[p + 1] : 0;
+      if (p + 1 < nblk) request(R, nxt);
+      __syncthreads();
+      if (ok) page_factors(L, tid, lane);
+      __syncthreads();
+      if (ok) {
+        int nolim[kCt];
+#pragma unroll
+        for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0;
+        attend_block(S, L, lane, false, nolim);
+      } else {
+        bad_page = true;
+      }
+      cur = nxt;
+    }
+    if (bad_page && tid == 0 && flags) atomicOr(flags, kFlagBadPage);
+    // back to the original basis
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) {
+      fwht_rows(S.o[ct], lane);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) S.o[ct][i] *= kInvSqrt128;
+    }
+  }
+
+  // ---- fp16 rows (original basis, causal) ---------------------------------------------------------
+  {
+    float mx = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct)
+      mx = fmaxf(mx, load_query(S.qv[ct], q_row(ct), valid[ct], g, lane, false, scale_log2));
+    mx = wave_max(mx);
+    // the previous phase read qmax before its last barrier
+    if (lane == 0) L.qmax[w] = mx;
+  }
+  const int off = nnew - nq;                                  // fp16 row of query 0 minus 0
+  const int last = off + min(i0 + qt, nq) - 1;                // last fp16 row any query of the tile sees
+  const size_t rstride = static_cast<size_t>(hkv) * kHeadDim;
+  const uint16_t* kb = k_new + (static_cast<size_t>(b) * max_new * hkv + kvh) * kHeadDim;
+  const uint16_t* vb = v_new + (static_cast<size_t>(b) * max_new * hkv + kvh) * kHeadDim;
+  int lim_abs[kCt];
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) lim_abs[ct] = valid[ct] ? off + i0 + ri[ct] : 0x7FFFFFFF;
+  for (int fb = 0; fb * kBlockTokens <= last; ++fb) {
+    __syncthreads();
+    store_fp16_block(L, kb, vb, rstride, fb * kBlockTokens, nnew, tid);
+    __syncthreads();
+    fp16_factors(L, tid);
+    __syncthreads();
+    const int base = fb * kBlockTokens;
+    const bool masked = base + kBlockTokens - 1 > off + i0;
+    int lim[kCt];
+#pragma unroll
+    for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
+    attend_block(S, L, lane, masked, lim);
+  }
+
+  // ---- normalise and store ---------------------------------------------------------------------------
+#pragma unroll
+  for (int ct = 0; ct < kCt; ++ct) {
+    const float l = sum32(sum16(S.l[ct]));
+    const float inv = valid[ct] ? 1.0f / l : 0.f;
+    if (inrange[ct]) {
+      float* o = out_row(ct);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4*>(o + 16 * mt + 4 * g) =
+            make_float4(S.o[ct][4 * mt] * inv, S.o[ct][4 * mt + 1] * inv, S.o[ct][4 * mt + 2] * inv,
+                        S.o[ct][4 * mt + 3] * inv);
+    }
+  }
+}
+
+hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
+                          const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
+                          const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
+                          int hq, int hkv, float scale_log2, float* out, uint32_t* flags, hipStream_t stream) {
+  const int G = hq / hkv;
+  const int qt = kPfRows / G;
+  const int ntile = (max_q + qt - 1) / qt;
+  const long pairs8 = (static_cast<long>(batch) * hkv + 7) / 8;
+  const long groups = 8 * pairs8 * ntile;
+  if (groups == 0) return hipSuccess;
+  if (groups > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(prefill_kernel, dim3(static_cast<unsigned>(groups)), dim3(kPfThreads), 0, stream,
+                     static_cast<const uint16_t*>(q), max_q, static_cast<const uint8_t*>(k_pool),
+                     static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, prefix_lens,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), max_new, new_lens,
+                     q_lens, batch, hq, hkv, qt, ntile, scale_log2, out, flags);
+  return hipGetLastError();
+}
+
+}  // namespace kvarn

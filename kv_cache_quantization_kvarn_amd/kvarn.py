@@ -33,7 +33,8 @@ class kvarn_config(ctypes.Structure):
 EXPORTS = ("kvarn_config_parse", "kvarn_page_bytes", "kvarn_quantize_blocks", "kvarn_dequantize_blocks",
            "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_decode_attention_tail",
            "kvarn_fp16_page_bytes",
-           "kvarn_fp16_decode_attention", "kvarn_read_flags", "kvarn_status_string", "kvarn_last_error")
+           "kvarn_fp16_decode_attention", "kvarn_prefill_attention", "kvarn_read_flags", "kvarn_status_string",
+           "kvarn_last_error")
 
 KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_SHAPE, KVARN_ERR_UNSUPPORTED, KVARN_ERR_WORKSPACE, KVARN_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 FLAG_BAD_PAGE, FLAG_BAD_SEQLEN = 1, 2
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
         "kvarn_decode_attention_tail": (I32, [CFG, P, P, P, I32, P, I32, P, P, P, I32, I32, I32, F32, P, P, SZ, P, P]),
         "kvarn_fp16_page_bytes": (SZ, [CFG]),
         "kvarn_fp16_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
+        "kvarn_prefill_attention": (I32, [CFG, P, I32, P, P, I32, P, I32, P, P, P, I32, P, P, I32, I32, I32, F32, P,
+                                          P, P]),
         "kvarn_read_flags": (I32, [P, P, P]),
         "kvarn_status_string": (ctypes.c_char_p, [I32]),
         "kvarn_last_error": (ctypes.c_char_p, []),
@@ -165,6 +168,20 @@ def kvarn_fp16_decode_attention(cfg, q: torch.Tensor, k_cache: torch.Tensor, v_c
                                             _ptr(seq_lens), batch, hq, num_kv_heads, float(softmax_scale), _ptr(out),
                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _ptr(dev_flags), _stream(stream)))
+
+
+def kvarn_prefill_attention(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_table: torch.Tensor, prefix_lens: torch.Tensor, k_new: torch.Tensor,
+                            v_new: torch.Tensor, new_lens: torch.Tensor, q_lens: torch.Tensor, num_kv_heads: int,
+                            out: torch.Tensor, softmax_scale: float = 0.0, dev_flags: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """Chunked prefill: q fp16 [B, max_q, Hq, 128] over packed pages and fp16 rows k_new, v_new [B, max_new, Hkv, 128]."""
+    batch, max_q, hq = q.shape[0], q.shape[1], q.shape[2]
+    _check(_lib.kvarn_prefill_attention(ctypes.byref(cfg), _ptr(q), max_q, _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                        _ptr(block_table), block_table.shape[1], _ptr(prefix_lens), _ptr(k_new),
+                                        _ptr(v_new), k_new.shape[1], _ptr(new_lens), _ptr(q_lens), batch, hq,
+                                        num_kv_heads, float(softmax_scale), _ptr(out), _ptr(dev_flags),
+                                        _stream(stream)))
 
 
 def kvarn_read_flags(dev_flags: torch.Tensor, stream=None) -> int:

@@ -155,3 +155,30 @@ def test_fp16_decode_validation():
     assert f16(vc=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
     assert f16(q=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE
     assert f16(npages=0) == K.KVARN_ERR_SHAPE
+
+
+def test_prefill_validation():
+    cfg = K.kvarn_config_parse()
+
+    def pf(q=FAKE, mq=64, kp=FAKE, vp=FAKE, npages=4, bt=FAKE, mb=2, pl=FAKE, kn=FAKE, vn=FAKE, mn=64, nl=FAKE,
+           ql=FAKE, b=1, hq=32, hkv=8, out=FAKE):
+        return K.library().kvarn_prefill_attention(ctypes.byref(cfg), q, mq, kp, vp, npages, bt, mb, pl, kn, vn, mn,
+                                                   nl, ql, b, hq, hkv, 0.0, out, None, None)
+
+    # every call below either fails validation or has no work: nothing is launched
+    assert pf(hq=30) == K.KVARN_ERR_SHAPE
+    assert pf(hq=128, hkv=8) == K.KVARN_ERR_UNSUPPORTED
+    assert pf(b=0) == K.KVARN_OK
+    assert pf(mq=0) == K.KVARN_OK
+    assert pf(mq=-1) == K.KVARN_ERR_SHAPE
+    assert pf(mn=-1) == K.KVARN_ERR_SHAPE
+    assert pf(ql=None) == K.KVARN_ERR_NULL
+    assert pf(kn=None) == K.KVARN_ERR_NULL
+    assert pf(bt=None) == K.KVARN_ERR_NULL
+    assert pf(npages=0) == K.KVARN_ERR_SHAPE
+    assert pf(mb=1 << 24) == K.KVARN_ERR_SHAPE
+    assert pf(b=70000) == K.KVARN_ERR_SHAPE
+    assert pf(q=ctypes.c_void_p(0x1008)) == K.KVARN_ERR_SHAPE
+    assert pf(vn=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
+    assert pf(kp=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE
+    assert pf(out=ctypes.c_void_p(0x1001)) == K.KVARN_ERR_SHAPE
