@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--prefill-workload", default="prefill_llama3_8b_16x7680p512")
     ap.add_argument("--no-fp16-baseline", action="store_true",
                     help="skip the fp16 paged decode baseline (measured outside the timed steps)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -241,6 +243,39 @@ def fp16_baseline(case, K, synth, acc, stream, reps, flush, sink, kvarn_flush_s)
             "protocol": "both decodes timed after a 512 MB read that evicts the last-level cache; median of %d" % reps}
 
 
+def prefill_measure(K, synth, acc, cfg, name, stream, reps, flush, sink):
+    """Chunked prefill over packed pages plus fp16 rows (a matrix-core bound kernel), cache-flushed."""
+    import torch
+    w = synth.PREFILL_WORKLOADS[name]
+    x = synth.prefill_inputs(w, "cuda")
+    kp, vp = K.alloc_pools(cfg, x.num_pages, w.hkv)
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_quantize_blocks(cfg, x.k_prefix, x.v_prefix, x.pages, kp, vp, fl)
+    out = torch.empty(tuple(x.q.shape), dtype=torch.float32, device="cuda")
+
+    def run():
+        K.kvarn_prefill_attention(cfg, x.q, kp, vp, x.block_table, x.prefix_lens, x.k_new, x.v_new, x.new_lens,
+                                  x.q_lens, w.hkv, out, dev_flags=fl, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    t = timed_after_flush(run, reps, stream, flush, sink)
+    assert K.kvarn_read_flags(fl) == 0, "device flags set by the prefill"
+    pairs = acc.prefill_pairs(x.prefix_lens.tolist(), x.new_lens.tolist(), x.q_lens.tolist(), w.hq)
+    flops = acc.prefill_flops(pairs)
+    nbytes = acc.prefill_bytes(w.batch * (w.prefix // 128), w.hkv, K.kvarn_page_bytes(cfg, 0), K.kvarn_page_bytes(cfg, 1),
+                               w.batch * w.chunk, w.batch * w.chunk, w.hq)
+    tflops = flops / t / 1e12
+    del kp, vp, out, x
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "us_median": round(t * 1e6, 2), "tflops": round(tflops, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": acc.MFMA_FP16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / acc.MFMA_FP16_PEAK_TFLOPS, 4)},
+            "flops_per_launch": flops, "attended_pairs": pairs, "bytes_per_launch": nbytes,
+            "gbps": round(nbytes / t / 1e9, 1), "query_tokens_per_s": round(w.batch * w.chunk / t, 1),
+            "protocol": "median of %d launches, each after a 512 MB read that evicts the last-level cache" % reps}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -301,6 +336,10 @@ def main():
     if not args.no_fp16_baseline:
         fp16 = fp16_baseline(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = prefill_measure(K, synth, acc, cfg, args.prefill_workload, stream, args.flush_reps, flush, flush_sink)
+
     step_bytes = case.q_bytes + case.d_bytes
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes / (elapsed / args.steps) / 1e9
@@ -338,6 +377,8 @@ def main():
     }
     if fp16 is not None:
         line["fp16_baseline"] = fp16
+    if prefill is not None:
+        line["prefill"] = prefill
     # dominant kernel by time: the one whose launches take longer in the step
     if q_avg_s >= d_avg_s:
         dom, ach = "quantize_kernel", q_gbps

@@ -44,3 +44,30 @@ def decode_bytes(total_blocks_attended: int, kv_heads: int, batch: int, q_heads:
     return (total_blocks_attended * kv_heads * (k_page + v_page)
             + batch * q_heads * (HEAD_DIM * 2 + HEAD_DIM * 4)
             + total_blocks_attended * 4 + batch * 4)
+
+
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix rate, TFLOP/s
+
+
+def prefill_pairs(prefix_lens, new_lens, q_lens, q_heads: int) -> int:
+    """Attended (query head, key) pairs of one chunked-prefill call: query i of sequence b sees
+    prefix + (new - q) + i + 1 keys."""
+    total = 0
+    for p, n, q in zip(prefix_lens, new_lens, q_lens):
+        p, n, q = int(p), int(n), int(q)
+        total += q * (p + n - q) + q * (q + 1) // 2
+    return total * q_heads
+
+
+def prefill_flops(pairs: int) -> int:
+    """Algorithmic flops of attention: 2 x head_dim for the score and 2 x head_dim for the value
+    product of every attended pair."""
+    return 4 * HEAD_DIM * pairs
+
+
+def prefill_bytes(prefix_blocks_total: int, kv_heads: int, k_page: int, v_page: int, new_rows_total: int,
+                  q_rows_total: int, q_heads: int) -> int:
+    """Algorithmic HBM bytes of one prefill call: packed pages and fp16 rows read once, fp16 queries
+    in, fp32 output out."""
+    return (prefix_blocks_total * kv_heads * (k_page + v_page) + new_rows_total * kv_heads * HEAD_DIM * 2 * FP16_BYTES
+            + q_rows_total * q_heads * HEAD_DIM * (FP16_BYTES + 4))

@@ -6,7 +6,7 @@
 // at fp16 row new_len - q_len + i and attends to every packed token and, causally, to the fp16 rows
 // up to its own.
 //
-// A workgroup of four waves takes 64 (query token, head) rows of one (sequence, KV head): 64 / G
+// A workgroup of eight waves takes 128 (query token, head) rows of one (sequence, KV head): 128 / G
 // query tokens times the G heads that share the KV head.  Wave w owns rows 16w .. 16w + 15, one
 // 16-column tile of v_mfma_f32_16x16x32_f16.  The KV blocks stream through LDS once per workgroup:
 //
@@ -35,11 +35,16 @@ namespace kvarn {
 
 namespace {
 
-constexpr int kPfWaves = 4;
+constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kCt = 1;                          // 16-column MFMA tiles (16 rows each) per wave
 constexpr int kPfRows = 16 * kCt * kPfWaves;    // (query token, head) rows per workgroup
 constexpr int kMetaWords = kMetaBytes / 4;
+constexpr int kPageChunks = (kKPageBytes + kVPageBytes) / 16;                 // 960
+constexpr int kRawPerThread = (kPageChunks + kPfThreads - 1) / kPfThreads;
+constexpr int kF16Chunks = kBlockTokens * kHeadDim / 8;                         // 2048 per fp16 block
+constexpr int kF16PerThread = (kF16Chunks + kPfThreads - 1) / kPfThreads;
+static_assert(kPfThreads >= 2 * kHeadDim, "the factor step gives every channel and token a thread");
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
@@ -157,15 +162,16 @@ struct PfState {
 // ---------------------------------------------------------------------------------------------
 
 // The 960 16-byte chunks of a packed page (key page 608, value page 352): thread tid takes chunks
-// tid, tid + 256, tid + 512 and tid + 768.
+// tid, tid + T, tid + 2T, ... (T threads per workgroup).
 struct PageRaw {
-  u32x4 c[4];
+  u32x4 c[kRawPerThread];
 };
 
 __device__ __forceinline__ void load_page_raw(PageRaw& R, const uint8_t* __restrict__ kp,
                                               const uint8_t* __restrict__ vp, int tid) {
+  asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kRawPerThread; ++k) {
     const int id = tid + kPfThreads * k;
     if (id < 608) {
       R.c[k] = *reinterpret_cast<const u32x4*>(kp + 16 * id);
@@ -176,8 +182,11 @@ __device__ __forceinline__ void load_page_raw(PageRaw& R, const uint8_t* __restr
 }
 
 __device__ __forceinline__ void store_page(PfLds& L, const PageRaw& R, int tid) {
+  // the store addresses are recomputed for every page (a few integer operations) rather than kept
+  // live across the page loop, where registers are short
+  asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < kRawPerThread; ++k) {
     const int id = tid + kPfThreads * k;
     const u32x4 x = R.c[k];
     if (id < 512) {
@@ -219,6 +228,7 @@ __device__ __forceinline__ void store_page(PfLds& L, const PageRaw& R, int tid) 
 // Factors of a packed page (every wave finds the maxima itself; threads 0-127 write the per-channel
 // arrays, 128-255 the per-token ones).
 __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
+  asm volatile("" : "+v"(tid), "+v"(lane));
   const uint16_t* ksc = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaScale / 2;
   const uint16_t* kzr = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaZero / 2;
   const float* krho = reinterpret_cast<const float*>(L.kmeta) + kMetaRho / 4;
@@ -231,7 +241,9 @@ __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
   const float e = fmaxf(ex2(kgam[i0]) * half_bits_to_float(ksc[i0]), ex2(kgam[i1]) * half_bits_to_float(ksc[i1]));
   const float f = fmaxf(ex2(vrho[i0]) * half_bits_to_float(vsc[i0]), ex2(vrho[i1]) * half_bits_to_float(vsc[i1]));
   const float emax = wave_max(e), fmax = wave_max(f);
-  const float qmax = fmaxf(fmaxf(L.qmax[0], L.qmax[1]), fmaxf(L.qmax[2], L.qmax[3]));
+  float qmax = 0.f;
+#pragma unroll
+  for (int x = 0; x < kPfWaves; ++x) qmax = fmaxf(qmax, L.qmax[x]);
   float sa, inv_sa, sw, inv_sw;
   page_scale(qmax * emax, sa, inv_sa);
   page_scale(fmax, sw, inv_sw);
@@ -241,7 +253,7 @@ __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
     L.ep[j] = eg * half_bits_to_float(ksc[j]) * sa;
     L.fz[j] = eg * half_bits_to_float(kzr[j]);
     L.gs[j] = ex2(vgam[j]) * inv_sw;
-  } else {
+  } else if (tid < 2 * kHeadDim) {
     const int t = tid - kHeadDim;
     const float ev = ex2(vrho[t]);
     L.pk[t] = ex2(krho[t]) * inv_sa;
@@ -260,10 +272,12 @@ __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
 __device__ __forceinline__ void store_fp16_block(PfLds& L, const uint16_t* __restrict__ kbase,
                                                  const uint16_t* __restrict__ vbase, size_t rstride, int r0,
                                                  int nrows, int tid) {
+  asm volatile("" : "+v"(tid));
   _Float16* vh = reinterpret_cast<_Float16*>(L.vf);
 #pragma unroll 2
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < kF16PerThread; ++k) {
     const int id = tid + kPfThreads * k;
+    if (id >= kF16Chunks) break;
     const int t = id >> 4, c = id & 15;  // token t, channels 8c .. 8c + 7
     const bool live = r0 + t < nrows;
     const size_t off = static_cast<size_t>(live ? r0 + t : 0) * rstride + 8 * c;
@@ -291,7 +305,9 @@ __device__ __forceinline__ void store_fp16_block(PfLds& L, const uint16_t* __res
 
 // Unit factors of an fp16 block under the scale of the raw query.
 __device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
-  const float qmax = fmaxf(fmaxf(L.qmax[0], L.qmax[1]), fmaxf(L.qmax[2], L.qmax[3]));
+  float qmax = 0.f;
+#pragma unroll
+  for (int x = 0; x < kPfWaves; ++x) qmax = fmaxf(qmax, L.qmax[x]);
   float sa, inv_sa, sw, inv_sw;
   page_scale(qmax, sa, inv_sa);
   page_scale(1.0f, sw, inv_sw);
@@ -299,7 +315,7 @@ __device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
     L.ep[tid] = sa;
     L.fz[tid] = 0.f;
     L.gs[tid] = inv_sw;
-  } else {
+  } else if (tid < 2 * kHeadDim) {
     const int t = tid - kHeadDim;
     L.pk[t] = inv_sa;
     L.fv[t] = sw;
@@ -317,6 +333,7 @@ __device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
 // masked: apply the causal limit lim[ct] (block-relative index of the last key row the lane's row
 // may see) to this block.
 __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, bool masked, const int (&lim)[kCt]) {
+  asm volatile("" : "+v"(lane));  // fragment addresses are recomputed per block, not kept live
   const int n = lane & 15, g = lane >> 4;
   const float sa = L.sa, sw = L.sw;
 
@@ -573,8 +590,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
       __syncthreads();  // every wave is done with the previous block
       if (ok) store_page(L, R, tid);
       const int nxt = p + 1 < nblk ? bt[p + 1] : 0;
-      if (p + 1 < nblk) request(R, nxt);
       __syncthreads();
+      if (p + 1 < nblk) request(R, nxt);
       if (ok) page_factors(L, tid, lane);
       __syncthreads();
       if (ok) {

@@ -182,3 +182,10 @@ def test_prefill_validation():
     assert pf(vn=ctypes.c_void_p(0x1002)) == K.KVARN_ERR_SHAPE
     assert pf(kp=ctypes.c_void_p(0x1004)) == K.KVARN_ERR_SHAPE
     assert pf(out=ctypes.c_void_p(0x1001)) == K.KVARN_ERR_SHAPE
+
+
+def test_prefill_accounting_matches_brute_force():
+    prefix, new, q, hq = [256, 0, 384], [40, 7, 130], [25, 7, 1], 6
+    brute = sum(p + (n - k) + i + 1 for p, n, k in zip(prefix, new, q) for i in range(k)) * hq
+    assert accounting.prefill_pairs(prefix, new, q, hq) == brute
+    assert accounting.prefill_flops(brute) == 4 * 128 * brute
