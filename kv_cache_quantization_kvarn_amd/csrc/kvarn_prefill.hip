@@ -328,148 +328,180 @@ __device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// One block against the wave's 32 rows
+// One block against the wave's 16 rows
 // ---------------------------------------------------------------------------------------------
-// masked: apply the causal limit lim[ct] (block-relative index of the last key row the lane's row
-// may see) to this block.
-__device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, bool masked, const int (&lim)[kCt]) {
+static_assert(kCt == 1, "the pipelined block step holds one 16-row tile per wave");
+
+// Online-softmax step over one half of a block: the lane's 16 products sc[lt][r] of tokens
+// 32g + 16h + 4lt + r, scaled here by 2^rho / sa and masked past `lim`.  Updates m and the lane's
+// share of l; returns the factor that rescales everything accumulated before, the row's value
+// offset term (u, times sw) and the value-product B operands of token pairs (lt, lt + 2).
+struct HalfOut {
+  f16x8 whi[2], wlo[2];
+  float alpha, vinit;
+};
+
+__device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x4 (&sc)[4], int h, int g, int lim) {
+  HalfOut R;
+  const int t0 = 32 * g + 16 * h;
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int lt = 0; lt < 4; ++lt) {
+    const float4 p4 = *reinterpret_cast<const float4*>(&L.pk[t0 + 4 * lt]);
+    const float pkv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s = sc[lt][r] * pkv[r];
+      sc[lt][r] = t0 + 4 * lt + r > lim ? -INFINITY : s;
+      mloc = fmaxf(mloc, sc[lt][r]);
+    }
+  }
+  mloc = max32(max16(mloc));
+  const float m_new = fmaxf(S.m[0], mloc);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing visible yet: every weight stays 0
+  R.alpha = ex2(S.m[0] - m_use);
+  S.m[0] = m_new;
+  float lsum = 0.f, usum = 0.f;
+#pragma unroll
+  for (int lt = 0; lt < 4; ++lt) {
+    const float4 z4 = *reinterpret_cast<const float4*>(&L.zv[t0 + 4 * lt]);
+    const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = ex2(sc[lt][r] - m_use);
+      lsum += p;
+      usum = fmaf(p, zvv[r], usum);
+      sc[lt][r] = p;
+    }
+  }
+  S.l[0] = fmaf(S.l[0], R.alpha, lsum);
+  R.vinit = L.sw * sum32(sum16(usum));
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const float4 fa = *reinterpret_cast<const float4*>(&L.fv[t0 + 4 * hf]);
+    const float4 fb = *reinterpret_cast<const float4*>(&L.fv[t0 + 4 * hf + 8]);
+    const float fva[4] = {fa.x, fa.y, fa.z, fa.w}, fvb[4] = {fb.x, fb.y, fb.z, fb.w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split2(sc[hf][j], fva[j], sc[hf + 2][j], fvb[j], hi[j], lo[j]);
+    R.whi[hf] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    R.wlo[hf] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+  }
+  return R;
+}
+
+// The block runs as two halves of 64 tokens (lane g: tokens 32g .. 32g + 15, then 32g + 16 ..
+// 32g + 31), each its own online-softmax step, so that matrix products and vector arithmetic of
+// different halves interleave in one wave: the half-1 scores run under the half-0 softmax, the
+// half-0 value products under the half-1 softmax.  lim: block-relative index of the last key row the
+// lane's row may see (INT_MAX: all).
+__device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, const int (&lim)[kCt]) {
   asm volatile("" : "+v"(lane));  // fragment addresses are recomputed per block, not kept live
   const int n = lane & 15, g = lane >> 4;
-  const float sa = L.sa, sw = L.sw;
+  const float sa = L.sa;
 
   // ---- b_r over this lane's 32 channels, then over the row's four lanes ---------------------------
-  float kinit[kCt];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) kinit[ct] = 0.f;
+  float kinit = 0.f;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const float4 f0 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g]);
     const float4 f1 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g + 4]);
     const float fz8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) kinit[ct] = fmaf(S.qv[ct][8 * ks + s], fz8[s], kinit[ct]);
+    for (int s = 0; s < 8; ++s) kinit = fmaf(S.qv[0][8 * ks + s], fz8[s], kinit);
   }
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) kinit[ct] = sa * sum32(sum16(kinit[ct]));
+  kinit = sa * sum32(sum16(kinit));
 
-  // ---- scores: D[token][row] = codes x coefficients ----------------------------------------------
-  // lane (n, g) ends with tokens 32g + 4mt + r of its row
-  f32x4 sc[kCt][8];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) sc[ct][mt] = f32x4{kinit[ct], kinit[ct], kinit[ct], kinit[ct]};
+  // ---- coefficient B operands of the four channel steps (slots 2s2, 2s2 + 1: channels s2, s2 + 4) --
+  f16x8 bhi[4], blo[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const float4 e0 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g]);
     const float4 e1 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g + 4]);
     const float ep8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-    f16x8 bhi[kCt], blo[kCt];
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) {
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)  // slots 2s2, 2s2 + 1 hold channels s2, s2 + 4 of the chunk
-        split2(S.qv[ct][8 * ks + s2], ep8[s2], S.qv[ct][8 * ks + s2 + 4], ep8[s2 + 4], h[s2], l[s2]);
-      bhi[ct] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
-      blo[ct] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
-    }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int t = 32 * (n >> 2) + 4 * mt + (n & 3);
-      const f16x8 a = __builtin_bit_cast(f16x8, L.kf[16 * t + ((4 * ks + g) ^ n)]);
-#pragma unroll
-      for (int ct = 0; ct < kCt; ++ct) {
-        sc[ct][mt] = mfma16x16x32(a, bhi[ct], sc[ct][mt]);
-        sc[ct][mt] = mfma16x16x32(a, blo[ct], sc[ct][mt]);
-      }
-    }
+    for (int s2 = 0; s2 < 4; ++s2)
+      split2(S.qv[0][8 * ks + s2], ep8[s2], S.qv[0][8 * ks + s2 + 4], ep8[s2 + 4], hi[s2], lo[s2]);
+    bhi[ks] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    blo[ks] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
   }
 
-  // ---- online softmax, value-side B operands -----------------------------------------------------
-  f16x8 whi[kCt][2][2], wlo[kCt][2][2];  // [ct][vv][hf]
-  float vinit[kCt];
-#pragma unroll
-  for (int ct = 0; ct < kCt; ++ct) {
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const float4 p4 = *reinterpret_cast<const float4*>(&L.pk[32 * g + 4 * mt]);
-      const float pkv[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float s = sc[ct][mt][r] * pkv[r];
-        if (masked && 32 * g + 4 * mt + r > lim[ct]) s = -INFINITY;
-        sc[ct][mt][r] = s;
-        mloc = fmaxf(mloc, s);
-      }
-    }
-    mloc = max32(max16(mloc));
-    const float m_new = fmaxf(S.m[ct], mloc);
-    const float alpha = ex2(S.m[ct] - m_new);
-    if (__builtin_amdgcn_ballot_w64(m_new != S.m[ct]) != 0) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) S.o[ct][i] *= alpha;
-    }
-    S.m[ct] = m_new;
-    float lsum = 0.f, usum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const float4 z4 = *reinterpret_cast<const float4*>(&L.zv[32 * g + 4 * mt]);
-      const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = ex2(sc[ct][mt][r] - m_new);
-        lsum += p;
-        usum = fmaf(p, zvv[r], usum);
-        sc[ct][mt][r] = p;
-      }
-    }
-    S.l[ct] = fmaf(S.l[ct], alpha, lsum);
-    vinit[ct] = sw * sum32(sum16(usum));
-    // slot pair j of operand (vv, hf): tokens 32g + 16vv + 4hf + j (tile 4vv + hf) and + 8 (tile + 2)
-#pragma unroll
-    for (int vv = 0; vv < 2; ++vv)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int m1 = 4 * vv + hf, m2 = m1 + 2;
-        const float4 fa = *reinterpret_cast<const float4*>(&L.fv[32 * g + 4 * m1]);
-        const float4 fb = *reinterpret_cast<const float4*>(&L.fv[32 * g + 4 * m2]);
-        const float fva[4] = {fa.x, fa.y, fa.z, fa.w}, fvb[4] = {fb.x, fb.y, fb.z, fb.w};
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split2(sc[ct][m1][j], fva[j], sc[ct][m2][j], fvb[j], h[j], l[j]);
-        whi[ct][vv][hf] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
-        wlo[ct][vv][hf] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
-      }
-  }
+  // score tile mt: D[token][row], A = key row 32(n/4) + 4mt + n%4; lane (n, g) gets tokens 32g + 4mt + r
+  auto key_frag = [&](int mt, int ks) {
+    const int t = 32 * (n >> 2) + 4 * mt + (n & 3);
+    return __builtin_bit_cast(f16x8, L.kf[16 * t + ((4 * ks + g) ^ n)]);
+  };
+  // value tile mt: D[channel][row], A = value row 16mt + n, token chunk 4g + c (c = 2 * half + hf)
+  auto val_frag = [&](int mt, int c) {
+    const int j = 16 * mt + n;
+    return __builtin_bit_cast(f16x8, L.vf[16 * j + ((4 * g + c) ^ n)]);
+  };
 
-  // ---- values: D[channel][row] = codes x weights, then o += 2^gamma D -----------------------------
+  // ---- half 0 scores -----------------------------------------------------------------------------
+  f32x4 s0[4], s1[4];
+#pragma unroll
+  for (int lt = 0; lt < 4; ++lt) {
+    s0[lt] = f32x4{kinit, kinit, kinit, kinit};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f16x8 a = key_frag(lt, ks);
+      s0[lt] = mfma16x16x32(a, bhi[ks], s0[lt]);
+      s0[lt] = mfma16x16x32(a, blo[ks], s0[lt]);
+    }
+  }
+  // ---- half 1 scores, with the half-0 softmax -----------------------------------------------------
+#pragma unroll
+  for (int lt = 0; lt < 4; ++lt) {
+    s1[lt] = f32x4{kinit, kinit, kinit, kinit};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f16x8 a = key_frag(4 + lt, ks);
+      s1[lt] = mfma16x16x32(a, bhi[ks], s1[lt]);
+      s1[lt] = mfma16x16x32(a, blo[ks], s1[lt]);
+    }
+  }
+  const HalfOut h0 = softmax_half(S, L, s0, 0, g, lim[0]);
+
+  // ---- half 0 value products, with the half-1 softmax ---------------------------------------------
+  f32x4 d[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    const int j = 16 * mt + n;
-    f32x4 d[kCt];
+    d[mt] = f32x4{h0.vinit, h0.vinit, h0.vinit, h0.vinit};
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct) d[ct] = f32x4{vinit[ct], vinit[ct], vinit[ct], vinit[ct]};
+    for (int hf = 0; hf < 2; ++hf) {
+      const f16x8 a = val_frag(mt, hf);
+      d[mt] = mfma16x16x32(a, h0.whi[hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h0.wlo[hf], d[mt]);
+    }
+  }
+  const HalfOut h1 = softmax_half(S, L, s1, 1, g, lim[0]);
+
+  // ---- half 1 value products on the rescaled half-0 partial --------------------------------------
 #pragma unroll
-    for (int vv = 0; vv < 2; ++vv)
+  for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const f16x8 a = __builtin_bit_cast(f16x8, L.vf[16 * j + ((4 * g + 2 * vv + hf) ^ n)]);
+    for (int r = 0; r < 4; ++r) d[mt][r] = fmaf(d[mt][r], h1.alpha, h1.vinit);
 #pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) {
-          d[ct] = mfma16x16x32(a, whi[ct][vv][hf], d[ct]);
-          d[ct] = mfma16x16x32(a, wlo[ct][vv][hf], d[ct]);
-        }
-      }
+    for (int hf = 0; hf < 2; ++hf) {
+      const f16x8 a = val_frag(mt, 2 + hf);
+      d[mt] = mfma16x16x32(a, h1.whi[hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h1.wlo[hf], d[mt]);
+    }
+  }
+
+  // ---- o = alpha o + 2^gamma d --------------------------------------------------------------------
+  const float alpha = h0.alpha * h1.alpha;
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) S.o[0][i] *= alpha;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
     const float4 g4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
     const float gsv[4] = {g4.x, g4.y, g4.z, g4.w};
 #pragma unroll
-    for (int ct = 0; ct < kCt; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S.o[ct][4 * mt + r] = fmaf(d[ct][r], gsv[r], S.o[ct][4 * mt + r]);
+    for (int r = 0; r < 4; ++r) S.o[0][4 * mt + r] = fmaf(d[mt][r], gsv[r], S.o[0][4 * mt + r]);
   }
 }
 
@@ -597,8 +629,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
       if (ok) {
         int nolim[kCt];
 #pragma unroll
-        for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0;
-        attend_block(S, L, lane, false, nolim);
+        for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0x7FFFFFFF;
+        attend_block(S, L, lane, nolim);
       } else {
         bad_page = true;
       }
@@ -639,11 +671,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     fp16_factors(L, tid);
     __syncthreads();
     const int base = fb * kBlockTokens;
-    const bool masked = base + kBlockTokens - 1 > off + i0;
     int lim[kCt];
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
-    attend_block(S, L, lane, masked, lim);
+    attend_block(S, L, lane, lim);
   }
 
   // ---- normalise and store ---------------------------------------------------------------------------
