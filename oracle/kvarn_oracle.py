@@ -34,6 +34,12 @@ Parameters the pages leave open, fixed here (each is one reading):
   * the rounding decision is taken in fp32 (the precision the kernel computes
     in): u = fp32(fp32(N - z) / s), code = clamp(round-half-even(u), 0, L);
     a group whose fp16 scale is 0 stores all-zero codes;
+  * formats: the post names kvarn_k4v2_g128; the same name pattern with 8-bit
+    keys and 4-bit values (kvarn_k{4,8}v{2,4}_g128) keeps every step and changes
+    only the number of levels (2^bits - 1) and the packing: 8-bit key codes one
+    byte each, token-major (byte 128*t + c); 4-bit value codes channel-major, two
+    tokens per byte (byte 64*c + t//2, even token in the low nibble).  A page's
+    bit width follows from its byte count;
   * decode: query head h reads KV head h // (Hq / Hkv); logits scaled by
     1/sqrt(128) unless a positive scale is given; plain softmax; output in the
     original (unrotated) basis.
@@ -49,14 +55,30 @@ BLOCK = 128
 HEAD_DIM = 128
 ITERS = 4
 EPS = 1e-6
-K_LEVELS = 15  # 4-bit keys
+K_LEVELS = 15  # 4-bit keys (the format the post names)
 V_LEVELS = 3   # 2-bit values
+K_BITS_ALLOWED = (4, 8)
+V_BITS_ALLOWED = (2, 4)
+META_BYTES = 2 * 256 + 2 * 512
 
 # Page byte format (one page = one 128-token block of one KV head).
 K_CODES_BYTES = BLOCK * HEAD_DIM // 2      # 8192: token-major, two channels per byte
 V_CODES_BYTES = BLOCK * HEAD_DIM // 4      # 4096: channel-major, four tokens per byte
 K_PAGE_BYTES = K_CODES_BYTES + 2 * 256 + 2 * 512   # 9728
 V_PAGE_BYTES = V_CODES_BYTES + 2 * 256 + 2 * 512   # 5632
+
+
+def page_bytes(bits: int) -> int:
+    """Bytes of one page whose codes have `bits` bits: 128 x 128 codes plus the metadata."""
+    return BLOCK * HEAD_DIM * bits // 8 + META_BYTES
+
+
+def bits_of_page(nbytes: int, is_v: bool) -> int:
+    """Code width of a page from its byte count (unambiguous within keys and within values)."""
+    for b in (V_BITS_ALLOWED if is_v else K_BITS_ALLOWED):
+        if nbytes == page_bytes(b):
+            return b
+    raise ValueError("a %s page of %d bytes matches no format" % ("value" if is_v else "key", nbytes))
 
 
 # --------------------------------------------------------------------------
@@ -142,8 +164,9 @@ def rtn_codes(values: np.ndarray, s16, z16, levels: int) -> np.ndarray:
     return np.clip(np.rint(u), 0, levels).astype(np.uint8)
 
 
-def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS) -> dict:
-    """Quantise one fp16 block [128 tokens, 128 channels] of K (is_v False) or V.
+def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS, bits: int = 0) -> dict:
+    """Quantise one fp16 block [128 tokens, 128 channels] of K (is_v False) or V, codes of
+    ``bits`` bits (default: 4 for K, 2 for V; levels 2^bits - 1).
 
     Returns the stored fields: codes [128, 128] (token, channel), scale and zero
     (fp16, per channel for K, per token for V), rho (fp32 per token) and gamma
@@ -155,15 +178,17 @@ def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = 
     rho32 = rho.astype(np.float32)
     gam32 = gam.astype(np.float32)
     n32 = normalized(r, rho32, gam32).astype(np.float32)
+    bits = bits or (2 if is_v else 4)
+    levels = (1 << bits) - 1
     codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
     ngroups = BLOCK if is_v else HEAD_DIM
     scale = np.zeros(ngroups, dtype=np.float16)
     zero = np.zeros(ngroups, dtype=np.float16)
     for g in range(ngroups):
         if is_v:
-            codes[g, :], scale[g], zero[g] = rtn_group(n32[g, :], V_LEVELS)
+            codes[g, :], scale[g], zero[g] = rtn_group(n32[g, :], levels)
         else:
-            codes[:, g], scale[g], zero[g] = rtn_group(n32[:, g], K_LEVELS)
+            codes[:, g], scale[g], zero[g] = rtn_group(n32[:, g], levels)
     return {"codes": codes, "scale": scale, "zero": zero, "rho": rho32, "gamma": gam32}
 
 
@@ -186,13 +211,18 @@ def dequantize_tile(fields: dict, is_v: bool) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Page byte format (stage 4 output; the layout itself is a reading)
 # --------------------------------------------------------------------------
-def pack_k_codes(codes: np.ndarray) -> bytes:
-    """K codes [token, channel] -> 8192 bytes: byte 64*t + k = ch 2k (bits 0-3) | ch 2k+1 (bits 4-7)."""
+def pack_k_codes(codes: np.ndarray, bits: int = 4) -> bytes:
+    """K codes [token, channel], token-major.  4 bits -> 8192 bytes: byte 64*t + k = ch 2k (bits 0-3)
+    | ch 2k+1 (bits 4-7).  8 bits -> 16384 bytes: byte 128*t + c."""
     c = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return c.tobytes()
     return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8).tobytes()
 
 
-def unpack_k_codes(buf: bytes) -> np.ndarray:
+def unpack_k_codes(buf: bytes, bits: int = 4) -> np.ndarray:
+    if bits == 8:
+        return np.frombuffer(bytes(buf[:BLOCK * HEAD_DIM]), dtype=np.uint8).reshape(BLOCK, HEAD_DIM).copy()
     b = np.frombuffer(bytes(buf[:K_CODES_BYTES]), dtype=np.uint8).reshape(BLOCK, HEAD_DIM // 2)
     codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
     codes[:, 0::2] = b & 0xF
@@ -200,26 +230,30 @@ def unpack_k_codes(buf: bytes) -> np.ndarray:
     return codes
 
 
-def pack_v_codes(codes: np.ndarray) -> bytes:
-    """V codes [token, channel] -> 4096 bytes: byte 32*c + k holds token 4k+i at bits 2i..2i+1."""
+def pack_v_codes(codes: np.ndarray, bits: int = 2) -> bytes:
+    """V codes [token, channel], channel-major.  2 bits -> 4096 bytes: byte 32*c + k holds token 4k+i at
+    bits 2i..2i+1.  4 bits -> 8192 bytes: byte 64*c + k holds token 2k (bits 0-3) and 2k+1 (bits 4-7)."""
     c = np.asarray(codes, dtype=np.uint8)
-    out = np.zeros((HEAD_DIM, BLOCK // 4), dtype=np.uint8)
-    for i in range(4):
-        out |= (c[i::4, :].T << (2 * i)).astype(np.uint8)
+    per = 8 // bits
+    out = np.zeros((HEAD_DIM, BLOCK // per), dtype=np.uint8)
+    for i in range(per):
+        out |= (c[i::per, :].T << (bits * i)).astype(np.uint8)
     return out.tobytes()
 
 
-def unpack_v_codes(buf: bytes) -> np.ndarray:
-    b = np.frombuffer(bytes(buf[:V_CODES_BYTES]), dtype=np.uint8).reshape(HEAD_DIM, BLOCK // 4)
+def unpack_v_codes(buf: bytes, bits: int = 2) -> np.ndarray:
+    per = 8 // bits
+    b = np.frombuffer(bytes(buf[:BLOCK * HEAD_DIM // per]), dtype=np.uint8).reshape(HEAD_DIM, BLOCK // per)
     codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
-    for i in range(4):
-        codes[i::4, :] = ((b >> (2 * i)) & 3).T
+    for i in range(per):
+        codes[i::per, :] = ((b >> (bits * i)) & ((1 << bits) - 1)).T
     return codes
 
 
-def encode_page(fields: dict, is_v: bool) -> bytes:
+def encode_page(fields: dict, is_v: bool, bits: int = 0) -> bytes:
     """Page = codes | scale fp16[128] | zero fp16[128] | rho fp32[128 tokens] | gamma fp32[128 channels], little endian."""
-    codes = pack_v_codes(fields["codes"]) if is_v else pack_k_codes(fields["codes"])
+    bits = bits or (2 if is_v else 4)
+    codes = pack_v_codes(fields["codes"], bits) if is_v else pack_k_codes(fields["codes"], bits)
     meta = (np.asarray(fields["scale"], dtype="<f2").tobytes() + np.asarray(fields["zero"], dtype="<f2").tobytes()
             + np.asarray(fields["rho"], dtype="<f4").tobytes() + np.asarray(fields["gamma"], dtype="<f4").tobytes())
     return codes + meta
@@ -227,10 +261,9 @@ def encode_page(fields: dict, is_v: bool) -> bytes:
 
 def decode_page(buf: bytes, is_v: bool) -> dict:
     buf = bytes(buf)
-    ncode = V_CODES_BYTES if is_v else K_CODES_BYTES
-    if len(buf) != ncode + 1536:
-        raise ValueError("page has %d bytes, expected %d" % (len(buf), ncode + 1536))
-    codes = unpack_v_codes(buf[:ncode]) if is_v else unpack_k_codes(buf[:ncode])
+    bits = bits_of_page(len(buf), is_v)
+    ncode = BLOCK * HEAD_DIM * bits // 8
+    codes = unpack_v_codes(buf[:ncode], bits) if is_v else unpack_k_codes(buf[:ncode], bits)
     o = ncode
     scale = np.frombuffer(buf[o:o + 256], dtype="<f2").copy()
     zero = np.frombuffer(buf[o + 256:o + 512], dtype="<f2").copy()
@@ -245,15 +278,19 @@ def decode_page(buf: bytes, is_v: bool) -> dict:
 def quantize_blocks(k16: np.ndarray, v16: np.ndarray, dst_pages, k_pool: np.ndarray, v_pool: np.ndarray) -> None:
     """k16, v16: fp16 [n_blocks*128, Hkv, 128]; block b of head h goes to page dst_pages[b] of each pool.
 
-    Pools are uint8 arrays [num_pages, Hkv, page_bytes], written in place.
+    Pools are uint8 arrays [num_pages, Hkv, page_bytes], written in place; the page sizes give the
+    code widths of the format.
     """
     n_tok, hkv, _ = k16.shape
+    kb, vb = bits_of_page(k_pool.shape[2], False), bits_of_page(v_pool.shape[2], True)
     for b in range(n_tok // BLOCK):
         p = int(dst_pages[b])
         for h in range(hkv):
             sl = slice(BLOCK * b, BLOCK * (b + 1))
-            k_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(k16[sl, h, :], False), False), np.uint8)
-            v_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(v16[sl, h, :], True), True), np.uint8)
+            k_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(k16[sl, h, :], False, bits=kb), False, kb),
+                                            np.uint8)
+            v_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(v16[sl, h, :], True, bits=vb), True, vb),
+                                            np.uint8)
 
 
 def dequantize_pages(pool: np.ndarray, pages, head: int, is_v: bool) -> np.ndarray:

@@ -196,7 +196,7 @@ def test_power_of_two_token_scaling_shifts_rho():
 
 
 # ---------------------------------------------------------------- rounding
-@pytest.mark.parametrize("levels", [15, 3])
+@pytest.mark.parametrize("levels", [255, 15, 3])
 def test_rtn_picks_nearest_grid_point(levels):
     r = rng(15)
     for trial in range(50):
@@ -213,7 +213,7 @@ def test_rtn_picks_nearest_grid_point(levels):
         assert q[np.argmin(v)] == 0 and q[np.argmax(v)] == levels
 
 
-@pytest.mark.parametrize("levels", [15, 3])
+@pytest.mark.parametrize("levels", [255, 15, 3])
 def test_rtn_scale_zero_and_error_bound(levels):
     r = rng(16)
     for trial in range(50):
@@ -554,3 +554,82 @@ def test_prefill_is_causal_and_empty_prefix_is_causal_sdpa():
     b = o.prefill(q, *args, kn2, vn2, np.array([n]), np.array([n]), 1)
     assert np.array_equal(a[0, :30], b[0, :30])
     assert not np.allclose(a[0, 30:], b[0, 30:])
+
+
+# ------------------------------------------------- format variants (8-bit keys, 4-bit values)
+def test_wide_pack_roundtrips_and_sizes():
+    assert (o.page_bytes(4), o.page_bytes(8), o.page_bytes(2)) == (9728, 17920, 5632)
+    assert o.bits_of_page(17920, False) == 8 and o.bits_of_page(9728, True) == 4 and o.bits_of_page(9728, False) == 4
+    with pytest.raises(ValueError):
+        o.bits_of_page(5632, False)
+    b8 = (np.arange(16384, dtype=np.int64) * 13 % 256).astype(np.uint8).tobytes()
+    assert o.pack_k_codes(o.unpack_k_codes(b8, 8), 8) == b8
+    b4 = (np.arange(8192, dtype=np.int64) * 7 % 256).astype(np.uint8).tobytes()
+    assert o.pack_v_codes(o.unpack_v_codes(b4, 4), 4) == b4
+    ck = rng(70).integers(0, 256, (128, 128)).astype(np.uint8)
+    cv = rng(71).integers(0, 16, (128, 128)).astype(np.uint8)
+    assert np.array_equal(o.unpack_k_codes(o.pack_k_codes(ck, 8), 8), ck)
+    assert np.array_equal(o.unpack_v_codes(o.pack_v_codes(cv, 4), 4), cv)
+
+
+@pytest.mark.parametrize("t,c", [(0, 0), (1, 0), (5, 64), (127, 127), (34, 3)])
+def test_wide_single_code_bit_positions(t, c):
+    ck = np.zeros((128, 128), np.uint8)
+    ck[t, c] = 201
+    bk = np.frombuffer(o.pack_k_codes(ck, 8), np.uint8)
+    assert np.flatnonzero(bk).tolist() == [128 * t + c] and bk[128 * t + c] == 201
+    cv = np.zeros((128, 128), np.uint8)
+    cv[t, c] = 11
+    bv = np.frombuffer(o.pack_v_codes(cv, 4), np.uint8)
+    assert np.flatnonzero(bv).tolist() == [64 * c + t // 2]
+    assert bv[64 * c + t // 2] == 11 << (4 * (t % 2))
+
+
+def test_wide_rtn_nearest_grid_point_255_levels():
+    r = rng(72)
+    for trial in range(20):
+        v = (r.standard_normal(128) * r.lognormal(0, 1)).astype(np.float32)
+        q, s, z = o.rtn_group(v, 255)
+        grid = float(z) + float(s) * np.arange(256)
+        for i in range(128):
+            d = np.abs(grid - float(v[i]))
+            assert d[q[i]] <= d.min() + 1e-6 * float(s)
+        assert q.min() == 0 and q.max() == 255
+
+
+def test_wide_group_axes_and_error_falls_with_bits():
+    x = fp16_block(73, outliers=4, mult=20.0)
+    xd = x.astype(np.float64)
+    fk8, fv4 = o.quantize_tile(x, False, bits=8), o.quantize_tile(x, True, bits=4)
+    assert np.all(fk8["codes"].min(axis=0) == 0) and np.all(fk8["codes"].max(axis=0) == 255)
+    assert np.all(fv4["codes"].min(axis=1) == 0) and np.all(fv4["codes"].max(axis=1) == 15)
+    # same rotation and normalisers whatever the width; only the grid changes
+    fk4 = o.quantize_tile(x, False)
+    assert np.array_equal(fk8["rho"], fk4["rho"]) and np.array_equal(fk8["gamma"], fk4["gamma"])
+    ek4 = np.linalg.norm(o.dequantize_tile(fk4, False) - xd)
+    ek8 = np.linalg.norm(o.dequantize_tile(fk8, False) - xd)
+    ev2 = np.linalg.norm(o.dequantize_tile(o.quantize_tile(x, True), True) - xd)
+    ev4 = np.linalg.norm(o.dequantize_tile(fv4, True) - xd)
+    # 16x and 5x finer grids: the error falls by well over the width ratio's square root
+    assert ek8 < ek4 / 8 and ev4 < ev2 / 3
+    for f, is_v, b in ((fk8, False, 8), (fv4, True, 4)):
+        g = o.decode_page(o.encode_page(f, is_v, b), is_v)
+        for key in f:
+            assert np.array_equal(np.asarray(f[key]), np.asarray(g[key]))
+
+
+def test_wide_pools_decode_closer_to_fp16_attention():
+    r = rng(74)
+    k = r.standard_normal((256, 1, 128)).astype(np.float16)
+    v = r.standard_normal((256, 1, 128)).astype(np.float16)
+    q = r.standard_normal((1, 4, 128)).astype(np.float16)
+    pages = np.arange(2)
+    exact = np.stack([o.attention(q[0, h].astype(np.float64), k[:, 0].astype(np.float64),
+                                  v[:, 0].astype(np.float64), 1 / np.sqrt(128)) for h in range(4)])
+    errs = {}
+    for kb, vb in ((4, 2), (8, 4)):
+        kp = np.zeros((2, 1, o.page_bytes(kb)), np.uint8)
+        vp = np.zeros((2, 1, o.page_bytes(vb)), np.uint8)
+        o.quantize_blocks(k, v, pages, kp, vp)
+        errs[kb, vb] = np.abs(o.decode(q, kp, vp, pages[None, :], np.array([256]), 1)[0] - exact).max()
+    assert errs[8, 4] < errs[4, 2] / 3
