@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-formats", action="store_true", help="skip the other code widths (k4v4, k8v2, k8v4)")
     ap.add_argument("--prefill-workload", default="prefill_llama3_8b_16x7680p512")
     ap.add_argument("--no-fp16-baseline", action="store_true",
                     help="skip the fp16 paged decode baseline (measured outside the timed steps)")
@@ -276,6 +277,46 @@ def prefill_measure(K, synth, acc, cfg, name, stream, reps, flush, sink):
             "protocol": "median of %d launches, each after a 512 MB read that evicts the last-level cache" % reps}
 
 
+def formats_measure(K, w, case, stream, reps, flush, sink):
+    """Quantise and decode launches of the workload's first layer in the other code widths.  Decode in
+    these formats runs on the generic path (the prefill kernel, one query per sequence)."""
+    import torch
+    from kv_cache_quantization_kvarn_amd import accounting as acc
+    res = {}
+    L0 = case.layers[0]
+    for name in ("kvarn_k4v4_g128", "kvarn_k8v2_g128", "kvarn_k8v4_g128"):
+        cfg = K.kvarn_config_parse(name)
+        kp, vp = K.alloc_pools(cfg, case.pm.num_pages, w.hkv)
+        if w.append_blocks:
+            from kv_cache_quantization_kvarn_amd import synth
+            k, v = synth.layer_kv(w, 0, synth.total_prefix_blocks(w) * 128, "cuda")
+            K.kvarn_quantize_blocks(cfg, k, v, case.pm.prefix_pages.cuda(), kp, vp, case.flags)
+            del k, v
+
+        def quant():
+            K.kvarn_quantize_blocks(cfg, L0["k"], L0["v"], L0["dst"], kp, vp, case.flags)
+
+        def dec():
+            K.kvarn_decode_attention(cfg, L0["q"], kp, vp, case.bt, case.sl, w.hkv, case.out, case.ws,
+                                     dev_flags=case.flags)
+
+        quant()
+        dec()
+        torch.cuda.synchronize()
+        tq = timed_after_flush(quant, reps, stream, flush, sink)
+        td = timed_after_flush(dec, reps, stream, flush, sink)
+        assert K.kvarn_read_flags(case.flags) == 0, "device flags set in format " + name
+        kb, vb = K.kvarn_page_bytes(cfg, False), K.kvarn_page_bytes(cfg, True)
+        qb = acc.quantize_bytes(L0["dst"].numel(), w.hkv, kb, vb)
+        db = acc.decode_bytes(int(case.pm.seq_lens.sum().item()) // 128, w.hkv, w.batch, w.hq, kb, vb)
+        res[name] = {"quantize_us": round(tq * 1e6, 2), "quantize_gbps": round(qb / tq / 1e9, 1),
+                     "decode_us": round(td * 1e6, 2), "decode_gbps": round(db / td / 1e9, 1),
+                     "page_bytes": [kb, vb], "decode_path": "generic (prefill kernel)"}
+        del kp, vp
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -336,6 +377,9 @@ def main():
     if not args.no_fp16_baseline:
         fp16 = fp16_baseline(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
 
+    formats = None
+    if not args.no_formats:
+        formats = formats_measure(K, w, case, stream, max(5, args.flush_reps // 2), flush, flush_sink)
     prefill = None
     if not args.no_prefill:
         prefill = prefill_measure(K, synth, acc, cfg, args.prefill_workload, stream, args.flush_reps, flush, flush_sink)
@@ -379,6 +423,8 @@ def main():
         line["fp16_baseline"] = fp16
     if prefill is not None:
         line["prefill"] = prefill
+    if formats is not None:
+        line["formats"] = formats
     # dominant kernel by time: the one whose launches take longer in the step
     if q_avg_s >= d_avg_s:
         dom, ach = "quantize_kernel", q_gbps

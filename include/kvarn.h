@@ -39,7 +39,7 @@ typedef enum {
   KVARN_OK = 0,
   KVARN_ERR_NULL = -1,        /* a required pointer is NULL */
   KVARN_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
-  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k4v2_g128 / head_dim 128 / block 128 */
+  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k{4,8}v{2,4}_g128 / head_dim 128 / block 128 */
   KVARN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
   KVARN_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
 } kvarn_status;
@@ -48,9 +48,12 @@ typedef enum {
 #define KVARN_FLAG_BAD_PAGE 1u    /* a page id outside [0, num_pages): that block is skipped */
 #define KVARN_FLAG_BAD_SEQLEN 2u  /* seq_len < 0, not a multiple of 128, or above max_blocks*128: sequence output is 0 */
 
-/* Format parameters.  Only the values of "kvarn_k4v2_g128" are supported:
- * head_dim 128, block_tokens 128, k_bits 4, v_bits 2, group_size 128,
- * norm_iters 4, eps 1e-6. */
+/* Format parameters.  Supported: head_dim 128, block_tokens 128, k_bits 4 or
+ * 8, v_bits 2 or 4, group_size 128, norm_iters 4, eps 1e-6.  The post names
+ * kvarn_k4v2_g128; the wider codes keep every step of the method and change
+ * the number of levels (2^bits - 1) and the packing only.  The matrix-core
+ * decode kernel serves k4v2; decode in the other formats runs on the prefill
+ * kernel with one query per sequence (same contract, no workspace use). */
 typedef struct {
   int32_t head_dim;
   int32_t block_tokens;
@@ -63,34 +66,37 @@ typedef struct {
 
 /* Fill *out from a cache dtype name of the form "kvarn_k<K>v<V>_g<G>"
  * (blog post, section "Pratik Çıkarımlar").  Parses any such name; names other
- * than "kvarn_k4v2_g128" parse but return KVARN_ERR_UNSUPPORTED. */
+ * than kvarn_k{4,8}v{2,4}_g128 parse but return KVARN_ERR_UNSUPPORTED. */
 kvarn_status kvarn_config_parse(const char* name, kvarn_config* out);
 
-/* Bytes of one page (one 128-token block of one KV head): 9728 for K
- * (is_v = 0), 5632 for V (is_v = 1); 0 for an unsupported config.
+/* Bytes of one page (one 128-token block of one KV head): C + 1536 with C =
+ * 128*128*bits/8 code bytes: K (is_v = 0) 9728 for 4 bits, 17920 for 8 bits;
+ * V (is_v = 1) 5632 for 2 bits, 9728 for 4 bits; 0 for an unsupported config.
  *
- * K page: [0, 8192) codes, token-major: byte 64*t + k holds channel 2k in bits
- *         0-3 and channel 2k+1 in bits 4-7 of token t;
- *         [8192, 8448) scale fp16[128 channels]; [8448, 8704) zero fp16[128 channels];
- *         [8704, 9216) rho fp32[128 tokens];     [9216, 9728) gamma fp32[128 channels].
- * V page: [0, 4096) codes, channel-major: byte 32*c + k holds token 4k+i in bits
- *         2i..2i+1 of channel c;
- *         [4096, 4352) scale fp16[128 tokens]; [4352, 4608) zero fp16[128 tokens];
- *         [4608, 5120) rho fp32[128 tokens];   [5120, 5632) gamma fp32[128 channels].
+ * K page: [0, C) codes, token-major: 4 bits: byte 64*t + k holds channel 2k in
+ *         bits 0-3 and channel 2k+1 in bits 4-7 of token t; 8 bits: byte 128*t + c;
+ *         then scale fp16[128 channels], zero fp16[128 channels], rho fp32[128
+ *         tokens], gamma fp32[128 channels] at C, C + 256, C + 512, C + 1024.
+ * V page: [0, C) codes, channel-major: 2 bits: byte 32*c + k holds token 4k+i
+ *         in bits 2i..2i+1 of channel c; 4 bits: byte 64*c + k holds token 2k in
+ *         bits 0-3 and token 2k+1 in bits 4-7;
+ *         then scale fp16[128 tokens], zero fp16[128 tokens], rho fp32[128
+ *         tokens], gamma fp32[128 channels] at the same offsets from C.
  * All little endian.  Dequantisation: x^[t] = H (N^ * 2^(rho[t] + gamma)), with
  * N^ = scale * code + zero and H the orthonormal Sylvester Hadamard matrix. */
 size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v);
 
 /* Quantise n_blocks 128-token blocks of K and V (blog post, "KVarN Nasıl
- * Çalışır?": rotate, normalise, round to nearest, pack) into pages.
+ * Çalışır?": rotate, normalise, round to nearest, pack) into pages of the
+ * config's format.
  *   k, v       fp16 [n_blocks*128, num_kv_heads, 128], contiguous; block b is
  *              rows 128b .. 128b+127.
  *   dst_pages  int32 [n_blocks] (device): page receiving block b (all heads).
  *              Entries must be distinct.  An entry outside [0, num_pages)
  *              sets KVARN_FLAG_BAD_PAGE and that block is not written.
- *   k_pool     bytes [num_pages, num_kv_heads, 9728]; v_pool bytes
- *              [num_pages, num_kv_heads, 5632]; written in place.  The pools
- *              must not overlap k or v.
+ *   k_pool     bytes [num_pages, num_kv_heads, kvarn_page_bytes(cfg, 0)];
+ *              v_pool bytes [num_pages, num_kv_heads, kvarn_page_bytes(cfg, 1)];
+ *              written in place.  The pools must not overlap k or v.
  *   n_blocks == 0 is a no-op returning KVARN_OK. */
 kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
                                    int32_t num_kv_heads, const int32_t* dst_pages, void* k_pool, void* v_pool,

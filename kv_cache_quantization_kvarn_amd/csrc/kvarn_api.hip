@@ -11,9 +11,11 @@
 
 namespace kvarn {
 hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
-                           void* k_pool, void* v_pool, int num_pages, uint32_t* flags, hipStream_t stream);
+                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, uint32_t* flags,
+                           hipStream_t stream);
 hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
-                             int n_blocks, int hkv, float* k_out, float* v_out, uint32_t* flags, hipStream_t stream);
+                             int n_blocks, int hkv, int kbits, int vbits, float* k_out, float* v_out,
+                             uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
                          const void* v_tail, int batch, int hq, int hkv, int blocks_per_split, int max_splits,
@@ -26,13 +28,13 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, float scale_log2, float* out, uint32_t* flags, hipStream_t stream);
+                          int hq, int hkv, int kbits, int vbits, int mode, float scale_log2, float* out,
+                          uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
 
-constexpr int kKPage = 9728;
-constexpr int kVPage = 5632;
+constexpr int kMetaBytes = 1536;
 constexpr int kMaxGroup = 8;
 constexpr int kPartFloats = 128 + 2;
 constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
@@ -46,16 +48,24 @@ kvarn_status fail(kvarn_status s, const char* msg) {
   return s;
 }
 
+// kvarn_k{4,8}v{2,4}_g128 with head_dim 128 and 128-token blocks
 bool config_ok(const kvarn_config* c) {
-  return c && c->head_dim == 128 && c->block_tokens == 128 && c->k_bits == 4 && c->v_bits == 2 &&
-         c->group_size == 128 && c->norm_iters == 4 && std::fabs(c->eps - 1e-6f) <= 1e-12f;
+  return c && c->head_dim == 128 && c->block_tokens == 128 && (c->k_bits == 4 || c->k_bits == 8) &&
+         (c->v_bits == 2 || c->v_bits == 4) && c->group_size == 128 && c->norm_iters == 4 &&
+         std::fabs(c->eps - 1e-6f) <= 1e-12f;
 }
+
+// the format the post names, which the matrix-core decode kernel is written for
+bool is_k4v2(const kvarn_config* c) { return c->k_bits == 4 && c->v_bits == 2; }
 
 kvarn_status check_config(const kvarn_config* c) {
   if (!c) return fail(KVARN_ERR_NULL, "config is NULL");
-  if (!config_ok(c)) return fail(KVARN_ERR_UNSUPPORTED, "only kvarn_k4v2_g128 (head_dim 128, block 128) is supported");
+  if (!config_ok(c))
+    return fail(KVARN_ERR_UNSUPPORTED, "supported formats: kvarn_k{4,8}v{2,4}_g128 (head_dim 128, block 128)");
   return KVARN_OK;
 }
+
+size_t page_bytes_of(int bits) { return static_cast<size_t>(128) * 128 * bits / 8 + kMetaBytes; }
 
 struct DecodePlan {
   int blocks_per_split;
@@ -145,6 +155,14 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
   const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kind != DecodeKind::fp16 && !is_k4v2(cfg)) {
+    // Other code widths: the generic path, the prefill kernel with one query per sequence that sees
+    // every packed token (and every tail row).  The workspace is not used.
+    return launch_status(kvarn::launch_prefill(q, 1, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
+                                               tail ? k_tail : q, tail ? v_tail : q, tail ? 128 : 0, seq_lens,
+                                               seq_lens, batch, num_q_heads, num_kv_heads, cfg->k_bits, cfg->v_bits,
+                                               tail ? 2 : 1, scale_log2, out, dev_flags, st));
+  }
   if (kind == DecodeKind::fp16)
     return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                                    batch, num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits,
@@ -171,13 +189,13 @@ kvarn_status kvarn_config_parse(const char* name, kvarn_config* out) {
   out->group_size = gs;
   out->norm_iters = 4;
   out->eps = 1e-6f;
-  if (!config_ok(out)) return fail(KVARN_ERR_UNSUPPORTED, "only kvarn_k4v2_g128 is implemented");
+  if (!config_ok(out)) return fail(KVARN_ERR_UNSUPPORTED, "implemented formats: kvarn_k{4,8}v{2,4}_g128");
   return KVARN_OK;
 }
 
 size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v) {
   if (!config_ok(cfg)) return 0;
-  return is_v ? kVPage : kKPage;
+  return page_bytes_of(is_v ? cfg->v_bits : cfg->k_bits);
 }
 
 kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
@@ -195,7 +213,7 @@ kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
   return launch_status(kvarn::launch_quantize(k, v, n_blocks, num_kv_heads, dst_pages, k_pool, v_pool, num_pages,
-                                              dev_flags, static_cast<hipStream_t>(stream)));
+                                              cfg->k_bits, cfg->v_bits, dev_flags, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool, const void* v_pool,
@@ -208,8 +226,8 @@ kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool
   if (n_blocks == 0 || (!k_out && !v_out)) return KVARN_OK;
   if (!pages || (k_out && !k_pool) || (v_out && !v_pool)) return fail(KVARN_ERR_NULL, "a tensor pointer is NULL");
   if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
-  return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, k_out, v_out,
-                                                dev_flags, static_cast<hipStream_t>(stream)));
+  return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, cfg->k_bits,
+                                                cfg->v_bits, k_out, v_out, dev_flags, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
@@ -289,7 +307,8 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
   const void* vn = max_new > 0 ? v_new : q;
   return launch_status(kvarn::launch_prefill(q, max_q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, prefix_lens,
                                              kn, vn, max_new, new_lens, q_lens, batch, num_q_heads, num_kv_heads,
-                                             scale_log2, out, dev_flags, static_cast<hipStream_t>(stream)));
+                                             cfg->k_bits, cfg->v_bits, 0, scale_log2, out, dev_flags,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

@@ -40,8 +40,18 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kCt = 1;                          // 16-column MFMA tiles (16 rows each) per wave
 constexpr int kPfRows = 16 * kCt * kPfWaves;    // (query token, head) rows per workgroup
 constexpr int kMetaWords = kMetaBytes / 4;
-constexpr int kPageChunks = (kKPageBytes + kVPageBytes) / 16;                 // 960
-constexpr int kRawPerThread = (kPageChunks + kPfThreads - 1) / kPfThreads;
+
+// Page geometry of a format (key / value code widths).
+template <int KB, int VB>
+struct PfFormat {
+  static constexpr int kKCode = kBlockTokens * kHeadDim * KB / 8;  // key code bytes
+  static constexpr int kVCode = kBlockTokens * kHeadDim * VB / 8;  // value code bytes
+  static constexpr int kKPage = kKCode + kMetaBytes, kVPage = kVCode + kMetaBytes;
+  static constexpr int kKCodeChunks = kKCode / 16, kVCodeChunks = kVCode / 16;
+  static constexpr int kKChunks = kKPage / 16;                  // key page, 16-byte chunks
+  static constexpr int kChunks = (kKPage + kVPage) / 16;        // both pages
+  static constexpr int kRawPerThread = (kChunks + kPfThreads - 1) / kPfThreads;
+};
 constexpr int kF16Chunks = kBlockTokens * kHeadDim / 8;                         // 2048 per fp16 block
 constexpr int kF16PerThread = (kF16Chunks + kPfThreads - 1) / kPfThreads;
 static_assert(kPfThreads >= 2 * kHeadDim, "the factor step gives every channel and token a thread");
@@ -161,66 +171,111 @@ struct PfState {
 // Staging of one block into LDS
 // ---------------------------------------------------------------------------------------------
 
-// The 960 16-byte chunks of a packed page (key page 608, value page 352): thread tid takes chunks
-// tid, tid + T, tid + 2T, ... (T threads per workgroup).
+// The 16-byte chunks of a key page and a value page (960 for k4v2): thread tid takes chunks tid,
+// tid + T, tid + 2T, ... (T threads per workgroup); key-page chunks come first.
+template <class F>
 struct PageRaw {
-  u32x4 c[kRawPerThread];
+  u32x4 c[F::kRawPerThread];
 };
 
-__device__ __forceinline__ void load_page_raw(PageRaw& R, const uint8_t* __restrict__ kp,
+template <class F>
+__device__ __forceinline__ void load_page_raw(PageRaw<F>& R, const uint8_t* __restrict__ kp,
                                               const uint8_t* __restrict__ vp, int tid) {
   asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int k = 0; k < kRawPerThread; ++k) {
+  for (int k = 0; k < F::kRawPerThread; ++k) {
     const int id = tid + kPfThreads * k;
-    if (id < 608) {
+    if (id < F::kKChunks) {
       R.c[k] = *reinterpret_cast<const u32x4*>(kp + 16 * id);
-    } else if (id < 960) {
-      R.c[k] = *reinterpret_cast<const u32x4*>(vp + 16 * (id - 608));
+    } else if (id < F::kChunks) {
+      R.c[k] = *reinterpret_cast<const u32x4*>(vp + 16 * (id - F::kKChunks));
     }
   }
 }
 
-__device__ __forceinline__ void store_page(PfLds& L, const PageRaw& R, int tid) {
+// A pair of 8-bit codes (bytes at bits 0..7 and 16..23 of x) as exact fp16 integers.
+__device__ __forceinline__ uint32_t byte_pair(uint32_t x) {
+  const uint32_t biased = (x & 0x00FF00FFu) | 0x64006400u;
+  const f16x2 c = __builtin_bit_cast(f16x2, biased) - f16x2{static_cast<_Float16>(1024.0f), static_cast<_Float16>(1024.0f)};
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+template <class F>
+__device__ __forceinline__ void store_page(PfLds& L, const PageRaw<F>& R, int tid) {
   // the store addresses are recomputed for every page (a few integer operations) rather than kept
   // live across the page loop, where registers are short
   asm volatile("" : "+v"(tid));
 #pragma unroll
-  for (int k = 0; k < kRawPerThread; ++k) {
+  for (int k = 0; k < F::kRawPerThread; ++k) {
     const int id = tid + kPfThreads * k;
     const u32x4 x = R.c[k];
-    if (id < 512) {
-      // key codes of token t, channels 32q .. 32q + 31 (dword m: channels 8(4q + m) + i at bits 4i)
-      const int t = id >> 2, q = id & 3;
+    constexpr int kc = F::kKCodeChunks, km = F::kKChunks, vc = F::kKChunks + F::kVCodeChunks;
+    if (id < kc) {
+      if constexpr (F::kKCode == kBlockTokens * kHeadDim / 2) {
+        // 4-bit key codes of token t, channels 32q .. 32q + 31 (dword m: channels 8(4q + m) + i at bits 4i)
+        const int t = id >> 2, q = id & 3;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x4 p;
-        p[0] = code_pair(x[m], 0x000F000Fu);        // channels 0, 4
-        p[1] = code_pair(x[m] >> 4, 0x000F000Fu);   // 1, 5
-        p[2] = code_pair(x[m] >> 8, 0x000F000Fu);   // 2, 6
-        p[3] = code_pair(x[m] >> 12, 0x000F000Fu);  // 3, 7
-        L.kf[16 * t + ((4 * q + m) ^ kkey(t))] = p;
-      }
-    } else if (id < 608) {
-      *reinterpret_cast<u32x4*>(&L.kmeta[4 * (id - 512)]) = x;
-    } else if (id < 864) {
-      // value codes of channel j, tokens 64h .. 64h + 63 (dword k: token 64h + 16k + m at bits 2m)
-      const int v = id - 608, j = v >> 1, h = v & 1;
-#pragma unroll
-      for (int k2 = 0; k2 < 4; ++k2) {
-        const uint32_t w = x[k2];
-        u32x4 a, b;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          a[pr] = code_pair(w >> (2 * pr), 0x00030003u);        // tokens pr, pr + 8
-          b[pr] = code_pair(w >> (2 * pr + 8), 0x00030003u);    // tokens 4 + pr, 12 + pr
+        for (int m = 0; m < 4; ++m) {
+          u32x4 p;
+          p[0] = code_pair(x[m], 0x000F000Fu);        // channels 0, 4
+          p[1] = code_pair(x[m] >> 4, 0x000F000Fu);   // 1, 5
+          p[2] = code_pair(x[m] >> 8, 0x000F000Fu);   // 2, 6
+          p[3] = code_pair(x[m] >> 12, 0x000F000Fu);  // 3, 7
+          L.kf[16 * t + ((4 * q + m) ^ kkey(t))] = p;
         }
-        const int c0 = 2 * (4 * h + k2);
-        L.vf[16 * j + (c0 ^ (j & 15))] = a;
-        L.vf[16 * j + ((c0 + 1) ^ (j & 15))] = b;
+      } else {
+        // 8-bit key codes of token t, channels 16q .. 16q + 15 (dword m: channels 16q + 4m + i at bits 8i)
+        const int t = id >> 3, q = id & 7;
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {  // chunk 2q + hc: channels 8(2q + hc) + (0, 4, 1, 5, 2, 6, 3, 7)
+          const uint32_t lo = x[2 * hc], hi = x[2 * hc + 1];
+          u32x4 p;
+          p[0] = byte_pair((lo & 0xFFu) | ((hi & 0xFFu) << 16));                 // channels 0, 4
+          p[1] = byte_pair(((lo >> 8) & 0xFFu) | (((hi >> 8) & 0xFFu) << 16));   // 1, 5
+          p[2] = byte_pair(((lo >> 16) & 0xFFu) | (((hi >> 16) & 0xFFu) << 16)); // 2, 6
+          p[3] = byte_pair((lo >> 24) | ((hi >> 24) << 16));                     // 3, 7
+          L.kf[16 * t + ((2 * q + hc) ^ kkey(t))] = p;
+        }
       }
-    } else if (id < 960) {
-      *reinterpret_cast<u32x4*>(&L.vmeta[4 * (id - 864)]) = x;
+    } else if (id < km) {
+      *reinterpret_cast<u32x4*>(&L.kmeta[4 * (id - kc)]) = x;
+    } else if (id < vc) {
+      if constexpr (F::kVCode == kBlockTokens * kHeadDim / 4) {
+        // 2-bit value codes of channel j, tokens 64h .. 64h + 63 (dword k: token 64h + 16k + m at bits 2m)
+        const int v = id - km, j = v >> 1, h = v & 1;
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const uint32_t w = x[k2];
+          u32x4 a, b;
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            a[pr] = code_pair(w >> (2 * pr), 0x00030003u);        // tokens pr, pr + 8
+            b[pr] = code_pair(w >> (2 * pr + 8), 0x00030003u);    // tokens 4 + pr, 12 + pr
+          }
+          const int c0 = 2 * (4 * h + k2);
+          L.vf[16 * j + (c0 ^ (j & 15))] = a;
+          L.vf[16 * j + ((c0 + 1) ^ (j & 15))] = b;
+        }
+      } else {
+        // 4-bit value codes of channel j, tokens 32h .. 32h + 31 (dwords 2u, 2u + 1: tokens 32h + 16u + m
+        // at bits 4m of the pair, m = 0..7 in the first dword, 8..15 in the second)
+        const int v = id - km, j = v >> 2, h = v & 3;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint32_t y0 = x[2 * u], y1 = x[2 * u + 1];
+          u32x4 a, b;
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            a[pr] = code_pair(((y0 >> (4 * pr)) & 0xFu) | (((y1 >> (4 * pr)) & 0xFu) << 16), 0x000F000Fu);
+            b[pr] = code_pair(((y0 >> (4 * pr + 16)) & 0xFu) | (((y1 >> (4 * pr + 16)) & 0xFu) << 16), 0x000F000Fu);
+          }
+          const int c0 = 2 * (2 * h + u);
+          L.vf[16 * j + (c0 ^ (j & 15))] = a;
+          L.vf[16 * j + ((c0 + 1) ^ (j & 15))] = b;
+        }
+      }
+    } else if (id < F::kChunks) {
+      *reinterpret_cast<u32x4*>(&L.vmeta[4 * (id - vc)]) = x;
     }
   }
 }
@@ -529,12 +584,22 @@ __device__ __forceinline__ float load_query(float (&qv)[32], const uint16_t* __r
 
 }  // namespace
 
+// mode 0: chunked prefill (lengths from prefix_lens, new_lens, q_lens).
+// mode 1: decode over packed pages only: prefix_lens holds seq_lens (multiples of 128), one query
+//         per sequence that sees every packed token.
+// mode 2: decode over packed pages plus an fp16 tail: prefix_lens holds seq_lens; the first
+//         seq_len & ~127 tokens are packed, the rest are rows of the tail (k_new / v_new with
+//         max_new = 128); one query that sees all of them.
+// In both decode modes the query sits after its sequence's last row, which the prefill formula
+// (query i at fp16 row new_len - q_len + i) gives with q_len = 1.
+template <int KB, int VB>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int max_q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ prefix_lens,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int max_new,
     const int32_t* __restrict__ new_lens, const int32_t* __restrict__ q_lens, int batch, int hq, int hkv, int qt,
-    int ntile, float scale_log2, float* __restrict__ out, uint32_t* __restrict__ flags) {
+    int ntile, int mode, float scale_log2, float* __restrict__ out, uint32_t* __restrict__ flags) {
+  using F = PfFormat<KB, VB>;
   __shared__ PfLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
 
@@ -549,9 +614,21 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
   const int G = hq / hkv;
   const int i0 = tile * qt;
 
-  const int prefix = prefix_lens[b], nnew = new_lens[b], nq = q_lens[b];
-  const bool bad = prefix < 0 || (prefix & 127) || prefix > kBlockTokens * max_blocks || nnew < 0 || nnew > max_new ||
-                   nq < 0 || nq > nnew || nq > max_q;
+  int prefix, nnew, nq;
+  bool bad;
+  if (mode == 0) {
+    prefix = prefix_lens[b];
+    nnew = new_lens[b];
+    nq = q_lens[b];
+    bad = prefix < 0 || (prefix & 127) || prefix > kBlockTokens * max_blocks || nnew < 0 || nnew > max_new ||
+          nq < 0 || nq > nnew || nq > max_q;
+  } else {
+    const int sl = prefix_lens[b];
+    prefix = mode == 1 ? sl : (sl & ~127);
+    nnew = mode == 1 ? 0 : (sl & 127);
+    nq = sl > 0 ? 1 : 0;
+    bad = sl < 0 || (mode == 1 && (sl & 127)) || prefix > kBlockTokens * max_blocks;
+  }
 
   // the lane's two rows
   int ri[kCt], rh[kCt];
@@ -587,6 +664,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     return;
   }
 
+  // a wave whose rows are all padding (the tail of the last tile; every wave but the first in the
+  // decode modes) stages blocks with the others but skips the products
+  const bool wave_live = __builtin_amdgcn_ballot_w64(valid[0]) != 0;
   PfState S;
 #pragma unroll
   for (int ct = 0; ct < kCt; ++ct) {
@@ -606,15 +686,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     mx = wave_max(mx);
     if (lane == 0) L.qmax[w] = mx;
     const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks;
-    const size_t kstride = static_cast<size_t>(kKPageBytes), vstride = static_cast<size_t>(kVPageBytes);
+    const size_t kstride = static_cast<size_t>(F::kKPage), vstride = static_cast<size_t>(F::kVPage);
     bool bad_page = false;
     // page p + 1 is requested before page p is attended; a page id out of range reads page 0 and
     // is skipped (the caller guarantees num_pages > 0)
-    auto request = [&](PageRaw& R, int page) {
+    auto request = [&](PageRaw<F>& R, int page) {
       const size_t unit = static_cast<size_t>(page >= 0 && page < num_pages ? page : 0) * hkv + kvh;
       load_page_raw(R, k_pool + unit * kstride, v_pool + unit * vstride, tid);
     };
-    PageRaw R;
+    PageRaw<F> R;
     int cur = bt[0];
     request(R, cur);
     for (int p = 0; p < nblk; ++p) {
@@ -630,7 +710,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
         int nolim[kCt];
 #pragma unroll
         for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0x7FFFFFFF;
-        attend_block(S, L, lane, nolim);
+        if (wave_live) attend_block(S, L, lane, nolim);
       } else {
         bad_page = true;
       }
@@ -656,7 +736,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     // the previous phase read qmax before its last barrier
     if (lane == 0) L.qmax[w] = mx;
   }
-  const int off = nnew - nq;                                  // fp16 row of query 0 minus 0
+  const int off = nnew - nq;                                  // fp16 row of query 0
   const int last = off + min(i0 + qt, nq) - 1;                // last fp16 row any query of the tile sees
   const size_t rstride = static_cast<size_t>(hkv) * kHeadDim;
   const uint16_t* kb = k_new + (static_cast<size_t>(b) * max_new * hkv + kvh) * kHeadDim;
@@ -674,7 +754,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     int lim[kCt];
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
-    attend_block(S, L, lane, lim);
+    if (wave_live) attend_block(S, L, lane, lim);
   }
 
   // ---- normalise and store ---------------------------------------------------------------------------
@@ -696,7 +776,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, float scale_log2, float* out, uint32_t* flags, hipStream_t stream) {
+                          int hq, int hkv, int kbits, int vbits, int mode, float scale_log2, float* out,
+                          uint32_t* flags, hipStream_t stream) {
   const int G = hq / hkv;
   const int qt = kPfRows / G;
   const int ntile = (max_q + qt - 1) / qt;
@@ -704,11 +785,13 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
   const long groups = 8 * pairs8 * ntile;
   if (groups == 0) return hipSuccess;
   if (groups > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(prefill_kernel, dim3(static_cast<unsigned>(groups)), dim3(kPfThreads), 0, stream,
+  auto kernel = kbits == 8 ? (vbits == 4 ? prefill_kernel<8, 4> : prefill_kernel<8, 2>)
+                           : (vbits == 4 ? prefill_kernel<4, 4> : prefill_kernel<4, 2>);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(groups)), dim3(kPfThreads), 0, stream,
                      static_cast<const uint16_t*>(q), max_q, static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, prefix_lens,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), max_new, new_lens,
-                     q_lens, batch, hq, hkv, qt, ntile, scale_log2, out, flags);
+                     q_lens, batch, hq, hkv, qt, ntile, mode, scale_log2, out, flags);
   return hipGetLastError();
 }
 

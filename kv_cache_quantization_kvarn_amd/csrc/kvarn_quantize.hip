@@ -188,12 +188,14 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[2][4], const f16x8 (&hb
 // All tiles of one kind (keys or values) owned by this workgroup: tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ...  The next tile's input is loaded while the current one is
 // normalised and packed.
-template <bool kIsV>
+template <bool kIsV, int kBits>
 __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, int hkv, int tiles,
                                                const int32_t* __restrict__ dst_pages, uint8_t* __restrict__ pool,
                                                int num_pages, uint32_t* __restrict__ flags, QuantLds& s) {
-  constexpr int kPageBytes = kIsV ? kVPageBytes : kKPageBytes;
-  constexpr int kCodeBytes = kIsV ? kVCodeBytes : kKCodeBytes;
+  static_assert(kIsV ? (kBits == 2 || kBits == 4) : (kBits == 4 || kBits == 8), "code width");
+  constexpr int kCodeBytes = kBlockTokens * kHeadDim * kBits / 8;
+  constexpr int kPageBytes = kCodeBytes + kMetaBytes;
+  constexpr float kLevels = static_cast<float>((1 << kBits) - 1);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes) = t_red;
   // the two threads of a pair (hf = 0, 1) compute identical values.
@@ -390,7 +392,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // clamp(u, 0, L) + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
     constexpr float kRoundMagic = 12582912.0f;
     if constexpr (!kIsV) {
-      // key groups: one channel over the 128 tokens, 16 levels
+      // key groups: one channel over the 128 tokens, 2^kBits levels
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -417,7 +419,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         }
         mn = mul_rn(fminf(mn, dpp_xor1(mn)), cf_c);
         mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), cf_c);
-        const uint32_t sb = float_to_half_bits((mx - mn) / 15.0f);
+        const uint32_t sb = float_to_half_bits((mx - mn) / kLevels);
         const uint32_t zb = float_to_half_bits(mn);
         const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
         const float inv = sf > 0.f ? 1.0f / sf : 0.f;
@@ -437,28 +439,48 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
       const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[8 * n + 4]);
       const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
-      // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
-      const int j = n & 3, q = n >> 2;
+      auto kcode = [&](int i, int c) {
+        return __float_as_uint(fminf(fmaxf(fmaf(R[i][c], qa[c], qb[c]), 0.f), kLevels) + kRoundMagic);
+      };
+      if constexpr (kBits == 4) {
+        // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
+        // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
+        const int j = n & 3, q = n >> 2;
 #pragma unroll
-      for (int ih = 0; ih < 2; ++ih) {
+        for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
-        for (int h4 = 0; h4 < 4; ++h4) {
-          uint32_t by[4];
+          for (int h4 = 0; h4 < 4; ++h4) {
+            uint32_t by[4];
 #pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const int i = 4 * ih + y;
-            const float ulo = fminf(fmaxf(fmaf(R[i][2 * h4], qa[2 * h4], qb[2 * h4]), 0.f), 15.f) + kRoundMagic;
-            const float uhi =
-                fminf(fmaxf(fmaf(R[i][2 * h4 + 1], qa[2 * h4 + 1], qb[2 * h4 + 1]), 0.f), 15.f) + kRoundMagic;
-            by[y] = __float_as_uint(ulo) | (__float_as_uint(uhi) << 4);
+            for (int y = 0; y < 4; ++y) {
+              const int i = 4 * ih + y;
+              by[y] = kcode(i, 2 * h4) | (kcode(i, 2 * h4 + 1) << 4);
+            }
+            const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
+            __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q, 0, 0);
           }
-          const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
-          __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q, 0, 0);
+        }
+      } else {
+        // one byte per code: halfword (i, h4) = code(2h4) | code(2h4 + 1) << 8 is bytes 32*h4 + 2n of token
+        // T(i) (128 bytes per token).  Lanes n and n ^ 1 swap halfwords so that the even lane holds
+        // the dword of token T(2k) and the odd lane that of token T(2k + 1), at bytes 32*h4 + 4(n/2).
+        const bool odd = n & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+          for (int h4 = 0; h4 < 4; ++h4) {
+            const uint32_t h0 = (kcode(2 * k, 2 * h4) & 0xFFu) | ((kcode(2 * k, 2 * h4 + 1) & 0xFFu) << 8);
+            const uint32_t h1 = (kcode(2 * k + 1, 2 * h4) & 0xFFu) | ((kcode(2 * k + 1, 2 * h4 + 1) & 0xFFu) << 8);
+            const uint32_t v = h0 | (h1 << 16);
+            const uint32_t p = dpp_u32(v, 0);  // lane n ^ 1
+            const uint32_t word = odd ? ((p >> 16) | (v & 0xFFFF0000u)) : ((v & 0xFFFFu) | (p << 16));
+            __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 2 * k + (odd ? 1 : 0)) * 128 + 32 * h4 +
+                                                                 4 * (n >> 1), 0, 0);
+          }
         }
       }
     } else {
-      // value groups: one token over the 128 channels, 4 levels
+      // value groups: one token over the 128 channels, 2^kBits levels
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -485,7 +507,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         }
         mn = mul_rn(fminf(mn, dpp_xor1(mn)), rf_t);
         mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), rf_t);
-        const uint32_t sb = float_to_half_bits((mx - mn) / 3.0f);
+        const uint32_t sb = float_to_half_bits((mx - mn) / kLevels);
         const uint32_t zb = float_to_half_bits(mn);
         const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
         const float inv = sf > 0.f ? 1.0f / sf : 0.f;
@@ -507,27 +529,53 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
         qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
       }
-      // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
-      // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
-      // of unit u: bytes 8w + 4ih .. +3 of that channel.
+      auto vcode = [&](int i, int c) {
+        return __float_as_uint(fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels) + kRoundMagic);
+      };
+      if constexpr (kBits == 2) {
+        // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
+        // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
+        // of unit u: bytes 8w + 4ih .. +3 of that channel.
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint32_t by[4];
+        for (int u = 0; u < 4; ++u) {
+          uint32_t by[4];
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int c = 2 * u + (y >> 1), ih = y & 1;
-          uint32_t b = 0;
+          for (int y = 0; y < 4; ++y) {
+            const int c = 2 * u + (y >> 1), ih = y & 1;
+            uint32_t b = 0;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int i = 4 * ih + k;
-            const float v = fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), 3.f) + kRoundMagic;
-            b = k == 0 ? __float_as_uint(v) : (b | (__float_as_uint(v) << (2 * k)));
+            for (int k = 0; k < 4; ++k) {
+              const int i = 4 * ih + k;
+              b = k == 0 ? vcode(i, c) : (b | (vcode(i, c) << (2 * k)));
+            }
+            by[y] = b;
           }
-          by[y] = b;
+          const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
+          const int c = 2 * u + (g >> 1), ih = g & 1;
+          __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 32 + 8 * w + 4 * ih, 0, 0);
         }
-        const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
-        const int c = 2 * u + (g >> 1), ih = g & 1;
-        __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 32 + 8 * w + 4 * ih, 0, 0);
+      } else {
+        // two codes per byte: halfword (c, ih) = codes of tokens T(4ih + k), k = 0..3, at bits 4k is
+        // bytes 16w + 8ih + 2g of channel C(c) (64 bytes per channel).  Rows g and g ^ 1 swap
+        // halfwords (v_permlane16_swap returns (lower row's value, upper row's value)) so that the
+        // even row holds the dword of ih = 0 and the odd row that of ih = 1, at bytes 16w + 8ih + 4(g/2).
+        const bool odd = g & 1;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          uint32_t hw[2];
+#pragma unroll
+          for (int ih = 0; ih < 2; ++ih) {
+            uint32_t b = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) b |= (vcode(4 * ih + k, c) & 0xFu) << (4 * k);
+            hw[ih] = b;
+          }
+          const uint32_t v = hw[0] | (hw[1] << 16);
+          const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+          const uint32_t word = odd ? ((r[0] >> 16) | (r[1] & 0xFFFF0000u)) : ((r[0] & 0xFFFFu) | (r[1] << 16));
+          __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 64 + 16 * w + 8 * (odd ? 1 : 0) +
+                                                                 4 * (g >> 1), 0, 0);
+        }
       }
     }
     {
@@ -544,22 +592,23 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 // Persistent quantiser: every workgroup walks the key tiles blockIdx.x, blockIdx.x + gridDim.x, ...
 // and then the value tiles with the same stride, so all workgroups carry the same mix of the two
 // kinds (a value tile costs more than a key tile).
+template <int kKBits, int kVBits>
 __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin, int hkv, int tiles,
                                                          const int32_t* __restrict__ dst_pages,
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
   __shared__ __align__(16) QuantLds lds;
-  quantize_tiles<false>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
-  quantize_tiles<true>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
+  quantize_tiles<false, kKBits>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
+  quantize_tiles<true, kVBits>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
 }
 
 // Test / inspection export: rebuild fp32 K^ or V^ of one tile in the original basis.
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ k_pool,
                                                          const uint8_t* __restrict__ v_pool, int num_pages,
-                                                         const int32_t* __restrict__ pages, int hkv,
-                                                         float* __restrict__ k_out, float* __restrict__ v_out,
-                                                         uint32_t* __restrict__ flags) {
+                                                         const int32_t* __restrict__ pages, int hkv, int kbits,
+                                                         int vbits, float* __restrict__ k_out,
+                                                         float* __restrict__ v_out, uint32_t* __restrict__ flags) {
   __shared__ float buf[kBlockTokens][kHeadDim + 1];
   const int tile = blockIdx.x;
   const bool is_v = tile & 1;
@@ -573,9 +622,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     if (threadIdx.x == 0 && flags) atomicOr(flags, kFlagBadPage);
     return;
   }
-  const uint8_t* pb = is_v ? v_pool + (static_cast<size_t>(page) * hkv + head) * kVPageBytes
-                           : k_pool + (static_cast<size_t>(page) * hkv + head) * kKPageBytes;
-  const uint8_t* meta = pb + (is_v ? kVCodeBytes : kKCodeBytes);
+  const int code_bytes = kBlockTokens * kHeadDim * (is_v ? vbits : kbits) / 8;
+  const uint8_t* pb = (is_v ? v_pool : k_pool) + (static_cast<size_t>(page) * hkv + head) * (code_bytes + kMetaBytes);
+  const uint8_t* meta = pb + code_bytes;
   const uint16_t* sc = reinterpret_cast<const uint16_t*>(meta + kMetaScale);
   const uint16_t* zr = reinterpret_cast<const uint16_t*>(meta + kMetaZero);
   const float* rho = reinterpret_cast<const float*>(meta + kMetaRho);
@@ -585,11 +634,11 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     uint32_t code;
     float s, z;
     if (is_v) {
-      code = (pb[32 * j + (t >> 2)] >> (2 * (t & 3))) & 3u;
+      code = vbits == 4 ? (pb[64 * j + (t >> 1)] >> (4 * (t & 1))) & 15u : (pb[32 * j + (t >> 2)] >> (2 * (t & 3))) & 3u;
       s = half_bits_to_float(sc[t]);
       z = half_bits_to_float(zr[t]);
     } else {
-      code = (pb[64 * t + (j >> 1)] >> (4 * (j & 1))) & 15u;
+      code = kbits == 8 ? pb[128 * t + j] : (pb[64 * t + (j >> 1)] >> (4 * (j & 1))) & 15u;
       s = half_bits_to_float(sc[j]);
       z = half_bits_to_float(zr[j]);
     }
@@ -619,7 +668,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 namespace kvarn {
 
 hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
-                           void* k_pool, void* v_pool, int num_pages, uint32_t* flags, hipStream_t stream) {
+                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, uint32_t* flags,
+                           hipStream_t stream) {
   const int tiles = n_blocks * hkv;  // per kind
   if (tiles == 0) return hipSuccess;
   // two persistent workgroups per compute unit
@@ -629,17 +679,20 @@ hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, 
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   const int groups = tiles < 2 * cus ? tiles : 2 * cus;
-  hipLaunchKernelGGL(quantize_kernel, dim3(groups), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
+  auto kernel = kbits == 8 ? (vbits == 4 ? quantize_kernel<8, 4> : quantize_kernel<8, 2>)
+                           : (vbits == 4 ? quantize_kernel<4, 4> : quantize_kernel<4, 2>);
+  hipLaunchKernelGGL(kernel, dim3(groups), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), hkv, tiles, dst_pages, static_cast<uint8_t*>(k_pool),
                      static_cast<uint8_t*>(v_pool), num_pages, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
-                             int n_blocks, int hkv, float* k_out, float* v_out, uint32_t* flags, hipStream_t stream) {
+                             int n_blocks, int hkv, int kbits, int vbits, float* k_out, float* v_out,
+                             uint32_t* flags, hipStream_t stream) {
   const unsigned tiles = 2u * static_cast<unsigned>(n_blocks) * static_cast<unsigned>(hkv);
   hipLaunchKernelGGL(dequantize_kernel, dim3(tiles), dim3(256), 0, stream, static_cast<const uint8_t*>(k_pool),
-                     static_cast<const uint8_t*>(v_pool), num_pages, pages, hkv, k_out, v_out, flags);
+                     static_cast<const uint8_t*>(v_pool), num_pages, pages, hkv, kbits, vbits, k_out, v_out, flags);
   return hipGetLastError();
 }
 

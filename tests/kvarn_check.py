@@ -68,7 +68,8 @@ class TileStats:
 
 def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: bool) -> None:
     """Compare one GPU-written page against the oracle's quantisation of the same fp16 tile."""
-    ref = o.quantize_tile(x16, is_v)
+    bits = o.bits_of_page(len(page_bytes), is_v)  # the format's code width
+    ref = o.quantize_tile(x16, is_v, bits=bits)
     got = o.decode_page(page_bytes, is_v)
     stats.tiles += 1
     for key in ("rho", "gamma"):
@@ -88,7 +89,7 @@ def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: boo
     # the rounding decision alone: oracle codes on the GPU's stored normalisers and grid
     n32 = o.normalized(o.rotate(x16.astype(np.float64)), got["rho"], got["gamma"]).astype(np.float32)
     cond = np.zeros_like(got["codes"])
-    levels = o.V_LEVELS if is_v else o.K_LEVELS
+    levels = (1 << bits) - 1
     for gi in range(128):
         if is_v:
             cond[gi, :] = o.rtn_codes(n32[gi, :], got["scale"][gi], got["zero"][gi], levels)
