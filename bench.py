@@ -66,6 +66,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-formats", action="store_true", help="skip the other code widths (k4v4, k8v2, k8v4)")
     ap.add_argument("--prefill-workload", default="prefill_llama3_8b_16x7680p512")
     ap.add_argument("--no-fp16-baseline", action="store_true",
@@ -367,6 +368,31 @@ def main():
     q_avg_s = sum(q_ms) / len(q_ms) / 1e3
     d_avg_s = sum(d_ms) / len(d_ms) / 1e3
 
+    # the same step captured once in a HIP graph and replayed (one launch of the whole step; for the
+    # 28-layer workload that is 56 kernels)
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0g = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0g) / args.steps * 1e3
+        assert K.kvarn_read_flags(case.flags) == 0, "device flags set during the graph replays"
+        del graph
+
     # decode alone after reading 512 MB (evicts the 256 MB last-level cache, leaving clean lines, so
     # the decode pays no write-back of the flush), timed per launch
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -421,6 +447,11 @@ def main():
     }
     if fp16 is not None:
         line["fp16_baseline"] = fp16
+    if graph_ms is not None:
+        line["graph"] = {"ms_per_step": round(graph_ms, 4), "value": round(step_bytes / (graph_ms / 1e3) / 1e9, 3),
+                         "kernels_per_step": 2 * w.layers,
+                         "protocol": "the timed step captured once in a HIP graph, %d replays timed like the eager steps"
+                                     % args.steps}
     if prefill is not None:
         line["prefill"] = prefill
     if formats is not None:
