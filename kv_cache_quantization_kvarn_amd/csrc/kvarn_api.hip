@@ -28,8 +28,8 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, int kbits, int vbits, int mode, float scale_log2, float* out,
-                          uint32_t* flags, hipStream_t stream);
+                          int hq, int hkv, int kbits, int vbits, int mode, int bps, int max_splits, float scale_log2,
+                          float* out, float* part, uint32_t* counters, uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
@@ -157,11 +157,13 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (kind != DecodeKind::fp16 && !is_k4v2(cfg)) {
     // Other code widths: the generic path, the prefill kernel with one query per sequence that sees
-    // every packed token (and every tail row).  The workspace is not used.
+    // every packed token (and every tail row), split over pages with the same plan, partials and
+    // counters as the matrix-core decode.
     return launch_status(kvarn::launch_prefill(q, 1, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                                tail ? k_tail : q, tail ? v_tail : q, tail ? 128 : 0, seq_lens,
                                                seq_lens, batch, num_q_heads, num_kv_heads, cfg->k_bits, cfg->v_bits,
-                                               tail ? 2 : 1, scale_log2, out, dev_flags, st));
+                                               tail ? 2 : 1, p.blocks_per_split, p.max_splits, scale_log2, out, part,
+                                               counters, dev_flags, st));
   }
   if (kind == DecodeKind::fp16)
     return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
@@ -307,8 +309,8 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
   const void* vn = max_new > 0 ? v_new : q;
   return launch_status(kvarn::launch_prefill(q, max_q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, prefix_lens,
                                              kn, vn, max_new, new_lens, q_lens, batch, num_q_heads, num_kv_heads,
-                                             cfg->k_bits, cfg->v_bits, 0, scale_log2, out, dev_flags,
-                                             static_cast<hipStream_t>(stream)));
+                                             cfg->k_bits, cfg->v_bits, 0, 0, 1, scale_log2, out, nullptr, nullptr,
+                                             dev_flags, static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

@@ -183,3 +183,30 @@ def test_k8v4_llama3_layer_decode_sampled(K):
         worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
     say("  decode max-abs diff %.3e over sampled heads" % worst)
     assert worst <= chk.ATTN_TOL
+
+
+def test_generic_decode_most_splits(K):
+    """1,024 blocks of one KV head plus a 90-token tail: 63 page splits and the tail split in one merge."""
+    cfg = K.kvarn_config_parse("kvarn_k4v4_g128")
+    say("case: kvarn_k4v4_g128 decode with a tail over 1,024 blocks (64 splits)")
+    g = torch.Generator().manual_seed(4096)
+    k, v = randn_kv(g, 1024 * 128, 1)
+    perm = torch.randperm(1024, generator=g).to(torch.int32)
+    kp, vp = quantize(K, cfg, k.cuda(), v.cuda(), perm, 1024, 0)
+    bt = perm.view(1, 1024).clone()
+    kt, vt = randn_kv(g, 128, 1)
+    kt, vt = kt.view(1, 128, 1, 128).cuda(), vt.view(1, 128, 1, 128).cuda()
+    q = torch.randn(1, 4, 128, generator=g).half().cuda()
+    sl = torch.tensor([1024 * 128 + 90], dtype=torch.int32)
+    ws = K.alloc_workspace(cfg, 1, 4, 1, 1024)
+    out = torch.full((1, 4, 128), float("nan"), device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for rep in range(2):  # the counters are back at zero after every call
+        K.kvarn_decode_attention_tail(cfg, q, kp, vp, bt.cuda(), sl.cuda(), kt, vt, 1, out, ws, dev_flags=fl)
+        torch.cuda.synchronize()
+        assert K.kvarn_read_flags(fl) == 0
+        ref = o.decode_tail(q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), bt.numpy(), sl.numpy(),
+                            kt.cpu().numpy(), vt.cpu().numpy(), 1)
+        d = float(np.abs(out.cpu().numpy() - ref).max())
+        say("  call %d: max-abs diff %.3e" % (rep, d))
+        assert d <= chk.ATTN_TOL
