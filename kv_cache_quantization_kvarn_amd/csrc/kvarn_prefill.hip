@@ -408,6 +408,7 @@ struct HalfOut {
   float alpha, vinit;
 };
 
+template <bool kMasked>
 __device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x4 (&sc)[4], int h, int g, int lim) {
   HalfOut R;
   const int t0 = 32 * g + 16 * h;
@@ -419,7 +420,7 @@ __device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float s = sc[lt][r] * pkv[r];
-      sc[lt][r] = t0 + 4 * lt + r > lim ? -INFINITY : s;
+      sc[lt][r] = kMasked && t0 + 4 * lt + r > lim ? -INFINITY : s;
       mloc = fmaxf(mloc, sc[lt][r]);
     }
   }
@@ -461,7 +462,8 @@ __device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x
 // 32g + 31), each its own online-softmax step, so that matrix products and vector arithmetic of
 // different halves interleave in one wave: the half-1 scores run under the half-0 softmax, the
 // half-0 value products under the half-1 softmax.  lim: block-relative index of the last key row the
-// lane's row may see (INT_MAX: all).
+// lane's row may see; kMasked false: every row sees the whole block (packed pages), no mask.
+template <bool kMasked>
 __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, const int (&lim)[kCt]) {
   asm volatile("" : "+v"(lane));  // fragment addresses are recomputed per block, not kept live
   const int n = lane & 15, g = lane >> 4;
@@ -528,7 +530,7 @@ __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lan
       s1[lt] = mfma16x16x32(a, blo[ks], s1[lt]);
     }
   }
-  const HalfOut h0 = softmax_half(S, L, s0, 0, g, lim[0]);
+  const HalfOut h0 = softmax_half<kMasked>(S, L, s0, 0, g, lim[0]);
 
   // ---- half 0 value products, with the half-1 softmax ---------------------------------------------
   f32x4 d[8];
@@ -542,7 +544,7 @@ __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lan
       d[mt] = mfma16x16x32(a, h0.wlo[hf], d[mt]);
     }
   }
-  const HalfOut h1 = softmax_half(S, L, s1, 1, g, lim[0]);
+  const HalfOut h1 = softmax_half<kMasked>(S, L, s1, 1, g, lim[0]);
 
   // ---- half 1 value products on the rescaled half-0 partial --------------------------------------
 #pragma unroll
@@ -742,7 +744,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
         int nolim[kCt];
 #pragma unroll
         for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0x7FFFFFFF;
-        if (wave_live) attend_block(S, L, lane, nolim);
+        if (wave_live) attend_block<false>(S, L, lane, nolim);
       } else {
         bad_page = true;
       }
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     int lim[kCt];
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
-    if (wave_live) attend_block(S, L, lane, lim);
+    if (wave_live) attend_block<true>(S, L, lane, lim);
   }
 
   if (mode != 0) {
