@@ -141,8 +141,10 @@ class Case:
                                       self.ws, dev_flags=self.flags)
 
 
-def cpu_baseline(w, seconds):
-    """The oracle on a bounded sample of the same workload, single thread, in the same GB/s units."""
+def _oracle_run(wname, seconds, part=0):
+    """The oracle on a bounded sample of one workload for about `seconds` of one thread: quantised
+    (block, KV head) tiles (K and V) for half the time, whole decodes of one sequence's KV head for
+    the other half.  Returns (tiles, quantise seconds, decodes, decode seconds, blocks per sequence)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -151,45 +153,91 @@ def cpu_baseline(w, seconds):
     from oracle import kvarn_oracle as o
 
     torch.set_num_threads(1)
+    w = synth.WORKLOADS[wname]
     k, v = synth.layer_kv(w, 0, 4 * 128, "cpu")
     kh, vh = k.numpy(), v.numpy()
     pm = synth.make_page_map(w)
     nb_seq = int(pm.seq_lens[0]) // 128
     with threadpool_limits(limits=1):
-        # quantize: (block, KV head) pairs, K and V tiles each
         t0 = time.perf_counter()
         nq = 0
         while time.perf_counter() - t0 < seconds / 2 or nq < 4:
-            b, h = nq % 4, (nq // 4) % w.hkv
+            b, h = (nq + part) % 4, ((nq + part) // 4) % w.hkv
             sl = slice(128 * b, 128 * b + 128)
             o.encode_page(o.quantize_tile(kh[sl, h], False), False)
             o.encode_page(o.quantize_tile(vh[sl, h], True), True)
             nq += 1
         tq = time.perf_counter() - t0
-        # decode: every query head of one KV head of one sequence over its blocks
         kp = np.zeros((4, 1, o.K_PAGE_BYTES), np.uint8)
         vp = np.zeros((4, 1, o.V_PAGE_BYTES), np.uint8)
         o.quantize_blocks(kh[:, :1], vh[:, :1], np.arange(4), kp, vp)
         blocks = np.arange(nb_seq) % 4  # the sequence's length, pages recycled from the sample
-        q = np.random.default_rng(0).standard_normal((1, w.gqa, 128)).astype(np.float16)
+        q = np.random.default_rng(part).standard_normal((1, w.gqa, 128)).astype(np.float16)
         t0 = time.perf_counter()
         nd = 0
         while time.perf_counter() - t0 < seconds / 2 or nd < 1:
             o.decode(q, kp, vp, blocks[None, :], np.array([nb_seq * 128]), 1)
             nd += 1
         td = time.perf_counter() - t0
-    q_bytes = nq * (65536 + 15360)
-    d_bytes = nd * (nb_seq * 15360 + w.gqa * 768 + nb_seq * 4)
-    return {
-        "value": round((q_bytes + d_bytes) / (tq + td) / 1e9, 6),
+    return nq, tq, nd, td, nb_seq
+
+
+def _oracle_part(args):
+    return _oracle_run(*args)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, seconds):
+    """The oracle on a bounded sample of the same workload in the same GB/s units: one thread, then one
+    single-threaded process per available core (at most 16) on slices of the same sample.  Runs before
+    the process touches the GPU (the worker processes are forked)."""
+    import multiprocessing
+
+    def rates(nq, tq, nd, td, nb_seq):
+        qb = nq * (65536 + 15360)
+        db = nd * (nb_seq * 15360 + w.gqa * 768 + nb_seq * 4)
+        return qb, db
+
+    nq, tq, nd, td, nb_seq = _oracle_run(w.name, seconds)
+    qb, db = rates(nq, tq, nd, td, nb_seq)
+    res = {
+        "value": round((qb + db) / (tq + td) / 1e9, 6),
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": ("%d (block, KV head) pairs quantized (K and V tiles) + %d decode(s) of %d query heads over one "
                    "%d-block sequence of one KV head; fp64 numpy oracle, 1 thread" % (nq, nd, w.gqa, nb_seq)),
-        "quantize_gbps": round(q_bytes / tq / 1e9, 6),
-        "decode_gbps": round(d_bytes / td / 1e9, 6),
+        "quantize_gbps": round(qb / tq / 1e9, 6),
+        "decode_gbps": round(db / td / 1e9, 6),
+        "cpu_model": cpu_model(),
     }
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    n = max(1, min(16, avail))
+    if n > 1:
+        ctx = multiprocessing.get_context("fork")
+        t0 = time.perf_counter()
+        with ctx.Pool(n) as pool:
+            parts = pool.map(_oracle_part, [(w.name, seconds / 2, i) for i in range(n)])
+        wall = time.perf_counter() - t0
+        qb = sum(rates(*r)[0] for r in parts)
+        db = sum(rates(*r)[1] for r in parts)
+        # every process spends half its time on each kind: the aggregate rate is bytes over wall time
+        res["all_cores"] = {"value": round((qb + db) / wall / 1e9, 6), "cores": n,
+                            "sample": "%d single-threaded processes, each the sample above for half the time" % n}
+    return res
 
 
 def timed_after_flush(fn, reps, stream, flush, sink):
@@ -330,10 +378,14 @@ def main():
     import torch
 
     from kv_cache_quantization_kvarn_amd import accounting as acc
-    from kv_cache_quantization_kvarn_amd import kvarn as K
     from kv_cache_quantization_kvarn_amd import synth
 
     w = synth.WORKLOADS[args.workload]
+    # the oracle baseline runs first: its worker processes are forked, which must happen before the
+    # process loads the HIP library or touches the GPU
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    from kv_cache_quantization_kvarn_amd import kvarn as K
+
     cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
     case = Case(K, w, cfg)
     stream = torch.cuda.current_stream()
@@ -466,7 +518,7 @@ def main():
                         "unit": "GB/s", "frac": round(ach / acc.HBM_PEAK_GBPS, 4), "traffic": traffic,
                         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
