@@ -33,20 +33,26 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("7ccd52bfc6ca996e", 663560299),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("7835744448ed177e", 130324352),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9ba7a8be53416ea9", 663560299),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("17e64f4b25ff8e91", 130324352),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
 
 
 def source_digest(kernel):
+    """Digest of the kernel's source code with comments and blank space removed, so that a comment
+    edit keeps the measurement while any change to the code drops it."""
     import hashlib
+    import re
     csrc = os.path.join(ROOT, "kv_cache_quantization_kvarn_amd", "csrc")
-    data = b""
+    data = ""
     for f in (KERNEL_SOURCE[kernel], "kvarn_common.h"):
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             data += fh.read()
-    return hashlib.sha256(data).hexdigest()[:16]
+    data = re.sub(r"/\*.*?\*/", " ", data, flags=re.S)
+    data = re.sub(r"//[^\n]*", " ", data)
+    data = " ".join(data.split())
+    return hashlib.sha256(data.encode()).hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):

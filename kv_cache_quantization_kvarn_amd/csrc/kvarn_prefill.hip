@@ -10,11 +10,12 @@
 // query tokens times the G heads that share the KV head.  Wave w owns rows 16w .. 16w + 15, one
 // 16-column tile of v_mfma_f32_16x16x32_f16.  The KV blocks stream through LDS once per workgroup:
 //
-//   * a packed page is loaded by all 256 lanes and its codes are written to LDS as exact fp16
-//     integers (0..15 for keys, 0..3 for values: normal numbers or zero, which the matrix cores
-//     multiply exactly, so no offset has to be removed), keys as [token][channel] rows and values
-//     as [channel][token] rows, the 16-byte chunks of a row XOR-swizzled so that the 16 lanes of a
-//     fragment read hit distinct banks;
+//   * a packed page is loaded by all 512 lanes (the next page's loads are in flight while the
+//     current one is attended) and its codes are written to LDS as exact fp16 integers (up to 255
+//     for 8-bit keys: normal numbers or zero, which the matrix cores multiply exactly, so no offset
+//     has to be removed), keys as [token][channel] rows and values as [channel][token] rows, the
+//     16-byte chunks of a row XOR-swizzled so that the 16 lanes of a fragment read hit distinct
+//     banks;
 //   * the page metadata becomes per-channel and per-token factors, and both products run with the
 //     codes as the A operand and the fp32 coefficients as an fp16 hi + lo pair of B operands (two
 //     products into one fp32 accumulator):
@@ -28,7 +29,9 @@
 //     rows follow in blocks of 128 through the same LDS layout (keys copied, values transposed),
 //     with unit factors, the raw query and the causal mask.
 //
-// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.
+// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.  The same
+// kernel serves decode in the code widths the matrix-core decode kernel does not (one query per
+// sequence, pages split over workgroups, see prefill_kernel's modes).
 #include "kvarn_common.h"
 
 namespace kvarn {

@@ -31,9 +31,12 @@
 //
 // Codes.  The normaliser of the group axis is folded into the rounding FMA
 // (u = M * (2^-x / s) - z / s with M the value scaled by the other normaliser),
-// codes are packed in registers (two nibbles or four 2-bit codes per byte),
-// transposed across lanes into whole dwords of the page (DPP within a quad for
-// keys, v_permlane16/32_swap across rows for values) and stored directly.
+// codes are packed in registers (two nibbles or four 2-bit codes per byte; one
+// byte per 8-bit key code, two 4-bit value codes per byte in the wider
+// formats), transposed across lanes into whole dwords of the page (DPP within a
+// quad or a lane pair for keys, v_permlane16/32_swap across rows for values)
+// and stored directly.  The code widths are template parameters; every other
+// step is shared.
 //
 // Scheduling.  Workgroups are persistent, two per compute unit; each walks its share of the key
 // tiles and then of the value tiles with a fixed stride.  The input of the next tile is fetched while the current
