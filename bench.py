@@ -37,6 +37,14 @@ MEASURED_TRAFFIC = {
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("17e64f4b25ff8e91", 130324352),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
+# VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
+MEASURED_VALU = {
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9ba7a8be53416ea9", 126355456),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("17e64f4b25ff8e91", 10897216),
+}
+# Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+
 
 
 def source_digest(kernel):
@@ -55,8 +63,8 @@ def source_digest(kernel):
     return hashlib.sha256(data.encode()).hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
-    entry = MEASURED_TRAFFIC.get((kernel, workload))
+def measured_traffic(kernel, workload, table=None):
+    entry = (MEASURED_TRAFFIC if table is None else table).get((kernel, workload))
     if entry is None or entry[0] != source_digest(kernel):
         return None
     return entry[1]
@@ -523,6 +531,15 @@ def main():
     line["roofline"] = {"kernel": "kvarn " + dom, "bound": "hbm", "achieved": round(ach, 1), "peak": acc.HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(ach / acc.HBM_PEAK_GBPS, 4), "traffic": traffic,
                         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
+    valu = measured_traffic(dom, w.name, MEASURED_VALU)
+    if valu is not None:
+        # the same launches seen as ALU work: VALU lane operations issued per second (wave64 -> 64 lanes)
+        avg_s = q_avg_s if dom == "quantize_kernel" else d_avg_s
+        t = valu * 64 / avg_s / 1e12
+        line["roofline"]["valu"] = {"achieved": round(t, 2), "peak": round(VALU_PEAK_TLANEOPS, 2),
+                                    "unit": "T lane-ops/s", "frac": round(t / VALU_PEAK_TLANEOPS, 4),
+                                    "insts_per_launch": valu,
+                                    "source": "rocprofv3 SQ_INSTS_VALU of the same kernel source"}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
