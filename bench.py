@@ -83,6 +83,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
     ap.add_argument("--no-formats", action="store_true", help="skip the other code widths (k4v4, k8v2, k8v4)")
     ap.add_argument("--prefill-workload", default="prefill_llama3_8b_16x7680p512")
+    ap.add_argument("--no-tail", action="store_true", help="skip the decode with fp16 tails")
     ap.add_argument("--no-fp16-baseline", action="store_true",
                     help="skip the fp16 paged decode baseline (measured outside the timed steps)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -307,6 +308,40 @@ def fp16_baseline(case, K, synth, acc, stream, reps, flush, sink, kvarn_flush_s)
             "protocol": "both decodes timed after a 512 MB read that evicts the last-level cache; median of %d" % reps}
 
 
+def tail_measure(case, K, synth, acc, stream, reps, flush, sink, packed_flush_s, tail_tokens=127):
+    """Decode over the layer-0 packed cache plus an fp16 tail of `tail_tokens` per sequence (127 is the
+    longest a tail gets), cache-flushed like the packed decode it is compared with."""
+    import torch
+    w, pm = case.w, case.pm
+    L0 = case.layers[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(synth.stream_seed(w, 9))
+    kt = torch.zeros(w.batch, 128, w.hkv, 128, dtype=torch.float16, device="cuda")
+    vt = torch.zeros_like(kt)
+    kt[:, :tail_tokens] = torch.randn(w.batch, tail_tokens, w.hkv, 128, generator=g, device="cuda").half()
+    vt[:, :tail_tokens] = torch.randn(w.batch, tail_tokens, w.hkv, 128, generator=g, device="cuda").half()
+    sl = (pm.seq_lens + tail_tokens).to(torch.int32).cuda()
+
+    def run():
+        K.kvarn_decode_attention_tail(case.cfg, L0["q"], L0["kp"], L0["vp"], case.bt, sl, kt, vt, w.hkv, case.out,
+                                      case.ws, dev_flags=case.flags, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    t = timed_after_flush(run, reps, stream, flush, sink)
+    assert K.kvarn_read_flags(case.flags) == 0, "device flags set by the tail decode"
+    kb, vb = K.kvarn_page_bytes(case.cfg, False), K.kvarn_page_bytes(case.cfg, True)
+    attended = int(pm.seq_lens.sum().item()) // 128
+    nbytes = acc.tail_decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb, w.batch * tail_tokens)
+    gbps = nbytes / t / 1e9
+    del kt, vt
+    torch.cuda.empty_cache()
+    return {"tail_tokens": tail_tokens, "us_median": round(t * 1e6, 2), "gbps": round(gbps, 1),
+            "pct_peak": round(100 * gbps / acc.HBM_PEAK_GBPS, 2), "bytes_per_launch": nbytes,
+            "vs_packed_only": round(t / packed_flush_s, 3),
+            "protocol": "median of %d launches, each after a 512 MB read that evicts the last-level cache" % reps}
+
+
 def prefill_measure(K, synth, acc, cfg, name, stream, reps, flush, sink):
     """Chunked prefill over packed pages plus fp16 rows (a matrix-core bound kernel), cache-flushed."""
     import torch
@@ -469,6 +504,10 @@ def main():
     if not args.no_fp16_baseline:
         fp16 = fp16_baseline(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
 
+    tail = None
+    if not args.no_tail:
+        tail = tail_measure(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
+
     formats = None
     if not args.no_formats:
         formats = formats_measure(K, w, case, stream, max(5, args.flush_reps // 2), flush, flush_sink)
@@ -513,6 +552,8 @@ def main():
     }
     if fp16 is not None:
         line["fp16_baseline"] = fp16
+    if tail is not None:
+        line["tail"] = tail
     if graph_ms is not None:
         line["graph"] = {"ms_per_step": round(graph_ms, 4), "value": round(step_bytes / (graph_ms / 1e3) / 1e9, 3),
                          "kernels_per_step": 2 * w.layers,

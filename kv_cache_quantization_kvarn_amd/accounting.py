@@ -46,6 +46,14 @@ def decode_bytes(total_blocks_attended: int, kv_heads: int, batch: int, q_heads:
             + total_blocks_attended * 4 + batch * 4)
 
 
+def tail_decode_bytes(total_blocks_attended: int, kv_heads: int, batch: int, q_heads: int, k_page: int, v_page: int,
+                      total_tail_tokens: int) -> int:
+    """Algorithmic HBM bytes of one decode step with fp16 tails: the packed decode's bytes plus one
+    fp16 K row and one fp16 V row (256 B each) per tail token and KV head."""
+    return (decode_bytes(total_blocks_attended, kv_heads, batch, q_heads, k_page, v_page)
+            + total_tail_tokens * kv_heads * 2 * HEAD_DIM * 2)
+
+
 MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix rate, TFLOP/s
 
 

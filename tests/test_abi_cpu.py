@@ -197,3 +197,10 @@ def test_prefill_accounting_matches_brute_force():
     brute = sum(p + (n - k) + i + 1 for p, n, k in zip(prefix, new, q) for i in range(k)) * hq
     assert accounting.prefill_pairs(prefix, new, q, hq) == brute
     assert accounting.prefill_flops(brute) == 4 * 128 * brute
+
+
+def test_tail_accounting_adds_one_k_and_one_v_row_per_tail_token():
+    base = accounting.decode_bytes(640, 8, 5, 32, 9728, 5632)
+    # 5 sequences with tails of 1..5 tokens, 8 KV heads: fp16 rows of 128 channels for K and for V
+    tail = accounting.tail_decode_bytes(640, 8, 5, 32, 9728, 5632, 1 + 2 + 3 + 4 + 5)
+    assert tail - base == 15 * 8 * (128 * 2) * 2
