@@ -377,7 +377,7 @@ def prefill_measure(K, synth, acc, cfg, name, stream, reps, flush, sink):
 
 def formats_measure(K, w, case, stream, reps, flush, sink):
     """Quantise and decode launches of the workload's first layer in the other code widths.  Decode in
-    these formats runs on the generic path (the prefill kernel, one query per sequence)."""
+    these formats runs on the matrix-core decode kernel instantiated for their code widths."""
     import torch
     from kv_cache_quantization_kvarn_amd import accounting as acc
     res = {}
@@ -409,7 +409,7 @@ def formats_measure(K, w, case, stream, reps, flush, sink):
         db = acc.decode_bytes(int(case.pm.seq_lens.sum().item()) // 128, w.hkv, w.batch, w.hq, kb, vb)
         res[name] = {"quantize_us": round(tq * 1e6, 2), "quantize_gbps": round(qb / tq / 1e9, 1),
                      "decode_us": round(td * 1e6, 2), "decode_gbps": round(db / td / 1e9, 1),
-                     "page_bytes": [kb, vb], "decode_path": "generic (prefill kernel)"}
+                     "page_bytes": [kb, vb]}
         del kp, vp
         torch.cuda.empty_cache()
     return res

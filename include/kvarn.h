@@ -51,9 +51,8 @@ typedef enum {
 /* Format parameters.  Supported: head_dim 128, block_tokens 128, k_bits 4 or
  * 8, v_bits 2 or 4, group_size 128, norm_iters 4, eps 1e-6.  The post names
  * kvarn_k4v2_g128; the wider codes keep every step of the method and change
- * the number of levels (2^bits - 1) and the packing only.  The matrix-core
- * decode kernel serves k4v2; decode in the other formats runs on the prefill
- * kernel with one query per sequence (same contract, no workspace use). */
+ * the number of levels (2^bits - 1) and the packing only.  Every entry point
+ * takes every format; the kernels are instantiated per pair of code widths. */
 typedef struct {
   int32_t head_dim;
   int32_t block_tokens;

@@ -18,9 +18,9 @@ hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pag
                              uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
-                         const void* v_tail, int batch, int hq, int hkv, int blocks_per_split, int max_splits,
-                         float scale_log2, float* out, float* part, uint32_t* counters, uint32_t* flags,
-                         hipStream_t stream);
+                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int blocks_per_split,
+                         int max_splits, float scale_log2, float* out, float* part, uint32_t* counters,
+                         uint32_t* flags, hipStream_t stream);
 hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_cache, int num_pages,
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
@@ -28,8 +28,8 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, int kbits, int vbits, int mode, int bps, int max_splits, float scale_log2,
-                          float* out, float* part, uint32_t* counters, uint32_t* flags, hipStream_t stream);
+                          int hq, int hkv, int kbits, int vbits, float scale_log2, float* out, uint32_t* flags,
+                          hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
@@ -56,7 +56,6 @@ bool config_ok(const kvarn_config* c) {
 }
 
 // the format the post names, which the matrix-core decode kernel is written for
-bool is_k4v2(const kvarn_config* c) { return c->k_bits == 4 && c->v_bits == 2; }
 
 kvarn_status check_config(const kvarn_config* c) {
   if (!c) return fail(KVARN_ERR_NULL, "config is NULL");
@@ -155,24 +154,14 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
   const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (kind != DecodeKind::fp16 && !is_k4v2(cfg)) {
-    // Other code widths: the generic path, the prefill kernel with one query per sequence that sees
-    // every packed token (and every tail row), split over pages with the same plan, partials and
-    // counters as the matrix-core decode.
-    return launch_status(kvarn::launch_prefill(q, 1, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
-                                               tail ? k_tail : q, tail ? v_tail : q, tail ? 128 : 0, seq_lens,
-                                               seq_lens, batch, num_q_heads, num_kv_heads, cfg->k_bits, cfg->v_bits,
-                                               tail ? 2 : 1, p.blocks_per_split, p.max_splits, scale_log2, out, part,
-                                               counters, dev_flags, st));
-  }
   if (kind == DecodeKind::fp16)
     return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                                    batch, num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits,
                                                    scale_log2, out, part, counters, dev_flags, st));
   return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                             tail ? k_tail : nullptr, tail ? v_tail : nullptr, batch, num_q_heads,
-                                            num_kv_heads, p.blocks_per_split, p.max_splits, scale_log2, out, part,
-                                            counters, dev_flags, st));
+                                            num_kv_heads, cfg->k_bits, cfg->v_bits, p.blocks_per_split, p.max_splits,
+                                            scale_log2, out, part, counters, dev_flags, st));
 }
 
 }  // namespace
@@ -309,8 +298,8 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
   const void* vn = max_new > 0 ? v_new : q;
   return launch_status(kvarn::launch_prefill(q, max_q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, prefix_lens,
                                              kn, vn, max_new, new_lens, q_lens, batch, num_q_heads, num_kv_heads,
-                                             cfg->k_bits, cfg->v_bits, 0, 0, 1, scale_log2, out, nullptr, nullptr,
-                                             dev_flags, static_cast<hipStream_t>(stream)));
+                                             cfg->k_bits, cfg->v_bits, scale_log2, out, dev_flags,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream) {

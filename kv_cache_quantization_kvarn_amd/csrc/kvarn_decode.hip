@@ -16,8 +16,10 @@
 // codes are dense (G x 128) x (128 x 128) products per page and run on
 // v_mfma_f32_16x16x32_f16.  Codes enter as exact fp16 integers off + c: one
 // mask-and-or (and for most pairs one shift) places a pair of codes in the
-// mantissa under a fixed exponent, which fixes the offset (16 or 64 for keys,
-// 4 or 16 for values).  The offsets are removed with sums of the very fp16
+// mantissa under a fixed exponent, which fixes the offset (4-bit keys 16 or 64,
+// 8-bit keys 1024; 2-bit values 4 or 16, 4-bit values 64).  The kernel is
+// instantiated per pair of code widths; only the page geometry, the code
+// loads and these conversions differ.  The offsets are removed with sums of the very fp16
 // coefficients the matrix cores multiplied.  (fp16 subnormal operands would
 // need no offset, but the matrix cores lose precision on them, biased toward
 // zero.)  The fp32 coefficients a_j and w_t enter as an fp16 hi + lo pair (hi in
@@ -86,6 +88,39 @@ __device__ __forceinline__ void value_codes(uint32_t w, uint32_t mag4, uint32_t 
   b[1] = and_or(r4, 0x00C000C0u, mag16);   // codes 5, 13
   b[2] = and_or(r4, 0x03000300u, mag4);    // codes 6, 14
   b[3] = and_or(r8, 0x00C000C0u, mag16);   // codes 7, 15
+  lo = __builtin_bit_cast(f16x8, a);
+  hi = __builtin_bit_cast(f16x8, b);
+}
+
+// Four fp16 pairs from the 8 byte-wide key codes of channels 8m .. 8m+7 (d0: channels 0-3,
+// d1: channels 4-7, channel i at bits 8i of its dword): elements in channel order, each code
+// in the low mantissa byte under `mag1024` (fp16 1024.0 twice), reading 1024 + c.
+__device__ __forceinline__ f16x8 key_codes8(uint32_t d0, uint32_t d1, uint32_t mag1024) {
+  u32x4 p;
+  p[0] = (d0 & 0xFFu) | ((d0 << 8) & 0x00FF0000u) | mag1024;          // channels 0, 1
+  p[1] = ((d0 >> 16) & 0xFFu) | ((d0 >> 8) & 0x00FF0000u) | mag1024;  // 2, 3
+  p[2] = (d1 & 0xFFu) | ((d1 << 8) & 0x00FF0000u) | mag1024;          // 4, 5
+  p[3] = ((d1 >> 16) & 0xFFu) | ((d1 >> 8) & 0x00FF0000u) | mag1024;  // 6, 7
+  return __builtin_bit_cast(f16x8, p);
+}
+
+// The two operands of value_codes from 16 nibble-wide value codes (d0: tokens 0-7, d1: tokens
+// 8-15, token i at bits 4i of its dword).  The low halves of d0 and d1 (tokens 0-3 and 8-11)
+// and the high halves (4-7 and 12-15) are put side by side, so that nibble j and nibble j + 4
+// of each are the pair (4hf + j, 4hf + j + 8); every nibble is moved to mantissa bits 4-7 under
+// `mag64` (fp16 64.0) and reads 64 + c.
+__device__ __forceinline__ void value_codes4(uint32_t d0, uint32_t d1, uint32_t mag64, f16x8& lo, f16x8& hi) {
+  const uint32_t e = (d0 & 0xFFFFu) | (d1 << 16);
+  const uint32_t f = (d0 >> 16) | (d1 & 0xFFFF0000u);
+  u32x4 a, b;
+  a[0] = and_or(e << 4, 0x00F000F0u, mag64);  // tokens 0, 8
+  a[1] = and_or(e, 0x00F000F0u, mag64);       // 1, 9
+  a[2] = and_or(e >> 4, 0x00F000F0u, mag64);  // 2, 10
+  a[3] = and_or(e >> 8, 0x00F000F0u, mag64);  // 3, 11
+  b[0] = and_or(f << 4, 0x00F000F0u, mag64);  // 4, 12
+  b[1] = and_or(f, 0x00F000F0u, mag64);       // 5, 13
+  b[2] = and_or(f >> 4, 0x00F000F0u, mag64);  // 6, 14
+  b[3] = and_or(f >> 8, 0x00F000F0u, mag64);  // 7, 15
   lo = __builtin_bit_cast(f16x8, a);
   hi = __builtin_bit_cast(f16x8, b);
 }
@@ -237,10 +272,35 @@ struct __align__(16) WaveLds {
   float gs[kHeadDim];              // 2^gamma (V) / value page scale, per channel
 };
 
+// Page geometry of one pair of code widths (4- or 8-bit keys, 2- or 4-bit values).
+template <int KB, int VB>
+struct DecFormat {
+  static constexpr int kKRow = kHeadDim * KB / 8;       // bytes of one token's key codes
+  static constexpr int kVRow = kBlockTokens * VB / 8;   // bytes of one channel's value codes
+  static constexpr int kKCode = kBlockTokens * kKRow;
+  static constexpr int kVCode = kHeadDim * kVRow;
+  static constexpr int kKPage = kKCode + kMetaBytes;
+  static constexpr int kVPage = kVCode + kMetaBytes;
+  // second coefficient slot of a lane: channel ch0 + 4 for nibbles (pairs j, j + 4 of a dword),
+  // ch0 + 1 for bytes (channel order)
+  static constexpr int kCh1 = KB == 8 ? 1 : 4;
+  // resident waves per SIMD: byte-wide keys need more page registers (4-bit keys with 4-bit values
+  // keep three waves at the cost of a two-register spill, which is faster than two waves)
+  static constexpr int kMinWaves = KB == 4 ? 3 : 2;
+};
+
+// Coefficient slots of a lane: channels ch0 and ch0 + kCh1, ch0 = 32*(lane/16) + 8*((lane/4)%4) +
+// (lane%4, or 2*(lane%4) for byte-wide key codes).
+template <int KB>
+__device__ __forceinline__ int coef_channel(int lane) {
+  return 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (KB == 8 ? 2 : 1) * (lane & 3);
+}
+
 // One page of one KV head as this lane loads it.
+template <int KB, int VB>
 struct PageRegs {
-  u32x4 kc[8];         // key codes: M-tile mt, row n -> token 32*(n/4) + 4*mt + n%4, channels 32g .. 32g+31
-  u32x2 vc[8];         // value codes: M-tile mt, row n -> channel 16mt + n, tokens 32g .. 32g+31
+  u32x4 kc[8][KB / 4];    // key codes: M-tile mt, row n -> token 32*(n/4) + 4*mt + n%4, channels 32g .. 32g+31
+  uint32_t vc[8][VB];     // value codes: M-tile mt, row n -> channel 16mt + n, tokens 32g .. 32g+31
   uint32_t ks0, ks1;   // key scale (fp16 bits) of channels ch0, ch1
   uint32_t kz0, kz1;   // key zero
   float kg0, kg1;      // key gamma
@@ -252,32 +312,47 @@ struct PageRegs {
 
 // Issues every load of one page without a branch: a bad page id reads page 0 instead (the
 // caller guarantees num_pages > 0) and only clears `ok`.
-__device__ __forceinline__ void load_page(PageRegs& P, int page, int num_pages, int hkv, int kvh,
+template <int KB, int VB>
+__device__ __forceinline__ void load_page(PageRegs<KB, VB>& P, int page, int num_pages, int hkv, int kvh,
                                           const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                                           int lane, int n, int g, int ch0) {
+  using F = DecFormat<KB, VB>;
   P.ok = page >= 0 && page < num_pages;
   const int safe = P.ok ? page : 0;
   // lane offsets are recomputed for every page (a few integer operations) rather than kept live
   // across the page loop, where registers are short
   asm volatile("" : "+v"(lane), "+v"(n), "+v"(g), "+v"(ch0));
-  const uint8_t* kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * kKPageBytes;
-  const uint8_t* vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * kVPageBytes;
+  const uint8_t* kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kKPage;
+  const uint8_t* vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kVPage;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
-    P.kc[mt] = *reinterpret_cast<const u32x4*>(kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * 64 + 16 * g);
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) P.vc[mt] = *reinterpret_cast<const u32x2*>(vp + (16 * mt + n) * 32 + 8 * g);
-  const uint8_t* km = kp + kKCodeBytes;
-  const uint8_t* vm = vp + kVCodeBytes;
+    for (int h = 0; h < KB / 4; ++h)
+      P.kc[mt][h] = *reinterpret_cast<const u32x4*>(kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * F::kKRow +
+                                                    (KB / 4) * 16 * g + 16 * h);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    if constexpr (VB == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(vp + (16 * mt + n) * F::kVRow + 8 * g);
+      P.vc[mt][0] = x[0];
+      P.vc[mt][1] = x[1];
+    } else {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(vp + (16 * mt + n) * F::kVRow + 16 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) P.vc[mt][k] = x[k];
+    }
+  }
+  const uint8_t* km = kp + F::kKCode;
+  const uint8_t* vm = vp + F::kVCode;
   const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + kMetaScale);
   const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + kMetaZero);
   const float* kgm = reinterpret_cast<const float*>(km + kMetaGamma);
   P.ks0 = ksc[ch0];
-  P.ks1 = ksc[ch0 + 4];
+  P.ks1 = ksc[ch0 + F::kCh1];
   P.kz0 = kzr[ch0];
-  P.kz1 = kzr[ch0 + 4];
+  P.kz1 = kzr[ch0 + F::kCh1];
   P.kg0 = kgm[ch0];
-  P.kg1 = kgm[ch0 + 4];
+  P.kg1 = kgm[ch0 + F::kCh1];
   P.kr = reinterpret_cast<const float2*>(km + kMetaRho)[lane];
   P.vs2 = reinterpret_cast<const uint32_t*>(vm + kMetaScale)[lane];
   P.vz2 = reinterpret_cast<const uint32_t*>(vm + kMetaZero)[lane];
@@ -293,8 +368,14 @@ struct WaveState {
   float acc[8][4];                     // o (rotated basis, hi or lo column) of channels 16mt + 4g + r
 };
 
-__device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, WaveLds& L, int G, int lane, int g,
-                                             int lo_col, uint32_t mag16, uint32_t mag64, uint32_t mag4) {
+// Magic fp16 exponent patterns (each twice, kept in vector registers) that turn codes into fp16 off + c.
+struct Mags {
+  uint32_t m16, m64, m4, m1024;
+};
+
+template <int KB, int VB>
+__device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveState& S, WaveLds& L, int G, int lane,
+                                             int g, int lo_col, const Mags& M) {
   // ---- key-side coefficients (this lane: slots ch0 and ch0 + 4, all heads) ---
   const float s0 = half_bits_to_float(P.ks0), s1 = half_bits_to_float(P.ks1);
   const float z0 = half_bits_to_float(P.kz0), z1 = half_bits_to_float(P.kz1);
@@ -316,8 +397,10 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   // with no positive key scale the coefficients are all zero but b is not: keep the page at unit scale
   const float inv_sa = live ? pow2i(ex - 14) : 1.f;
   const float e0s = e0 * sa, e1s = e1 * sa;
-  // the key offsets of this lane's two slots: 64 for nibbles 1 and 5 of a dword, else 16
-  const _Float16 off = (lane & 3) == 1 ? static_cast<_Float16>(64.0f) : static_cast<_Float16>(16.0f);
+  // the key offsets of this lane's two slots: 1024 for bytes; for nibbles 64 for nibbles 1 and 5
+  // of a dword, else 16
+  const _Float16 off = KB == 8 ? static_cast<_Float16>(1024.0f)
+                               : ((lane & 3) == 1 ? static_cast<_Float16>(64.0f) : static_cast<_Float16>(16.0f));
   const f16x2 offp = {off, off};
   float q0[kMaxGroup], q1[kMaxGroup];
   {
@@ -382,8 +465,14 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
     f32x4 da = {kinit, kinit, kinit, kinit}, db = da;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      da = mfma16x16x32(key_codes(P.kc[mt][ks], mag16, mag64), cb[ks], da);
-      db = mfma16x16x32(key_codes(P.kc[mt + 4][ks], mag16, mag64), cb[ks], db);
+      if constexpr (KB == 4) {
+        da = mfma16x16x32(key_codes(P.kc[mt][0][ks], M.m16, M.m64), cb[ks], da);
+        db = mfma16x16x32(key_codes(P.kc[mt + 4][0][ks], M.m16, M.m64), cb[ks], db);
+      } else {
+        const int h = ks >> 1, d = 2 * (ks & 1);
+        da = mfma16x16x32(key_codes8(P.kc[mt][h][d], P.kc[mt][h][d + 1], M.m1024), cb[ks], da);
+        db = mfma16x16x32(key_codes8(P.kc[mt + 4][h][d], P.kc[mt + 4][h][d + 1], M.m1024), cb[ks], db);
+      }
     }
     const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
     const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
@@ -433,7 +522,8 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       split_prod(pv[hf][j], fvv[hf][j], pv[hf + 2][j], fvv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
-  // value offsets (4 for even tokens, 16 for odd) of exactly the fp16 weights used
+  // value offsets (2-bit codes: 4 for even tokens, 16 for odd; 4-bit codes: 64) of exactly the fp16
+  // weights used
   {
     const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 #pragma unroll
@@ -448,7 +538,8 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
   lsum = head_sum(lsum);
   S.l_run = fmaf(S.l_run, alpha, lsum);
   // u minus the value offsets, in value-page-scaled units, enters the hi columns
-  const float ucorr = head_sum(fmaf(usum, sw, -fmaf(16.f, wod, 4.f * wev)));
+  const float voff = VB == 2 ? fmaf(16.f, wod, 4.f * wev) : 64.f * (wev + wod);
+  const float ucorr = head_sum(fmaf(usum, sw, -voff));
   const float vinit = sel_lo(ucorr, 0.f);
   f16x8 wb[2][2];  // [u][hf]
 #pragma unroll
@@ -476,7 +567,11 @@ __device__ __forceinline__ void process_page(const PageRegs& P, WaveState& S, Wa
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f16x8 c0, c1;
-      value_codes(P.vc[mt][u], mag4, mag16, c0, c1);
+      if constexpr (VB == 2) {
+        value_codes(P.vc[mt][u], M.m4, M.m16, c0, c1);
+      } else {
+        value_codes4(P.vc[mt][2 * u], P.vc[mt][2 * u + 1], M.m64, c0, c1);
+      }
       d = mfma16x16x32(c0, wb[u][0], d);
       d = mfma16x16x32(c1, wb[u][1], d);
     }
@@ -620,7 +715,8 @@ __device__ __forceinline__ void tail_partial(const uint16_t* __restrict__ qrow0,
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 3) void decode_kernel(
+template <int KB, int VB>
+__global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, int hq, int hkv,
@@ -695,9 +791,9 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
     for (int h = 0; h < kMaxGroup; ++h)
       qraw[h] = reinterpret_cast<const uint32_t*>(qb + (h < G ? h : 0) * kHeadDim)[lane];
     __builtin_amdgcn_sched_barrier(0);
-    // coefficient slots of this lane: channels ch0 = 32*(lane/16) + 8*((lane/4)%4) + lane%4 and ch0 + 4
-    const int ch0 = 32 * (lane >> 4) + 8 * ((lane >> 2) & 3) + (lane & 3);
-    PageRegs A;
+    const int ch0 = coef_channel<KB>(lane);
+    constexpr int ch1 = DecFormat<KB, VB>::kCh1;
+    PageRegs<KB, VB> A;
     load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -717,14 +813,14 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    uint32_t mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag4 = 0x44004400u;  // fp16 16 / 64 / 4, twice
-    asm volatile("" : "+v"(mag16), "+v"(mag64), "+v"(mag4));
+    Mags M{0x4C004C00u, 0x54005400u, 0x44004400u, 0x64006400u};  // fp16 16 / 64 / 4 / 1024, twice
+    asm volatile("" : "+v"(M.m16), "+v"(M.m64), "+v"(M.m4), "+v"(M.m1024));
     WaveState S;
     float qmax = 0.f;
   #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       const float a = qt[h][ch0];
-      const float c = qt[h][ch0 + 4];
+      const float c = qt[h][ch0 + ch1];
       qlane[lane][h] = a;
       qlane[lane][kMaxGroup + h] = c;
       qmax = fmaxf(qmax, fmaxf(fabsf(a), fabsf(c)));
@@ -746,7 +842,7 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
     bool bad_page = false;
     if (wu < cnt) {
       if (A.ok) {
-        process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+        process_page(A, S, L, G, lane, g, lo_col, M);
       } else {
         bad_page = true;
       }
@@ -754,7 +850,7 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
     for (int i = wu + kWaves; i < cnt; i += kWaves) {
       load_page(A, bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
       if (A.ok) {
-        process_page(A, S, L, G, lane, g, lo_col, mag16, mag64, mag4);
+        process_page(A, S, L, G, lane, g, lo_col, M);
       } else {
         bad_page = true;
       }
@@ -855,10 +951,12 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
-                         const void* v_tail, int batch, int hq, int hkv, int blocks_per_split, int max_splits,
-                         float scale_log2, float* out, float* part, uint32_t* counters, uint32_t* flags,
-                         hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
+                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int blocks_per_split,
+                         int max_splits, float scale_log2, float* out, float* part, uint32_t* counters,
+                         uint32_t* flags, hipStream_t stream) {
+  auto kern = kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4> : decode_kernel<8, 2>)
+                         : (vbits == 4 ? decode_kernel<4, 4> : decode_kernel<4, 2>);
+  hipLaunchKernelGGL(kern, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens,
                      static_cast<const uint16_t*>(k_tail), static_cast<const uint16_t*>(v_tail), hq, hkv,

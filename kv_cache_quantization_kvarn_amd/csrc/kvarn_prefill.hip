@@ -29,9 +29,7 @@
 //     rows follow in blocks of 128 through the same LDS layout (keys copied, values transposed),
 //     with unit factors, the raw query and the causal mask.
 //
-// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.  The same
-// kernel serves decode in the code widths the matrix-core decode kernel does not (one query per
-// sequence, pages split over workgroups, see prefill_kernel's modes).
+// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.
 #include "kvarn_common.h"
 
 namespace kvarn {
@@ -74,19 +72,7 @@ struct __align__(16) PfLds {
   float zv[kBlockTokens];       // per token: value 2^rho z
   float sa, sw;                 // the block's power-of-two coefficient scales
   float qmax[kPfWaves];         // per wave: max |query coefficient| of the current phase
-  int last;                     // decode modes: this workgroup merges the splits
 };
-
-constexpr int kPartStride = kHeadDim + 2;  // decode-mode partial: o[128], m, l per (split, query head)
-
-// Agent-scope relaxed accesses to the split partials and counters: they go through to the
-// device-coherent level, so workgroups on other XCDs see them without an L2-wide fence.
-__device__ __forceinline__ void store_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Swizzle key of a key row: the 16 lanes of a score fragment read tokens 32(n/4) + 4mt + n%4, whose
 // keys are exactly n = 0..15.
@@ -601,25 +587,15 @@ __device__ __forceinline__ float load_query(float (&qv)[32], const uint16_t* __r
 
 }  // namespace
 
-// mode 0: chunked prefill (lengths from prefix_lens, new_lens, q_lens).
-// mode 1: decode over packed pages only: prefix_lens holds seq_lens (multiples of 128), one query
-//         per sequence that sees every packed token.
-// mode 2: decode over packed pages plus an fp16 tail: prefix_lens holds seq_lens; the first
-//         seq_len & ~127 tokens are packed, the rest are rows of the tail (k_new / v_new with
-//         max_new = 128); one query that sees all of them.
-// In both decode modes the query sits after its sequence's last row, which the prefill formula
-// (query i at fp16 row new_len - q_len + i) gives with q_len = 1.  The tile index is then a split
-// of the sequence's pages (bps pages each; in mode 2 one more split takes the tail rows): every
-// split writes a partial (o in the original basis, m, l) per head to `part`, counts itself in at
-// counters[pair], and the last to arrive merges the partials with log-sum-exp weights.
+// One workgroup per (sequence, KV head, tile of qt queries): query i of a sequence sits at fp16 row
+// new_len - q_len + i and sees every packed token and the fp16 rows up to its own.
 template <int KB, int VB>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int max_q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ prefix_lens,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int max_new,
     const int32_t* __restrict__ new_lens, const int32_t* __restrict__ q_lens, int batch, int hq, int hkv, int qt,
-    int ntile, int mode, int bps, float scale_log2, float* __restrict__ out, float* __restrict__ part,
-    uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
+    int ntile, float scale_log2, float* __restrict__ out, uint32_t* __restrict__ flags) {
   using F = PfFormat<KB, VB>;
   __shared__ PfLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
@@ -633,23 +609,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
   if (pair >= batch * hkv) return;
   const int b = pair / hkv, kvh = pair - b * hkv;
   const int G = hq / hkv;
-  const int i0 = mode == 0 ? tile * qt : 0;
+  const int i0 = tile * qt;
 
-  int prefix, nnew, nq;
-  bool bad;
-  if (mode == 0) {
-    prefix = prefix_lens[b];
-    nnew = new_lens[b];
-    nq = q_lens[b];
-    bad = prefix < 0 || (prefix & 127) || prefix > kBlockTokens * max_blocks || nnew < 0 || nnew > max_new ||
-          nq < 0 || nq > nnew || nq > max_q;
-  } else {
-    const int sl = prefix_lens[b];
-    prefix = mode == 1 ? sl : (sl & ~127);
-    nnew = mode == 1 ? 0 : (sl & 127);
-    nq = sl > 0 ? 1 : 0;
-    bad = sl < 0 || (mode == 1 && (sl & 127)) || prefix > kBlockTokens * max_blocks;
-  }
+  const int prefix = prefix_lens[b], nnew = new_lens[b], nq = q_lens[b];
+  const bool bad = prefix < 0 || (prefix & 127) || prefix > kBlockTokens * max_blocks || nnew < 0 ||
+                   nnew > max_new || nq < 0 || nq > nnew || nq > max_q;
 
   // the lane's two rows
   int ri[kCt], rh[kCt];
@@ -673,7 +637,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
   };
 
   if (bad || i0 >= nq) {
-    if (mode != 0 && tile != 0) return;  // the first split writes the zero rows
     // no query of this tile: zero rows (and flag a bad length)
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
@@ -686,8 +649,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     return;
   }
 
-  // a wave whose rows are all padding (the tail of the last tile; every wave but the first in the
-  // decode modes) stages blocks with the others but skips the products
+  // a wave whose rows are all padding (the tail of the last tile) stages blocks with the others but
+  // skips the products
   const bool wave_live = __builtin_amdgcn_ballot_w64(valid[0]) != 0;
   PfState S;
 #pragma unroll
@@ -698,24 +661,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     for (int i = 0; i < 32; ++i) S.o[ct][i] = 0.f;
   }
   const int nblk = prefix >> 7;
-  // packed blocks [pb0, pb1) and whether the fp16 rows are attended here (all of them in mode 0)
-  int pb0 = 0, pb1 = nblk, nsplit = 1;
-  bool rows_here = true;
-  if (mode != 0) {
-    const int npsplit = (nblk + bps - 1) / bps;
-    nsplit = npsplit + (nnew > 0 ? 1 : 0);
-    if (tile >= nsplit) return;
-    if (tile < npsplit) {
-      pb0 = tile * bps;
-      pb1 = min(nblk, pb0 + bps);
-      rows_here = false;
-    } else {
-      pb0 = pb1 = 0;
-    }
-  }
 
   // ---- packed prefix (rotated basis) ----------------------------------------------------------------
-  if (pb1 > pb0) {
+  if (nblk > 0) {
     float mx = 0.f;
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct)
@@ -732,15 +680,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
       load_page_raw(R, k_pool + unit * kstride, v_pool + unit * vstride, tid);
     };
     PageRaw<F> R;
-    int cur = bt[pb0];
+    int cur = bt[0];
     request(R, cur);
-    for (int p = pb0; p < pb1; ++p) {
+    for (int p = 0; p < nblk; ++p) {
       const bool ok = cur >= 0 && cur < num_pages;
       __syncthreads();  // every wave is done with the previous block
       if (ok) store_page(L, R, tid);
-      const int nxt = p + 1 < pb1 ? bt[p + 1] : 0;
+      const int nxt = p + 1 < nblk ? bt[p + 1] : 0;
       __syncthreads();
-      if (p + 1 < pb1) request(R, nxt);
+      if (p + 1 < nblk) request(R, nxt);
       if (ok) page_factors(L, tid, lane);
       __syncthreads();
       if (ok) {
@@ -774,7 +722,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     if (lane == 0) L.qmax[w] = mx;
   }
   const int off = nnew - nq;                                  // fp16 row of query 0
-  const int last = rows_here ? off + min(i0 + qt, nq) - 1 : -1;  // last fp16 row any query of the tile sees
+  const int last = off + min(i0 + qt, nq) - 1;                // last fp16 row any query of the tile sees
   const size_t rstride = static_cast<size_t>(hkv) * kHeadDim;
   const uint16_t* kb = k_new + (static_cast<size_t>(b) * max_new * hkv + kvh) * kHeadDim;
   const uint16_t* vb = v_new + (static_cast<size_t>(b) * max_new * hkv + kvh) * kHeadDim;
@@ -792,66 +740,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
     if (wave_live) attend_block<true>(S, L, lane, lim);
-  }
-
-  if (mode != 0) {
-    // ---- decode modes: partial of this split, then the merge by the last split to arrive -----------
-    const float l = sum32(sum16(S.l[0]));
-    if (valid[0]) {
-      float* pp = part + ((static_cast<size_t>(pair) * ntile + tile) * kMaxGroup + rh[0]) * kPartStride;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) store_coherent(pp + 16 * mt + 4 * g + r, S.o[0][4 * mt + r]);
-      if (g == 0) {
-        store_coherent(pp + kHeadDim, S.m[0]);
-        store_coherent(pp + kHeadDim + 1, l);
-      }
-    }
-    // every wave waits until its stores are acknowledged before the workgroup counts itself in
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t prev = __hip_atomic_fetch_add(counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      L.last = prev == static_cast<uint32_t>(nsplit - 1);
-    }
-    __syncthreads();
-    if (!L.last) return;
-    if (tid == 0) __hip_atomic_store(counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // wave w merges head w; lane s holds the maximum and sum of split s, lane l output channels 2l, 2l + 1
-    if (w < G) {
-      constexpr size_t kSplitStride = static_cast<size_t>(kMaxGroup) * kPartStride;
-      const float* ph = part + (static_cast<size_t>(pair) * ntile * kMaxGroup + w) * kPartStride;
-      const int sp = lane < nsplit ? lane : 0;
-      const float ms = load_coherent(ph + sp * kSplitStride + kHeadDim);
-      const float ls = load_coherent(ph + sp * kSplitStride + kHeadDim + 1);
-      const float msv = lane < nsplit ? ms : -INFINITY;
-      const float mx = wave_max(msv);
-      const float wgt = msv == -INFINITY ? 0.f : ex2(msv - mx);
-      const float den = rows4_sum(row16_sum(lane < nsplit ? wgt * ls : 0.f));
-      float n0 = 0.f, n1 = 0.f;
-      for (int s0 = 0; s0 < nsplit; s0 += 8) {
-        float2 o8[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int sk = s0 + k < nsplit ? s0 + k : 0;
-          const float* pq = ph + sk * kSplitStride + 2 * lane;
-          o8[k] = make_float2(load_coherent(pq), load_coherent(pq + 1));
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int src = s0 + k < nsplit ? s0 + k : 0;
-          const float wsrc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), src));
-          const float wk = s0 + k < nsplit ? wsrc : 0.f;
-          n0 = fmaf(wk, o8[k].x, n0);
-          n1 = fmaf(wk, o8[k].y, n1);
-        }
-      }
-      const float inv = den > 0.f ? 1.0f / den : 0.f;
-      float* ob = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G + w) * kHeadDim;
-      reinterpret_cast<float2*>(ob)[lane] = make_float2(n0 * inv, n1 * inv);
-    }
-    return;
   }
 
   // ---- normalise and store ---------------------------------------------------------------------------
@@ -873,11 +761,11 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, int kbits, int vbits, int mode, int bps, int max_splits, float scale_log2,
-                          float* out, float* part, uint32_t* counters, uint32_t* flags, hipStream_t stream) {
+                          int hq, int hkv, int kbits, int vbits, float scale_log2, float* out, uint32_t* flags,
+                          hipStream_t stream) {
   const int G = hq / hkv;
   const int qt = kPfRows / G;
-  const int ntile = mode == 0 ? (max_q + qt - 1) / qt : max_splits;
+  const int ntile = (max_q + qt - 1) / qt;
   const long pairs8 = (static_cast<long>(batch) * hkv + 7) / 8;
   const long groups = 8 * pairs8 * ntile;
   if (groups == 0) return hipSuccess;
@@ -888,7 +776,7 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
                      static_cast<const uint16_t*>(q), max_q, static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, prefix_lens,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), max_new, new_lens,
-                     q_lens, batch, hq, hkv, qt, ntile, mode, bps, scale_log2, out, part, counters, flags);
+                     q_lens, batch, hq, hkv, qt, ntile, scale_log2, out, flags);
   return hipGetLastError();
 }
 

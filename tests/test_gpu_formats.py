@@ -141,12 +141,61 @@ def test_decode_tail_and_prefill(K, name):
     d = float(np.abs(outp.cpu().numpy() - ref).max())
     say("  prefill max-abs diff %.3e" % d)
     assert d <= chk.ATTN_TOL
-    # bad lengths are flagged in the generic decode too
+    # bad lengths are flagged in these formats too
     K.kvarn_decode_attention(cfg, q, kp, vp, bt.cuda(), torch.tensor([128, 0, 200, 0], dtype=torch.int32).cuda(), hkv,
                              out, ws, dev_flags=fl)
     torch.cuda.synchronize()
     assert K.kvarn_read_flags(fl) & 2
     assert torch.all(out[2] == 0)
+
+
+@pytest.mark.parametrize("name", FORMATS)
+@pytest.mark.parametrize("G", [1, 3, 8])
+def test_decode_group_sizes(K, name, G):
+    """Decode with a tail at 1, 3 and 8 query heads per KV head: every column count of the
+    coefficient operands, ragged lengths, a bad page id flagged and skipped."""
+    cfg = K.kvarn_config_parse(name)
+    hkv = 2
+    hq = G * hkv
+    say("case: %s decode with a tail, G = %d, ragged, paged" % (name, G))
+    g = torch.Generator().manual_seed(700 + 10 * G + len(name))
+    nblk = [2, 7, 0, 4]
+    total = sum(nblk)
+    k, v = randn_kv(g, total * 128, hkv)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    kp, vp = quantize(K, cfg, k.cuda(), v.cuda(), perm, total, 0)
+    bt = torch.full((4, 8), -1, dtype=torch.int32)
+    off = 0
+    for b, nb in enumerate(nblk):
+        bt[b, :nb] = perm[off:off + nb]
+        off += nb
+    q = torch.randn(4, hq, 128, generator=g).half().cuda()
+    kt, vt = randn_kv(g, 4 * 128, hkv)
+    kt, vt = kt.view(4, 128, hkv, 128).cuda(), vt.view(4, 128, hkv, 128).cuda()
+    slt = torch.tensor([128 * 2 + 1, 128 * 7 + 126, 64, 128 * 4], dtype=torch.int32)
+    ws = K.alloc_workspace(cfg, 4, hq, hkv, bt.shape[1])
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((4, hq, 128), float("nan"), device="cuda")
+    K.kvarn_decode_attention_tail(cfg, q, kp, vp, bt.cuda(), slt.cuda(), kt, vt, hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    ref = o.decode_tail(q.cpu().numpy(), kph, vph, bt.numpy(), slt.numpy(), kt.cpu().numpy(), vt.cpu().numpy(), hkv)
+    d = float(np.abs(out.cpu().numpy() - ref).max())
+    say("  decode with tail max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
+    # a page id past the pool: flagged, that page skipped, the other sequences untouched
+    bad = bt.clone()
+    bad[1, 3] = total + 5
+    sl = torch.tensor([128 * nb for nb in nblk], dtype=torch.int32)
+    K.kvarn_decode_attention(cfg, q, kp, vp, bad.cuda(), sl.cuda(), hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) & 1
+    ref = o.decode(q.cpu().numpy(), kph, vph, bt.numpy(), sl.numpy(), hkv, seqs=[0, 3])
+    got = out.cpu().numpy()
+    d = max(float(np.abs(got[b] - ref[b]).max()) for b in (0, 3))
+    assert d <= chk.ATTN_TOL
+    assert np.all(got[2] == 0)
 
 
 def test_k8v4_llama3_layer_decode_sampled(K):
@@ -185,7 +234,7 @@ def test_k8v4_llama3_layer_decode_sampled(K):
     assert worst <= chk.ATTN_TOL
 
 
-def test_generic_decode_most_splits(K):
+def test_wide_decode_most_splits(K):
     """1,024 blocks of one KV head plus a 90-token tail: 63 page splits and the tail split in one merge."""
     cfg = K.kvarn_config_parse("kvarn_k4v4_g128")
     say("case: kvarn_k4v4_g128 decode with a tail over 1,024 blocks (64 splits)")
