@@ -40,6 +40,11 @@ Parameters the pages leave open, fixed here (each is one reading):
     byte each, token-major (byte 128*t + c); 4-bit value codes channel-major, two
     tokens per byte (byte 64*c + t//2, even token in the low nibble).  A page's
     bit width follows from its byte count;
+  * group size 64 (kvarn_k{4,8}v{2,4}_g64): each group of the group-128 format
+    splits into two halves of 64 consecutive elements -- a key group is one
+    channel over tokens 64h .. 64h+63, a value group one token over channels
+    64h .. 64h+63 -- each with its own fp16 scale and zero, stored half-major
+    (entry 128*h + j); every other step is unchanged;
   * decode: query head h reads KV head h // (Hq / Hkv); logits scaled by
     1/sqrt(128) unless a positive scale is given; plain softmax; output in the
     original (unrotated) basis.
@@ -59,7 +64,8 @@ K_LEVELS = 15  # 4-bit keys (the format the post names)
 V_LEVELS = 3   # 2-bit values
 K_BITS_ALLOWED = (4, 8)
 V_BITS_ALLOWED = (2, 4)
-META_BYTES = 2 * 256 + 2 * 512
+GROUPS_ALLOWED = (128, 64)
+META_BYTES = 2 * 256 + 2 * 512  # group size 128
 
 # Page byte format (one page = one 128-token block of one KV head).
 K_CODES_BYTES = BLOCK * HEAD_DIM // 2      # 8192: token-major, two channels per byte
@@ -68,17 +74,28 @@ K_PAGE_BYTES = K_CODES_BYTES + 2 * 256 + 2 * 512   # 9728
 V_PAGE_BYTES = V_CODES_BYTES + 2 * 256 + 2 * 512   # 5632
 
 
-def page_bytes(bits: int) -> int:
+def meta_bytes(group: int = 128) -> int:
+    """Metadata of one page: scale and zero fp16 per group (128 // group per channel or token), rho and gamma fp32[128]."""
+    return 2 * 2 * 128 * (BLOCK // group) + 2 * 4 * 128
+
+
+def page_bytes(bits: int, group: int = 128) -> int:
     """Bytes of one page whose codes have `bits` bits: 128 x 128 codes plus the metadata."""
-    return BLOCK * HEAD_DIM * bits // 8 + META_BYTES
+    return BLOCK * HEAD_DIM * bits // 8 + meta_bytes(group)
+
+
+def format_of_page(nbytes: int, is_v: bool):
+    """(code width, group size) of a page from its byte count (unambiguous within keys and within values)."""
+    for b in (V_BITS_ALLOWED if is_v else K_BITS_ALLOWED):
+        for gs in GROUPS_ALLOWED:
+            if nbytes == page_bytes(b, gs):
+                return b, gs
+    raise ValueError("a %s page of %d bytes matches no format" % ("value" if is_v else "key", nbytes))
 
 
 def bits_of_page(nbytes: int, is_v: bool) -> int:
-    """Code width of a page from its byte count (unambiguous within keys and within values)."""
-    for b in (V_BITS_ALLOWED if is_v else K_BITS_ALLOWED):
-        if nbytes == page_bytes(b):
-            return b
-    raise ValueError("a %s page of %d bytes matches no format" % ("value" if is_v else "key", nbytes))
+    """Code width of a page from its byte count."""
+    return format_of_page(nbytes, is_v)[0]
 
 
 # --------------------------------------------------------------------------
@@ -164,13 +181,15 @@ def rtn_codes(values: np.ndarray, s16, z16, levels: int) -> np.ndarray:
     return np.clip(np.rint(u), 0, levels).astype(np.uint8)
 
 
-def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS, bits: int = 0) -> dict:
+def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS, bits: int = 0,
+                  group: int = 128) -> dict:
     """Quantise one fp16 block [128 tokens, 128 channels] of K (is_v False) or V, codes of
-    ``bits`` bits (default: 4 for K, 2 for V; levels 2^bits - 1).
+    ``bits`` bits (default: 4 for K, 2 for V; levels 2^bits - 1), groups of ``group`` elements.
 
     Returns the stored fields: codes [128, 128] (token, channel), scale and zero
-    (fp16, per channel for K, per token for V), rho (fp32 per token) and gamma
-    (fp32 per channel).
+    (fp16, per channel for K, per token for V: shape [128] for group 128, [2, 128]
+    for group 64 with row h the groups over elements 64h .. 64h+63), rho (fp32 per
+    token) and gamma (fp32 per channel).
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
     r = rotate(x)
@@ -181,26 +200,37 @@ def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = 
     bits = bits or (2 if is_v else 4)
     levels = (1 << bits) - 1
     codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
-    ngroups = BLOCK if is_v else HEAD_DIM
-    scale = np.zeros(ngroups, dtype=np.float16)
-    zero = np.zeros(ngroups, dtype=np.float16)
-    for g in range(ngroups):
-        if is_v:
-            codes[g, :], scale[g], zero[g] = rtn_group(n32[g, :], levels)
-        else:
-            codes[:, g], scale[g], zero[g] = rtn_group(n32[:, g], levels)
+    nseg = BLOCK // group
+    scale = np.zeros((nseg, 128), dtype=np.float16)
+    zero = np.zeros((nseg, 128), dtype=np.float16)
+    for h in range(nseg):
+        seg = slice(group * h, group * (h + 1))
+        for g in range(128):
+            if is_v:
+                codes[g, seg], scale[h, g], zero[h, g] = rtn_group(n32[g, seg], levels)
+            else:
+                codes[seg, g], scale[h, g], zero[h, g] = rtn_group(n32[seg, g], levels)
+    if nseg == 1:
+        scale, zero = scale[0], zero[0]
     return {"codes": codes, "scale": scale, "zero": zero, "rho": rho32, "gamma": gam32}
+
+
+def group_params(fields: dict, is_v: bool):
+    """Scale and zero of every element's own group, as fp16 arrays [128 tokens, 128 channels]."""
+    s = np.asarray(fields["scale"], dtype=np.float16).reshape(-1, 128)
+    z = np.asarray(fields["zero"], dtype=np.float16).reshape(-1, 128)
+    group = BLOCK // s.shape[0]
+    idx = np.arange(128) // group  # half of each token (keys) or channel (values)
+    if is_v:
+        return s[idx[None, :], np.arange(128)[:, None]], z[idx[None, :], np.arange(128)[:, None]]
+    return s[idx[:, None], np.arange(128)[None, :]], z[idx[:, None], np.arange(128)[None, :]]
 
 
 def dequantize_tile(fields: dict, is_v: bool) -> np.ndarray:
     """Rebuild a block in the original basis: N^ = s*q + z, R^ = N^ * 2^(rho+gamma), X^[t] = H @ R^[t]."""
     q = fields["codes"].astype(np.float64)
-    s = fields["scale"].astype(np.float64)
-    z = fields["zero"].astype(np.float64)
-    if is_v:
-        n_hat = q * s[:, None] + z[:, None]
-    else:
-        n_hat = q * s[None, :] + z[None, :]
+    s, z = group_params(fields, is_v)
+    n_hat = q * s.astype(np.float64) + z.astype(np.float64)
     rho = fields["rho"].astype(np.float64)
     gam = fields["gamma"].astype(np.float64)
     r_hat = n_hat * np.exp2(rho[:, None] + gam[None, :])
@@ -251,7 +281,8 @@ def unpack_v_codes(buf: bytes, bits: int = 2) -> np.ndarray:
 
 
 def encode_page(fields: dict, is_v: bool, bits: int = 0) -> bytes:
-    """Page = codes | scale fp16[128] | zero fp16[128] | rho fp32[128 tokens] | gamma fp32[128 channels], little endian."""
+    """Page = codes | scale fp16[groups] | zero fp16[groups] | rho fp32[128 tokens] | gamma fp32[128 channels],
+    little endian; groups = 128, or 2 x 128 half-major for group size 64."""
     bits = bits or (2 if is_v else 4)
     codes = pack_v_codes(fields["codes"], bits) if is_v else pack_k_codes(fields["codes"], bits)
     meta = (np.asarray(fields["scale"], dtype="<f2").tobytes() + np.asarray(fields["zero"], dtype="<f2").tobytes()
@@ -261,14 +292,18 @@ def encode_page(fields: dict, is_v: bool, bits: int = 0) -> bytes:
 
 def decode_page(buf: bytes, is_v: bool) -> dict:
     buf = bytes(buf)
-    bits = bits_of_page(len(buf), is_v)
+    bits, group = format_of_page(len(buf), is_v)
     ncode = BLOCK * HEAD_DIM * bits // 8
     codes = unpack_v_codes(buf[:ncode], bits) if is_v else unpack_k_codes(buf[:ncode], bits)
     o = ncode
-    scale = np.frombuffer(buf[o:o + 256], dtype="<f2").copy()
-    zero = np.frombuffer(buf[o + 256:o + 512], dtype="<f2").copy()
-    rho = np.frombuffer(buf[o + 512:o + 1024], dtype="<f4").copy()
-    gam = np.frombuffer(buf[o + 1024:o + 1536], dtype="<f4").copy()
+    nsz = 256 * (BLOCK // group)  # bytes of the scales, and of the zeros
+    scale = np.frombuffer(buf[o:o + nsz], dtype="<f2").copy()
+    zero = np.frombuffer(buf[o + nsz:o + 2 * nsz], dtype="<f2").copy()
+    o += 2 * nsz
+    rho = np.frombuffer(buf[o:o + 512], dtype="<f4").copy()
+    gam = np.frombuffer(buf[o + 512:o + 1024], dtype="<f4").copy()
+    if group != BLOCK:
+        scale, zero = scale.reshape(BLOCK // group, 128), zero.reshape(BLOCK // group, 128)
     return {"codes": codes, "scale": scale, "zero": zero, "rho": rho, "gamma": gam}
 
 
@@ -282,15 +317,15 @@ def quantize_blocks(k16: np.ndarray, v16: np.ndarray, dst_pages, k_pool: np.ndar
     code widths of the format.
     """
     n_tok, hkv, _ = k16.shape
-    kb, vb = bits_of_page(k_pool.shape[2], False), bits_of_page(v_pool.shape[2], True)
+    (kb, kg), (vb, vg) = format_of_page(k_pool.shape[2], False), format_of_page(v_pool.shape[2], True)
     for b in range(n_tok // BLOCK):
         p = int(dst_pages[b])
         for h in range(hkv):
             sl = slice(BLOCK * b, BLOCK * (b + 1))
-            k_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(k16[sl, h, :], False, bits=kb), False, kb),
-                                            np.uint8)
-            v_pool[p, h, :] = np.frombuffer(encode_page(quantize_tile(v16[sl, h, :], True, bits=vb), True, vb),
-                                            np.uint8)
+            k_pool[p, h, :] = np.frombuffer(
+                encode_page(quantize_tile(k16[sl, h, :], False, bits=kb, group=kg), False, kb), np.uint8)
+            v_pool[p, h, :] = np.frombuffer(
+                encode_page(quantize_tile(v16[sl, h, :], True, bits=vb, group=vg), True, vb), np.uint8)
 
 
 def dequantize_pages(pool: np.ndarray, pages, head: int, is_v: bool) -> np.ndarray:

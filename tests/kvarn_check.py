@@ -68,8 +68,8 @@ class TileStats:
 
 def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: bool) -> None:
     """Compare one GPU-written page against the oracle's quantisation of the same fp16 tile."""
-    bits = o.bits_of_page(len(page_bytes), is_v)  # the format's code width
-    ref = o.quantize_tile(x16, is_v, bits=bits)
+    bits, group = o.format_of_page(len(page_bytes), is_v)  # the format's code width and group size
+    ref = o.quantize_tile(x16, is_v, bits=bits, group=group)
     got = o.decode_page(page_bytes, is_v)
     stats.tiles += 1
     for key in ("rho", "gamma"):
@@ -81,7 +81,7 @@ def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: boo
         d = f16_ulp_distance(got[key], ref[key])
         stats.sz_exact += int((d == 0).sum())
         stats.sz_maxulp = max(stats.sz_maxulp, int(d.max()))
-    stats.groups += len(ref["scale"])
+    stats.groups += ref["scale"].size
     diff = np.abs(got["codes"].astype(np.int32) - ref["codes"].astype(np.int32))
     stats.codes += diff.size
     stats.code_mismatch += int((diff != 0).sum())
@@ -90,9 +90,12 @@ def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: boo
     n32 = o.normalized(o.rotate(x16.astype(np.float64)), got["rho"], got["gamma"]).astype(np.float32)
     cond = np.zeros_like(got["codes"])
     levels = (1 << bits) - 1
-    for gi in range(128):
-        if is_v:
-            cond[gi, :] = o.rtn_codes(n32[gi, :], got["scale"][gi], got["zero"][gi], levels)
-        else:
-            cond[:, gi] = o.rtn_codes(n32[:, gi], got["scale"][gi], got["zero"][gi], levels)
+    gs, gz = got["scale"].reshape(-1, 128), got["zero"].reshape(-1, 128)
+    for h in range(gs.shape[0]):
+        seg = slice(group * h, group * (h + 1))
+        for gi in range(128):
+            if is_v:
+                cond[gi, seg] = o.rtn_codes(n32[gi, seg], gs[h, gi], gz[h, gi], levels)
+            else:
+                cond[seg, gi] = o.rtn_codes(n32[seg, gi], gs[h, gi], gz[h, gi], levels)
     stats.cond_mismatch += int((cond != got["codes"]).sum())

@@ -633,3 +633,101 @@ def test_wide_pools_decode_closer_to_fp16_attention():
         o.quantize_blocks(k, v, pages, kp, vp)
         errs[kb, vb] = np.abs(o.decode(q, kp, vp, pages[None, :], np.array([256]), 1)[0] - exact).max()
     assert errs[8, 4] < errs[4, 2] / 3
+
+
+# ---- group size 64 ----------------------------------------------------------------------------------------
+# Reading: every group of the group-128 format splits into two halves of 64 consecutive elements (keys: one
+# channel over tokens 64h .. 64h+63; values: one token over channels 64h .. 64h+63), each with its own scale
+# and zero stored half-major; every other step is unchanged.
+
+def test_g64_page_sizes_and_format_lookup():
+    assert (o.page_bytes(4, 64), o.page_bytes(8, 64), o.page_bytes(2, 64)) == (10240, 18432, 6144)
+    for is_v, widths in ((False, (4, 8)), (True, (2, 4))):
+        for b in widths:
+            for gs in (128, 64):
+                assert o.format_of_page(o.page_bytes(b, gs), is_v) == (b, gs)
+
+
+@pytest.mark.parametrize("is_v,bits", [(False, 4), (True, 2), (False, 8), (True, 4)])
+def test_g64_groups_are_subsets_of_g128_groups(is_v, bits):
+    """A half group's range lies inside its whole group's: scale no larger, zero no smaller (fp16 rounding
+    is monotone), and strictly inside for at least one half of every group of random data."""
+    x = fp16_block(81 + bits, outliers=4, mult=20.0)
+    f128 = o.quantize_tile(x, is_v, bits=bits)
+    f64 = o.quantize_tile(x, is_v, bits=bits, group=64)
+    assert f64["scale"].shape == (2, 128) and f64["zero"].shape == (2, 128)
+    assert np.array_equal(f64["rho"], f128["rho"]) and np.array_equal(f64["gamma"], f128["gamma"])
+    s128, z128 = f128["scale"].astype(np.float64), f128["zero"].astype(np.float64)
+    s64, z64 = f64["scale"].astype(np.float64), f64["zero"].astype(np.float64)
+    assert np.all(s64 <= s128[None, :]) and np.all(z64 >= z128[None, :])
+    # each whole group's minimum sits in one of its halves, whose zero then equals the whole group's
+    assert np.all(np.minimum(z64[0], z64[1]) == z128)
+    # every whole group has a strictly narrower half (the half without its minimum or its maximum); the
+    # half holding both (about one group in two) keeps the whole range
+    assert np.all(np.minimum(s64[0], s64[1]) < s128)
+    assert 0.6 < (s64 < s128[None, :]).mean() < 0.95
+
+
+@pytest.mark.parametrize("is_v,bits", [(False, 4), (True, 2), (False, 8), (True, 4)])
+def test_g64_codes_reconstruct_on_their_own_half_grid(is_v, bits):
+    """Every element lies within half a step of z + s*code on the grid of the half it belongs to (keys: the
+    token's half, values: the channel's half), up to the fp16 rounding of the grid's ends; the other half's
+    grid misses some elements by far more."""
+    x = fp16_block(91 + bits, outliers=4, mult=20.0)
+    f = o.quantize_tile(x, is_v, bits=bits, group=64)
+    n = o.normalized(o.rotate(x.astype(np.float64)), f["rho"], f["gamma"])
+    levels = (1 << bits) - 1
+
+    def worst(scale, zero):
+        g = {"scale": scale, "zero": zero}
+        s, z = [a.astype(np.float64) for a in o.group_params(g, is_v)]
+        err = np.abs(n - (z + s * f["codes"]))
+        slack = 2.0 ** -10 * np.maximum(np.abs(z), np.abs(z + levels * s)) + 1e-6
+        return float((err / (s / 2 + slack)).max())
+
+    assert worst(f["scale"], f["zero"]) <= 1.0
+    assert worst(f["scale"][::-1], f["zero"][::-1]) > 2.0
+
+
+def test_g64_equals_g128_when_the_halves_repeat():
+    """Tokens 64..127 repeating tokens 0..63 and channels 64..127 empty make both halves of every group hold
+    the same normalised values (H maps [a, 0] to [H64 a, H64 a] / sqrt 2), so the half groups carry the
+    whole groups' scale, zero and codes."""
+    r = rng(95)
+    x = np.zeros((128, 128))
+    x[:64, :64] = r.standard_normal((64, 64)) * np.where(r.random(64) < 0.1, 15.0, 1.0)[None, :]
+    x[64:, :64] = x[:64, :64]
+    x = x.astype(np.float16)
+    for is_v, bits in ((False, 4), (True, 2), (False, 8), (True, 4)):
+        f128 = o.quantize_tile(x, is_v, bits=bits)
+        f64 = o.quantize_tile(x, is_v, bits=bits, group=64)
+        assert np.array_equal(f64["codes"], f128["codes"])
+        for key in ("scale", "zero"):
+            assert np.array_equal(f64[key][0], f128[key]) and np.array_equal(f64[key][1], f128[key])
+
+
+def test_g64_page_layout_half_major():
+    sc = np.arange(256, dtype=np.float16).reshape(2, 128)
+    f = {"codes": np.zeros((128, 128), np.uint8), "scale": sc, "zero": -sc,
+         "rho": np.full(128, 0.5, np.float32), "gamma": np.full(128, -1.0, np.float32)}
+    for is_v, bits, base in ((False, 4, 8192), (True, 2, 4096), (False, 8, 16384), (True, 4, 8192)):
+        pg = o.encode_page(f, is_v, bits)
+        assert len(pg) == o.page_bytes(bits, 64)
+        a = np.frombuffer(pg, np.uint8)
+        # entry 128*h + j: scale of half 1, index 2 is 130.0 at byte 2 * 130
+        assert np.frombuffer(a[base + 260:base + 262].tobytes(), "<f2")[0] == 130.0
+        assert np.frombuffer(a[base + 512 + 260:base + 512 + 262].tobytes(), "<f2")[0] == -130.0
+        assert a[base + 1024:base + 1028].tolist() == [0, 0, 0, 0x3F]
+        assert a[base + 1536:base + 1540].tolist() == [0, 0, 0x80, 0xBF]
+        g = o.decode_page(pg, is_v)
+        for key in f:
+            assert np.array_equal(np.asarray(f[key]), np.asarray(g[key]))
+
+
+def test_g64_reconstruction_error_below_g128():
+    x = fp16_block(97, outliers=4, mult=20.0)
+    xd = x.astype(np.float64)
+    for is_v in (False, True):
+        e128 = np.linalg.norm(o.dequantize_tile(o.quantize_tile(x, is_v), is_v) - xd)
+        e64 = np.linalg.norm(o.dequantize_tile(o.quantize_tile(x, is_v, group=64), is_v) - xd)
+        assert e64 < e128
