@@ -11,10 +11,10 @@
 
 namespace kvarn {
 hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
-                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, uint32_t* flags,
-                           hipStream_t stream);
+                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, int group,
+                           uint32_t* flags, hipStream_t stream);
 hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
-                             int n_blocks, int hkv, int kbits, int vbits, float* k_out, float* v_out,
+                             int n_blocks, int hkv, int kbits, int vbits, int group, float* k_out, float* v_out,
                              uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
@@ -34,7 +34,6 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
 
 namespace {
 
-constexpr int kMetaBytes = 1536;
 constexpr int kMaxGroup = 8;
 constexpr int kPartFloats = 128 + 2;
 constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
@@ -48,23 +47,25 @@ kvarn_status fail(kvarn_status s, const char* msg) {
   return s;
 }
 
-// kvarn_k{4,8}v{2,4}_g128 with head_dim 128 and 128-token blocks
+// kvarn_k{4,8}v{2,4}_g{128,64} with head_dim 128 and 128-token blocks
 bool config_ok(const kvarn_config* c) {
   return c && c->head_dim == 128 && c->block_tokens == 128 && (c->k_bits == 4 || c->k_bits == 8) &&
-         (c->v_bits == 2 || c->v_bits == 4) && c->group_size == 128 && c->norm_iters == 4 &&
-         std::fabs(c->eps - 1e-6f) <= 1e-12f;
+         (c->v_bits == 2 || c->v_bits == 4) && (c->group_size == 128 || c->group_size == 64) &&
+         c->norm_iters == 4 && std::fabs(c->eps - 1e-6f) <= 1e-12f;
 }
-
-// the format the post names, which the matrix-core decode kernel is written for
 
 kvarn_status check_config(const kvarn_config* c) {
   if (!c) return fail(KVARN_ERR_NULL, "config is NULL");
   if (!config_ok(c))
-    return fail(KVARN_ERR_UNSUPPORTED, "supported formats: kvarn_k{4,8}v{2,4}_g128 (head_dim 128, block 128)");
+    return fail(KVARN_ERR_UNSUPPORTED, "supported formats: kvarn_k{4,8}v{2,4}_g{128,64} (head_dim 128, block 128)");
   return KVARN_OK;
 }
 
-size_t page_bytes_of(int bits) { return static_cast<size_t>(128) * 128 * bits / 8 + kMetaBytes; }
+// codes plus scale and zero fp16 per group (two groups per channel or token for group size 64), rho and
+// gamma fp32[128]
+size_t page_bytes_of(int bits, int group) {
+  return static_cast<size_t>(128) * 128 * bits / 8 + (group == 64 ? 2048 : 1536);
+}
 
 struct DecodePlan {
   int blocks_per_split;
@@ -140,6 +141,8 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
   if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  if (kind != DecodeKind::fp16 && cfg->group_size != 128)
+    return fail(KVARN_ERR_UNSUPPORTED, "decode over group-size-64 pages is not built");
   const bool tail = kind == DecodeKind::packed_tail;
   if (tail) {
     if (!k_tail || !v_tail) return fail(KVARN_ERR_NULL, "k_tail or v_tail is NULL");
@@ -180,13 +183,13 @@ kvarn_status kvarn_config_parse(const char* name, kvarn_config* out) {
   out->group_size = gs;
   out->norm_iters = 4;
   out->eps = 1e-6f;
-  if (!config_ok(out)) return fail(KVARN_ERR_UNSUPPORTED, "implemented formats: kvarn_k{4,8}v{2,4}_g128");
+  if (!config_ok(out)) return fail(KVARN_ERR_UNSUPPORTED, "implemented formats: kvarn_k{4,8}v{2,4}_g{128,64}");
   return KVARN_OK;
 }
 
 size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v) {
   if (!config_ok(cfg)) return 0;
-  return page_bytes_of(is_v ? cfg->v_bits : cfg->k_bits);
+  return page_bytes_of(is_v ? cfg->v_bits : cfg->k_bits, cfg->group_size);
 }
 
 kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
@@ -204,7 +207,8 @@ kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
   return launch_status(kvarn::launch_quantize(k, v, n_blocks, num_kv_heads, dst_pages, k_pool, v_pool, num_pages,
-                                              cfg->k_bits, cfg->v_bits, dev_flags, static_cast<hipStream_t>(stream)));
+                                              cfg->k_bits, cfg->v_bits, cfg->group_size, dev_flags,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool, const void* v_pool,
@@ -218,7 +222,8 @@ kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool
   if (!pages || (k_out && !k_pool) || (v_out && !v_pool)) return fail(KVARN_ERR_NULL, "a tensor pointer is NULL");
   if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
   return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, cfg->k_bits,
-                                                cfg->v_bits, k_out, v_out, dev_flags, static_cast<hipStream_t>(stream)));
+                                                cfg->v_bits, cfg->group_size, k_out, v_out, dev_flags,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
@@ -271,6 +276,7 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
                                      float softmax_scale, float* out, uint32_t* dev_flags, void* stream) {
   kvarn_status s = check_config(cfg);
   if (s != KVARN_OK) return s;
+  if (cfg->group_size != 128) return fail(KVARN_ERR_UNSUPPORTED, "prefill over group-size-64 pages is not built");
   if (batch < 0 || max_q < 0 || max_new < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
       num_pages < 0)
     return fail(KVARN_ERR_SHAPE, "negative or zero size");

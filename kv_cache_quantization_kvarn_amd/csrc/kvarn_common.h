@@ -24,8 +24,22 @@ constexpr float kNormEps = 1e-6f;
 constexpr float kInvSqrt128 = 0.08838834764831845f;  // 2^-3.5, the orthonormal Hadamard scale
 constexpr int kMaxGroup = 8;                           // query heads per KV head handled by one decode wave
 
-// Offsets inside a page's metadata block.
+// Offsets inside a page's metadata block (group size 128).
 constexpr int kMetaScale = 0, kMetaZero = 256, kMetaRho = 512, kMetaGamma = 1024;
+
+// Metadata block of a page with groups of kGroup elements: scale fp16[n], zero fp16[n], rho fp32[128
+// tokens], gamma fp32[128 channels], with n = 128 groups for group size 128 and 2 x 128 for group
+// size 64 (half-major: entry 128*h + j is the group over elements 64h .. 64h+63 of channel / token j).
+template <int kGroup>
+struct MetaLayout {
+  static_assert(kGroup == 128 || kGroup == 64, "group size");
+  static constexpr int kHalves = kBlockTokens / kGroup;
+  static constexpr int kScale = 0;
+  static constexpr int kZero = 2 * 128 * kHalves;
+  static constexpr int kRho = 2 * kZero;
+  static constexpr int kGamma = kRho + 4 * 128;
+  static constexpr int kBytes = kGamma + 4 * 128;
+};
 
 constexpr uint32_t kFlagBadPage = 1u;
 constexpr uint32_t kFlagBadSeqLen = 2u;

@@ -135,7 +135,7 @@ struct QuantLds {
   float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
   float rfl[kBlockTokens], rfl2[kBlockTokens];  // 2^-rho / sqrt(128) and its square, token order
   float cfl[kHeadDim], cfl2[kHeadDim];          // 2^-gamma and its square, chan_slot order
-  float mul_a[kHeadDim], mul_b[kHeadDim];     // rounding FMA of each group
+  float mul_a[2][kHeadDim], mul_b[2][kHeadDim];  // rounding FMA of each group (by half for group size 64)
   float mul_c[kHeadDim];                      // column means for the centred fallback
   float mul_r[kBlockTokens];                  // row means for the centred fallback
   int recenter[2];                            // column-pass fallback flag, by parity
@@ -191,13 +191,15 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[2][4], const f16x8 (&hb
 // All tiles of one kind (keys or values) owned by this workgroup: tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ...  The next tile's input is loaded while the current one is
 // normalised and packed.
-template <bool kIsV, int kBits>
+template <bool kIsV, int kBits, int kGroup>
 __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, int hkv, int tiles,
                                                const int32_t* __restrict__ dst_pages, uint8_t* __restrict__ pool,
                                                int num_pages, uint32_t* __restrict__ flags, QuantLds& s) {
   static_assert(kIsV ? (kBits == 2 || kBits == 4) : (kBits == 4 || kBits == 8), "code width");
+  using Meta = MetaLayout<kGroup>;
+  constexpr bool kHalf = kGroup == 64;  // two groups per channel (keys) or token (values)
   constexpr int kCodeBytes = kBlockTokens * kHeadDim * kBits / 8;
-  constexpr int kPageBytes = kCodeBytes + kMetaBytes;
+  constexpr int kPageBytes = kCodeBytes + Meta::kBytes;
   constexpr float kLevels = static_cast<float>((1 << kBits) - 1);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   // Reducer role of this thread: row t_red (row passes) / channel c_red (column passes) = t_red;
@@ -386,7 +388,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 
     // normalisers: rho of row t_red from one thread of the pair, gamma of column t_red from the other
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hf ? gam_c : rho_t), dst,
-                                          kCodeBytes + (hf ? kMetaGamma : kMetaRho) + 4 * t_red, 0, 0);
+                                          kCodeBytes + (hf ? Meta::kGamma : Meta::kRho) + 4 * t_red, 0, 0);
 
     // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
     // M = R' times the normaliser across the group axis; N = M times the group's own
@@ -420,26 +422,41 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           mn = fminf(mn, fminf(v.x, v.z));
           mx = fmaxf(mx, fmaxf(v.y, v.w));
         }
-        mn = mul_rn(fminf(mn, dpp_xor1(mn)), cf_c);
-        mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), cf_c);
+        // thread hf of the pair holds the partials of token half hf (waves 2hf, 2hf + 1): one group of
+        // each half for group size 64, merged into the channel's one group otherwise
+        if constexpr (!kHalf) {
+          mn = fminf(mn, dpp_xor1(mn));
+          mx = fmaxf(mx, dpp_xor1(mx));
+        }
+        mn = mul_rn(mn, cf_c);
+        mx = mul_rn(mx, cf_c);
         const uint32_t sb = float_to_half_bits((mx - mn) / kLevels);
         const uint32_t zb = float_to_half_bits(mn);
         const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
         const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-        // scale from one thread of the pair, zero from the other
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
-                                              kCodeBytes + (hf ? kMetaZero : kMetaScale) + 2 * t_red, 0, 0);
-        if (hf == 0) {
-          s.mul_a[chan_slot(t_red)] = cf_c * inv;
+        if constexpr (kHalf) {
+          const int gi = 128 * hf + t_red;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(sb), dst, kCodeBytes + Meta::kScale + 2 * gi, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(zb), dst, kCodeBytes + Meta::kZero + 2 * gi, 0, 0);
+          s.mul_a[hf][chan_slot(t_red)] = cf_c * inv;
+          s.mul_b[hf][chan_slot(t_red)] = -zf * inv;
         } else {
-          s.mul_b[chan_slot(t_red)] = -zf * inv;
+          // scale from one thread of the pair, zero from the other
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
+                                                kCodeBytes + (hf ? Meta::kZero : Meta::kScale) + 2 * t_red, 0, 0);
+          if (hf == 0) {
+            s.mul_a[0][chan_slot(t_red)] = cf_c * inv;
+          } else {
+            s.mul_b[0][chan_slot(t_red)] = -zf * inv;
+          }
         }
       }
       __syncthreads();
-      const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[8 * n]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[8 * n + 4]);
-      const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[8 * n]);
-      const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[8 * n + 4]);
+      const int kh = kHalf ? (w >> 1) : 0;  // the groups of this wave's tokens
+      const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[kh][8 * n]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[kh][8 * n + 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[kh][8 * n]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[kh][8 * n + 4]);
       const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       auto kcode = [&](int i, int c) {
@@ -488,50 +505,91 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int c = 0; c < 8; ++c) R[i][c] *= cf[c];
+      // the lane's channels c = 0..3 lie in channels 0..63, c = 4..7 in 64..127 (chan_of)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float a = R[i][0], b = R[i][0];
 #pragma unroll
-        for (int c = 1; c < 8; ++c) {
+        for (int c = 1; c < 4; ++c) {
           a = fminf(a, R[i][c]);
           b = fmaxf(b, R[i][c]);
         }
-        *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+        if constexpr (kHalf) {
+          float a1 = R[i][4], b1 = R[i][4];
+#pragma unroll
+          for (int c = 5; c < 8; ++c) {
+            a1 = fminf(a1, R[i][c]);
+            b1 = fmaxf(b1, R[i][c]);
+          }
+          // channel half 0 in the channel array, half 1 in the (now idle) row array
+          *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+          *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(a1, b1);
+        } else {
+#pragma unroll
+          for (int c = 4; c < 8; ++c) {
+            a = fminf(a, R[i][c]);
+            b = fmaxf(b, R[i][c]);
+          }
+          *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+        }
       }
       __syncthreads();
       {
-        const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
         float mn = INFINITY, mx = -INFINITY;
+        if constexpr (kHalf) {
+          // thread hf of the pair reduces channel half hf of token t_red: all 16 lanes' partials
+          const float4* p = reinterpret_cast<const float4*>(hf ? s.part_row[t_red] : s.part[t_red]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float4 v = p[k];
-          mn = fminf(mn, fminf(v.x, v.z));
-          mx = fmaxf(mx, fmaxf(v.y, v.w));
+          for (int k = 0; k < 8; ++k) {
+            const float4 v = p[k];
+            mn = fminf(mn, fminf(v.x, v.z));
+            mx = fmaxf(mx, fmaxf(v.y, v.w));
+          }
+        } else {
+          const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float4 v = p[k];
+            mn = fminf(mn, fminf(v.x, v.z));
+            mx = fmaxf(mx, fmaxf(v.y, v.w));
+          }
+          mn = fminf(mn, dpp_xor1(mn));
+          mx = fmaxf(mx, dpp_xor1(mx));
         }
-        mn = mul_rn(fminf(mn, dpp_xor1(mn)), rf_t);
-        mx = mul_rn(fmaxf(mx, dpp_xor1(mx)), rf_t);
+        mn = mul_rn(mn, rf_t);
+        mx = mul_rn(mx, rf_t);
         const uint32_t sb = float_to_half_bits((mx - mn) / kLevels);
         const uint32_t zb = float_to_half_bits(mn);
         const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
         const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
-                                              kCodeBytes + (hf ? kMetaZero : kMetaScale) + 2 * t_red, 0, 0);
-        if (hf == 0) {
-          s.mul_a[t_red] = rf_t * inv;
+        if constexpr (kHalf) {
+          const int gi = 128 * hf + t_red;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(sb), dst, kCodeBytes + Meta::kScale + 2 * gi, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(zb), dst, kCodeBytes + Meta::kZero + 2 * gi, 0, 0);
+          s.mul_a[hf][t_red] = rf_t * inv;
+          s.mul_b[hf][t_red] = -zf * inv;
         } else {
-          s.mul_b[t_red] = -zf * inv;
+          __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
+                                                kCodeBytes + (hf ? Meta::kZero : Meta::kScale) + 2 * t_red, 0, 0);
+          if (hf == 0) {
+            s.mul_a[0][t_red] = rf_t * inv;
+          } else {
+            s.mul_b[0][t_red] = -zf * inv;
+          }
         }
       }
       __syncthreads();
       float qa[8], qb[8];
-      {
-        const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[32 * w + 4 * g]);
-        const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[32 * w + 16 + 4 * g]);
-        const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[32 * w + 4 * g]);
-        const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[32 * w + 16 + 4 * g]);
+      // rounding factors of the lane's 8 tokens for channel half vh (the only half for group size 128)
+      auto load_q = [&](int vh) {
+        const float4 a0 = *reinterpret_cast<const float4*>(&s.mul_a[vh][32 * w + 4 * g]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&s.mul_a[vh][32 * w + 16 + 4 * g]);
+        const float4 b0 = *reinterpret_cast<const float4*>(&s.mul_b[vh][32 * w + 4 * g]);
+        const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[vh][32 * w + 16 + 4 * g]);
         qa[0] = a0.x; qa[1] = a0.y; qa[2] = a0.z; qa[3] = a0.w; qa[4] = a1.x; qa[5] = a1.y; qa[6] = a1.z; qa[7] = a1.w;
         qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
-      }
+      };
+      load_q(0);
       auto vcode = [&](int i, int c) {
         return __float_as_uint(fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels) + kRoundMagic);
       };
@@ -541,6 +599,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         // of unit u: bytes 8w + 4ih .. +3 of that channel.
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          if (kHalf && u == 2) load_q(1);  // channels c = 4..7 from here on
           uint32_t by[4];
 #pragma unroll
           for (int y = 0; y < 4; ++y) {
@@ -565,6 +624,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         const bool odd = g & 1;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
+          if (kHalf && c == 4) load_q(1);  // channels c = 4..7 from here on
           uint32_t hw[2];
 #pragma unroll
           for (int ih = 0; ih < 2; ++ih) {
@@ -595,22 +655,22 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 // Persistent quantiser: every workgroup walks the key tiles blockIdx.x, blockIdx.x + gridDim.x, ...
 // and then the value tiles with the same stride, so all workgroups carry the same mix of the two
 // kinds (a value tile costs more than a key tile).
-template <int kKBits, int kVBits>
+template <int kKBits, int kVBits, int kGroup>
 __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin, int hkv, int tiles,
                                                          const int32_t* __restrict__ dst_pages,
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
   __shared__ __align__(16) QuantLds lds;
-  quantize_tiles<false, kKBits>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
-  quantize_tiles<true, kVBits>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
+  quantize_tiles<false, kKBits, kGroup>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
+  quantize_tiles<true, kVBits, kGroup>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
 }
 
 // Test / inspection export: rebuild fp32 K^ or V^ of one tile in the original basis.
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restrict__ k_pool,
                                                          const uint8_t* __restrict__ v_pool, int num_pages,
                                                          const int32_t* __restrict__ pages, int hkv, int kbits,
-                                                         int vbits, float* __restrict__ k_out,
+                                                         int vbits, int group, float* __restrict__ k_out,
                                                          float* __restrict__ v_out, uint32_t* __restrict__ flags) {
   __shared__ float buf[kBlockTokens][kHeadDim + 1];
   const int tile = blockIdx.x;
@@ -626,24 +686,28 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
     return;
   }
   const int code_bytes = kBlockTokens * kHeadDim * (is_v ? vbits : kbits) / 8;
-  const uint8_t* pb = (is_v ? v_pool : k_pool) + (static_cast<size_t>(page) * hkv + head) * (code_bytes + kMetaBytes);
+  const bool half = group == 64;
+  const int meta_bytes = half ? MetaLayout<64>::kBytes : MetaLayout<128>::kBytes;
+  const uint8_t* pb = (is_v ? v_pool : k_pool) + (static_cast<size_t>(page) * hkv + head) * (code_bytes + meta_bytes);
   const uint8_t* meta = pb + code_bytes;
-  const uint16_t* sc = reinterpret_cast<const uint16_t*>(meta + kMetaScale);
-  const uint16_t* zr = reinterpret_cast<const uint16_t*>(meta + kMetaZero);
-  const float* rho = reinterpret_cast<const float*>(meta + kMetaRho);
-  const float* gam = reinterpret_cast<const float*>(meta + kMetaGamma);
+  const uint16_t* sc = reinterpret_cast<const uint16_t*>(meta + (half ? MetaLayout<64>::kScale : MetaLayout<128>::kScale));
+  const uint16_t* zr = reinterpret_cast<const uint16_t*>(meta + (half ? MetaLayout<64>::kZero : MetaLayout<128>::kZero));
+  const float* rho = reinterpret_cast<const float*>(meta + (half ? MetaLayout<64>::kRho : MetaLayout<128>::kRho));
+  const float* gam = reinterpret_cast<const float*>(meta + (half ? MetaLayout<64>::kGamma : MetaLayout<128>::kGamma));
   for (int e = threadIdx.x; e < kBlockTokens * kHeadDim; e += blockDim.x) {
     const int t = e >> 7, j = e & 127;
     uint32_t code;
     float s, z;
     if (is_v) {
       code = vbits == 4 ? (pb[64 * j + (t >> 1)] >> (4 * (t & 1))) & 15u : (pb[32 * j + (t >> 2)] >> (2 * (t & 3))) & 3u;
-      s = half_bits_to_float(sc[t]);
-      z = half_bits_to_float(zr[t]);
+      const int gi = (half ? 128 * (j >> 6) : 0) + t;  // value group: token t, channel half
+      s = half_bits_to_float(sc[gi]);
+      z = half_bits_to_float(zr[gi]);
     } else {
       code = kbits == 8 ? pb[128 * t + j] : (pb[64 * t + (j >> 1)] >> (4 * (j & 1))) & 15u;
-      s = half_bits_to_float(sc[j]);
-      z = half_bits_to_float(zr[j]);
+      const int gi = (half ? 128 * (t >> 6) : 0) + j;  // key group: channel j, token half
+      s = half_bits_to_float(sc[gi]);
+      z = half_bits_to_float(zr[gi]);
     }
     buf[t][j] = fmaf(s, static_cast<float>(code), z) * exp2f(rho[t] + gam[j]);
   }
@@ -671,8 +735,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 namespace kvarn {
 
 hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, const int32_t* dst_pages,
-                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, uint32_t* flags,
-                           hipStream_t stream) {
+                           void* k_pool, void* v_pool, int num_pages, int kbits, int vbits, int group,
+                           uint32_t* flags, hipStream_t stream) {
   const int tiles = n_blocks * hkv;  // per kind
   if (tiles == 0) return hipSuccess;
   // two persistent workgroups per compute unit
@@ -682,8 +746,11 @@ hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, 
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e != hipSuccess) return e;
   const int groups = tiles < 2 * cus ? tiles : 2 * cus;
-  auto kernel = kbits == 8 ? (vbits == 4 ? quantize_kernel<8, 4> : quantize_kernel<8, 2>)
-                           : (vbits == 4 ? quantize_kernel<4, 4> : quantize_kernel<4, 2>);
+  auto kernel = group == 64
+                    ? (kbits == 8 ? (vbits == 4 ? quantize_kernel<8, 4, 64> : quantize_kernel<8, 2, 64>)
+                                  : (vbits == 4 ? quantize_kernel<4, 4, 64> : quantize_kernel<4, 2, 64>))
+                    : (kbits == 8 ? (vbits == 4 ? quantize_kernel<8, 4, 128> : quantize_kernel<8, 2, 128>)
+                                  : (vbits == 4 ? quantize_kernel<4, 4, 128> : quantize_kernel<4, 2, 128>));
   hipLaunchKernelGGL(kernel, dim3(groups), dim3(256), 0, stream, static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), hkv, tiles, dst_pages, static_cast<uint8_t*>(k_pool),
                      static_cast<uint8_t*>(v_pool), num_pages, flags);
@@ -691,11 +758,12 @@ hipError_t launch_quantize(const void* k, const void* v, int n_blocks, int hkv, 
 }
 
 hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
-                             int n_blocks, int hkv, int kbits, int vbits, float* k_out, float* v_out,
+                             int n_blocks, int hkv, int kbits, int vbits, int group, float* k_out, float* v_out,
                              uint32_t* flags, hipStream_t stream) {
   const unsigned tiles = 2u * static_cast<unsigned>(n_blocks) * static_cast<unsigned>(hkv);
   hipLaunchKernelGGL(dequantize_kernel, dim3(tiles), dim3(256), 0, stream, static_cast<const uint8_t*>(k_pool),
-                     static_cast<const uint8_t*>(v_pool), num_pages, pages, hkv, kbits, vbits, k_out, v_out, flags);
+                     static_cast<const uint8_t*>(v_pool), num_pages, pages, hkv, kbits, vbits, group, k_out, v_out,
+                     flags);
   return hipGetLastError();
 }
 

@@ -33,11 +33,12 @@ def test_config_parse():
     assert (cfg.head_dim, cfg.block_tokens, cfg.k_bits, cfg.v_bits, cfg.group_size, cfg.norm_iters) == \
         (128, 128, 4, 2, 128, 4)
     assert abs(cfg.eps - 1e-6) < 1e-12
-    for kb, vb in ((4, 4), (8, 2), (8, 4)):
-        c = K.kvarn_config_parse("kvarn_k%dv%d_g128" % (kb, vb))
-        assert (c.k_bits, c.v_bits, c.group_size) == (kb, vb, 128)
-    for bad in ("kvarn_k8v4_g64", "kvarn_k4v2_g128x", "fp8", "kvarn_k4v2", "kvarn_k2v2_g128", "kvarn_k4v8_g128",
-                "kvarn_k16v4_g128"):
+    for kb, vb in ((4, 2), (4, 4), (8, 2), (8, 4)):
+        for gs in (128, 64):
+            c = K.kvarn_config_parse("kvarn_k%dv%d_g%d" % (kb, vb, gs))
+            assert (c.k_bits, c.v_bits, c.group_size) == (kb, vb, gs)
+    for bad in ("kvarn_k8v4_g32", "kvarn_k4v2_g256", "kvarn_k4v2_g128x", "fp8", "kvarn_k4v2", "kvarn_k2v2_g128",
+                "kvarn_k4v8_g128", "kvarn_k16v4_g128"):
         with pytest.raises(K.KvarnError) as e:
             K.kvarn_config_parse(bad)
         assert e.value.status == K.KVARN_ERR_UNSUPPORTED
@@ -51,9 +52,12 @@ def test_page_bytes_match_the_oracle_format():
     assert K.kvarn_page_bytes(cfg, False) == o.K_PAGE_BYTES == 9728
     assert K.kvarn_page_bytes(cfg, True) == o.V_PAGE_BYTES == 5632
     for kb, vb in ((4, 2), (4, 4), (8, 2), (8, 4)):
-        c = K.kvarn_config_parse("kvarn_k%dv%d_g128" % (kb, vb))
-        assert K.kvarn_page_bytes(c, False) == o.page_bytes(kb) and K.kvarn_page_bytes(c, True) == o.page_bytes(vb)
+        for gs in (128, 64):
+            c = K.kvarn_config_parse("kvarn_k%dv%d_g%d" % (kb, vb, gs))
+            assert K.kvarn_page_bytes(c, False) == o.page_bytes(kb, gs)
+            assert K.kvarn_page_bytes(c, True) == o.page_bytes(vb, gs)
     assert (o.page_bytes(8), o.page_bytes(4)) == (17920, 9728)
+    assert (o.page_bytes(4, 64), o.page_bytes(2, 64)) == (10240, 6144)
     bad = K.kvarn_config()
     assert K.kvarn_page_bytes(bad, False) == 0
 

@@ -1,0 +1,98 @@
+"""GPU parity of group size 64 (kvarn_k{4,8}v{2,4}_g64) against the oracle.
+
+Reading: each group of the group-128 format splits into two halves of 64 consecutive elements (keys: one
+channel over tokens 64h .. 64h+63; values: one token over channels 64h .. 64h+63) with their own fp16
+scale and zero, stored half-major.  Bars as for group 128: codes within one level (mismatch fraction
+<= 1e-4), scale / zero within one fp16 ulp, normalisers 2e-5, dequantised values max-abs 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_kvarn_amd import synth
+from oracle import kvarn_oracle as o
+import kvarn_check as chk
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["kvarn_k4v2_g64", "kvarn_k4v4_g64", "kvarn_k8v2_g64", "kvarn_k8v4_g64"]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kv_cache_quantization_kvarn_amd import kvarn
+    return kvarn
+
+
+def quantize(K, cfg, k, v, pages, num_pages, poison):
+    kp, vp = K.alloc_pools(cfg, num_pages, k.shape[1])
+    kp.fill_(poison)
+    vp.fill_(poison)
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_quantize_blocks(cfg, k, v, pages.to("cuda", torch.int32), kp, vp, fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    return kp, vp
+
+
+@pytest.mark.parametrize("name", FORMATS)
+def test_quantize_dequantize_every_tile_g64(K, name):
+    cfg = K.kvarn_config_parse(name)
+    w = synth.WORKLOADS["tiny_1x1024"]
+    say("case: %s quantise + dequantise, %s, every tile, every page byte" % (name, w.name))
+    pm = synth.make_page_map(w)
+    k, v = synth.layer_kv(w, 0, 1024, "cuda")
+    kp, vp = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0xA5)
+    kp2, vp2 = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0x5A)
+    assert torch.equal(kp, kp2) and torch.equal(vp, vp2)  # every byte written, deterministically
+    assert kp.shape[2] == o.page_bytes(cfg.k_bits, 64) and vp.shape[2] == o.page_bytes(cfg.v_bits, 64)
+    stats = chk.TileStats()
+    kh, vh, kph, vph = k.cpu().numpy(), v.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy()
+    for blk in range(8):
+        p = int(pm.prefix_pages[blk])
+        for h in range(w.hkv):
+            sl = slice(128 * blk, 128 * blk + 128)
+            chk.compare_tile(stats, kh[sl, h], kph[p, h].tobytes(), False)
+            chk.compare_tile(stats, vh[sl, h], vph[p, h].tobytes(), True)
+    say("  " + stats.summary())
+    stats.check()
+    assert stats.groups == 8 * w.hkv * 2 * 256  # two halves of 128 groups per page, K and V
+    ko = torch.empty(1024, w.hkv, 128, dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    K.kvarn_dequantize_blocks(cfg, kp, vp, pm.prefix_pages.cuda(), ko, vo)
+    torch.cuda.synchronize()
+    koh, voh = ko.cpu().numpy(), vo.cpu().numpy()
+    worst = 0.0
+    for blk in range(8):
+        p = int(pm.prefix_pages[blk])
+        for h in range(w.hkv):
+            for pool, outh, is_v in ((kph, koh, False), (vph, voh, True)):
+                ref = o.dequantize_tile(o.decode_page(pool[p, h].tobytes(), is_v), is_v)
+                worst = max(worst, float(np.abs(outh[128 * blk:128 * blk + 128, h] - ref).max()))
+    say("  dequantised max-abs diff %.3e" % worst)
+    assert worst <= chk.DEQUANT_TOL
+
+
+def test_llama3_layer_g64_sampled_tiles(K):
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g64")
+    w = synth.WORKLOADS["llama3_8b_layer_16x8192"]
+    say("case: kvarn_k4v2_g64, %s full size, sampled tiles" % w.name)
+    pm = synth.make_page_map(w)
+    n = synth.total_prefix_blocks(w)
+    k, v = synth.layer_kv(w, 0, n * 128, "cuda")
+    kp, vp = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0)
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    stats = chk.TileStats()
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    for blk, h in ((0, 0), (511, 3), (1023, 7)):
+        p = int(pm.prefix_pages[blk])
+        sl = slice(128 * blk, 128 * blk + 128)
+        chk.compare_tile(stats, kh[sl, h], kph[p, h].tobytes(), False)
+        chk.compare_tile(stats, vh[sl, h], vph[p, h].tobytes(), True)
+    say("  " + stats.summary())
+    stats.check()
