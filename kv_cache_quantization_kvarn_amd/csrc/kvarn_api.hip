@@ -18,9 +18,9 @@ hipError_t launch_dequantize(const void* k_pool, const void* v_pool, int num_pag
                              uint32_t* flags, hipStream_t stream);
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
-                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int blocks_per_split,
-                         int max_splits, float scale_log2, float* out, float* part, uint32_t* counters,
-                         uint32_t* flags, hipStream_t stream);
+                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int group,
+                         int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
+                         uint32_t* counters, uint32_t* flags, hipStream_t stream);
 hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_cache, int num_pages,
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
@@ -141,8 +141,6 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(KVARN_ERR_SHAPE, "q and out must be 16-byte aligned");
   if (max_blocks_per_seq > 0 && num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
-  if (kind != DecodeKind::fp16 && cfg->group_size != 128)
-    return fail(KVARN_ERR_UNSUPPORTED, "decode over group-size-64 pages is not built");
   const bool tail = kind == DecodeKind::packed_tail;
   if (tail) {
     if (!k_tail || !v_tail) return fail(KVARN_ERR_NULL, "k_tail or v_tail is NULL");
@@ -163,8 +161,9 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
                                                    scale_log2, out, part, counters, dev_flags, st));
   return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                             tail ? k_tail : nullptr, tail ? v_tail : nullptr, batch, num_q_heads,
-                                            num_kv_heads, cfg->k_bits, cfg->v_bits, p.blocks_per_split, p.max_splits,
-                                            scale_log2, out, part, counters, dev_flags, st));
+                                            num_kv_heads, cfg->k_bits, cfg->v_bits, cfg->group_size,
+                                            p.blocks_per_split, p.max_splits, scale_log2, out, part, counters,
+                                            dev_flags, st));
 }
 
 }  // namespace

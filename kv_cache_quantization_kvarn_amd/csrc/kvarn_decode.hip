@@ -264,29 +264,35 @@ __device__ __forceinline__ void wave_fwht(float& x0, float& x1, int lane) {
 
 __device__ __forceinline__ float wave_sum_all(float x) { return sum_xor32(sum_xor16(row16_sum(x))); }
 
+// Per-wave page state in shared memory; NH = groups per channel (keys) or token (values): 1 for group
+// size 128, 2 for group size 64 (index = the half of the block's tokens / channels).
+template <int NH>
 struct __align__(16) WaveLds {
-  uint32_t coef[16][kCoefStride];  // key-side B operand: [column][slot] packed fp16 pairs
-  float pk[kHeadDim];              // 2^rho (K) / key page scale, per token
-  float fv[kHeadDim];              // 2^rho s (V) * value page scale, per token
-  float zv[kHeadDim];              // 2^rho z (V), per token
-  float gs[kHeadDim];              // 2^gamma (V) / value page scale, per channel
+  uint32_t coef[NH][16][kCoefStride];  // key-side B operand per token half: [column][slot] packed fp16 pairs
+  float pk[kHeadDim];                  // 2^rho (K) / key page scale, per token
+  float fv[NH][kHeadDim];              // 2^rho s (V) * value page scale, per channel half and token
+  float zv[NH][kHeadDim];              // 2^rho z (V), per channel half and token
+  float gs[kHeadDim];                  // 2^gamma (V) / value page scale, per channel
 };
 
-// Page geometry of one pair of code widths (4- or 8-bit keys, 2- or 4-bit values).
-template <int KB, int VB>
+// Page geometry of one pair of code widths (4- or 8-bit keys, 2- or 4-bit values) and group size.
+template <int KB, int VB, int GS>
 struct DecFormat {
+  using Meta = MetaLayout<GS>;
+  static constexpr int kHalves = Meta::kHalves;
   static constexpr int kKRow = kHeadDim * KB / 8;       // bytes of one token's key codes
   static constexpr int kVRow = kBlockTokens * VB / 8;   // bytes of one channel's value codes
   static constexpr int kKCode = kBlockTokens * kKRow;
   static constexpr int kVCode = kHeadDim * kVRow;
-  static constexpr int kKPage = kKCode + kMetaBytes;
-  static constexpr int kVPage = kVCode + kMetaBytes;
+  static constexpr int kKPage = kKCode + Meta::kBytes;
+  static constexpr int kVPage = kVCode + Meta::kBytes;
   // second coefficient slot of a lane: channel ch0 + 4 for nibbles (pairs j, j + 4 of a dword),
   // ch0 + 1 for bytes (channel order)
   static constexpr int kCh1 = KB == 8 ? 1 : 4;
-  // resident waves per SIMD: byte-wide keys need more page registers (4-bit keys with 4-bit values
-  // keep three waves at the cost of a two-register spill, which is faster than two waves)
-  static constexpr int kMinWaves = KB == 4 ? 3 : 2;
+  // resident waves per SIMD: byte-wide keys and two groups per channel / token need more registers
+  // (4-bit keys with 4-bit values keep three waves at the cost of a two-register spill, which is
+  // faster than two waves)
+  static constexpr int kMinWaves = KB == 4 && GS == 128 ? 3 : 2;
 };
 
 // Coefficient slots of a lane: channels ch0 and ch0 + kCh1, ch0 = 32*(lane/16) + 8*((lane/4)%4) +
@@ -297,26 +303,28 @@ __device__ __forceinline__ int coef_channel(int lane) {
 }
 
 // One page of one KV head as this lane loads it.
-template <int KB, int VB>
+template <int KB, int VB, int GS>
 struct PageRegs {
+  static constexpr int NH = DecFormat<KB, VB, GS>::kHalves;
   u32x4 kc[8][KB / 4];    // key codes: M-tile mt, row n -> token 32*(n/4) + 4*mt + n%4, channels 32g .. 32g+31
   uint32_t vc[8][VB];     // value codes: M-tile mt, row n -> channel 16mt + n, tokens 32g .. 32g+31
-  uint32_t ks0, ks1;   // key scale (fp16 bits) of channels ch0, ch1
-  uint32_t kz0, kz1;   // key zero
-  float kg0, kg1;      // key gamma
-  float2 kr;           // key rho of tokens 2*lane, 2*lane+1
-  uint32_t vs2, vz2;   // value scale / zero (fp16 pairs) of tokens 2*lane, 2*lane+1
-  float2 vr, vg;       // value rho of those tokens, value gamma of channels 2*lane, 2*lane+1
+  uint32_t ks0[NH], ks1[NH];  // key scale (fp16 bits) of channels ch0, ch1, per token half
+  uint32_t kz0[NH], kz1[NH];  // key zero
+  float kg0, kg1;             // key gamma
+  float2 kr;                  // key rho of tokens 2*lane, 2*lane+1
+  uint32_t vs2[NH], vz2[NH];  // value scale / zero (fp16 pairs) of tokens 2*lane, 2*lane+1, per channel half
+  float2 vr, vg;              // value rho of those tokens, value gamma of channels 2*lane, 2*lane+1
   bool ok;
 };
 
 // Issues every load of one page without a branch: a bad page id reads page 0 instead (the
 // caller guarantees num_pages > 0) and only clears `ok`.
-template <int KB, int VB>
-__device__ __forceinline__ void load_page(PageRegs<KB, VB>& P, int page, int num_pages, int hkv, int kvh,
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void load_page(PageRegs<KB, VB, GS>& P, int page, int num_pages, int hkv, int kvh,
                                           const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
                                           int lane, int n, int g, int ch0) {
-  using F = DecFormat<KB, VB>;
+  using F = DecFormat<KB, VB, GS>;
+  using Meta = typename F::Meta;
   P.ok = page >= 0 && page < num_pages;
   const int safe = P.ok ? page : 0;
   // lane offsets are recomputed for every page (a few integer operations) rather than kept live
@@ -344,20 +352,23 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB>& P, int page, int num
   }
   const uint8_t* km = kp + F::kKCode;
   const uint8_t* vm = vp + F::kVCode;
-  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + kMetaScale);
-  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + kMetaZero);
-  const float* kgm = reinterpret_cast<const float*>(km + kMetaGamma);
-  P.ks0 = ksc[ch0];
-  P.ks1 = ksc[ch0 + F::kCh1];
-  P.kz0 = kzr[ch0];
-  P.kz1 = kzr[ch0 + F::kCh1];
+  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + Meta::kScale);
+  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + Meta::kZero);
+  const float* kgm = reinterpret_cast<const float*>(km + Meta::kGamma);
+#pragma unroll
+  for (int hh = 0; hh < F::kHalves; ++hh) {  // group entry 128*hh + j (half-major)
+    P.ks0[hh] = ksc[128 * hh + ch0];
+    P.ks1[hh] = ksc[128 * hh + ch0 + F::kCh1];
+    P.kz0[hh] = kzr[128 * hh + ch0];
+    P.kz1[hh] = kzr[128 * hh + ch0 + F::kCh1];
+    P.vs2[hh] = reinterpret_cast<const uint32_t*>(vm + Meta::kScale)[64 * hh + lane];
+    P.vz2[hh] = reinterpret_cast<const uint32_t*>(vm + Meta::kZero)[64 * hh + lane];
+  }
   P.kg0 = kgm[ch0];
   P.kg1 = kgm[ch0 + F::kCh1];
-  P.kr = reinterpret_cast<const float2*>(km + kMetaRho)[lane];
-  P.vs2 = reinterpret_cast<const uint32_t*>(vm + kMetaScale)[lane];
-  P.vz2 = reinterpret_cast<const uint32_t*>(vm + kMetaZero)[lane];
-  P.vr = reinterpret_cast<const float2*>(vm + kMetaRho)[lane];
-  P.vg = reinterpret_cast<const float2*>(vm + kMetaGamma)[lane];
+  P.kr = reinterpret_cast<const float2*>(km + Meta::kRho)[lane];
+  P.vr = reinterpret_cast<const float2*>(vm + Meta::kRho)[lane];
+  P.vg = reinterpret_cast<const float2*>(vm + Meta::kGamma)[lane];
 }
 
 // Per-wave state carried across pages.
@@ -373,20 +384,38 @@ struct Mags {
   uint32_t m16, m64, m4, m1024;
 };
 
-template <int KB, int VB>
-__device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveState& S, WaveLds& L, int G, int lane,
-                                             int g, int lo_col, const Mags& M) {
-  // ---- key-side coefficients (this lane: slots ch0 and ch0 + 4, all heads) ---
-  const float s0 = half_bits_to_float(P.ks0), s1 = half_bits_to_float(P.ks1);
-  const float z0 = half_bits_to_float(P.kz0), z1 = half_bits_to_float(P.kz1);
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void process_page(const PageRegs<KB, VB, GS>& P, WaveState& S,
+                                             WaveLds<DecFormat<KB, VB, GS>::kHalves>& L, int G, int lane, int g,
+                                             int lo_col, const Mags& M) {
+  // NH = 2 (group size 64): key groups differ between the token halves, value groups between the
+  // channel halves.  A lane's score rows are tokens of quarter g, i.e. of half g / 2; value M-tiles
+  // 0-3 are channels 0-63 and 4-7 channels 64-127.
+  constexpr int NH = DecFormat<KB, VB, GS>::kHalves;
+  // ---- key-side coefficients (this lane: slots ch0 and ch1, all heads), per token half -----------
   const float eg0 = ex2(P.kg0), eg1 = ex2(P.kg1);
-  const float e0 = eg0 * s0, e1 = eg1 * s1;
-  const float f0 = eg0 * z0, f1 = eg1 * z1;
-  // ---- value-side per-token factors (this lane: tokens 2*lane, 2*lane+1) -----
+  float e0[NH], e1[NH], f0[NH], f1[NH];
+  float emx = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    e0[hh] = eg0 * half_bits_to_float(P.ks0[hh]);
+    e1[hh] = eg1 * half_bits_to_float(P.ks1[hh]);
+    f0[hh] = eg0 * half_bits_to_float(P.kz0[hh]);
+    f1[hh] = eg1 * half_bits_to_float(P.kz1[hh]);
+    emx = fmaxf(emx, fmaxf(e0[hh], e1[hh]));
+  }
+  // ---- value-side per-token factors (this lane: tokens 2*lane, 2*lane+1), per channel half -------
   const float vr0 = ex2(P.vr.x), vr1 = ex2(P.vr.y);
-  const float F0 = vr0 * half_bits_to_float(P.vs2 & 0xFFFFu), F1 = vr1 * half_bits_to_float(P.vs2 >> 16);
-  const float emax = wave_max_all(fmaxf(e0, e1));
-  const float fmaxv = wave_max_all(fmaxf(F0, F1));
+  float F0[NH], F1[NH];
+  float fmx = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    F0[hh] = vr0 * half_bits_to_float(P.vs2[hh] & 0xFFFFu);
+    F1[hh] = vr1 * half_bits_to_float(P.vs2[hh] >> 16);
+    fmx = fmaxf(fmx, fmaxf(F0[hh], F1[hh]));
+  }
+  const float emax = wave_max_all(emx);
+  const float fmaxv = wave_max_all(fmx);
 
   int ex;
   const float prod = S.qmax * emax;
@@ -396,7 +425,6 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveStat
   const float sa = live ? pow2i(14 - ex) : 1.f;  // |a * sa| < 2^14
   // with no positive key scale the coefficients are all zero but b is not: keep the page at unit scale
   const float inv_sa = live ? pow2i(ex - 14) : 1.f;
-  const float e0s = e0 * sa, e1s = e1 * sa;
   // the key offsets of this lane's two slots: 1024 for bytes; for nibbles 64 for nibbles 1 and 5
   // of a dword, else 16
   const _Float16 off = KB == 8 ? static_cast<_Float16>(1024.0f)
@@ -409,22 +437,30 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveStat
     q0[0] = a.x; q0[1] = a.y; q0[2] = a.z; q0[3] = a.w; q0[4] = b.x; q0[5] = b.y; q0[6] = b.z; q0[7] = b.w;
     q1[0] = c.x; q1[1] = c.y; q1[2] = c.z; q1[3] = c.w; q1[4] = d.x; q1[5] = d.y; q1[6] = d.z; q1[7] = d.w;
   }
-  float bp[kMaxGroup];
+  float kinit[NH];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
-      uint32_t hi, lo;
-      split_prod(q0[h], e0s, q1[h], e1s, hi, lo);
-      L.coef[h][lane] = hi;
-      L.coef[8 + h][lane] = lo;
-      // offset contribution of exactly the fp16 coefficients the matrix cores use
-      const float aoff = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo), offp,
-                                                __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi), offp, 0.f, false),
-                                                false);
-      bp[h] = fmaf(-inv_sa, aoff, fmaf(q0[h], f0, q1[h] * f1));
-    } else {
-      bp[h] = 0.f;
+  for (int hh = 0; hh < NH; ++hh) {
+    const float e0s = e0[hh] * sa, e1s = e1[hh] * sa;
+    float bp[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < G) {
+        uint32_t hi, lo;
+        split_prod(q0[h], e0s, q1[h], e1s, hi, lo);
+        L.coef[hh][h][lane] = hi;
+        L.coef[hh][8 + h][lane] = lo;
+        // offset contribution of exactly the fp16 coefficients the matrix cores use
+        const float aoff = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, lo), offp,
+                                                  __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, hi), offp, 0.f,
+                                                                         false),
+                                                  false);
+        bp[h] = fmaf(-inv_sa, aoff, fmaf(q0[h], f0[hh], q1[h] * f1[hh]));
+      } else {
+        bp[h] = 0.f;
+      }
     }
+    // b (offsets removed) of this lane's head, in key-page-scaled units, enters the hi columns
+    kinit[hh] = sel_lo(head_reduce8(bp, lane) * sa, 0.f);
   }
 
   int exf;
@@ -437,53 +473,61 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveStat
   const int t0 = 2 * lane;
   L.pk[t0] = ex2(P.kr.x) * inv_sa;
   L.pk[t0 + 1] = ex2(P.kr.y) * inv_sa;
-  L.fv[t0] = F0 * sw;
-  L.fv[t0 + 1] = F1 * sw;
-  L.zv[t0] = vr0 * half_bits_to_float(P.vz2 & 0xFFFFu);
-  L.zv[t0 + 1] = vr1 * half_bits_to_float(P.vz2 >> 16);
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    L.fv[hh][t0] = F0[hh] * sw;
+    L.fv[hh][t0 + 1] = F1[hh] * sw;
+    L.zv[hh][t0] = vr0 * half_bits_to_float(P.vz2[hh] & 0xFFFFu);
+    L.zv[hh][t0 + 1] = vr1 * half_bits_to_float(P.vz2[hh] >> 16);
+  }
   L.gs[t0] = ex2(P.vg.x) * inv_sw;
   L.gs[t0 + 1] = ex2(P.vg.y) * inv_sw;
-  // b (offsets removed) of this lane's head, in key-page-scaled units, enters the hi columns
-  const float bsum = head_reduce8(bp, lane);
-  const float kinit = sel_lo(bsum * sa, 0.f);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
   // ---- key side: scores ---------------------------------------------------
-  const int n = lane & 15;
-  f16x8 cb[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    cb[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&L.coef[n][16 * g + 4 * ks]));
   // M-tiles mt and mt + 4 give this lane's tokens of the hi and lo halves; lanes 0-7 of a row
-  // keep tile mt, lanes 8-15 tile mt + 4 (tokens 32g + 16*lo_col + 4mt + r)
+  // keep tile mt, lanes 8-15 tile mt + 4 (tokens 32g + 16*lo_col + 4mt + r).  With two token
+  // halves the products run once per half's coefficients and lanes of quarters 2, 3 keep the second.
+  const int n = lane & 15;
   float sm[4][4];
-  float mloc = -INFINITY;
   const float* pkp = &L.pk[32 * g + 16 * lo_col];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    f32x4 da = {kinit, kinit, kinit, kinit}, db = da;
+  for (int hh = 0; hh < NH; ++hh) {
+    f16x8 cb[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if constexpr (KB == 4) {
-        da = mfma16x16x32(key_codes(P.kc[mt][0][ks], M.m16, M.m64), cb[ks], da);
-        db = mfma16x16x32(key_codes(P.kc[mt + 4][0][ks], M.m16, M.m64), cb[ks], db);
-      } else {
-        const int h = ks >> 1, d = 2 * (ks & 1);
-        da = mfma16x16x32(key_codes8(P.kc[mt][h][d], P.kc[mt][h][d + 1], M.m1024), cb[ks], da);
-        db = mfma16x16x32(key_codes8(P.kc[mt + 4][h][d], P.kc[mt + 4][h][d + 1], M.m1024), cb[ks], db);
+    for (int ks = 0; ks < 4; ++ks)
+      cb[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(&L.coef[hh][n][16 * g + 4 * ks]));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 da = {kinit[hh], kinit[hh], kinit[hh], kinit[hh]}, db = da;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (KB == 4) {
+          da = mfma16x16x32(key_codes(P.kc[mt][0][ks], M.m16, M.m64), cb[ks], da);
+          db = mfma16x16x32(key_codes(P.kc[mt + 4][0][ks], M.m16, M.m64), cb[ks], db);
+        } else {
+          const int h = ks >> 1, d = 2 * (ks & 1);
+          da = mfma16x16x32(key_codes8(P.kc[mt][h][d], P.kc[mt][h][d + 1], M.m1024), cb[ks], da);
+          db = mfma16x16x32(key_codes8(P.kc[mt + 4][h][d], P.kc[mt + 4][h][d + 1], M.m1024), cb[ks], db);
+        }
+      }
+      const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
+      const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float xa = da[r] + dpp<kDppXor8>(da[r]);
+        const float xb = db[r] + dpp<kDppXor8>(db[r]);
+        const float v = pkv[r] * sel_lo(xa, xb);
+        sm[mt][r] = hh == 0 ? v : (g >= 2 ? v : sm[mt][r]);
       }
     }
-    const float4 pk4 = *reinterpret_cast<const float4*>(pkp + 4 * mt);
-    const float pkv[4] = {pk4.x, pk4.y, pk4.z, pk4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float sa = da[r] + dpp<kDppXor8>(da[r]);
-      const float sb = db[r] + dpp<kDppXor8>(db[r]);
-      sm[mt][r] = pkv[r] * sel_lo(sa, sb);
-      mloc = fmaxf(mloc, sm[mt][r]);
-    }
   }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, sm[mt][r]);
   mloc = head_max(mloc);
   const float m_new = fmaxf(S.m_run, mloc);
   const float alpha = ex2(S.m_run - m_new);
@@ -496,89 +540,97 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB>& P, WaveStat
   }
   S.m_run = m_new;
 
-  // ---- softmax weights, value-side B operand -------------------------------
-  const float* fvp = &L.fv[32 * g + 16 * lo_col];
-  const float* zvp = &L.zv[32 * g + 16 * lo_col];
-  float lsum = 0.f, usum = 0.f, wev = 0.f, wod = 0.f;
-  float pv[4][4], fvv[4][4];
+  // ---- softmax weights ----------------------------------------------------
+  float lsum = 0.f;
+  float pv[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const float4 f4 = *reinterpret_cast<const float4*>(fvp + 4 * mt);
-    const float4 z4 = *reinterpret_cast<const float4*>(zvp + 4 * mt);
-    fvv[mt][0] = f4.x; fvv[mt][1] = f4.y; fvv[mt][2] = f4.z; fvv[mt][3] = f4.w;
-    const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = ex2(sm[mt][r] - m_new);
       lsum += p;
-      usum = fmaf(p, zvv[r], usum);
       pv[mt][r] = p;
     }
-  }
-  // w_t = p_t * fv_t; pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
-  uint32_t own_hi[2][4], own_lo[2][4];
+  lsum = head_sum(lsum);
+  S.l_run = fmaf(S.l_run, alpha, lsum);
+
+  // ---- value side, per channel half: B operand, then o (rotated basis, hi and lo columns apart) --
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int vh = 0; vh < NH; ++vh) {
+    const float* fvp = &L.fv[vh][32 * g + 16 * lo_col];
+    const float* zvp = &L.zv[vh][32 * g + 16 * lo_col];
+    float usum = 0.f, wev = 0.f, wod = 0.f;
+    float fvv[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      split_prod(pv[hf][j], fvv[hf][j], pv[hf + 2][j], fvv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
-  // value offsets (2-bit codes: 4 for even tokens, 16 for odd; 4-bit codes: 64) of exactly the fp16
-  // weights used
-  {
-    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    for (int mt = 0; mt < 4; ++mt) {
+      const float4 f4 = *reinterpret_cast<const float4*>(fvp + 4 * mt);
+      const float4 z4 = *reinterpret_cast<const float4*>(zvp + 4 * mt);
+      fvv[mt][0] = f4.x; fvv[mt][1] = f4.y; fvv[mt][2] = f4.z; fvv[mt][3] = f4.w;
+      const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) usum = fmaf(pv[mt][r], zvv[r], usum);
+    }
+    // w_t = p_t * fv_t; pair (hf, j) = tokens 4hf + j and 4hf + j + 8 of this lane's 16
+    uint32_t own_hi[2][4], own_lo[2][4];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
+      for (int j = 0; j < 4; ++j)
+        split_prod(pv[hf][j], fvv[hf][j], pv[hf + 2][j], fvv[hf + 2][j], own_hi[hf][j], own_lo[hf][j]);
+    // value offsets (2-bit codes: 4 for even tokens, 16 for odd; 4-bit codes: 64) of exactly the fp16
+    // weights used
+    {
+      const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float& acc = (j & 1) ? wod : wev;
+          acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_hi[hf][j]), ones, acc, false);
+          acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_lo[hf][j]), ones, acc, false);
+        }
+    }
+    // u minus the value offsets, in value-page-scaled units, enters the hi columns
+    const float voff = VB == 2 ? fmaf(16.f, wod, 4.f * wev) : 64.f * (wev + wod);
+    const float ucorr = head_sum(fmaf(usum, sw, -voff));
+    const float vinit = sel_lo(ucorr, 0.f);
+    f16x8 wb[2][2];  // [u][hf]
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      u32x4 mine, other;
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float& acc = (j & 1) ? wod : wev;
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_hi[hf][j]), ones, acc, false);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, own_lo[hf][j]), ones, acc, false);
+        mine[j] = sel_lo_u32(own_hi[hf][j], own_lo[hf][j]);
+        other[j] = dpp_u32_xor8(sel_lo_u32(own_lo[hf][j], own_hi[hf][j]));
       }
-  }
-  lsum = head_sum(lsum);
-  S.l_run = fmaf(S.l_run, alpha, lsum);
-  // u minus the value offsets, in value-page-scaled units, enters the hi columns
-  const float voff = VB == 2 ? fmaf(16.f, wod, 4.f * wev) : 64.f * (wev + wod);
-  const float ucorr = head_sum(fmaf(usum, sw, -voff));
-  const float vinit = sel_lo(ucorr, 0.f);
-  f16x8 wb[2][2];  // [u][hf]
+      u32x4 u0, u1;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    u32x4 mine, other;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      mine[j] = sel_lo_u32(own_hi[hf][j], own_lo[hf][j]);
-      other[j] = dpp_u32_xor8(sel_lo_u32(own_lo[hf][j], own_hi[hf][j]));
-    }
-    u32x4 u0, u1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u0[j] = sel_lo_u32(mine[j], other[j]);
-      u1[j] = sel_lo_u32(other[j], mine[j]);
-    }
-    wb[0][hf] = __builtin_bit_cast(f16x8, u0);
-    wb[1][hf] = __builtin_bit_cast(f16x8, u1);
-  }
-
-  // ---- value side: o (rotated basis), hi and lo columns kept apart ----------
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    f32x4 d = {vinit, vinit, vinit, vinit};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f16x8 c0, c1;
-      if constexpr (VB == 2) {
-        value_codes(P.vc[mt][u], M.m4, M.m16, c0, c1);
-      } else {
-        value_codes4(P.vc[mt][2 * u], P.vc[mt][2 * u + 1], M.m64, c0, c1);
+      for (int j = 0; j < 4; ++j) {
+        u0[j] = sel_lo_u32(mine[j], other[j]);
+        u1[j] = sel_lo_u32(other[j], mine[j]);
       }
-      d = mfma16x16x32(c0, wb[u][0], d);
-      d = mfma16x16x32(c1, wb[u][1], d);
+      wb[0][hf] = __builtin_bit_cast(f16x8, u0);
+      wb[1][hf] = __builtin_bit_cast(f16x8, u1);
     }
-    const float4 gs4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
-    const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(d[r], gsv[r], S.acc[mt][r]);
+    for (int mt = (NH == 1 ? 0 : 4 * vh); mt < (NH == 1 ? 8 : 4 * vh + 4); ++mt) {
+      f32x4 d = {vinit, vinit, vinit, vinit};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        f16x8 c0, c1;
+        if constexpr (VB == 2) {
+          value_codes(P.vc[mt][u], M.m4, M.m16, c0, c1);
+        } else {
+          value_codes4(P.vc[mt][2 * u], P.vc[mt][2 * u + 1], M.m64, c0, c1);
+        }
+        d = mfma16x16x32(c0, wb[u][0], d);
+        d = mfma16x16x32(c1, wb[u][1], d);
+      }
+      const float4 gs4 = *reinterpret_cast<const float4*>(&L.gs[16 * mt + 4 * g]);
+      const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(d[r], gsv[r], S.acc[mt][r]);
+    }
   }
 }
 
@@ -715,8 +767,8 @@ __device__ __forceinline__ void tail_partial(const uint16_t* __restrict__ qrow0,
 
 }  // namespace
 
-template <int KB, int VB>
-__global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_kernel(
+template <int KB, int VB, int GS>
+__global__ __launch_bounds__(256, (DecFormat<KB, VB, GS>::kMinWaves)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, int hq, int hkv,
@@ -725,7 +777,7 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_ke
   // The per-wave page buffers are live only inside the page loop; before it each wave uses its own
   // buffer as scratch for the query transform, and the four-wave merge after it reuses the memory.
   __shared__ union __align__(16) {
-    WaveLds wl[kWaves];
+    WaveLds<DecFormat<KB, VB, GS>::kHalves> wl[kWaves];
     struct {
       float wacc[kWaves][kMaxGroup][kHeadDim];   // per-wave o
     } t;
@@ -792,8 +844,8 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_ke
       qraw[h] = reinterpret_cast<const uint32_t*>(qb + (h < G ? h : 0) * kHeadDim)[lane];
     __builtin_amdgcn_sched_barrier(0);
     const int ch0 = coef_channel<KB>(lane);
-    constexpr int ch1 = DecFormat<KB, VB>::kCh1;
-    PageRegs<KB, VB> A;
+    constexpr int ch1 = DecFormat<KB, VB, GS>::kCh1;
+    PageRegs<KB, VB, GS> A;
     load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
     __builtin_amdgcn_sched_barrier(0);
 
@@ -801,8 +853,8 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_ke
     // Every wave transforms all heads itself (in registers) and writes the same values into the
     // shared per-lane array, so no workgroup barrier is needed; the wave's own page buffer serves as
     // scratch for the change of layout.
-    WaveLds& L = U.wl[w];
-    float (*qt)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&L.coef[0][0]);  // [kMaxGroup][128]
+    auto& L = U.wl[w];
+    float (*qt)[kHeadDim] = reinterpret_cast<float (*)[kHeadDim]>(&L.coef[0][0][0]);  // [kMaxGroup][128]
     const float qscale = kInvSqrt128 * scale_log2;
   #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
@@ -836,7 +888,7 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_ke
   #pragma unroll
       for (int r = 0; r < 4; ++r) S.acc[mt][r] = 0.f;
     // unused coefficient columns stay zero
-    for (int e = lane; e < 16 * kCoefStride; e += 64) (&L.coef[0][0])[e] = 0u;
+    for (int e = lane; e < DecFormat<KB, VB, GS>::kHalves * 16 * kCoefStride; e += 64) (&L.coef[0][0][0])[e] = 0u;
 
     // ---- pages of this wave: w, w + 4, ... ---------------------------------------
     bool bad_page = false;
@@ -951,11 +1003,13 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB>::kMinWaves)) void decode_ke
 
 hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, int num_pages,
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
-                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int blocks_per_split,
-                         int max_splits, float scale_log2, float* out, float* part, uint32_t* counters,
-                         uint32_t* flags, hipStream_t stream) {
-  auto kern = kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4> : decode_kernel<8, 2>)
-                         : (vbits == 4 ? decode_kernel<4, 4> : decode_kernel<4, 2>);
+                         const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int group,
+                         int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
+                         uint32_t* counters, uint32_t* flags, hipStream_t stream) {
+  auto kern = group == 64 ? (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 64> : decode_kernel<8, 2, 64>)
+                                        : (vbits == 4 ? decode_kernel<4, 4, 64> : decode_kernel<4, 2, 64>))
+                          : (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 128> : decode_kernel<8, 2, 128>)
+                                        : (vbits == 4 ? decode_kernel<4, 4, 128> : decode_kernel<4, 2, 128>));
   hipLaunchKernelGGL(kern, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens,

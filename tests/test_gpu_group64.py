@@ -96,3 +96,87 @@ def test_llama3_layer_g64_sampled_tiles(K):
         chk.compare_tile(stats, vh[sl, h], vph[p, h].tobytes(), True)
     say("  " + stats.summary())
     stats.check()
+
+
+def randn_kv(g, n, hkv):
+    k = torch.randn(n, hkv, 128, generator=g).mul_(torch.where(torch.rand(128, generator=g) < 0.04, 20.0, 1.0))
+    v = torch.randn(n, hkv, 128, generator=g) * torch.exp(0.5 * torch.randn(n, hkv, 1, generator=g))
+    return k.half(), v.half()
+
+
+@pytest.mark.parametrize("name", FORMATS)
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_decode_g64(K, name, G):
+    """Decode over packed pages, then with an fp16 tail, ragged and paged; a bad page id flagged."""
+    cfg = K.kvarn_config_parse(name)
+    hkv = 2
+    hq = G * hkv
+    say("case: %s decode and decode with a tail, G = %d, ragged, paged" % (name, G))
+    g = torch.Generator().manual_seed(900 + 10 * G + len(name) + cfg.k_bits + cfg.v_bits)
+    nblk = [3, 0, 6, 1]
+    total = sum(nblk)
+    k, v = randn_kv(g, total * 128, hkv)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    kp, vp = quantize(K, cfg, k.cuda(), v.cuda(), perm, total, 0)
+    bt = torch.full((4, 7), -1, dtype=torch.int32)
+    off = 0
+    for b, nb in enumerate(nblk):
+        bt[b, :nb] = perm[off:off + nb]
+        off += nb
+    q = torch.randn(4, hq, 128, generator=g).half().cuda()
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    ws = K.alloc_workspace(cfg, 4, hq, hkv, bt.shape[1])
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sl = torch.tensor([128 * nb for nb in nblk], dtype=torch.int32)
+    out = torch.full((4, hq, 128), float("nan"), device="cuda")
+    K.kvarn_decode_attention(cfg, q, kp, vp, bt.cuda(), sl.cuda(), hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.decode(q.cpu().numpy(), kph, vph, bt.numpy(), sl.numpy(), hkv)
+    got = out.cpu().numpy()
+    assert np.all(got[1] == 0)
+    d = float(np.abs(got - ref).max())
+    say("  decode max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
+    kt, vt = randn_kv(g, 4 * 128, hkv)
+    kt, vt = kt.view(4, 128, hkv, 128).cuda(), vt.view(4, 128, hkv, 128).cuda()
+    slt = torch.tensor([128 * 3 + 50, 127, 128 * 6, 128 + 1], dtype=torch.int32)
+    K.kvarn_decode_attention_tail(cfg, q, kp, vp, bt.cuda(), slt.cuda(), kt, vt, hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.decode_tail(q.cpu().numpy(), kph, vph, bt.numpy(), slt.numpy(), kt.cpu().numpy(), vt.cpu().numpy(), hkv)
+    d = float(np.abs(out.cpu().numpy() - ref).max())
+    say("  decode with tail max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
+    bad = bt.clone()
+    bad[2, 4] = total + 3
+    K.kvarn_decode_attention(cfg, q, kp, vp, bad.cuda(), sl.cuda(), hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) & 1
+
+
+def test_llama3_layer_g64_decode_sampled(K):
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g64")
+    w = synth.WORKLOADS["llama3_8b_layer_16x8192"]
+    say("case: kvarn_k4v2_g64, %s full size decode, sampled heads" % w.name)
+    pm = synth.make_page_map(w)
+    n = synth.total_prefix_blocks(w)
+    k, v = synth.layer_kv(w, 0, n * 128, "cuda")
+    kp, vp = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0)
+    del k, v
+    q = synth.make_q(w, 0, "cuda")
+    ws = K.alloc_workspace(cfg, w.batch, w.hq, w.hkv, pm.block_table.shape[1])
+    out = torch.empty(w.batch, w.hq, 128, device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_decode_attention(cfg, q, kp, vp, pm.block_table.cuda(), pm.seq_lens.cuda(), w.hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    got = out.cpu().numpy()
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    worst = 0.0
+    for b, h in ((0, 0), (9, 17), (15, 31)):
+        ref = o.decode(q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(), w.hkv,
+                       seqs=[b], heads=[h])
+        worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
+    say("  decode max-abs diff %.3e over sampled heads" % worst)
+    assert worst <= chk.ATTN_TOL
