@@ -28,8 +28,8 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, int kbits, int vbits, float scale_log2, float* out, uint32_t* flags,
-                          hipStream_t stream);
+                          int hq, int hkv, int kbits, int vbits, int group, float scale_log2, float* out,
+                          uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
 
 namespace {
@@ -275,7 +275,6 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
                                      float softmax_scale, float* out, uint32_t* dev_flags, void* stream) {
   kvarn_status s = check_config(cfg);
   if (s != KVARN_OK) return s;
-  if (cfg->group_size != 128) return fail(KVARN_ERR_UNSUPPORTED, "prefill over group-size-64 pages is not built");
   if (batch < 0 || max_q < 0 || max_new < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
       num_pages < 0)
     return fail(KVARN_ERR_SHAPE, "negative or zero size");
@@ -303,7 +302,7 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
   const void* vn = max_new > 0 ? v_new : q;
   return launch_status(kvarn::launch_prefill(q, max_q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, prefix_lens,
                                              kn, vn, max_new, new_lens, q_lens, batch, num_q_heads, num_kv_heads,
-                                             cfg->k_bits, cfg->v_bits, scale_log2, out, dev_flags,
+                                             cfg->k_bits, cfg->v_bits, cfg->group_size, scale_log2, out, dev_flags,
                                              static_cast<hipStream_t>(stream)));
 }
 

@@ -40,14 +40,16 @@ constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kCt = 1;                          // 16-column MFMA tiles (16 rows each) per wave
 constexpr int kPfRows = 16 * kCt * kPfWaves;    // (query token, head) rows per workgroup
-constexpr int kMetaWords = kMetaBytes / 4;
+constexpr int kMetaWords = MetaLayout<64>::kBytes / 4;  // room for either group size
 
-// Page geometry of a format (key / value code widths).
-template <int KB, int VB>
+// Page geometry of a format (key / value code widths, group size).
+template <int KB, int VB, int GS>
 struct PfFormat {
+  using Meta = MetaLayout<GS>;
+  static constexpr int kHalves = Meta::kHalves;
   static constexpr int kKCode = kBlockTokens * kHeadDim * KB / 8;  // key code bytes
   static constexpr int kVCode = kBlockTokens * kHeadDim * VB / 8;  // value code bytes
-  static constexpr int kKPage = kKCode + kMetaBytes, kVPage = kVCode + kMetaBytes;
+  static constexpr int kKPage = kKCode + Meta::kBytes, kVPage = kVCode + Meta::kBytes;
   static constexpr int kKCodeChunks = kKCode / 16, kVCodeChunks = kVCode / 16;
   static constexpr int kKChunks = kKPage / 16;                  // key page, 16-byte chunks
   static constexpr int kChunks = (kKPage + kVPage) / 16;        // both pages
@@ -64,12 +66,14 @@ struct __align__(16) PfLds {
   u32x4 vf[kHeadDim * 16];      // values: channel row j, chunk c (8 token slots) at 16j + (c ^ (j & 15))
   uint32_t kmeta[kMetaWords];   // the page's raw key / value metadata
   uint32_t vmeta[kMetaWords];
-  float ep[kHeadDim];           // per channel: key 2^gamma s * sa
-  float fz[kHeadDim];           // per channel: key 2^gamma z
+  // [0] only for group size 128; [h] of group size 64: the key groups over token half h, the value
+  // groups over channel half h
+  float ep[2][kHeadDim];        // per channel: key 2^gamma s * sa
+  float fz[2][kHeadDim];        // per channel: key 2^gamma z
   float gs[kHeadDim];           // per channel: value 2^gamma / sw
   float pk[kBlockTokens];       // per token: key 2^rho / sa
-  float fv[kBlockTokens];       // per token: value 2^rho s * sw
-  float zv[kBlockTokens];       // per token: value 2^rho z
+  float fv[2][kBlockTokens];    // per token: value 2^rho s * sw
+  float zv[2][kBlockTokens];    // per token: value 2^rho z
   float sa, sw;                 // the block's power-of-two coefficient scales
   float qmax[kPfWaves];         // per wave: max |query coefficient| of the current phase
 };
@@ -282,20 +286,29 @@ __device__ __forceinline__ void store_page(PfLds& L, const PageRaw<F>& R, int ti
 }
 
 // Factors of a packed page (every wave finds the maxima itself; threads 0-127 write the per-channel
-// arrays, 128-255 the per-token ones).
+// arrays, 128-255 the per-token ones).  Group entries are half-major (entry 128*h + j).
+template <int GS>
 __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
+  using Meta = MetaLayout<GS>;
+  constexpr int NH = Meta::kHalves;
   asm volatile("" : "+v"(tid), "+v"(lane));
-  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaScale / 2;
-  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(L.kmeta) + kMetaZero / 2;
-  const float* krho = reinterpret_cast<const float*>(L.kmeta) + kMetaRho / 4;
-  const float* kgam = reinterpret_cast<const float*>(L.kmeta) + kMetaGamma / 4;
-  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(L.vmeta) + kMetaScale / 2;
-  const uint16_t* vzr = reinterpret_cast<const uint16_t*>(L.vmeta) + kMetaZero / 2;
-  const float* vrho = reinterpret_cast<const float*>(L.vmeta) + kMetaRho / 4;
-  const float* vgam = reinterpret_cast<const float*>(L.vmeta) + kMetaGamma / 4;
+  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(L.kmeta) + Meta::kScale / 2;
+  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(L.kmeta) + Meta::kZero / 2;
+  const float* krho = reinterpret_cast<const float*>(L.kmeta) + Meta::kRho / 4;
+  const float* kgam = reinterpret_cast<const float*>(L.kmeta) + Meta::kGamma / 4;
+  const uint16_t* vsc = reinterpret_cast<const uint16_t*>(L.vmeta) + Meta::kScale / 2;
+  const uint16_t* vzr = reinterpret_cast<const uint16_t*>(L.vmeta) + Meta::kZero / 2;
+  const float* vrho = reinterpret_cast<const float*>(L.vmeta) + Meta::kRho / 4;
+  const float* vgam = reinterpret_cast<const float*>(L.vmeta) + Meta::kGamma / 4;
   const int i0 = 2 * lane, i1 = 2 * lane + 1;
-  const float e = fmaxf(ex2(kgam[i0]) * half_bits_to_float(ksc[i0]), ex2(kgam[i1]) * half_bits_to_float(ksc[i1]));
-  const float f = fmaxf(ex2(vrho[i0]) * half_bits_to_float(vsc[i0]), ex2(vrho[i1]) * half_bits_to_float(vsc[i1]));
+  float e = 0.f, f = 0.f;
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    e = fmaxf(e, fmaxf(ex2(kgam[i0]) * half_bits_to_float(ksc[128 * hh + i0]),
+                       ex2(kgam[i1]) * half_bits_to_float(ksc[128 * hh + i1])));
+    f = fmaxf(f, fmaxf(ex2(vrho[i0]) * half_bits_to_float(vsc[128 * hh + i0]),
+                       ex2(vrho[i1]) * half_bits_to_float(vsc[128 * hh + i1])));
+  }
   const float emax = wave_max(e), fmax = wave_max(f);
   float qmax = 0.f;
 #pragma unroll
@@ -306,15 +319,21 @@ __device__ __forceinline__ void page_factors(PfLds& L, int tid, int lane) {
   if (tid < kHeadDim) {
     const int j = tid;
     const float eg = ex2(kgam[j]);
-    L.ep[j] = eg * half_bits_to_float(ksc[j]) * sa;
-    L.fz[j] = eg * half_bits_to_float(kzr[j]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      L.ep[hh][j] = eg * half_bits_to_float(ksc[128 * hh + j]) * sa;
+      L.fz[hh][j] = eg * half_bits_to_float(kzr[128 * hh + j]);
+    }
     L.gs[j] = ex2(vgam[j]) * inv_sw;
   } else if (tid < 2 * kHeadDim) {
     const int t = tid - kHeadDim;
     const float ev = ex2(vrho[t]);
     L.pk[t] = ex2(krho[t]) * inv_sa;
-    L.fv[t] = ev * half_bits_to_float(vsc[t]) * sw;
-    L.zv[t] = ev * half_bits_to_float(vzr[t]);
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      L.fv[hh][t] = ev * half_bits_to_float(vsc[128 * hh + t]) * sw;
+      L.zv[hh][t] = ev * half_bits_to_float(vzr[128 * hh + t]);
+    }
   }
   if (tid == 0) {
     L.sa = sa;
@@ -368,14 +387,14 @@ __device__ __forceinline__ void fp16_factors(PfLds& L, int tid) {
   page_scale(qmax, sa, inv_sa);
   page_scale(1.0f, sw, inv_sw);
   if (tid < kHeadDim) {
-    L.ep[tid] = sa;
-    L.fz[tid] = 0.f;
+    L.ep[0][tid] = sa;
+    L.fz[0][tid] = 0.f;
     L.gs[tid] = inv_sw;
   } else if (tid < 2 * kHeadDim) {
     const int t = tid - kHeadDim;
     L.pk[t] = inv_sa;
-    L.fv[t] = sw;
-    L.zv[t] = 0.f;
+    L.fv[0][t] = sw;
+    L.zv[0][t] = 0.f;
   }
   if (tid == 0) {
     L.sa = sa;
@@ -392,14 +411,17 @@ static_assert(kCt == 1, "the pipelined block step holds one 16-row tile per wave
 // 32g + 16h + 4lt + r, scaled here by 2^rho / sa and masked past `lim`.  Updates m and the lane's
 // share of l; returns the factor that rescales everything accumulated before, the row's value
 // offset term (u, times sw) and the value-product B operands of token pairs (lt, lt + 2).
+// NH = 2 (group size 64): one B operand and offset term per channel half of the value groups.
+template <int NH>
 struct HalfOut {
-  f16x8 whi[2], wlo[2];
-  float alpha, vinit;
+  f16x8 whi[NH][2], wlo[NH][2];
+  float alpha, vinit[NH];
 };
 
-template <bool kMasked>
-__device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x4 (&sc)[4], int h, int g, int lim) {
-  HalfOut R;
+template <bool kMasked, int NH>
+__device__ __forceinline__ HalfOut<NH> softmax_half(PfState& S, const PfLds& L, f32x4 (&sc)[4], int h, int g,
+                                                    int lim) {
+  HalfOut<NH> R;
   const int t0 = 32 * g + 16 * h;
   float mloc = -INFINITY;
 #pragma unroll
@@ -418,31 +440,41 @@ __device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x
   const float m_use = m_new == -INFINITY ? 0.f : m_new;  // nothing visible yet: every weight stays 0
   R.alpha = ex2(S.m[0] - m_use);
   S.m[0] = m_new;
-  float lsum = 0.f, usum = 0.f;
+  float lsum = 0.f, usum[NH];
+#pragma unroll
+  for (int vh = 0; vh < NH; ++vh) usum[vh] = 0.f;
 #pragma unroll
   for (int lt = 0; lt < 4; ++lt) {
-    const float4 z4 = *reinterpret_cast<const float4*>(&L.zv[t0 + 4 * lt]);
-    const float zvv[4] = {z4.x, z4.y, z4.z, z4.w};
+    float zvv[NH][4];
+#pragma unroll
+    for (int vh = 0; vh < NH; ++vh) {
+      const float4 z4 = *reinterpret_cast<const float4*>(&L.zv[vh][t0 + 4 * lt]);
+      zvv[vh][0] = z4.x; zvv[vh][1] = z4.y; zvv[vh][2] = z4.z; zvv[vh][3] = z4.w;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = ex2(sc[lt][r] - m_use);
       lsum += p;
-      usum = fmaf(p, zvv[r], usum);
+#pragma unroll
+      for (int vh = 0; vh < NH; ++vh) usum[vh] = fmaf(p, zvv[vh][r], usum[vh]);
       sc[lt][r] = p;
     }
   }
   S.l[0] = fmaf(S.l[0], R.alpha, lsum);
-  R.vinit = L.sw * sum32(sum16(usum));
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const float4 fa = *reinterpret_cast<const float4*>(&L.fv[t0 + 4 * hf]);
-    const float4 fb = *reinterpret_cast<const float4*>(&L.fv[t0 + 4 * hf + 8]);
-    const float fva[4] = {fa.x, fa.y, fa.z, fa.w}, fvb[4] = {fb.x, fb.y, fb.z, fb.w};
-    uint32_t hi[4], lo[4];
+  for (int vh = 0; vh < NH; ++vh) {
+    R.vinit[vh] = L.sw * sum32(sum16(usum[vh]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split2(sc[hf][j], fva[j], sc[hf + 2][j], fvb[j], hi[j], lo[j]);
-    R.whi[hf] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    R.wlo[hf] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    for (int hf = 0; hf < 2; ++hf) {
+      const float4 fa = *reinterpret_cast<const float4*>(&L.fv[vh][t0 + 4 * hf]);
+      const float4 fb = *reinterpret_cast<const float4*>(&L.fv[vh][t0 + 4 * hf + 8]);
+      const float fva[4] = {fa.x, fa.y, fa.z, fa.w}, fvb[4] = {fb.x, fb.y, fb.z, fb.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) split2(sc[hf][j], fva[j], sc[hf + 2][j], fvb[j], hi[j], lo[j]);
+      R.whi[vh][hf] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+      R.wlo[vh][hf] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    }
   }
   return R;
 }
@@ -452,38 +484,43 @@ __device__ __forceinline__ HalfOut softmax_half(PfState& S, const PfLds& L, f32x
 // different halves interleave in one wave: the half-1 scores run under the half-0 softmax, the
 // half-0 value products under the half-1 softmax.  lim: block-relative index of the last key row the
 // lane's row may see; kMasked false: every row sees the whole block (packed pages), no mask.
-template <bool kMasked>
+template <bool kMasked, int NH>
 __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lane, const int (&lim)[kCt]) {
   asm volatile("" : "+v"(lane));  // fragment addresses are recomputed per block, not kept live
   const int n = lane & 15, g = lane >> 4;
   const float sa = L.sa;
 
-  // ---- b_r over this lane's 32 channels, then over the row's four lanes ---------------------------
-  float kinit = 0.f;
+  // ---- b_r over this lane's 32 channels, then over the row's four lanes (per key token half) -------
+  float kinit[NH];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const float4 f0 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g]);
-    const float4 f1 = *reinterpret_cast<const float4*>(&L.fz[32 * ks + 8 * g + 4]);
-    const float fz8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+  for (int hh = 0; hh < NH; ++hh) {
+    float b = 0.f;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) kinit = fmaf(S.qv[0][8 * ks + s], fz8[s], kinit);
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4 f0 = *reinterpret_cast<const float4*>(&L.fz[hh][32 * ks + 8 * g]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&L.fz[hh][32 * ks + 8 * g + 4]);
+      const float fz8[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) b = fmaf(S.qv[0][8 * ks + s], fz8[s], b);
+    }
+    kinit[hh] = sa * sum32(sum16(b));
   }
-  kinit = sa * sum32(sum16(kinit));
 
   // ---- coefficient B operands of the four channel steps (slots 2s2, 2s2 + 1: channels s2, s2 + 4) --
-  f16x8 bhi[4], blo[4];
+  auto coef_ops = [&](int hh, f16x8 (&bhi)[4], f16x8 (&blo)[4]) {
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const float4 e0 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g]);
-    const float4 e1 = *reinterpret_cast<const float4*>(&L.ep[32 * ks + 8 * g + 4]);
-    const float ep8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-    uint32_t hi[4], lo[4];
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4 e0 = *reinterpret_cast<const float4*>(&L.ep[hh][32 * ks + 8 * g]);
+      const float4 e1 = *reinterpret_cast<const float4*>(&L.ep[hh][32 * ks + 8 * g + 4]);
+      const float ep8[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+      uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      split2(S.qv[0][8 * ks + s2], ep8[s2], S.qv[0][8 * ks + s2 + 4], ep8[s2 + 4], hi[s2], lo[s2]);
-    bhi[ks] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    blo[ks] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
-  }
+      for (int s2 = 0; s2 < 4; ++s2)
+        split2(S.qv[0][8 * ks + s2], ep8[s2], S.qv[0][8 * ks + s2 + 4], ep8[s2 + 4], hi[s2], lo[s2]);
+      bhi[ks] = __builtin_bit_cast(f16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+      blo[ks] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    }
+  };
 
   // score tile mt: D[token][row], A = key row 32(n/4) + 4mt + n%4; lane (n, g) gets tokens 32g + 4mt + r
   auto key_frag = [&](int mt, int ks) {
@@ -496,55 +533,85 @@ __device__ __forceinline__ void attend_block(PfState& S, const PfLds& L, int lan
     return __builtin_bit_cast(f16x8, L.vf[16 * j + ((4 * g + c) ^ n)]);
   };
 
-  // ---- half 0 scores -----------------------------------------------------------------------------
-  f32x4 s0[4], s1[4];
+  f32x4 s0[4], s1[4], d[8];
+  if constexpr (NH == 1) {
+    f16x8 bhi[4], blo[4];
+    coef_ops(0, bhi, blo);
+    // ---- half 0 scores ---------------------------------------------------------------------------
 #pragma unroll
-  for (int lt = 0; lt < 4; ++lt) {
-    s0[lt] = f32x4{kinit, kinit, kinit, kinit};
+    for (int lt = 0; lt < 4; ++lt) {
+      s0[lt] = f32x4{kinit[0], kinit[0], kinit[0], kinit[0]};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f16x8 a = key_frag(lt, ks);
-      s0[lt] = mfma16x16x32(a, bhi[ks], s0[lt]);
-      s0[lt] = mfma16x16x32(a, blo[ks], s0[lt]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 a = key_frag(lt, ks);
+        s0[lt] = mfma16x16x32(a, bhi[ks], s0[lt]);
+        s0[lt] = mfma16x16x32(a, blo[ks], s0[lt]);
+      }
+    }
+    // ---- half 1 scores, with the half-0 softmax -----------------------------------------------------
+#pragma unroll
+    for (int lt = 0; lt < 4; ++lt) {
+      s1[lt] = f32x4{kinit[0], kinit[0], kinit[0], kinit[0]};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 a = key_frag(4 + lt, ks);
+        s1[lt] = mfma16x16x32(a, bhi[ks], s1[lt]);
+        s1[lt] = mfma16x16x32(a, blo[ks], s1[lt]);
+      }
+    }
+  } else {
+    // Two key token halves: lane group g holds tokens of quarter g, i.e. of half g / 2.  Every score
+    // tile is computed with each half's coefficients; groups 2 and 3 keep the second result.
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      f16x8 bhi[4], blo[4];
+      coef_ops(hh, bhi, blo);
+#pragma unroll
+      for (int lt = 0; lt < 8; ++lt) {
+        f32x4 t = {kinit[hh], kinit[hh], kinit[hh], kinit[hh]};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f16x8 a = key_frag(lt, ks);
+          t = mfma16x16x32(a, bhi[ks], t);
+          t = mfma16x16x32(a, blo[ks], t);
+        }
+        f32x4& dst = lt < 4 ? s0[lt & 3] : s1[lt & 3];
+        if (hh == 0) {
+          dst = t;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dst[r] = g >= 2 ? t[r] : dst[r];
+        }
+      }
     }
   }
-  // ---- half 1 scores, with the half-0 softmax -----------------------------------------------------
-#pragma unroll
-  for (int lt = 0; lt < 4; ++lt) {
-    s1[lt] = f32x4{kinit, kinit, kinit, kinit};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f16x8 a = key_frag(4 + lt, ks);
-      s1[lt] = mfma16x16x32(a, bhi[ks], s1[lt]);
-      s1[lt] = mfma16x16x32(a, blo[ks], s1[lt]);
-    }
-  }
-  const HalfOut h0 = softmax_half<kMasked>(S, L, s0, 0, g, lim[0]);
+  const HalfOut<NH> h0 = softmax_half<kMasked, NH>(S, L, s0, 0, g, lim[0]);
 
-  // ---- half 0 value products, with the half-1 softmax ---------------------------------------------
-  f32x4 d[8];
+  // ---- half 0 value products, with the half-1 softmax (value M-tiles 4-7 are channel half 1) -------
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
-    d[mt] = f32x4{h0.vinit, h0.vinit, h0.vinit, h0.vinit};
+    const int vh = NH == 1 ? 0 : (mt >> 2);
+    d[mt] = f32x4{h0.vinit[vh], h0.vinit[vh], h0.vinit[vh], h0.vinit[vh]};
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const f16x8 a = val_frag(mt, hf);
-      d[mt] = mfma16x16x32(a, h0.whi[hf], d[mt]);
-      d[mt] = mfma16x16x32(a, h0.wlo[hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h0.whi[vh][hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h0.wlo[vh][hf], d[mt]);
     }
   }
-  const HalfOut h1 = softmax_half<kMasked>(S, L, s1, 1, g, lim[0]);
+  const HalfOut<NH> h1 = softmax_half<kMasked, NH>(S, L, s1, 1, g, lim[0]);
 
   // ---- half 1 value products on the rescaled half-0 partial --------------------------------------
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
+    const int vh = NH == 1 ? 0 : (mt >> 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) d[mt][r] = fmaf(d[mt][r], h1.alpha, h1.vinit);
+    for (int r = 0; r < 4; ++r) d[mt][r] = fmaf(d[mt][r], h1.alpha, h1.vinit[vh]);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const f16x8 a = val_frag(mt, 2 + hf);
-      d[mt] = mfma16x16x32(a, h1.whi[hf], d[mt]);
-      d[mt] = mfma16x16x32(a, h1.wlo[hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h1.whi[vh][hf], d[mt]);
+      d[mt] = mfma16x16x32(a, h1.wlo[vh][hf], d[mt]);
     }
   }
 
@@ -589,14 +656,14 @@ __device__ __forceinline__ float load_query(float (&qv)[32], const uint16_t* __r
 
 // One workgroup per (sequence, KV head, tile of qt queries): query i of a sequence sits at fp16 row
 // new_len - q_len + i and sees every packed token and the fp16 rows up to its own.
-template <int KB, int VB>
+template <int KB, int VB, int GS>
 __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     const uint16_t* __restrict__ q, int max_q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ prefix_lens,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int max_new,
     const int32_t* __restrict__ new_lens, const int32_t* __restrict__ q_lens, int batch, int hq, int hkv, int qt,
     int ntile, float scale_log2, float* __restrict__ out, uint32_t* __restrict__ flags) {
-  using F = PfFormat<KB, VB>;
+  using F = PfFormat<KB, VB, GS>;
   __shared__ PfLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, n = lane & 15, g = lane >> 4;
 
@@ -689,13 +756,13 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
       const int nxt = p + 1 < nblk ? bt[p + 1] : 0;
       __syncthreads();
       if (p + 1 < nblk) request(R, nxt);
-      if (ok) page_factors(L, tid, lane);
+      if (ok) page_factors<GS>(L, tid, lane);
       __syncthreads();
       if (ok) {
         int nolim[kCt];
 #pragma unroll
         for (int ct = 0; ct < kCt; ++ct) nolim[ct] = 0x7FFFFFFF;
-        if (wave_live) attend_block<false>(S, L, lane, nolim);
+        if (wave_live) attend_block<false, F::kHalves>(S, L, lane, nolim);
       } else {
         bad_page = true;
       }
@@ -739,7 +806,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
     int lim[kCt];
 #pragma unroll
     for (int ct = 0; ct < kCt; ++ct) lim[ct] = lim_abs[ct] == 0x7FFFFFFF ? 0x7FFFFFFF : lim_abs[ct] - base;
-    if (wave_live) attend_block<true>(S, L, lane, lim);
+    if (wave_live) attend_block<true, 1>(S, L, lane, lim);
   }
 
   // ---- normalise and store ---------------------------------------------------------------------------
@@ -761,8 +828,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void prefill_kernel(
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
-                          int hq, int hkv, int kbits, int vbits, float scale_log2, float* out, uint32_t* flags,
-                          hipStream_t stream) {
+                          int hq, int hkv, int kbits, int vbits, int group, float scale_log2, float* out,
+                          uint32_t* flags, hipStream_t stream) {
   const int G = hq / hkv;
   const int qt = kPfRows / G;
   const int ntile = (max_q + qt - 1) / qt;
@@ -770,8 +837,10 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
   const long groups = 8 * pairs8 * ntile;
   if (groups == 0) return hipSuccess;
   if (groups > 0x7FFFFFFFL) return hipErrorInvalidConfiguration;
-  auto kernel = kbits == 8 ? (vbits == 4 ? prefill_kernel<8, 4> : prefill_kernel<8, 2>)
-                           : (vbits == 4 ? prefill_kernel<4, 4> : prefill_kernel<4, 2>);
+  auto kernel = group == 64 ? (kbits == 8 ? (vbits == 4 ? prefill_kernel<8, 4, 64> : prefill_kernel<8, 2, 64>)
+                                          : (vbits == 4 ? prefill_kernel<4, 4, 64> : prefill_kernel<4, 2, 64>))
+                            : (kbits == 8 ? (vbits == 4 ? prefill_kernel<8, 4, 128> : prefill_kernel<8, 2, 128>)
+                                          : (vbits == 4 ? prefill_kernel<4, 4, 128> : prefill_kernel<4, 2, 128>));
   hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(groups)), dim3(kPfThreads), 0, stream,
                      static_cast<const uint16_t*>(q), max_q, static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, prefix_lens,

@@ -180,3 +180,42 @@ def test_llama3_layer_g64_decode_sampled(K):
         worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()))
     say("  decode max-abs diff %.3e over sampled heads" % worst)
     assert worst <= chk.ATTN_TOL
+
+
+@pytest.mark.parametrize("name,G", [("kvarn_k4v2_g64", 4), ("kvarn_k4v4_g64", 8), ("kvarn_k8v2_g64", 1),
+                                    ("kvarn_k8v4_g64", 3)])
+def test_prefill_g64(K, name, G):
+    """Chunked prefill over group-64 packed pages plus fp16 rows, ragged, against the oracle."""
+    cfg = K.kvarn_config_parse(name)
+    hkv = 2
+    hq = G * hkv
+    say("case: %s chunked prefill, G = %d, ragged, paged" % (name, G))
+    g = torch.Generator().manual_seed(1200 + 10 * G + cfg.k_bits + cfg.v_bits)
+    nblk = [2, 0, 4, 1]
+    total = sum(nblk)
+    k, v = randn_kv(g, total * 128, hkv)
+    perm = torch.randperm(total, generator=g).to(torch.int32)
+    kp, vp = quantize(K, cfg, k.cuda(), v.cuda(), perm, total, 0)
+    bt = torch.full((4, 5), -1, dtype=torch.int32)
+    off = 0
+    for b, nb in enumerate(nblk):
+        bt[b, :nb] = perm[off:off + nb]
+        off += nb
+    sl = torch.tensor([128 * nb for nb in nblk], dtype=torch.int32)
+    new_lens = torch.tensor([100, 40, 130, 7], dtype=torch.int32)
+    q_lens = torch.tensor([60, 40, 130, 0], dtype=torch.int32)
+    kn, vn = randn_kv(g, 4 * 136, hkv)
+    kn, vn = kn.view(4, 136, hkv, 128).cuda(), vn.view(4, 136, hkv, 128).cuda()
+    qp = torch.randn(4, 130, hq, 128, generator=g).half().cuda()
+    outp = torch.full((4, 130, hq, 128), float("nan"), device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_prefill_attention(cfg, qp, kp, vp, bt.cuda(), sl.cuda(), kn, vn, new_lens.cuda(), q_lens.cuda(), hkv, outp,
+                              dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.prefill(qp.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), bt.numpy(), sl.numpy(), kn.cpu().numpy(),
+                    vn.cpu().numpy(), new_lens.numpy(), q_lens.numpy(), hkv)
+    got = outp.cpu().numpy()
+    d = float(np.abs(got - ref).max())  # rows past q_len are zero on both sides; a NaN fails
+    say("  prefill max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
