@@ -81,7 +81,8 @@ def parse():
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
-    ap.add_argument("--no-formats", action="store_true", help="skip the other code widths (k4v4, k8v2, k8v4)")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the other formats (code widths k4v4, k8v2, k8v4; group size 64)")
     ap.add_argument("--prefill-workload", default="prefill_llama3_8b_16x7680p512")
     ap.add_argument("--no-tail", action="store_true", help="skip the decode with fp16 tails")
     ap.add_argument("--no-fp16-baseline", action="store_true",
@@ -382,7 +383,8 @@ def formats_measure(K, w, case, stream, reps, flush, sink):
     from kv_cache_quantization_kvarn_amd import accounting as acc
     res = {}
     L0 = case.layers[0]
-    for name in ("kvarn_k4v4_g128", "kvarn_k8v2_g128", "kvarn_k8v4_g128"):
+    for name in ("kvarn_k4v4_g128", "kvarn_k8v2_g128", "kvarn_k8v4_g128", "kvarn_k4v2_g64", "kvarn_k4v4_g64",
+                 "kvarn_k8v2_g64", "kvarn_k8v4_g64"):
         cfg = K.kvarn_config_parse(name)
         kp, vp = K.alloc_pools(cfg, case.pm.num_pages, w.hkv)
         if w.append_blocks:
@@ -514,6 +516,10 @@ def main():
     prefill = None
     if not args.no_prefill:
         prefill = prefill_measure(K, synth, acc, cfg, args.prefill_workload, stream, args.flush_reps, flush, flush_sink)
+        g64 = prefill_measure(K, synth, acc, K.kvarn_config_parse("kvarn_k4v2_g64"), args.prefill_workload, stream,
+                              max(5, args.flush_reps // 2), flush, flush_sink)
+        prefill["group64"] = {"format": "kvarn_k4v2_g64", "us_median": g64["us_median"], "tflops": g64["tflops"],
+                              "frac": g64["roofline"]["frac"]}
 
     step_bytes = case.q_bytes + case.d_bytes
     ms_per_step = elapsed / args.steps * 1e3

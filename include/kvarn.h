@@ -39,7 +39,7 @@ typedef enum {
   KVARN_OK = 0,
   KVARN_ERR_NULL = -1,        /* a required pointer is NULL */
   KVARN_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
-  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k{4,8}v{2,4}_g128 / head_dim 128 / block 128 */
+  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k{4,8}v{2,4}_g{128,64} / head_dim 128 / block 128 */
   KVARN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
   KVARN_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
 } kvarn_status;
@@ -49,10 +49,13 @@ typedef enum {
 #define KVARN_FLAG_BAD_SEQLEN 2u  /* seq_len < 0, not a multiple of 128, or above max_blocks*128: sequence output is 0 */
 
 /* Format parameters.  Supported: head_dim 128, block_tokens 128, k_bits 4 or
- * 8, v_bits 2 or 4, group_size 128, norm_iters 4, eps 1e-6.  The post names
- * kvarn_k4v2_g128; the wider codes keep every step of the method and change
- * the number of levels (2^bits - 1) and the packing only.  Every entry point
- * takes every format; the kernels are instantiated per pair of code widths. */
+ * 8, v_bits 2 or 4, group_size 128 or 64, norm_iters 4, eps 1e-6.  The post
+ * names kvarn_k4v2_g128; the wider codes keep every step of the method and
+ * change the number of levels (2^bits - 1) and the packing only.  Group size 64
+ * splits every group into two halves of 64 consecutive elements (a key group:
+ * one channel over tokens 64h .. 64h+63; a value group: one token over channels
+ * 64h .. 64h+63), each with its own scale and zero.  Every entry point takes
+ * every format; the kernels are instantiated per code widths and group size. */
 typedef struct {
   int32_t head_dim;
   int32_t block_tokens;
@@ -65,12 +68,14 @@ typedef struct {
 
 /* Fill *out from a cache dtype name of the form "kvarn_k<K>v<V>_g<G>"
  * (blog post, section "Pratik Çıkarımlar").  Parses any such name; names other
- * than kvarn_k{4,8}v{2,4}_g128 parse but return KVARN_ERR_UNSUPPORTED. */
+ * than kvarn_k{4,8}v{2,4}_g{128,64} parse but return KVARN_ERR_UNSUPPORTED. */
 kvarn_status kvarn_config_parse(const char* name, kvarn_config* out);
 
-/* Bytes of one page (one 128-token block of one KV head): C + 1536 with C =
- * 128*128*bits/8 code bytes: K (is_v = 0) 9728 for 4 bits, 17920 for 8 bits;
- * V (is_v = 1) 5632 for 2 bits, 9728 for 4 bits; 0 for an unsupported config.
+/* Bytes of one page (one 128-token block of one KV head): C + M with C =
+ * 128*128*bits/8 code bytes and M = 1536 metadata bytes for group size 128,
+ * 2048 for group size 64.  Group size 128: K (is_v = 0) 9728 for 4 bits, 17920
+ * for 8 bits; V (is_v = 1) 5632 for 2 bits, 9728 for 4 bits.  Group size 64:
+ * 512 more each.  0 for an unsupported config.
  *
  * K page: [0, C) codes, token-major: 4 bits: byte 64*t + k holds channel 2k in
  *         bits 0-3 and channel 2k+1 in bits 4-7 of token t; 8 bits: byte 128*t + c;
@@ -81,6 +86,10 @@ kvarn_status kvarn_config_parse(const char* name, kvarn_config* out);
  *         bits 0-3 and token 2k+1 in bits 4-7;
  *         then scale fp16[128 tokens], zero fp16[128 tokens], rho fp32[128
  *         tokens], gamma fp32[128 channels] at the same offsets from C.
+ * Group size 64: scale fp16[2][128] and zero fp16[2][128] (entry 128*h + j: the
+ *         group of channel j over tokens 64h .. 64h+63 for K, of token j over
+ *         channels 64h .. 64h+63 for V), rho, gamma at C, C + 512, C + 1024,
+ *         C + 1536.
  * All little endian.  Dequantisation: x^[t] = H (N^ * 2^(rho[t] + gamma)), with
  * N^ = scale * code + zero and H the orthonormal Sylvester Hadamard matrix. */
 size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v);
