@@ -33,14 +33,14 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9ba7a8be53416ea9", 663506092),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("3243801607111df3", 130363897),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("09b2cb24717213ac", 663228518),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 130372039),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9ba7a8be53416ea9", 126355456),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("3243801607111df3", 10894144),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("09b2cb24717213ac", 126357504),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 10894144),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12

@@ -295,11 +295,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         }
         rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
         rf_t = ex2(-rho_t) * kInvSqrt128;
-        if (hf == 0) {
-          s.rfl[t_red] = rf_t;
-        } else {
-          s.rfl2[t_red] = rf_t * rf_t;
-        }
+        (hf ? s.rfl2 : s.rfl)[t_red] = hf ? rf_t * rf_t : rf_t;
       }
       wave_lds_sync();
       {
@@ -332,11 +328,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         const float var = fmaf(-mu, mu, ey2);
         const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
         const float cf_new = ex2(-gam_new);
-        if (hf == 0) {
-          s.cfl[chan_slot(t_red)] = cf_new;
-        } else {
-          s.cfl2[chan_slot(t_red)] = cf_new * cf_new;
-        }
+        (hf ? s.cfl2 : s.cfl)[chan_slot(t_red)] = hf ? cf_new * cf_new : cf_new;
         // any column whose one-sweep variance could have lost digits redoes the pass centred;
         // the flag of the next pass is cleared here (every read of it happened before this
         // pass's first barrier)
@@ -363,11 +355,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           const float cvar = reduce_pairs(s.part[t_red], hf).x * inv128;
           gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
           cf_c = ex2(-gam_c);
-          if (hf == 0) {
-            s.cfl[chan_slot(t_red)] = cf_c;
-          } else {
-            s.cfl2[chan_slot(t_red)] = cf_c * cf_c;
-          }
+          (hf ? s.cfl2 : s.cfl)[chan_slot(t_red)] = hf ? cf_c * cf_c : cf_c;
           __syncthreads();
         } else {
           gam_c = gam_new;
@@ -444,11 +432,8 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           // scale from one thread of the pair, zero from the other
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
                                                 kCodeBytes + (hf ? Meta::kZero : Meta::kScale) + 2 * t_red, 0, 0);
-          if (hf == 0) {
-            s.mul_a[0][chan_slot(t_red)] = cf_c * inv;
-          } else {
-            s.mul_b[0][chan_slot(t_red)] = -zf * inv;
-          }
+          // one per-lane address instead of a branch on hf: straight-line code schedules better
+          (hf ? s.mul_b[0] : s.mul_a[0])[chan_slot(t_red)] = hf ? -zf * inv : cf_c * inv;
         }
       }
       __syncthreads();
@@ -571,11 +556,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         } else {
           __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(hf ? zb : sb), dst,
                                                 kCodeBytes + (hf ? Meta::kZero : Meta::kScale) + 2 * t_red, 0, 0);
-          if (hf == 0) {
-            s.mul_a[0][t_red] = rf_t * inv;
-          } else {
-            s.mul_b[0][t_red] = -zf * inv;
-          }
+          (hf ? s.mul_b[0] : s.mul_a[0])[t_red] = hf ? -zf * inv : rf_t * inv;
         }
       }
       __syncthreads();
