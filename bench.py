@@ -33,13 +33,13 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("09b2cb24717213ac", 663228518),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 130372039),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("3d708e7840efa3e9", 663464043),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 130372329),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("09b2cb24717213ac", 126357504),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("3d708e7840efa3e9", 126926848),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 10894144),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
