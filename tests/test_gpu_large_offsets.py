@@ -1,0 +1,104 @@
+"""Pages past 4 GiB in the packed pools: every kernel forms 64-bit page addresses.
+
+A key pool of more than 4.4 GB (56K+ pages of 8 KV heads) receives blocks in its last pages and near its
+start; quantise, dequantise, decode with an fp16 tail and chunked prefill over those pages are compared
+with the oracle on copies of just the pages used (same bars as the other parity tests).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvarn_oracle as o
+import kvarn_check as chk
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kv_cache_quantization_kvarn_amd import kvarn
+    return kvarn
+
+
+@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v4_g64"])
+def test_pages_past_4gib(K, name):
+    cfg = K.kvarn_config_parse(name)
+    hkv, hq = 8, 32
+    kb = K.kvarn_page_bytes(cfg, False)
+    num_pages = int(4.4e9) // (hkv * kb) + 8
+    say("case: %s, %d pages x %d heads: key pool %.2f GB, blocks in the last pages" %
+        (name, num_pages, hkv, num_pages * hkv * kb / 1e9))
+    assert num_pages * hkv * kb > 2 ** 32
+    g = torch.Generator().manual_seed(4242 + cfg.k_bits)
+    pages = torch.tensor([num_pages - 1, 7, num_pages - 2], dtype=torch.int32)
+    k = torch.randn(3 * 128, hkv, 128, generator=g).mul_(torch.where(torch.rand(128, generator=g) < 0.04, 20.0, 1.0))
+    v = torch.randn(3 * 128, hkv, 128, generator=g) * torch.exp(0.5 * torch.randn(3 * 128, hkv, 1, generator=g))
+    k, v = k.half().cuda(), v.half().cuda()
+    kp, vp = K.alloc_pools(cfg, num_pages, hkv)
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_quantize_blocks(cfg, k, v, pages.cuda(), kp, vp, fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    # the pages used, copied out, renumbered 0, 1, 2 for the oracle
+    kph = kp[pages.long().cuda()].cpu().numpy()
+    vph = vp[pages.long().cuda()].cpu().numpy()
+    stats = chk.TileStats()
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    for blk in range(3):
+        for h in (0, 5, 7):
+            sl = slice(128 * blk, 128 * blk + 128)
+            chk.compare_tile(stats, kh[sl, h], kph[blk, h].tobytes(), False)
+            chk.compare_tile(stats, vh[sl, h], vph[blk, h].tobytes(), True)
+    say("  " + stats.summary())
+    stats.check()
+    # dequantise straight from the large pools
+    ko = torch.empty(3 * 128, hkv, 128, dtype=torch.float32, device="cuda")
+    vo = torch.empty_like(ko)
+    K.kvarn_dequantize_blocks(cfg, kp, vp, pages.cuda(), ko, vo, fl)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for blk in range(3):
+        for h in (0, 7):
+            for pool, outd, is_v in ((kph, ko, False), (vph, vo, True)):
+                ref = o.dequantize_tile(o.decode_page(pool[blk, h].tobytes(), is_v), is_v)
+                worst = max(worst, float(np.abs(outd[128 * blk:128 * blk + 128, h].cpu().numpy() - ref).max()))
+    say("  dequantised max-abs diff %.3e" % worst)
+    assert worst <= chk.DEQUANT_TOL
+    # decode with a tail over the three pages
+    bt = pages.view(1, 3).cuda()
+    local_bt = np.arange(3, dtype=np.int32).reshape(1, 3)
+    q = torch.randn(1, hq, 128, generator=g).half().cuda()
+    kt = torch.randn(1, 128, hkv, 128, generator=g).half().cuda()
+    vt = torch.randn(1, 128, hkv, 128, generator=g).half().cuda()
+    sl = torch.tensor([3 * 128 + 45], dtype=torch.int32)
+    ws = K.alloc_workspace(cfg, 1, hq, hkv, 3)
+    out = torch.full((1, hq, 128), float("nan"), device="cuda")
+    K.kvarn_decode_attention_tail(cfg, q, kp, vp, bt, sl.cuda(), kt, vt, hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.decode_tail(q.cpu().numpy(), kph, vph, local_bt, sl.numpy(), kt.cpu().numpy(), vt.cpu().numpy(), hkv)
+    d = float(np.abs(out.cpu().numpy() - ref).max())
+    say("  decode with tail max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
+    # chunked prefill over the same pages
+    new_lens = torch.tensor([70], dtype=torch.int32)
+    q_lens = torch.tensor([20], dtype=torch.int32)
+    qp = torch.randn(1, 20, hq, 128, generator=g).half().cuda()
+    outp = torch.full((1, 20, hq, 128), float("nan"), device="cuda")
+    prefix = torch.tensor([3 * 128], dtype=torch.int32)
+    K.kvarn_prefill_attention(cfg, qp, kp, vp, bt, prefix.cuda(), kt, vt, new_lens.cuda(), q_lens.cuda(), hkv, outp,
+                              dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.prefill(qp.cpu().numpy(), kph, vph, local_bt, prefix.numpy(), kt.cpu().numpy(), vt.cpu().numpy(),
+                    new_lens.numpy(), q_lens.numpy(), hkv)
+    d = float(np.abs(outp.cpu().numpy() - ref).max())
+    say("  prefill max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
+    del kp, vp
+    torch.cuda.empty_cache()
