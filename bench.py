@@ -33,14 +33,14 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("3d708e7840efa3e9", 663464043),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 130372329),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("c3c43f5f0107ac35", 663334184),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 130374155),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("3d708e7840efa3e9", 126926848),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("2e14a538e36f44ce", 10894144),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("c3c43f5f0107ac35", 126926848),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 10894144),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -48,8 +48,8 @@ VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 
 
 def source_digest(kernel):
-    """Digest of the kernel's source code with comments and blank space removed, so that a comment
-    edit keeps the measurement while any change to the code drops it."""
+    """Digest of the kernel's source code with comments and blank space removed, and of its compiler
+    flags, so that a comment edit keeps the measurement while any change to the code drops it."""
     import hashlib
     import re
     csrc = os.path.join(ROOT, "kv_cache_quantization_kvarn_amd", "csrc")
@@ -60,6 +60,9 @@ def source_digest(kernel):
     data = re.sub(r"/\*.*?\*/", " ", data, flags=re.S)
     data = re.sub(r"//[^\n]*", " ", data)
     data = " ".join(data.split())
+    # the compiler flags of that source are part of what was measured
+    from kv_cache_quantization_kvarn_amd import build
+    data += " flags: " + " ".join(build.FLAGS + build.EXTRA.get(KERNEL_SOURCE[kernel], []))
     return hashlib.sha256(data.encode()).hexdigest()[:16]
 
 

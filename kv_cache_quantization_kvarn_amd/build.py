@@ -17,8 +17,11 @@ SOURCES = ["kvarn_api.hip", "kvarn_quantize.hip", "kvarn_decode.hip", "kvarn_fp1
 
 # Packed fp32 VALU instructions are disabled for device code; the host pass
 # ignores the feature (and says so).
-FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source scheduler choice: the quantiser (bound by vector-ALU issue) runs about 2% faster when
+# memory clauses are kept together; the other kernels are fastest with the default scheduler.
+EXTRA = {"kvarn_quantize.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def hipcc() -> str:
@@ -28,17 +31,30 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-o", tmp] + srcs
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, err))
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError("hipcc failed (%d): %s\n%s" % (res.returncode, " ".join(cmd), err))
+    return err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link libkvarn.so."""
+    import concurrent.futures
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="kvarn_build_") as tmpdir:
+        jobs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            jobs.append((obj, [hipcc()] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as pool:
+            msgs = list(pool.map(_run, [cmd for _, cmd in jobs]))
+        tmp = LIB + ".tmp"
+        msgs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in jobs]))
+    if verbose and any(m.strip() for m in msgs):
+        print("\n".join(m for m in msgs if m.strip()), file=sys.stderr)
     os.replace(tmp, LIB)
     return LIB
 
