@@ -18,9 +18,11 @@
 // mask-and-or (and for most pairs one shift) places a pair of codes in the
 // mantissa under a fixed exponent, which fixes the offset (4-bit keys 16 or 64,
 // 8-bit keys 1024; 2-bit values 4 or 16, 4-bit values 64).  The kernel is
-// instantiated per pair of code widths; only the page geometry, the code
-// loads and these conversions differ.  The offsets are removed with sums of the very fp16
-// coefficients the matrix cores multiplied.  (fp16 subnormal operands would
+// instantiated per code widths and group size; only the page geometry, the
+// code loads and these conversions differ, and for group size 64 (two scale /
+// zero sets per channel or token) the key products run once per token half and
+// the value products take their channel half's weights.  The offsets are
+// removed with sums of the very fp16 coefficients the matrix cores multiplied.  (fp16 subnormal operands would
 // need no offset, but the matrix cores lose precision on them, biased toward
 // zero.)  The fp32 coefficients a_j and w_t enter as an fp16 hi + lo pair (hi in
 // matrix columns 0-7, lo in columns 8-15) after a power-of-two page scale keeps
@@ -28,8 +30,9 @@
 // of one query head.  The per-head constants (b and u, offsets removed) enter
 // as the accumulator input of the first product of each chain.
 //
-// Latency: three workgroups (twelve waves) share a compute unit, so one wave's
-// page loads overlap the others' arithmetic; a wave's first page is requested
+// Latency: three workgroups (twelve waves) share a compute unit with 4-bit keys
+// and group size 128 (two otherwise), so one wave's page loads overlap the
+// others' arithmetic; a wave's first page is requested
 // together with the query, before the query transform, which then runs under
 // that page's HBM latency.  Both 128-point transforms (q~ = H q at the start,
 // H o at the end) run in registers, two entries per lane, with DPP and

@@ -29,7 +29,11 @@
 //     rows follow in blocks of 128 through the same LDS layout (keys copied, values transposed),
 //     with unit factors, the raw query and the causal mask.
 //
-// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.
+// Online softmax in log2 units over all blocks; the output is fp32 in the original basis.  The kernel
+// is instantiated per code widths and group size; with group size 64 the scale and zero differ between
+// the token halves of a key group and the channel halves of a value group, so the score products run
+// once per token half (a lane keeps the half its rows belong to) and each channel half of the value
+// products takes its own weights.
 #include "kvarn_common.h"
 
 namespace kvarn {

@@ -35,8 +35,11 @@
 // byte per 8-bit key code, two 4-bit value codes per byte in the wider
 // formats), transposed across lanes into whole dwords of the page (DPP within a
 // quad or a lane pair for keys, v_permlane16/32_swap across rows for values)
-// and stored directly.  The code widths are template parameters; every other
-// step is shared.
+// and stored directly.  The code widths and the group size are template
+// parameters; every other step is shared.  With group size 64 a key group is one
+// channel over a token half and a value group one token over a channel half: the
+// two threads of a min/max reducer pair then keep their own half (waves 0-1 vs
+// 2-3 for keys; a lane's channels c = 0-3 vs 4-7 for values) instead of merging.
 //
 // Scheduling.  Workgroups are persistent, two per compute unit; each walks its share of the key
 // tiles and then of the value tiles with a fixed stride.  The input of the next tile is fetched while the current
