@@ -22,11 +22,12 @@ def K():
     return kvarn
 
 
-def test_graph_replays_match_eager(K):
-    cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
+@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v4_g64"])
+def test_graph_replays_match_eager(K, name):
+    cfg = K.kvarn_config_parse(name)
     layers, batch, hq, hkv, nblk = 3, 4, 12, 2, 6
-    say("case: %d-layer step (quantise %d blocks x %d heads, decode %d sequences) captured, replayed 4 times"
-        % (layers, batch * nblk, hkv, batch))
+    say("case: %s, %d-layer step (quantise %d blocks x %d heads, decode %d sequences) captured, replayed 4 times"
+        % (name, layers, batch * nblk, hkv, batch))
     g = torch.Generator().manual_seed(515)
     L = []
     for _ in range(layers):
