@@ -219,3 +219,46 @@ def test_prefill_g64(K, name, G):
     d = float(np.abs(got - ref).max())  # rows past q_len are zero on both sides; a NaN fails
     say("  prefill max-abs diff %.3e" % d)
     assert d <= chk.ATTN_TOL
+
+
+def test_g64_half_constant_keys(K):
+    """Tokens 0..63 of every key block identical: each key group of token half 0 is constant, so its fp16
+    scale is 0 (all codes 0, the zero carries the value) while half 1's groups are not.  Quantise and
+    decode (with one zero-scale half per page) against the oracle."""
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g64")
+    hkv, hq = 2, 8
+    say("case: kvarn_k4v2_g64 with constant-in-time key halves, decode G = 4")
+    g = torch.Generator().manual_seed(777)
+    nb = 3
+    k = torch.randn(nb * 128, hkv, 128, generator=g)
+    for b in range(nb):
+        k[128 * b:128 * b + 64] = k[128 * b:128 * b + 1]
+    v = torch.randn(nb * 128, hkv, 128, generator=g)
+    k, v = k.half().cuda(), v.half().cuda()
+    pages = torch.tensor([2, 0, 1], dtype=torch.int32)
+    kp, vp = quantize(K, cfg, k, v, pages, nb, 0)
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    stats = chk.TileStats()
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    for b in range(nb):
+        for h in range(hkv):
+            sl = slice(128 * b, 128 * b + 128)
+            chk.compare_tile(stats, kh[sl, h], kph[int(pages[b]), h].tobytes(), False)
+            chk.compare_tile(stats, vh[sl, h], vph[int(pages[b]), h].tobytes(), True)
+            f = o.decode_page(kph[int(pages[b]), h].tobytes(), False)
+            assert np.all(f["scale"][0] == 0) and np.all(f["scale"][1] > 0)
+    say("  " + stats.summary())
+    stats.check()
+    q = torch.randn(1, hq, 128, generator=g).half().cuda()
+    bt = pages.view(1, nb)
+    sl = torch.tensor([nb * 128], dtype=torch.int32)
+    ws = K.alloc_workspace(cfg, 1, hq, hkv, nb)
+    out = torch.full((1, hq, 128), float("nan"), device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_decode_attention(cfg, q, kp, vp, bt.cuda(), sl.cuda(), hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    ref = o.decode(q.cpu().numpy(), kph, vph, bt.numpy(), sl.numpy(), hkv)
+    d = float(np.abs(out.cpu().numpy() - ref).max())
+    say("  decode max-abs diff %.3e" % d)
+    assert d <= chk.ATTN_TOL
