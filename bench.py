@@ -423,7 +423,7 @@ def formats_measure(K, w, case, stream, reps, flush, sink):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("this build measures one GPU only; --gpus %d is not supported (run with --gpus 1)" % args.gpus,
+        print("bench.py measures one GPU only; --gpus %d is not supported (run with --gpus 1)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
