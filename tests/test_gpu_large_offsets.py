@@ -102,3 +102,44 @@ def test_pages_past_4gib(K, name):
     assert d <= chk.ATTN_TOL
     del kp, vp
     torch.cuda.empty_cache()
+
+
+def test_decode_at_the_batch_limit(K):
+    """65,535 sequences (the largest batch the ABI accepts; it is the decode grid's second dimension), one
+    packed block each, one KV head with G = 2: sampled sequences against the oracle, and the 65,536th rejected."""
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
+    batch, hkv, hq = 65535, 1, 2
+    say("case: kvarn_k4v2_g128 decode, batch %d (one block each), Hkv %d, G %d" % (batch, hkv, hq))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(65535)
+    k = torch.randn(batch * 128, hkv, 128, generator=g, device="cuda").half()
+    v = torch.randn(batch * 128, hkv, 128, generator=g, device="cuda").half()
+    pages = torch.arange(batch, dtype=torch.int32, device="cuda").flip(0).contiguous()  # block b -> page batch-1-b
+    kp, vp = K.alloc_pools(cfg, batch, hkv)
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_quantize_blocks(cfg, k, v, pages, kp, vp, fl)
+    del k, v
+    q = torch.randn(batch, hq, 128, generator=g, device="cuda").half()
+    bt = pages.view(batch, 1)
+    sl = torch.full((batch,), 128, dtype=torch.int32, device="cuda")
+    ws = K.alloc_workspace(cfg, batch, hq, hkv, 1)
+    out = torch.full((batch, hq, 128), float("nan"), device="cuda")
+    K.kvarn_decode_attention(cfg, q, kp, vp, bt, sl, hkv, out, ws, dev_flags=fl)
+    torch.cuda.synchronize()
+    assert K.kvarn_read_flags(fl) == 0
+    assert not torch.isnan(out).any()
+    worst = 0.0
+    for b in (0, 1, 32767, 65533, 65534):
+        p = int(pages[b])
+        ref = o.decode(q[b:b + 1].cpu().numpy(), kp[p:p + 1].cpu().numpy(), vp[p:p + 1].cpu().numpy(),
+                       np.zeros((1, 1), np.int32), np.array([128]), hkv)
+        worst = max(worst, float(np.abs(out[b].cpu().numpy() - ref[0]).max()))
+    say("  decode max-abs diff %.3e on sampled sequences" % worst)
+    assert worst <= chk.ATTN_TOL
+    with pytest.raises(K.KvarnError):
+        big = torch.zeros(batch + 1, hq, 128, dtype=torch.float16, device="cuda")
+        K.kvarn_decode_attention(cfg, big, kp, vp, torch.zeros(batch + 1, 1, dtype=torch.int32, device="cuda"),
+                                 torch.zeros(batch + 1, dtype=torch.int32, device="cuda"), hkv,
+                                 torch.zeros(batch + 1, hq, 128, device="cuda"), ws)
+    del kp, vp, out, ws
+    torch.cuda.empty_cache()
