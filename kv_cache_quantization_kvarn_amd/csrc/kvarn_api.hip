@@ -220,6 +220,8 @@ kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool
   if (n_blocks == 0 || (!k_out && !v_out)) return KVARN_OK;
   if (!pages || (k_out && !k_pool) || (v_out && !v_pool)) return fail(KVARN_ERR_NULL, "a tensor pointer is NULL");
   if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
+  // one workgroup per (block, KV head, K or V): the grid and the kernel's tile index are 32-bit
+  if (static_cast<long>(n_blocks) * num_kv_heads * 2 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "too many tiles");
   return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, cfg->k_bits,
                                                 cfg->v_bits, cfg->group_size, k_out, v_out, dev_flags,
                                                 static_cast<hipStream_t>(stream)));

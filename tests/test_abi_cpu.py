@@ -208,3 +208,74 @@ def test_tail_accounting_adds_one_k_and_one_v_row_per_tail_token():
     # 5 sequences with tails of 1..5 tokens, 8 KV heads: fp16 rows of 128 channels for K and for V
     tail = accounting.tail_decode_bytes(640, 8, 5, 32, 9728, 5632, 1 + 2 + 3 + 4 + 5)
     assert tail - base == 15 * 8 * (128 * 2) * 2
+
+
+def test_dequantize_validation():
+    cfg = K.kvarn_config_parse()
+
+    def dq(kp=FAKE, vp=FAKE, npages=4, pages=FAKE, n=1, h=8, ko=FAKE, vo=FAKE):
+        return K.library().kvarn_dequantize_blocks(ctypes.byref(cfg), kp, vp, npages, pages, n, h, ko, vo, None, None)
+
+    assert dq(n=-1) == K.KVARN_ERR_SHAPE
+    assert dq(h=0) == K.KVARN_ERR_SHAPE
+    assert dq(n=0) == K.KVARN_OK
+    assert dq(ko=None, vo=None) == K.KVARN_OK  # nothing requested
+    assert dq(pages=None) == K.KVARN_ERR_NULL
+    assert dq(kp=None) == K.KVARN_ERR_NULL
+    assert dq(npages=0) == K.KVARN_ERR_SHAPE
+    # 2 * n_blocks * Hkv tiles must fit the 32-bit grid and tile index
+    assert dq(n=1 << 20, h=1 << 10) == K.KVARN_ERR_SHAPE
+    assert "too many tiles" in K.library().kvarn_last_error().decode()
+
+
+def test_binding_rejects_what_the_abi_would_misread():
+    """The Python binding checks dtype, shape, layout and device before any C call (host tensors
+    here: every rule but the device one fires first, and the device rule fires last)."""
+    import torch
+    cfg = K.kvarn_config_parse()
+    kb, vb = K.kvarn_page_bytes(cfg, False), K.kvarn_page_bytes(cfg, True)
+    k = torch.zeros(256, 2, 128, dtype=torch.float16)
+    pages = torch.zeros(2, dtype=torch.int32)
+    kp = torch.zeros(4, 2, kb, dtype=torch.uint8)
+    vp = torch.zeros(4, 2, vb, dtype=torch.uint8)
+
+    def bad(fn, *a, match):
+        with pytest.raises(ValueError, match=match):
+            fn(*a)
+
+    bad(K.kvarn_quantize_blocks, cfg, k[:200], k[:200], pages, kp, vp, match="whole number of 128-token blocks")
+    bad(K.kvarn_quantize_blocks, cfg, k.float(), k, pages, kp, vp, match="k must be torch.float16")
+    bad(K.kvarn_quantize_blocks, cfg, k, k[:128], pages, kp, vp, match="v must have shape")
+    bad(K.kvarn_quantize_blocks, cfg, k, k, pages[:1], kp, vp, match="dst_pages must have shape")
+    bad(K.kvarn_quantize_blocks, cfg, k, k, pages.long(), kp, vp, match="dst_pages must be torch.int32")
+    bad(K.kvarn_quantize_blocks, cfg, k, k, pages, kp[:, :1], vp, match="k_pool must have shape")
+    bad(K.kvarn_quantize_blocks, cfg, k, k, pages, kp, vp[:3], match="v_pool must have shape")
+    bad(K.kvarn_quantize_blocks, cfg, k, k.transpose(0, 1).contiguous().transpose(0, 1), pages, kp, vp,
+        match="v must be contiguous")
+    bad(K.kvarn_quantize_blocks, cfg, k, k, pages, kp, vp, match="k must be in GPU memory")
+
+    q = torch.zeros(3, 8, 128, dtype=torch.float16)
+    bt = torch.zeros(3, 5, dtype=torch.int32)
+    sl = torch.zeros(3, dtype=torch.int32)
+    out = torch.zeros(3, 8, 128, dtype=torch.float32)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    bad(K.kvarn_decode_attention, cfg, q, kp, vp, bt, sl, 3, out, ws, match="not a multiple")
+    bad(K.kvarn_decode_attention, cfg, q, kp, vp, bt[:2], sl, 2, out, ws, match="block_table must have shape")
+    bad(K.kvarn_decode_attention, cfg, q, kp, vp, bt, sl, 2, out.half(), ws, match="out must be torch.float32")
+    bad(K.kvarn_decode_attention, cfg, q, kp, vp, bt, sl, 4, out, ws, match="k_pool must have shape")
+    bad(K.kvarn_decode_attention, cfg, q, kp, vp, bt, sl, 2, out, ws, match="q must be in GPU memory")
+    tail = torch.zeros(3, 128, 2, 128, dtype=torch.float16)
+    bad(K.kvarn_decode_attention_tail, cfg, q, kp, vp, bt, sl, tail[:, :64], tail, 2, out, ws,
+        match="k_tail must have shape")
+    kc = torch.zeros(4, 2, 128, 128, dtype=torch.float16)
+    bad(K.kvarn_fp16_decode_attention, cfg, q, kc, kc[:, :1], bt, sl, 2, out, ws, match="v_cache must have shape")
+    ko = torch.zeros(256, 2, 128, dtype=torch.float32)
+    bad(K.kvarn_dequantize_blocks, cfg, kp, vp, pages, ko[:128], None, match="k_out must have shape")
+    bad(K.kvarn_dequantize_blocks, cfg, kp, vp, pages, None, None, match="at least one")
+    qp = torch.zeros(3, 16, 8, 128, dtype=torch.float16)
+    kn = torch.zeros(3, 32, 2, 128, dtype=torch.float16)
+    outp = torch.zeros(3, 16, 8, 128, dtype=torch.float32)
+    bad(K.kvarn_prefill_attention, cfg, qp, kp, vp, bt, sl, kn, kn[:, :16], sl, sl, 2, outp,
+        match="v_new must have shape")
+    bad(K.kvarn_prefill_attention, cfg, qp, kp, vp, bt, sl, kn, kn, sl, sl, 2, outp[:, :8],
+        match="out must have shape")

@@ -3,7 +3,7 @@
 Reading: each group of the group-128 format splits into two halves of 64 consecutive elements (keys: one
 channel over tokens 64h .. 64h+63; values: one token over channels 64h .. 64h+63) with their own fp16
 scale and zero, stored half-major.  Bars as for group 128: codes within one level (mismatch fraction
-<= 1e-4), scale / zero within one fp16 ulp, normalisers 2e-5, dequantised values max-abs 2e-3.
+<= 1e-4), scale / zero within one fp16 ulp, normalisers 1e-5, dequantised values max-abs 2e-3.
 """
 import numpy as np
 import pytest

@@ -13,6 +13,9 @@ import kvarn_check as chk
 
 pytestmark = pytest.mark.gpu
 
+# Largest difference allowed between two split plans of the same decode (see the test below).
+SPLIT_PLAN_TOL = 2.5e-5
+
 
 def say(msg):
     print(msg, flush=True)
@@ -212,10 +215,12 @@ def test_decode_split_invariance_and_determinism(K, cfg):
     padded[0, :8] = pm.block_table[0, :8]
     c, _ = gpu_decode(K, cfg, q, kp, vp, padded, pm.seq_lens, w.hkv)  # a different pages-per-split plan
     # another plan changes the running maxima, hence the fp16 hi+lo split of the softmax weights
-    # (about 2^-20 relative each) and the fp32 summation order: differences stay near 1e-5
+    # (about 2^-20 relative each) and the fp32 summation order.  The kernels are deterministic, so
+    # the difference is a fixed number for this input and build: 1.33e-5, measured on MI355X.  The bar
+    # is below twice that, so a change to the merge or the rescaling that adds error shows up here.
     diff = float((a - c).abs().max())
     say("  split-plan difference %.3e" % diff)
-    assert diff <= 1e-4
+    assert diff <= SPLIT_PLAN_TOL
 
 
 def test_custom_softmax_scale(K, cfg):
