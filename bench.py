@@ -3,9 +3,12 @@
 One step = one pass of the whole path over one batch of synthetic input:
 quantise every 128-token block of K and V of the workload into packed pages,
 then one decode-attention step of every sequence over the packed cache.  The
-default workload is one Llama-3-8B-shaped layer (16 sequences x 8192 tokens,
-32 query / 8 KV heads, head_dim 128).  Inputs are resident in HBM before the
-timed region starts.
+default (headline) workload is the largest single-GPU step: a Qwen2.5-1.5B-shaped
+model, 28 layers of 64 sequences x 4096 tokens, 12 query / 2 KV heads,
+head_dim 128 (28 quantise and 28 decode launches per step).  The other workloads
+(tiny, one Llama-3-8B layer, one 131,072-token sequence, the paged mix of 128
+sequences) are timed the same way and reported in the same line under
+"configs".  Inputs are resident in HBM before the timed region starts.
 
 Prints one JSON line (rank 0).  Throughput is algorithmic bytes / time:
   quantize: 65536 B of fp16 in + 15360 B of pages out per (block, KV head)
@@ -21,6 +24,8 @@ import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -78,9 +83,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama3_8b_layer_16x8192")
+    ap.add_argument("--workload", default="qwen25_1p5b_28layer_64x4096",
+                    help="the headline workload (the largest single-GPU step by default)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload summaries of the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle time for each of the two CPU-baseline legs (one thread, all cores)")
     ap.add_argument("--flush-reps", type=int, default=20, help="decode-only repetitions after a cache flush")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill measurement")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay of the step")
@@ -159,50 +168,72 @@ class Case:
         self.K.kvarn_decode_attention(self.cfg, L["q"], L["kp"], L["vp"], self.bt, self.sl, self.w.hkv, self.out,
                                       self.ws, dev_flags=self.flags)
 
+    def step(self, stream, events=None):
+        """One step: quantise every layer, then one decode step of every layer.  `events[layer]` holds
+        four timing events recorded around that layer's quantise and decode launches."""
+        for li, L in enumerate(self.layers):
+            if events is not None:
+                events[li][0].record(stream)
+            self.quantize(L)
+            if events is not None:
+                events[li][1].record(stream)
+        for li, L in enumerate(self.layers):
+            if events is not None:
+                events[li][2].record(stream)
+            self.decode(L)
+            if events is not None:
+                events[li][3].record(stream)
 
-def _oracle_run(wname, seconds, part=0):
-    """The oracle on a bounded sample of one workload for about `seconds` of one thread: quantised
-    (block, KV head) tiles (K and V) for half the time, whole decodes of one sequence's KV head for
-    the other half.  Returns (tiles, quantise seconds, decodes, decode seconds, blocks per sequence)."""
-    import numpy as np
+
+def time_steps(case, stream, steps, warmup):
+    """Warm-up steps, then `steps` timed steps bracketed by device synchronisation.  Returns the wall
+    time of the timed steps and the average quantise and decode launch times (HIP events)."""
     import torch
-    from threadpoolctl import threadpool_limits
+    for _ in range(warmup):
+        case.step(stream)
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in case.layers] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        case.step(stream, evs[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert case.K.kvarn_read_flags(case.flags) == 0, "device flags set during the benchmark"
+    q_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    d_ms = [e[2].elapsed_time(e[3]) for st in evs for e in st]
+    return elapsed, sum(q_ms) / len(q_ms) / 1e3, sum(d_ms) / len(d_ms) / 1e3
 
+
+def config_summary(K, cfg, name, stream, steps, warmup, reps, flush, sink):
+    """Step rate, per-launch quantise and decode rates and the cache-flushed decode of one workload."""
+    import torch
+    from kv_cache_quantization_kvarn_amd import accounting as acc
     from kv_cache_quantization_kvarn_amd import synth
-    from oracle import kvarn_oracle as o
-
-    torch.set_num_threads(1)
-    w = synth.WORKLOADS[wname]
-    k, v = synth.layer_kv(w, 0, 4 * 128, "cpu")
-    kh, vh = k.numpy(), v.numpy()
-    pm = synth.make_page_map(w)
-    nb_seq = int(pm.seq_lens[0]) // 128
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        nq = 0
-        while time.perf_counter() - t0 < seconds / 2 or nq < 4:
-            b, h = (nq + part) % 4, ((nq + part) // 4) % w.hkv
-            sl = slice(128 * b, 128 * b + 128)
-            o.encode_page(o.quantize_tile(kh[sl, h], False), False)
-            o.encode_page(o.quantize_tile(vh[sl, h], True), True)
-            nq += 1
-        tq = time.perf_counter() - t0
-        kp = np.zeros((4, 1, o.K_PAGE_BYTES), np.uint8)
-        vp = np.zeros((4, 1, o.V_PAGE_BYTES), np.uint8)
-        o.quantize_blocks(kh[:, :1], vh[:, :1], np.arange(4), kp, vp)
-        blocks = np.arange(nb_seq) % 4  # the sequence's length, pages recycled from the sample
-        q = np.random.default_rng(part).standard_normal((1, w.gqa, 128)).astype(np.float16)
-        t0 = time.perf_counter()
-        nd = 0
-        while time.perf_counter() - t0 < seconds / 2 or nd < 1:
-            o.decode(q, kp, vp, blocks[None, :], np.array([nb_seq * 128]), 1)
-            nd += 1
-        td = time.perf_counter() - t0
-    return nq, tq, nd, td, nb_seq
-
-
-def _oracle_part(args):
-    return _oracle_run(*args)
+    w = synth.WORKLOADS[name]
+    case = Case(K, w, cfg)
+    elapsed, q_s, d_s = time_steps(case, stream, steps, warmup)
+    d_flush = timed_after_flush(lambda: case.decode(case.layers[0]), reps, stream, flush, sink)
+    step_bytes = case.q_bytes + case.d_bytes
+    pk = lambda gbps: round(gbps / acc.HBM_PEAK_GBPS, 4)
+    qg, dg, fg = case.q_bytes_launch / q_s / 1e9, case.d_bytes_launch / d_s / 1e9, case.d_bytes_launch / d_flush / 1e9
+    res = {"ms_per_step": round(elapsed / steps * 1e3, 4), "value": round(step_bytes / (elapsed / steps) / 1e9, 1),
+           "layers": w.layers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+           "seq_len": w.seq_len or list(w.seq_len_range),
+           "quantize": {"us_per_launch": round(q_s * 1e6, 2), "gbps": round(qg, 1), "frac": pk(qg),
+                        "bytes_per_launch": case.q_bytes_launch,
+                        "tokens_per_s": round(case.q_tokens / (q_s * w.layers), 1)},
+           "decode": {"us_per_launch": round(d_s * 1e6, 2), "gbps": round(dg, 1), "frac": pk(dg),
+                      "bytes_per_launch": case.d_bytes_launch, "tokens_per_s": round(w.batch / (d_s * w.layers), 1),
+                      "context_tokens_per_s": round(case.ctx_tokens / d_s, 1),
+                      "after_cache_flush": {"us_median": round(d_flush * 1e6, 2), "gbps": round(fg, 1),
+                                            "frac": pk(fg)}},
+           "steps": steps}
+    if w.append_blocks:
+        res["quantize"]["what"] = "append: one 128-token block per sequence, into pages of a permuted pool"
+    del case
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_model():
@@ -216,46 +247,67 @@ def cpu_model():
     return "unknown"
 
 
+def _oracle_pass(C, acc, w, kh, vh, blocks, kp, vp, q, bt, sl, seconds, threads, qblocks_per_call):
+    """Repeated C++-oracle quantise calls (qblocks_per_call blocks of every KV head, K and V) for half of
+    `seconds`, then repeated whole decode calls over `bt` for the other half.  Returns bytes and times."""
+    kb, vb = kp.shape[2], vp.shape[2]
+    t0 = time.perf_counter()
+    nq = 0
+    while time.perf_counter() - t0 < seconds / 2 or nq < 1:
+        lo = (nq * qblocks_per_call) % (blocks - qblocks_per_call + 1)
+        C.quantize_blocks(kh[128 * lo:128 * (lo + qblocks_per_call)], vh[128 * lo:128 * (lo + qblocks_per_call)],
+                          np.arange(qblocks_per_call, dtype=np.int32), kp, vp, threads=threads)
+        nq += 1
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    nd = 0
+    while time.perf_counter() - t0 < seconds / 2 or nd < 1:
+        C.decode(q, kp, vp, bt, sl, w.hkv, threads=threads)
+        nd += 1
+    td = time.perf_counter() - t0
+    qbytes = nq * acc.quantize_bytes(qblocks_per_call, w.hkv, kb, vb)
+    attended = int(sl.sum()) // 128
+    dbytes = nd * acc.decode_bytes(attended, w.hkv, q.shape[0], w.hq, kb, vb)
+    return qbytes, tq, dbytes, td, nq, nd
+
+
 def cpu_baseline(w, seconds):
-    """The oracle on a bounded sample of the same workload in the same GB/s units: one thread, then one
-    single-threaded process per available core (at most 16) on slices of the same sample.  Runs before
-    the process touches the GPU (the worker processes are forked)."""
-    import multiprocessing
+    """The C++ oracle (double precision, FWHT mode, the one the parity tests use at full size) on a
+    bounded sample of the same workload, in the same GB/s units: one thread, then one thread per
+    available core (at most 16).  The sample: layer 0's first blocks quantised (K and V of every KV
+    head), and decode steps of sequences of the workload's length over those pages."""
+    from kv_cache_quantization_kvarn_amd import accounting as acc
+    from kv_cache_quantization_kvarn_amd import synth
+    from oracle import kvarn_oracle_cpp as C
 
-    def rates(nq, tq, nd, td, nb_seq):
-        qb = nq * (65536 + 15360)
-        db = nd * (nb_seq * 15360 + w.gqa * 768 + nb_seq * 4)
-        return qb, db
-
-    nq, tq, nd, td, nb_seq = _oracle_run(w.name, seconds)
-    qb, db = rates(nq, tq, nd, td, nb_seq)
-    res = {
-        "value": round((qb + db) / (tq + td) / 1e9, 6),
-        "unit": "GB/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": ("%d (block, KV head) pairs quantized (K and V tiles) + %d decode(s) of %d query heads over one "
-                   "%d-block sequence of one KV head; fp64 numpy oracle, 1 thread" % (nq, nd, w.gqa, nb_seq)),
-        "quantize_gbps": round(qb / tq / 1e9, 6),
-        "decode_gbps": round(db / td / 1e9, 6),
-        "cpu_model": cpu_model(),
-    }
     try:
         avail = len(os.sched_getaffinity(0))
     except AttributeError:
         avail = os.cpu_count() or 1
     n = max(1, min(16, avail))
-    if n > 1:
-        ctx = multiprocessing.get_context("fork")
-        t0 = time.perf_counter()
-        with ctx.Pool(n) as pool:
-            parts = pool.map(_oracle_part, [(w.name, seconds / 2, i) for i in range(n)])
-        wall = time.perf_counter() - t0
-        qb = sum(rates(*r)[0] for r in parts)
-        db = sum(rates(*r)[1] for r in parts)
-        # every process spends half its time on each kind: the aggregate rate is bytes over wall time
-        res["all_cores"] = {"value": round((qb + db) / wall / 1e9, 6), "cores": n,
-                            "sample": "%d single-threaded processes, each the sample above for half the time" % n}
+    pm = synth.make_page_map(w)
+    nb_seq = int(pm.seq_lens[0]) // 128
+    blocks = 16 * n
+    k, v = synth.layer_kv(w, 0, blocks * 128, "cpu")
+    kh, vh = k.numpy(), v.numpy()
+    kp = np.zeros((blocks, w.hkv, 9728), np.uint8)
+    vp = np.zeros((blocks, w.hkv, 5632), np.uint8)
+    C.quantize_blocks(kh, vh, np.arange(blocks, dtype=np.int32), kp, vp)
+    res = {"unit": "GB/s", "kind": "oracle", "cpu_model": cpu_model()}
+    for threads, key in ((1, "one_thread"), (n, "all_cores")):
+        seqs = threads  # one sequence per thread per decode call
+        bt = (np.arange(seqs * nb_seq, dtype=np.int32) % blocks).reshape(seqs, nb_seq)
+        sl = np.full(seqs, nb_seq * 128, np.int32)
+        q = synth.make_q(w, 0, "cpu").numpy()[:1].repeat(seqs, axis=0)
+        qb, tq, db, td, nq, nd = _oracle_pass(C, acc, w, kh, vh, blocks, kp, vp, q, bt, sl, seconds, threads,
+                                              max(1, threads))
+        res[key] = {"value": round((qb + db) / (tq + td) / 1e9, 6), "cores": threads,
+                    "quantize_gbps": round(qb / tq / 1e9, 6), "decode_gbps": round(db / td / 1e9, 6),
+                    "sample": "%d quantise calls of %d block(s) x %d KV heads (K and V) + %d decode calls of %d "
+                              "sequence(s) x %d query heads over %d blocks each; C++ oracle, %d thread(s)"
+                              % (nq, max(1, threads), w.hkv, nd, seqs, w.hq, nb_seq, threads)}
+    top = res["all_cores"]
+    res.update(value=top["value"], cores=top["cores"], sample=top["sample"])
     return res
 
 
@@ -435,8 +487,7 @@ def main():
     from kv_cache_quantization_kvarn_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    # the oracle baseline runs first: its worker processes are forked, which must happen before the
-    # process loads the HIP library or touches the GPU
+    # the oracle baseline runs first, before the GPU work (it uses the host's cores only)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     from kv_cache_quantization_kvarn_amd import kvarn as K
 
@@ -444,35 +495,10 @@ def main():
     case = Case(K, w, cfg)
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for li, L in enumerate(case.layers):
-            if events is not None:
-                events[li][0].record(stream)
-            case.quantize(L)
-            if events is not None:
-                events[li][1].record(stream)
-        for li, L in enumerate(case.layers):
-            if events is not None:
-                events[li][2].record(stream)
-            case.decode(L)
-            if events is not None:
-                events[li][3].record(stream)
+    def step():
+        case.step(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in case.layers] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(evs[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    assert K.kvarn_read_flags(case.flags) == 0, "device flags set during the benchmark"
-    q_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    d_ms = [e[2].elapsed_time(e[3]) for st in evs for e in st]
-    q_avg_s = sum(q_ms) / len(q_ms) / 1e3
-    d_avg_s = sum(d_ms) / len(d_ms) / 1e3
+    elapsed, q_avg_s, d_avg_s = time_steps(case, stream, args.steps, args.warmup)
 
     # the same step captured once in a HIP graph and replayed (one launch of the whole step; for the
     # 28-layer workload that is 56 kernels)
@@ -524,6 +550,15 @@ def main():
         prefill["group64"] = {"format": "kvarn_k4v2_g64", "us_median": g64["us_median"], "tflops": g64["tflops"],
                               "frac": g64["roofline"]["frac"]}
 
+    # the other workloads, each timed like the headline step (a summary object per workload)
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for name in synth.WORKLOADS:
+            if name != w.name:
+                configs[name] = config_summary(K, cfg, name, stream, args.steps, args.warmup, args.flush_reps, flush,
+                                               flush_sink)
+
     step_bytes = case.q_bytes + case.d_bytes
     ms_per_step = elapsed / args.steps * 1e3
     value = step_bytes / (elapsed / args.steps) / 1e9
@@ -572,15 +607,22 @@ def main():
         line["prefill"] = prefill
     if formats is not None:
         line["formats"] = formats
+    if configs is not None:
+        line["configs"] = configs
     # dominant kernel by time: the one whose launches take longer in the step
     if q_avg_s >= d_avg_s:
         dom, ach = "quantize_kernel", q_gbps
     else:
         dom, ach = "decode_kernel", d_gbps
     traffic = measured_traffic(dom, w.name)
+    units = case.layers[0]["dst"].numel() * w.hkv if dom == "quantize_kernel" else int(case.pm.seq_lens.sum()) // 128 * w.hkv
     line["roofline"] = {"kernel": "kvarn " + dom, "bound": "hbm", "achieved": round(ach, 1), "peak": acc.HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(ach / acc.HBM_PEAK_GBPS, 4), "traffic": traffic,
-                        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
+                        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                        "algorithmic_bytes_per_launch": case.q_bytes_launch if dom == "quantize_kernel" else case.d_bytes_launch,
+                        "units_per_launch": units,
+                        "unit_of_work": "(128-token block, KV head)",
+                        "us_per_launch": round((q_avg_s if dom == "quantize_kernel" else d_avg_s) * 1e6, 2)}
     valu = measured_traffic(dom, w.name, MEASURED_VALU)
     if valu is not None:
         # the same launches seen as ALU work: VALU lane operations issued per second (wave64 -> 64 lanes)

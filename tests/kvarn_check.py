@@ -99,3 +99,62 @@ def compare_tile(stats: TileStats, x16: np.ndarray, page_bytes: bytes, is_v: boo
             else:
                 cond[seg, gi] = o.rtn_codes(n32[seg, gi], gs[h, gi], gz[h, gi], levels)
     stats.cond_mismatch += int((cond != got["codes"]).sum())
+
+
+# ------------------------------------------------------------------ whole pools (vectorised)
+def unpack_codes(pool: np.ndarray, is_v: bool, bits: int, head_dim: int = 128) -> np.ndarray:
+    """Codes [..., 128 tokens, head_dim channels] of every page in a pool [..., page_bytes]."""
+    d = head_dim
+    lead = pool.shape[:-1]
+    if not is_v:
+        if bits == 8:
+            return pool[..., :128 * d].reshape(lead + (128, d))
+        b = pool[..., :64 * d].reshape(lead + (128, d // 2))
+        return np.stack([b & 15, b >> 4], axis=-1).reshape(lead + (128, d))
+    per = 8 // bits
+    b = pool[..., :d * 128 // per].reshape(lead + (d, 128 // per))
+    parts = [(b >> (bits * i)) & ((1 << bits) - 1) for i in range(per)]  # token per*k + i
+    return np.swapaxes(np.stack(parts, axis=-1).reshape(lead + (d, 128)), -1, -2)
+
+
+def meta_views(pool: np.ndarray, is_v: bool, bits: int, group: int, head_dim: int = 128):
+    """(scale, zero, rho, gamma) arrays of every page of a pool, from the page layout."""
+    d = head_dim
+    code = 128 * d * bits // 8
+    n = (d // min(group, d)) * 128 if is_v else (128 // group) * d
+    meta = np.ascontiguousarray(pool[..., code:])
+    scale = meta[..., :2 * n].view("<f2")
+    zero = meta[..., 2 * n:4 * n].view("<f2")
+    rho = meta[..., 4 * n:4 * n + 512].view("<f4")
+    gam = meta[..., 4 * n + 512:4 * n + 512 + 4 * d].view("<f4")
+    return scale, zero, rho, gam
+
+
+def compare_pools(stats: TileStats, got: np.ndarray, ref: np.ndarray, is_v: bool, bits: int, group: int,
+                  head_dim: int = 128) -> None:
+    """Compare pages the GPU wrote with the oracle's pages for the same inputs, many pages at once.
+
+    got, ref: uint8 [..., page_bytes] holding the same (block, head) units in the same order."""
+    assert got.shape == ref.shape
+    n_pages = int(np.prod(got.shape[:-1]))
+    flat_g = got.reshape(n_pages, got.shape[-1])
+    flat_r = ref.reshape(n_pages, ref.shape[-1])
+    chunk = 512
+    for a in range(0, n_pages, chunk):
+        g, r = flat_g[a:a + chunk], flat_r[a:a + chunk]
+        diff = np.abs(unpack_codes(g, is_v, bits, head_dim).astype(np.int16)
+                      - unpack_codes(r, is_v, bits, head_dim).astype(np.int16))
+        stats.codes += diff.size
+        stats.code_mismatch += int(np.count_nonzero(diff))
+        stats.code_maxdiff = max(stats.code_maxdiff, int(diff.max()))
+        mg, mr = meta_views(g, is_v, bits, group, head_dim), meta_views(r, is_v, bits, group, head_dim)
+        for x, y in zip(mg[:2], mr[:2]):
+            d = f16_ulp_distance(x, y)
+            stats.sz_exact += int((d == 0).sum())
+            stats.sz_maxulp = max(stats.sz_maxulp, int(d.max()))
+        stats.groups += mr[0].size
+        for x, y in zip(mg[2:], mr[2:]):
+            x64, y64 = x.astype(np.float64), y.astype(np.float64)
+            err = np.abs(x64 - y64) / np.maximum(1.0, np.abs(y64))
+            stats.norm_maxerr = max(stats.norm_maxerr, float(err.max()))
+        stats.tiles += g.shape[0]

@@ -9,6 +9,7 @@ import torch
 
 from kv_cache_quantization_kvarn_amd import synth
 from oracle import kvarn_oracle as o
+from oracle import kvarn_oracle_cpp as C
 import kvarn_check as chk
 
 pytestmark = pytest.mark.gpu
@@ -320,13 +321,47 @@ def test_empty_calls(K, cfg):
 
 
 # ------------------------------------------------------------- full sizes
+# Whole-workload parity against the C++ oracle (same readings as the Python oracle, pinned to it page
+# by page in test_oracle_cpp.py, and fast enough to redo every tile and every decode row); a few tiles
+# per case also go through the Python oracle with its rounding-decision check.
 def sample_pairs(rng, batch, hq, n):
     return sorted({(int(rng.integers(batch)), int(rng.integers(hq))) for _ in range(n)})
 
 
+def compare_pools_full(kph, vph, kpo, vpo, label):
+    stats = chk.TileStats()
+    chk.compare_pools(stats, kph, kpo, False, 4, 128)
+    chk.compare_pools(stats, vph, vpo, True, 2, 128)
+    say("  %s vs C++ oracle: %s" % (label, stats.summary()))
+    stats.check()
+    return stats
+
+
+def compare_decode_full(out, q_host, kph, vph, bt, sl, hkv, pairs=None, label="decode"):
+    ref = C.decode(q_host, kph, vph, bt, sl, hkv, pairs=pairs)
+    got = out.astype(np.float64)
+    mask = ~np.isnan(ref)
+    worst = float(np.abs(got[mask] - ref[mask]).max())
+    rows = int(mask[..., 0].sum())
+    say("  %s max-abs diff vs C++ oracle on the same pages: %.3e over %d (seq, head) rows" % (label, worst, rows))
+    assert worst <= chk.ATTN_TOL
+    return worst
+
+
+def python_oracle_tiles(k_host, v_host, kph, vph, pages, tiles):
+    """A few tiles through the Python oracle, with the rounding-decision-only check."""
+    stats = chk.TileStats()
+    for b, h in tiles:
+        p = int(pages[b])
+        chk.compare_tile(stats, k_host[b][:, h], kph[p, h].tobytes(), False)
+        chk.compare_tile(stats, v_host[b][:, h], vph[p, h].tobytes(), True)
+    say("  Python oracle, %d tiles: %s" % (2 * len(tiles), stats.summary()))
+    stats.check()
+
+
 def test_llama3_layer_full_size(K, cfg):
     w = synth.WORKLOADS["llama3_8b_layer_16x8192"]
-    say("case: %s full size: quantize 1024 blocks x 8 heads, decode 16 x 32 heads; sampled vs oracle" % w.name)
+    say("case: %s full size: all 16,384 tiles and all 512 (seq, head) decode rows vs the C++ oracle" % w.name)
     pm = synth.make_page_map(w)
     k, v = synth.layer_kv(w, 0, 16 * 8192, "cuda")
     q = synth.make_q(w, 0, "cuda")
@@ -334,26 +369,21 @@ def test_llama3_layer_full_size(K, cfg):
     assert fl == 0
     out, fl = gpu_decode(K, cfg, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv)
     assert fl == 0
-    assert torch.isfinite(out).all()
-    rng = np.random.default_rng(11)
-    tiles = [(int(rng.integers(1024)), int(rng.integers(8))) for _ in range(24)]
-    kh = {b: k[128 * b:128 * b + 128].cpu().numpy() for b, _ in tiles}
-    vh = {b: v[128 * b:128 * b + 128].cpu().numpy() for b, _ in tiles}
+    kh, vh, qh = k.cpu().numpy(), v.cpu().numpy(), q.cpu().numpy()
     kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
-    stats = chk.TileStats()
-    for b, h in tiles:
-        p = int(pm.prefix_pages[b])
-        chk.compare_tile(stats, kh[b][:, h], kph[p, h].tobytes(), False)
-        chk.compare_tile(stats, vh[b][:, h], vph[p, h].tobytes(), True)
-    say("  " + stats.summary())
-    stats.check()
-    compare_decode(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(), w.hkv,
-                   sample_pairs(rng, 16, 32, 6))
+    kpo, vpo = np.zeros_like(kph), np.zeros_like(vph)
+    assert C.quantize_blocks(kh, vh, pm.prefix_pages.numpy(), kpo, vpo) == 0
+    compare_pools_full(kph, vph, kpo, vpo, "every tile")
+    compare_decode_full(out.cpu().numpy(), qh, kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(), w.hkv)
+    rng = np.random.default_rng(11)
+    tiles = [(int(rng.integers(1024)), int(rng.integers(8))) for _ in range(6)]
+    python_oracle_tiles({b: kh[128 * b:128 * b + 128] for b, _ in tiles},
+                        {b: vh[128 * b:128 * b + 128] for b, _ in tiles}, kph, vph, pm.prefix_pages, tiles)
 
 
 def test_long_context_full_size(K, cfg):
     w = synth.WORKLOADS["long_context_1x131072"]
-    say("case: %s full size: 1024 blocks per head, split-K decode; one KV head vs oracle" % w.name)
+    say("case: %s full size: all 16,384 tiles, split-K decode of all 32 heads vs the C++ oracle" % w.name)
     pm = synth.make_page_map(w)
     k, v = synth.layer_kv(w, 0, 131072, "cuda")
     q = synth.make_q(w, 0, "cuda")
@@ -361,52 +391,62 @@ def test_long_context_full_size(K, cfg):
     assert fl == 0
     out, fl = gpu_decode(K, cfg, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv)
     assert fl == 0
-    rng = np.random.default_rng(12)
-    tiles = [(int(rng.integers(1024)), int(rng.integers(8))) for _ in range(12)]
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
     kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
-    stats = chk.TileStats()
-    for b, h in tiles:
-        p = int(pm.prefix_pages[b])
-        chk.compare_tile(stats, k[128 * b:128 * b + 128, h].cpu().numpy(), kph[p, h].tobytes(), False)
-        chk.compare_tile(stats, v[128 * b:128 * b + 128, h].cpu().numpy(), vph[p, h].tobytes(), True)
-    say("  " + stats.summary())
-    stats.check()
-    kvh = int(rng.integers(8))
-    compare_decode(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(), w.hkv,
-                   [(0, 4 * kvh + j) for j in range(4)])
+    kpo, vpo = np.zeros_like(kph), np.zeros_like(vph)
+    assert C.quantize_blocks(kh, vh, pm.prefix_pages.numpy(), kpo, vpo) == 0
+    compare_pools_full(kph, vph, kpo, vpo, "every tile")
+    compare_decode_full(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(),
+                        w.hkv)
+    rng = np.random.default_rng(12)
+    tiles = [(int(rng.integers(1024)), int(rng.integers(8))) for _ in range(4)]
+    python_oracle_tiles({b: kh[128 * b:128 * b + 128] for b, _ in tiles},
+                        {b: vh[128 * b:128 * b + 128] for b, _ in tiles}, kph, vph, pm.prefix_pages, tiles)
 
 
-def test_qwen_28_layers_sampled_layers(K, cfg):
+def test_qwen_28_layers(K, cfg):
     w = synth.WORKLOADS["qwen25_1p5b_28layer_64x4096"]
     pm = synth.make_page_map(w)
     rng = np.random.default_rng(13)
-    for layer in (0, 27):
-        say("case: %s layer %d full size: quantize 2048 blocks x 2 heads, decode 64 x 12 heads" % (w.name, layer))
+    say("case: %s, all 28 layers: 128 sampled blocks (both heads, K and V) per layer, and all 768 "
+        "(seq, head) decode rows per layer, vs the C++ oracle" % w.name)
+    total = chk.TileStats()
+    worst = 0.0
+    for layer in range(w.layers):
         k, v = synth.layer_kv(w, layer, 64 * 4096, "cuda")
         q = synth.make_q(w, layer, "cuda")
         kp, vp, fl = gpu_quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages)
         assert fl == 0
         out, fl = gpu_decode(K, cfg, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv)
         assert fl == 0
-        tiles = [(int(rng.integers(2048)), int(rng.integers(2))) for _ in range(8)]
+        blocks = np.sort(rng.choice(2048, size=128, replace=False))
+        rows = torch.from_numpy((blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)).cuda()
+        ks, vs = k[rows].cpu().numpy(), v[rows].cpu().numpy()
         kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+        pages = pm.prefix_pages.numpy()[blocks]
+        kpo = np.zeros((128, w.hkv, kph.shape[2]), np.uint8)
+        vpo = np.zeros((128, w.hkv, vph.shape[2]), np.uint8)
+        assert C.quantize_blocks(ks, vs, np.arange(128, dtype=np.int32), kpo, vpo) == 0
         stats = chk.TileStats()
-        for b, h in tiles:
-            p = int(pm.prefix_pages[b])
-            chk.compare_tile(stats, k[128 * b:128 * b + 128, h].cpu().numpy(), kph[p, h].tobytes(), False)
-            chk.compare_tile(stats, v[128 * b:128 * b + 128, h].cpu().numpy(), vph[p, h].tobytes(), True)
-        say("  " + stats.summary())
+        chk.compare_pools(stats, kph[pages], kpo, False, 4, 128)
+        chk.compare_pools(stats, vph[pages], vpo, True, 2, 128)
         stats.check()
-        compare_decode(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(),
-                       w.hkv, sample_pairs(rng, 64, 12, 4))
+        total.merge(stats)
+        ref = C.decode(q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(), w.hkv)
+        d = float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max())
+        worst = max(worst, d)
+        assert d <= chk.ATTN_TOL, "layer %d decode diff %.3e" % (layer, d)
         del k, v, kp, vp
+    say("  all layers, sampled tiles: " + total.summary())
+    say("  all layers, every decode row: max-abs diff %.3e" % worst)
 
 
 def test_paged_mixed_full_size(K, cfg):
     w = synth.WORKLOADS["paged_mixed_128xU1k_32k"]
     pm = synth.make_page_map(w)
     n_prefix = synth.total_prefix_blocks(w)
-    say("case: %s full size: fill %d prefix blocks, append 128 blocks, decode 128 x 64 heads" % (w.name, n_prefix))
+    say("case: %s full size: fill %d prefix blocks, append 128 blocks, decode 128 x 64 heads; every appended "
+        "tile, 2%% of prefix blocks and every decode row vs the C++ oracle" % (w.name, n_prefix))
     k, v = synth.layer_kv(w, 0, n_prefix * 128, "cuda")
     ka, va = synth.layer_kv(w, 0, w.batch * 128, "cuda", append=True)
     kp, vp, fl = gpu_quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages)
@@ -417,16 +457,28 @@ def test_paged_mixed_full_size(K, cfg):
     out, fl = gpu_decode(K, cfg, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv)
     assert fl == 0
     kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
-    # appended blocks vs oracle
-    stats = chk.TileStats()
-    for b in (0, 63, 127):
-        for h in (0, 5):
-            p = int(pm.append_pages[b])
-            chk.compare_tile(stats, ka[128 * b:128 * b + 128, h].cpu().numpy(), kph[p, h].tobytes(), False)
-            chk.compare_tile(stats, va[128 * b:128 * b + 128, h].cpu().numpy(), vph[p, h].tobytes(), True)
-    say("  " + stats.summary())
-    stats.check()
+    # every appended tile
+    kah, vah = ka.cpu().numpy(), va.cpu().numpy()
+    kpo = np.zeros((w.batch, w.hkv, kph.shape[2]), np.uint8)
+    vpo = np.zeros((w.batch, w.hkv, vph.shape[2]), np.uint8)
+    assert C.quantize_blocks(kah, vah, np.arange(w.batch, dtype=np.int32), kpo, vpo) == 0
+    ap = pm.append_pages.numpy()
+    compare_pools_full(kph[ap], vph[ap], kpo, vpo, "every appended tile (%d)" % (2 * w.batch * w.hkv))
+    # 2% of the prefix blocks, every head
+    rng = np.random.default_rng(14)
+    nb = max(1, n_prefix // 50)
+    blocks = np.sort(rng.choice(n_prefix, size=nb, replace=False))
+    rows = torch.from_numpy((blocks[:, None] * 128 + np.arange(128)[None, :]).reshape(-1)).cuda()
+    ks, vs = k[rows].cpu().numpy(), v[rows].cpu().numpy()
+    kpo = np.zeros((nb, w.hkv, kph.shape[2]), np.uint8)
+    vpo = np.zeros((nb, w.hkv, vph.shape[2]), np.uint8)
+    assert C.quantize_blocks(ks, vs, np.arange(nb, dtype=np.int32), kpo, vpo) == 0
+    pp = pm.prefix_pages.numpy()[blocks]
+    compare_pools_full(kph[pp], vph[pp], kpo, vpo, "%d prefix blocks (%d tiles)" % (nb, 2 * nb * w.hkv))
+    del k, v
+    compare_decode_full(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), pm.seq_lens.numpy(),
+                        w.hkv)
     lens = pm.seq_lens.numpy()
-    shortest, longest = int(np.argmin(lens)), int(np.argmax(lens))
-    compare_decode(out.cpu().numpy(), q.cpu().numpy(), kph, vph, pm.block_table.numpy(), lens, w.hkv,
-                   [(shortest, 0), (shortest, 63), (longest, 8), (longest, 17), (50, 40)])
+    python_oracle_tiles({b: kah[128 * b:128 * b + 128] for b in (0, 127)},
+                        {b: vah[128 * b:128 * b + 128] for b in (0, 127)}, kph, vph, ap, [(0, 0), (127, 5)])
+    say("  lengths %d .. %d tokens" % (lens.min(), lens.max()))
