@@ -144,6 +144,25 @@ kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, cons
                                     int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale, float* out,
                                     void* workspace, size_t workspace_bytes, uint32_t* dev_flags, void* stream);
 
+/* kvarn_decode_attention without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  The split
+ * partials and arrival counters live in a fixed scratch array inside the library: 64 MiB per GPU,
+ * held from the first call on that GPU until the process ends (1 MiB of counters, 63 MiB of
+ * partials).  The call allocates nothing and frees nothing.  Same arguments, plan, results (bit for
+ * bit), error model and output as kvarn_decode_attention otherwise.
+ *   Limits: batch * num_kv_heads <= 262144, and the partials of the call's split plan,
+ *   batch * num_kv_heads * splits * 8 * 130 * 4 bytes, at most 63 MiB (every configuration whose
+ *   kvarn_decode_workspace_bytes is at most 64 MiB fits); beyond them the call returns
+ *   KVARN_ERR_WORKSPACE and launches nothing.
+ *   The first call on a GPU clears the counters with a small kernel on `stream`; every call leaves
+ *   them at zero again.  All calls on one GPU share the array: calls that overlap in time on one GPU
+ *   (on different streams or from different threads) race and must not be issued. */
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                            const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                            int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale,
+                                            float* out, uint32_t* dev_flags, void* stream);
+
 /* Decode over the packed pages plus an fp16 tail: the tokens past the last
  * full block stay uncompressed until their block fills (blocks are quantised
  * whole, "KVarN Nasıl Çalışır?").  Same arguments, plan, workspace

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/kvarn.h"
@@ -31,6 +32,21 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
                           int hq, int hkv, int kbits, int vbits, int group, float scale_log2, float* out,
                           uint32_t* flags, hipStream_t stream);
 }  // namespace kvarn
+
+// Scratch memory of the allocation-free decode entry point (kvarn_decode_attention_noalloc): the
+// arrival counters in the first kScratchCounterBytes, the split partials after them.  Each GPU the
+// library runs on holds its own copy for the life of the process.  Host code never uses this name as
+// an address: the per-device address comes from hipGetSymbolAddress (scratch_address below).
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+constexpr size_t kScratchCounterBytes = static_cast<size_t>(1) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Sets n words to zero (a kernel, not a memset, so that a caller may capture it in a HIP graph).
+__global__ void zero_words(uint32_t* __restrict__ p, size_t n) {
+  for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
 
 namespace {
 
@@ -109,7 +125,42 @@ kvarn_status launch_status(hipError_t e) {
   return KVARN_ERR_LAUNCH;
 }
 
+// Device address of `scratch` on the current device, looked up once per device.  The first lookup on a
+// device also clears the counter region with a fill kernel on `stream` (every decode call leaves the
+// counters it used at zero again, so later calls need no clearing).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kvarn_status scratch_address(hipStream_t stream, unsigned char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launch_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVARN_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e);
+      return KVARN_ERR_LAUNCH;
+    }
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+                       kScratchCounterBytes / sizeof(uint32_t));
+    e = hipGetLastError();
+    if (e != hipSuccess) return launch_status(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return KVARN_OK;
+}
+
 enum class DecodeKind { packed, packed_tail, fp16 };
+
+// Partials of one decode call (split results of every (sequence, KV head) under the plan).
+size_t partial_bytes(int batch, int hkv, int max_splits) {
+  return static_cast<size_t>(batch) * hkv * max_splits * kMaxGroup * kPartFloats * sizeof(float);
+}
 
 // Validation and launch shared by the packed decode (with or without an fp16 tail) and the fp16
 // baseline (same plan, workspace, partials and error model; the pools and the kernel differ).
@@ -118,7 +169,7 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
                            int32_t max_blocks_per_seq, const int32_t* seq_lens, const void* k_tail,
                            const void* v_tail, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                            float softmax_scale, float* out, void* workspace, size_t ws_bytes, uint32_t* dev_flags,
-                           void* stream) {
+                           void* stream, bool use_scratch = false) {
   kvarn_status s = check_config(cfg);
   if (s != KVARN_OK) return s;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
@@ -133,9 +184,11 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   if (static_cast<long>(max_blocks_per_seq) * 128 + 127 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "max_blocks too large");
   if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
   const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
-  const size_t need = workspace_bytes(batch, num_kv_heads, mb);
-  if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
-  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (!use_scratch) {
+    const size_t need = workspace_bytes(batch, num_kv_heads, mb);
+    if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
@@ -150,8 +203,24 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   const DecodePlan p = plan_decode(batch, num_kv_heads, mb, tail);
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
   const float scale_log2 = scale * 1.4426950408889634f;
-  uint32_t* counters = static_cast<uint32_t*>(workspace);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(batch, num_kv_heads));
+  uint32_t* counters;
+  float* part;
+  if (use_scratch) {
+    if (static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t) > kScratchCounterBytes)
+      return fail(KVARN_ERR_WORKSPACE, "batch * num_kv_heads above the 262,144 counters of the fixed scratch memory");
+    if (partial_bytes(batch, num_kv_heads, p.max_splits) > kScratchBytes - kScratchCounterBytes)
+      return fail(KVARN_ERR_WORKSPACE,
+                  "the split partials of this call exceed the 63 MiB of fixed scratch memory; use "
+                  "kvarn_decode_attention with a workspace");
+    unsigned char* base = nullptr;
+    s = scratch_address(static_cast<hipStream_t>(stream), &base);
+    if (s != KVARN_OK) return s;
+    counters = reinterpret_cast<uint32_t*>(base);
+    part = reinterpret_cast<float*>(base + kScratchCounterBytes);
+  } else {
+    counters = static_cast<uint32_t*>(workspace);
+    part = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(batch, num_kv_heads));
+  }
   // An empty block table is passed as a harmless non-null pointer; no page is read when max_blocks is 0.
   const int32_t* bt = max_blocks_per_seq > 0 ? block_table : seq_lens;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -253,6 +322,16 @@ kvarn_status kvarn_decode_attention_tail(const kvarn_config* cfg, const void* q,
   return decode_common(DecodeKind::packed_tail, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq,
                        seq_lens, k_tail, v_tail, batch, num_q_heads, num_kv_heads, softmax_scale, out, workspace,
                        ws_bytes, dev_flags, stream);
+}
+
+kvarn_status kvarn_decode_attention_noalloc(const kvarn_config* cfg, const void* q, const void* k_pool,
+                                            const void* v_pool, int32_t num_pages, const int32_t* block_table,
+                                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                            int32_t num_q_heads, int32_t num_kv_heads, float softmax_scale,
+                                            float* out, uint32_t* dev_flags, void* stream) {
+  return decode_common(DecodeKind::packed, cfg, q, k_pool, v_pool, num_pages, block_table, max_blocks_per_seq,
+                       seq_lens, nullptr, nullptr, batch, num_q_heads, num_kv_heads, softmax_scale, out, nullptr, 0,
+                       dev_flags, stream, true);
 }
 
 size_t kvarn_fp16_page_bytes(const kvarn_config* cfg) {

@@ -31,7 +31,8 @@ class kvarn_config(ctypes.Structure):
 
 
 EXPORTS = ("kvarn_config_parse", "kvarn_page_bytes", "kvarn_quantize_blocks", "kvarn_dequantize_blocks",
-           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_decode_attention_tail",
+           "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_decode_attention_noalloc",
+           "kvarn_decode_attention_tail",
            "kvarn_fp16_page_bytes",
            "kvarn_fp16_decode_attention", "kvarn_prefill_attention", "kvarn_read_flags", "kvarn_status_string",
            "kvarn_last_error")
@@ -53,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "kvarn_dequantize_blocks": (I32, [CFG, P, P, I32, P, I32, I32, P, P, P, P]),
         "kvarn_decode_workspace_bytes": (SZ, [CFG, I32, I32, I32, I32]),
         "kvarn_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
+        "kvarn_decode_attention_noalloc": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, P]),
         "kvarn_decode_attention_tail": (I32, [CFG, P, P, P, I32, P, I32, P, P, P, I32, I32, I32, F32, P, P, SZ, P, P]),
         "kvarn_fp16_page_bytes": (SZ, [CFG]),
         "kvarn_fp16_decode_attention": (I32, [CFG, P, P, P, I32, P, I32, P, I32, I32, I32, F32, P, P, SZ, P, P]),
@@ -206,6 +208,23 @@ def kvarn_decode_attention(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                                        num_kv_heads, float(softmax_scale), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(), _ptr(dev_flags),
                                        _stream(stream)))
+
+
+def kvarn_decode_attention_noalloc(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                   block_table: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int,
+                                   out: torch.Tensor, softmax_scale: float = 0.0,
+                                   dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
+    """kvarn_decode_attention with the library's fixed scratch memory instead of a workspace."""
+    _need(q, "q", torch.float16, (None, None, 128))
+    _need_decode(q, block_table, seq_lens, num_kv_heads, out, torch.zeros(0, dtype=torch.uint8), dev_flags)
+    _need_pools(cfg, k_pool, v_pool, num_kv_heads)
+    _on_gpu(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens, out=out,
+            dev_flags=dev_flags)
+    batch, hq = q.shape[0], q.shape[1]
+    _check(_lib.kvarn_decode_attention_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(k_pool), _ptr(v_pool), k_pool.shape[0],
+                                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, hq,
+                                               num_kv_heads, float(softmax_scale), _ptr(out), _ptr(dev_flags),
+                                               _stream(stream)))
 
 
 def kvarn_decode_attention_tail(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
