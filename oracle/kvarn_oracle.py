@@ -74,28 +74,46 @@ K_PAGE_BYTES = K_CODES_BYTES + 2 * 256 + 2 * 512   # 9728
 V_PAGE_BYTES = V_CODES_BYTES + 2 * 256 + 2 * 512   # 5632
 
 
-def meta_bytes(group: int = 128) -> int:
-    """Metadata of one page: scale and zero fp16 per group (128 // group per channel or token), rho and gamma fp32[128]."""
-    return 2 * 2 * 128 * (BLOCK // group) + 2 * 4 * 128
+HEAD_DIMS_ALLOWED = (64, 128, 256)
 
 
-def page_bytes(bits: int, group: int = 128) -> int:
-    """Bytes of one page whose codes have `bits` bits: 128 x 128 codes plus the metadata."""
-    return BLOCK * HEAD_DIM * bits // 8 + meta_bytes(group)
+def value_group_channels(group: int, head_dim: int = HEAD_DIM) -> int:
+    """Channels in one value group: the group size, or the whole token row when the head is narrower."""
+    return min(group, head_dim)
 
 
-def format_of_page(nbytes: int, is_v: bool):
-    """(code width, group size) of a page from its byte count (unambiguous within keys and within values)."""
+def n_groups(group: int, head_dim: int = HEAD_DIM, is_v: bool = False) -> int:
+    """Scale/zero entries of one page: keys have 128 // group groups per channel, values head_dim //
+    value_group_channels groups per token."""
+    if is_v:
+        return (head_dim // value_group_channels(group, head_dim)) * BLOCK
+    return (BLOCK // group) * head_dim
+
+
+def meta_bytes(group: int = 128, head_dim: int = HEAD_DIM, is_v: bool = False) -> int:
+    """Metadata of one page: scale and zero fp16 per group, rho fp32[128 tokens], gamma fp32[head_dim]."""
+    return 2 * 2 * n_groups(group, head_dim, is_v) + 4 * BLOCK + 4 * head_dim
+
+
+def page_bytes(bits: int, group: int = 128, head_dim: int = HEAD_DIM, is_v: bool = False) -> int:
+    """Bytes of one page whose codes have `bits` bits: 128 x head_dim codes plus the metadata."""
+    return BLOCK * head_dim * bits // 8 + meta_bytes(group, head_dim, is_v)
+
+
+def format_of_page(nbytes: int, is_v: bool, head_dim: int = HEAD_DIM):
+    """(code width, group size) of a page from its byte count (unambiguous within keys and within values
+    of one head size)."""
     for b in (V_BITS_ALLOWED if is_v else K_BITS_ALLOWED):
         for gs in GROUPS_ALLOWED:
-            if nbytes == page_bytes(b, gs):
+            if nbytes == page_bytes(b, gs, head_dim, is_v):
                 return b, gs
-    raise ValueError("a %s page of %d bytes matches no format" % ("value" if is_v else "key", nbytes))
+    raise ValueError("a %s page of %d bytes matches no format at head_dim %d"
+                     % ("value" if is_v else "key", nbytes, head_dim))
 
 
-def bits_of_page(nbytes: int, is_v: bool) -> int:
+def bits_of_page(nbytes: int, is_v: bool, head_dim: int = HEAD_DIM) -> int:
     """Code width of a page from its byte count."""
-    return format_of_page(nbytes, is_v)[0]
+    return format_of_page(nbytes, is_v, head_dim)[0]
 
 
 # --------------------------------------------------------------------------
@@ -110,13 +128,22 @@ def hadamard(n: int = HEAD_DIM) -> np.ndarray:
     return h / np.sqrt(n)
 
 
-_H = hadamard()
+_H_BY_SIZE = {}
+
+
+def _h(n: int) -> np.ndarray:
+    if n not in _H_BY_SIZE:
+        _H_BY_SIZE[n] = hadamard(n)
+    return _H_BY_SIZE[n]
+
+
+_H = _h(HEAD_DIM)
 
 
 def rotate(x: np.ndarray) -> np.ndarray:
-    """Rotate every token row of a [tokens, 128] block along channels: R[t] = H @ x[t]."""
+    """Rotate every token row of a [tokens, D] block along its D channels: R[t] = H_D @ x[t]."""
     x = np.asarray(x, dtype=np.float64)
-    return x @ _H.T
+    return x @ _h(x.shape[-1]).T
 
 
 # --------------------------------------------------------------------------
@@ -183,15 +210,16 @@ def rtn_codes(values: np.ndarray, s16, z16, levels: int) -> np.ndarray:
 
 def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = EPS, bits: int = 0,
                   group: int = 128) -> dict:
-    """Quantise one fp16 block [128 tokens, 128 channels] of K (is_v False) or V, codes of
+    """Quantise one fp16 block [128 tokens, D channels] of K (is_v False) or V, codes of
     ``bits`` bits (default: 4 for K, 2 for V; levels 2^bits - 1), groups of ``group`` elements.
 
-    Returns the stored fields: codes [128, 128] (token, channel), scale and zero
-    (fp16, per channel for K, per token for V: shape [128] for group 128, [2, 128]
-    for group 64 with row h the groups over elements 64h .. 64h+63), rho (fp32 per
-    token) and gamma (fp32 per channel).
+    Returns the stored fields: codes [128, D] (token, channel), scale and zero (fp16): for K per
+    channel, shape [D] for group 128 or [2, D] for group 64 (row h: tokens 64h .. 64h+63); for V per
+    token, shape [128] when one group spans the token's channels or [n, 128] (row h: channels
+    gv*h .. gv*h + gv - 1, gv = min(group, D)); rho (fp32 per token) and gamma (fp32 per channel).
     """
     x = np.asarray(x16, dtype=np.float16).astype(np.float64)
+    d = x.shape[1]
     r = rotate(x)
     rho, gam = normalize(r, iters, eps)
     rho32 = rho.astype(np.float32)
@@ -199,13 +227,14 @@ def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = 
     n32 = normalized(r, rho32, gam32).astype(np.float32)
     bits = bits or (2 if is_v else 4)
     levels = (1 << bits) - 1
-    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
-    nseg = BLOCK // group
-    scale = np.zeros((nseg, 128), dtype=np.float16)
-    zero = np.zeros((nseg, 128), dtype=np.float16)
+    codes = np.zeros((BLOCK, d), dtype=np.uint8)
+    span = value_group_channels(group, d) if is_v else group  # elements along the group axis
+    nseg = (d if is_v else BLOCK) // span
+    scale = np.zeros((nseg, BLOCK if is_v else d), dtype=np.float16)
+    zero = np.zeros_like(scale)
     for h in range(nseg):
-        seg = slice(group * h, group * (h + 1))
-        for g in range(128):
+        seg = slice(span * h, span * (h + 1))
+        for g in range(scale.shape[1]):
             if is_v:
                 codes[g, seg], scale[h, g], zero[h, g] = rtn_group(n32[g, seg], levels)
             else:
@@ -216,14 +245,22 @@ def quantize_tile(x16: np.ndarray, is_v: bool, iters: int = ITERS, eps: float = 
 
 
 def group_params(fields: dict, is_v: bool):
-    """Scale and zero of every element's own group, as fp16 arrays [128 tokens, 128 channels]."""
-    s = np.asarray(fields["scale"], dtype=np.float16).reshape(-1, 128)
-    z = np.asarray(fields["zero"], dtype=np.float16).reshape(-1, 128)
-    group = BLOCK // s.shape[0]
-    idx = np.arange(128) // group  # half of each token (keys) or channel (values)
+    """Scale and zero of every element's own group, as fp16 arrays [128 tokens, D channels] (D from the
+    codes or gamma when present, else 128)."""
+    if "codes" in fields:
+        d = fields["codes"].shape[1]
+    elif "gamma" in fields:
+        d = len(fields["gamma"])
+    else:
+        d = np.asarray(fields["scale"]).shape[-1] if not is_v else HEAD_DIM
+    n = BLOCK if is_v else d  # entries per group row: tokens (values) or channels (keys)
+    s = np.asarray(fields["scale"], dtype=np.float16).reshape(-1, n)
+    z = np.asarray(fields["zero"], dtype=np.float16).reshape(-1, n)
     if is_v:
-        return s[idx[None, :], np.arange(128)[:, None]], z[idx[None, :], np.arange(128)[:, None]]
-    return s[idx[:, None], np.arange(128)[None, :]], z[idx[:, None], np.arange(128)[None, :]]
+        idx = np.arange(d) // (d // s.shape[0])  # group of each channel
+        return s[idx[None, :], np.arange(BLOCK)[:, None]], z[idx[None, :], np.arange(BLOCK)[:, None]]
+    idx = np.arange(BLOCK) // (BLOCK // s.shape[0])  # group of each token
+    return s[idx[:, None], np.arange(d)[None, :]], z[idx[:, None], np.arange(d)[None, :]]
 
 
 def dequantize_tile(fields: dict, is_v: bool) -> np.ndarray:
@@ -235,7 +272,7 @@ def dequantize_tile(fields: dict, is_v: bool) -> np.ndarray:
     gam = fields["gamma"].astype(np.float64)
     r_hat = n_hat * np.exp2(rho[:, None] + gam[None, :])
     # H is symmetric and its own inverse, so the inverse rotation is H again.
-    return r_hat @ _H.T
+    return r_hat @ _h(r_hat.shape[1]).T
 
 
 # --------------------------------------------------------------------------
@@ -250,11 +287,12 @@ def pack_k_codes(codes: np.ndarray, bits: int = 4) -> bytes:
     return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8).tobytes()
 
 
-def unpack_k_codes(buf: bytes, bits: int = 4) -> np.ndarray:
+def unpack_k_codes(buf: bytes, bits: int = 4, head_dim: int = HEAD_DIM) -> np.ndarray:
+    d = head_dim
     if bits == 8:
-        return np.frombuffer(bytes(buf[:BLOCK * HEAD_DIM]), dtype=np.uint8).reshape(BLOCK, HEAD_DIM).copy()
-    b = np.frombuffer(bytes(buf[:K_CODES_BYTES]), dtype=np.uint8).reshape(BLOCK, HEAD_DIM // 2)
-    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
+        return np.frombuffer(bytes(buf[:BLOCK * d]), dtype=np.uint8).reshape(BLOCK, d).copy()
+    b = np.frombuffer(bytes(buf[:BLOCK * d // 2]), dtype=np.uint8).reshape(BLOCK, d // 2)
+    codes = np.zeros((BLOCK, d), dtype=np.uint8)
     codes[:, 0::2] = b & 0xF
     codes[:, 1::2] = b >> 4
     return codes
@@ -265,24 +303,24 @@ def pack_v_codes(codes: np.ndarray, bits: int = 2) -> bytes:
     bits 2i..2i+1.  4 bits -> 8192 bytes: byte 64*c + k holds token 2k (bits 0-3) and 2k+1 (bits 4-7)."""
     c = np.asarray(codes, dtype=np.uint8)
     per = 8 // bits
-    out = np.zeros((HEAD_DIM, BLOCK // per), dtype=np.uint8)
+    out = np.zeros((c.shape[1], BLOCK // per), dtype=np.uint8)
     for i in range(per):
         out |= (c[i::per, :].T << (bits * i)).astype(np.uint8)
     return out.tobytes()
 
 
-def unpack_v_codes(buf: bytes, bits: int = 2) -> np.ndarray:
+def unpack_v_codes(buf: bytes, bits: int = 2, head_dim: int = HEAD_DIM) -> np.ndarray:
     per = 8 // bits
-    b = np.frombuffer(bytes(buf[:BLOCK * HEAD_DIM // per]), dtype=np.uint8).reshape(HEAD_DIM, BLOCK // per)
-    codes = np.zeros((BLOCK, HEAD_DIM), dtype=np.uint8)
+    b = np.frombuffer(bytes(buf[:BLOCK * head_dim // per]), dtype=np.uint8).reshape(head_dim, BLOCK // per)
+    codes = np.zeros((BLOCK, head_dim), dtype=np.uint8)
     for i in range(per):
         codes[i::per, :] = ((b >> (bits * i)) & ((1 << bits) - 1)).T
     return codes
 
 
 def encode_page(fields: dict, is_v: bool, bits: int = 0) -> bytes:
-    """Page = codes | scale fp16[groups] | zero fp16[groups] | rho fp32[128 tokens] | gamma fp32[128 channels],
-    little endian; groups = 128, or 2 x 128 half-major for group size 64."""
+    """Page = codes | scale fp16[groups] | zero fp16[groups] | rho fp32[128 tokens] | gamma fp32[D channels],
+    little endian; the group entries row-major as quantize_tile returns them (group row h, then entry)."""
     bits = bits or (2 if is_v else 4)
     codes = pack_v_codes(fields["codes"], bits) if is_v else pack_k_codes(fields["codes"], bits)
     meta = (np.asarray(fields["scale"], dtype="<f2").tobytes() + np.asarray(fields["zero"], dtype="<f2").tobytes()
@@ -290,20 +328,22 @@ def encode_page(fields: dict, is_v: bool, bits: int = 0) -> bytes:
     return codes + meta
 
 
-def decode_page(buf: bytes, is_v: bool) -> dict:
+def decode_page(buf: bytes, is_v: bool, head_dim: int = HEAD_DIM) -> dict:
     buf = bytes(buf)
-    bits, group = format_of_page(len(buf), is_v)
-    ncode = BLOCK * HEAD_DIM * bits // 8
-    codes = unpack_v_codes(buf[:ncode], bits) if is_v else unpack_k_codes(buf[:ncode], bits)
+    d = head_dim
+    bits, group = format_of_page(len(buf), is_v, d)
+    ncode = BLOCK * d * bits // 8
+    codes = unpack_v_codes(buf[:ncode], bits, d) if is_v else unpack_k_codes(buf[:ncode], bits, d)
     o = ncode
-    nsz = 256 * (BLOCK // group)  # bytes of the scales, and of the zeros
-    scale = np.frombuffer(buf[o:o + nsz], dtype="<f2").copy()
-    zero = np.frombuffer(buf[o + nsz:o + 2 * nsz], dtype="<f2").copy()
-    o += 2 * nsz
-    rho = np.frombuffer(buf[o:o + 512], dtype="<f4").copy()
-    gam = np.frombuffer(buf[o + 512:o + 1024], dtype="<f4").copy()
-    if group != BLOCK:
-        scale, zero = scale.reshape(BLOCK // group, 128), zero.reshape(BLOCK // group, 128)
+    n = n_groups(group, d, is_v)
+    scale = np.frombuffer(buf[o:o + 2 * n], dtype="<f2").copy()
+    zero = np.frombuffer(buf[o + 2 * n:o + 4 * n], dtype="<f2").copy()
+    o += 4 * n
+    rho = np.frombuffer(buf[o:o + 4 * BLOCK], dtype="<f4").copy()
+    gam = np.frombuffer(buf[o + 4 * BLOCK:o + 4 * BLOCK + 4 * d], dtype="<f4").copy()
+    per_row = BLOCK if is_v else d
+    if n > per_row:
+        scale, zero = scale.reshape(n // per_row, per_row), zero.reshape(n // per_row, per_row)
     return {"codes": codes, "scale": scale, "zero": zero, "rho": rho, "gamma": gam}
 
 
@@ -311,13 +351,13 @@ def decode_page(buf: bytes, is_v: bool) -> dict:
 # Whole-call drivers (the two entry points of the path)
 # --------------------------------------------------------------------------
 def quantize_blocks(k16: np.ndarray, v16: np.ndarray, dst_pages, k_pool: np.ndarray, v_pool: np.ndarray) -> None:
-    """k16, v16: fp16 [n_blocks*128, Hkv, 128]; block b of head h goes to page dst_pages[b] of each pool.
+    """k16, v16: fp16 [n_blocks*128, Hkv, D]; block b of head h goes to page dst_pages[b] of each pool.
 
     Pools are uint8 arrays [num_pages, Hkv, page_bytes], written in place; the page sizes give the
     code widths of the format.
     """
-    n_tok, hkv, _ = k16.shape
-    (kb, kg), (vb, vg) = format_of_page(k_pool.shape[2], False), format_of_page(v_pool.shape[2], True)
+    n_tok, hkv, d = k16.shape
+    (kb, kg), (vb, vg) = format_of_page(k_pool.shape[2], False, d), format_of_page(v_pool.shape[2], True, d)
     for b in range(n_tok // BLOCK):
         p = int(dst_pages[b])
         for h in range(hkv):
@@ -328,17 +368,18 @@ def quantize_blocks(k16: np.ndarray, v16: np.ndarray, dst_pages, k_pool: np.ndar
                 encode_page(quantize_tile(v16[sl, h, :], True, bits=vb, group=vg), True, vb), np.uint8)
 
 
-def dequantize_pages(pool: np.ndarray, pages, head: int, is_v: bool) -> np.ndarray:
-    """Concatenate dequantised blocks of one KV head over a page list -> [len(pages)*128, 128] fp64."""
+def dequantize_pages(pool: np.ndarray, pages, head: int, is_v: bool, head_dim: int = HEAD_DIM) -> np.ndarray:
+    """Concatenate dequantised blocks of one KV head over a page list -> [len(pages)*128, D] fp64."""
     if len(pages) == 0:
-        return np.zeros((0, HEAD_DIM))
-    return np.concatenate([dequantize_tile(decode_page(pool[int(p), head].tobytes(), is_v), is_v) for p in pages])
+        return np.zeros((0, head_dim))
+    return np.concatenate([dequantize_tile(decode_page(pool[int(p), head].tobytes(), is_v, head_dim), is_v)
+                           for p in pages])
 
 
 def attention(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float) -> np.ndarray:
     """out = softmax(scale * K^ q) V^ for one query vector (fp64, max-subtracted)."""
     if k_hat.shape[0] == 0:
-        return np.zeros(HEAD_DIM)
+        return np.zeros(len(q))
     logits = scale * (k_hat @ np.asarray(q, dtype=np.float64))
     w = np.exp(logits - logits.max())
     return (w / w.sum()) @ v_hat
@@ -352,10 +393,10 @@ def decode(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table:
     h reads KV head h // (Hq // Hkv).  ``seqs`` / ``heads`` restrict the work to
     a sample (other rows stay NaN).
     """
-    bsz, hq, _ = q16.shape
+    bsz, hq, d = q16.shape
     group = hq // num_kv_heads
-    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
-    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    out = np.full((bsz, hq, d), np.nan)
     for b in (range(bsz) if seqs is None else seqs):
         pages = block_table[b, : int(seq_lens[b]) // BLOCK]
         hs = range(hq) if heads is None else heads
@@ -363,7 +404,7 @@ def decode(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table:
         for h in hs:
             g = h // group
             if g not in cache:
-                cache[g] = (dequantize_pages(k_pool, pages, g, False), dequantize_pages(v_pool, pages, g, True))
+                cache[g] = (dequantize_pages(k_pool, pages, g, False, d), dequantize_pages(v_pool, pages, g, True, d))
             out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
     return out
 
@@ -379,7 +420,7 @@ def fp16_pages(cache16: np.ndarray, pages, head: int) -> np.ndarray:
     cache16: fp16 [num_pages, Hkv, 128 tokens, 128 channels].
     """
     if len(pages) == 0:
-        return np.zeros((0, HEAD_DIM))
+        return np.zeros((0, cache16.shape[-1]))
     return np.concatenate([np.asarray(cache16[int(p), head], dtype=np.float64) for p in pages])
 
 
@@ -390,10 +431,10 @@ def fp16_decode(q16: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, block
 
     Same addressing and scale as ``decode``; ``seqs`` / ``heads`` restrict the work to a sample.
     """
-    bsz, hq, _ = q16.shape
+    bsz, hq, d = q16.shape
     group = hq // num_kv_heads
-    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
-    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    out = np.full((bsz, hq, d), np.nan)
     for b in (range(bsz) if seqs is None else seqs):
         pages = block_table[b, : int(seq_lens[b]) // BLOCK]
         for h in (range(hq) if heads is None else heads):
@@ -414,10 +455,10 @@ def decode_tail(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_t
     """Decode of q [B, Hq, 128] over the first seq_lens[b] // 128 packed blocks followed by the
     seq_lens[b] % 128 tail tokens k_tail[b, :t, g], v_tail[b, :t, g] (fp16 [B, 128, Hkv, 128]) -> fp64.
     """
-    bsz, hq, _ = q16.shape
+    bsz, hq, d = q16.shape
     group = hq // num_kv_heads
-    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
-    out = np.full((bsz, hq, HEAD_DIM), np.nan)
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    out = np.full((bsz, hq, d), np.nan)
     for b in (range(bsz) if seqs is None else seqs):
         nblk, ntail = int(seq_lens[b]) // BLOCK, int(seq_lens[b]) % BLOCK
         pages = block_table[b, :nblk]
@@ -425,9 +466,9 @@ def decode_tail(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_t
         for h in (range(hq) if heads is None else heads):
             g = h // group
             if g not in cache:
-                cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False),
+                cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False, d),
                                             np.asarray(k_tail[b, :ntail, g], dtype=np.float64)]),
-                            np.concatenate([dequantize_pages(v_pool, pages, g, True),
+                            np.concatenate([dequantize_pages(v_pool, pages, g, True, d),
                                             np.asarray(v_tail[b, :ntail, g], dtype=np.float64)]))
             out[b, h] = attention(np.asarray(q16[b, h], dtype=np.float64), cache[g][0], cache[g][1], scale)
     return out
@@ -453,10 +494,10 @@ def prefill(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table
     Query rows at or past q_lens[b] are zero.  ``seqs`` / ``rows`` / ``heads`` restrict the work
     to a sample (the rest stays NaN).
     """
-    bsz, max_q, hq, _ = q16.shape
+    bsz, max_q, hq, d = q16.shape
     group = hq // num_kv_heads
-    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(HEAD_DIM)
-    out = np.full((bsz, max_q, hq, HEAD_DIM), np.nan)
+    scale = softmax_scale if softmax_scale > 0 else 1.0 / np.sqrt(d)
+    out = np.full((bsz, max_q, hq, d), np.nan)
     for b in (range(bsz) if seqs is None else seqs):
         pages = block_table[b, : int(prefix_lens[b]) // BLOCK]
         n_new, n_q = int(new_lens[b]), int(q_lens[b])
@@ -469,9 +510,9 @@ def prefill(q16: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, block_table
                     continue
                 g = h // group
                 if g not in cache:
-                    cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False),
+                    cache[g] = (np.concatenate([dequantize_pages(k_pool, pages, g, False, d),
                                                 np.asarray(k_new[b, :n_new, g], dtype=np.float64)]),
-                                np.concatenate([dequantize_pages(v_pool, pages, g, True),
+                                np.concatenate([dequantize_pages(v_pool, pages, g, True, d),
                                                 np.asarray(v_new[b, :n_new, g], dtype=np.float64)]))
                 last = n_pre + (n_new - n_q) + i  # the query's own row
                 out[b, i, h] = attention(np.asarray(q16[b, i, h], dtype=np.float64), cache[g][0][: last + 1],
