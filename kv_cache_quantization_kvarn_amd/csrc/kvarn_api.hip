@@ -26,6 +26,17 @@ hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
                               uint32_t* counters, uint32_t* flags, hipStream_t stream);
+hipError_t launch_quantize_hd(const void* k, const void* v, int n_blocks, int hkv, int head_dim,
+                              const int32_t* dst_pages, void* k_pool, void* v_pool, int num_pages, int kbits,
+                              int vbits, int group, uint32_t* flags, hipStream_t stream);
+hipError_t launch_dequantize_hd(const void* k_pool, const void* v_pool, int num_pages, const int32_t* pages,
+                                int n_blocks, int hkv, int head_dim, int kbits, int vbits, int group, float* k_out,
+                                float* v_out, uint32_t* flags, hipStream_t stream);
+hipError_t launch_decode_hd(const void* q, const void* k_pool, const void* v_pool, int num_pages,
+                            const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
+                            int hkv, int head_dim, int kbits, int vbits, int group, int blocks_per_split,
+                            int max_splits, float scale_log2, float* out, float* part, uint32_t* counters,
+                            uint32_t* flags, hipStream_t stream);
 hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const void* v_pool, int num_pages,
                           const int32_t* block_table, int max_blocks, const int32_t* prefix_lens, const void* k_new,
                           const void* v_new, int max_new, const int32_t* new_lens, const int32_t* q_lens, int batch,
@@ -51,7 +62,6 @@ __global__ void zero_words(uint32_t* __restrict__ p, size_t n) {
 namespace {
 
 constexpr int kMaxGroup = 8;
-constexpr int kPartFloats = 128 + 2;
 constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
 constexpr long kTargetGroups = 768;    // workgroups (4 waves each): one pass over 256 CUs at 3 workgroups per CU
 constexpr long kMaxPagesPerSplit = 32;
@@ -63,9 +73,10 @@ kvarn_status fail(kvarn_status s, const char* msg) {
   return s;
 }
 
-// kvarn_k{4,8}v{2,4}_g{128,64} with head_dim 128 and 128-token blocks
+// kvarn_k{4,8}v{2,4}_g{128,64} with head_dim 64, 128 or 256 and 128-token blocks
 bool config_ok(const kvarn_config* c) {
-  return c && c->head_dim == 128 && c->block_tokens == 128 && (c->k_bits == 4 || c->k_bits == 8) &&
+  return c && (c->head_dim == 64 || c->head_dim == 128 || c->head_dim == 256) && c->block_tokens == 128 &&
+         (c->k_bits == 4 || c->k_bits == 8) &&
          (c->v_bits == 2 || c->v_bits == 4) && (c->group_size == 128 || c->group_size == 64) &&
          c->norm_iters == 4 && std::fabs(c->eps - 1e-6f) <= 1e-12f;
 }
@@ -73,14 +84,24 @@ bool config_ok(const kvarn_config* c) {
 kvarn_status check_config(const kvarn_config* c) {
   if (!c) return fail(KVARN_ERR_NULL, "config is NULL");
   if (!config_ok(c))
-    return fail(KVARN_ERR_UNSUPPORTED, "supported formats: kvarn_k{4,8}v{2,4}_g{128,64} (head_dim 128, block 128)");
+    return fail(KVARN_ERR_UNSUPPORTED,
+                "supported formats: kvarn_k{4,8}v{2,4}_g{128,64} (head_dim 64, 128 or 256; block 128)");
   return KVARN_OK;
 }
 
-// codes plus scale and zero fp16 per group (two groups per channel or token for group size 64), rho and
-// gamma fp32[128]
-size_t page_bytes_of(int bits, int group) {
-  return static_cast<size_t>(128) * 128 * bits / 8 + (group == 64 ? 2048 : 1536);
+// Entry points built for 128-channel heads only (decode with an fp16 tail, the fp16 baseline, prefill).
+kvarn_status check_config_128(const kvarn_config* c) {
+  kvarn_status s = check_config(c);
+  if (s == KVARN_OK && c->head_dim != 128) return fail(KVARN_ERR_UNSUPPORTED, "this entry point needs head_dim 128");
+  return s;
+}
+
+// codes plus scale and zero fp16 per group, rho fp32[128 tokens] and gamma fp32[head_dim]: key groups are
+// one channel over `group` tokens, value groups one token over min(group, head_dim) channels
+size_t page_bytes_of(int bits, int group, int head_dim, bool is_v) {
+  const int vgc = group < head_dim ? group : head_dim;
+  const size_t groups = is_v ? static_cast<size_t>(head_dim / vgc) * 128 : static_cast<size_t>(128 / group) * head_dim;
+  return static_cast<size_t>(128) * head_dim * bits / 8 + 4 * groups + 4 * 128 + 4 * static_cast<size_t>(head_dim);
 }
 
 struct DecodePlan {
@@ -111,12 +132,15 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 size_t counter_bytes(int batch, int hkv) { return align256(static_cast<size_t>(batch) * hkv * sizeof(uint32_t)); }
 
+// Floats of one split partial of one query head: o[head_dim], m, l.
+size_t part_floats(int head_dim) { return static_cast<size_t>(head_dim) + 2; }
+
 // Room for the partials of either plan (with or without an fp16 tail split).
-size_t workspace_bytes(int batch, int hkv, int max_blocks) {
+size_t workspace_bytes(int batch, int hkv, int max_blocks, int head_dim) {
   const int a = plan_decode(batch, hkv, max_blocks).max_splits;
   const int b = plan_decode(batch, hkv, max_blocks, true).max_splits;
   return counter_bytes(batch, hkv) +
-         static_cast<size_t>(batch) * hkv * (a > b ? a : b) * kMaxGroup * kPartFloats * sizeof(float);
+         static_cast<size_t>(batch) * hkv * (a > b ? a : b) * kMaxGroup * part_floats(head_dim) * sizeof(float);
 }
 
 kvarn_status launch_status(hipError_t e) {
@@ -158,8 +182,8 @@ kvarn_status scratch_address(hipStream_t stream, unsigned char** out) {
 enum class DecodeKind { packed, packed_tail, fp16 };
 
 // Partials of one decode call (split results of every (sequence, KV head) under the plan).
-size_t partial_bytes(int batch, int hkv, int max_splits) {
-  return static_cast<size_t>(batch) * hkv * max_splits * kMaxGroup * kPartFloats * sizeof(float);
+size_t partial_bytes(int batch, int hkv, int max_splits, int head_dim) {
+  return static_cast<size_t>(batch) * hkv * max_splits * kMaxGroup * part_floats(head_dim) * sizeof(float);
 }
 
 // Validation and launch shared by the packed decode (with or without an fp16 tail) and the fp16
@@ -170,8 +194,9 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
                            const void* v_tail, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                            float softmax_scale, float* out, void* workspace, size_t ws_bytes, uint32_t* dev_flags,
                            void* stream, bool use_scratch = false) {
-  kvarn_status s = check_config(cfg);
+  kvarn_status s = kind == DecodeKind::packed ? check_config(cfg) : check_config_128(cfg);
   if (s != KVARN_OK) return s;
+  const int D = cfg->head_dim;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 || num_pages < 0)
     return fail(KVARN_ERR_SHAPE, "negative or zero size");
   if (num_q_heads % num_kv_heads != 0) return fail(KVARN_ERR_SHAPE, "num_q_heads must be a multiple of num_kv_heads");
@@ -185,7 +210,7 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
   if (batch > 65535 || num_kv_heads > 65535) return fail(KVARN_ERR_SHAPE, "batch or num_kv_heads above 65535");
   const int mb = max_blocks_per_seq > 0 ? max_blocks_per_seq : 1;
   if (!use_scratch) {
-    const size_t need = workspace_bytes(batch, num_kv_heads, mb);
+    const size_t need = workspace_bytes(batch, num_kv_heads, mb, D);
     if (!workspace || ws_bytes < need) return fail(KVARN_ERR_WORKSPACE, "workspace missing or smaller than required");
     if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(KVARN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
@@ -201,14 +226,14 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
       return fail(KVARN_ERR_SHAPE, "tails must be 16-byte aligned");
   }
   const DecodePlan p = plan_decode(batch, num_kv_heads, mb, tail);
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(128.0f);
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(D));
   const float scale_log2 = scale * 1.4426950408889634f;
   uint32_t* counters;
   float* part;
   if (use_scratch) {
     if (static_cast<size_t>(batch) * num_kv_heads * sizeof(uint32_t) > kScratchCounterBytes)
       return fail(KVARN_ERR_WORKSPACE, "batch * num_kv_heads above the 262,144 counters of the fixed scratch memory");
-    if (partial_bytes(batch, num_kv_heads, p.max_splits) > kScratchBytes - kScratchCounterBytes)
+    if (partial_bytes(batch, num_kv_heads, p.max_splits, D) > kScratchBytes - kScratchCounterBytes)
       return fail(KVARN_ERR_WORKSPACE,
                   "the split partials of this call exceed the 63 MiB of fixed scratch memory; use "
                   "kvarn_decode_attention with a workspace");
@@ -228,6 +253,11 @@ kvarn_status decode_common(DecodeKind kind, const kvarn_config* cfg, const void*
     return launch_status(kvarn::launch_fp16_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                                    batch, num_q_heads, num_kv_heads, p.blocks_per_split, p.max_splits,
                                                    scale_log2, out, part, counters, dev_flags, st));
+  if (D != 128)
+    return launch_status(kvarn::launch_decode_hd(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens, batch,
+                                                 num_q_heads, num_kv_heads, D, cfg->k_bits, cfg->v_bits,
+                                                 cfg->group_size, p.blocks_per_split, p.max_splits, scale_log2, out,
+                                                 part, counters, dev_flags, st));
   return launch_status(kvarn::launch_decode(q, k_pool, v_pool, num_pages, bt, max_blocks_per_seq, seq_lens,
                                             tail ? k_tail : nullptr, tail ? v_tail : nullptr, batch, num_q_heads,
                                             num_kv_heads, cfg->k_bits, cfg->v_bits, cfg->group_size,
@@ -257,7 +287,7 @@ kvarn_status kvarn_config_parse(const char* name, kvarn_config* out) {
 
 size_t kvarn_page_bytes(const kvarn_config* cfg, int is_v) {
   if (!config_ok(cfg)) return 0;
-  return page_bytes_of(is_v ? cfg->v_bits : cfg->k_bits, cfg->group_size);
+  return page_bytes_of(is_v ? cfg->v_bits : cfg->k_bits, cfg->group_size, cfg->head_dim, is_v != 0);
 }
 
 kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const void* v, int32_t n_blocks,
@@ -274,6 +304,10 @@ kvarn_status kvarn_quantize_blocks(const kvarn_config* cfg, const void* k, const
     return fail(KVARN_ERR_SHAPE, "k and v must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15)
     return fail(KVARN_ERR_SHAPE, "pools must be 16-byte aligned");
+  if (cfg->head_dim != 128)
+    return launch_status(kvarn::launch_quantize_hd(k, v, n_blocks, num_kv_heads, cfg->head_dim, dst_pages, k_pool,
+                                                   v_pool, num_pages, cfg->k_bits, cfg->v_bits, cfg->group_size,
+                                                   dev_flags, static_cast<hipStream_t>(stream)));
   return launch_status(kvarn::launch_quantize(k, v, n_blocks, num_kv_heads, dst_pages, k_pool, v_pool, num_pages,
                                               cfg->k_bits, cfg->v_bits, cfg->group_size, dev_flags,
                                               static_cast<hipStream_t>(stream)));
@@ -291,6 +325,10 @@ kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool
   if (num_pages == 0) return fail(KVARN_ERR_SHAPE, "num_pages is 0");
   // one workgroup per (block, KV head, K or V): the grid and the kernel's tile index are 32-bit
   if (static_cast<long>(n_blocks) * num_kv_heads * 2 > 0x7FFFFFFFL) return fail(KVARN_ERR_SHAPE, "too many tiles");
+  if (cfg->head_dim != 128)
+    return launch_status(kvarn::launch_dequantize_hd(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads,
+                                                     cfg->head_dim, cfg->k_bits, cfg->v_bits, cfg->group_size, k_out,
+                                                     v_out, dev_flags, static_cast<hipStream_t>(stream)));
   return launch_status(kvarn::launch_dequantize(k_pool, v_pool, num_pages, pages, n_blocks, num_kv_heads, cfg->k_bits,
                                                 cfg->v_bits, cfg->group_size, k_out, v_out, dev_flags,
                                                 static_cast<hipStream_t>(stream)));
@@ -300,7 +338,7 @@ size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int3
                                     int32_t num_kv_heads, int32_t max_blocks_per_seq) {
   if (!config_ok(cfg) || batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || max_blocks_per_seq < 0) return 0;
   if (batch == 0) return 0;
-  return workspace_bytes(batch, num_kv_heads, max_blocks_per_seq > 0 ? max_blocks_per_seq : 1);
+  return workspace_bytes(batch, num_kv_heads, max_blocks_per_seq > 0 ? max_blocks_per_seq : 1, cfg->head_dim);
 }
 
 kvarn_status kvarn_decode_attention(const kvarn_config* cfg, const void* q, const void* k_pool,
@@ -335,7 +373,7 @@ kvarn_status kvarn_decode_attention_noalloc(const kvarn_config* cfg, const void*
 }
 
 size_t kvarn_fp16_page_bytes(const kvarn_config* cfg) {
-  return config_ok(cfg) ? static_cast<size_t>(128) * 128 * sizeof(uint16_t) : 0;
+  return config_ok(cfg) && cfg->head_dim == 128 ? static_cast<size_t>(128) * 128 * sizeof(uint16_t) : 0;
 }
 
 kvarn_status kvarn_fp16_decode_attention(const kvarn_config* cfg, const void* q, const void* k_cache,
@@ -354,7 +392,7 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
                                      const void* v_new, int32_t max_new, const int32_t* new_lens,
                                      const int32_t* q_lens, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                      float softmax_scale, float* out, uint32_t* dev_flags, void* stream) {
-  kvarn_status s = check_config(cfg);
+  kvarn_status s = check_config_128(cfg);
   if (s != KVARN_OK) return s;
   if (batch < 0 || max_q < 0 || max_new < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
       num_pages < 0)

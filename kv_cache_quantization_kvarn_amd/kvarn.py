@@ -128,23 +128,28 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(int(stream))
 
 
-def _need_decode(q, block_table, seq_lens, num_kv_heads, out, workspace, dev_flags) -> None:
-    """Arguments every decode entry point shares: q fp16 [B, Hq, 128], block_table int32 [B, max_blocks],
-    seq_lens int32 [B], out fp32 [B, Hq, 128], a byte workspace and optional int32 flags."""
-    _need(q, "q", torch.float16, (None, None, 128))
+def _need_decode(q, block_table, seq_lens, num_kv_heads, out, workspace, dev_flags, head_dim: int = 128) -> None:
+    """Arguments every decode entry point shares: q fp16 [B, Hq, D], block_table int32 [B, max_blocks],
+    seq_lens int32 [B], out fp32 [B, Hq, D], a byte workspace and optional int32 flags."""
+    _need(q, "q", torch.float16, (None, None, head_dim))
     batch, hq = q.shape[0], q.shape[1]
     if num_kv_heads <= 0 or hq % num_kv_heads:
         raise ValueError("%d query heads are not a multiple of %d KV heads" % (hq, num_kv_heads))
     _need(block_table, "block_table", torch.int32, (batch, None))
     _need(seq_lens, "seq_lens", torch.int32, (batch,))
-    _need(out, "out", torch.float32, (batch, hq, 128))
+    _need(out, "out", torch.float32, (batch, hq, head_dim))
     _need(workspace, "workspace", torch.uint8, (None,))
     _need(dev_flags, "dev_flags", torch.int32, None, optional=True)
 
 
-def kvarn_config_parse(name: str = "kvarn_k4v2_g128") -> kvarn_config:
+def kvarn_config_parse(name: str = "kvarn_k4v2_g128", head_dim: int = 128) -> kvarn_config:
+    """The format of a cache dtype name, for heads of `head_dim` channels (the name carries no head size;
+    the library parses it with head_dim 128, and 64 and 256 are the other sizes it builds)."""
     cfg = kvarn_config()
     _check(_lib.kvarn_config_parse(name.encode(), ctypes.byref(cfg)))
+    cfg.head_dim = head_dim
+    if _lib.kvarn_page_bytes(ctypes.byref(cfg), 0) == 0:
+        raise KvarnError(KVARN_ERR_UNSUPPORTED, "head_dim %d is not supported (64, 128 or 256)" % head_dim)
     return cfg
 
 
@@ -154,12 +159,12 @@ def kvarn_page_bytes(cfg: kvarn_config, is_v: bool) -> int:
 
 def kvarn_quantize_blocks(cfg, k: torch.Tensor, v: torch.Tensor, dst_pages: torch.Tensor, k_pool: torch.Tensor,
                           v_pool: torch.Tensor, dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
-    """k, v: fp16 [n_blocks*128, Hkv, 128]; dst_pages int32 [n_blocks]; pools uint8 [pages, Hkv, page_bytes]."""
-    _need(k, "k", torch.float16, (None, None, 128))
+    """k, v: fp16 [n_blocks*128, Hkv, D]; dst_pages int32 [n_blocks]; pools uint8 [pages, Hkv, page_bytes]."""
+    _need(k, "k", torch.float16, (None, None, cfg.head_dim))
     n_tok, hkv = k.shape[0], k.shape[1]
     if n_tok % 128:
         raise ValueError("k holds %d tokens, not a whole number of 128-token blocks" % n_tok)
-    _need(v, "v", torch.float16, (n_tok, hkv, 128))
+    _need(v, "v", torch.float16, (n_tok, hkv, cfg.head_dim))
     _need(dst_pages, "dst_pages", torch.int32, (n_tok // 128,))
     _need_pools(cfg, k_pool, v_pool, hkv)
     _need(dev_flags, "dev_flags", torch.int32, None, optional=True)
@@ -171,12 +176,12 @@ def kvarn_quantize_blocks(cfg, k: torch.Tensor, v: torch.Tensor, dst_pages: torc
 def kvarn_dequantize_blocks(cfg, k_pool: torch.Tensor, v_pool: torch.Tensor, pages: torch.Tensor,
                             k_out: Optional[torch.Tensor], v_out: Optional[torch.Tensor],
                             dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
-    """k_out, v_out: fp32 [n_blocks*128, Hkv, 128] (either may be None); pages int32 [n_blocks]."""
+    """k_out, v_out: fp32 [n_blocks*128, Hkv, D] (either may be None); pages int32 [n_blocks]."""
     out = k_out if k_out is not None else v_out
     if out is None:
         raise ValueError("at least one of k_out and v_out is required")
     _need(pages, "pages", torch.int32, (None,))
-    shape = (128 * pages.shape[0], k_pool.shape[1], 128)
+    shape = (128 * pages.shape[0], k_pool.shape[1], cfg.head_dim)
     _need(k_out, "k_out", torch.float32, shape, optional=True)
     _need(v_out, "v_out", torch.float32, shape, optional=True)
     _need_pools(cfg, k_pool, v_pool)
@@ -197,8 +202,8 @@ def kvarn_decode_attention(cfg, q: torch.Tensor, k_pool: torch.Tensor, v_pool: t
                            block_table: torch.Tensor, seq_lens: torch.Tensor, num_kv_heads: int, out: torch.Tensor,
                            workspace: torch.Tensor, softmax_scale: float = 0.0,
                            dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
-    """q fp16 [B, Hq, 128]; block_table int32 [B, max_blocks]; seq_lens int32 [B]; out fp32 [B, Hq, 128]."""
-    _need_decode(q, block_table, seq_lens, num_kv_heads, out, workspace, dev_flags)
+    """q fp16 [B, Hq, D]; block_table int32 [B, max_blocks]; seq_lens int32 [B]; out fp32 [B, Hq, D]."""
+    _need_decode(q, block_table, seq_lens, num_kv_heads, out, workspace, dev_flags, cfg.head_dim)
     _need_pools(cfg, k_pool, v_pool, num_kv_heads)
     batch, hq = q.shape[0], q.shape[1]
     _on_gpu(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens, out=out,
@@ -215,8 +220,8 @@ def kvarn_decode_attention_noalloc(cfg, q: torch.Tensor, k_pool: torch.Tensor, v
                                    out: torch.Tensor, softmax_scale: float = 0.0,
                                    dev_flags: Optional[torch.Tensor] = None, stream=None) -> None:
     """kvarn_decode_attention with the library's fixed scratch memory instead of a workspace."""
-    _need(q, "q", torch.float16, (None, None, 128))
-    _need_decode(q, block_table, seq_lens, num_kv_heads, out, torch.zeros(0, dtype=torch.uint8), dev_flags)
+    _need_decode(q, block_table, seq_lens, num_kv_heads, out, torch.zeros(0, dtype=torch.uint8), dev_flags,
+                 cfg.head_dim)
     _need_pools(cfg, k_pool, v_pool, num_kv_heads)
     _on_gpu(q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table, seq_lens=seq_lens, out=out,
             dev_flags=dev_flags)

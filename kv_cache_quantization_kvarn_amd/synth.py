@@ -45,6 +45,7 @@ class Workload:
     paged: bool = False              # random physical page permutation
     append_blocks: int = 0           # blocks appended per sequence before decode
     index: int = 0
+    head_dim: int = HEAD_DIM
 
     @property
     def gqa(self) -> int:
@@ -61,6 +62,20 @@ WORKLOADS: Dict[str, Workload] = {
                  n_outlier=8, outlier_mult=50.0, index=3),
         Workload("paged_mixed_128xU1k_32k", batch=128, seq_len_range=(1024, 32768), hq=64, hkv=8,
                  paged=True, append_blocks=1, index=4),
+    ]
+}
+
+
+# Heads of 64 and 256 channels (the other head sizes of the format), one layer each at full size:
+# a Llama-3.2-1B-like layer (32 query / 8 KV heads of 64 channels) and a Gemma-2-9B-like layer
+# (16 query / 8 KV heads of 256 channels), 16 sequences of 8192 tokens.
+HEAD_DIM_WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_d64_1x1024", batch=1, seq_len=1024, hq=32, hkv=8, index=20, head_dim=64),
+        Workload("tiny_d256_1x1024", batch=1, seq_len=1024, hq=16, hkv=8, index=21, head_dim=256),
+        Workload("llama32_1b_layer_d64_16x8192", batch=16, seq_len=8192, hq=32, hkv=8, index=22, head_dim=64),
+        Workload("gemma2_9b_layer_d256_16x8192", batch=16, seq_len=8192, hq=16, hkv=8, index=23, head_dim=256),
     ]
 }
 
@@ -89,24 +104,24 @@ def seq_lens_for(w: Workload) -> List[int]:
 def outlier_channels(w: Workload, layer: int) -> torch.Tensor:
     """[Hkv, n_outlier] distinct channel ids per KV head (seeded shuffle)."""
     g = _gen("cpu", stream_seed(w, 4, layer))
-    rows = [torch.randperm(HEAD_DIM, generator=g)[: w.n_outlier] for _ in range(w.hkv)]
+    rows = [torch.randperm(getattr(w, "head_dim", HEAD_DIM), generator=g)[: w.n_outlier] for _ in range(w.hkv)]
     return torch.stack(rows) if rows else torch.zeros(0, w.n_outlier, dtype=torch.long)
 
 
 def make_kv(n_tokens: int, hkv: int, *, n_outlier: int, outlier_mult: float, outliers: torch.Tensor,
-            seed_k: int, seed_v: int, device) -> tuple:
-    """fp16 K, V of shape [n_tokens, hkv, 128] with the outlier / log-normal recipe above."""
+            seed_k: int, seed_v: int, device, head_dim: int = HEAD_DIM) -> tuple:
+    """fp16 K, V of shape [n_tokens, hkv, head_dim] with the outlier / log-normal recipe above."""
     gk = _gen(device, seed_k)
-    k = torch.randn(n_tokens, hkv, HEAD_DIM, generator=gk, device=device, dtype=torch.float32)
+    k = torch.randn(n_tokens, hkv, head_dim, generator=gk, device=device, dtype=torch.float32)
     if n_outlier > 0:
-        mult = torch.ones(hkv, HEAD_DIM, device=device, dtype=torch.float32)
+        mult = torch.ones(hkv, head_dim, device=device, dtype=torch.float32)
         for h in range(hkv):
             mult[h, outliers[h].to(device)] = outlier_mult
         k.mul_(mult)
     k16 = k.to(torch.float16)
     del k
     gv = _gen(device, seed_v)
-    v = torch.randn(n_tokens, hkv, HEAD_DIM, generator=gv, device=device, dtype=torch.float32)
+    v = torch.randn(n_tokens, hkv, head_dim, generator=gv, device=device, dtype=torch.float32)
     scale = torch.exp(0.5 * torch.randn(n_tokens, hkv, 1, generator=gv, device=device, dtype=torch.float32))
     v.mul_(scale)
     v16 = v.to(torch.float16)
@@ -118,12 +133,13 @@ def layer_kv(w: Workload, layer: int, n_tokens: int, device, append: bool = Fals
     sk, sv = (7, 8) if append else (1, 2)
     return make_kv(n_tokens, w.hkv, n_outlier=w.n_outlier, outlier_mult=w.outlier_mult,
                    outliers=outlier_channels(w, layer),
-                   seed_k=stream_seed(w, sk, layer), seed_v=stream_seed(w, sv, layer), device=device)
+                   seed_k=stream_seed(w, sk, layer), seed_v=stream_seed(w, sv, layer), device=device,
+                   head_dim=w.head_dim)
 
 
 def make_q(w: Workload, layer: int, device) -> torch.Tensor:
     g = _gen(device, stream_seed(w, 3, layer))
-    return torch.randn(w.batch, w.hq, HEAD_DIM, generator=g, device=device, dtype=torch.float32).to(torch.float16)
+    return torch.randn(w.batch, w.hq, w.head_dim, generator=g, device=device, dtype=torch.float32).to(torch.float16)
 
 
 @dataclasses.dataclass

@@ -1,0 +1,227 @@
+"""GPU parity of heads of 64 and 256 channels (kvarn_k{4,8}v{2,4}_g{128,64} at head_dim 64 / 256)
+against the oracles, through the C ABI.
+
+Quantise: every tile of the tiny shapes in every format, with every page byte written; the full-size
+layers (a Llama-3.2-1B-like layer of 64-channel heads, a Gemma-2-9B-like layer of 256-channel heads)
+tile by tile against the C++ oracle.  Dequantise on the same bytes.  Decode on ragged paged caches at
+G = 1, 4, 6, 8, with an empty sequence, a bad page id and a bad length, several split plans, and the
+full-size layers on every (sequence, query head).  Bars as for head_dim 128.
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_kvarn_amd import synth
+from oracle import kvarn_oracle as o
+from oracle import kvarn_oracle_cpp as C
+import kvarn_check as chk
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [64, 256]
+FORMATS = ["kvarn_k4v2_g128", "kvarn_k4v4_g128", "kvarn_k8v2_g128", "kvarn_k8v4_g128", "kvarn_k4v2_g64",
+           "kvarn_k4v4_g64", "kvarn_k8v2_g64", "kvarn_k8v4_g64"]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def K():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from kv_cache_quantization_kvarn_amd import kvarn
+    return kvarn
+
+
+def quantize(K, cfg, k, v, pages, num_pages, poison=0xA5):
+    kp, vp = K.alloc_pools(cfg, num_pages, k.shape[1])
+    kp.fill_(poison)
+    vp.fill_(poison)
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_quantize_blocks(cfg, k, v, pages.to("cuda", torch.int32), kp, vp, fl)
+    torch.cuda.synchronize()
+    return kp, vp, K.kvarn_read_flags(fl)
+
+
+def decode(K, cfg, q, kp, vp, bt, sl, hkv, scale=0.0):
+    bt = bt.to("cuda", torch.int32).contiguous()
+    ws = K.alloc_workspace(cfg, q.shape[0], q.shape[1], hkv, bt.shape[1])
+    out = torch.full((q.shape[0], q.shape[1], cfg.head_dim), float("nan"), device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    K.kvarn_decode_attention(cfg, q, kp, vp, bt, sl.to("cuda", torch.int32), hkv, out, ws, scale, fl)
+    torch.cuda.synchronize()
+    return out, K.kvarn_read_flags(fl)
+
+
+def bits_of(cfg):
+    return cfg.k_bits, cfg.v_bits, cfg.group_size
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("name", FORMATS)
+def test_quantize_every_tile_and_every_byte(K, d, name):
+    cfg = K.kvarn_config_parse(name, d)
+    w = synth.HEAD_DIM_WORKLOADS["tiny_d%d_1x1024" % d]
+    say("case: quantize %s at head_dim %d, all %d tiles vs the Python oracle" % (name, d, 2 * 8 * w.hkv))
+    pm = synth.make_page_map(w)
+    k, v = synth.layer_kv(w, 0, 1024, "cuda")
+    a = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0x00)
+    b = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages, 0xFF)
+    assert a[2] == 0 and b[2] == 0
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), "a page byte was not written"
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    kph, vph = a[0].cpu().numpy(), a[1].cpu().numpy()
+    kb, vb, group = bits_of(cfg)
+    stats = chk.TileStats()
+    for blk in range(8):
+        p = int(pm.prefix_pages[blk])
+        for h in range(w.hkv):
+            for is_v, x, pool, bits in ((False, kh, kph, kb), (True, vh, vph, vb)):
+                tile = x[128 * blk:128 * blk + 128, h]
+                ref = np.frombuffer(o.encode_page(o.quantize_tile(tile, is_v, bits=bits, group=group), is_v, bits),
+                                    np.uint8)
+                chk.compare_pools(stats, pool[p, h][None], ref[None], is_v, bits, group, d)
+    say("  " + stats.summary())
+    stats.check()
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v4_g64"])
+def test_dequantize_same_bytes(K, d, name):
+    cfg = K.kvarn_config_parse(name, d)
+    w = synth.HEAD_DIM_WORKLOADS["tiny_d%d_1x1024" % d]
+    say("case: dequantize %s at head_dim %d vs the oracle on the same bytes" % (name, d))
+    pm = synth.make_page_map(w)
+    k, v = synth.layer_kv(w, 0, 1024, "cuda")
+    kp, vp, _ = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages)
+    ko = torch.empty(1024, w.hkv, d, device="cuda")
+    vo = torch.empty_like(ko)
+    K.kvarn_dequantize_blocks(cfg, kp, vp, pm.prefix_pages.cuda(), ko, vo)
+    torch.cuda.synchronize()
+    kph, vph, koh, voh = kp.cpu().numpy(), vp.cpu().numpy(), ko.cpu().numpy(), vo.cpu().numpy()
+    worst = 0.0
+    for blk in range(8):
+        p = int(pm.prefix_pages[blk])
+        for h in range(w.hkv):
+            for pool, outh, is_v in ((kph, koh, False), (vph, voh, True)):
+                ref = o.dequantize_tile(o.decode_page(pool[p, h].tobytes(), is_v, d), is_v)
+                worst = max(worst, float(np.abs(outh[128 * blk:128 * blk + 128, h] - ref).max()))
+    say("  dequantised max-abs diff %.3e" % worst)
+    assert worst <= chk.DEQUANT_TOL
+
+
+def ragged_cache(K, cfg, lens, hkv, seed):
+    d = cfg.head_dim
+    g = torch.Generator().manual_seed(seed)
+    nblk = sum(l // 128 for l in lens)
+    n = max(nblk, 1)
+    k = torch.randn(n * 128, hkv, d, generator=g) * torch.where(torch.rand(d, generator=g) < 0.04, 20.0, 1.0)
+    v = torch.randn(n * 128, hkv, d, generator=g) * torch.exp(0.5 * torch.randn(n * 128, hkv, 1, generator=g))
+    perm = torch.randperm(n, generator=g).to(torch.int32)
+    kp, vp, fl = quantize(K, cfg, k.half().cuda(), v.half().cuda(), perm, n)
+    assert fl == 0
+    bt = torch.full((len(lens), max(max(lens) // 128, 1) + 3), -1, dtype=torch.int32)
+    off = 0
+    for b, l in enumerate(lens):
+        bt[b, :l // 128] = perm[off:off + l // 128]
+        off += l // 128
+    return kp, vp, bt, torch.tensor(lens, dtype=torch.int32)
+
+
+def check_decode(out, q, kp, vp, bt, sl, hkv, scale=0.0, label=""):
+    ref = C.decode(q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), bt.numpy(), sl.numpy(), hkv, scale)
+    got = out.cpu().numpy().astype(np.float64)
+    worst = float(np.abs(got - ref).max())
+    say("  %s decode max-abs diff vs C++ oracle %.3e" % (label, worst))
+    assert worst <= chk.ATTN_TOL
+    return worst
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("hq,hkv,lens", [
+    (4, 4, [128, 640]),
+    (12, 2, [384, 0, 1280, 128]),
+    (16, 2, [2048, 256]),
+    (3, 1, [896, 1152, 128]),
+])
+def test_decode_ragged_paged(K, d, hq, hkv, lens):
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128", d)
+    say("case: decode head_dim %d hq=%d hkv=%d lens=%s" % (d, hq, hkv, lens))
+    kp, vp, bt, sl = ragged_cache(K, cfg, lens, hkv, 100 + d + hq)
+    q = torch.randn(len(lens), hq, d, generator=torch.Generator().manual_seed(7)).half().cuda()
+    out, fl = decode(K, cfg, q, kp, vp, bt, sl, hkv)
+    assert fl == 0
+    for b, l in enumerate(lens):
+        if l == 0:
+            assert torch.all(out[b] == 0)
+    check_decode(out, q, kp, vp, bt, sl, hkv)
+
+
+@pytest.mark.parametrize("d", DIMS)
+@pytest.mark.parametrize("name", FORMATS)
+def test_decode_every_format(K, d, name):
+    cfg = K.kvarn_config_parse(name, d)
+    say("case: decode %s at head_dim %d, G = 8, explicit scale" % (name, d))
+    kp, vp, bt, sl = ragged_cache(K, cfg, [1024, 256, 0, 640], 2, 200 + d)
+    q = torch.randn(4, 16, d, generator=torch.Generator().manual_seed(8)).half().cuda()
+    out, fl = decode(K, cfg, q, kp, vp, bt, sl, 2, 0.05)
+    assert fl == 0
+    check_decode(out, q, kp, vp, bt, sl, 2, 0.05, name)
+
+
+@pytest.mark.parametrize("d", DIMS)
+def test_decode_flags_splits_and_determinism(K, d):
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128", d)
+    say("case: head_dim %d decode: bad page, bad length, split plans, determinism, 1024 blocks" % d)
+    kp, vp, bt, sl = ragged_cache(K, cfg, [512, 384], 1, 300 + d)
+    q = torch.randn(2, 4, d, generator=torch.Generator().manual_seed(9)).half().cuda()
+    a, fa = decode(K, cfg, q, kp, vp, bt, sl, 1)
+    b, fb = decode(K, cfg, q, kp, vp, bt, sl, 1)
+    assert fa == fb == 0 and torch.equal(a, b)
+    padded = torch.full((2, 3000), -1, dtype=torch.int32)
+    padded[:, :bt.shape[1]] = bt
+    c, _ = decode(K, cfg, q, kp, vp, padded, sl, 1)  # another pages-per-split plan
+    diff = float((a - c).abs().max())
+    say("  split-plan difference %.3e" % diff)
+    assert diff <= 1e-5
+    bad = bt.clone()
+    bad[0, 1] = 99
+    x, fx = decode(K, cfg, q, kp, vp, bad, torch.tensor([512, 200], dtype=torch.int32), 1)
+    assert fx == 3 and torch.all(x[1] == 0)
+    keep = bt.clone()
+    keep[0, :3] = bt[0, [0, 2, 3]]
+    y, _ = decode(K, cfg, q, kp, vp, keep, torch.tensor([384, 384], dtype=torch.int32), 1)
+    assert float((x[0] - y[0]).abs().max()) <= 1e-5  # the bad page is skipped
+    # 1024 blocks in one sequence: 64 splits merge
+    kp2, vp2, bt2, sl2 = ragged_cache(K, cfg, [1024 * 128], 1, 400 + d)
+    q2 = torch.randn(1, 8, d, generator=torch.Generator().manual_seed(10)).half().cuda()
+    out2, f2 = decode(K, cfg, q2, kp2, vp2, bt2, sl2, 1)
+    assert f2 == 0
+    check_decode(out2, q2, kp2, vp2, bt2, sl2, 1, label="1024 blocks")
+
+
+@pytest.mark.parametrize("name", ["llama32_1b_layer_d64_16x8192", "gemma2_9b_layer_d256_16x8192"])
+def test_full_size_layer(K, name):
+    w = synth.HEAD_DIM_WORKLOADS[name]
+    d = w.head_dim
+    cfg = K.kvarn_config_parse("kvarn_k4v2_g128", d)
+    say("case: %s full size: all %d tiles and all %d decode rows vs the C++ oracle"
+        % (name, 2 * 1024 * w.hkv, w.batch * w.hq))
+    pm = synth.make_page_map(w)
+    k, v = synth.layer_kv(w, 0, w.batch * w.seq_len, "cuda")
+    q = synth.make_q(w, 0, "cuda")
+    kp, vp, fl = quantize(K, cfg, k, v, pm.prefix_pages, pm.num_pages)
+    assert fl == 0
+    out, fl = decode(K, cfg, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv)
+    assert fl == 0
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    kph, vph = kp.cpu().numpy(), vp.cpu().numpy()
+    kpo, vpo = np.zeros_like(kph), np.zeros_like(vph)
+    assert C.quantize_blocks(kh, vh, pm.prefix_pages.numpy(), kpo, vpo) == 0
+    stats = chk.TileStats()
+    chk.compare_pools(stats, kph, kpo, False, 4, 128, d)
+    chk.compare_pools(stats, vph, vpo, True, 2, 128, d)
+    say("  every tile vs C++ oracle: " + stats.summary())
+    stats.check()
+    check_decode(out, q, kp, vp, pm.block_table, pm.seq_lens, w.hkv, label="every row")
