@@ -40,12 +40,16 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 MEASURED_TRAFFIC = {
     ("quantize_kernel", "llama3_8b_layer_16x8192"): ("f54a6bbd6ca3fc55", 663500959),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 130369125),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("f54a6bbd6ca3fc55", 332495992),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("245d6f737a5acc3c", 67515580),
 }
 KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
     ("quantize_kernel", "llama3_8b_layer_16x8192"): ("f54a6bbd6ca3fc55", 126926848),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 10894144),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("f54a6bbd6ca3fc55", 64427909),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("245d6f737a5acc3c", 6061378),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -87,6 +91,8 @@ def parse():
                     help="the headline workload (the largest single-GPU step by default)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload summaries of the other configurations")
+    ap.add_argument("--no-head-dims", action="store_true",
+                    help="skip the layers with heads of 64 and 256 channels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time for each of the two CPU-baseline legs (one thread, all cores)")
@@ -147,17 +153,18 @@ class Case:
         self.bt = pm.block_table.cuda()
         self.sl = pm.seq_lens.cuda()
         self.ws = K.alloc_workspace(cfg, w.batch, w.hq, w.hkv, pm.block_table.shape[1])
-        self.out = torch.empty(w.batch, w.hq, 128, dtype=torch.float32, device="cuda")
+        self.out = torch.empty(w.batch, w.hq, w.head_dim, dtype=torch.float32, device="cuda")
         self.flags = torch.zeros(1, dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
         from kv_cache_quantization_kvarn_amd import accounting as acc
         kb, vb = K.kvarn_page_bytes(cfg, False), K.kvarn_page_bytes(cfg, True)
         qblocks = self.layers[0]["dst"].numel()
         attended = int(pm.seq_lens.sum().item()) // 128
-        self.q_bytes = acc.quantize_bytes(qblocks, w.hkv, kb, vb) * w.layers
-        self.d_bytes = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb) * w.layers
-        self.q_bytes_launch = acc.quantize_bytes(qblocks, w.hkv, kb, vb)
-        self.d_bytes_launch = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb)
+        d = w.head_dim
+        self.q_bytes = acc.quantize_bytes(qblocks, w.hkv, kb, vb, d) * w.layers
+        self.d_bytes = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb, head_dim=d) * w.layers
+        self.q_bytes_launch = acc.quantize_bytes(qblocks, w.hkv, kb, vb, d)
+        self.d_bytes_launch = acc.decode_bytes(attended, w.hkv, w.batch, w.hq, kb, vb, head_dim=d)
         self.q_tokens = qblocks * 128 * w.layers
         self.ctx_tokens = attended * 128
 
@@ -205,12 +212,12 @@ def time_steps(case, stream, steps, warmup):
     return elapsed, sum(q_ms) / len(q_ms) / 1e3, sum(d_ms) / len(d_ms) / 1e3
 
 
-def config_summary(K, cfg, name, stream, steps, warmup, reps, flush, sink):
+def config_summary(K, cfg, name, stream, steps, warmup, reps, flush, sink, workloads=None):
     """Step rate, per-launch quantise and decode rates and the cache-flushed decode of one workload."""
     import torch
     from kv_cache_quantization_kvarn_amd import accounting as acc
     from kv_cache_quantization_kvarn_amd import synth
-    w = synth.WORKLOADS[name]
+    w = (workloads or synth.WORKLOADS)[name]
     case = Case(K, w, cfg)
     elapsed, q_s, d_s = time_steps(case, stream, steps, warmup)
     d_flush = timed_after_flush(lambda: case.decode(case.layers[0]), reps, stream, flush, sink)
@@ -550,6 +557,18 @@ def main():
         prefill["group64"] = {"format": "kvarn_k4v2_g64", "us_median": g64["us_median"], "tflops": g64["tflops"],
                               "frac": g64["roofline"]["frac"]}
 
+    # heads of 64 and 256 channels: one full-size layer each, quantise and decode launches
+    head_dims = None
+    if not args.no_head_dims:
+        head_dims = {}
+        for name, hw in synth.HEAD_DIM_WORKLOADS.items():
+            if name.startswith("tiny"):
+                continue
+            hcfg = K.kvarn_config_parse("kvarn_k4v2_g128", hw.head_dim)
+            head_dims[name] = config_summary(K, hcfg, name, stream, args.steps, args.warmup, args.flush_reps, flush,
+                                             flush_sink, workloads=synth.HEAD_DIM_WORKLOADS)
+            head_dims[name]["head_dim"] = hw.head_dim
+
     # the other workloads, each timed like the headline step (a summary object per workload)
     configs = None
     if not args.no_configs:
@@ -609,6 +628,8 @@ def main():
         line["formats"] = formats
     if configs is not None:
         line["configs"] = configs
+    if head_dims is not None:
+        line["head_dims"] = head_dims
     # dominant kernel by time: the one whose launches take longer in the step
     if q_avg_s >= d_avg_s:
         dom, ach = "quantize_kernel", q_gbps

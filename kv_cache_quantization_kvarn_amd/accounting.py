@@ -28,21 +28,21 @@ def capacity_ratio(k_page: int, v_page: int) -> float:
     return fp16_kv_bytes(1, 1, BLOCK_TOKENS) / packed_bytes_per_block_head(k_page, v_page)
 
 
-def quantize_bytes(n_blocks: int, kv_heads: int, k_page: int, v_page: int) -> int:
+def quantize_bytes(n_blocks: int, kv_heads: int, k_page: int, v_page: int, head_dim: int = HEAD_DIM) -> int:
     """Algorithmic HBM bytes of one quantize call: fp16 K and V in, packed pages out."""
-    return n_blocks * kv_heads * (fp16_kv_bytes(1, 1, BLOCK_TOKENS) + k_page + v_page)
+    return n_blocks * kv_heads * (fp16_kv_bytes(1, 1, BLOCK_TOKENS, head_dim) + k_page + v_page)
 
 
 def decode_bytes(total_blocks_attended: int, kv_heads: int, batch: int, q_heads: int, k_page: int, v_page: int,
-                 max_blocks_per_seq: int = 0) -> int:
+                 max_blocks_per_seq: int = 0, head_dim: int = HEAD_DIM) -> int:
     """Algorithmic HBM bytes of one decode step.
 
-    Packed pages of every attended (block, KV head), the fp16 query (256 B per
-    query head), the fp32 output (512 B per query head), the block-table
-    entries read (4 B per attended block) and the sequence lengths.
+    Packed pages of every attended (block, KV head), the fp16 query (2 B per
+    channel and query head), the fp32 output (4 B per channel and query head),
+    the block-table entries read (4 B per attended block) and the sequence lengths.
     """
     return (total_blocks_attended * kv_heads * (k_page + v_page)
-            + batch * q_heads * (HEAD_DIM * 2 + HEAD_DIM * 4)
+            + batch * q_heads * (head_dim * 2 + head_dim * 4)
             + total_blocks_attended * 4 + batch * 4)
 
 

@@ -953,7 +953,19 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB, GS>::kMinWaves)) void decod
   // fence would write back (release) or invalidate (acquire) this XCD's whole L2.  Instead the
   // partials are written and read with agent-scope atomic accesses, which go through to the
   // device-coherent level, and each wave waits until its stores are acknowledged before the
-  // workgroup counts itself in.
+  // workgroup counts itself in.  Why this orders the hand-off on gfx950:
+  //   * an agent-scope relaxed store or load is a global store / load with the sc1 bit (LLVM's
+  //     AMDGPU memory model for the GFX940 family), which is performed at the device-coherent level
+  //     and never served from, or left in, a non-coherent XCD-private L2 line;
+  //   * on this GFX9-family target the vmcnt counter covers stores as well as loads (there is no
+  //     separate store counter), so s_waitcnt vmcnt(0) returns only once every partial store of the
+  //     wave is acknowledged, i.e. visible at that level; the barrier then covers all four waves;
+  //   * the counter add is an agent-scope atomic, issued after that point in program order, and the
+  //     last arriver issues its partial loads only after the add has returned (through the barrier
+  //     that publishes last_flag), so every load sees every store that preceded an add.
+  // Invariant that the argument needs: every access to the partials and counters, here, in the tail
+  // split and in the merge, goes through store_coherent / load_coherent / the atomic add; no plain
+  // load or store ever touches them.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {

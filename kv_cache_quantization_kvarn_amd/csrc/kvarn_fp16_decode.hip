@@ -269,6 +269,8 @@ __global__ __launch_bounds__(256, 3) void fp16_decode_kernel(
   }
   // The stores are acknowledged before the workgroup counts itself in (no fence: an agent-scope
   // fence would write back or invalidate this XCD's whole L2).
+  // Fence-free hand-off, as in the packed decode: agent-scope (sc1) partial stores, vmcnt(0) covering
+  // them, then the agent-scope counter add; every access to partials and counters is one of these.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {

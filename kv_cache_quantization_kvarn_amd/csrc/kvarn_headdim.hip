@@ -812,8 +812,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
     store_coherent(pp + D, mr);
     store_coherent(pp + D + 1, lr);
   }
-  // Hand-off without fences, as in the 128-channel decode: partials go through agent-scope atomic
-  // accesses, and each wave waits until its stores are acknowledged before the workgroup counts in.
+  // Hand-off without fences, as in the 128-channel decode: partials go through agent-scope (sc1)
+  // atomic accesses, vmcnt(0) covers the stores before the workgroup counts in with an agent-scope
+  // add, and every access to partials and counters is one of these.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {

@@ -239,7 +239,8 @@ class PrefillInputs:
     """Inputs of one chunked-prefill step (device tensors unless noted).
 
     ``k_prefix``/``v_prefix``: fp16 [batch*prefix, Hkv, 128], sequence-major (quantise input);
-    ``pages``: int32 [batch*prefix/128] page of every prefix block; ``block_table``: int32
+    ``pages``: int32 [batch*prefix/128] page of every prefix block (a seeded permutation of the
+    pages); ``block_table``: int32
     [batch, prefix/128 + chunk/128 + 1] (-1 past the prefix); ``prefix_lens``, ``new_lens``,
     ``q_lens``: int32 [batch]; ``k_new``/``v_new``: fp16 [batch, chunk, Hkv, 128];
     ``q``: fp16 [batch, chunk, Hq, 128].
@@ -267,7 +268,8 @@ def prefill_inputs(w: PrefillWorkload, device) -> PrefillInputs:
     g = _gen(device, stream_seed(w, 3))
     q = torch.randn(w.batch, w.chunk, w.hq, HEAD_DIM, generator=g, device=device, dtype=torch.float32)
     total = max(w.batch * nblk, 1)
-    pages = torch.arange(w.batch * nblk, dtype=torch.int32)
+    # physical pages in a seeded random permutation, as a paged cache holds them
+    pages = torch.randperm(w.batch * nblk, generator=_gen("cpu", stream_seed(w, 6))).to(torch.int32)
     table = torch.full((w.batch, nblk + (w.chunk + BLOCK_TOKENS - 1) // BLOCK_TOKENS + 1), -1, dtype=torch.int32)
     for b in range(w.batch):
         table[b, :nblk] = pages[b * nblk:(b + 1) * nblk]
