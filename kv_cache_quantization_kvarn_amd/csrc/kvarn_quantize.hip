@@ -60,6 +60,12 @@ __device__ __forceinline__ int chan_slot(int ch) { return 8 * ((ch >> 1) & 15) +
 
 constexpr int kPartStride = 36;  // floats per row of the partial-sum array (16 slots x 2 + pad)
 
+// Slot of lane (w, g, n) in a channel's row of column partials.  The 16 lanes of a row write channels
+// 2n (+ 32k) apart, i.e. rows 72 floats apart, which would put lanes n and n + 4 on the same banks; the
+// XOR with n / 4 spreads them over every bank (for 32 and for 64 banks) and keeps each slot in its half
+// (slots 0-7: waves 0-1, 8-15: waves 2-3), which the group-size-64 reducers read separately.
+__device__ __forceinline__ int col_slot(int w, int g, int n) { return (4 * w + g) ^ (n >> 2); }
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -73,9 +79,11 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x, int ctrl_xor2) {
 // Sum of the 8 (s1, s2) slot pairs of one row half, then with the partner thread (lane ^ 1).
 __device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
   const float4* p = reinterpret_cast<const float4*>(row + 16 * hf);
-  float a = 0.f, b = 0.f;
+  float a = p[0].x, b = p[0].y;
+  a += p[0].z;
+  b += p[0].w;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 1; k < 4; ++k) {
     const float4 v = p[k];
     a += v.x;
     b += v.y;
@@ -169,8 +177,26 @@ __device__ __forceinline__ void load_tile(f16x8 (&xa)[2][4], const uint16_t* __r
 
 // R' = X H for the wave's 32 tokens (unnormalised): output chunk h4 of each 16-token tile is the
 // sum over input chunks gi of H4[gi][h4] * (X_gi H32), with H4's -1 entries taken by hbn = -hb.
+// Also the first row pass's moments, straight from the fp16 input: with every column normaliser 1,
+// sum_j R'_tj = 128 x_t0 (only input channel 0 meets a row of H made of ones) and sum_j R'_tj^2 =
+// 128 sum_k x_tk^2 (the +-1 matrix times its transpose is 128 I).  m1[mt], m2[mt] belong to token
+// 32w + 16 mt + n and are the same in the four lanes of each column n.
 __device__ __forceinline__ void rotate(const f16x8 (&xa)[2][4], const f16x8 (&hb)[2], const f16x8 (&hbn)[2],
-                                       float (&R)[8][8], float (&P)[8][8]) {
+                                       float (&R)[8][8], float (&P)[8][8], float (&m1)[2], float (&m2)[2], int g) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    float q = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const h2 x = {xa[mt][gi][i], xa[mt][gi][i + 1]};
+        q = __builtin_amdgcn_fdot2(x, x, q, false);
+      }
+    m2[mt] = 128.f * rows4_sum(q);
+    m1[mt] = 128.f * rows4_sum(g == 0 ? static_cast<float>(xa[mt][0][0]) : 0.f);
+  }
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -233,8 +259,9 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
   // arrived meanwhile) and fetches the one after it; past the end, the last tile stands in
   f16x8 xa[2][4];
   float R[8][8], P[8][8];
+  float m1[2], m2[2];  // first row pass's moments of tokens 32w + 16 mt + n
   load_tile(xa, in, tile, hkv, w, n, g);
-  rotate(xa, hb, hbn, R, P);
+  rotate(xa, hb, hbn, R, P, m1, m2, g);
   load_tile(xa, in, tile + stride < tiles ? tile + stride : tile, hkv, w, n, g);
   for (; tile < tiles; tile += stride) {
     const int blk = tile / hkv;
@@ -260,8 +287,15 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     for (int it = 0; it < kNormIters; ++it) {
       // ---------------- row pass: moments over channels of R' * cf ------------
       // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
-      // the wave (no workgroup barrier) is enough.
-      {
+      // the wave (no workgroup barrier) is enough.  The first pass takes its moments from the
+      // input (rotate), the others form 16 partial sums per token.
+      if (it == 0) {
+        if (g == 0) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+            *reinterpret_cast<float2*>(&s.part_row[32 * w + 16 * mt + n][0]) = make_float2(m1[mt], m2[mt]);
+        }
+      } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float s1 = 0.f, s2 = 0.f;
@@ -275,7 +309,8 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
       }
       wave_lds_sync();
       {
-        const float2 m = reduce_pairs(s.part_row[t_red], hf);
+        const float2 m = it == 0 ? *reinterpret_cast<const float2*>(&s.part_row[t_red][0])
+                                 : reduce_pairs(s.part_row[t_red], hf);
         const float mu = m.x * inv128, ey2 = m.y * inv128;
         float var = fmaf(-mu, mu, ey2);
         if (__builtin_amdgcn_ballot_w64(!(var >= 0.5f * ey2)) != 0) {
@@ -321,7 +356,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
             s1 = fmaf(R[i][c], rf[i], s1);
             s2 = fmaf(P[i][c], r2[i], s2);
           }
-          *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(s1, s2);
+          *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(s1, s2);
         }
       }
       __syncthreads();
@@ -352,7 +387,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
               const float d = fmaf(R[i][c], rf[i], -mc[c]);
               q = fmaf(d, d, q);
             }
-            *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(q, 0.f);
+            *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(q, 0.f);
           }
           __syncthreads();
           const float cvar = reduce_pairs(s.part[t_red], hf).x * inv128;
@@ -401,7 +436,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           a = fminf(a, R[i][c]);
           b = fmaxf(b, R[i][c]);
         }
-        *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * (4 * w + g)]) = make_float2(a, b);
+        *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(a, b);
       }
       __syncthreads();
       {
@@ -627,7 +662,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     }
     {
       const int next = tile + stride < tiles ? tile + stride : tile;
-      rotate(xa, hb, hbn, R, P);
+      rotate(xa, hb, hbn, R, P, m1, m2, g);
       load_tile(xa, in, next + stride < tiles ? next + stride : next, hkv, w, n, g);
     }
   }
