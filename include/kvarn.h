@@ -13,7 +13,8 @@
  *
  * Conventions for every call:
  *   - All tensor arguments are device pointers owned by the caller; the library
- *     never allocates, frees or synchronises (except kvarn_read_flags).
+ *     never allocates, frees or synchronises (except kvarn_read_flags, and
+ *     kvarn_quantize_blocks while debug checks are on: kvarn_set_debug_checks).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously.  Calls are re-entrant; two calls that write the
  *     same pages or the same workspace must not overlap.
@@ -21,7 +22,9 @@
  *     Problems that only the device can see (a page id outside [0, num_pages),
  *     a bad sequence length) set bits in the optional `dev_flags` word (device
  *     memory, OR-ed atomically) and the offending unit of work is skipped.
- *   - Shapes: tokens of a 128-token block are consecutive rows; head_dim is 128.
+ *   - Shapes: tokens of a 128-token block are consecutive rows; head_dim is
+ *     cfg->head_dim (64, 128 or 256; 128 only for the decode with an fp16
+ *     tail, the fp16 baseline and prefill).
  *   - No exceptions cross this boundary; kvarn_last_error() describes the last
  *     failure of the calling thread.
  */
@@ -39,7 +42,7 @@ typedef enum {
   KVARN_OK = 0,
   KVARN_ERR_NULL = -1,        /* a required pointer is NULL */
   KVARN_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or inconsistent */
-  KVARN_ERR_UNSUPPORTED = -3, /* a configuration other than kvarn_k{4,8}v{2,4}_g{128,64} / head_dim 128 / block 128 */
+  KVARN_ERR_UNSUPPORTED = -3, /* a format other than kvarn_k{4,8}v{2,4}_g{128,64} / head_dim 64, 128, 256 / block 128 */
   KVARN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
   KVARN_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
 } kvarn_status;
@@ -48,7 +51,7 @@ typedef enum {
 #define KVARN_FLAG_BAD_PAGE 1u    /* a page id outside [0, num_pages): that block is skipped */
 #define KVARN_FLAG_BAD_SEQLEN 2u  /* seq_len < 0, not a multiple of 128, or above max_blocks*128: sequence output is 0 */
 
-/* Format parameters.  Supported: head_dim 128, block_tokens 128, k_bits 4 or
+/* Format parameters.  Supported: head_dim 64, 128 or 256, block_tokens 128, k_bits 4 or
  * 8, v_bits 2 or 4, group_size 128 or 64, norm_iters 4, eps 1e-6.  The post
  * names kvarn_k4v2_g128; the wider codes keep every step of the method and
  * change the number of levels (2^bits - 1) and the packing only.  Group size 64
@@ -123,7 +126,11 @@ kvarn_status kvarn_dequantize_blocks(const kvarn_config* cfg, const void* k_pool
  * partials and per-(sequence, KV head) arrival counters).  The workspace
  * must be zero-filled before its first use; every call leaves the counter
  * region zero again, so later calls with the same or smaller sizes need no
- * clearing. */
+ * clearing.  The split plan spreads over the compute units of the current
+ * device, so the size is that device's: query it with the device current that
+ * will run the decode.  Returns 0 for an unsupported config, batch <= 0, a
+ * non-positive head count, max_blocks_per_seq < 0, batch or num_kv_heads above
+ * 65535, or max_blocks_per_seq * 128 above 2^31 - 1. */
 size_t kvarn_decode_workspace_bytes(const kvarn_config* cfg, int32_t batch, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t max_blocks_per_seq);
 
@@ -232,6 +239,13 @@ kvarn_status kvarn_prefill_attention(const kvarn_config* cfg, const void* q, int
 /* Copy *dev_flags to *host_out after the work queued on `stream` finishes
  * (synchronises the stream). */
 kvarn_status kvarn_read_flags(const uint32_t* dev_flags, uint32_t* host_out, void* stream);
+
+/* Debug checks, process-wide (on by default in a build with -DKVARN_DEBUG, off
+ * otherwise).  While on, kvarn_quantize_blocks first checks that the in-range
+ * entries of dst_pages are distinct (two blocks quantised into one page in one
+ * call would race on its bytes): it allocates a bitmap, waits for `stream`, and returns KVARN_ERR_SHAPE, writing nothing,
+ * when two entries name the same page.  Not for graph capture. */
+void kvarn_set_debug_checks(int on);
 
 const char* kvarn_status_string(kvarn_status s);
 const char* kvarn_last_error(void);

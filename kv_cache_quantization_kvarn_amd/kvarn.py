@@ -34,8 +34,8 @@ EXPORTS = ("kvarn_config_parse", "kvarn_page_bytes", "kvarn_quantize_blocks", "k
            "kvarn_decode_workspace_bytes", "kvarn_decode_attention", "kvarn_decode_attention_noalloc",
            "kvarn_decode_attention_tail",
            "kvarn_fp16_page_bytes",
-           "kvarn_fp16_decode_attention", "kvarn_prefill_attention", "kvarn_read_flags", "kvarn_status_string",
-           "kvarn_last_error")
+           "kvarn_fp16_decode_attention", "kvarn_prefill_attention", "kvarn_read_flags", "kvarn_set_debug_checks",
+           "kvarn_status_string", "kvarn_last_error")
 
 KVARN_OK, KVARN_ERR_NULL, KVARN_ERR_SHAPE, KVARN_ERR_UNSUPPORTED, KVARN_ERR_WORKSPACE, KVARN_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
 FLAG_BAD_PAGE, FLAG_BAD_SEQLEN = 1, 2
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "kvarn_prefill_attention": (I32, [CFG, P, I32, P, P, I32, P, I32, P, P, P, I32, P, P, I32, I32, I32, F32, P,
                                           P, P]),
         "kvarn_read_flags": (I32, [P, P, P]),
+        "kvarn_set_debug_checks": (None, [ctypes.c_int]),
         "kvarn_status_string": (ctypes.c_char_p, [I32]),
         "kvarn_last_error": (ctypes.c_char_p, []),
     }
@@ -305,6 +306,12 @@ def kvarn_read_flags(dev_flags: torch.Tensor, stream=None) -> int:
     host = ctypes.c_uint32(0)
     _check(_lib.kvarn_read_flags(_ptr(dev_flags), ctypes.byref(host), _stream(stream)))
     return int(host.value)
+
+
+def kvarn_set_debug_checks(on: bool) -> None:
+    """Process-wide debug checks: while on, kvarn_quantize_blocks raises KvarnError (SHAPE) when two
+    entries of dst_pages name the same page, before anything is written (it waits for the stream)."""
+    _lib.kvarn_set_debug_checks(1 if on else 0)
 
 
 # ---- allocation helpers (device memory through torch) ----------------------

@@ -402,10 +402,12 @@ int kvo_dequantize_page(const uint8_t* page, int is_v, int head_dim, int bits, i
 }
 
 // Decode attention: out[b][h][D] (double) for every sequence b and query head h, or only for the
-// (b, h) pairs listed in `pairs` ([n_pairs][2]; NULL = all; other rows are left untouched).
+// (b, h) pairs listed in `pairs` ([n_pairs][2]; NULL = all; other rows are left untouched; a pair out
+// of range returns -1 before anything is computed).
 // Sequence b attends to pages block_table[b][0 .. seq_lens[b]/128) (an id outside [0, num_pages) is
 // left out) and, when k_tail / v_tail are given (fp16 [batch][128][hkv][D]), to the seq_lens[b] % 128
-// tail rows after them; without tails the remainder is ignored.  Returns -1 for an unknown format.
+// tail rows after them; without tails the remainder is ignored.  A length below 0 or with more full
+// blocks than max_blocks gives zeros.  Returns -1 for an unknown format.
 int kvo_decode(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool, int num_pages,
                const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const uint16_t* k_tail,
                const uint16_t* v_tail, int batch, int hq, int hkv, int head_dim, int kbits, int vbits, int group,
@@ -418,7 +420,11 @@ int kvo_decode(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool, 
   // work list: (sequence, KV head) units, each with the query heads it serves
   std::vector<std::vector<int>> heads(static_cast<size_t>(batch) * hkv);
   if (pairs) {
-    for (int i = 0; i < n_pairs; ++i) heads[static_cast<size_t>(pairs[2 * i]) * hkv + pairs[2 * i + 1] / G].push_back(pairs[2 * i + 1]);
+    for (int i = 0; i < n_pairs; ++i) {
+      const int pb = pairs[2 * i], ph = pairs[2 * i + 1];
+      if (pb < 0 || pb >= batch || ph < 0 || ph >= hq) return -1;
+      heads[static_cast<size_t>(pb) * hkv + ph / G].push_back(ph);
+    }
   } else {
     for (int b = 0; b < batch; ++b)
       for (int h = 0; h < hq; ++h) heads[static_cast<size_t>(b) * hkv + h / G].push_back(h);
@@ -429,7 +435,9 @@ int kvo_decode(const uint16_t* q, const uint8_t* k_pool, const uint8_t* v_pool, 
   parallel_for(static_cast<long>(units.size()), threads, [&](long ui) {
     const long u = units[ui];
     const int b = static_cast<int>(u / hkv), g = static_cast<int>(u % hkv);
-    const int len = seq_lens[b];
+    // a length below 0 or past the block table gives a sequence with no rows (output 0)
+    const int raw = seq_lens[b];
+    const int len = raw < 0 || raw / kBlock > max_blocks ? 0 : raw;
     const int ntail = (k_tail && v_tail) ? len % kBlock : 0;
     // a page id outside [0, num_pages) names no block: that block is left out
     std::vector<int> pages;

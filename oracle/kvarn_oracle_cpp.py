@@ -37,6 +37,42 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Sanitizer builds of the oracle with its self-test driver (kvarn_oracle_selftest.cpp): AddressSanitizer
+# with UndefinedBehaviorSanitizer, and ThreadSanitizer for the threaded driver.
+SELFTEST_SRC = os.path.join(HERE, "kvarn_oracle_selftest.cpp")
+SELFTEST_FLAGS = {"asan": ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer"],
+                  "tsan": ["-fsanitize=thread"]}
+SELFTEST_ENV = {"ASAN_OPTIONS": "detect_leaks=1:halt_on_error=1", "UBSAN_OPTIONS": "print_stacktrace=1:halt_on_error=1",
+                "TSAN_OPTIONS": "halt_on_error=1"}
+
+
+def selftest_path(kind: str) -> str:
+    return os.path.join(HERE, "_build", "oracle_selftest_" + kind)
+
+
+def build_selftest(kind: str) -> str:
+    """Compile the oracle and its self-test under one sanitizer kind ("asan" or "tsan")."""
+    exe = selftest_path(kind)
+    os.makedirs(os.path.dirname(exe), exist_ok=True)
+    cmd = (["g++", "-std=c++17", "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", "-Werror",
+            "-pthread"] + SELFTEST_FLAGS[kind] + ["-o", exe + ".tmp", SRC, SELFTEST_SRC])
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("g++ failed (%d): %s\n%s" % (res.returncode, " ".join(cmd), res.stdout + res.stderr))
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
+def run_selftest(kind: str, timeout: float = 600) -> subprocess.CompletedProcess:
+    """Run one sanitizer build of the self-test, building it first if it is missing or older than its sources."""
+    exe = selftest_path(kind)
+    if not os.path.exists(exe) or max(os.path.getmtime(SRC), os.path.getmtime(SELFTEST_SRC)) > os.path.getmtime(exe):
+        build_selftest(kind)
+    env = dict(os.environ)
+    env.update(SELFTEST_ENV)
+    return subprocess.run([exe], capture_output=True, text=True, timeout=timeout, env=env)
+
+
 _lib = None
 
 
