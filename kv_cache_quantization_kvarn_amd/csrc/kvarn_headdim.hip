@@ -25,11 +25,13 @@
 //
 // Decode.  One workgroup of four waves per (sequence, KV head, split), the same split plan, partial
 // layout and fence-free hand-off as the 128-channel decode.  With q~ = H q (orthonormal H) the page
-// contractions run in the rotated basis on the vector ALU:
+// contractions run in the rotated basis,
 //     score_t = 2^rho_t * sum_j q~_j 2^gamma_j (s c_tj + z)       (key group of channel j, half of t)
 //     o~_j   += 2^gamma_j * sum_t p_t 2^rho_t (s c_tj + z)        (value group of token t, group of j)
-// with online softmax; the last workgroup of a (sequence, KV head) merges the splits and applies H.
-#include "kvarn_common.h"
+// both code sums as dense products on the matrix cores (codes as exact fp16 operands, the fp32
+// coefficients as fp16 hi + lo), with online softmax; the last workgroup of a (sequence, KV head)
+// merges the splits and applies H.
+#include "kvarn_codes.h"
 
 namespace kvarn {
 
@@ -239,8 +241,7 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
   }
   if (tid < D) *reinterpret_cast<float*>(&s.page[Pg::kGamma + 4 * tid]) = gam_red;
 
-  // ---- groups: min/max, fp16 scale and zero, rounding factors, codes --------------------------
-  uint32_t code[NT][NC];
+  // ---- groups: min/max, fp16 scale and zero, rounding factors; codes packed as they are made ------
   if constexpr (!kIsV) {
     // key groups: channel j over the GS tokens of half h (a lane's tokens lie in one half)
     constexpr int KH = kBlockTokens / GS;
@@ -288,72 +289,71 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
     __syncthreads();
     const int kh = (w * TW) / GS;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float qa = s.qa[kh][chan(c)], qb = s.qb[kh][chan(c)];
+    for (int ho = 0; ho < CH; ++ho) {
+      // the rounding factors of this lane's channel pair (2 ho, 2 ho + 1): one byte of each token
+      const float qa0 = s.qa[kh][chan(2 * ho)], qb0 = s.qb[kh][chan(2 * ho)];
+      const float qa1 = s.qa[kh][chan(2 * ho + 1)], qb1 = s.qb[kh][chan(2 * ho + 1)];
 #pragma unroll
-      for (int i = 0; i < NT; ++i) code[i][c] = rne_code<L>(fmaf(R[i][c], qa, qb));
+      for (int i = 0; i < NT; ++i) {
+        const uint32_t c0 = rne_code<L>(fmaf(R[i][2 * ho], qa0, qb0));
+        const uint32_t c1 = rne_code<L>(fmaf(R[i][2 * ho + 1], qa1, qb1));
+        if constexpr (BITS == 4)
+          s.page[(D / 2) * tok(i) + 16 * ho + n] = static_cast<uint8_t>(c0 | (c1 << 4));
+        else
+          *reinterpret_cast<uint16_t*>(&s.page[D * tok(i) + 32 * ho + 2 * n]) = static_cast<uint16_t>(c0 | (c1 << 8));
+      }
     }
   } else {
-    // value groups: token t over the channels of group vg (a chunk pair's worth or more)
+    // value groups: token t over the channels of group vg (a chunk pair's worth or more); a byte of
+    // the page holds one channel's codes of four consecutive tokens, those of one 4-token row of a tile
     constexpr int VGC = Pg::kVGroup, NVG = D / VGC, CPG = NC / NVG;  // lane channels per group
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int c = 0; c < NC; ++c) R[i][c] *= cf[c];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
+    for (int mt = 0; mt < MT; ++mt) {
+      const int t0 = w * TW + 16 * mt + 4 * g;  // the four consecutive tokens of this lane
 #pragma unroll
       for (int vg = 0; vg < NVG; ++vg) {
-        float a = R[i][CPG * vg], b = R[i][CPG * vg];
+        float qa[4], qb[4];
 #pragma unroll
-        for (int c = CPG * vg + 1; c < CPG * (vg + 1); ++c) {
-          a = fminf(a, R[i][c]);
-          b = fmaxf(b, R[i][c]);
-        }
-        const float mn = mul_rn(row16_min(a), rf[i]);
-        const float mx = mul_rn(row16_max(b), rf[i]);
-        const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
-        const uint32_t zb = float_to_half_bits(mn);
-        const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
-        const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-        if (n == 0) {
-          *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * (kBlockTokens * vg + tok(i))]) =
-              static_cast<uint16_t>(sb);
-          *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * (kBlockTokens * vg + tok(i))]) =
-              static_cast<uint16_t>(zb);
-        }
-        const float qa = rf[i] * inv, qb = -zf * inv;
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * mt + r;
+          float a = R[i][CPG * vg], b = R[i][CPG * vg];
 #pragma unroll
-        for (int c = CPG * vg; c < CPG * (vg + 1); ++c) code[i][c] = rne_code<L>(fmaf(R[i][c], qa, qb));
+          for (int c = CPG * vg + 1; c < CPG * (vg + 1); ++c) {
+            a = fminf(a, R[i][c]);
+            b = fmaxf(b, R[i][c]);
+          }
+          const float mn = mul_rn(row16_min(a), rf[i]);
+          const float mx = mul_rn(row16_max(b), rf[i]);
+          const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
+          const uint32_t zb = float_to_half_bits(mn);
+          const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+          const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+          if (n == 0) {
+            *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * (kBlockTokens * vg + tok(i))]) =
+                static_cast<uint16_t>(sb);
+            *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * (kBlockTokens * vg + tok(i))]) =
+                static_cast<uint16_t>(zb);
+          }
+          qa[r] = rf[i] * inv;
+          qb[r] = -zf * inv;
+        }
+#pragma unroll
+        for (int c = CPG * vg; c < CPG * (vg + 1); ++c) {
+          uint32_t k4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) k4[r] = rne_code<L>(fmaf(R[4 * mt + r][c], qa[r], qb[r]));
+          if constexpr (BITS == 2)
+            s.page[32 * chan(c) + t0 / 4] = static_cast<uint8_t>(k4[0] | (k4[1] << 2) | (k4[2] << 4) | (k4[3] << 6));
+          else
+            *reinterpret_cast<uint16_t*>(&s.page[64 * chan(c) + t0 / 2]) =
+                static_cast<uint16_t>(k4[0] | (k4[1] << 4) | (k4[2] << 8) | (k4[3] << 12));
+        }
       }
     }
-  }
-
-  // ---- pack into the page image ----------------------------------------------------------------
-  if constexpr (!kIsV) {
-#pragma unroll
-    for (int i = 0; i < NT; ++i)
-#pragma unroll
-      for (int ho = 0; ho < CH; ++ho) {
-        if constexpr (BITS == 4)
-          s.page[(D / 2) * tok(i) + 16 * ho + n] = static_cast<uint8_t>(code[i][2 * ho] | (code[i][2 * ho + 1] << 4));
-        else
-          *reinterpret_cast<uint16_t*>(&s.page[D * tok(i) + 32 * ho + 2 * n]) =
-              static_cast<uint16_t>(code[i][2 * ho] | (code[i][2 * ho + 1] << 8));
-      }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int t0 = w * TW + 16 * mt + 4 * g;  // four consecutive tokens of this lane
-        if constexpr (BITS == 2)
-          s.page[32 * chan(c) + t0 / 4] = static_cast<uint8_t>(code[4 * mt][c] | (code[4 * mt + 1][c] << 2) |
-                                                               (code[4 * mt + 2][c] << 4) | (code[4 * mt + 3][c] << 6));
-        else
-          *reinterpret_cast<uint16_t*>(&s.page[64 * chan(c) + t0 / 2]) = static_cast<uint16_t>(
-              code[4 * mt][c] | (code[4 * mt + 1][c] << 4) | (code[4 * mt + 2][c] << 8) | (code[4 * mt + 3][c] << 12));
-      }
   }
   __syncthreads();
   if (ok) {
@@ -476,29 +476,77 @@ __device__ __forceinline__ void lds_fwht_rows(float (*x)[D], int rows) {
   }
 }
 
+// x as fp16 hi + lo: hi the nearest fp16 of x, lo the nearest fp16 of x - hi (exact in fp32), about
+// 22 significant bits together.  hi is pinned so that the value stored and the value subtracted agree.
+__device__ __forceinline__ void split_hl(float x, _Float16& hi, _Float16& lo) {
+  _Float16 h = static_cast<_Float16>(x);
+  asm("" : "+v"(h));
+  hi = h;
+  lo = static_cast<_Float16>(x - static_cast<float>(h));
+}
+
+// Slot of channel j in a key coefficient column: 8-channel groups in the element order of key_codes
+// (channels 0,4,1,5,2,6,3,7) for 4-bit codes, in channel order for 8-bit codes.
+template <int KB>
+__device__ __forceinline__ int key_slot(int j) {
+  return KB == 4 ? (j & ~7) + 2 * (j & 3) + ((j >> 2) & 1) : j;
+}
+// Offset the code conversion adds to the code of channel j (kvarn_codes.h).
+template <int KB>
+__device__ __forceinline__ float key_offset(int j) {
+  return KB == 8 ? 1024.f : ((j & 3) == 1 ? 64.f : 16.f);
+}
+// Slot of token t in a value weight column: 16-token groups in the element order of value_codes and
+// value_codes4 (tokens 0,8,1,9,2,10,3,11 then 4,12,5,13,6,14,7,15).
+__device__ __forceinline__ int value_slot(int t) {
+  const int o = t & 15;
+  return (t & ~15) + 8 * ((o & 7) >> 2) + 2 * (o & 3) + (o >> 3);
+}
+template <int VB>
+__device__ __forceinline__ float value_offset(int t) {
+  return VB == 4 ? 64.f : ((t & 1) ? 16.f : 4.f);
+}
+
 template <int D, int KB, int VB, int GS>
 struct DhdLds {
   using PK = HdPage<D, false, KB, GS>;
   using PV = HdPage<D, true, VB, GS>;
-  static constexpr int KH = kBlockTokens / GS;     // key token halves
-  static constexpr int NVG = D / PV::kVGroup;      // value channel groups
-  float qt[kMaxGroup][D];                          // q~ per head (and the merged output at the end)
-  float acoef[KH][D][kMaxGroup];                   // q~_j 2^gamma_j s, per key half, channel, head
-  float bpart[kDecWaves][KH][kMaxGroup];           // per-wave sums of q~_j 2^gamma_j z
-  float score[kMaxGroup][kBlockTokens];            // scores (log2 units), then p
-  float wcoef[NVG][kBlockTokens][kMaxGroup];       // p_t 2^rho_t s, per value group, token, head
-  float upart[kDecWaves][NVG][kMaxGroup];          // per-wave sums of p_t 2^rho_t z
-  float vs[NVG][kBlockTokens], vz[NVG][kBlockTokens];  // 2^rho_t s and 2^rho_t z of the value page
-  float krho[kBlockTokens];                        // 2^rho_t of the key page
-  float mstat[kMaxGroup], alpha[kMaxGroup], lpage[kMaxGroup];
-  float opart[kDecThreads / D > 1 ? kDecThreads / D : 1][kMaxGroup][D];  // value-side token parts
-  float sm[64][kMaxGroup], sl[64][kMaxGroup];      // split maxima and sums during the merge
+  static constexpr int KH = kBlockTokens / GS;       // key groups per channel (token halves)
+  static constexpr int NVG = D / PV::kVGroup;        // value groups per token (channel groups)
+  static constexpr int kKStride = D + 8;             // fp16 per key coefficient column (padded)
+  static constexpr int kVStride = kBlockTokens + 8;  // fp16 per value weight column (padded)
+  float qt[kMaxGroup][D];                            // q~ per head; the split's o~, then the output
+  _Float16 kcoef[KH][16][kKStride];                  // key B operand: hi (columns 0-7), lo (8-15) of a_j sa
+  _Float16 vcoef[NVG][16][kVStride];                 // value B operand: hi, lo of w_t sw
+  float score[kMaxGroup][kBlockTokens];              // scores (log2 units)
+  float krho[kBlockTokens];                          // 2^rho_t / sa * scale (keys)
+  float vsr[NVG][kBlockTokens], vzr[NVG][kBlockTokens];  // 2^rho_t s sw, 2^rho_t z sw (values)
+  float gsv[D];                                      // 2^gamma_j / sw (values)
+  float bpart[kDecWaves][KH][kMaxGroup];             // per-wave sums of b sa, offsets removed
+  float upart[kDecWaves][NVG][kMaxGroup];            // per-wave sums of u sw, offsets removed
+  float red[kDecWaves][2];                           // per-wave maxima of the key and value scale factors
+  float qred[kDecWaves];                             // per-wave maxima of |q~|
+  float alpha[kMaxGroup];                            // this page's rescale factor per head
+  float mrun[kMaxGroup], lrun[kMaxGroup];            // running maximum and sum per head
+  float sm[64][kMaxGroup], sl[64][kMaxGroup];        // split maxima and sums during the merge
   int last;
 };
 
 }  // namespace
 
 // Decode over pages of D-channel heads: grid (Hkv, batch, splits), four waves per workgroup.
+// Per page, with the notation of the 128-channel decode (a_j = q~_j 2^gamma_j s_j, b = sum_j q~_j
+// 2^gamma_j z_j; w_t = p_t 2^rho_t s_t, u = sum_t p_t 2^rho_t z_t):
+//   (1) largest key and value scale factors of the page, then fp16 hi/lo operands a_j sa and the
+//       constants b, in power-of-two page scales sa and sw that keep every operand below 2^14;
+//   (2) scores on the matrix cores: wave w takes tokens 32w .. 32w+31 (two 16-token tiles, D/32 chained
+//       v_mfma_f32_16x16x32_f16 each), lane (n, g) loading its token's codes of channels
+//       (D/4)g .. (D/4)(g+1)-1; the columns are the heads' hi and lo coefficients;
+//   (3) online softmax per head (wave w: heads w and w + 4), writing the value operands w_t sw;
+//   (4) values on the matrix cores: wave w takes channels (D/4)w .. (D/4)(w+1)-1, 16 per tile, lane
+//       (n, g) loading its channel's codes of tokens 32g .. 32g+31; o~_j <- alpha o~_j + 2^gamma_j (...).
+// Codes enter as fp16 off + c (kvarn_codes.h); the offsets leave with sums of the fp16 operands used.
+// Each part of a page is loaded into registers right after its last use on the previous page.
 template <int D, int KB, int VB, int GS>
 __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
@@ -509,15 +557,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
   using PK = typename L::PK;
   using PV = typename L::PV;
   constexpr int KH = L::KH, NVG = L::NVG, VGC = PV::kVGroup;
-  constexpr int PS = D + 2;                           // partial stride: o~[D], m, l
-  constexpr int VPARTS = kDecThreads / D > 1 ? kDecThreads / D : 1;  // threads per value channel
-  constexpr int VTOK = kBlockTokens / VPARTS;         // tokens per value thread
-  constexpr int CPT = D / 2;                          // key channels per score thread
+  constexpr int PS = D + 2;              // partial stride: o~[D], m, l
+  constexpr int KC = D / 32;             // 32-channel steps of a key tile
+  constexpr int KWT = D * KB / 128;      // key code dwords of a lane per token tile
+  constexpr int VMT = D / 64;            // 16-channel value tiles per wave
+  constexpr int VWT = VB;                // value code dwords of a lane per value tile (32 tokens)
+  static_assert(KWT == 2 || KWT % 4 == 0, "key code loads");
   __shared__ __align__(16) L s;
 
   const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = hq / hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int sl_b = seq_lens[b];
   float* out_b = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * D;
   const bool bad = sl_b < 0 || sl_b > max_blocks * kBlockTokens || (sl_b & (kBlockTokens - 1)) != 0;
@@ -534,7 +584,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
   const size_t pair = static_cast<size_t>(b) * hkv + kvh;
   float* pbase = part + pair * max_splits * kMaxGroup * PS;
 
-  // ---- q~ = H q / sqrt(D) for the G heads (rows past G are zero) --------------------------------
+  // ---- q~ = H q / sqrt(D) for the G heads (rows past G are zero), and max |q~| -------------------
   const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * D;
   for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
     const int h = e / D, j = e - h * D;
@@ -542,55 +592,178 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
   }
   __syncthreads();
   lds_fwht_rows<D>(s.qt, kMaxGroup);
-  for (int e = tid; e < kMaxGroup * D; e += kDecThreads) s.qt[e / D][e % D] *= HdGeom<D>::kInvSqrtD;
-  __syncthreads();
-
-  // value side: thread owns channel vj, tokens [vpart * VTOK, + VTOK)
-  const int vj = tid % D, vpart = tid / D;
-  const bool vthread = vpart < VPARTS;
-  const int vgrp = vj / VGC;
-  float o[kMaxGroup];
-  float m_run[kMaxGroup], l_run[kMaxGroup];
-#pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    o[h] = 0.f;
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
+  {
+    float qm = 0.f;
+    for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
+      const float v = s.qt[e / D][e % D] * HdGeom<D>::kInvSqrtD;
+      s.qt[e / D][e % D] = v;
+      qm = fmaxf(qm, fabsf(v));
+    }
+    qm = wave_maxp(qm);
+    if (lane == 0) s.qred[w] = qm;
   }
-  // score side: thread owns token st, channel half sh
-  const int st = tid >> 1, sh = tid & 1;
+  if (tid < kMaxGroup) {
+    s.mrun[tid] = -INFINITY;
+    s.lrun[tid] = 0.f;
+  }
+  __syncthreads();
+  const float qmax = fmaxf(fmaxf(s.qred[0], s.qred[1]), fmaxf(s.qred[2], s.qred[3]));
+
+  // exponent patterns of the code conversions, kept in vector registers
+  uint32_t mag4 = 0x44004400u, mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag1024 = 0x64006400u;
+  asm volatile("" : "+v"(mag4), "+v"(mag16), "+v"(mag64), "+v"(mag1024));
 
   const int p0 = split * blocks_per_split;
   const int p1 = min(nblk, p0 + blocks_per_split);
+  const int32_t* bt_b = block_table + static_cast<size_t>(b) * max_blocks;
   bool bad_page = false;
-  for (int pi = p0; pi < p1; ++pi) {
-    const int page = block_table[static_cast<size_t>(b) * max_blocks + pi];
-    if (page < 0 || page >= num_pages) {
+  // next valid page at or after position pi (page ids outside [0, num_pages) are skipped)
+  auto next_valid = [&](int pi) {
+    for (; pi < p1; ++pi) {
+      const int pg = bt_b[pi];
+      if (pg >= 0 && pg < num_pages) return pi;
       bad_page = true;
-      continue;
     }
-    const uint8_t* kp = k_pool + (static_cast<size_t>(page) * hkv + kvh) * PK::kBytes;
-    const uint8_t* vp = v_pool + (static_cast<size_t>(page) * hkv + kvh) * PV::kBytes;
-    // (1) page coefficients
+    return p1;
+  };
+  const int kh_w = (32 * w) / GS;  // key group (token half) of this wave's tokens
+  // One page's data in registers.
+  uint32_t kw[2][KWT];   // key codes: token tile mt, token 32w + 16mt + n, channel quarter g
+  uint32_t vw[VMT][VWT];  // value codes: channel (D/4)w + 16mt + n, tokens 32g .. 32g+31
+  float m_kg = 0.f, m_ks[KH], m_kz[KH], m_vg = 0.f;  // channel tid: key gamma, scale, zero; value gamma
+  float m_kr = 0.f, m_vr = 0.f, m_vs[NVG], m_vz[NVG];  // token tid: key rho; value rho, scale, zero
+#pragma unroll
+  for (int kh = 0; kh < KH; ++kh) m_ks[kh] = m_kz[kh] = 0.f;
+#pragma unroll
+  for (int vg = 0; vg < NVG; ++vg) m_vs[vg] = m_vz[vg] = 0.f;
+  auto page_k = [&](int pi) { return k_pool + (static_cast<size_t>(bt_b[pi]) * hkv + kvh) * PK::kBytes; };
+  auto page_v = [&](int pi) { return v_pool + (static_cast<size_t>(bt_b[pi]) * hkv + kvh) * PV::kBytes; };
+  auto load_meta = [&](int pi) {
+    const uint8_t* kp = page_k(pi);
+    const uint8_t* vp = page_v(pi);
+    if (tid < D) {
+      m_kg = reinterpret_cast<const float*>(kp + PK::kGamma)[tid];
+      m_vg = reinterpret_cast<const float*>(vp + PV::kGamma)[tid];
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) {
+        m_ks[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kScale)[D * kh + tid]);
+        m_kz[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kZero)[D * kh + tid]);
+      }
+    }
+    if (tid < kBlockTokens) {
+      m_kr = reinterpret_cast<const float*>(kp + PK::kRho)[tid];
+      m_vr = reinterpret_cast<const float*>(vp + PV::kRho)[tid];
+#pragma unroll
+      for (int vg = 0; vg < NVG; ++vg) {
+        m_vs[vg] = half_bits_to_float(reinterpret_cast<const uint16_t*>(vp + PV::kScale)[kBlockTokens * vg + tid]);
+        m_vz[vg] = half_bits_to_float(reinterpret_cast<const uint16_t*>(vp + PV::kZero)[kBlockTokens * vg + tid]);
+      }
+    }
+  };
+  auto load_k = [&](int pi) {
+    const uint8_t* kp = page_k(pi);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const uint8_t* src = kp + (32 * w + 16 * mt + n) * (D * KB / 8) + g * (D * KB / 32);
+      if constexpr (KWT == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        kw[mt][0] = x[0];
+        kw[mt][1] = x[1];
+      } else {
+#pragma unroll
+        for (int k4 = 0; k4 < KWT / 4; ++k4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(src + 16 * k4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kw[mt][4 * k4 + e] = x[e];
+        }
+      }
+    }
+  };
+  auto load_v = [&](int pi) {
+    const uint8_t* vp = page_v(pi);
+#pragma unroll
+    for (int mt = 0; mt < VMT; ++mt) {
+      const uint8_t* src = vp + ((D / 4) * w + 16 * mt + n) * (kBlockTokens * VB / 8) + g * (32 * VB / 8);
+      if constexpr (VB == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        vw[mt][0] = x[0];
+        vw[mt][1] = x[1];
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vw[mt][e] = x[e];
+      }
+    }
+  };
+  f32x4 oacc[VMT];  // o~ (rotated basis) of channels (D/4)w + 16mt + 4g + r, head n & 7
+#pragma unroll
+  for (int mt = 0; mt < VMT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int cur = next_valid(p0);
+  if (cur < p1) {
+    load_meta(cur);
+    load_k(cur);
+    load_v(cur);
+  }
+  while (cur < p1) {
+    const int nxt = next_valid(cur + 1);
+    const int pf = nxt < p1 ? nxt : cur;  // page whose data is fetched during this one
+    // (1) largest scale factors, then the operands and constants of the page
     {
+      float ek = 0.f, ev = 0.f;
+      if (tid < D) {
+        float mx = 0.f;
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) mx = fmaxf(mx, m_ks[kh]);
+        ek = ex2(m_kg) * mx;
+      }
+      if (tid < kBlockTokens) {
+        float mx = 0.f;
+#pragma unroll
+        for (int vg = 0; vg < NVG; ++vg) mx = fmaxf(mx, m_vs[vg]);
+        ev = ex2(m_vr) * mx;
+      }
+      ek = wave_maxp(ek);
+      ev = wave_maxp(ev);
+      if (lane == 0) {
+        s.red[w][0] = ek;
+        s.red[w][1] = ev;
+      }
+    }
+    // every wave is past the previous page's value step (which reads gsv, vcoef, upart, alpha)
+    __syncthreads();
+    {
+      const float ek = fmaxf(fmaxf(s.red[0][0], s.red[1][0]), fmaxf(s.red[2][0], s.red[3][0]));
+      const float ev = fmaxf(fmaxf(s.red[0][1], s.red[1][1]), fmaxf(s.red[2][1], s.red[3][1]));
+      // |a_j sa| < 2^14 and, as p <= 1, |w_t sw| < 2^14; with no positive factor the page keeps unit scale
+      const float kprod = qmax * ek;
+      int ex = 0, exv = 0;
+      frexpf(kprod, &ex);
+      frexpf(ev, &exv);
+      ex = min(max(ex, -100), 100);
+      exv = min(max(exv, -100), 100);
+      const float sa = kprod > 0.f ? pow2i(14 - ex) : 1.f, inv_sa = kprod > 0.f ? pow2i(ex - 14) : 1.f;
+      const float sw = ev > 0.f ? pow2i(14 - exv) : 1.f, inv_sw = ev > 0.f ? pow2i(exv - 14) : 1.f;
       float bp[KH][kMaxGroup];
 #pragma unroll
       for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) bp[kh][h] = 0.f;
-      for (int j = tid; j < D; j += kDecThreads) {
-        const float gj = ex2(reinterpret_cast<const float*>(kp + PK::kGamma)[j]);
+      if (tid < D) {
+        const int j = tid, slot = key_slot<KB>(j);
+        const float gk = ex2(m_kg) * sa, off = key_offset<KB>(j);
 #pragma unroll
-        for (int kh = 0; kh < KH; ++kh) {
-          const float sj = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kScale)[D * kh + j]);
-          const float zj = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kZero)[D * kh + j]);
+        for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
           for (int h = 0; h < kMaxGroup; ++h) {
-            const float qg = s.qt[h][j] * gj;
-            s.acoef[kh][j][h] = qg * sj;
-            bp[kh][h] = fmaf(qg, zj, bp[kh][h]);
+            const float qg = s.qt[h][j] * gk;
+            _Float16 hi, lo;
+            split_hl(qg * m_ks[kh], hi, lo);
+            s.kcoef[kh][h][slot] = hi;
+            s.kcoef[kh][8 + h][slot] = lo;
+            bp[kh][h] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
           }
-        }
+        s.gsv[j] = ex2(m_vg) * inv_sw;
       }
 #pragma unroll
       for (int kh = 0; kh < KH; ++kh)
@@ -600,217 +773,150 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
           if (lane == 0) s.bpart[w][kh][h] = t;
         }
       if (tid < kBlockTokens) {
-        const int t = tid;
-        s.krho[t] = ex2(reinterpret_cast<const float*>(kp + PK::kRho)[t]);
-        const float vr = ex2(reinterpret_cast<const float*>(vp + PV::kRho)[t]);
+        s.krho[tid] = ex2(m_kr) * inv_sa * scale_log2;
+        const float vr = ex2(m_vr) * sw;
 #pragma unroll
         for (int vg = 0; vg < NVG; ++vg) {
-          s.vs[vg][t] = vr * half_bits_to_float(reinterpret_cast<const uint16_t*>(vp + PV::kScale)[kBlockTokens * vg + t]);
-          s.vz[vg][t] = vr * half_bits_to_float(reinterpret_cast<const uint16_t*>(vp + PV::kZero)[kBlockTokens * vg + t]);
+          s.vsr[vg][tid] = vr * m_vs[vg];
+          s.vzr[vg][tid] = vr * m_vz[vg];
         }
       }
+      load_meta(pf);
     }
     __syncthreads();
-    // (2) scores: thread (token st, channel half sh)
+    // (2) scores of tokens 32w + 16mt + 4g + r for the head of column n (hi and lo columns summed)
     {
-      const int kh = st / GS;
-      float acc[kMaxGroup];
+      f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      const _Float16* cb = &s.kcoef[kh_w][n][(D / 4) * g];
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.f;
-      if constexpr (KB == 4) {
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(kp + (D / 2) * st + (D / 4) * sh);
-#pragma unroll 2
-        for (int k = 0; k < CPT / 8; ++k) {
-          const uint32_t x = row[k];
+      for (int kc = 0; kc < KC; ++kc) {
+        const f16x8 bop = *reinterpret_cast<const f16x8*>(cb + 8 * kc);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float c = static_cast<float>((x >> (4 * e)) & 15u);
-            const int j = CPT * sh + 8 * k + e;
-            const float4 a0 = *reinterpret_cast<const float4*>(&s.acoef[kh][j][0]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&s.acoef[kh][j][4]);
-            acc[0] = fmaf(a0.x, c, acc[0]);
-            acc[1] = fmaf(a0.y, c, acc[1]);
-            acc[2] = fmaf(a0.z, c, acc[2]);
-            acc[3] = fmaf(a0.w, c, acc[3]);
-            acc[4] = fmaf(a1.x, c, acc[4]);
-            acc[5] = fmaf(a1.y, c, acc[5]);
-            acc[6] = fmaf(a1.z, c, acc[6]);
-            acc[7] = fmaf(a1.w, c, acc[7]);
+        for (int mt = 0; mt < 2; ++mt) {
+          f16x8 aop;
+          if constexpr (KB == 4) {
+            aop = key_codes(kw[mt][kc], mag16, mag64);
+          } else {
+            aop = key_codes8(kw[mt][2 * kc], kw[mt][2 * kc + 1], mag1024);
           }
-        }
-      } else {
-        const uint32_t* row = reinterpret_cast<const uint32_t*>(kp + D * st + (D / 2) * sh);
-#pragma unroll 2
-        for (int k = 0; k < CPT / 4; ++k) {
-          const uint32_t x = row[k];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float c = static_cast<float>((x >> (8 * e)) & 255u);
-            const int j = CPT * sh + 4 * k + e;
-            const float4 a0 = *reinterpret_cast<const float4*>(&s.acoef[kh][j][0]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&s.acoef[kh][j][4]);
-            acc[0] = fmaf(a0.x, c, acc[0]);
-            acc[1] = fmaf(a0.y, c, acc[1]);
-            acc[2] = fmaf(a0.z, c, acc[2]);
-            acc[3] = fmaf(a0.w, c, acc[3]);
-            acc[4] = fmaf(a1.x, c, acc[4]);
-            acc[5] = fmaf(a1.y, c, acc[5]);
-            acc[6] = fmaf(a1.z, c, acc[6]);
-            acc[7] = fmaf(a1.w, c, acc[7]);
-          }
+          d[mt] = mfma16x16x32(aop, bop, d[mt]);
         }
       }
-      // the two halves of the token (lanes 2k, 2k+1) add in the same order
+      load_k(pf);
+      const int h = n & 7;
+      const float bsum = s.bpart[0][kh_w][h] + s.bpart[1][kh_w][h] + s.bpart[2][kh_w][h] + s.bpart[3][kh_w][h];
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        const float other = dpp<kDppXor1>(acc[h]);
-        acc[h] = sh ? other + acc[h] : acc[h] + other;
-      }
-      if (sh == 0) {
-        const float rt = s.krho[st] * scale_log2;
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          const float bsum = s.bpart[0][kh][h] + s.bpart[1][kh][h] + s.bpart[2][kh][h] + s.bpart[3][kh][h];
-          s.score[h][st] = (acc[h] + bsum) * rt;
+        for (int r = 0; r < 4; ++r) {
+          const float x = d[mt][r] + dpp<kDppXor8>(d[mt][r]);
+          const int t = 32 * w + 16 * mt + 4 * g + r;
+          if (n < 8) s.score[h][t] = (x + bsum) * s.krho[t];
         }
-      }
     }
     __syncthreads();
     // (3) online softmax per head: wave w takes heads w and w + 4; lane l tokens 2l, 2l + 1
-    for (int h = w; h < kMaxGroup; h += kDecWaves) {
-      if (h >= G) {
-        if (lane == 0) {
-          s.alpha[h] = 1.f;
-          s.lpage[h] = 0.f;
-          s.mstat[h] = 0.f;
+    {
+      const int t0 = 2 * lane, t1 = 2 * lane + 1;
+      const int v0 = value_slot(t0), v1 = value_slot(t1);
+      for (int h = w; h < kMaxGroup; h += kDecWaves) {
+        if (h >= G) {
+          if (lane == 0) s.alpha[h] = 1.f;
+#pragma unroll
+          for (int vg = 0; vg < NVG; ++vg) {
+            s.vcoef[vg][h][v0] = s.vcoef[vg][8 + h][v0] = static_cast<_Float16>(0.f);
+            s.vcoef[vg][h][v1] = s.vcoef[vg][8 + h][v1] = static_cast<_Float16>(0.f);
+            if (lane == 0) s.upart[w][vg][h] = 0.f;
+          }
+          continue;
         }
+        const float s0 = s.score[h][t0], s1 = s.score[h][t1];
+        const float pm = wave_maxp(fmaxf(s0, s1));
+        const float mold = s.mrun[h];
+        const float mnew = fmaxf(mold, pm);
+        const float e0 = ex2(s0 - mnew), e1 = ex2(s1 - mnew);
+        const float lp = wave_sump(e0 + e1);
 #pragma unroll
         for (int vg = 0; vg < NVG; ++vg) {
-          s.wcoef[vg][2 * lane][h] = 0.f;
-          s.wcoef[vg][2 * lane + 1][h] = 0.f;
-          if (lane == 0) s.upart[w][vg][h] = 0.f;
+          _Float16 h0, l0, h1, l1;
+          split_hl(e0 * s.vsr[vg][t0], h0, l0);
+          split_hl(e1 * s.vsr[vg][t1], h1, l1);
+          s.vcoef[vg][h][v0] = h0;
+          s.vcoef[vg][8 + h][v0] = l0;
+          s.vcoef[vg][h][v1] = h1;
+          s.vcoef[vg][8 + h][v1] = l1;
+          const float off = value_offset<VB>(t0) * (static_cast<float>(h0) + static_cast<float>(l0)) +
+                            value_offset<VB>(t1) * (static_cast<float>(h1) + static_cast<float>(l1));
+          const float u = wave_sump(fmaf(e0, s.vzr[vg][t0], e1 * s.vzr[vg][t1]) - off);
+          if (lane == 0) s.upart[w][vg][h] = u;
         }
-        continue;
+        if (lane == 0) {
+          const float al = mold == -INFINITY ? 0.f : ex2(mold - mnew);
+          s.alpha[h] = al;
+          s.lrun[h] = fmaf(al, s.lrun[h], lp);
+          s.mrun[h] = mnew;
+        }
       }
-      const float s0 = s.score[h][2 * lane], s1 = s.score[h][2 * lane + 1];
-      const float pm = wave_maxp(fmaxf(s0, s1));
-      const float mnew = fmaxf(m_run[h], pm);
-      const float e0 = ex2(s0 - mnew), e1 = ex2(s1 - mnew);
-      const float lp = wave_sump(e0 + e1);
+      // each head's u sums go to the slot of the wave that handles it; clear this wave's other slots
+      for (int h = 0; h < kMaxGroup; ++h)
+        if ((h % kDecWaves) != w && lane == 0) {
 #pragma unroll
-      for (int vg = 0; vg < NVG; ++vg) {
-        s.wcoef[vg][2 * lane][h] = e0 * s.vs[vg][2 * lane];
-        s.wcoef[vg][2 * lane + 1][h] = e1 * s.vs[vg][2 * lane + 1];
-        const float u = wave_sump(fmaf(e0, s.vz[vg][2 * lane], e1 * s.vz[vg][2 * lane + 1]));
-        if (lane == 0) s.upart[w][vg][h] = u;
-      }
-      if (lane == 0) {
-        s.alpha[h] = m_run[h] == -INFINITY ? 0.f : ex2(m_run[h] - mnew);
-        s.lpage[h] = lp;
-        s.mstat[h] = mnew;
-      }
+          for (int vg = 0; vg < NVG; ++vg) s.upart[w][vg][h] = 0.f;
+        }
     }
-    // heads h >= G and waves without heads leave upart of their (w, h) unwritten above only when
-    // h >= G is handled by another wave: clear this wave's other slots
-    for (int h = 0; h < kMaxGroup; ++h)
-      if ((h % kDecWaves) != w && lane == 0) {
-#pragma unroll
-        for (int vg = 0; vg < NVG; ++vg) s.upart[w][vg][h] = 0.f;
-      }
     __syncthreads();
-    // every thread keeps the running statistics of every head
+    // (4) values: channels (D/4)w + 16mt + 4g + r for the head of column n (hi and lo columns summed)
+    {
+      const int h = n & 7;
+      const float al = s.alpha[h];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
-        l_run[h] = fmaf(s.alpha[h], l_run[h], s.lpage[h]);
-        m_run[h] = s.mstat[h];
-      }
-    }
-    // (4) values: o~_j <- alpha o~_j + 2^gamma_j (sum_t w_t c_tj + u); the u term from part 0 only
-    if (vthread) {
-      float acc[kMaxGroup];
+      for (int mt = 0; mt < VMT; ++mt) {
+        const int jb = (D / 4) * w + 16 * mt;
+        const int vg = jb / VGC;
+        const _Float16* wb = &s.vcoef[vg][n][32 * g];
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.f;
-      const int t0 = vpart * VTOK;
-      if constexpr (VB == 2) {
-        const uint32_t* col = reinterpret_cast<const uint32_t*>(vp + 32 * vj + t0 / 4);
-#pragma unroll 2
-        for (int k = 0; k < VTOK / 16; ++k) {
-          const uint32_t x = col[k];
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float c = static_cast<float>((x >> (2 * e)) & 3u);
-            const int t = t0 + 16 * k + e;
-            const float4 a0 = *reinterpret_cast<const float4*>(&s.wcoef[vgrp][t][0]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&s.wcoef[vgrp][t][4]);
-            acc[0] = fmaf(a0.x, c, acc[0]);
-            acc[1] = fmaf(a0.y, c, acc[1]);
-            acc[2] = fmaf(a0.z, c, acc[2]);
-            acc[3] = fmaf(a0.w, c, acc[3]);
-            acc[4] = fmaf(a1.x, c, acc[4]);
-            acc[5] = fmaf(a1.y, c, acc[5]);
-            acc[6] = fmaf(a1.z, c, acc[6]);
-            acc[7] = fmaf(a1.w, c, acc[7]);
+        for (int u = 0; u < 2; ++u) {
+          f16x8 c0, c1;
+          if constexpr (VB == 2) {
+            value_codes(vw[mt][u], mag4, mag16, c0, c1);
+          } else {
+            value_codes4(vw[mt][2 * u], vw[mt][2 * u + 1], mag64, c0, c1);
           }
+          d = mfma16x16x32(c0, *reinterpret_cast<const f16x8*>(wb + 16 * u), d);
+          d = mfma16x16x32(c1, *reinterpret_cast<const f16x8*>(wb + 16 * u + 8), d);
         }
-      } else {
-        const uint32_t* col = reinterpret_cast<const uint32_t*>(vp + 64 * vj + t0 / 2);
-#pragma unroll 2
-        for (int k = 0; k < VTOK / 8; ++k) {
-          const uint32_t x = col[k];
+        const float uh = s.upart[0][vg][h] + s.upart[1][vg][h] + s.upart[2][vg][h] + s.upart[3][vg][h];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float c = static_cast<float>((x >> (4 * e)) & 15u);
-            const int t = t0 + 8 * k + e;
-            const float4 a0 = *reinterpret_cast<const float4*>(&s.wcoef[vgrp][t][0]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&s.wcoef[vgrp][t][4]);
-            acc[0] = fmaf(a0.x, c, acc[0]);
-            acc[1] = fmaf(a0.y, c, acc[1]);
-            acc[2] = fmaf(a0.z, c, acc[2]);
-            acc[3] = fmaf(a0.w, c, acc[3]);
-            acc[4] = fmaf(a1.x, c, acc[4]);
-            acc[5] = fmaf(a1.y, c, acc[5]);
-            acc[6] = fmaf(a1.z, c, acc[6]);
-            acc[7] = fmaf(a1.w, c, acc[7]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float x = d[r] + dpp<kDppXor8>(d[r]);
+          oacc[mt][r] = fmaf(al, oacc[mt][r], s.gsv[jb + 4 * g + r] * (x + uh));
         }
       }
-      const float gj = ex2(reinterpret_cast<const float*>(vp + PV::kGamma)[vj]);
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        float u = 0.f;
-        if (vpart == 0) u = s.upart[0][vgrp][h] + s.upart[1][vgrp][h] + s.upart[2][vgrp][h] + s.upart[3][vgrp][h];
-        o[h] = fmaf(s.alpha[h], o[h], gj * (acc[h] + u));
-      }
+      load_v(pf);
     }
-    __syncthreads();  // the next page rewrites the coefficient arrays
+    // no barrier here: the next page's step (1) writes only s.red before its barrier
+    cur = nxt;
   }
   if (bad_page && tid == 0 && flags) atomicOr(flags, kFlagBadPage);
 
   // ---- this split's partial: o~ (rotated basis), m, l per head ----------------------------------
-  if (vthread) {
+  __syncthreads();  // every wave is out of the page loop (q~ is no longer read)
+  if (n < 8) {
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) s.opart[vpart][h][vj] = o[h];
+    for (int mt = 0; mt < VMT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.qt[n][(D / 4) * w + 16 * mt + 4 * g + r] = oacc[mt][r];
   }
   __syncthreads();
   for (int e = tid; e < G * D; e += kDecThreads) {
     const int h = e / D, j = e - h * D;
-    float t = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < VPARTS; ++pp) t += s.opart[pp][h][j];
-    store_coherent(pbase + (static_cast<size_t>(split) * kMaxGroup + h) * PS + j, t);
+    store_coherent(pbase + (static_cast<size_t>(split) * kMaxGroup + h) * PS + j, s.qt[h][j]);
   }
   if (tid < G) {
     float* pp = pbase + (static_cast<size_t>(split) * kMaxGroup + tid) * PS;
-    float mr = 0.f, lr = 0.f;
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h)
-      if (h == tid) {
-        mr = m_run[h];
-        lr = l_run[h];
-      }
-    store_coherent(pp + D, mr);
-    store_coherent(pp + D + 1, lr);
+    store_coherent(pp + D, s.mrun[tid]);
+    store_coherent(pp + D + 1, s.lrun[tid]);
   }
   // Hand-off without fences, as in the 128-channel decode: partials go through agent-scope (sc1)
   // atomic accesses, vmcnt(0) covers the stores before the workgroup counts in with an agent-scope
