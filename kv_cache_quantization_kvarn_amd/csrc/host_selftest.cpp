@@ -126,6 +126,29 @@ void test_plans() {
   check(p.blocks_per_split == 8 && p.max_splits == 4, "plan: 64 x 2 heads x 32 pages");
   p = kvarn_host::plan_decode(64, 2, 32, 32);
   check(p.blocks_per_split == 32 && p.max_splits == 1, "plan: 32 CUs");
+  // the kernel choice: two workgroups per CU with prefetch while splits stay at 16 pages or fewer
+  kvarn_host::DecodeChoice c = kvarn_host::choose_decode(64, 2, 32, 256, false, true);
+  check(c.prefetch && c.plan.blocks_per_split == 8 && c.plan.max_splits == 4, "choice: 64 x 2 x 32 prefetches");
+  c = kvarn_host::choose_decode(128, 8, 256, 256, false, true);
+  check(!c.prefetch && c.plan.blocks_per_split == 32 && c.plan.max_splits == 8, "choice: long splits stream");
+  c = kvarn_host::choose_decode(16, 8, 64, 256, false, false);
+  check(!c.prefetch && c.plan.blocks_per_split == 12, "choice: format without a prefetching kernel");
+  // one 131,072-token sequence: 64 splits of 16 pages; with an fp16 tail the 63-split cap makes them 20
+  c = kvarn_host::choose_decode(1, 8, 1024, 256, false, true);
+  check(c.prefetch && c.plan.blocks_per_split == 16 && c.plan.max_splits == 64, "choice: one long sequence");
+  c = kvarn_host::choose_decode(1, 8, 1024, 256, true, true);
+  check(!c.prefetch && c.plan.blocks_per_split == 20 && c.plan.max_splits == 53, "choice: one long sequence, tail");
+  // every choice fits the workspace
+  for (int cus : {32, 256, 304})
+    for (int batch : {1, 3, 64, 1000})
+      for (int mb = 1; mb <= 700; mb += 23)
+        for (bool tail : {false, true})
+          for (bool can : {false, true}) {
+            c = kvarn_host::choose_decode(batch, 8, mb, cus, tail, can);
+            check(kvarn_host::workspace_bytes(batch, 8, mb, 128, cus) >=
+                      kvarn_host::counter_bytes(batch, 8) + kvarn_host::partial_bytes(batch, 8, c.plan.max_splits, 128),
+                  "choice fits the workspace", batch, mb, cus);
+          }
 }
 
 void test_quantize() {
@@ -215,10 +238,12 @@ void test_decode() {
     return a;
   };
   bool run = false;
-  kvarn_host::DecodePlan p{};
+  kvarn_host::DecodeChoice p{};
   using K = kvarn_host::DecodeKind;
   kvarn_host::DecodeArgs a = args(K::packed, &c128, 16, 32, 8, 64);
-  check(kvarn_host::validate_decode(a, &run, &p) == KVARN_OK && run && p.blocks_per_split == 12 && p.max_splits == 6,
+  // 16 x 8 heads x 64 pages at two workgroups per CU: 16 pages per split, short enough to prefetch
+  check(kvarn_host::validate_decode(a, &run, &p) == KVARN_OK && run && p.prefetch && p.plan.blocks_per_split == 16 &&
+            p.plan.max_splits == 4,
         "decode ok");
   a.ws_bytes = kvarn_host::workspace_bytes(16, 8, 64, 128, 256);
   check(kvarn_host::validate_decode(a, &run, &p) == KVARN_OK && run, "decode with the exact workspace");
@@ -277,12 +302,14 @@ void test_decode() {
               check(s == KVARN_OK && batch > 0 && batch <= 65535 && hh[1] > 0 && hh[1] <= 65535 && mb >= 0 &&
                         static_cast<long>(mb) * 128 + 127 <= INT_MAX && hh[0] % hh[1] == 0 && hh[0] / hh[1] <= 8,
                     "decode launches only valid shapes", batch, hh[0], mb);
-              check(p.blocks_per_split % 4 == 0 && p.max_splits >= 1 && p.max_splits <= 64 &&
-                        static_cast<long>(p.max_splits - (kind == K::packed_tail ? 1 : 0)) * p.blocks_per_split >=
-                            (mb > 0 ? mb : 1),
+              check(p.plan.blocks_per_split % 4 == 0 && p.plan.max_splits >= 1 && p.plan.max_splits <= 64 &&
+                        static_cast<long>(p.plan.max_splits - (kind == K::packed_tail ? 1 : 0)) *
+                                p.plan.blocks_per_split >= (mb > 0 ? mb : 1),
                     "decode plan", batch, hh[0], mb);
+              check(!p.prefetch || (kind != K::fp16 && p.plan.blocks_per_split <= 16), "prefetch only for short "
+                    "packed splits", batch, hh[0], mb);
               if (scratch)
-                check(kvarn_host::partial_bytes(batch, hh[1], p.max_splits, 128) <=
+                check(kvarn_host::partial_bytes(batch, hh[1], p.plan.max_splits, 128) <=
                           kvarn_host::kScratchBytes - kvarn_host::kScratchCounterBytes,
                       "no-alloc partials fit", batch, hh[0], mb);
             }

@@ -22,7 +22,7 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, 
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
                          const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int group,
                          int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
-                         uint32_t* counters, uint32_t* flags, hipStream_t stream);
+                         uint32_t* counters, uint32_t* flags, bool prefetch, hipStream_t stream);
 hipError_t launch_fp16_decode(const void* q, const void* k_cache, const void* v_cache, int num_pages,
                               const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int batch, int hq,
                               int hkv, int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
@@ -46,6 +46,7 @@ hipError_t launch_prefill(const void* q, int max_q, const void* k_pool, const vo
 }  // namespace kvarn
 
 using kvarn_host::DecodeArgs;
+using kvarn_host::DecodeChoice;
 using kvarn_host::DecodeKind;
 using kvarn_host::DecodePlan;
 using kvarn_host::fail;
@@ -174,9 +175,10 @@ kvarn_status decode_common(DecodeArgs a, uint32_t* dev_flags, float softmax_scal
                            void* stream) {
   a.cus = device_cus();
   bool run = false;
-  DecodePlan p{};
-  kvarn_status s = kvarn_host::validate_decode(a, &run, &p);
+  DecodeChoice choice{};
+  kvarn_status s = kvarn_host::validate_decode(a, &run, &choice);
   if (s != KVARN_OK || !run) return s;
+  const DecodePlan& p = choice.plan;
   const int D = a.cfg->head_dim;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(static_cast<float>(D));
   const float scale_log2 = scale * 1.4426950408889634f;
@@ -209,7 +211,7 @@ kvarn_status decode_common(DecodeArgs a, uint32_t* dev_flags, float softmax_scal
                                             tail ? a.k_tail : nullptr, tail ? a.v_tail : nullptr, a.batch,
                                             a.num_q_heads, a.num_kv_heads, a.cfg->k_bits, a.cfg->v_bits,
                                             a.cfg->group_size, p.blocks_per_split, p.max_splits, scale_log2, out, part,
-                                            counters, dev_flags, st));
+                                            counters, dev_flags, choice.prefetch, st));
 }
 
 DecodeArgs decode_args(DecodeKind kind, const kvarn_config* cfg, const void* q, const void* k_pool, const void* v_pool,

@@ -223,8 +223,10 @@ struct DecFormat {
   static constexpr int kCh1 = KB == 8 ? 1 : 4;
   // resident waves per SIMD: byte-wide keys and two groups per channel / token need more registers
   // (4-bit keys with 4-bit values keep three waves at the cost of a two-register spill, which is
-  // faster than two waves)
+  // faster than two waves).  The prefetching kernel (kCanPrefetch formats only) runs at two.
   static constexpr int kMinWaves = KB == 4 && GS == 128 ? 3 : 2;
+  // Formats whose next-page registers fit at two waves per SIMD without spills.
+  static constexpr bool kCanPrefetch = KB == 4 && GS == 128;
 };
 
 // Coefficient slots of a lane: channels ch0 and ch0 + kCh1, ch0 = 32*(lane/16) + 8*((lane/4)%4) +
@@ -249,41 +251,36 @@ struct PageRegs {
   bool ok;
 };
 
-// Issues every load of one page without a branch: a bad page id reads page 0 instead (the
-// caller guarantees num_pages > 0) and only clears `ok`.
+// Page bases of one (page, KV head).  A bad page id reads page 0 instead (the caller guarantees
+// num_pages > 0) and only clears `ok`, so every load is issued without a branch.
+struct PagePtrs {
+  const uint8_t* kp;
+  const uint8_t* vp;
+  bool ok;
+};
 template <int KB, int VB, int GS>
-__device__ __forceinline__ void load_page(PageRegs<KB, VB, GS>& P, int page, int num_pages, int hkv, int kvh,
-                                          const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
-                                          int lane, int n, int g, int ch0) {
+__device__ __forceinline__ PagePtrs page_ptrs(int page, int num_pages, int hkv, int kvh,
+                                              const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool) {
+  using F = DecFormat<KB, VB, GS>;
+  PagePtrs r;
+  r.ok = page >= 0 && page < num_pages;
+  const int safe = r.ok ? page : 0;
+  r.kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kKPage;
+  r.vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kVPage;
+  return r;
+}
+
+// The three parts of a page a lane loads: metadata (consumed first), key codes, value codes.  Lane
+// offsets are recomputed for every page (a few integer operations) rather than kept live across the
+// page loop, where registers are short.
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void load_meta(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int lane, int ch0) {
   using F = DecFormat<KB, VB, GS>;
   using Meta = typename F::Meta;
-  P.ok = page >= 0 && page < num_pages;
-  const int safe = P.ok ? page : 0;
-  // lane offsets are recomputed for every page (a few integer operations) rather than kept live
-  // across the page loop, where registers are short
-  asm volatile("" : "+v"(lane), "+v"(n), "+v"(g), "+v"(ch0));
-  const uint8_t* kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kKPage;
-  const uint8_t* vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kVPage;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int h = 0; h < KB / 4; ++h)
-      P.kc[mt][h] = *reinterpret_cast<const u32x4*>(kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * F::kKRow +
-                                                    (KB / 4) * 16 * g + 16 * h);
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    if constexpr (VB == 2) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(vp + (16 * mt + n) * F::kVRow + 8 * g);
-      P.vc[mt][0] = x[0];
-      P.vc[mt][1] = x[1];
-    } else {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(vp + (16 * mt + n) * F::kVRow + 16 * g);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) P.vc[mt][k] = x[k];
-    }
-  }
-  const uint8_t* km = kp + F::kKCode;
-  const uint8_t* vm = vp + F::kVCode;
+  asm volatile("" : "+v"(lane), "+v"(ch0));
+  P.ok = pg.ok;
+  const uint8_t* km = pg.kp + F::kKCode;
+  const uint8_t* vm = pg.vp + F::kVCode;
   const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + Meta::kScale);
   const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + Meta::kZero);
   const float* kgm = reinterpret_cast<const float*>(km + Meta::kGamma);
@@ -302,6 +299,41 @@ __device__ __forceinline__ void load_page(PageRegs<KB, VB, GS>& P, int page, int
   P.vr = reinterpret_cast<const float2*>(vm + Meta::kRho)[lane];
   P.vg = reinterpret_cast<const float2*>(vm + Meta::kGamma)[lane];
 }
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void load_kcodes(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int n, int g) {
+  using F = DecFormat<KB, VB, GS>;
+  asm volatile("" : "+v"(n), "+v"(g));
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int h = 0; h < KB / 4; ++h)
+      P.kc[mt][h] = *reinterpret_cast<const u32x4*>(pg.kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * F::kKRow +
+                                                    (KB / 4) * 16 * g + 16 * h);
+}
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void load_vcodes(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int n, int g) {
+  using F = DecFormat<KB, VB, GS>;
+  asm volatile("" : "+v"(n), "+v"(g));
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    if constexpr (VB == 2) {
+      const u32x2 x = *reinterpret_cast<const u32x2*>(pg.vp + (16 * mt + n) * F::kVRow + 8 * g);
+      P.vc[mt][0] = x[0];
+      P.vc[mt][1] = x[1];
+    } else {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(pg.vp + (16 * mt + n) * F::kVRow + 16 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) P.vc[mt][k] = x[k];
+    }
+  }
+}
+template <int KB, int VB, int GS>
+__device__ __forceinline__ void load_page(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int lane, int n, int g,
+                                          int ch0) {
+  load_kcodes(P, pg, n, g);
+  load_vcodes(P, pg, n, g);
+  load_meta(P, pg, lane, ch0);
+}
 
 // Per-wave state carried across pages.
 struct WaveState {
@@ -316,10 +348,13 @@ struct Mags {
   uint32_t m16, m64, m4, m1024;
 };
 
-template <int KB, int VB, int GS>
-__device__ __forceinline__ void process_page(const PageRegs<KB, VB, GS>& P, WaveState& S,
+// One page of the wave.  With PF, the next page's parts are loaded into P as soon as this page's
+// copies have been used (metadata after the coefficients, key codes after the scores, value codes at
+// the end), so that their HBM latency runs under the rest of this page.
+template <int KB, int VB, int GS, bool PF>
+__device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState& S,
                                              WaveLds<DecFormat<KB, VB, GS>::kHalves>& L, int G, int lane, int g,
-                                             int lo_col, const Mags& M) {
+                                             int lo_col, const Mags& M, const PagePtrs& next, int ch0) {
   // NH = 2 (group size 64): key groups differ between the token halves, value groups between the
   // channel halves.  A lane's score rows are tokens of quarter g, i.e. of half g / 2; value M-tiles
   // 0-3 are channels 0-63 and 4-7 channels 64-127.
@@ -414,6 +449,7 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB, GS>& P, Wave
   }
   L.gs[t0] = ex2(P.vg.x) * inv_sw;
   L.gs[t0 + 1] = ex2(P.vg.y) * inv_sw;
+  if constexpr (PF) load_meta(P, next, lane, ch0);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
@@ -455,6 +491,7 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB, GS>& P, Wave
       }
     }
   }
+  if constexpr (PF) load_kcodes(P, next, n, g);
   float mloc = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -564,6 +601,7 @@ __device__ __forceinline__ void process_page(const PageRegs<KB, VB, GS>& P, Wave
       for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(d[r], gsv[r], S.acc[mt][r]);
     }
   }
+  if constexpr (PF) load_vcodes(P, next, lane & 15, g);
 }
 
 // The fp16 tail of one (sequence, KV head): the ntail < 128 tokens after the last full block, token
@@ -699,8 +737,10 @@ __device__ __forceinline__ void tail_partial(const uint16_t* __restrict__ qrow0,
 
 }  // namespace
 
-template <int KB, int VB, int GS>
-__global__ __launch_bounds__(256, (DecFormat<KB, VB, GS>::kMinWaves)) void decode_kernel(
+// PF: the next page of a wave is loaded during the current one (two waves per SIMD); without it
+// every page is loaded when its turn comes (three waves per SIMD for 4-bit keys at group size 128).
+template <int KB, int VB, int GS, bool PF>
+__global__ __launch_bounds__(256, (PF ? 2 : DecFormat<KB, VB, GS>::kMinWaves)) void decode_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, int hq, int hkv,
@@ -778,7 +818,7 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB, GS>::kMinWaves)) void decod
     const int ch0 = coef_channel<KB>(lane);
     constexpr int ch1 = DecFormat<KB, VB, GS>::kCh1;
     PageRegs<KB, VB, GS> A;
-    load_page(A, wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
+    load_page(A, page_ptrs<KB, VB, GS>(wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool), lane, n, g, ch0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- rotated, scaled query ------------------------------------------------
@@ -824,19 +864,35 @@ __global__ __launch_bounds__(256, (DecFormat<KB, VB, GS>::kMinWaves)) void decod
 
     // ---- pages of this wave: w, w + 4, ... ---------------------------------------
     bool bad_page = false;
-    if (wu < cnt) {
-      if (A.ok) {
-        process_page(A, S, L, G, lane, g, lo_col, M);
-      } else {
-        bad_page = true;
+    if constexpr (PF) {
+      static_assert(!PF || DecFormat<KB, VB, GS>::kCanPrefetch, "format without a prefetching kernel");
+      for (int i = wu; i < cnt; i += kWaves) {
+        // the wave's next page, or this one again after the last (those loads hit in L2 and go unused)
+        const PagePtrs nx = page_ptrs<KB, VB, GS>(bt[i + kWaves < cnt ? i + kWaves : i], num_pages, hkv, kvh,
+                                                  k_pool, v_pool);
+        if (A.ok) {
+          process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, nx, ch0);
+        } else {
+          bad_page = true;
+          load_page(A, nx, lane, n, g, ch0);
+        }
       }
-    }
-    for (int i = wu + kWaves; i < cnt; i += kWaves) {
-      load_page(A, bt[i], num_pages, hkv, kvh, k_pool, v_pool, lane, n, g, ch0);
-      if (A.ok) {
-        process_page(A, S, L, G, lane, g, lo_col, M);
-      } else {
-        bad_page = true;
+    } else {
+      const PagePtrs none{k_pool, v_pool, false};  // no next-page loads in this format
+      if (wu < cnt) {
+        if (A.ok) {
+          process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, none, ch0);
+        } else {
+          bad_page = true;
+        }
+      }
+      for (int i = wu + kWaves; i < cnt; i += kWaves) {
+        load_page(A, page_ptrs<KB, VB, GS>(bt[i], num_pages, hkv, kvh, k_pool, v_pool), lane, n, g, ch0);
+        if (A.ok) {
+          process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, none, ch0);
+        } else {
+          bad_page = true;
+        }
       }
     }
     if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
@@ -949,11 +1005,13 @@ hipError_t launch_decode(const void* q, const void* k_pool, const void* v_pool, 
                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, const void* k_tail,
                          const void* v_tail, int batch, int hq, int hkv, int kbits, int vbits, int group,
                          int blocks_per_split, int max_splits, float scale_log2, float* out, float* part,
-                         uint32_t* counters, uint32_t* flags, hipStream_t stream) {
-  auto kern = group == 64 ? (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 64> : decode_kernel<8, 2, 64>)
-                                        : (vbits == 4 ? decode_kernel<4, 4, 64> : decode_kernel<4, 2, 64>))
-                          : (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 128> : decode_kernel<8, 2, 128>)
-                                        : (vbits == 4 ? decode_kernel<4, 4, 128> : decode_kernel<4, 2, 128>));
+                         uint32_t* counters, uint32_t* flags, bool prefetch, hipStream_t stream) {
+  auto kern = group == 64 ? (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 64, false> : decode_kernel<8, 2, 64, false>)
+                                        : (vbits == 4 ? decode_kernel<4, 4, 64, false> : decode_kernel<4, 2, 64, false>))
+                          : (kbits == 8 ? (vbits == 4 ? decode_kernel<8, 4, 128, false> : decode_kernel<8, 2, 128, false>)
+                                        : (vbits == 4 ? decode_kernel<4, 4, 128, false> : decode_kernel<4, 2, 128, false>));
+  if (prefetch && kbits == 4 && group == 128)
+    kern = vbits == 4 ? decode_kernel<4, 4, 128, true> : decode_kernel<4, 2, 128, true>;
   hipLaunchKernelGGL(kern, dim3(hkv, batch, max_splits), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),
                      static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens,

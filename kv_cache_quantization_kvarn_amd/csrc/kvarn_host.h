@@ -19,7 +19,9 @@ namespace kvarn_host {
 constexpr int kMaxGroup = 8;           // query heads per KV head the decode and prefill kernels hold
 constexpr int kMaxSplitsPerPair = 64;  // the decode kernel's merge holds at most this many splits
 constexpr long kMaxPagesPerSplit = 32;
-constexpr int kWorkgroupsPerCu = 3;    // decode workgroups (4 waves each) resident per CU in one pass
+constexpr int kWorkgroupsPerCu = 3;    // decode workgroups (4 waves each) per CU in one pass, three waves per SIMD
+constexpr int kPrefetchWorkgroupsPerCu = 2;  // the same for the prefetching decode (two waves per SIMD)
+constexpr int kPrefetchMaxPagesPerSplit = 16;  // longer splits stream better with the third wave than with prefetch
 constexpr int kDefaultCus = 256;       // used when the device cannot be asked
 
 // Scratch memory of the allocation-free decode: counters first, split partials after them.
@@ -92,11 +94,12 @@ struct DecodePlan {
 };
 
 // Pages per split (a multiple of the 4 waves of a workgroup): about one pass of workgroups over the
-// device's CUs, at most 32 pages per split so mixed lengths balance, and at most 64 splits per
-// (sequence, KV head) so the final merge stays short (63 page splits when an fp16 tail adds one).
-// Callers bound batch, num_kv_heads (65535) and max_blocks (2^24 - 1), so `units` fits in a long.
-inline DecodePlan plan_decode(int batch, int hkv, int max_blocks, int cus, bool tail = false) {
-  const long target = static_cast<long>(cus > 0 ? cus : kDefaultCus) * kWorkgroupsPerCu;
+// device's CUs (wgs_per_cu each), at most 32 pages per split so mixed lengths balance, and at most 64
+// splits per (sequence, KV head) so the final merge stays short (63 page splits when an fp16 tail adds
+// one).  Callers bound batch, num_kv_heads (65535) and max_blocks (2^24 - 1), so `units` fits in a long.
+inline DecodePlan plan_decode(int batch, int hkv, int max_blocks, int cus, bool tail = false,
+                              int wgs_per_cu = kWorkgroupsPerCu) {
+  const long target = static_cast<long>(cus > 0 ? cus : kDefaultCus) * wgs_per_cu;
   const long units = static_cast<long>(batch) * hkv * max_blocks;
   long bps = (units + target - 1) / target;
   if (bps > kMaxPagesPerSplit) bps = kMaxPagesPerSplit;
@@ -129,11 +132,31 @@ inline bool decode_sizes_in_range(int batch, int hkv, int max_blocks) {
   return batch <= 65535 && hkv <= 65535 && static_cast<long>(max_blocks) * 128 + 127 <= 0x7FFFFFFFL;
 }
 
-// Room for the partials of either plan (with or without an fp16 tail split).
+// The plan a packed decode launches with, and whether it runs the prefetching kernel: formats that
+// have one first try two workgroups per CU and take them when the splits stay short (a wave then has
+// at most four pages, whose loads the prefetch hides); otherwise three workgroups per CU without it.
+struct DecodeChoice {
+  DecodePlan plan;
+  bool prefetch;
+};
+inline DecodeChoice choose_decode(int batch, int hkv, int max_blocks, int cus, bool tail, bool can_prefetch) {
+  if (can_prefetch) {
+    const DecodePlan p = plan_decode(batch, hkv, max_blocks, cus, tail, kPrefetchWorkgroupsPerCu);
+    if (p.blocks_per_split <= kPrefetchMaxPagesPerSplit) return DecodeChoice{p, true};
+  }
+  return DecodeChoice{plan_decode(batch, hkv, max_blocks, cus, tail), false};
+}
+
+// Room for the partials of every plan a decode of these sizes may choose (with or without an fp16
+// tail split, with or without prefetch).
 inline size_t workspace_bytes(int batch, int hkv, int max_blocks, int head_dim, int cus) {
-  const int a = plan_decode(batch, hkv, max_blocks, cus).max_splits;
-  const int b = plan_decode(batch, hkv, max_blocks, cus, true).max_splits;
-  return counter_bytes(batch, hkv) + partial_bytes(batch, hkv, a > b ? a : b, head_dim);
+  int splits = 0;
+  for (int tail = 0; tail < 2; ++tail)
+    for (int wpc : {kWorkgroupsPerCu, kPrefetchWorkgroupsPerCu}) {
+      const int m = plan_decode(batch, hkv, max_blocks, cus, tail != 0, wpc).max_splits;
+      splits = m > splits ? m : splits;
+    }
+  return counter_bytes(batch, hkv) + partial_bytes(batch, hkv, splits, head_dim);
 }
 
 // kvarn_decode_workspace_bytes: 0 for an unsupported config, a bad or out-of-range shape, or batch 0.
@@ -200,8 +223,8 @@ struct DecodeArgs {
 };
 
 // Validation of the packed decode (with or without an fp16 tail), its allocation-free variant and the
-// fp16 baseline; on success with *run, *plan is the split plan to launch.
-inline kvarn_status validate_decode(const DecodeArgs& a, bool* run, DecodePlan* plan) {
+// fp16 baseline; on success with *run, *choice is the split plan to launch and the kernel to run it.
+inline kvarn_status validate_decode(const DecodeArgs& a, bool* run, DecodeChoice* choice) {
   *run = false;
   kvarn_status s = a.kind == DecodeKind::packed ? check_config(a.cfg) : check_config_128(a.cfg);
   if (s != KVARN_OK) return s;
@@ -234,7 +257,10 @@ inline kvarn_status validate_decode(const DecodeArgs& a, bool* run, DecodePlan* 
     if (misaligned(a.k_tail, 16) || misaligned(a.v_tail, 16))
       return fail(KVARN_ERR_SHAPE, "tails must be 16-byte aligned");
   }
-  const DecodePlan p = plan_decode(a.batch, a.num_kv_heads, mb, a.cus, tail);
+  // a prefetching kernel exists for 128-channel heads with 4-bit keys and group size 128
+  const bool can_prefetch = a.kind != DecodeKind::fp16 && D == 128 && a.cfg->k_bits == 4 && a.cfg->group_size == 128;
+  const DecodeChoice c = choose_decode(a.batch, a.num_kv_heads, mb, a.cus, tail, can_prefetch);
+  const DecodePlan& p = c.plan;
   if (a.use_scratch) {
     if (static_cast<size_t>(a.batch) * a.num_kv_heads * sizeof(uint32_t) > kScratchCounterBytes)
       return fail(KVARN_ERR_WORKSPACE, "batch * num_kv_heads above the 262,144 counters of the fixed scratch memory");
@@ -243,7 +269,7 @@ inline kvarn_status validate_decode(const DecodeArgs& a, bool* run, DecodePlan* 
                   "the split partials of this call exceed the 63 MiB of fixed scratch memory; use "
                   "kvarn_decode_attention with a workspace");
   }
-  *plan = p;
+  *choice = c;
   *run = true;
   return KVARN_OK;
 }
