@@ -176,30 +176,42 @@ class Case:
                                       self.ws, dev_flags=self.flags)
 
     def step(self, stream, events=None):
-        """One step: quantise every layer, then one decode step of every layer.  `events[layer]` holds
-        four timing events recorded around that layer's quantise and decode launches."""
+        """One step: quantise every layer, then one decode step of every layer.  `events` maps a layer
+        index to four timing events recorded around that layer's quantise and decode launches; the
+        layers it names are the timed sample."""
+        events = events or {}
         for li, L in enumerate(self.layers):
-            if events is not None:
-                events[li][0].record(stream)
+            ev = events.get(li)
+            if ev:
+                ev[0].record(stream)
             self.quantize(L)
-            if events is not None:
-                events[li][1].record(stream)
+            if ev:
+                ev[1].record(stream)
         for li, L in enumerate(self.layers):
-            if events is not None:
-                events[li][2].record(stream)
+            ev = events.get(li)
+            if ev:
+                ev[2].record(stream)
             self.decode(L)
-            if events is not None:
-                events[li][3].record(stream)
+            if ev:
+                ev[3].record(stream)
+
+
+def event_layers(n_layers):
+    """Layers whose launches carry timing events in every timed step: four evenly spaced layers (all
+    of a workload with fewer), so that the markers do not perturb the step they time."""
+    return sorted(set(range(0, n_layers, max(1, n_layers // 4))))
 
 
 def time_steps(case, stream, steps, warmup):
     """Warm-up steps, then `steps` timed steps bracketed by device synchronisation.  Returns the wall
-    time of the timed steps and the average quantise and decode launch times (HIP events)."""
+    time of the timed steps and the average quantise and decode launch times (HIP events around the
+    sampled layers' launches of every timed step)."""
     import torch
     for _ in range(warmup):
         case.step(stream)
     torch.cuda.synchronize()
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in case.layers] for _ in range(steps)]
+    sample = event_layers(len(case.layers))
+    evs = [{li: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for li in sample} for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -207,8 +219,8 @@ def time_steps(case, stream, steps, warmup):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     assert case.K.kvarn_read_flags(case.flags) == 0, "device flags set during the benchmark"
-    q_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    d_ms = [e[2].elapsed_time(e[3]) for st in evs for e in st]
+    q_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st.values()]
+    d_ms = [e[2].elapsed_time(e[3]) for st in evs for e in st.values()]
     return elapsed, sum(q_ms) / len(q_ms) / 1e3, sum(d_ms) / len(d_ms) / 1e3
 
 
@@ -479,6 +491,11 @@ def formats_measure(K, w, case, stream, reps, flush, sink):
     return res
 
 
+def progress(msg):
+    """A phase of the run, on stderr (stdout carries only the result line)."""
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -496,6 +513,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     # the oracle baseline runs first, before the GPU work (it uses the host's cores only)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    progress("cpu baseline done" if cpu else "cpu baseline skipped")
     from kv_cache_quantization_kvarn_amd import kvarn as K
 
     cfg = K.kvarn_config_parse("kvarn_k4v2_g128")
@@ -506,6 +524,7 @@ def main():
         case.step(stream)
 
     elapsed, q_avg_s, d_avg_s = time_steps(case, stream, args.steps, args.warmup)
+    progress("%s: %d steps timed, %.3f ms per step" % (w.name, args.steps, elapsed / args.steps * 1e3))
 
     # the same step captured once in a HIP graph and replayed (one launch of the whole step; for the
     # 28-layer workload that is 56 kernels)
@@ -531,6 +550,7 @@ def main():
         graph_ms = (time.perf_counter() - t0g) / args.steps * 1e3
         assert K.kvarn_read_flags(case.flags) == 0, "device flags set during the graph replays"
         del graph
+        progress("graph replays timed")
 
     # decode alone after reading 512 MB (evicts the 256 MB last-level cache, leaving clean lines, so
     # the decode pays no write-back of the flush), timed per launch
@@ -546,10 +566,13 @@ def main():
     if not args.no_tail:
         tail = tail_measure(case, K, synth, acc, stream, args.flush_reps, flush, flush_sink, d_flush_s)
 
+    progress("cache-flushed decode, fp16 baseline and tail done")
     formats = None
     if not args.no_formats:
         formats = formats_measure(K, w, case, stream, max(5, args.flush_reps // 2), flush, flush_sink)
     prefill = None
+    if formats is not None:
+        progress("formats done")
     if not args.no_prefill:
         prefill = prefill_measure(K, synth, acc, cfg, args.prefill_workload, stream, args.flush_reps, flush, flush_sink)
         g64 = prefill_measure(K, synth, acc, K.kvarn_config_parse("kvarn_k4v2_g64"), args.prefill_workload, stream,
@@ -568,6 +591,7 @@ def main():
             head_dims[name] = config_summary(K, hcfg, name, stream, args.steps, args.warmup, args.flush_reps, flush,
                                              flush_sink, workloads=synth.HEAD_DIM_WORKLOADS)
             head_dims[name]["head_dim"] = hw.head_dim
+            progress(name + " done")
 
     # the other workloads, each timed like the headline step (a summary object per workload)
     configs = None
@@ -577,6 +601,7 @@ def main():
             if name != w.name:
                 configs[name] = config_summary(K, cfg, name, stream, args.steps, args.warmup, args.flush_reps, flush,
                                                flush_sink)
+                progress(name + " done")
 
     step_bytes = case.q_bytes + case.d_bytes
     ms_per_step = elapsed / args.steps * 1e3
