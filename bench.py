@@ -43,7 +43,10 @@ MEASURED_TRAFFIC = {
     ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("f54a6bbd6ca3fc55", 332495992),
     ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("245d6f737a5acc3c", 67515580),
 }
-KERNEL_SOURCE = {"quantize_kernel": "kvarn_quantize.hip", "decode_kernel": "kvarn_decode.hip"}
+# the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
+# helpers and the host plan that picks its launch shape and instance
+KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
+                 "decode_kernel": ("kvarn_decode.hip", "kvarn_codes.h", "kvarn_host.h")}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
     ("quantize_kernel", "llama3_8b_layer_16x8192"): ("f54a6bbd6ca3fc55", 126926848),
@@ -63,7 +66,7 @@ def source_digest(kernel):
     import re
     csrc = os.path.join(ROOT, "kv_cache_quantization_kvarn_amd", "csrc")
     data = ""
-    for f in (KERNEL_SOURCE[kernel], "kvarn_common.h"):
+    for f in KERNEL_SOURCE[kernel] + ("kvarn_common.h",):
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             data += fh.read()
     data = re.sub(r"/\*.*?\*/", " ", data, flags=re.S)

@@ -257,6 +257,7 @@ struct PagePtrs {
   const uint8_t* kp;
   const uint8_t* vp;
   bool ok;
+  bool load;  // false: nothing to prefetch (the wave's last page)
 };
 template <int KB, int VB, int GS>
 __device__ __forceinline__ PagePtrs page_ptrs(int page, int num_pages, int hkv, int kvh,
@@ -267,6 +268,7 @@ __device__ __forceinline__ PagePtrs page_ptrs(int page, int num_pages, int hkv, 
   const int safe = r.ok ? page : 0;
   r.kp = k_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kKPage;
   r.vp = v_pool + (static_cast<size_t>(safe) * hkv + kvh) * F::kVPage;
+  r.load = true;
   return r;
 }
 
@@ -449,7 +451,9 @@ __device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState&
   }
   L.gs[t0] = ex2(P.vg.x) * inv_sw;
   L.gs[t0 + 1] = ex2(P.vg.y) * inv_sw;
-  if constexpr (PF) load_meta(P, next, lane, ch0);
+  if constexpr (PF) {
+    if (next.load) load_meta(P, next, lane, ch0);
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
@@ -491,7 +495,9 @@ __device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState&
       }
     }
   }
-  if constexpr (PF) load_kcodes(P, next, n, g);
+  if constexpr (PF) {
+    if (next.load) load_kcodes(P, next, n, g);
+  }
   float mloc = -INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -601,7 +607,9 @@ __device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState&
       for (int r = 0; r < 4; ++r) S.acc[mt][r] = fmaf(d[r], gsv[r], S.acc[mt][r]);
     }
   }
-  if constexpr (PF) load_vcodes(P, next, lane & 15, g);
+  if constexpr (PF) {
+    if (next.load) load_vcodes(P, next, lane & 15, g);
+  }
 }
 
 // The fp16 tail of one (sequence, KV head): the ntail < 128 tokens after the last full block, token
@@ -867,18 +875,19 @@ __global__ __launch_bounds__(256, (PF ? 2 : DecFormat<KB, VB, GS>::kMinWaves)) v
     if constexpr (PF) {
       static_assert(!PF || DecFormat<KB, VB, GS>::kCanPrefetch, "format without a prefetching kernel");
       for (int i = wu; i < cnt; i += kWaves) {
-        // the wave's next page, or this one again after the last (those loads hit in L2 and go unused)
-        const PagePtrs nx = page_ptrs<KB, VB, GS>(bt[i + kWaves < cnt ? i + kWaves : i], num_pages, hkv, kvh,
-                                                  k_pool, v_pool);
+        // the wave's next page (after its last one: no loads)
+        PagePtrs nx = page_ptrs<KB, VB, GS>(bt[i + kWaves < cnt ? i + kWaves : i], num_pages, hkv, kvh,
+                                            k_pool, v_pool);
+        nx.load = i + kWaves < cnt;
         if (A.ok) {
           process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, nx, ch0);
         } else {
           bad_page = true;
-          load_page(A, nx, lane, n, g, ch0);
+          if (nx.load) load_page(A, nx, lane, n, g, ch0);
         }
       }
     } else {
-      const PagePtrs none{k_pool, v_pool, false};  // no next-page loads in this format
+      const PagePtrs none{k_pool, v_pool, false, false};  // no next-page loads in this format
       if (wu < cnt) {
         if (A.ok) {
           process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, none, ch0);
