@@ -258,6 +258,11 @@ void test_decode() {
   check(kvarn_host::validate_decode(a, &run, &p) == KVARN_ERR_SHAPE, "decode heads not a multiple");
   a = args(K::packed_tail, &c64, 16, 32, 8, 64);
   check(kvarn_host::validate_decode(a, &run, &p) == KVARN_ERR_UNSUPPORTED, "tail decode needs head_dim 128");
+  // 64-channel heads: two workgroups per CU (512 on 256 CUs: 16 pages per split for 16 x 8 x 64)
+  a = args(K::packed, &c64, 16, 32, 8, 64);
+  check(kvarn_host::validate_decode(a, &run, &p) == KVARN_OK && run && !p.prefetch && p.plan.blocks_per_split == 16 &&
+            p.plan.max_splits == 4,
+        "decode plan at 64 channels");
   a = args(K::packed_tail, &c128, 16, 32, 8, 64);
   a.v_tail = nullptr;
   check(kvarn_host::validate_decode(a, &run, &p) == KVARN_ERR_NULL, "tail decode without v_tail");

@@ -507,6 +507,55 @@ __device__ __forceinline__ float value_offset(int t) {
   return VB == 4 ? 64.f : ((t & 1) ? 16.f : 4.f);
 }
 
+// The end of every split workgroup of the head-size decodes, after its partial (o~, m, l per head) is
+// stored: count in, and the last workgroup of the (sequence, KV head) merges the splits (log-sum-exp)
+// and writes o = H o~ / sqrt(D).  Hand-off without fences, as in the 128-channel decode: partials go
+// through agent-scope (sc1) atomic accesses, vmcnt(0) covers the stores before the workgroup counts in
+// with an agent-scope add, and every access to partials and counters is one of these.
+template <int D>
+__device__ __forceinline__ void split_merge(float (&qt)[kMaxGroup][D], float (&sm)[64][kMaxGroup],
+                                            float (&sl)[64][kMaxGroup], int& last, const float* __restrict__ pbase,
+                                            uint32_t* __restrict__ counter, int nsplit, int G, float* __restrict__ out_b) {
+  constexpr int PS = D + 2;
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == static_cast<uint32_t>(nsplit - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int e = tid; e < nsplit * kMaxGroup; e += kDecThreads) {
+    const int sp = e / kMaxGroup, h = e - sp * kMaxGroup;
+    const float* pp = pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * PS;
+    sm[sp][h] = h < G ? load_coherent(pp + D) : -INFINITY;
+    sl[sp][h] = h < G ? load_coherent(pp + D + 1) : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
+    const int h = e / D, j = e - h * D;
+    float val = 0.f;
+    if (h < G) {
+      float mx = -INFINITY;
+      for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, sm[sp][h]);
+      float num = 0.f, den = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) {
+        const float ms = sm[sp][h];
+        const float wgt = ms == -INFINITY ? 0.f : ex2(ms - mx);
+        den = fmaf(wgt, sl[sp][h], den);
+        num = fmaf(wgt, load_coherent(pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * PS + j), num);
+      }
+      val = den > 0.f ? num / den : 0.f;
+    }
+    qt[h][j] = val;
+  }
+  __syncthreads();
+  lds_fwht_rows<D>(qt, kMaxGroup);
+  for (int e = tid; e < G * D; e += kDecThreads) out_b[e] = qt[e / D][e % D] * HdGeom<D>::kInvSqrtD;
+}
+
 template <int D, int KB, int VB, int GS>
 struct DhdLds {
   using PK = HdPage<D, false, KB, GS>;
@@ -918,47 +967,382 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
     store_coherent(pp + D, s.mrun[tid]);
     store_coherent(pp + D + 1, s.lrun[tid]);
   }
-  // Hand-off without fences, as in the 128-channel decode: partials go through agent-scope (sc1)
-  // atomic accesses, vmcnt(0) covers the stores before the workgroup counts in with an agent-scope
-  // add, and every access to partials and counters is one of these.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s.last = prev == static_cast<uint32_t>(nsplit - 1);
-  }
-  __syncthreads();
-  if (!s.last) return;
-  if (tid == 0) __hip_atomic_store(counters + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  split_merge<D>(s.qt, s.sm, s.sl, s.last, pbase, counters + pair, nsplit, G, out_b);
+}
 
-  // ---- merge the splits (log-sum-exp), then o = H o~ / sqrt(D) ----------------------------------
-  for (int e = tid; e < nsplit * kMaxGroup; e += kDecThreads) {
-    const int sp = e / kMaxGroup, h = e - sp * kMaxGroup;
-    const float* pp = pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * PS;
-    s.sm[sp][h] = h < G ? load_coherent(pp + D) : -INFINITY;
-    s.sl[sp][h] = h < G ? load_coherent(pp + D + 1) : 0.f;
-  }
-  __syncthreads();
-  for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
-    const int h = e / D, j = e - h * D;
-    float val = 0.f;
-    if (h < G) {
-      float mx = -INFINITY;
-      for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, s.sm[sp][h]);
-      float num = 0.f, den = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) {
-        const float ms = s.sm[sp][h];
-        const float wgt = ms == -INFINITY ? 0.f : ex2(ms - mx);
-        den = fmaf(wgt, s.sl[sp][h], den);
-        num = fmaf(wgt, load_coherent(pbase + (static_cast<size_t>(sp) * kMaxGroup + h) * PS + j), num);
-      }
-      val = den > 0.f ? num / den : 0.f;
+namespace {
+
+// Sums over the 64 lanes of v[lane & 7]: every lane gets the total of head lane & 7 (three pairwise
+// stages halve the values per lane, lanes l^1, l^2 and (l + 4) mod 16, then lanes l^8, l^16, l^32).
+__device__ __forceinline__ float head_sums8(const float (&v)[kMaxGroup], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+  float s4[4], s2[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) s4[k] = (b0 ? v[2 * k + 1] : v[2 * k]) + dpp<kDppXor1>(b0 ? v[2 * k] : v[2 * k + 1]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    s2[m] = (b1 ? s4[2 * m + 1] : s4[2 * m]) + dpp<kDppXor2>(b1 ? s4[2 * m] : s4[2 * m + 1]);
+  // (lane + 4) mod 16 always has the other value of bit 2
+  float t = (b2 ? s2[1] : s2[0]) + dpp<kDppRor4>(b2 ? s2[0] : s2[1]);
+  t += dpp<kDppXor8>(t);
+  return rows_sum(t);
+}
+
+template <int KB, int VB, int GS>
+struct D64Lds {
+  static constexpr int KH = kBlockTokens / GS;  // key groups per channel (token halves)
+  struct Wave {
+    _Float16 kcoef[KH][16][64 + 8];             // key B operand: hi (columns 0-7), lo (8-15) of a_j sa
+    _Float16 vcoef[16][kBlockTokens + 8];       // value B operand: hi, lo of w_t sw
+    float krho[kBlockTokens];                   // 2^rho_t / sa * scale (keys)
+    float vsr[kBlockTokens], vzr[kBlockTokens];  // 2^rho_t s sw, 2^rho_t z sw (values)
+    float gsv[64];                              // 2^gamma_j / sw (values)
+  };
+  float qt[kMaxGroup][64];                      // q~ per head; the merged output at the end
+  union {
+    Wave wv[kDecWaves];                         // each wave's page, during the page loop
+    float wo[kDecWaves][kMaxGroup][64];         // each wave's o~ for the merge of the waves
+  } u;
+  float wm[kDecWaves][kMaxGroup], wl[kDecWaves][kMaxGroup];
+  float qred[kDecWaves];
+  float sm[64][kMaxGroup], sl[64][kMaxGroup];
+  int last;
+};
+
+}  // namespace
+
+// Decode over pages of 64-channel heads, one page per wave: grid (Hkv, batch, splits), four waves per
+// workgroup, wave w taking every fourth page of the split.  A 64-channel page is small enough for one
+// wave, so no page needs a workgroup barrier: per page the wave builds its fp16 hi/lo coefficient
+// operands in its own LDS (lane j: channel j), scores 128 tokens on the matrix cores (eight 16-token
+// tiles, two chained products each), runs the online softmax in registers (lane (n, g) holds the 32
+// scores of head n & 7 for tokens 16mt + 4g + r; the four 16-lane rows finish the max and sum), writes
+// its weight column of the value operand and accumulates o~ of all 64 channels (four 16-channel tiles,
+// four products each).  The four waves merge through LDS at the end; the split partial, hand-off and
+// last-workgroup merge are those of the head-size decode.  Each part of the next page is loaded right
+// after its last use on the current one.
+template <int KB, int VB, int GS>
+__global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
+    int num_pages, const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seq_lens,
+    int hq, int hkv, int blocks_per_split, int max_splits, float scale_log2, float* __restrict__ out,
+    float* __restrict__ part, uint32_t* __restrict__ counters, uint32_t* __restrict__ flags) {
+  constexpr int D = 64;
+  using L = D64Lds<KB, VB, GS>;
+  using PK = HdPage<D, false, KB, GS>;
+  using PV = HdPage<D, true, VB, GS>;
+  constexpr int KH = L::KH;
+  constexpr int PS = D + 2;
+  constexpr int KWT = KB / 2;  // key code dwords of a lane per token tile (16 channels)
+  constexpr int KROW = D * KB / 8, VROW = kBlockTokens * VB / 8;
+  static_assert(PV::kVGroup == D, "one value group per token at 64 channels");
+  __shared__ __align__(16) L s;
+
+  const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int G = hq / hkv;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4, h = n & 7;
+  const int sl_b = seq_lens[b];
+  float* out_b = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * D;
+  const bool bad = sl_b < 0 || sl_b > max_blocks * kBlockTokens || (sl_b & (kBlockTokens - 1)) != 0;
+  const int nblk = bad ? 0 : sl_b / kBlockTokens;
+  if (nblk == 0) {
+    if (split == 0) {
+      if (bad && tid == 0 && flags) atomicOr(flags, kFlagBadSeqLen);
+      for (int e = tid; e < G * D; e += kDecThreads) out_b[e] = 0.f;
     }
-    s.qt[h][j] = val;
+    return;
+  }
+  const int nsplit = (nblk + blocks_per_split - 1) / blocks_per_split;
+  if (split >= nsplit) return;
+  const size_t pair = static_cast<size_t>(b) * hkv + kvh;
+  float* pbase = part + pair * max_splits * kMaxGroup * PS;
+
+  // ---- q~ = H q / sqrt(D) for the G heads (rows past G are zero), and max |q~| -------------------
+  const uint16_t* qb = q + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * D;
+  for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
+    const int hh = e / D, j = e - hh * D;
+    s.qt[hh][j] = hh < G ? half_bits_to_float(qb[hh * D + j]) : 0.f;
   }
   __syncthreads();
   lds_fwht_rows<D>(s.qt, kMaxGroup);
-  for (int e = tid; e < G * D; e += kDecThreads) out_b[e] = s.qt[e / D][e % D] * HdGeom<D>::kInvSqrtD;
+  {
+    float qm = 0.f;
+    for (int e = tid; e < kMaxGroup * D; e += kDecThreads) {
+      const float v = s.qt[e / D][e % D] * HdGeom<D>::kInvSqrtD;
+      s.qt[e / D][e % D] = v;
+      qm = fmaxf(qm, fabsf(v));
+    }
+    qm = wave_maxp(qm);
+    if (lane == 0) s.qred[w] = qm;
+  }
+  __syncthreads();
+  const float qmax = fmaxf(fmaxf(s.qred[0], s.qred[1]), fmaxf(s.qred[2], s.qred[3]));
+  float qj[kMaxGroup];  // q~ of channel `lane`, every head
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) qj[hh] = s.qt[hh][lane];
+
+  uint32_t mag4 = 0x44004400u, mag16 = 0x4C004C00u, mag64 = 0x54005400u, mag1024 = 0x64006400u;
+  asm volatile("" : "+v"(mag4), "+v"(mag16), "+v"(mag64), "+v"(mag1024));
+
+  const int p0 = split * blocks_per_split;
+  const int cnt = min(nblk, p0 + blocks_per_split) - p0;
+  const int32_t* bt = block_table + static_cast<size_t>(b) * max_blocks + p0;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto& W = s.u.wv[w];
+
+  // one page's data in registers
+  uint32_t kw[8][KWT];  // key codes: token 16mt + n, channels 16g .. 16g+15
+  uint32_t vw[4][VB];   // value codes: channel 16mt + n, tokens 32g .. 32g+31
+  float m_kg = 0.f, m_ks[KH], m_kz[KH], m_vg = 0.f;  // channel `lane`
+  float2 m_kr, m_vr;                                 // tokens 2 lane, 2 lane + 1
+  uint32_t m_vs = 0u, m_vz = 0u;                     // value scale / zero (fp16 pair) of those tokens
+  auto valid = [&](int i) {
+    const int pg = bt[i];
+    return pg >= 0 && pg < num_pages;
+  };
+  auto base_k = [&](int i) { return k_pool + (static_cast<size_t>(valid(i) ? bt[i] : 0) * hkv + kvh) * PK::kBytes; };
+  auto base_v = [&](int i) { return v_pool + (static_cast<size_t>(valid(i) ? bt[i] : 0) * hkv + kvh) * PV::kBytes; };
+  auto load_meta = [&](int i) {
+    const uint8_t* kp = base_k(i);
+    const uint8_t* vp = base_v(i);
+    m_kg = reinterpret_cast<const float*>(kp + PK::kGamma)[lane];
+    m_vg = reinterpret_cast<const float*>(vp + PV::kGamma)[lane];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      m_ks[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kScale)[D * kh + lane]);
+      m_kz[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kZero)[D * kh + lane]);
+    }
+    m_kr = reinterpret_cast<const float2*>(kp + PK::kRho)[lane];
+    m_vr = reinterpret_cast<const float2*>(vp + PV::kRho)[lane];
+    m_vs = reinterpret_cast<const uint32_t*>(vp + PV::kScale)[lane];
+    m_vz = reinterpret_cast<const uint32_t*>(vp + PV::kZero)[lane];
+  };
+  auto load_k = [&](int i) {
+    const uint8_t* kp = base_k(i);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const uint8_t* src = kp + (16 * mt + n) * KROW + g * (KROW / 4);
+      if constexpr (KWT == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        kw[mt][0] = x[0];
+        kw[mt][1] = x[1];
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kw[mt][e] = x[e];
+      }
+    }
+  };
+  auto load_v = [&](int i) {
+    const uint8_t* vp = base_v(i);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const uint8_t* src = vp + (16 * mt + n) * VROW + g * (VROW / 4);
+      if constexpr (VB == 2) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(src);
+        vw[mt][0] = x[0];
+        vw[mt][1] = x[1];
+      } else {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vw[mt][e] = x[e];
+      }
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;  // online softmax of head h (lane's column)
+  f32x4 oacc[4];                        // o~ of channels 16mt + 4g + r, head h
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad_page = false;
+  if (wu < cnt) {
+    load_meta(wu);
+    load_k(wu);
+    load_v(wu);
+  }
+  for (int i = wu; i < cnt; i += kDecWaves) {
+    const bool more = i + kDecWaves < cnt;  // wave-uniform, like everything decided per page
+    const int nx = i + kDecWaves;
+    if (!valid(i)) {
+      // a page id outside [0, num_pages) names no block: skipped (its registers were filled from page 0)
+      bad_page = true;
+      if (more) {
+        load_meta(nx);
+        load_k(nx);
+        load_v(nx);
+      }
+      continue;
+    }
+    // (1) page scales, coefficient operands, per-token and per-channel factors
+    float b_h[KH];  // b sa (offsets removed) of head h, per token half
+    {
+      float kmx = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) kmx = fmaxf(kmx, m_ks[kh]);
+      const float ek = wave_maxp(ex2(m_kg) * kmx);
+      const float vr0 = ex2(m_vr.x), vr1 = ex2(m_vr.y);
+      const float vs0 = half_bits_to_float(m_vs & 0xFFFFu), vs1 = half_bits_to_float(m_vs >> 16);
+      const float ev = wave_maxp(fmaxf(vr0 * vs0, vr1 * vs1));
+      const float kprod = qmax * ek;
+      int ex = 0, exv = 0;
+      frexpf(kprod, &ex);
+      frexpf(ev, &exv);
+      ex = min(max(ex, -100), 100);
+      exv = min(max(exv, -100), 100);
+      const float sa = kprod > 0.f ? pow2i(14 - ex) : 1.f, inv_sa = kprod > 0.f ? pow2i(ex - 14) : 1.f;
+      const float sw = ev > 0.f ? pow2i(14 - exv) : 1.f, inv_sw = ev > 0.f ? pow2i(exv - 14) : 1.f;
+      const int slot = key_slot<KB>(lane);
+      const float gk = ex2(m_kg) * sa, off = key_offset<KB>(lane);
+#pragma unroll
+      for (int kh = 0; kh < KH; ++kh) {
+        float bp[kMaxGroup];
+#pragma unroll
+        for (int hh = 0; hh < kMaxGroup; ++hh) {
+          const float qg = qj[hh] * gk;
+          _Float16 hi, lo;
+          split_hl(qg * m_ks[kh], hi, lo);
+          W.kcoef[kh][hh][slot] = hi;
+          W.kcoef[kh][8 + hh][slot] = lo;
+          bp[hh] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
+        }
+        b_h[kh] = head_sums8(bp, lane);
+      }
+      const int t0 = 2 * lane;
+      W.krho[t0] = ex2(m_kr.x) * inv_sa * scale_log2;
+      W.krho[t0 + 1] = ex2(m_kr.y) * inv_sa * scale_log2;
+      W.vsr[t0] = vr0 * sw * vs0;
+      W.vsr[t0 + 1] = vr1 * sw * vs1;
+      W.vzr[t0] = vr0 * sw * half_bits_to_float(m_vz & 0xFFFFu);
+      W.vzr[t0 + 1] = vr1 * sw * half_bits_to_float(m_vz >> 16);
+      W.gsv[lane] = ex2(m_vg) * inv_sw;
+      if (more) load_meta(nx);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // (2) scores of tokens 16mt + 4g + r for head h (hi and lo columns summed)
+    float sc[8][4];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int kh = (16 * mt) / GS;
+      const _Float16* cb = &W.kcoef[kh][n][16 * g];
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        f16x8 aop;
+        if constexpr (KB == 4) {
+          aop = key_codes(kw[mt][kc], mag16, mag64);
+        } else {
+          aop = key_codes8(kw[mt][2 * kc], kw[mt][2 * kc + 1], mag1024);
+        }
+        d = mfma16x16x32(aop, *reinterpret_cast<const f16x8*>(cb + 8 * kc), d);
+      }
+      const float4 kr = *reinterpret_cast<const float4*>(&W.krho[16 * mt + 4 * g]);
+      const float krv[4] = {kr.x, kr.y, kr.z, kr.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[mt][r] = (d[r] + dpp<kDppXor8>(d[r]) + b_h[kh]) * krv[r];
+    }
+    if (more) load_k(nx);
+    // (3) online softmax of head h over the page's 128 tokens, and the value operands
+    float u_h;
+    {
+      float pm = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pm = fmaxf(pm, sc[mt][r]);
+      pm = rows_max(pm);
+      const float mnew = fmaxf(m_run, pm);
+      const float al = m_run == -INFINITY ? 0.f : ex2(m_run - mnew);
+      float lp = 0.f, up = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const float4 vs4 = *reinterpret_cast<const float4*>(&W.vsr[16 * mt + 4 * g]);
+        const float4 vz4 = *reinterpret_cast<const float4*>(&W.vzr[16 * mt + 4 * g]);
+        const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w}, vzv[4] = {vz4.x, vz4.y, vz4.z, vz4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * mt + 4 * g + r;
+          const float e = ex2(sc[mt][r] - mnew);
+          lp += e;
+          _Float16 hi, lo;
+          split_hl(e * vsv[r], hi, lo);
+          W.vcoef[n][value_slot(t)] = n < 8 ? hi : lo;  // this lane's column: hi for n < 8, lo for n >= 8
+          up = fmaf(e, vzv[r], up) - value_offset<VB>(t) * (static_cast<float>(hi) + static_cast<float>(lo));
+        }
+      }
+      lp = rows_sum(lp);
+      u_h = rows_sum(up);
+      l_run = fmaf(al, l_run, lp);
+      m_run = mnew;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[mt][r] *= al;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // (4) values: o~_j += 2^gamma_j (sum_t w_t c_tj + u), channels 16mt + 4g + r
+    {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const _Float16* wb = &W.vcoef[n][32 * g];
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          f16x8 c0, c1;
+          if constexpr (VB == 2) {
+            value_codes(vw[mt][uu], mag4, mag16, c0, c1);
+          } else {
+            value_codes4(vw[mt][2 * uu], vw[mt][2 * uu + 1], mag64, c0, c1);
+          }
+          d = mfma16x16x32(c0, *reinterpret_cast<const f16x8*>(wb + 16 * uu), d);
+          d = mfma16x16x32(c1, *reinterpret_cast<const f16x8*>(wb + 16 * uu + 8), d);
+        }
+        const float4 gs4 = *reinterpret_cast<const float4*>(&W.gsv[16 * mt + 4 * g]);
+        const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[mt][r] = fmaf(gsv[r], d[r] + dpp<kDppXor8>(d[r]) + u_h, oacc[mt][r]);
+      }
+    }
+    if (more) load_v(nx);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
+
+  // ---- merge the four waves, then this split's partial: o~ (rotated basis), m, l per head ----------
+  __syncthreads();  // every wave is out of the page loop: its page buffers may be reused
+  if (n < 8) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s.u.wo[w][n][16 * mt + 4 * g + r] = oacc[mt][r];
+    if (g == 0) {
+      s.wm[w][n] = m_run;
+      s.wl[w][n] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += kDecThreads) {
+    const int hh = e / D, j = e - hh * D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x) mx = fmaxf(mx, s.wm[x][hh]);
+    float o = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int x = 0; x < kDecWaves; ++x) {
+      const float wgt = s.wm[x][hh] == -INFINITY ? 0.f : ex2(s.wm[x][hh] - mx);
+      o = fmaf(wgt, s.u.wo[x][hh][j], o);
+      lsum = fmaf(wgt, s.wl[x][hh], lsum);
+    }
+    float* pp = pbase + (static_cast<size_t>(split) * kMaxGroup + hh) * PS;
+    store_coherent(pp + j, o);
+    if (j == 0) {
+      store_coherent(pp + D, mx);
+      store_coherent(pp + D + 1, lsum);
+    }
+  }
+  split_merge<D>(s.qt, s.sm, s.sl, s.last, pbase, counters + pair, nsplit, G, out_b);
 }
 
 hipError_t launch_quantize_hd(const void* k, const void* v, int n_blocks, int hkv, int head_dim,
@@ -1007,7 +1391,8 @@ hipError_t launch_decode_hd(const void* q, const void* k_pool, const void* v_poo
                             uint32_t* flags, hipStream_t stream) {
 #define KVARN_DHD(D, KB, VB, GS)                                                                                   \
   if (head_dim == D && kbits == KB && vbits == VB && group == GS) {                                                \
-    hipLaunchKernelGGL((decode_hd_kernel<D, KB, VB, GS>), dim3(hkv, batch, max_splits), dim3(kDecThreads), 0,       \
+    auto kern = D == 64 ? decode_hd64_kernel<KB, VB, GS> : decode_hd_kernel<D, KB, VB, GS>;                         \
+    hipLaunchKernelGGL(kern, dim3(hkv, batch, max_splits), dim3(kDecThreads), 0,                                     \
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint8_t*>(k_pool),              \
                        static_cast<const uint8_t*>(v_pool), num_pages, block_table, max_blocks, seq_lens, hq, hkv,  \
                        blocks_per_split, max_splits, scale_log2, out, part, counters, flags);                      \

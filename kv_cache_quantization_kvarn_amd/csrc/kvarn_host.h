@@ -259,7 +259,10 @@ inline kvarn_status validate_decode(const DecodeArgs& a, bool* run, DecodeChoice
   }
   // a prefetching kernel exists for 128-channel heads with 4-bit keys and group size 128
   const bool can_prefetch = a.kind != DecodeKind::fp16 && D == 128 && a.cfg->k_bits == 4 && a.cfg->group_size == 128;
-  const DecodeChoice c = choose_decode(a.batch, a.num_kv_heads, mb, a.cus, tail, can_prefetch);
+  // the 64-channel decode (a page per wave, two waves per SIMD) plans two workgroups per CU
+  const DecodeChoice c = D == 64 ? DecodeChoice{plan_decode(a.batch, a.num_kv_heads, mb, a.cus, tail,
+                                                            kPrefetchWorkgroupsPerCu), false}
+                                 : choose_decode(a.batch, a.num_kv_heads, mb, a.cus, tail, can_prefetch);
   const DecodePlan& p = c.plan;
   if (a.use_scratch) {
     if (static_cast<size_t>(a.batch) * a.num_kv_heads * sizeof(uint32_t) > kScratchCounterBytes)
