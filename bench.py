@@ -38,10 +38,10 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("f54a6bbd6ca3fc55", 663500959),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 130369125),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("f54a6bbd6ca3fc55", 332495992),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("245d6f737a5acc3c", 67515580),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("a27679966e4aaf7f", 663256619),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("a27679966e4aaf7f", 332434420),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("6dafcdab08c5e6e5", 67420351),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("6dafcdab08c5e6e5", 129024224),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
 # helpers and the host plan that picks its launch shape and instance
@@ -49,10 +49,10 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
                  "decode_kernel": ("kvarn_decode.hip", "kvarn_codes.h", "kvarn_host.h")}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("f54a6bbd6ca3fc55", 126926848),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("245d6f737a5acc3c", 10894144),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("f54a6bbd6ca3fc55", 64427909),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("245d6f737a5acc3c", 6061378),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("a27679966e4aaf7f", 120274944),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("a27679966e4aaf7f", 61213158),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("6dafcdab08c5e6e5", 6171970),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("6dafcdab08c5e6e5", 10341056),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
