@@ -120,6 +120,23 @@ __device__ __forceinline__ float head_sum(float x) {
 // Max over the whole wave, identical in every lane.
 __device__ __forceinline__ float wave_max_all(float x) { return max_xor32(max_xor16(row16_max(x))); }
 
+// The same for values that are never negative (scales and their products): such floats, with the
+// sign bit cleared, order like unsigned integers, and the integer max takes its DPP operand
+// directly (a float max would first canonicalise the moved value).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  uint32_t u = __float_as_uint(x) & 0x7FFFFFFFu;
+  auto mx = [&](uint32_t v) { u = u > v ? u : v; };
+  mx(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), kDppXor1, 0xF, 0xF, true)));
+  mx(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), kDppXor2, 0xF, 0xF, true)));
+  mx(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), kDppXor7, 0xF, 0xF, true)));
+  mx(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(u), kDppXor8, 0xF, 0xF, true)));
+  auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = r[0] > r[1] ? r[0] : r[1];
+  r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  u = r[0] > r[1] ? r[0] : r[1];
+  return __uint_as_float(u);
+}
+
 // Sum over all 64 lanes of v[l & 7] (for each lane l): a transpose-reduce that halves the
 // number of values per lane at each of the first three stages (partners l^1, l^2 and l+4 mod
 // 16, the last one a row rotation), then adds across lanes l^8, l^16, l^32.
@@ -274,56 +291,60 @@ __device__ __forceinline__ PagePtrs page_ptrs(int page, int num_pages, int hkv, 
 
 // The three parts of a page a lane loads: metadata (consumed first), key codes, value codes.  Lane
 // offsets are recomputed for every page (a few integer operations) rather than kept live across the
-// page loop, where registers are short.
+// page loop, where registers are short.  They are unsigned 32-bit byte offsets from the wave-uniform
+// page base, so each load takes the base from scalar registers, the lane offset from one vector
+// register and the per-load constant as its immediate.
 template <int KB, int VB, int GS>
 __device__ __forceinline__ void load_meta(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int lane, int ch0) {
   using F = DecFormat<KB, VB, GS>;
   using Meta = typename F::Meta;
   asm volatile("" : "+v"(lane), "+v"(ch0));
   P.ok = pg.ok;
-  const uint8_t* km = pg.kp + F::kKCode;
-  const uint8_t* vm = pg.vp + F::kVCode;
-  const uint16_t* ksc = reinterpret_cast<const uint16_t*>(km + Meta::kScale);
-  const uint16_t* kzr = reinterpret_cast<const uint16_t*>(km + Meta::kZero);
-  const float* kgm = reinterpret_cast<const float*>(km + Meta::kGamma);
+  const uint32_t c2 = 2u * static_cast<uint32_t>(ch0), c4 = 4u * static_cast<uint32_t>(ch0);
+  const uint32_t l4 = 4u * static_cast<uint32_t>(lane), l8 = 8u * static_cast<uint32_t>(lane);
+  auto u16 = [](const uint8_t* a) { return static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(a)); };
+  auto u32 = [](const uint8_t* a) { return *reinterpret_cast<const uint32_t*>(a); };
+  auto f32 = [](const uint8_t* a) { return *reinterpret_cast<const float*>(a); };
+  auto f2 = [](const uint8_t* a) { return *reinterpret_cast<const float2*>(a); };
 #pragma unroll
   for (int hh = 0; hh < F::kHalves; ++hh) {  // group entry 128*hh + j (half-major)
-    P.ks0[hh] = ksc[128 * hh + ch0];
-    P.ks1[hh] = ksc[128 * hh + ch0 + F::kCh1];
-    P.kz0[hh] = kzr[128 * hh + ch0];
-    P.kz1[hh] = kzr[128 * hh + ch0 + F::kCh1];
-    P.vs2[hh] = reinterpret_cast<const uint32_t*>(vm + Meta::kScale)[64 * hh + lane];
-    P.vz2[hh] = reinterpret_cast<const uint32_t*>(vm + Meta::kZero)[64 * hh + lane];
+    P.ks0[hh] = u16(pg.kp + c2 + (F::kKCode + Meta::kScale + 256 * hh));
+    P.ks1[hh] = u16(pg.kp + c2 + (F::kKCode + Meta::kScale + 256 * hh + 2 * F::kCh1));
+    P.kz0[hh] = u16(pg.kp + c2 + (F::kKCode + Meta::kZero + 256 * hh));
+    P.kz1[hh] = u16(pg.kp + c2 + (F::kKCode + Meta::kZero + 256 * hh + 2 * F::kCh1));
+    P.vs2[hh] = u32(pg.vp + l4 + (F::kVCode + Meta::kScale + 256 * hh));
+    P.vz2[hh] = u32(pg.vp + l4 + (F::kVCode + Meta::kZero + 256 * hh));
   }
-  P.kg0 = kgm[ch0];
-  P.kg1 = kgm[ch0 + F::kCh1];
-  P.kr = reinterpret_cast<const float2*>(km + Meta::kRho)[lane];
-  P.vr = reinterpret_cast<const float2*>(vm + Meta::kRho)[lane];
-  P.vg = reinterpret_cast<const float2*>(vm + Meta::kGamma)[lane];
+  P.kg0 = f32(pg.kp + c4 + (F::kKCode + Meta::kGamma));
+  P.kg1 = f32(pg.kp + c4 + (F::kKCode + Meta::kGamma + 4 * F::kCh1));
+  P.kr = f2(pg.kp + l8 + (F::kKCode + Meta::kRho));
+  P.vr = f2(pg.vp + l8 + (F::kVCode + Meta::kRho));
+  P.vg = f2(pg.vp + l8 + (F::kVCode + Meta::kGamma));
 }
 template <int KB, int VB, int GS>
 __device__ __forceinline__ void load_kcodes(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int n, int g) {
   using F = DecFormat<KB, VB, GS>;
   asm volatile("" : "+v"(n), "+v"(g));
+  const uint32_t off = static_cast<uint32_t>((32 * (n >> 2) + (n & 3)) * F::kKRow + (KB / 4) * 16 * g);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int h = 0; h < KB / 4; ++h)
-      P.kc[mt][h] = *reinterpret_cast<const u32x4*>(pg.kp + (32 * (n >> 2) + 4 * mt + (n & 3)) * F::kKRow +
-                                                    (KB / 4) * 16 * g + 16 * h);
+      P.kc[mt][h] = *reinterpret_cast<const u32x4*>(pg.kp + off + (4 * mt * F::kKRow + 16 * h));
 }
 template <int KB, int VB, int GS>
 __device__ __forceinline__ void load_vcodes(PageRegs<KB, VB, GS>& P, const PagePtrs& pg, int n, int g) {
   using F = DecFormat<KB, VB, GS>;
   asm volatile("" : "+v"(n), "+v"(g));
+  const uint32_t off = static_cast<uint32_t>(n * F::kVRow + (VB == 2 ? 8 : 16) * g);
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
     if constexpr (VB == 2) {
-      const u32x2 x = *reinterpret_cast<const u32x2*>(pg.vp + (16 * mt + n) * F::kVRow + 8 * g);
+      const u32x2 x = *reinterpret_cast<const u32x2*>(pg.vp + off + 16 * mt * F::kVRow);
       P.vc[mt][0] = x[0];
       P.vc[mt][1] = x[1];
     } else {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(pg.vp + (16 * mt + n) * F::kVRow + 16 * g);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(pg.vp + off + 16 * mt * F::kVRow);
 #pragma unroll
       for (int k = 0; k < 4; ++k) P.vc[mt][k] = x[k];
     }
@@ -383,8 +404,8 @@ __device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState&
     F1[hh] = vr1 * half_bits_to_float(P.vs2[hh] >> 16);
     fmx = fmaxf(fmx, fmaxf(F0[hh], F1[hh]));
   }
-  const float emax = wave_max_all(emx);
-  const float fmaxv = wave_max_all(fmx);
+  const float emax = wave_max_nonneg(emx);
+  const float fmaxv = wave_max_nonneg(fmx);
 
   int ex;
   const float prod = S.qmax * emax;
@@ -825,8 +846,23 @@ __global__ __launch_bounds__(256, (PF ? 2 : DecFormat<KB, VB, GS>::kMinWaves)) v
     __builtin_amdgcn_sched_barrier(0);
     const int ch0 = coef_channel<KB>(lane);
     constexpr int ch1 = DecFormat<KB, VB, GS>::kCh1;
+    // The prefetching kernel visits only the valid pages of the wave (w, w + 4, ...): an invalid id
+    // is passed over by a scalar search and flagged, so its page loop has no per-page branch and the
+    // loads of the next page land in the very registers of the current one (a branch around a bad
+    // page would make the two paths hold the page in different registers, and the copies at their
+    // join wait on every load).  The other kernels test each page as they load it.
+    bool bad_page = false;
+    auto next_valid = [&](int i) {  // first index >= i in steps of kWaves with a valid page id, or >= cnt
+      for (; i < cnt; i += kWaves) {
+        const int pid = bt[i];
+        if (pid >= 0 && pid < num_pages) break;
+        bad_page = true;
+      }
+      return i;
+    };
+    const int i0 = PF ? next_valid(wu) : wu;
     PageRegs<KB, VB, GS> A;
-    load_page(A, page_ptrs<KB, VB, GS>(wu < cnt ? bt[wu] : -1, num_pages, hkv, kvh, k_pool, v_pool), lane, n, g, ch0);
+    load_page(A, page_ptrs<KB, VB, GS>(i0 < cnt ? bt[i0] : -1, num_pages, hkv, kvh, k_pool, v_pool), lane, n, g, ch0);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- rotated, scaled query ------------------------------------------------
@@ -871,20 +907,15 @@ __global__ __launch_bounds__(256, (PF ? 2 : DecFormat<KB, VB, GS>::kMinWaves)) v
     for (int e = lane; e < DecFormat<KB, VB, GS>::kHalves * 16 * kCoefStride; e += 64) (&L.coef[0][0][0])[e] = 0u;
 
     // ---- pages of this wave: w, w + 4, ... ---------------------------------------
-    bool bad_page = false;
+    static_assert(!PF || DecFormat<KB, VB, GS>::kCanPrefetch, "format without a prefetching kernel");
     if constexpr (PF) {
-      static_assert(!PF || DecFormat<KB, VB, GS>::kCanPrefetch, "format without a prefetching kernel");
-      for (int i = wu; i < cnt; i += kWaves) {
-        // the wave's next page (after its last one: no loads)
-        PagePtrs nx = page_ptrs<KB, VB, GS>(bt[i + kWaves < cnt ? i + kWaves : i], num_pages, hkv, kvh,
-                                            k_pool, v_pool);
-        nx.load = i + kWaves < cnt;
-        if (A.ok) {
-          process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, nx, ch0);
-        } else {
-          bad_page = true;
-          if (nx.load) load_page(A, nx, lane, n, g, ch0);
-        }
+      for (int i = i0; i < cnt;) {
+        // the wave's next valid page (after its last one: no loads)
+        const int nxt = next_valid(i + kWaves);
+        PagePtrs nx = page_ptrs<KB, VB, GS>(bt[nxt < cnt ? nxt : i], num_pages, hkv, kvh, k_pool, v_pool);
+        nx.load = nxt < cnt;
+        process_page<KB, VB, GS, PF>(A, S, L, G, lane, g, lo_col, M, nx, ch0);
+        i = nxt;
       }
     } else {
       const PagePtrs none{k_pool, v_pool, false, false};  // no next-page loads in this format
