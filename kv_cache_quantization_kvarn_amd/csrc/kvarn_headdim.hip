@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
 
   const int kvh = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
   const int G = hq / hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4, h = n & 7;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
   const int sl_b = seq_lens[b];
   float* out_b = out + (static_cast<size_t>(b) * hq + static_cast<size_t>(kvh) * G) * D;
   const bool bad = sl_b < 0 || sl_b > max_blocks * kBlockTokens || (sl_b & (kBlockTokens - 1)) != 0;
