@@ -747,6 +747,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
   f32x4 oacc[VMT];  // o~ (rotated basis) of channels (D/4)w + 16mt + 4g + r, head n & 7
 #pragma unroll
   for (int mt = 0; mt < VMT; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Columns of heads >= G are zero for the whole loop and the pages fill only those of heads < G;
+  // every u slot starts at zero and a page writes only the slots of the heads its wave handles.
+  // (The first page's barriers order these stores before any read.)
+  for (int e = tid; e < KH * 16 * L::kKStride; e += kDecThreads)
+    if (((e / L::kKStride) & 7) >= G) (&s.kcoef[0][0][0])[e] = static_cast<_Float16>(0.f);
+  for (int e = tid; e < NVG * 16 * L::kVStride; e += kDecThreads)
+    if (((e / L::kVStride) & 7) >= G) (&s.vcoef[0][0][0])[e] = static_cast<_Float16>(0.f);
+  for (int e = tid; e < kDecWaves * NVG * kMaxGroup; e += kDecThreads) (&s.upart[0][0][0])[e] = 0.f;
+  if (tid < kMaxGroup) s.alpha[tid] = 1.f;
 
   int cur = next_valid(p0);
   if (cur < p1) {
@@ -805,12 +814,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
         for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
           for (int h = 0; h < kMaxGroup; ++h) {
-            const float qg = s.qt[h][j] * gk;
-            _Float16 hi, lo;
-            split_hl(qg * m_ks[kh], hi, lo);
-            s.kcoef[kh][h][slot] = hi;
-            s.kcoef[kh][8 + h][slot] = lo;
-            bp[kh][h] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
+            if (h < G) {
+              const float qg = s.qt[h][j] * gk;
+              _Float16 hi, lo;
+              split_hl(qg * m_ks[kh], hi, lo);
+              s.kcoef[kh][h][slot] = hi;
+              s.kcoef[kh][8 + h][slot] = lo;
+              bp[kh][h] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
+            }
           }
         s.gsv[j] = ex2(m_vg) * inv_sw;
       }
@@ -818,8 +829,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
       for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) {
-          const float t = wave_sump(bp[kh][h]);
-          if (lane == 0) s.bpart[w][kh][h] = t;
+          if (h < G) {
+            const float t = wave_sump(bp[kh][h]);
+            if (lane == 0) s.bpart[w][kh][h] = t;
+          }
         }
       if (tid < kBlockTokens) {
         s.krho[tid] = ex2(m_kr) * inv_sa * scale_log2;
@@ -868,17 +881,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
     {
       const int t0 = 2 * lane, t1 = 2 * lane + 1;
       const int v0 = value_slot(t0), v1 = value_slot(t1);
-      for (int h = w; h < kMaxGroup; h += kDecWaves) {
-        if (h >= G) {
-          if (lane == 0) s.alpha[h] = 1.f;
-#pragma unroll
-          for (int vg = 0; vg < NVG; ++vg) {
-            s.vcoef[vg][h][v0] = s.vcoef[vg][8 + h][v0] = static_cast<_Float16>(0.f);
-            s.vcoef[vg][h][v1] = s.vcoef[vg][8 + h][v1] = static_cast<_Float16>(0.f);
-            if (lane == 0) s.upart[w][vg][h] = 0.f;
-          }
-          continue;
-        }
+      for (int h = w; h < G; h += kDecWaves) {
         const float s0 = s.score[h][t0], s1 = s.score[h][t1];
         const float pm = wave_maxp(fmaxf(s0, s1));
         const float mold = s.mrun[h];
@@ -906,12 +909,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd_kernel(
           s.mrun[h] = mnew;
         }
       }
-      // each head's u sums go to the slot of the wave that handles it; clear this wave's other slots
-      for (int h = 0; h < kMaxGroup; ++h)
-        if ((h % kDecWaves) != w && lane == 0) {
-#pragma unroll
-          for (int vg = 0; vg < NVG; ++vg) s.upart[w][vg][h] = 0.f;
-        }
     }
     __syncthreads();
     // (4) values: channels (D/4)w + 16mt + 4g + r for the head of column n (hi and lo columns summed)
