@@ -95,6 +95,23 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_sump(float x) { return rows_sum(row16_sum(x)); }
+
+// Transposed sum over the 16 lanes of a DPP row: lane n returns the row's total of v[n].  Each stage
+// halves the values a lane holds: it keeps the half whose index bit k equals its own lane bit k and
+// adds the partner's copy of that half, the partners being lanes n^1, n^2, (n - 4) mod 16 and n^8
+// (each differs from n in bit k and agrees in the bits already used).  45 operations for 16 sums, in
+// place of 64 for 16 separate reductions.
+__device__ __forceinline__ float row_transpose_sum16(const float (&v)[16], int n) {
+  const bool b0 = n & 1, b1 = n & 2, b2 = n & 4, b3 = n & 8;
+  float a[8], b[4], c[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (b0 ? v[2 * j + 1] : v[2 * j]) + dpp<kDppXor1>(b0 ? v[2 * j] : v[2 * j + 1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = (b1 ? a[2 * j + 1] : a[2 * j]) + dpp<kDppXor2>(b1 ? a[2 * j] : a[2 * j + 1]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) c[j] = (b2 ? b[2 * j + 1] : b[2 * j]) + dpp<kDppRor4>(b2 ? b[2 * j] : b[2 * j + 1]);
+  return (b3 ? c[1] : c[0]) + dpp<kDppXor8>(b3 ? c[0] : c[1]);
+}
 __device__ __forceinline__ float wave_maxp(float x) { return rows_max(row16_max(x)); }
 
 // code = round-half-even(clamp(x, 0, L)): the low mantissa bits of clamp + 1.5 * 2^23
@@ -114,6 +131,7 @@ struct QhdLds {
   float part_b[HdGeom<D>::kWaves][D];              // per-wave column maxima
   float col[D];                                    // column means, then 2^-gamma
   float qa[kBlockTokens / GS][D], qb[kBlockTokens / GS][D];  // key rounding factors per token half
+  float rowv[D == 64 ? HdGeom<D>::kWaves : 1][64];  // 64 channels: per-wave token means, then 2^-rho / sqrt(D)
 };
 
 // Quantise one tile (block blk of head `head`, keys or values) into the page image, then store it.
@@ -166,6 +184,7 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
 
   // ---- normalisation: rf = 2^-rho / sqrt(D) per token, cf = 2^-gamma per channel -------------
   float rho[NT], rf[NT], cf[NC];
+  float rho_own = 0.f, rf_own = Gm::kInvSqrtD;  // 64 channels: normaliser of token tok(n), kept by lane n
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     rho[i] = 0.f;
@@ -176,21 +195,68 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
   float gam_red = 0.f, cf_red = 1.f;  // gamma of channel tid, kept by reducer thread tid < D
   for (int it = 0; it < kNormIters; ++it) {
     // row pass: per token, over its D channels (16 lanes of a DPP row)
+    if constexpr (NT == 16) {
+      // 64 channels: the 16 lanes of a row share their 16 tokens, so a transposed sum leaves lane n
+      // with token n's moment, lane n updates that token's normaliser, and the wave's LDS row hands
+      // the means and then the factors back to every lane (wave-local: program order suffices)
+      float* rv = &s.rowv[w][16 * g];
+      float acc[16];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      float s1 = 0.f;
+      for (int i = 0; i < NT; ++i) {
+        float s1 = 0.f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
-      const float m = row16_sum(s1) * kInvD;
-      float s2 = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const float d = fmaf(R[i][c], cf[c], -m);
-        s2 = fmaf(d, d, s2);
+        for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
+        acc[i] = s1;
       }
-      const float v = row16_sum(s2) * kInvD;
-      rho[i] += 0.5f * lg2(fmaf(v, rf[i] * rf[i], kNormEps));
-      rf[i] = ex2(-rho[i]) * Gm::kInvSqrtD;
+      rv[n] = row_transpose_sum16(acc, n) * kInvD;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      float mi[16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 x = *reinterpret_cast<const float4*>(rv + 4 * k);
+        mi[4 * k] = x.x; mi[4 * k + 1] = x.y; mi[4 * k + 2] = x.z; mi[4 * k + 3] = x.w;
+      }
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float s2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const float d = fmaf(R[i][c], cf[c], -mi[i]);
+          s2 = fmaf(d, d, s2);
+        }
+        acc[i] = s2;
+      }
+      const float v = row_transpose_sum16(acc, n) * kInvD;
+      rho_own += 0.5f * lg2(fmaf(v, rf_own * rf_own, kNormEps));
+      rf_own = ex2(-rho_own) * Gm::kInvSqrtD;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      rv[n] = rf_own;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 x = *reinterpret_cast<const float4*>(rv + 4 * k);
+        rf[4 * k] = x.x; rf[4 * k + 1] = x.y; rf[4 * k + 2] = x.z; rf[4 * k + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
+        const float m = row16_sum(s1) * kInvD;
+        float s2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const float d = fmaf(R[i][c], cf[c], -m);
+          s2 = fmaf(d, d, s2);
+        }
+        const float v = row16_sum(s2) * kInvD;
+        rho[i] += 0.5f * lg2(fmaf(v, rf[i] * rf[i], kNormEps));
+        rf[i] = ex2(-rho[i]) * Gm::kInvSqrtD;
+      }
     }
     // column pass: per channel, over the 128 tokens (four rows of the wave, then the waves)
 #pragma unroll
@@ -235,7 +301,9 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
     for (int c = 0; c < NC; ++c) cf[c] = s.col[chan(c)];
   }
   // normalisers into the page image: rho of each token from lane n == 0 of its row, gamma from the reducer
-  if (n == 0) {
+  if constexpr (NT == 16) {
+    *reinterpret_cast<float*>(&s.page[Pg::kRho + 4 * tok(n)]) = rho_own;
+  } else if (n == 0) {
 #pragma unroll
     for (int i = 0; i < NT; ++i) *reinterpret_cast<float*>(&s.page[Pg::kRho + 4 * tok(i)]) = rho[i];
   }
@@ -367,7 +435,7 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
 
 // One workgroup per (block, KV head, K or V): tile index 2 (block * hkv + head) + (0 keys, 1 values).
 template <int D, int KB, int VB, int GS>
-__global__ __launch_bounds__(HdGeom<D>::kThreads) void quantize_hd_kernel(
+__global__ __launch_bounds__(HdGeom<D>::kThreads, D == 64 ? 3 : 1) void quantize_hd_kernel(
     const uint16_t* __restrict__ kin, const uint16_t* __restrict__ vin, int hkv,
     const int32_t* __restrict__ dst_pages, uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
     int num_pages, uint32_t* __restrict__ flags) {
@@ -1157,6 +1225,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
     load_k(wu);
     load_v(wu);
   }
+  // key operand columns of heads >= G stay zero for the whole loop; the pages fill the others
+  for (int e = lane; e < KH * 16 * (64 + 8); e += 64)
+    if (((e / (64 + 8)) & 7) >= G) (&W.kcoef[0][0][0])[e] = static_cast<_Float16>(0.f);
   for (int i = wu; i < cnt; i += kDecWaves) {
     const bool more = i + kDecWaves < cnt;  // wave-uniform, like everything decided per page
     const int nx = i + kDecWaves;
@@ -1195,12 +1266,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
         float bp[kMaxGroup];
 #pragma unroll
         for (int hh = 0; hh < kMaxGroup; ++hh) {
-          const float qg = qj[hh] * gk;
-          _Float16 hi, lo;
-          split_hl(qg * m_ks[kh], hi, lo);
-          W.kcoef[kh][hh][slot] = hi;
-          W.kcoef[kh][8 + hh][slot] = lo;
-          bp[hh] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
+          bp[hh] = 0.f;
+          if (hh < G) {
+            const float qg = qj[hh] * gk;
+            _Float16 hi, lo;
+            split_hl(qg * m_ks[kh], hi, lo);
+            W.kcoef[kh][hh][slot] = hi;
+            W.kcoef[kh][8 + hh][slot] = lo;
+            bp[hh] = fmaf(qg, m_kz[kh], -off * (static_cast<float>(hi) + static_cast<float>(lo)));
+          }
         }
         b_h[kh] = head_sums8(bp, lane);
       }
