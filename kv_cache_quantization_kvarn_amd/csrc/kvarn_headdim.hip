@@ -20,8 +20,11 @@
 // Row moments reduce inside the wave (the 16 lanes of a DPP row hold every channel of their
 // tokens); column moments reduce across the four rows of the wave and then across waves through
 // LDS.  Every pass is centred in two sweeps (mean, then the mean square of the deviations), so no
-// fp32 cancellation can lose digits.  The page is assembled in LDS (codes, scale/zero, rho, gamma)
-// and written with 16-byte stores.
+// fp32 cancellation can lose digits, except the first row pass: with every column normaliser 1 its
+// moments follow from the input (a token's mean is its first input value, its mean square the square
+// sum of its inputs), and it is taken from them when every token of the wave keeps its mean square
+// above twice its squared mean (at most one bit lost to cancellation), else centred as the others.
+// The page is assembled in LDS (codes, scale/zero, rho, gamma) and written with 16-byte stores.
 //
 // Decode.  One workgroup of four waves per (sequence, KV head, split), the same split plan, partial
 // layout and fence-free hand-off as the 128-channel decode.  With q~ = H q (orthonormal H) the page
@@ -132,6 +135,7 @@ struct QhdLds {
   float col[D];                                    // column means, then 2^-gamma
   float qa[kBlockTokens / GS][D], qb[kBlockTokens / GS][D];  // key rounding factors per token half
   float rowv[D == 64 ? HdGeom<D>::kWaves : 1][64];  // 64 channels: per-wave token means, then 2^-rho / sqrt(D)
+  float2 tokm[HdGeom<D>::kWaves][HdGeom<D>::kTokPerWave];  // first row pass: mean and mean square per token
 };
 
 // Quantise one tile (block blk of head `head`, keys or values) into the page image, then store it.
@@ -181,6 +185,28 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
 #pragma unroll
         for (int r = 0; r < 4; ++r) R[4 * mt + r][2 * ho + hh] = d[r];
       }
+  // The first row pass's moments from the input: with every column normaliser still 1, a token's
+  // mean over the rotated channels is its first input value (only row 0 of the +-1 matrix sums to
+  // D) and its mean square the square sum of its inputs (the matrix times its transpose is D I).
+  // Row g = 0 of the wave stores them for token w*TW + 16 mt + n.
+  {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float q = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < CH; ++gi)
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const h2 x = {xa[mt][gi][i], xa[mt][gi][i + 1]};
+          q = __builtin_amdgcn_fdot2(x, x, q, false);
+        }
+      q = rows_sum(q);
+      if (g == 0) s.tokm[w][16 * mt + n] = make_float2(static_cast<float>(xa[mt][0][0]), q);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
 
   // ---- normalisation: rf = 2^-rho / sqrt(D) per token, cf = 2^-gamma per channel -------------
   float rho[NT], rf[NT], cf[NC];
@@ -200,34 +226,44 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
       // with token n's moment, lane n updates that token's normaliser, and the wave's LDS row hands
       // the means and then the factors back to every lane (wave-local: program order suffices)
       float* rv = &s.rowv[w][16 * g];
-      float acc[16];
-#pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float s1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
-        acc[i] = s1;
+      float v = 0.f;  // variance of token tok(n)
+      bool from_input = false;
+      if (it == 0) {
+        // one sweep from the input moments, unless a token's mean could cancel digits of its variance
+        const float2 me = s.tokm[w][16 * (n >> 2) + 4 * g + (n & 3)];
+        v = fmaf(-me.x, me.x, me.y);
+        from_input = __builtin_amdgcn_ballot_w64(!(v >= 0.5f * me.y)) == 0;
       }
-      rv[n] = row_transpose_sum16(acc, n) * kInvD;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      float mi[16];
+      if (!from_input) {
+        float acc[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float4 x = *reinterpret_cast<const float4*>(rv + 4 * k);
-        mi[4 * k] = x.x; mi[4 * k + 1] = x.y; mi[4 * k + 2] = x.z; mi[4 * k + 3] = x.w;
-      }
+        for (int i = 0; i < NT; ++i) {
+          float s1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float s2 = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float d = fmaf(R[i][c], cf[c], -mi[i]);
-          s2 = fmaf(d, d, s2);
+          for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
+          acc[i] = s1;
         }
-        acc[i] = s2;
+        rv[n] = row_transpose_sum16(acc, n) * kInvD;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        float mi[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float4 x = *reinterpret_cast<const float4*>(rv + 4 * k);
+          mi[4 * k] = x.x; mi[4 * k + 1] = x.y; mi[4 * k + 2] = x.z; mi[4 * k + 3] = x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          float s2 = 0.f;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const float d = fmaf(R[i][c], cf[c], -mi[i]);
+            s2 = fmaf(d, d, s2);
+          }
+          acc[i] = s2;
+        }
+        v = row_transpose_sum16(acc, n) * kInvD;
       }
-      const float v = row_transpose_sum16(acc, n) * kInvD;
       rho_own += 0.5f * lg2(fmaf(v, rf_own * rf_own, kNormEps));
       rf_own = ex2(-rho_own) * Gm::kInvSqrtD;
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -241,21 +277,43 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
         rf[4 * k] = x.x; rf[4 * k + 1] = x.y; rf[4 * k + 2] = x.z; rf[4 * k + 3] = x.w;
       }
     } else {
+      bool from_input = false;
+      if (it == 0) {
+        // one sweep from the input moments, unless a token's mean could cancel digits of its variance
+        float vi[NT];
+        bool fine = true;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        float s1 = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
-        const float m = row16_sum(s1) * kInvD;
-        float s2 = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float d = fmaf(R[i][c], cf[c], -m);
-          s2 = fmaf(d, d, s2);
+        for (int i = 0; i < NT; ++i) {
+          const float2 me = s.tokm[w][16 * (i >> 2) + 4 * g + (i & 3)];
+          vi[i] = fmaf(-me.x, me.x, me.y);
+          fine = fine && vi[i] >= 0.5f * me.y;
         }
-        const float v = row16_sum(s2) * kInvD;
-        rho[i] += 0.5f * lg2(fmaf(v, rf[i] * rf[i], kNormEps));
-        rf[i] = ex2(-rho[i]) * Gm::kInvSqrtD;
+        from_input = __builtin_amdgcn_ballot_w64(!fine) == 0;
+        if (from_input) {
+#pragma unroll
+          for (int i = 0; i < NT; ++i) {
+            rho[i] += 0.5f * lg2(fmaf(vi[i], rf[i] * rf[i], kNormEps));
+            rf[i] = ex2(-rho[i]) * Gm::kInvSqrtD;
+          }
+        }
+      }
+      if (!from_input) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+          float s1 = 0.f;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) s1 = fmaf(R[i][c], cf[c], s1);
+          const float m = row16_sum(s1) * kInvD;
+          float s2 = 0.f;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const float d = fmaf(R[i][c], cf[c], -m);
+            s2 = fmaf(d, d, s2);
+          }
+          const float v = row16_sum(s2) * kInvD;
+          rho[i] += 0.5f * lg2(fmaf(v, rf[i] * rf[i], kNormEps));
+          rf[i] = ex2(-rho[i]) * Gm::kInvSqrtD;
+        }
       }
     }
     // column pass: per channel, over the 128 tokens (four rows of the wave, then the waves)
