@@ -305,6 +305,45 @@ def test_device_flags(K, cfg):
     assert float((out[0] - good[0]).abs().max()) <= 1e-6
 
 
+def test_bad_pages_skipped_at_every_position(K, cfg):
+    # 128 (sequence, KV head) pairs over 64 blocks: the plan gives 4 splits of 16 pages, four per wave,
+    # on the prefetching kernel, which passes over invalid ids by a scalar search of the wave's list
+    say("case: invalid page ids first, consecutive, last and throughout waves' page lists (prefetching plan)")
+    g = torch.Generator().manual_seed(11)
+    batch, hkv, hq, nb, npages = 64, 2, 12, 64, 24
+    k = torch.randn(npages * 128, hkv, 128, generator=g)
+    k = k.mul_(torch.where(torch.rand(128, generator=g) < 0.04, 20.0, 1.0))
+    v = torch.randn(npages * 128, hkv, 128, generator=g) * torch.exp(0.5 * torch.randn(npages * 128, hkv, 1, generator=g))
+    kp, vp, fl = gpu_quantize(K, cfg, k.half().cuda(), v.half().cuda(), torch.arange(npages, dtype=torch.int32), npages)
+    assert fl == 0
+    bt = torch.randint(0, npages, (batch, nb), generator=g, dtype=torch.int32)
+    bad = {0: [0],                       # first page of wave 0
+           1: [0, 4, 8],                 # wave 0's first three pages in a row
+           2: [15, 31, 47, 63],          # the last page of every split
+           3: list(range(nb)),           # no valid page at all
+           4: list(range(16, 32)),       # a whole split
+           5: [1, 2, 3, 60, 61, 62, 63]}  # first pages of three waves, then a split's tail
+    for b, pos in bad.items():
+        for j, p_ in enumerate(pos):
+            bt[b, p_] = -1 if j % 2 == 0 else npages + 5
+    sl = torch.full((batch,), nb * 128, dtype=torch.int32)
+    q = torch.randn(batch, hq, 128, generator=g).half().cuda()
+    out, fl = gpu_decode(K, cfg, q, kp, vp, bt, sl, hkv)
+    assert fl == 1
+    outh = out.cpu().numpy()
+    assert np.all(outh[3] == 0)  # nothing to attend to
+    # reference: attention over each sequence's valid pages only, packed to the front of its row
+    ref_bt = torch.full_like(bt, -1)
+    ref_sl = torch.zeros_like(sl)
+    for b in range(batch):
+        keep = bt[b][(bt[b] >= 0) & (bt[b] < npages)]
+        ref_bt[b, :len(keep)] = keep
+        ref_sl[b] = 128 * len(keep)
+    seqs = [0, 1, 2, 4, 5, 6, 63]
+    compare_decode_full(outh, q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), ref_bt.numpy(), ref_sl.numpy(),
+                        hkv, pairs=[(b, h) for b in seqs for h in range(hq)], label="decode with invalid pages")
+
+
 def test_empty_calls(K, cfg):
     say("case: zero blocks and zero batch")
     kp, vp = K.alloc_pools(cfg, 1, 1)
