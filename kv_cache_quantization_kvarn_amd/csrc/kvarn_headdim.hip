@@ -77,19 +77,13 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
   return p;
 }
 
-// Sum / min / max over lanes l, l^16, l^32, l^48 (permlane swaps return the pair in lane order, so
+// Sum / max over lanes l, l^16, l^32, l^48 (permlane swaps return the pair in lane order, so
 // every lane combines the same values in the same order and gets identical bits).
 __device__ __forceinline__ float rows_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float rows_min(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float rows_max(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -98,6 +92,33 @@ __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_sump(float x) { return rows_sum(row16_sum(x)); }
+
+// Transposed sum (or min, max) over the four 16-lane rows of a wave of NC values per lane: v[c] is
+// combined over lanes l, l^16, l^32, l^48 and lane l of row g keeps the results of c = 4m + g, out[m].  A swap of the
+// odd rows of one register with the even rows of another (v_permlane16_swap) pairs v[2k] of the even
+// rows with v[2k + 1] of the odd ones, so one swap and one add per pair halve the values a lane holds;
+// v_permlane32_swap does the same across the two row pairs.  3 NC / 4 swaps and adds, in place of
+// four operations (two swaps, two adds) per value for separate sums.
+template <int NC, class Op>
+__device__ __forceinline__ void rows_transpose(const float (&v)[NC], float (&out)[NC / 4], Op op) {
+  float h[NC / 2];
+#pragma unroll
+  for (int k = 0; k < NC / 2; ++k) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[2 * k]), __float_as_uint(v[2 * k + 1]),
+                                                    false, false);
+    h[k] = op(__uint_as_float(r[0]), __uint_as_float(r[1]));  // c = 2k + (row & 1)
+  }
+#pragma unroll
+  for (int m = 0; m < NC / 4; ++m) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(h[2 * m]), __float_as_uint(h[2 * m + 1]),
+                                                    false, false);
+    out[m] = op(__uint_as_float(r[0]), __uint_as_float(r[1]));  // c = 4m + row
+  }
+}
+template <int NC>
+__device__ __forceinline__ void rows_transpose_sum(const float (&v)[NC], float (&out)[NC / 4]) {
+  rows_transpose(v, out, [](float a, float b) { return a + b; });
+}
 
 // Transposed sum over the 16 lanes of a DPP row: lane n returns the row's total of v[n].  Each stage
 // halves the values a lane holds: it keeps the half whose index bit k equals its own lane bit k and
@@ -317,13 +338,17 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
       }
     }
     // column pass: per channel, over the 128 tokens (four rows of the wave, then the waves)
+    {
+      float s1[NC], t1[NC / 4];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float s1 = 0.f;
+      for (int c = 0; c < NC; ++c) {
+        s1[c] = 0.f;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) s1 = fmaf(R[i][c], rf[i], s1);
-      s1 = rows_sum(s1);
-      if (g == 0) s.part_a[w][chan(c)] = s1;
+        for (int i = 0; i < NT; ++i) s1[c] = fmaf(R[i][c], rf[i], s1[c]);
+      }
+      rows_transpose_sum(s1, t1);
+#pragma unroll
+      for (int m = 0; m < NC / 4; ++m) s.part_a[w][chan(4 * m + g)] = t1[m];
     }
     __syncthreads();
     if (tid < D) {
@@ -333,17 +358,21 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
       s.col[tid] = t * kInvBlock;
     }
     __syncthreads();
+    {
+      float s2[NC], t2[NC / 4];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const float m = s.col[chan(c)];
-      float s2 = 0.f;
+      for (int c = 0; c < NC; ++c) {
+        const float m = s.col[chan(c)];
+        s2[c] = 0.f;
 #pragma unroll
-      for (int i = 0; i < NT; ++i) {
-        const float d = fmaf(R[i][c], rf[i], -m);
-        s2 = fmaf(d, d, s2);
+        for (int i = 0; i < NT; ++i) {
+          const float d = fmaf(R[i][c], rf[i], -m);
+          s2[c] = fmaf(d, d, s2[c]);
+        }
       }
-      s2 = rows_sum(s2);
-      if (g == 0) s.part_a[w][chan(c)] = s2;
+      rows_transpose_sum(s2, t2);
+#pragma unroll
+      for (int m = 0; m < NC / 4; ++m) s.part_a[w][chan(4 * m + g)] = t2[m];
     }
     __syncthreads();
     if (tid < D) {
@@ -375,19 +404,24 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int c = 0; c < NC; ++c) R[i][c] *= rf[i];
+    {
+      float a[NC], b[NC], ta[NC / 4], tb[NC / 4];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float a = R[0][c], b = R[0][c];
+      for (int c = 0; c < NC; ++c) {
+        a[c] = R[0][c];
+        b[c] = R[0][c];
 #pragma unroll
-      for (int i = 1; i < NT; ++i) {
-        a = fminf(a, R[i][c]);
-        b = fmaxf(b, R[i][c]);
+        for (int i = 1; i < NT; ++i) {
+          a[c] = fminf(a[c], R[i][c]);
+          b[c] = fmaxf(b[c], R[i][c]);
+        }
       }
-      a = rows_min(a);
-      b = rows_max(b);
-      if (g == 0) {
-        s.part_a[w][chan(c)] = a;
-        s.part_b[w][chan(c)] = b;
+      rows_transpose(a, ta, [](float x, float y) { return fminf(x, y); });
+      rows_transpose(b, tb, [](float x, float y) { return fmaxf(x, y); });
+#pragma unroll
+      for (int m = 0; m < NC / 4; ++m) {
+        s.part_a[w][chan(4 * m + g)] = ta[m];
+        s.part_b[w][chan(4 * m + g)] = tb[m];
       }
     }
     __syncthreads();
