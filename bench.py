@@ -38,10 +38,10 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("a27679966e4aaf7f", 663324565),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("a27679966e4aaf7f", 332395558),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("5cffa2c0ffb3f4d0", 67420140),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("5cffa2c0ffb3f4d0", 129020928),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("a27679966e4aaf7f", 663253717),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("a27679966e4aaf7f", 332419988),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397599),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 128998464),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
 # helpers and the host plan that picks its launch shape and instance
@@ -51,8 +51,8 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
 MEASURED_VALU = {
     ("quantize_kernel", "llama3_8b_layer_16x8192"): ("a27679966e4aaf7f", 120274944),
     ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("a27679966e4aaf7f", 61213158),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("5cffa2c0ffb3f4d0", 6171970),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("5cffa2c0ffb3f4d0", 10341056),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 5967170),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 9927360),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
