@@ -110,13 +110,6 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
   return p;
 }
 
-// Low bytes of four registers, packed little endian into one dword.
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u);  // [b0.0, b1.0, 0, 0]
-  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);  // [0, 0, b2.0, b3.0]
-  return lo | hi;
-}
-
 // 4x4 byte transpose inside each quad of lanes (DPP): lane j holds bytes B[j][0..3] and
 // receives B[0..3][j].
 __device__ __forceinline__ uint32_t quad_transpose(uint32_t v, int j) {
@@ -419,8 +412,9 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
     // M = R' times the normaliser across the group axis; N = M times the group's own
     // normaliser (positive), so the group's min and max of N are those of M scaled, and
-    // that factor is folded into the rounding FMA.  Codes come out of
-    // clamp(u, 0, L) + 1.5*2^23, whose low mantissa bits hold round-half-even(u).
+    // that factor is folded into the rounding FMA.  Codes are round-half-even(clamp(u, 0, L)):
+    // the byte conversion v_cvt_pk_u8_f32 for 4-bit keys and 2-bit values, the low mantissa bits
+    // of clamp(u, 0, L) + 1.5*2^23 for the other widths.
     constexpr float kRoundMagic = 12582912.0f;
     if constexpr (!kIsV) {
       // key groups: one channel over the 128 tokens, 2^kBits levels
@@ -487,19 +481,24 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
       };
       if constexpr (kBits == 4) {
         // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
-        // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j)
+        // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j).
+        // v_cvt_pk_u8_f32 rounds the clamped value to nearest even (as the magic add does) and
+        // writes it into byte y, so the even-channel codes of the four tokens fill one dword, the
+        // odd-channel codes another, and one shift-or pairs them.
         const int j = n & 3, q = n >> 2;
+        auto kclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[c], qb[c]), 0.f), kLevels); };
 #pragma unroll
         for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
           for (int h4 = 0; h4 < 4; ++h4) {
-            uint32_t by[4];
+            uint32_t ce = 0, co = 0;
 #pragma unroll
             for (int y = 0; y < 4; ++y) {
               const int i = 4 * ih + y;
-              by[y] = kcode(i, 2 * h4) | (kcode(i, 2 * h4 + 1) << 4);
+              ce = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(i, 2 * h4), y, ce);
+              co = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(i, 2 * h4 + 1), y, co);
             }
-            const uint32_t word = quad_transpose(pack4(by[0], by[1], by[2], by[3]), j);
+            const uint32_t word = quad_transpose(ce | (co << 4), j);
             __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 4 * ih + j) * 64 + 16 * h4 + 4 * q, 0, 0);
           }
         }
@@ -616,22 +615,23 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
         // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
         // of unit u: bytes 8w + 4ih .. +3 of that channel.
+        // v_cvt_pk_u8_f32 (round to nearest even, into byte y) gathers the k-th code of the four
+        // bytes in one dword per k; shifts by 2k put the four dwords' codes side by side in every byte.
+        auto vclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels); };
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (kHalf && u == 2) load_q(1);  // channels c = 4..7 from here on
-          uint32_t by[4];
+          uint32_t d[4];
 #pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const int c = 2 * u + (y >> 1), ih = y & 1;
-            uint32_t b = 0;
+          for (int k = 0; k < 4; ++k) {
+            d[k] = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int i = 4 * ih + k;
-              b = k == 0 ? vcode(i, c) : (b | (vcode(i, c) << (2 * k)));
+            for (int y = 0; y < 4; ++y) {
+              const int c = 2 * u + (y >> 1), ih = y & 1;
+              d[k] = __builtin_amdgcn_cvt_pk_u8_f32(vclamp(4 * ih + k, c), y, d[k]);
             }
-            by[y] = b;
           }
-          const uint32_t word = row_transpose(pack4(by[0], by[1], by[2], by[3]), g);
+          const uint32_t word = row_transpose(d[0] | (d[1] << 2) | (d[2] << 4) | (d[3] << 6), g);
           const int c = 2 * u + (g >> 1), ih = g & 1;
           __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 32 + 8 * w + 4 * ih, 0, 0);
         }
