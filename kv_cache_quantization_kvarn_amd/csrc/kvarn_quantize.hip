@@ -412,10 +412,8 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // ---- 3. per-group min/max, fp16 scale and zero, round to nearest, pack ------
     // M = R' times the normaliser across the group axis; N = M times the group's own
     // normaliser (positive), so the group's min and max of N are those of M scaled, and
-    // that factor is folded into the rounding FMA.  Codes are round-half-even(clamp(u, 0, L)):
-    // the byte conversion v_cvt_pk_u8_f32 for 4-bit keys and 2-bit values, the low mantissa bits
-    // of clamp(u, 0, L) + 1.5*2^23 for the other widths.
-    constexpr float kRoundMagic = 12582912.0f;
+    // that factor is folded into the rounding FMA.  Codes are round-half-even(clamp(u, 0, L)) by the
+    // byte conversion v_cvt_pk_u8_f32, which also places each code in a chosen byte of a dword.
     if constexpr (!kIsV) {
       // key groups: one channel over the 128 tokens, 2^kBits levels
 #pragma unroll
@@ -476,9 +474,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
       const float4 b1 = *reinterpret_cast<const float4*>(&s.mul_b[kh][8 * n + 4]);
       const float qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       const float qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      auto kcode = [&](int i, int c) {
-        return __float_as_uint(fminf(fmaxf(fmaf(R[i][c], qa[c], qb[c]), 0.f), kLevels) + kRoundMagic);
-      };
+      auto kclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[c], qb[c]), 0.f), kLevels); };
       if constexpr (kBits == 4) {
         // byte (i, h4) = code(c = 2h4) | code(c = 2h4 + 1) << 4 is byte 16*h4 + n of token T(i);
         // a quad transpose gives lane j of quad q the dword at bytes 16*h4 + 4q of token T(4*ih + j).
@@ -486,7 +482,6 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         // writes it into byte y, so the even-channel codes of the four tokens fill one dword, the
         // odd-channel codes another, and one shift-or pairs them.
         const int j = n & 3, q = n >> 2;
-        auto kclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[c], qb[c]), 0.f), kLevels); };
 #pragma unroll
         for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
@@ -511,9 +506,10 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         for (int k = 0; k < 4; ++k) {
 #pragma unroll
           for (int h4 = 0; h4 < 4; ++h4) {
-            const uint32_t h0 = (kcode(2 * k, 2 * h4) & 0xFFu) | ((kcode(2 * k, 2 * h4 + 1) & 0xFFu) << 8);
-            const uint32_t h1 = (kcode(2 * k + 1, 2 * h4) & 0xFFu) | ((kcode(2 * k + 1, 2 * h4 + 1) & 0xFFu) << 8);
-            const uint32_t v = h0 | (h1 << 16);
+            uint32_t v = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(2 * k, 2 * h4), 0, 0u);
+            v = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(2 * k, 2 * h4 + 1), 1, v);
+            v = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(2 * k + 1, 2 * h4), 2, v);
+            v = __builtin_amdgcn_cvt_pk_u8_f32(kclamp(2 * k + 1, 2 * h4 + 1), 3, v);
             const uint32_t p = dpp_u32(v, 0);  // lane n ^ 1
             const uint32_t word = odd ? ((p >> 16) | (v & 0xFFFF0000u)) : ((v & 0xFFFFu) | (p << 16));
             __builtin_amdgcn_raw_buffer_store_b32(word, dst, tok_of(w, g, 2 * k + (odd ? 1 : 0)) * 128 + 32 * h4 +
@@ -608,16 +604,13 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         qb[0] = b0.x; qb[1] = b0.y; qb[2] = b0.z; qb[3] = b0.w; qb[4] = b1.x; qb[5] = b1.y; qb[6] = b1.z; qb[7] = b1.w;
       };
       load_q(0);
-      auto vcode = [&](int i, int c) {
-        return __float_as_uint(fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels) + kRoundMagic);
-      };
+      auto vclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels); };
       if constexpr (kBits == 2) {
         // byte (c, ih) = codes of tokens T(4ih + y), y = 0..3, at bits 2y: byte 8w + 4ih + g of
         // channel C(c).  A row transpose gives row y the dword of combination (c, ih) = (2u + y/2, y%2)
         // of unit u: bytes 8w + 4ih .. +3 of that channel.
         // v_cvt_pk_u8_f32 (round to nearest even, into byte y) gathers the k-th code of the four
         // bytes in one dword per k; shifts by 2k put the four dwords' codes side by side in every byte.
-        auto vclamp = [&](int i, int c) { return fminf(fmaxf(fmaf(R[i][c], qa[i], qb[i]), 0.f), kLevels); };
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (kHalf && u == 2) load_q(1);  // channels c = 4..7 from here on
@@ -644,15 +637,15 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           if (kHalf && c == 4) load_q(1);  // channels c = 4..7 from here on
-          uint32_t hw[2];
+          // byte 2 ih + kk holds tokens T(4 ih + 2 kk) (low nibble) and T(4 ih + 2 kk + 1) (high nibble)
+          uint32_t ce = 0, co = 0;
 #pragma unroll
-          for (int ih = 0; ih < 2; ++ih) {
-            uint32_t b = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) b |= (vcode(4 * ih + k, c) & 0xFu) << (4 * k);
-            hw[ih] = b;
+          for (int y = 0; y < 4; ++y) {
+            const int i = 4 * (y >> 1) + 2 * (y & 1);
+            ce = __builtin_amdgcn_cvt_pk_u8_f32(vclamp(i, c), y, ce);
+            co = __builtin_amdgcn_cvt_pk_u8_f32(vclamp(i + 1, c), y, co);
           }
-          const uint32_t v = hw[0] | (hw[1] << 16);
+          const uint32_t v = ce | (co << 4);
           const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
           const uint32_t word = odd ? ((r[0] >> 16) | (r[1] & 0xFFFF0000u)) : ((r[0] & 0xFFFFu) | (r[1] << 16));
           __builtin_amdgcn_raw_buffer_store_b32(word, dst, chan_of(n, c) * 64 + 16 * w + 8 * (odd ? 1 : 0) +
