@@ -120,21 +120,25 @@ __device__ __forceinline__ void rows_transpose_sum(const float (&v)[NC], float (
   rows_transpose(v, out, [](float a, float b) { return a + b; });
 }
 
-// Transposed sum over the 16 lanes of a DPP row: lane n returns the row's total of v[n].  Each stage
+// Transposed sum (or min, max) over the 16 lanes of a DPP row: lane n returns the row's total of v[n].  Each stage
 // halves the values a lane holds: it keeps the half whose index bit k equals its own lane bit k and
 // adds the partner's copy of that half, the partners being lanes n^1, n^2, (n - 4) mod 16 and n^8
 // (each differs from n in bit k and agrees in the bits already used).  45 operations for 16 sums, in
 // place of 64 for 16 separate reductions.
-__device__ __forceinline__ float row_transpose_sum16(const float (&v)[16], int n) {
+template <class Op>
+__device__ __forceinline__ float row_transpose16(const float (&v)[16], int n, Op op) {
   const bool b0 = n & 1, b1 = n & 2, b2 = n & 4, b3 = n & 8;
   float a[8], b[4], c[2];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) a[j] = (b0 ? v[2 * j + 1] : v[2 * j]) + dpp<kDppXor1>(b0 ? v[2 * j] : v[2 * j + 1]);
+  for (int j = 0; j < 8; ++j) a[j] = op(b0 ? v[2 * j + 1] : v[2 * j], dpp<kDppXor1>(b0 ? v[2 * j] : v[2 * j + 1]));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = (b1 ? a[2 * j + 1] : a[2 * j]) + dpp<kDppXor2>(b1 ? a[2 * j] : a[2 * j + 1]);
+  for (int j = 0; j < 4; ++j) b[j] = op(b1 ? a[2 * j + 1] : a[2 * j], dpp<kDppXor2>(b1 ? a[2 * j] : a[2 * j + 1]));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) c[j] = (b2 ? b[2 * j + 1] : b[2 * j]) + dpp<kDppRor4>(b2 ? b[2 * j] : b[2 * j + 1]);
-  return (b3 ? c[1] : c[0]) + dpp<kDppXor8>(b3 ? c[0] : c[1]);
+  for (int j = 0; j < 2; ++j) c[j] = op(b2 ? b[2 * j + 1] : b[2 * j], dpp<kDppRor4>(b2 ? b[2 * j] : b[2 * j + 1]));
+  return op(b3 ? c[1] : c[0], dpp<kDppXor8>(b3 ? c[0] : c[1]));
+}
+__device__ __forceinline__ float row_transpose_sum16(const float (&v)[16], int n) {
+  return row_transpose16(v, n, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ float wave_maxp(float x) { return rows_max(row16_max(x)); }
 
@@ -471,35 +475,83 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
     for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int c = 0; c < NC; ++c) R[i][c] *= cf[c];
+    // 64 channels (one value group per token): lane n finds token tok(n)'s minimum and maximum by
+    // transposed reductions, computes its scale, zero and rounding factors once, and the wave's LDS
+    // row (the first row pass's moment slots, free by now) hands the factors to every lane
+    [[maybe_unused]] float qv[NT][2];
+    if constexpr (NT == 16) {
+      static_assert(NVG == 1, "one value group per token at 64 channels");
+      float a[16], b[16];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        a[i] = R[i][0];
+        b[i] = R[i][0];
+#pragma unroll
+        for (int c = 1; c < NC; ++c) {
+          a[i] = fminf(a[i], R[i][c]);
+          b[i] = fmaxf(b[i], R[i][c]);
+        }
+      }
+      const float mn = mul_rn(row_transpose16(a, n, [](float x, float y) { return fminf(x, y); }), rf_own);
+      const float mx = mul_rn(row_transpose16(b, n, [](float x, float y) { return fmaxf(x, y); }), rf_own);
+      const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
+      const uint32_t zb = float_to_half_bits(mn);
+      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+      *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * tok(n)]) = static_cast<uint16_t>(sb);
+      *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * tok(n)]) = static_cast<uint16_t>(zb);
+      float2* tq = &s.tokm[w][0];
+      tq[16 * (n >> 2) + 4 * g + (n & 3)] = make_float2(rf_own * inv, -zf * inv);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float4 x = *reinterpret_cast<const float4*>(&tq[16 * mt + 4 * g + 2 * h2]);
+          qv[4 * mt + 2 * h2][0] = x.x;
+          qv[4 * mt + 2 * h2][1] = x.y;
+          qv[4 * mt + 2 * h2 + 1][0] = x.z;
+          qv[4 * mt + 2 * h2 + 1][1] = x.w;
+        }
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int t0 = w * TW + 16 * mt + 4 * g;  // the four consecutive tokens of this lane
 #pragma unroll
       for (int vg = 0; vg < NVG; ++vg) {
         float qa[4], qb[4];
+        if constexpr (NT == 16) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * mt + r;
-          float a = R[i][CPG * vg], b = R[i][CPG * vg];
+          for (int r = 0; r < 4; ++r) {
+            qa[r] = qv[4 * mt + r][0];
+            qb[r] = qv[4 * mt + r][1];
+          }
+        } else {
 #pragma unroll
-          for (int c = CPG * vg + 1; c < CPG * (vg + 1); ++c) {
-            a = fminf(a, R[i][c]);
-            b = fmaxf(b, R[i][c]);
+          for (int r = 0; r < 4; ++r) {
+            const int i = 4 * mt + r;
+            float a = R[i][CPG * vg], b = R[i][CPG * vg];
+#pragma unroll
+            for (int c = CPG * vg + 1; c < CPG * (vg + 1); ++c) {
+              a = fminf(a, R[i][c]);
+              b = fmaxf(b, R[i][c]);
+            }
+            const float mn = mul_rn(row16_min(a), rf[i]);
+            const float mx = mul_rn(row16_max(b), rf[i]);
+            const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
+            const uint32_t zb = float_to_half_bits(mn);
+            const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+            const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+            if (n == 0) {
+              *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * (kBlockTokens * vg + tok(i))]) =
+                  static_cast<uint16_t>(sb);
+              *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * (kBlockTokens * vg + tok(i))]) =
+                  static_cast<uint16_t>(zb);
+            }
+            qa[r] = rf[i] * inv;
+            qb[r] = -zf * inv;
           }
-          const float mn = mul_rn(row16_min(a), rf[i]);
-          const float mx = mul_rn(row16_max(b), rf[i]);
-          const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
-          const uint32_t zb = float_to_half_bits(mn);
-          const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
-          const float inv = sf > 0.f ? 1.0f / sf : 0.f;
-          if (n == 0) {
-            *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * (kBlockTokens * vg + tok(i))]) =
-                static_cast<uint16_t>(sb);
-            *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * (kBlockTokens * vg + tok(i))]) =
-                static_cast<uint16_t>(zb);
-          }
-          qa[r] = rf[i] * inv;
-          qb[r] = -zf * inv;
         }
 #pragma unroll
         for (int c = CPG * vg; c < CPG * (vg + 1); ++c) {
