@@ -137,6 +137,20 @@ __device__ __forceinline__ float row_transpose16(const float (&v)[16], int n, Op
   for (int j = 0; j < 2; ++j) c[j] = op(b2 ? b[2 * j + 1] : b[2 * j], dpp<kDppRor4>(b2 ? b[2 * j] : b[2 * j + 1]));
   return op(b3 ? c[1] : c[0], dpp<kDppXor8>(b3 ? c[0] : c[1]));
 }
+// The same over 8 values: after three halving stages (partners n^1, n^2, (n - 4) mod 16) lanes n and
+// n^8 hold the combination of v[n & 7] over their halves of the row, and one exchange across them
+// completes it: lane n returns the row's total of v[n & 7].
+template <class Op>
+__device__ __forceinline__ float row_transpose8(const float (&v)[8], int n, Op op) {
+  const bool b0 = n & 1, b1 = n & 2, b2 = n & 4;
+  float a[4], b[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a[j] = op(b0 ? v[2 * j + 1] : v[2 * j], dpp<kDppXor1>(b0 ? v[2 * j] : v[2 * j + 1]));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) b[j] = op(b1 ? a[2 * j + 1] : a[2 * j], dpp<kDppXor2>(b1 ? a[2 * j] : a[2 * j + 1]));
+  const float c = op(b2 ? b[1] : b[0], dpp<kDppRor4>(b2 ? b[0] : b[1]));
+  return op(c, dpp<kDppXor8>(c));
+}
 __device__ __forceinline__ float row_transpose_sum16(const float (&v)[16], int n) {
   return row_transpose16(v, n, [](float x, float y) { return x + y; });
 }
@@ -160,7 +174,9 @@ struct QhdLds {
   float col[D];                                    // column means, then 2^-gamma
   float qa[kBlockTokens / GS][D], qb[kBlockTokens / GS][D];  // key rounding factors per token half
   float rowv[D == 64 ? HdGeom<D>::kWaves : 1][64];  // 64 channels: per-wave token means, then 2^-rho / sqrt(D)
-  float2 tokm[HdGeom<D>::kWaves][HdGeom<D>::kTokPerWave];  // first row pass: mean and mean square per token
+  alignas(16) float2 tokm[HdGeom<D>::kWaves][HdGeom<D>::kTokPerWave];  // first row pass: mean, mean square
+  // 256 channels: value rounding factors per (token, channel group) of each wave
+  alignas(16) float2 vfac[D == 256 ? HdGeom<D>::kWaves : 1][D == 256 ? 2 * HdGeom<D>::kTokPerWave : 1];
 };
 
 // Quantise one tile (block blk of head `head`, keys or values) into the page image, then store it.
@@ -479,6 +495,52 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
     // transposed reductions, computes its scale, zero and rounding factors once, and the wave's LDS
     // row (the first row pass's moment slots, free by now) hands the factors to every lane
     [[maybe_unused]] float qv[NT][2];
+    [[maybe_unused]] float qw[NT][2][2];  // 256 channels: [token][group][qa, qb]
+    if constexpr (NT == 4 && NVG == 2) {
+      // 256 channels: 4 tokens x 2 channel groups per lane, so the row's 16 lanes reduce the 8 groups
+      // transposed, lanes n and n^8 ending with group (token (n & 7) / 2, half n & 1); each such lane
+      // computes that group's scale, zero and factors once and the wave's LDS rows hand them back
+      float a[8], b[8];
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int vg = 0; vg < NVG; ++vg) {
+          float x = R[i][CPG * vg], y = R[i][CPG * vg];
+#pragma unroll
+          for (int c = CPG * vg + 1; c < CPG * (vg + 1); ++c) {
+            x = fminf(x, R[i][c]);
+            y = fmaxf(y, R[i][c]);
+          }
+          a[2 * i + vg] = x;
+          b[2 * i + vg] = y;
+        }
+      const int io = (n & 7) >> 1, vo = n & 1;  // this lane's (token, group)
+      const float rfo = io == 0 ? rf[0] : io == 1 ? rf[1] : io == 2 ? rf[2] : rf[3];
+      const float mn = mul_rn(row_transpose8(a, n, [](float x, float y) { return fminf(x, y); }), rfo);
+      const float mx = mul_rn(row_transpose8(b, n, [](float x, float y) { return fmaxf(x, y); }), rfo);
+      const uint32_t sb = float_to_half_bits((mx - mn) / static_cast<float>(L));
+      const uint32_t zb = float_to_half_bits(mn);
+      const float sf = half_bits_to_float(sb), zf = half_bits_to_float(zb);
+      const float inv = sf > 0.f ? 1.0f / sf : 0.f;
+      float2* vf = &s.vfac[w][0];
+      if (n < 8) {
+        *reinterpret_cast<uint16_t*>(&s.page[Pg::kScale + 2 * (kBlockTokens * vo + tok(io))]) =
+            static_cast<uint16_t>(sb);
+        *reinterpret_cast<uint16_t*>(&s.page[Pg::kZero + 2 * (kBlockTokens * vo + tok(io))]) =
+            static_cast<uint16_t>(zb);
+        vf[8 * g + 2 * io + vo] = make_float2(rfo * inv, -zf * inv);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 x = *reinterpret_cast<const float4*>(&vf[8 * g + 2 * k]);
+        qw[k][0][0] = x.x;
+        qw[k][0][1] = x.y;
+        qw[k][1][0] = x.z;
+        qw[k][1][1] = x.w;
+      }
+    }
     if constexpr (NT == 16) {
       static_assert(NVG == 1, "one value group per token at 64 channels");
       float a[16], b[16];
@@ -526,6 +588,12 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
           for (int r = 0; r < 4; ++r) {
             qa[r] = qv[4 * mt + r][0];
             qb[r] = qv[4 * mt + r][1];
+          }
+        } else if constexpr (NT == 4 && NVG == 2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            qa[r] = qw[r][vg][0];
+            qb[r] = qw[r][vg][1];
           }
         } else {
 #pragma unroll
