@@ -1373,32 +1373,44 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
   float m_kg = 0.f, m_ks[KH], m_kz[KH], m_vg = 0.f;  // channel `lane`
   float2 m_kr, m_vr;                                 // tokens 2 lane, 2 lane + 1
   uint32_t m_vs = 0u, m_vz = 0u;                     // value scale / zero (fp16 pair) of those tokens
-  auto valid = [&](int i) {
-    const int pg = bt[i];
-    return pg >= 0 && pg < num_pages;
+  // The wave visits only its valid pages: a scalar search over the page ids passes over invalid ones
+  // and flags them, so the page loop has no per-page branch and the next page's loads land in the
+  // very registers of the current one.  Loads take the wave-uniform page base from scalar registers
+  // and an unsigned lane offset.
+  bool bad_page = false;
+  auto next_valid = [&](int i) {  // first index >= i in steps of kDecWaves with a valid page id, or >= cnt
+    for (; i < cnt; i += kDecWaves) {
+      const int pg = bt[i];
+      if (pg >= 0 && pg < num_pages) break;
+      bad_page = true;
+    }
+    return i;
   };
-  auto base_k = [&](int i) { return k_pool + (static_cast<size_t>(valid(i) ? bt[i] : 0) * hkv + kvh) * PK::kBytes; };
-  auto base_v = [&](int i) { return v_pool + (static_cast<size_t>(valid(i) ? bt[i] : 0) * hkv + kvh) * PV::kBytes; };
+  auto base_k = [&](int i) { return k_pool + (static_cast<size_t>(bt[i]) * hkv + kvh) * PK::kBytes; };
+  auto base_v = [&](int i) { return v_pool + (static_cast<size_t>(bt[i]) * hkv + kvh) * PV::kBytes; };
   auto load_meta = [&](int i) {
     const uint8_t* kp = base_k(i);
     const uint8_t* vp = base_v(i);
-    m_kg = reinterpret_cast<const float*>(kp + PK::kGamma)[lane];
-    m_vg = reinterpret_cast<const float*>(vp + PV::kGamma)[lane];
+    const uint32_t l2 = 2u * static_cast<uint32_t>(lane), l4 = 4u * static_cast<uint32_t>(lane);
+    const uint32_t l8 = 8u * static_cast<uint32_t>(lane);
+    m_kg = *reinterpret_cast<const float*>(kp + l4 + PK::kGamma);
+    m_vg = *reinterpret_cast<const float*>(vp + l4 + PV::kGamma);
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh) {
-      m_ks[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kScale)[D * kh + lane]);
-      m_kz[kh] = half_bits_to_float(reinterpret_cast<const uint16_t*>(kp + PK::kZero)[D * kh + lane]);
+      m_ks[kh] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(kp + l2 + (PK::kScale + 2 * D * kh)));
+      m_kz[kh] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(kp + l2 + (PK::kZero + 2 * D * kh)));
     }
-    m_kr = reinterpret_cast<const float2*>(kp + PK::kRho)[lane];
-    m_vr = reinterpret_cast<const float2*>(vp + PV::kRho)[lane];
-    m_vs = reinterpret_cast<const uint32_t*>(vp + PV::kScale)[lane];
-    m_vz = reinterpret_cast<const uint32_t*>(vp + PV::kZero)[lane];
+    m_kr = *reinterpret_cast<const float2*>(kp + l8 + PK::kRho);
+    m_vr = *reinterpret_cast<const float2*>(vp + l8 + PV::kRho);
+    m_vs = *reinterpret_cast<const uint32_t*>(vp + l4 + PV::kScale);
+    m_vz = *reinterpret_cast<const uint32_t*>(vp + l4 + PV::kZero);
   };
   auto load_k = [&](int i) {
     const uint8_t* kp = base_k(i);
+    const uint32_t off = static_cast<uint32_t>(n * KROW + g * (KROW / 4));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-      const uint8_t* src = kp + (16 * mt + n) * KROW + g * (KROW / 4);
+      const uint8_t* src = kp + off + 16 * mt * KROW;
       if constexpr (KWT == 2) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(src);
         kw[mt][0] = x[0];
@@ -1412,9 +1424,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
   };
   auto load_v = [&](int i) {
     const uint8_t* vp = base_v(i);
+    const uint32_t off = static_cast<uint32_t>(n * VROW + g * (VROW / 4));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const uint8_t* src = vp + (16 * mt + n) * VROW + g * (VROW / 4);
+      const uint8_t* src = vp + off + 16 * mt * VROW;
       if constexpr (VB == 2) {
         const u32x2 x = *reinterpret_cast<const u32x2*>(src);
         vw[mt][0] = x[0];
@@ -1431,28 +1444,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
   f32x4 oacc[4];                        // o~ of channels 16mt + 4g + r, head h
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) oacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool bad_page = false;
-  if (wu < cnt) {
-    load_meta(wu);
-    load_k(wu);
-    load_v(wu);
+  const int i0 = next_valid(wu);
+  if (i0 < cnt) {
+    load_meta(i0);
+    load_k(i0);
+    load_v(i0);
   }
   // key operand columns of heads >= G stay zero for the whole loop; the pages fill the others
   for (int e = lane; e < KH * 16 * (64 + 8); e += 64)
     if (((e / (64 + 8)) & 7) >= G) (&W.kcoef[0][0][0])[e] = static_cast<_Float16>(0.f);
-  for (int i = wu; i < cnt; i += kDecWaves) {
-    const bool more = i + kDecWaves < cnt;  // wave-uniform, like everything decided per page
-    const int nx = i + kDecWaves;
-    if (!valid(i)) {
-      // a page id outside [0, num_pages) names no block: skipped (its registers were filled from page 0)
-      bad_page = true;
-      if (more) {
-        load_meta(nx);
-        load_k(nx);
-        load_v(nx);
-      }
-      continue;
-    }
+  for (int i = i0; i < cnt;) {
+    const int nx = next_valid(i + kDecWaves);  // the wave's next valid page
+    const bool more = nx < cnt;                // wave-uniform, like everything decided per page
     // (1) page scales, coefficient operands, per-token and per-channel factors
     float b_h[KH];  // b sa (offsets removed) of head h, per token half
     {
@@ -1590,6 +1593,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
     if (more) load_v(nx);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    i = nx;
   }
   if (bad_page && lane == 0 && flags) atomicOr(flags, kFlagBadPage);
 
