@@ -58,12 +58,24 @@ __device__ __forceinline__ int chan_of(int n, int c) { return 32 * (c >> 1) + 2 
 // (lane n reads slots 8n .. 8n+7, slot 8n + c holding channel chan_of(n, c))
 __device__ __forceinline__ int chan_slot(int ch) { return 8 * ((ch >> 1) & 15) + 2 * (ch >> 5) + (ch & 1); }
 
-constexpr int kPartStride = 36;  // floats per row of the partial-sum array (16 slots x 2 + pad)
+// Partial sums, 16 slots of two floats per row (token or channel), kept as two half arrays: slots
+// 0-7 in half 0, 8-15 in half 1, rows kSlotStride floats apart, half 1 starting 32 floats further
+// (modulo the 64 four-byte LDS banks) than a whole number of bank rows after half 0.  Both access
+// patterns are then conflict-free: the reducers of 8 consecutive rows (one half each) read 16-byte
+// chunks that cover all 64 banks once (row starts 20 floats apart, the halves 32 apart), and the 16
+// lanes of a token-indexed write (one row, slots n) cover 32 banks, the rows 4 further the other 32.
+constexpr int kSlotStride = 20;
+constexpr int kHalfOffset = kBlockTokens * kSlotStride + 32;
+struct PartRows {
+  float f[kHalfOffset + kBlockTokens * kSlotStride];
+  __device__ float* slot(int row, int sl) { return f + (sl >> 3) * kHalfOffset + row * kSlotStride + 2 * (sl & 7); }
+  __device__ float* half(int row, int hf) { return f + hf * kHalfOffset + row * kSlotStride; }
+};
 
 // Slot of lane (w, g, n) in a channel's row of column partials.  The 16 lanes of a row write channels
-// 2n (+ 32k) apart, i.e. rows 72 floats apart, which would put lanes n and n + 4 on the same banks; the
-// XOR with n / 4 spreads them over every bank (for 32 and for 64 banks) and keeps each slot in its half
-// (slots 0-7: waves 0-1, 8-15: waves 2-3), which the group-size-64 reducers read separately.
+// 2n (+ 32k) apart, i.e. rows 40 floats apart (8 banks modulo 64), which would put lanes n and n + 8
+// on the same banks; the XOR with n / 4 moves them apart and keeps each slot in its half (slots 0-7:
+// waves 0-1, 8-15: waves 2-3), which the group-size-64 reducers read separately.
 __device__ __forceinline__ int col_slot(int w, int g, int n) { return (4 * w + g) ^ (n >> 2); }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -76,9 +88,9 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x, int ctrl_xor2) {
                    : static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), kDppXor1, 0xF, 0xF, true));
 }
 
-// Sum of the 8 (s1, s2) slot pairs of one row half, then with the partner thread (lane ^ 1).
-__device__ __forceinline__ float2 reduce_pairs(const float* row, int hf) {
-  const float4* p = reinterpret_cast<const float4*>(row + 16 * hf);
+// Sum of the 8 (s1, s2) slot pairs of one row half (hf), then with the partner thread (lane ^ 1).
+__device__ __forceinline__ float2 reduce_pairs(const float* half_row, int hf) {
+  const float4* p = reinterpret_cast<const float4*>(half_row);
   float a = p[0].x, b = p[0].y;
   a += p[0].z;
   b += p[0].w;
@@ -135,8 +147,8 @@ __device__ __forceinline__ uint32_t row_transpose(uint32_t v, int r) {
 // every wave.  Separate arrays let a wave run its next row pass while others still reduce a
 // column pass.
 struct QuantLds {
-  float part_row[kBlockTokens][kPartStride];  // per token: 16 partial pairs
-  float part[kHeadDim][kPartStride];          // per channel: 16 partial pairs
+  PartRows part_row;  // per token: 16 partial pairs
+  PartRows part;      // per channel (column passes, key min/max) or per token (value min/max)
   float rfl[kBlockTokens], rfl2[kBlockTokens];  // 2^-rho / sqrt(128) and its square, token order
   float cfl[kHeadDim], cfl2[kHeadDim];          // 2^-gamma and its square, chan_slot order
   float mul_a[2][kHeadDim], mul_b[2][kHeadDim];  // rounding FMA of each group (by half for group size 64)
@@ -212,11 +224,15 @@ __device__ __forceinline__ void rotate(const f16x8 (&xa)[2][4], const f16x8 (&hb
 
 // All tiles of one kind (keys or values) owned by this workgroup: tiles blockIdx.x,
 // blockIdx.x + gridDim.x, ...  The next tile's input is loaded while the current one is
-// normalised and packed.
+// normalised and packed.  One pipeline runs through both kinds: the key pass starts it, and its
+// last prefetches fetch the workgroup's first value tiles (from vin), so the value pass begins with
+// its first tile rotated (R, P, m1, m2) and its second in flight (xa).
 template <bool kIsV, int kBits, int kGroup>
-__device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, int hkv, int tiles,
-                                               const int32_t* __restrict__ dst_pages, uint8_t* __restrict__ pool,
-                                               int num_pages, uint32_t* __restrict__ flags, QuantLds& s) {
+__device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, const uint16_t* __restrict__ vin,
+                                               int hkv, int tiles, const int32_t* __restrict__ dst_pages,
+                                               uint8_t* __restrict__ pool, int num_pages,
+                                               uint32_t* __restrict__ flags, QuantLds& s, f16x8 (&xa)[2][4],
+                                               float (&R)[8][8], float (&P)[8][8], float (&m1)[2], float (&m2)[2]) {
   static_assert(kIsV ? (kBits == 2 || kBits == 4) : (kBits == 4 || kBits == 8), "code width");
   using Meta = MetaLayout<kGroup>;
   constexpr bool kHalf = kGroup == 64;  // two groups per channel (keys) or token (values)
@@ -247,15 +263,17 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
   }
   bool bad = false;
   const int stride = static_cast<int>(gridDim.x);
-  int tile = blockIdx.x;
+  const int first = static_cast<int>(blockIdx.x);
+  int tile = first;
   // software pipeline: the loop body packs tile `tile`, then rotates the next tile (whose input
-  // arrived meanwhile) and fetches the one after it; past the end, the last tile stands in
-  f16x8 xa[2][4];
-  float R[8][8], P[8][8];
-  float m1[2], m2[2];  // first row pass's moments of tokens 32w + 16 mt + n
-  load_tile(xa, in, tile, hkv, w, n, g);
-  rotate(xa, hb, hbn, R, P, m1, m2, g);
-  load_tile(xa, in, tile + stride < tiles ? tile + stride : tile, hkv, w, n, g);
+  // arrived meanwhile) and fetches the one after it; the workgroup's tiles run keys first, then
+  // values, and past the last value tile the last one stands in
+  if constexpr (!kIsV) {
+    load_tile(xa, in, tile, hkv, w, n, g);
+    rotate(xa, hb, hbn, R, P, m1, m2, g);
+    const bool more = tile + stride < tiles;
+    load_tile(xa, more ? in : vin, more ? tile + stride : first, hkv, w, n, g);
+  }
   for (; tile < tiles; tile += stride) {
     const int blk = tile / hkv;
     const int head = tile - blk * hkv;
@@ -286,7 +304,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         if (g == 0) {
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
-            *reinterpret_cast<float2*>(&s.part_row[32 * w + 16 * mt + n][0]) = make_float2(m1[mt], m2[mt]);
+            *reinterpret_cast<float2*>(s.part_row.slot(32 * w + 16 * mt + n, 0)) = make_float2(m1[mt], m2[mt]);
         }
       } else {
 #pragma unroll
@@ -297,13 +315,13 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
             s1 = fmaf(R[i][c], cf[c], s1);
             s2 = fmaf(P[i][c], c2[c], s2);
           }
-          *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(s1, s2);
+          *reinterpret_cast<float2*>(s.part_row.slot(tok_of(w, g, i), n)) = make_float2(s1, s2);
         }
       }
       wave_lds_sync();
       {
-        const float2 m = it == 0 ? *reinterpret_cast<const float2*>(&s.part_row[t_red][0])
-                                 : reduce_pairs(s.part_row[t_red], hf);
+        const float2 m = it == 0 ? *reinterpret_cast<const float2*>(s.part_row.slot(t_red, 0))
+                                 : reduce_pairs(s.part_row.half(t_red, hf), hf);
         const float mu = m.x * inv128, ey2 = m.y * inv128;
         float var = fmaf(-mu, mu, ey2);
         if (__builtin_amdgcn_ballot_w64(!(var >= 0.5f * ey2)) != 0) {
@@ -319,10 +337,10 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
               const float d = fmaf(R[i][c], cf[c], -mi);
               q = fmaf(d, d, q);
             }
-            *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(q, 0.f);
+            *reinterpret_cast<float2*>(s.part_row.slot(tok_of(w, g, i), n)) = make_float2(q, 0.f);
           }
           wave_lds_sync();
-          var = reduce_pairs(s.part_row[t_red], hf).x * inv128;
+          var = reduce_pairs(s.part_row.half(t_red, hf), hf).x * inv128;
         }
         rho_t += 0.5f * lg2(fmaf(var, rf_t * rf_t, kNormEps));
         rf_t = ex2(-rho_t) * kInvSqrt128;
@@ -349,12 +367,12 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
             s1 = fmaf(R[i][c], rf[i], s1);
             s2 = fmaf(P[i][c], r2[i], s2);
           }
-          *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(s1, s2);
+          *reinterpret_cast<float2*>(s.part.slot(chan_of(n, c), col_slot(w, g, n))) = make_float2(s1, s2);
         }
       }
       __syncthreads();
       {
-        const float2 m = reduce_pairs(s.part[t_red], hf);
+        const float2 m = reduce_pairs(s.part.half(t_red, hf), hf);
         const float mu = m.x * inv128, ey2 = m.y * inv128;
         const float var = fmaf(-mu, mu, ey2);
         const float gam_new = gam_c + 0.5f * lg2(fmaf(var, cf_c * cf_c, kNormEps));
@@ -380,10 +398,10 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
               const float d = fmaf(R[i][c], rf[i], -mc[c]);
               q = fmaf(d, d, q);
             }
-            *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(q, 0.f);
+            *reinterpret_cast<float2*>(s.part.slot(chan_of(n, c), col_slot(w, g, n))) = make_float2(q, 0.f);
           }
           __syncthreads();
-          const float cvar = reduce_pairs(s.part[t_red], hf).x * inv128;
+          const float cvar = reduce_pairs(s.part.half(t_red, hf), hf).x * inv128;
           gam_c += 0.5f * lg2(fmaf(cvar, cf_c * cf_c, kNormEps));
           cf_c = ex2(-gam_c);
           (hf ? s.cfl2 : s.cfl)[chan_slot(t_red)] = hf ? cf_c * cf_c : cf_c;
@@ -428,11 +446,11 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
           a = fminf(a, R[i][c]);
           b = fmaxf(b, R[i][c]);
         }
-        *reinterpret_cast<float2*>(&s.part[chan_of(n, c)][2 * col_slot(w, g, n)]) = make_float2(a, b);
+        *reinterpret_cast<float2*>(s.part.slot(chan_of(n, c), col_slot(w, g, n))) = make_float2(a, b);
       }
       __syncthreads();
       {
-        const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
+        const float4* p = reinterpret_cast<const float4*>(s.part.half(t_red, hf));
         float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -540,15 +558,15 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
             b1 = fmaxf(b1, R[i][c]);
           }
           // channel half 0 in the channel array, half 1 in the (now idle) row array
-          *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
-          *reinterpret_cast<float2*>(&s.part_row[tok_of(w, g, i)][2 * n]) = make_float2(a1, b1);
+          *reinterpret_cast<float2*>(s.part.slot(tok_of(w, g, i), n)) = make_float2(a, b);
+          *reinterpret_cast<float2*>(s.part_row.slot(tok_of(w, g, i), n)) = make_float2(a1, b1);
         } else {
 #pragma unroll
           for (int c = 4; c < 8; ++c) {
             a = fminf(a, R[i][c]);
             b = fmaxf(b, R[i][c]);
           }
-          *reinterpret_cast<float2*>(&s.part[tok_of(w, g, i)][2 * n]) = make_float2(a, b);
+          *reinterpret_cast<float2*>(s.part.slot(tok_of(w, g, i), n)) = make_float2(a, b);
         }
       }
       __syncthreads();
@@ -556,15 +574,17 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         float mn = INFINITY, mx = -INFINITY;
         if constexpr (kHalf) {
           // thread hf of the pair reduces channel half hf of token t_red: all 16 lanes' partials
-          const float4* p = reinterpret_cast<const float4*>(hf ? s.part_row[t_red] : s.part[t_red]);
+          PartRows& pr = hf ? s.part_row : s.part;
+          const float4* p0 = reinterpret_cast<const float4*>(pr.half(t_red, 0));
+          const float4* p1 = reinterpret_cast<const float4*>(pr.half(t_red, 1));
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const float4 v = p[k];
+            const float4 v = k < 4 ? p0[k] : p1[k - 4];
             mn = fminf(mn, fminf(v.x, v.z));
             mx = fmaxf(mx, fmaxf(v.y, v.w));
           }
         } else {
-          const float4* p = reinterpret_cast<const float4*>(s.part[t_red] + 16 * hf);
+          const float4* p = reinterpret_cast<const float4*>(s.part.half(t_red, hf));
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const float4 v = p[k];
@@ -653,10 +673,18 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
         }
       }
     }
-    {
-      const int next = tile + stride < tiles ? tile + stride : tile;
+    const int next = tile + stride;
+    if constexpr (!kIsV) {
+      // xa holds key tile `next`, or the first value tile once the keys are done
       rotate(xa, hb, hbn, R, P, m1, m2, g);
-      load_tile(xa, in, next + stride < tiles ? next + stride : next, hkv, w, n, g);
+      const bool more = next + stride < tiles;
+      const int vt = next < tiles ? first : (first + stride < tiles ? first + stride : first);
+      load_tile(xa, more ? in : vin, more ? next + stride : vt, hkv, w, n, g);
+    } else {
+      // past the last value tile the last one stands in (a uniform branch here measured slower)
+      const int nt = next < tiles ? next : tile;
+      rotate(xa, hb, hbn, R, P, m1, m2, g);
+      load_tile(xa, in, nt + stride < tiles ? nt + stride : nt, hkv, w, n, g);
     }
   }
   if (bad && tid == 0 && flags) atomicOr(flags, kFlagBadPage);
@@ -666,7 +694,8 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 
 // Persistent quantiser: every workgroup walks the key tiles blockIdx.x, blockIdx.x + gridDim.x, ...
 // and then the value tiles with the same stride, so all workgroups carry the same mix of the two
-// kinds (a value tile costs more than a key tile).
+// kinds (a value tile costs more than a key tile).  The input pipeline (xa: the tile in flight;
+// R, P, m1, m2: the rotated one) runs on from the keys into the values without a second fill.
 template <int kKBits, int kVBits, int kGroup>
 __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __restrict__ kin,
                                                          const uint16_t* __restrict__ vin, int hkv, int tiles,
@@ -674,8 +703,13 @@ __global__ __launch_bounds__(256, 2) void quantize_kernel(const uint16_t* __rest
                                                          uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
                                                          int num_pages, uint32_t* __restrict__ flags) {
   __shared__ __align__(16) QuantLds lds;
-  quantize_tiles<false, kKBits, kGroup>(kin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds);
-  quantize_tiles<true, kVBits, kGroup>(vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds);
+  f16x8 xa[2][4];         // input in flight
+  float R[8][8], P[8][8];  // rotated tile and its squares
+  float m1[2], m2[2];      // first row pass's moments of tokens 32w + 16 mt + n
+  quantize_tiles<false, kKBits, kGroup>(kin, vin, hkv, tiles, dst_pages, k_pool, num_pages, flags, lds, xa, R, P,
+                                        m1, m2);
+  quantize_tiles<true, kVBits, kGroup>(vin, vin, hkv, tiles, dst_pages, v_pool, num_pages, flags, lds, xa, R, P,
+                                       m1, m2);
 }
 
 // Test / inspection export: rebuild fp32 K^ or V^ of one tile in the original basis.
