@@ -38,10 +38,10 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("2d0d97d1e559f552", 663243243),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("2d0d97d1e559f552", 332362674),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397643),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 128998432),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("881c2b1f1d6df233", 663125419),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("881c2b1f1d6df233", 331839649),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397593),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 128998400),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
 # helpers and the host plan that picks its launch shape and instance
@@ -49,8 +49,8 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
                  "decode_kernel": ("kvarn_decode.hip", "kvarn_codes.h", "kvarn_host.h")}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("2d0d97d1e559f552", 116736000),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("2d0d97d1e559f552", 59443686),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("881c2b1f1d6df233", 116273152),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("881c2b1f1d6df233", 59079142),
     ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 5967170),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 9927360),
 }
