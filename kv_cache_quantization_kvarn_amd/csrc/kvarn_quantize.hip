@@ -43,7 +43,7 @@
 //
 // Scheduling.  Workgroups are persistent, two per compute unit; each walks its share of the key
 // tiles and then of the value tiles with a fixed stride.  The input of the next tile is fetched while the current
-// one is normalised; the page stores go through a buffer resource (size zero for an invalid page)
+// one is normalised, across the switch from keys to values too; the page stores go through a buffer resource (size zero for an invalid page)
 // so that every tile issues the same memory operations and the wait for the prefetched input
 // never has to drain the stores.
 #include "kvarn_common.h"
