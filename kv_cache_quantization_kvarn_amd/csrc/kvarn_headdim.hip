@@ -68,6 +68,31 @@ struct HdPage {
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sign patterns of the exact +-1 H32 operand of the rotation (Sylvester: entry (k, o) is
+// (-1)^popcount(k & o)).  A lane's 8-long k-chunk k = 8g + i (i = 0..7) of output column o has
+// signs (-1)^(popcount(i & (o & 7)) + popcount(g & (o >> 3))), since the two index parts share no
+// bits.  Entry o7 + 8p holds the chunk for o & 7 = o7 and second parity p as four fp16 pairs
+// (element i in half i % 2 of word i / 2); entry ^ 8 is its negation.
+struct H32Signs {
+  uint32_t w[16][4];
+};
+constexpr H32Signs make_h32_signs() {
+  H32Signs t{};
+  for (int e = 0; e < 16; ++e)
+    for (int k = 0; k < 4; ++k) {
+      uint32_t word = 0;
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * k + h;
+        int par = e >> 3;
+        for (int b = 0; b < 3; ++b) par ^= ((i & e) >> b) & 1;
+        word |= (0x3C00u | (par ? 0x8000u : 0u)) << (16 * h);
+      }
+      t.w[e][k] = word;
+    }
+  return t;
+}
+__constant__ const H32Signs kH32Signs = make_h32_signs();
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Rounded product the compiler may not fuse into a later add (a constant group must get range 0).
@@ -203,15 +228,17 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
       xa[mt][gi] = *reinterpret_cast<const f16x8*>(src + static_cast<size_t>(w * TW + 16 * mt + n) * tstride +
                                                     32 * gi + 8 * g);
   // H32 block: B[k][col] = (-1)^popcount(k & o), input index k = 8g + i, output o = 2n + hh
+  // (hbn = -hb), from the sign table
   f16x8 hb[2], hbn[2];
+  {
+    const int par = __popc(g & (n >> 2)) & 1;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool neg = __popc((8 * g + i) & (2 * n + hh)) & 1;
-      hb[hh][i] = neg ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
-      hbn[hh][i] = neg ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+    for (int hh = 0; hh < 2; ++hh) {
+      const int e = ((2 * n + hh) & 7) + 8 * par;
+      hb[hh] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(kH32Signs.w[e]));
+      hbn[hh] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(kH32Signs.w[e ^ 8]));
     }
+  }
   // ---- rotation R' = sqrt(D) R: output chunk ho = sum_gi H_{D/32}[gi][ho] (X_gi H32) ---------
   float R[NT][NC];
 #pragma unroll
