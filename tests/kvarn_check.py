@@ -18,7 +18,7 @@ import numpy as np
 from oracle import kvarn_oracle as o
 
 CODE_MISMATCH_FRACTION = 1e-4
-NORM_TOL = 1e-5  # the survey's bar; the kernels measure <= 5.1e-7
+NORM_TOL = 1e-5  # relative bar for rho and gamma; the kernels measure <= 5.1e-7
 DEQUANT_TOL = 2e-3
 ATTN_TOL = 2e-3
 
