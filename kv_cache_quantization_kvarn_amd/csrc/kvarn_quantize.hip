@@ -107,6 +107,30 @@ __device__ __forceinline__ float2 reduce_pairs(const float* half_row, int hf) {
   return hf ? make_float2(a2 + a, b2 + b) : make_float2(a + a2, b + b2);
 }
 
+// Minimum and maximum of partials read back from LDS (or across lanes), as the instructions
+// themselves: the compiler would otherwise quiet every operand first, since it cannot tell that
+// a value loaded from memory is not a signalling NaN (these are all results of arithmetic).
+__device__ __forceinline__ float min3_raw(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float min_raw(float a, float b) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Orders LDS accesses between lanes of one wave (LDS operations of a wave complete in order).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -287,14 +311,10 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // rf = 2^-rho / sqrt(128) multiplies the unnormalised R' (so R' rf = R 2^-rho).
     float rho_t = 0.f, rf_t = kInvSqrt128;  // normaliser of row t_red
     float gam_c = 0.f, cf_c = 1.f;          // normaliser of column c_red (= t_red)
-    float rf[8], cf[8], r2[8], c2[8];  // normalisers of the lane's tokens / channels, and squares
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      rf[k] = kInvSqrt128;
-      cf[k] = 1.f;
-      r2[k] = kInvSqrt128 * kInvSqrt128;
-      c2[k] = 1.f;
-    }
+    // normalisers of the lane's tokens / channels, and squares: every pass reads them from LDS
+    // before use (the first row pass, from the input, needs none; its centred fallback takes the
+    // column normalisers as 1)
+    float rf[8], cf[8], r2[8], c2[8];
     for (int it = 0; it < kNormIters; ++it) {
       // ---------------- row pass: moments over channels of R' * cf ------------
       // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
@@ -334,7 +354,7 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
             float q = 0.f;
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-              const float d = fmaf(R[i][c], cf[c], -mi);
+              const float d = fmaf(R[i][c], it == 0 ? 1.f : cf[c], -mi);
               q = fmaf(d, d, q);
             }
             *reinterpret_cast<float2*>(s.part_row.slot(tok_of(w, g, i), n)) = make_float2(q, 0.f);
@@ -455,14 +475,14 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const float4 v = p[k];
-          mn = fminf(mn, fminf(v.x, v.z));
-          mx = fmaxf(mx, fmaxf(v.y, v.w));
+          mn = min3_raw(mn, v.x, v.z);
+          mx = max3_raw(mx, v.y, v.w);
         }
         // thread hf of the pair holds the partials of token half hf (waves 2hf, 2hf + 1): one group of
         // each half for group size 64, merged into the channel's one group otherwise
         if constexpr (!kHalf) {
-          mn = fminf(mn, dpp_xor1(mn));
-          mx = fmaxf(mx, dpp_xor1(mx));
+          mn = min_raw(mn, dpp_xor1(mn));
+          mx = max_raw(mx, dpp_xor1(mx));
         }
         mn = mul_rn(mn, cf_c);
         mx = mul_rn(mx, cf_c);
@@ -580,19 +600,19 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const float4 v = k < 4 ? p0[k] : p1[k - 4];
-            mn = fminf(mn, fminf(v.x, v.z));
-            mx = fmaxf(mx, fmaxf(v.y, v.w));
+            mn = min3_raw(mn, v.x, v.z);
+            mx = max3_raw(mx, v.y, v.w);
           }
         } else {
           const float4* p = reinterpret_cast<const float4*>(s.part.half(t_red, hf));
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const float4 v = p[k];
-            mn = fminf(mn, fminf(v.x, v.z));
-            mx = fmaxf(mx, fmaxf(v.y, v.w));
+            mn = min3_raw(mn, v.x, v.z);
+            mx = max3_raw(mx, v.y, v.w);
           }
-          mn = fminf(mn, dpp_xor1(mn));
-          mx = fmaxf(mx, dpp_xor1(mx));
+          mn = min_raw(mn, dpp_xor1(mn));
+          mx = max_raw(mx, dpp_xor1(mx));
         }
         mn = mul_rn(mn, rf_t);
         mx = mul_rn(mx, rf_t);
