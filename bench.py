@@ -38,9 +38,9 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("881c2b1f1d6df233", 663125419),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("881c2b1f1d6df233", 331839649),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397593),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 663109696),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 331831686),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397587),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 128998400),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
@@ -49,8 +49,8 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
                  "decode_kernel": ("kvarn_decode.hip", "kvarn_codes.h", "kvarn_host.h")}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("881c2b1f1d6df233", 116273152),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("881c2b1f1d6df233", 59079142),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 113885184),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 57931483),
     ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 5967170),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 9927360),
 }
