@@ -88,6 +88,17 @@ __device__ __forceinline__ uint32_t dpp_u32_xor8(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), kDppXor8, 0xF, 0xF, true));
 }
 
+// One bank-masked row_ror:8 move each: lanes 8-15 of every 16-lane row take `src` of lane l ^ 8 and
+// lanes 0-7 keep `keep` (take_xor8_hi), or lanes 0-7 take it and lanes 8-15 keep (take_xor8_lo).
+__device__ __forceinline__ uint32_t take_xor8_hi(uint32_t keep, uint32_t src) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(keep), static_cast<int>(src), kDppXor8, 0xF, 0xC, false));
+}
+__device__ __forceinline__ uint32_t take_xor8_lo(uint32_t keep, uint32_t src) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(keep), static_cast<int>(src), kDppXor8, 0xF, 0x3, false));
+}
+
 // x from lane l^16 and l^32 (v_permlane16_swap / v_permlane32_swap on two copies of x).  The
 // pair (self, partner) is returned in lane order, so both lanes of a pair combine the same two
 // values in the same order and get identical bits.
@@ -593,17 +604,13 @@ __device__ __forceinline__ void process_page(PageRegs<KB, VB, GS>& P, WaveState&
     f16x8 wb[2][2];  // [u][hf]
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      u32x4 mine, other;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        mine[j] = sel_lo_u32(own_hi[hf][j], own_lo[hf][j]);
-        other[j] = dpp_u32_xor8(sel_lo_u32(own_lo[hf][j], own_hi[hf][j]));
-      }
+      // u0: the tokens of lanes 0-7, hi parts in columns 0-7 and lo parts (from lane n ^ 8) in 8-15;
+      // u1: the tokens of lanes 8-15, hi parts (from lane n ^ 8) in 0-7 and lo parts in 8-15
       u32x4 u0, u1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        u0[j] = sel_lo_u32(mine[j], other[j]);
-        u1[j] = sel_lo_u32(other[j], mine[j]);
+        u0[j] = take_xor8_hi(own_hi[hf][j], own_lo[hf][j]);
+        u1[j] = take_xor8_lo(own_lo[hf][j], own_hi[hf][j]);
       }
       wb[0][hf] = __builtin_bit_cast(f16x8, u0);
       wb[1][hf] = __builtin_bit_cast(f16x8, u1);
