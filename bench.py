@@ -38,10 +38,10 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 663109696),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 331831686),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 67397587),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 128998400),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 663109547),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 331824679),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("f710cd0b8e1bd9f5", 67394593),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("f710cd0b8e1bd9f5", 128996416),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
 # helpers and the host plan that picks its launch shape and instance
@@ -51,8 +51,8 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
 MEASURED_VALU = {
     ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 113885184),
     ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 57931483),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("e2a0df74244bfff0", 5967170),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("e2a0df74244bfff0", 9927360),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("f710cd0b8e1bd9f5", 5836098),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("f710cd0b8e1bd9f5", 9665216),
 }
 # Issue rate of non-packed fp32 VALU lane operations: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
 VALU_PEAK_TLANEOPS = 256 * 4 * 16 * 2.4e9 / 1e12
