@@ -1532,13 +1532,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    // (2) scores of tokens 16mt + 4g + r for head h (hi and lo columns summed)
+    // (2) scores of tokens 16mt + 4g + r for head h (hi and lo columns summed; b enters the hi
+    // column's accumulator)
     float sc[8][4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const int kh = (16 * mt) / GS;
       const _Float16* cb = &W.kcoef[kh][n][16 * g];
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      const float bi = n < 8 ? b_h[kh] : 0.f;
+      f32x4 d = {bi, bi, bi, bi};
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         f16x8 aop;
@@ -1552,7 +1554,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
       const float4 kr = *reinterpret_cast<const float4*>(&W.krho[16 * mt + 4 * g]);
       const float krv[4] = {kr.x, kr.y, kr.z, kr.w};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[mt][r] = (d[r] + dpp<kDppXor8>(d[r]) + b_h[kh]) * krv[r];
+      for (int r = 0; r < 4; ++r) sc[mt][r] = (d[r] + dpp<kDppXor8>(d[r])) * krv[r];
     }
     if (more) load_k(nx);
     // (3) online softmax of head h over the page's 128 tokens, and the value operands
@@ -1566,7 +1568,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
       pm = rows_max(pm);
       const float mnew = fmaxf(m_run, pm);
       const float al = m_run == -INFINITY ? 0.f : ex2(m_run - mnew);
-      float lp = 0.f, up = 0.f;
+      // the value offsets of exactly the fp16 weights used: sum over tokens of off_t (hi + lo), one
+      // v_dot2 of the packed pair per token (t has the parity of r)
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 off_even = {static_cast<_Float16>(value_offset<VB>(0)), static_cast<_Float16>(value_offset<VB>(0))};
+      const h2 off_odd = {static_cast<_Float16>(value_offset<VB>(1)), static_cast<_Float16>(value_offset<VB>(1))};
+      float lp = 0.f, up = 0.f, uo = 0.f;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const float4 vs4 = *reinterpret_cast<const float4*>(&W.vsr[16 * mt + 4 * g]);
@@ -1580,11 +1587,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
           _Float16 hi, lo;
           split_hl(e * vsv[r], hi, lo);
           W.vcoef[n][value_slot(t)] = n < 8 ? hi : lo;  // this lane's column: hi for n < 8, lo for n >= 8
-          up = fmaf(e, vzv[r], up) - value_offset<VB>(t) * (static_cast<float>(hi) + static_cast<float>(lo));
+          up = fmaf(e, vzv[r], up);
+          const h2 hl = {hi, lo};
+          uo = __builtin_amdgcn_fdot2(hl, (r & 1) ? off_odd : off_even, uo, false);
         }
       }
       lp = rows_sum(lp);
-      u_h = rows_sum(up);
+      u_h = rows_sum(up - uo);
       l_run = fmaf(al, l_run, lp);
       m_run = mnew;
 #pragma unroll
@@ -1594,12 +1603,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    // (4) values: o~_j += 2^gamma_j (sum_t w_t c_tj + u), channels 16mt + 4g + r
+    // (4) values: o~_j += 2^gamma_j (sum_t w_t c_tj + u), channels 16mt + 4g + r (u enters the hi
+    // column's accumulator)
     {
+      const float ui = n < 8 ? u_h : 0.f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const _Float16* wb = &W.vcoef[n][32 * g];
-        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+        f32x4 d = {ui, ui, ui, ui};
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
           f16x8 c0, c1;
@@ -1614,7 +1625,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_hd64_kernel(
         const float4 gs4 = *reinterpret_cast<const float4*>(&W.gsv[16 * mt + 4 * g]);
         const float gsv[4] = {gs4.x, gs4.y, gs4.z, gs4.w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[mt][r] = fmaf(gsv[r], d[r] + dpp<kDppXor8>(d[r]) + u_h, oacc[mt][r]);
+        for (int r = 0; r < 4; ++r) oacc[mt][r] = fmaf(gsv[r], d[r] + dpp<kDppXor8>(d[r]), oacc[mt][r]);
       }
     }
     if (more) load_v(nx);
