@@ -254,6 +254,30 @@ def test_degenerate_tiles(K, cfg):
                      [(b, h) for b in range(4) for h in range(2)])
 
 
+def test_mean_dominated_rows_and_columns(K, cfg):
+    """Blocks whose rows or columns have a mean far above their spread, so that the one-sweep
+    variance would cancel and the kernel's centred fallback passes run: a dominant input channel 0
+    (every rotated row has mean x_t0 against a spread of the other channels), a common offset on
+    every token (every rotated column has a large mean over the tokens), and both together."""
+    say("case: mean-dominated rows (dominant channel 0) and columns (common token offset)")
+    g = torch.Generator().manual_seed(4242)
+    hkv = 2
+    base = torch.randn(128, hkv, 128, generator=g)
+    rows = base.clone()
+    rows[:, :, 0] += 20.0
+    offset = torch.randn(1, hkv, 128, generator=g) * 8.0
+    cols = base + offset
+    both = cols.clone()
+    both[:, :, 0] += 30.0
+    k = torch.cat([rows, cols, both]).half()
+    v = torch.cat([cols, both, rows]).half()
+    pages = torch.arange(3, dtype=torch.int32)
+    kp, vp, fl = gpu_quantize(K, cfg, k.cuda(), v.cuda(), pages, 3)
+    assert fl == 0
+    compare_quantize(k.numpy(), v.numpy(), kp.cpu().numpy(), vp.cpu().numpy(), pages.numpy(),
+                     [(b, h) for b in range(3) for h in range(hkv)])
+
+
 def test_decode_over_zero_scale_pages(K, cfg):
     """Pages whose every key scale or every value scale is zero still carry the zero point:
     keys constant in time (each key group is one channel over the block, so min = max), and
