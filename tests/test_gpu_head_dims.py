@@ -87,6 +87,42 @@ def test_quantize_every_tile_and_every_byte(K, d, name):
 
 
 @pytest.mark.parametrize("d", DIMS)
+def test_quantize_mean_dominated(K, d):
+    """Rows and columns whose mean is far above their spread: a dominant input channel 0 (every
+    rotated row's mean is x_t0, so the first row pass's input moments fail their guard and the
+    pass runs centred) and a common token offset (every rotated column has a large mean)."""
+    name = "kvarn_k4v2_g128"
+    cfg = K.kvarn_config_parse(name, d)
+    say("case: mean-dominated rows and columns at head_dim %d" % d)
+    g = torch.Generator().manual_seed(4343 + d)
+    hkv = 2
+    base = torch.randn(128, hkv, d, generator=g)
+    rows = base.clone()
+    rows[:, :, 0] += 20.0
+    cols = base + torch.randn(1, hkv, d, generator=g) * 8.0
+    both = cols.clone()
+    both[:, :, 0] += 30.0
+    k = torch.cat([rows, cols, both]).half().cuda()
+    v = torch.cat([cols, both, rows]).half().cuda()
+    pages = torch.arange(3, dtype=torch.int32)
+    a = quantize(K, cfg, k, v, pages, 3)
+    assert a[2] == 0
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    kph, vph = a[0].cpu().numpy(), a[1].cpu().numpy()
+    kb, vb, group = bits_of(cfg)
+    stats = chk.TileStats()
+    for blk in range(3):
+        for h in range(hkv):
+            for is_v, x, pool, bits in ((False, kh, kph, kb), (True, vh, vph, vb)):
+                tile = x[128 * blk:128 * blk + 128, h]
+                ref = np.frombuffer(o.encode_page(o.quantize_tile(tile, is_v, bits=bits, group=group), is_v, bits),
+                                    np.uint8)
+                chk.compare_pools(stats, pool[blk, h][None], ref[None], is_v, bits, group, d)
+    say("  " + stats.summary())
+    stats.check()
+
+
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v4_g64"])
 def test_dequantize_same_bytes(K, d, name):
     cfg = K.kvarn_config_parse(name, d)
