@@ -278,6 +278,44 @@ def test_mean_dominated_rows_and_columns(K, cfg):
                      [(b, h) for b in range(3) for h in range(hkv)])
 
 
+def test_extreme_magnitudes(K, cfg):
+    """fp16 inputs at the ends of the format: every value +-65504 (rotated sums near 2^23 and
+    squares near 2^46 in fp32), every value a subnormal (+-2^-24 .. 2^-15), and tokens of the two
+    magnitudes mixed in one block."""
+    say("case: fp16 max-magnitude block, subnormal block, mixed block")
+    g = torch.Generator().manual_seed(6550)
+    hkv = 2
+    sign = torch.randint(0, 2, (128, hkv, 128), generator=g).float() * 2 - 1
+    big = sign * 65504.0
+    tiny = torch.randint(-1023, 1024, (128, hkv, 128), generator=g).float() * 2.0 ** -24  # subnormal grid
+    mixed = torch.where(torch.arange(128).view(128, 1, 1) % 3 == 0, big * torch.rand(128, hkv, 128, generator=g),
+                        tiny)
+    k = torch.cat([big, tiny, mixed]).half()
+    v = torch.cat([tiny, mixed, big]).half()
+    assert torch.isfinite(k.float()).all() and torch.isfinite(v.float()).all()
+    pages = torch.arange(3, dtype=torch.int32)
+    kp, vp, fl = gpu_quantize(K, cfg, k.cuda(), v.cuda(), pages, 3)
+    assert fl == 0
+    compare_quantize(k.numpy(), v.numpy(), kp.cpu().numpy(), vp.cpu().numpy(), pages.numpy(),
+                     [(b, h) for b in range(3) for h in range(hkv)])
+    # decode over those pages, alone and together (explicit small scale: the max-magnitude keys
+    # would otherwise put every softmax weight on one token)
+    q = torch.randn(4, 8, 128, generator=g).half().cuda()
+    bt = torch.tensor([[0, -1, -1], [1, -1, -1], [2, -1, -1], [0, 1, 2]], dtype=torch.int32)
+    sl = torch.tensor([128, 128, 128, 384], dtype=torch.int32)
+    out, fl = gpu_decode(K, cfg, q, kp, vp, bt, sl, hkv, scale=1e-6)
+    assert fl == 0
+    # outputs reach ~6e4 here, so the fixed 2e-3 bar is applied relative to each row's magnitude
+    ref = o.decode(q.cpu().numpy(), kp.cpu().numpy(), vp.cpu().numpy(), bt.numpy(), sl.numpy(), hkv, 1e-6)
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in range(4):
+        for h in range(8):
+            worst = max(worst, float(np.abs(got[b, h] - ref[b, h]).max()) / max(1.0, float(np.abs(ref[b, h]).max())))
+    say("  decode max-abs diff / max(1, row magnitude): %.3e" % worst)
+    assert worst <= chk.ATTN_TOL
+
+
 def test_decode_over_zero_scale_pages(K, cfg):
     """Pages whose every key scale or every value scale is zero still carry the zero point:
     keys constant in time (each key group is one channel over the block, so min = max), and
