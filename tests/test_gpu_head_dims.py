@@ -123,6 +123,37 @@ def test_quantize_mean_dominated(K, d):
 
 
 @pytest.mark.parametrize("d", DIMS)
+def test_quantize_fp16_extremes(K, d):
+    """Blocks at the ends of fp16: every value +-65504, every value subnormal, the two mixed."""
+    name = "kvarn_k4v2_g128"
+    cfg = K.kvarn_config_parse(name, d)
+    say("case: fp16 max-magnitude, subnormal and mixed blocks at head_dim %d" % d)
+    g = torch.Generator().manual_seed(6551 + d)
+    hkv = 2
+    big = (torch.randint(0, 2, (128, hkv, d), generator=g).float() * 2 - 1) * 65504.0
+    tiny = torch.randint(-1023, 1024, (128, hkv, d), generator=g).float() * 2.0 ** -24
+    mixed = torch.where(torch.arange(128).view(128, 1, 1) % 3 == 0, big * torch.rand(128, hkv, d, generator=g), tiny)
+    k = torch.cat([big, tiny, mixed]).half().cuda()
+    v = torch.cat([tiny, mixed, big]).half().cuda()
+    pages = torch.arange(3, dtype=torch.int32)
+    a = quantize(K, cfg, k, v, pages, 3)
+    assert a[2] == 0
+    kh, vh = k.cpu().numpy(), v.cpu().numpy()
+    kph, vph = a[0].cpu().numpy(), a[1].cpu().numpy()
+    kb, vb, group = bits_of(cfg)
+    stats = chk.TileStats()
+    for blk in range(3):
+        for h in range(hkv):
+            for is_v, x, pool, bits in ((False, kh, kph, kb), (True, vh, vph, vb)):
+                tile = x[128 * blk:128 * blk + 128, h]
+                ref = np.frombuffer(o.encode_page(o.quantize_tile(tile, is_v, bits=bits, group=group), is_v, bits),
+                                    np.uint8)
+                chk.compare_pools(stats, pool[blk, h][None], ref[None], is_v, bits, group, d)
+    say("  " + stats.summary())
+    stats.check()
+
+
+@pytest.mark.parametrize("d", DIMS)
 @pytest.mark.parametrize("name", ["kvarn_k4v2_g128", "kvarn_k8v4_g64"])
 def test_dequantize_same_bytes(K, d, name):
     cfg = K.kvarn_config_parse(name, d)
