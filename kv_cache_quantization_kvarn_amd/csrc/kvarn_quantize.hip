@@ -315,6 +315,9 @@ __device__ __forceinline__ void quantize_tiles(const uint16_t* __restrict__ in, 
     // before use (the first row pass, from the input, needs none; its centred fallback takes the
     // column normalisers as 1)
     float rf[8], cf[8], r2[8], c2[8];
+    // unrolled: the first pass's special cases resolve at compile time and the scheduler can
+    // overlap each pass's tail with the next one's start (3.5% on the headline layer)
+#pragma unroll
     for (int it = 0; it < kNormIters; ++it) {
       // ---------------- row pass: moments over channels of R' * cf ------------
       // Wave-local: the tokens of wave w are reduced by threads of wave w, so LDS order within
