@@ -38,10 +38,10 @@ METRIC = "quantize GB/s + packed decode-attn GB/s & tok/s, % of MI355X HBM peak"
 # kernel source it was measured on; once the source changes the figure no longer applies and is reported
 # as null.
 MEASURED_TRAFFIC = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 663109547),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 331824679),
-    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("f710cd0b8e1bd9f5", 67394593),
-    ("decode_kernel", "llama3_8b_layer_16x8192"): ("f710cd0b8e1bd9f5", 128996416),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9fdbec7513ad9de4", 663418347),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("9fdbec7513ad9de4", 332141624),
+    ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("f710cd0b8e1bd9f5", 67394583),
+    ("decode_kernel", "llama3_8b_layer_16x8192"): ("f710cd0b8e1bd9f5", 128996384),
 }
 # the sources each kernel's measurements depend on: its own file, and for the decode the code conversion
 # helpers and the host plan that picks its launch shape and instance
@@ -49,8 +49,8 @@ KERNEL_SOURCE = {"quantize_kernel": ("kvarn_quantize.hip",),
                  "decode_kernel": ("kvarn_decode.hip", "kvarn_codes.h", "kvarn_host.h")}
 # VALU instructions per launch (rocprofv3 SQ_INSTS_VALU, wave64), keyed like MEASURED_TRAFFIC.
 MEASURED_VALU = {
-    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("6a4eabf971d70ba2", 113885184),
-    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("6a4eabf971d70ba2", 57931483),
+    ("quantize_kernel", "llama3_8b_layer_16x8192"): ("9fdbec7513ad9de4", 111398912),
+    ("quantize_kernel", "qwen25_1p5b_28layer_64x4096"): ("9fdbec7513ad9de4", 56650476),
     ("decode_kernel", "qwen25_1p5b_28layer_64x4096"): ("f710cd0b8e1bd9f5", 5836098),
     ("decode_kernel", "llama3_8b_layer_16x8192"): ("f710cd0b8e1bd9f5", 9665216),
 }
