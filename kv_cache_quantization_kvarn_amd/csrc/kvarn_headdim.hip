@@ -287,6 +287,7 @@ __device__ __forceinline__ void quantize_hd_tile(const uint16_t* __restrict__ in
 #pragma unroll
   for (int c = 0; c < NC; ++c) cf[c] = 1.f;
   float gam_red = 0.f, cf_red = 1.f;  // gamma of channel tid, kept by reducer thread tid < D
+#pragma unroll
   for (int it = 0; it < kNormIters; ++it) {
     // row pass: per token, over its D channels (16 lanes of a DPP row)
     if constexpr (NT == 16) {
